@@ -1,0 +1,131 @@
+/*
+ * libgemm — FP8 (E4M3) per-tensor-scaled GEMM and FP16 GEMM for AMD Instinct
+ * MI355X (gfx950), with the amax and FP8 quantize steps that feed it.
+ *
+ * Sources that define the operations (cited per entry point below):
+ *   P1  DeepGEMM deep-dive article (hnwysp.cn, news 84236)
+ *   P2  "DeepGEMM实战：FP8矩阵乘法与JIT编译优化指南" (sheratonhq.com, news 156926)
+ *   P3  "HGEMM优化：深度学习中的矩阵乘法性能提升策略" (jsqmd.com, news 710660)
+ *
+ * Common conventions
+ *   - Every matrix is row-major and densely packed: A[M,K], B[K,N], C[M,N]
+ *     (leading dimensions K, N and N). Element (i,j) of C is at C + i*N + j.
+ *   - Every data pointer is a device pointer (memory the current HIP device
+ *     can read or write). Scale arguments are device pointers to ONE float.
+ *   - The caller owns every buffer. The library allocates no device memory and
+ *     keeps no per-call state; entry points are reentrant and thread-safe.
+ *   - Each call validates its arguments on the host first; on any error it
+ *     returns a negative status and enqueues nothing. On success the work is
+ *     enqueued on `stream` (NULL = the null stream) and the call returns
+ *     without synchronising; faults during execution surface at the caller's
+ *     next synchronisation, as for any HIP kernel.
+ *   - Outputs must not overlap inputs.
+ *   - Results never depend on pointer alignment; 16-byte aligned pointers and
+ *     row lengths that are multiples of 16 bytes take the fastest kernels.
+ *   - Dimensions are int64_t; each must be in [0, 2^31 - 1].
+ */
+#ifndef LIBGEMM_H
+#define LIBGEMM_H
+
+#include <stdint.h>
+
+#include <hip/hip_runtime_api.h> /* hipStream_t */
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+/* ------------------------------------------------------------ statuses */
+#define GEMM_OK 0
+#define GEMM_ERR_NULL (-1)        /* a required pointer is NULL                          */
+#define GEMM_ERR_DIM (-2)         /* a dimension is negative or above 2^31 - 1             */
+#define GEMM_ERR_DTYPE (-3)       /* unknown out_dtype, or one the entry point cannot write */
+#define GEMM_ERR_SCALE (-4)       /* sOut is NULL while out_dtype == GEMM_OUT_E4M3         */
+#define GEMM_ERR_LAUNCH (-5)      /* the HIP runtime rejected a kernel launch              */
+#define GEMM_ERR_UNSUPPORTED (-6) /* no kernel for this request                            */
+#define GEMM_ERR_DEVICE (-7)      /* no current HIP device, or it is not gfx950            */
+#define GEMM_ERR_ALIAS (-8)       /* the output overlaps an input                          */
+
+/* ------------------------------------------------------- output types */
+#define GEMM_OUT_F32 0  /* float                                                  */
+#define GEMM_OUT_F16 1  /* IEEE binary16, round to nearest even, overflow to inf   */
+#define GEMM_OUT_E4M3 2 /* OCP E4M3 code (uint8), nearest even, saturate at +-448 */
+
+/*
+ * gemm_f16 — C = A·B for FP16 operands with FP32 accumulation.
+ * P3 §1.3 (half-precision GEMM with a 32-bit accumulator) and P1 §4.1 (the
+ * [1,4096]x[4096,12288] projection as the M = 1 case).
+ *   A          device, _Float16[M*K], row-major
+ *   B          device, _Float16[K*N], row-major
+ *   C          device, float[M*N] (out_dtype GEMM_OUT_F32) or _Float16[M*N]
+ *              (GEMM_OUT_F16); written, never read
+ *   out_dtype  GEMM_OUT_F32 or GEMM_OUT_F16 (anything else: GEMM_ERR_DTYPE)
+ *   M, N, K    M = 0 or N = 0 is a no-op; K = 0 writes zeros (the empty sum)
+ * M <= 16 runs an HBM-streaming kernel, larger M an MFMA tile kernel; the
+ * choice never changes which outputs are written.
+ */
+int gemm_f16(const void* A, const void* B, void* C, int out_dtype,
+             int64_t M, int64_t N, int64_t K, hipStream_t stream);
+
+/*
+ * gemm_fp8_scaled — C = (sA·A)(sB·B) for E4M3 operands, FP32 accumulation.
+ * P2 §2.1 (FP8 inputs, FP32 accumulator), §3.2 (per-tensor scales applied
+ * once to the accumulator at write-back; an FP8 output is divided by its own
+ * output scale), §4.3 (the call takes A, B, M, N, K and the scales; output
+ * FP32 or FP8, FP8 needing an output scale).
+ *   A, B       device, uint8 E4M3 codes, A[M*K] and B[K*N] row-major
+ *   sA, sB     device pointers to one float each (per-tensor scales)
+ *   sOut       device pointer to one float; required iff out_dtype ==
+ *              GEMM_OUT_E4M3 (else ignored, may be NULL)
+ *   C          device, float / _Float16 / uint8 per out_dtype, [M*N]
+ *   out_dtype  GEMM_OUT_F32, GEMM_OUT_F16 or GEMM_OUT_E4M3
+ * Element value: y = acc·(sA·sB) with acc the FP32 sum of decoded products;
+ * F32 writes y, F16 writes RNE(y), E4M3 writes E4M3(y / sOut).
+ */
+int gemm_fp8_scaled(const uint8_t* A, const uint8_t* B, const float* sA, const float* sB,
+                    const float* sOut, void* C, int out_dtype,
+                    int64_t M, int64_t N, int64_t K, hipStream_t stream);
+
+/*
+ * quantize_fp8 — q[i] = E4M3(fl32(x[i] / scale)).
+ * P2 §4.3 (fp8 = clamp(round(x / scale), -448, 448)): the quotient is the
+ * correctly rounded FP32 division; it is rounded to the nearest E4M3 value
+ * (ties to the even code) and saturated at +-448; +-inf saturate, NaN gives
+ * the code 0x7F; -0 and negative values that round to zero give 0x80.
+ *   x      device, float[n]
+ *   n      number of elements (0: no-op)
+ *   scale  device pointer to one float (e.g. the one amax_f32 writes)
+ *   q      device, uint8[n], written; must not overlap x
+ */
+int quantize_fp8(const float* x, int64_t n, const float* scale, uint8_t* q, hipStream_t stream);
+
+/*
+ * amax_f32 — *amax = max_i |x[i]| (exact; NaN if any x[i] is NaN; 0 for
+ * n = 0) and, when scale != NULL, *scale = fl32(*amax / 448), replaced by 1
+ * when that is 0 (P2 §3.2: per-tensor scale = max|x| / 448, 448 being the
+ * largest E4M3 value; P1 §3.3: the maximum is taken on the GPU on a stream).
+ *   x      device, float[n]
+ *   amax   device pointer to one float, written
+ *   scale  device pointer to one float or NULL; written when non-NULL
+ */
+int amax_f32(const float* x, int64_t n, float* amax, float* scale, hipStream_t stream);
+
+/* Human-readable name of a status code (a static string). */
+const char* gemm_status_str(int status);
+
+/*
+ * gemm_select_config — host-only query of the shape-to-kernel selector
+ * (P3 §3.1: tile sizes chosen from M, N and K; P2 §3.3: a smaller tile when
+ * edge waste is high). Writes the name of the kernel configuration that
+ * gemm_f16 (kind 0) or gemm_fp8_scaled (kind 1) would launch for this shape
+ * into buf (NUL-terminated, truncated to buflen) and returns GEMM_OK, or a
+ * negative status for invalid arguments. Makes no HIP call.
+ */
+int gemm_select_config(int kind, int out_dtype, int64_t M, int64_t N, int64_t K,
+                       char* buf, int buflen);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* LIBGEMM_H */

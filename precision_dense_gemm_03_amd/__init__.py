@@ -1,0 +1,185 @@
+"""Python binding of libgemm (include/libgemm.h): argument marshalling only.
+
+Every step of the GEMM path runs in the HIP kernels of libgemm.so; this module
+only turns torch tensors (device memory) and streams into the C-ABI's plain
+pointers and sizes, and turns negative statuses into exceptions. It has no
+fallback: if libgemm.so is not built, every call raises.
+
+Functions keep the C names:
+    gemm_f16(A, B, C, stream=None)
+    gemm_fp8_scaled(A, B, sA, sB, C, sOut=None, stream=None)
+    quantize_fp8(x, scale, q=None, stream=None) -> q
+    amax_f32(x, amax=None, scale=None, stream=None) -> (amax, scale)
+    select_config(kind, out_dtype, M, N, K) -> str   (host-only query)
+The output dtype of a GEMM is taken from C: float32, float16, or uint8
+(E4M3 codes; torch.float8_e4m3fn tensors are accepted and viewed as uint8).
+"""
+import ctypes
+import os
+
+PKG_DIR = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(PKG_DIR, "libgemm.so")
+
+OUT_F32 = 0
+OUT_F16 = 1
+OUT_E4M3 = 2
+KIND_F16 = 0
+KIND_FP8 = 1
+
+GEMM_OK = 0
+STATUS_NAMES = {
+    0: "GEMM_OK", -1: "GEMM_ERR_NULL", -2: "GEMM_ERR_DIM", -3: "GEMM_ERR_DTYPE",
+    -4: "GEMM_ERR_SCALE", -5: "GEMM_ERR_LAUNCH", -6: "GEMM_ERR_UNSUPPORTED",
+    -7: "GEMM_ERR_DEVICE", -8: "GEMM_ERR_ALIAS",
+}
+
+_lib = None
+
+
+class GemmError(RuntimeError):
+    def __init__(self, status, what):
+        self.status = status
+        super().__init__(f"{what}: {STATUS_NAMES.get(status, status)} ({status_str(status)})")
+
+
+def lib() -> ctypes.CDLL:
+    """The loaded libgemm.so (raises if it has not been built)."""
+    global _lib
+    if _lib is not None:
+        return _lib
+    if not os.path.exists(LIB_PATH):
+        raise RuntimeError(f"{LIB_PATH} is missing: build it first (python __graft_entry__.py build, "
+                           "or python precision_dense_gemm_03_amd/_build.py)")
+    L = ctypes.CDLL(LIB_PATH)
+    vp, i64, i32 = ctypes.c_void_p, ctypes.c_int64, ctypes.c_int
+    L.gemm_f16.restype = i32
+    L.gemm_f16.argtypes = [vp, vp, vp, i32, i64, i64, i64, vp]
+    L.gemm_fp8_scaled.restype = i32
+    L.gemm_fp8_scaled.argtypes = [vp, vp, vp, vp, vp, vp, i32, i64, i64, i64, vp]
+    L.quantize_fp8.restype = i32
+    L.quantize_fp8.argtypes = [vp, i64, vp, vp, vp]
+    L.amax_f32.restype = i32
+    L.amax_f32.argtypes = [vp, i64, vp, vp, vp]
+    L.gemm_status_str.restype = ctypes.c_char_p
+    L.gemm_status_str.argtypes = [i32]
+    L.gemm_select_config.restype = i32
+    L.gemm_select_config.argtypes = [i32, i32, i64, i64, i64, ctypes.c_char_p, i32]
+    _lib = L
+    return L
+
+
+def status_str(status: int) -> str:
+    return lib().gemm_status_str(int(status)).decode()
+
+
+def _check(status: int, what: str):
+    if status != GEMM_OK:
+        raise GemmError(status, what)
+
+
+def _torch():
+    import torch
+    return torch
+
+
+def _stream_handle(stream):
+    if stream is None:
+        return _torch().cuda.current_stream().cuda_stream
+    if isinstance(stream, int):
+        return stream
+    return stream.cuda_stream
+
+
+def _ptr(t):
+    if t is None:
+        return None
+    if not t.is_cuda:
+        raise ValueError("libgemm takes device tensors")
+    if not t.is_contiguous():
+        raise ValueError("libgemm takes contiguous (row-major) tensors")
+    return t.data_ptr()
+
+
+def _out_dtype(C):
+    torch = _torch()
+    if C.dtype == torch.float32:
+        return OUT_F32
+    if C.dtype == torch.float16:
+        return OUT_F16
+    if C.dtype in (torch.uint8, torch.float8_e4m3fn):
+        return OUT_E4M3
+    raise ValueError(f"unsupported output dtype {C.dtype}")
+
+
+def _dims(A, B, C):
+    if A.dim() != 2 or B.dim() != 2 or C.dim() != 2:
+        raise ValueError("A, B and C must be 2-D")
+    M, K = A.shape
+    K2, N = B.shape
+    if K2 != K or tuple(C.shape) != (M, N):
+        raise ValueError(f"shape mismatch: A{tuple(A.shape)} B{tuple(B.shape)} C{tuple(C.shape)}")
+    return M, N, K
+
+
+def gemm_f16(A, B, C, stream=None):
+    """C = A @ B for float16 A[M,K], B[K,N]; C float32 or float16 [M,N]."""
+    torch = _torch()
+    if A.dtype != torch.float16 or B.dtype != torch.float16:
+        raise ValueError("gemm_f16 takes float16 operands")
+    M, N, K = _dims(A, B, C)
+    _check(lib().gemm_f16(_ptr(A), _ptr(B), _ptr(C), _out_dtype(C), M, N, K, _stream_handle(stream)), "gemm_f16")
+    return C
+
+
+def _u8(t):
+    torch = _torch()
+    if t.dtype == torch.float8_e4m3fn:
+        return t.view(torch.uint8)
+    if t.dtype != torch.uint8:
+        raise ValueError("E4M3 tensors must be uint8 codes or torch.float8_e4m3fn")
+    return t
+
+
+def gemm_fp8_scaled(A, B, sA, sB, C, sOut=None, stream=None):
+    """C = (sA*A) @ (sB*B) for E4M3 A[M,K], B[K,N]; sA, sB (and sOut for an
+    E4M3 C) are one-element float32 device tensors."""
+    A, B = _u8(A), _u8(B)
+    out = _out_dtype(C)
+    Cv = _u8(C) if out == OUT_E4M3 else C
+    M, N, K = _dims(A, B, Cv)
+    _check(lib().gemm_fp8_scaled(_ptr(A), _ptr(B), _ptr(sA), _ptr(sB), _ptr(sOut), _ptr(Cv), out, M, N, K,
+                                 _stream_handle(stream)), "gemm_fp8_scaled")
+    return C
+
+
+def quantize_fp8(x, scale, q=None, stream=None):
+    """E4M3 codes of x / scale (uint8, same shape as x)."""
+    torch = _torch()
+    if x.dtype != torch.float32:
+        raise ValueError("quantize_fp8 takes float32 input")
+    if q is None:
+        q = torch.empty(x.shape, dtype=torch.uint8, device=x.device)
+    qv = _u8(q)
+    if qv.numel() != x.numel():
+        raise ValueError("q must have as many elements as x")
+    _check(lib().quantize_fp8(_ptr(x), x.numel(), _ptr(scale), _ptr(qv), _stream_handle(stream)), "quantize_fp8")
+    return q
+
+
+def amax_f32(x, amax=None, scale=None, stream=None):
+    """(amax, scale): max|x| and max|x|/448 (1 if that is 0) as 1-element device tensors."""
+    torch = _torch()
+    if x.dtype != torch.float32:
+        raise ValueError("amax_f32 takes float32 input")
+    if amax is None:
+        amax = torch.empty(1, dtype=torch.float32, device=x.device)
+    if scale is None:
+        scale = torch.empty(1, dtype=torch.float32, device=x.device)
+    _check(lib().amax_f32(_ptr(x), x.numel(), _ptr(amax), _ptr(scale), _stream_handle(stream)), "amax_f32")
+    return amax, scale
+
+
+def select_config(kind: int, out_dtype: int, M: int, N: int, K: int) -> str:
+    buf = ctypes.create_string_buffer(128)
+    _check(lib().gemm_select_config(kind, out_dtype, M, N, K, buf, len(buf)), "gemm_select_config")
+    return buf.value.decode()

@@ -1,0 +1,157 @@
+// C-ABI entry points of libgemm (declared in include/libgemm.h).
+//
+// Every entry point validates its arguments before any HIP call, so invalid
+// requests return a status and enqueue nothing; then it checks (once per
+// device) that the current device is gfx950, selects a kernel configuration
+// from the shape and launches on the caller's stream without synchronising.
+#include <hip/hip_runtime.h>
+
+#include <atomic>
+#include <cstdio>
+#include <cstring>
+
+#include "kernels.h"
+#include "libgemm.h"
+
+using namespace libgemm;
+
+namespace {
+
+constexpr int64_t kMaxDim = 0x7FFFFFFF;
+constexpr int kMaxDevices = 64;
+
+bool dim_ok(int64_t d) { return d >= 0 && d <= kMaxDim; }
+
+// Byte ranges [p, p+n) and [q, q+m) overlap (empty ranges never do).
+bool overlaps(const void* p, int64_t n, const void* q, int64_t m) {
+    if (!p || !q || n <= 0 || m <= 0) return false;
+    const uintptr_t a = (uintptr_t)p, b = (uintptr_t)q;
+    return a < b + (uintptr_t)m && b < a + (uintptr_t)n;
+}
+
+int64_t out_size(int out_dtype) { return out_dtype == GEMM_OUT_F32 ? 4 : (out_dtype == GEMM_OUT_F16 ? 2 : 1); }
+
+// 0 unknown, 1 gfx950, 2 other architecture; filled once per device.
+std::atomic<int> g_device_state[kMaxDevices];
+
+int check_device() {
+    int dev = -1;
+    if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices) {
+        (void)hipGetLastError();
+        return GEMM_ERR_DEVICE;
+    }
+    int st = g_device_state[dev].load(std::memory_order_acquire);
+    if (st == 0) {
+        hipDeviceProp_t prop;
+        if (hipGetDeviceProperties(&prop, dev) != hipSuccess) {
+            (void)hipGetLastError();
+            return GEMM_ERR_DEVICE;
+        }
+        st = (std::strncmp(prop.gcnArchName, "gfx950", 6) == 0) ? 1 : 2;
+        g_device_state[dev].store(st, std::memory_order_release);
+    }
+    return st == 1 ? GEMM_OK : GEMM_ERR_DEVICE;
+}
+
+int status_of(hipError_t e) {
+    if (e == hipSuccess) return GEMM_OK;
+    (void)hipGetLastError();
+    return GEMM_ERR_LAUNCH;
+}
+
+int run_gemm(int kind, const GemmArgs& a) {
+    int st = check_device();
+    if (st != GEMM_OK) return st;
+    if (a.M == 0 || a.N == 0) return GEMM_OK;
+    if (a.K == 0) return status_of(launch_fill_zero(a.C, a.M * a.N, a.out_dtype, a.stream));
+    const GemmConfig* cfg = select_config(kind, a.out_dtype, a.M, a.N, a.K);
+    if (!cfg) return GEMM_ERR_UNSUPPORTED;
+    return status_of(cfg->launch(a));
+}
+
+}  // namespace
+
+extern "C" {
+
+int gemm_f16(const void* A, const void* B, void* C, int out_dtype, int64_t M, int64_t N, int64_t K,
+             hipStream_t stream) {
+    if (out_dtype != GEMM_OUT_F32 && out_dtype != GEMM_OUT_F16) return GEMM_ERR_DTYPE;
+    if (!dim_ok(M) || !dim_ok(N) || !dim_ok(K)) return GEMM_ERR_DIM;
+    if (M > 0 && N > 0) {
+        if (!C) return GEMM_ERR_NULL;
+        if (K > 0 && (!A || !B)) return GEMM_ERR_NULL;
+        const int64_t cbytes = M * N * out_size(out_dtype);
+        if (K > 0 && (overlaps(C, cbytes, A, M * K * 2) || overlaps(C, cbytes, B, K * N * 2))) return GEMM_ERR_ALIAS;
+    }
+    GemmArgs a{A, B, C, nullptr, nullptr, nullptr, out_dtype, M, N, K, stream};
+    return run_gemm(KIND_F16, a);
+}
+
+int gemm_fp8_scaled(const uint8_t* A, const uint8_t* B, const float* sA, const float* sB, const float* sOut,
+                    void* C, int out_dtype, int64_t M, int64_t N, int64_t K, hipStream_t stream) {
+    if (out_dtype != GEMM_OUT_F32 && out_dtype != GEMM_OUT_F16 && out_dtype != GEMM_OUT_E4M3)
+        return GEMM_ERR_DTYPE;
+    if (!dim_ok(M) || !dim_ok(N) || !dim_ok(K)) return GEMM_ERR_DIM;
+    if (M > 0 && N > 0) {
+        if (!C || !sA || !sB) return GEMM_ERR_NULL;
+        if (out_dtype == GEMM_OUT_E4M3 && !sOut) return GEMM_ERR_SCALE;
+        if (K > 0 && (!A || !B)) return GEMM_ERR_NULL;
+        const int64_t cbytes = M * N * out_size(out_dtype);
+        if (K > 0 && (overlaps(C, cbytes, A, M * K) || overlaps(C, cbytes, B, K * N))) return GEMM_ERR_ALIAS;
+        if (overlaps(C, cbytes, sA, 4) || overlaps(C, cbytes, sB, 4) ||
+            (out_dtype == GEMM_OUT_E4M3 && overlaps(C, cbytes, sOut, 4)))
+            return GEMM_ERR_ALIAS;
+    }
+    GemmArgs a{A, B, C, sA, sB, out_dtype == GEMM_OUT_E4M3 ? sOut : nullptr, out_dtype, M, N, K, stream};
+    return run_gemm(KIND_FP8, a);
+}
+
+int quantize_fp8(const float* x, int64_t n, const float* scale, uint8_t* q, hipStream_t stream) {
+    if (n < 0) return GEMM_ERR_DIM;
+    if (n == 0) return GEMM_OK;
+    if (!x || !scale || !q) return GEMM_ERR_NULL;
+    if (overlaps(q, n, x, 4 * n) || overlaps(q, n, scale, 4)) return GEMM_ERR_ALIAS;
+    const int st = check_device();
+    if (st != GEMM_OK) return st;
+    return status_of(launch_quantize(x, n, scale, q, stream));
+}
+
+int amax_f32(const float* x, int64_t n, float* amax, float* scale, hipStream_t stream) {
+    if (n < 0) return GEMM_ERR_DIM;
+    if (!amax) return GEMM_ERR_NULL;
+    if (n > 0 && !x) return GEMM_ERR_NULL;
+    if (overlaps(amax, 4, x, 4 * n) || overlaps(scale, 4, x, 4 * n) || overlaps(amax, 4, scale, 4))
+        return GEMM_ERR_ALIAS;
+    const int st = check_device();
+    if (st != GEMM_OK) return st;
+    return status_of(launch_amax(x, n, amax, scale, stream));
+}
+
+const char* gemm_status_str(int status) {
+    switch (status) {
+        case GEMM_OK: return "ok";
+        case GEMM_ERR_NULL: return "a required pointer is NULL";
+        case GEMM_ERR_DIM: return "a dimension is negative or above 2^31-1";
+        case GEMM_ERR_DTYPE: return "unsupported output dtype";
+        case GEMM_ERR_SCALE: return "sOut is required for E4M3 output";
+        case GEMM_ERR_LAUNCH: return "kernel launch failed";
+        case GEMM_ERR_UNSUPPORTED: return "no kernel for this request";
+        case GEMM_ERR_DEVICE: return "no current HIP device, or it is not gfx950";
+        case GEMM_ERR_ALIAS: return "output overlaps an input";
+        default: return "unknown status";
+    }
+}
+
+int gemm_select_config(int kind, int out_dtype, int64_t M, int64_t N, int64_t K, char* buf, int buflen) {
+    if (kind != KIND_F16 && kind != KIND_FP8) return GEMM_ERR_DTYPE;
+    if (out_dtype < GEMM_OUT_F32 || out_dtype > GEMM_OUT_E4M3 || (kind == KIND_F16 && out_dtype == GEMM_OUT_E4M3))
+        return GEMM_ERR_DTYPE;
+    if (!dim_ok(M) || !dim_ok(N) || !dim_ok(K)) return GEMM_ERR_DIM;
+    if (!buf || buflen <= 0) return GEMM_ERR_NULL;
+    const GemmConfig* cfg = select_config(kind, out_dtype, M, N, K);
+    if (!cfg) return GEMM_ERR_UNSUPPORTED;
+    std::snprintf(buf, (size_t)buflen, "%s", cfg->name);
+    return GEMM_OK;
+}
+
+}  // extern "C"

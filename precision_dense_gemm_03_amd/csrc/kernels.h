@@ -1,0 +1,48 @@
+// Internal interface between the C-ABI layer, the shape selector and the kernels.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace libgemm {
+
+enum OperandKind { KIND_F16 = 0, KIND_FP8 = 1 };
+
+// Arguments every GEMM launcher receives (validated by the C-ABI layer).
+struct GemmArgs {
+    const void* A;
+    const void* B;
+    void* C;
+    const float* sA;   // device scalars; NULL for FP16 (scale 1)
+    const float* sB;
+    const float* sOut; // device scalar; only read for E4M3 output
+    int out_dtype;
+    int64_t M, N, K;
+    hipStream_t stream;
+};
+
+typedef hipError_t (*GemmLauncher)(const GemmArgs&);
+
+// One entry of the compiled-in configuration table.
+struct GemmConfig {
+    const char* name;   // e.g. "tile_fp8_256x256x128_w2x2"
+    int kind;           // OperandKind
+    int family;         // 0 = MFMA tile kernel, 1 = M<=16 streaming kernel
+    int bm, bn, bk;     // tile (stream: bm = max M, bn = columns per block, bk = k-slices)
+    GemmLauncher launch;
+};
+
+// Configuration tables, defined next to their kernels.
+const GemmConfig* tile_configs(int* count);
+const GemmConfig* stream_configs(int* count);
+
+// Shape -> configuration (host only, no HIP calls). Returns NULL if none fits.
+const GemmConfig* select_config(int kind, int out_dtype, int64_t M, int64_t N, int64_t K);
+
+// amax / quantize launchers.
+hipError_t launch_amax(const float* x, int64_t n, float* amax, float* scale, hipStream_t stream);
+hipError_t launch_quantize(const float* x, int64_t n, const float* scale, uint8_t* q, hipStream_t stream);
+// Writes zeros to an [M,N] output of the given dtype (the K = 0 empty sum).
+hipError_t launch_fill_zero(void* C, int64_t count, int out_dtype, hipStream_t stream);
+
+}  // namespace libgemm

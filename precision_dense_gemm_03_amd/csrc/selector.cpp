@@ -1,0 +1,77 @@
+// Shape -> kernel configuration selector (host only; makes no HIP call).
+//
+// "HGEMM优化：深度学习中的矩阵乘法性能提升策略" (jsqmd.com news 710660) §3.1 picks
+// the tile from M, N and K instead of one fixed tile, and §1.1 separates small,
+// medium and large problems; "DeepGEMM实战：FP8矩阵乘法与JIT编译优化指南" §3.3 picks a
+// smaller tile when the edge tile would be mostly padding (M = 65 on a 64 tile)
+// and §5.2 allows a manual override of the tile choice. On MI355X the rules are
+// re-derived for 256 compute units:
+//   1. M <= 16 (decode): the HBM-streaming kernel sized for the smallest
+//      compiled M bound >= M (FP8 streaming kernels exist up to M = 4).
+//   2. Otherwise the MFMA tile kernel: the largest square tile (256, 128, 64)
+//      whose grid still gives every CU a tile (>= 256 tiles) and whose padded
+//      area wastes at most 25 %; if none fills the chip, the tile with the
+//      most tiles (64).
+//   3. LIBGEMM_CONFIG=<config name> replaces the choice when that config can
+//      serve the request (same operand kind; streaming configs need M <= bound).
+#include <cstdlib>
+#include <cstring>
+
+#include "kernels.h"
+
+namespace libgemm {
+
+namespace {
+
+constexpr int64_t kNumCUs = 256;
+
+const GemmConfig* find_named(const char* name, int kind, int64_t M) {
+    int ns = 0, nt = 0;
+    const GemmConfig* st = stream_configs(&ns);
+    const GemmConfig* tt = tile_configs(&nt);
+    for (int i = 0; i < ns; ++i)
+        if (std::strcmp(st[i].name, name) == 0 && st[i].kind == kind && M <= st[i].bm) return &st[i];
+    for (int i = 0; i < nt; ++i)
+        if (std::strcmp(tt[i].name, name) == 0 && tt[i].kind == kind) return &tt[i];
+    return nullptr;
+}
+
+const GemmConfig* tile_with(int kind, int bm) {
+    int nt = 0;
+    const GemmConfig* tt = tile_configs(&nt);
+    for (int i = 0; i < nt; ++i)
+        if (tt[i].kind == kind && tt[i].bm == bm) return &tt[i];
+    return nullptr;
+}
+
+}  // namespace
+
+const GemmConfig* select_config(int kind, int out_dtype, int64_t M, int64_t N, int64_t K) {
+    (void)out_dtype;
+    (void)K;
+    if (const char* env = std::getenv("LIBGEMM_CONFIG")) {
+        if (const GemmConfig* c = find_named(env, kind, M)) return c;
+    }
+    if (M <= 16) {
+        const GemmConfig* best = nullptr;
+        int ns = 0;
+        const GemmConfig* st = stream_configs(&ns);
+        for (int i = 0; i < ns; ++i) {
+            const GemmConfig& c = st[i];
+            if (c.kind == kind && M <= c.bm && (!best || c.bm < best->bm)) best = &c;
+        }
+        if (best) return best;
+    }
+    static const int sizes[] = {256, 128, 64};
+    for (int bm : sizes) {
+        const int64_t tm = (M + bm - 1) / bm, tn = (N + bm - 1) / bm;
+        const double useful = (double)M * (double)N;
+        const double padded = (double)(tm * bm) * (double)(tn * bm);
+        if (tm * tn >= kNumCUs && useful >= 0.75 * padded) {
+            if (const GemmConfig* c = tile_with(kind, bm)) return c;
+        }
+    }
+    return tile_with(kind, 64);
+}
+
+}  // namespace libgemm

@@ -1,0 +1,441 @@
+"""GPU parity: the HIP path through the C-ABI against the oracle, element by element.
+
+Quantize and amax must be bit-exact; GEMM outputs must satisfy the per-element
+bounds in tests/parity.py. Inputs are the seeded synthetic workloads (module
+workloads) plus edge, degenerate and adversarial cases. Each test prints the
+case it is about to launch.
+"""
+import numpy as np
+import pytest
+import torch
+
+import oracle as orc
+import precision_dense_gemm_03_amd as g
+import workloads as wl
+from parity import check_e4m3, check_f16, check_f32, fp8_dot_allowance
+
+pytestmark = pytest.mark.gpu
+
+DEV = torch.device("cuda:0")
+
+
+def say(*a):
+    print(*a, flush=True)
+
+
+@pytest.fixture(scope="module", autouse=True)
+def _gpu():
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    torch.cuda.set_device(DEV)
+    g.lib()  # fails loudly when libgemm.so is missing
+    yield
+    torch.cuda.synchronize()
+
+
+def dev(x):
+    return torch.from_numpy(np.ascontiguousarray(x)).to(DEV)
+
+
+def host(t):
+    torch.cuda.synchronize()
+    return t.cpu().numpy()
+
+
+def scalar(v):
+    return torch.tensor([float(np.float32(v))], dtype=torch.float32, device=DEV)
+
+
+def fp8_chain(xa, xb):
+    """GPU amax -> scale -> quantize for both operands, checked bit-exact
+    against the oracle. Returns device codes, device scales and the oracle's
+    host codes and scales."""
+    out = []
+    for x in (xa, xb):
+        tx = dev(x)
+        amax, s = g.amax_f32(tx)
+        q = g.quantize_fp8(tx, s)
+        oa = orc.amax(x)
+        os_ = orc.scale_from_amax(oa)
+        assert host(amax).view(np.uint32)[0] == np.float32(oa).view(np.uint32), "amax bits"
+        assert host(s).view(np.uint32)[0] == np.float32(os_).view(np.uint32), "scale bits"
+        oq = orc.quantize(x, os_)
+        assert np.array_equal(host(q), oq), "quantized codes"
+        out.append((q, s, oq, os_))
+        del tx
+    return out
+
+
+def sample_rows(M, n=24):
+    rows = set([0, M - 1, M // 2])
+    rows.update(range(0, M, max(1, M // n)))
+    return sorted(r for r in rows if 0 <= r < M)
+
+
+# ------------------------------------------------------------ amax / quantize
+
+@pytest.mark.parametrize("n", [1, 15, 16, 17, 4096, 1000003, 1024 * 1024])
+def test_amax_scale_bit_exact(n):
+    say(f"amax n={n}")
+    x = wl.random_normal_f32((n,), 100 + n)
+    x[n // 3] = -7.75
+    tx = dev(x)
+    amax, s = g.amax_f32(tx)
+    assert host(amax)[0] == orc.amax(x)
+    assert host(s).view(np.uint32)[0] == orc.scale_from_amax(orc.amax(x)).view(np.uint32)
+    # unaligned start (4 bytes past a 16-byte boundary): scalar path
+    if n > 2:
+        amax2, s2 = g.amax_f32(tx[1:])
+        assert host(amax2)[0] == orc.amax(x[1:])
+
+
+def test_amax_special_values():
+    say("amax special values")
+    for x, expect in [(np.zeros(1000, np.float32), 0.0),
+                      (np.array([1e-45, -2e-45], np.float32), np.float32(2e-45)),
+                      (np.array([1.0, -np.inf, 3.0], np.float32), np.inf)]:
+        amax, s = g.amax_f32(dev(x))
+        assert host(amax)[0] == expect
+        assert host(s)[0] == orc.scale_from_amax(orc.amax(x))
+    x = wl.random_normal_f32((100000,), 7)
+    x[12345] = np.nan
+    amax, s = g.amax_f32(dev(x))
+    assert np.isnan(host(amax)[0]) and np.isnan(host(s)[0])
+    amax, s = g.amax_f32(torch.empty(0, dtype=torch.float32, device=DEV))
+    assert host(amax)[0] == 0.0 and host(s)[0] == 1.0
+
+
+@pytest.mark.parametrize("w", [wl.C2, wl.C4[2], wl.C4[6]], ids=lambda w: w.name)
+def test_quantize_workloads_bit_exact(w):
+    say(f"quantize {w.name}")
+    fp8_chain(wl.operand(w, 0), wl.operand(w, 1))
+
+
+def test_quantize_unaligned_and_tails():
+    x = wl.random_normal_f32((100003,), 11) * np.float32(30.0)
+    s = np.float32(0.0371)
+    tx, ts = dev(x), scalar(s)
+    for lo, hi in [(0, 100003), (1, 100003), (3, 77), (16, 16 + 33), (5, 6)]:
+        say(f"quantize slice {lo}:{hi}")
+        q = torch.empty(hi - lo + 1, dtype=torch.uint8, device=DEV)[1:]  # unaligned output too
+        g.quantize_fp8(tx[lo:hi], ts, q)
+        assert np.array_equal(host(q), orc.quantize(x[lo:hi], s))
+
+
+@pytest.mark.parametrize("s", [1.0, 3.0, 0.37, 1e-3, 2.5e5, 1e-30])
+def test_quantize_random_patterns_with_scales(s):
+    say(f"quantize random bit patterns s={s}")
+    bits = np.random.default_rng(int(s * 1000) % 2**32).integers(0, 2**32, 1 << 22, dtype=np.uint64).astype(np.uint32)
+    x = bits.view(np.float32)
+    q = g.quantize_fp8(dev(x), scalar(s))
+    assert np.array_equal(host(q), orc.quantize(x, np.float32(s)))
+
+
+def test_quantize_all_fp32_bit_patterns():
+    """All 2^32 inputs with scale 1 (so the codec alone is under test)."""
+    chunk = 1 << 28
+    one = scalar(1.0)
+    q = torch.empty(chunk, dtype=torch.uint8, device=DEV)
+    for start in range(0, 1 << 32, chunk):
+        say(f"quantize exhaustive chunk {start:#x}")
+        v = torch.arange(start, start + chunk, dtype=torch.int64, device=DEV)
+        v = torch.where(v >= 2 ** 31, v - 2 ** 32, v)          # the same 32 bits as a signed value
+        xs = v.to(torch.int32).view(torch.float32)
+        del v
+        g.quantize_fp8(xs, one, q)
+        ref = orc.e4m3_encode_f32bits(np.arange(chunk, dtype=np.uint32) + np.uint32(start))
+        got = host(q)
+        if not np.array_equal(got, ref):
+            i = int(np.argmax(got != ref))
+            raise AssertionError(f"bits {start + i:#010x}: got {got[i]:#04x} ref {ref[i]:#04x}")
+        del xs
+
+
+# ------------------------------------------------------------------ GEMM
+
+def run_f16(a16, b16, out):
+    M, K = a16.shape
+    N = b16.shape[1]
+    C = torch.empty((M, N), dtype=torch.float32 if out == g.OUT_F32 else torch.float16, device=DEV)
+    g.gemm_f16(dev(a16), dev(b16), C)
+    return host(C)
+
+
+def run_fp8(qa, qb, sa, sb, out, s_out=None):
+    M, K = qa.shape
+    N = qb.shape[1]
+    dt = {g.OUT_F32: torch.float32, g.OUT_F16: torch.float16, g.OUT_E4M3: torch.uint8}[out]
+    C = torch.empty((M, N), dtype=dt, device=DEV)
+    g.gemm_fp8_scaled(qa, qb, sa, sb, C, None if s_out is None else scalar(s_out))
+    return host(C)
+
+
+def check_f16_gemm(a16, b16, out, rows=None, what=""):
+    got = run_f16(a16, b16, out)
+    R, S = orc.gemm(orc.FMT_F16, a16.view(np.uint16), b16.view(np.uint16), rows=rows)
+    if rows is not None:
+        got = got[rows]
+    (check_f32 if out == g.OUT_F32 else check_f16)(got, R, S, what=what)
+
+
+def test_gemm_f16_C1_256cube_f32out():
+    w = wl.C1
+    say(f"gemm {w.name}")
+    check_f16_gemm(wl.operand(w, 0), wl.operand(w, 1), g.OUT_F32, what=w.name)
+
+
+def test_gemm_fp8_C2_1024cube_f32out():
+    w = wl.C2
+    say(f"gemm {w.name}")
+    (qa, sa, oqa, osa), (qb, sb, oqb, osb) = fp8_chain(wl.operand(w, 0), wl.operand(w, 1))
+    got = run_fp8(qa, qb, sa, sb, g.OUT_F32)
+    R, S = orc.gemm(orc.FMT_E4M3, oqa, oqb)
+    check_f32(got, R, S, osa, osb, what=w.name)
+
+
+def test_gemm_all_sizes_1_to_8():
+    say("gemm all (M,N,K) in [1..8]^3")
+    seed = 0
+    sa, sb = scalar(0.75), scalar(1.5)
+    for M in range(1, 9):
+        for N in range(1, 9):
+            for K in range(1, 9):
+                seed += 1
+                a16 = wl.random_f16((M, K), seed)
+                b16 = wl.random_f16((K, N), 5000 + seed)
+                R, S = orc.gemm(orc.FMT_F16, a16.view(np.uint16), b16.view(np.uint16))
+                check_f32(run_f16(a16, b16, g.OUT_F32), R, S, what=f"f16 {M}x{N}x{K}")
+                check_f16(run_f16(a16, b16, g.OUT_F16), R, S, what=f"f16->f16 {M}x{N}x{K}")
+                ca = wl.random_e4m3_codes((M, K), seed)
+                cb = wl.random_e4m3_codes((K, N), 5000 + seed)
+                R, S = orc.gemm(orc.FMT_E4M3, ca, cb)
+                T = fp8_dot_allowance(ca, cb)
+                check_f32(run_fp8(dev(ca), dev(cb), sa, sb, g.OUT_F32), R, S, 0.75, 1.5, what=f"fp8 {M}x{N}x{K}", T=T)
+                V = R * 0.75 * 1.5
+                s_out = orc.scale_from_amax(np.float32(np.max(np.abs(V))))
+                check_e4m3(run_fp8(dev(ca), dev(cb), sa, sb, g.OUT_E4M3, s_out), R, S, 0.75, 1.5, s_out,
+                           what=f"fp8->e4m3 {M}x{N}x{K}", T=T)
+
+
+EDGE = [(m, n, k) for m in (1, 63, 65, 127, 129) for (n, k) in ((1000, 1000), (520, 999), (4096, 4096))]
+
+
+@pytest.mark.parametrize("M,N,K", EDGE)
+def test_gemm_f16_edges(M, N, K):
+    say(f"gemm f16 edge {M}x{N}x{K}")
+    a16 = wl.random_f16((M, K), M * 7 + K)
+    b16 = wl.random_f16((K, N), N * 3 + K)
+    check_f16_gemm(a16, b16, g.OUT_F32, what=f"f16 {M}x{N}x{K}")
+    check_f16_gemm(a16, b16, g.OUT_F16, what=f"f16->f16 {M}x{N}x{K}")
+
+
+@pytest.mark.parametrize("M,N,K", EDGE)
+def test_gemm_fp8_edges(M, N, K):
+    say(f"gemm fp8 edge {M}x{N}x{K}")
+    ca = wl.random_e4m3_codes((M, K), M * 11 + K)
+    cb = wl.random_e4m3_codes((K, N), N * 13 + K)
+    sa, sb = np.float32(0.02), np.float32(0.003)
+    # full-range codes: the rows checked carry the FP8 matrix-core allowance
+    rows = None if N * K <= 1 << 20 else sample_rows(M, 6)
+    R, S = orc.gemm(orc.FMT_E4M3, ca, cb, rows=rows)
+    T = fp8_dot_allowance(ca, cb, rows=rows)
+    sel = slice(None) if rows is None else rows
+    ta, tb, tsa, tsb = dev(ca), dev(cb), scalar(sa), scalar(sb)
+    check_f32(run_fp8(ta, tb, tsa, tsb, g.OUT_F32)[sel], R, S, sa, sb, what="f32", T=T)
+    check_f16(run_fp8(ta, tb, tsa, tsb, g.OUT_F16)[sel], R, S, sa, sb, what="f16", T=T)
+    s_out = orc.scale_from_amax(np.float32(np.max(np.abs(R * float(sa) * float(sb)))))
+    check_e4m3(run_fp8(ta, tb, tsa, tsb, g.OUT_E4M3, s_out)[sel], R, S, sa, sb, s_out, what="e4m3", T=T)
+
+
+@pytest.mark.parametrize("w", wl.C3, ids=lambda w: w.name)
+def test_decode_C3(w):
+    say(f"gemm {w.name}")
+    check_f16_gemm(wl.operand(w, 0), wl.operand(w, 1), g.OUT_F16, what=w.name)
+
+
+@pytest.mark.parametrize("w", wl.C4, ids=lambda w: w.name)
+def test_fp8_C4_fp8_output(w):
+    say(f"gemm {w.name}")
+    (qa, sa, oqa, osa), (qb, sb, oqb, osb) = fp8_chain(wl.operand(w, 0), wl.operand(w, 1))
+    rows = None if w.M <= 129 else sample_rows(w.M)
+    R, S = orc.gemm(orc.FMT_E4M3, oqa, oqb, rows=rows)
+    V = R * float(osa) * float(osb)
+    s_out = orc.scale_from_amax(np.float32(np.max(np.abs(V))))  # over the oracle-computed rows
+    got = run_fp8(qa, qb, sa, sb, g.OUT_E4M3, s_out)
+    if rows is not None:
+        got = got[rows]
+    check_e4m3(got, R, S, osa, osb, s_out, what=w.name)
+
+
+def test_fp8_C5_large_f16out_sampled():
+    w = wl.C5_FP8
+    say(f"gemm {w.name}")
+    (qa, sa, oqa, osa), (qb, sb, oqb, osb) = fp8_chain(wl.operand(w, 0), wl.operand(w, 1))
+    rows = sample_rows(w.M, 16)
+    got = run_fp8(qa, qb, sa, sb, g.OUT_F16)[rows]
+    R, S = orc.gemm(orc.FMT_E4M3, oqa, oqb, rows=rows)
+    check_f16(got, R, S, osa, osb, what=w.name)
+
+
+@pytest.mark.parametrize("w", [wl.C5_F16, wl.M0], ids=lambda w: w.name)
+def test_f16_large_sampled(w):
+    say(f"gemm {w.name}")
+    a16, b16 = wl.operand(w, 0), wl.operand(w, 1)
+    check_f16_gemm(a16, b16, g.OUT_F16, rows=sample_rows(w.M, 16), what=w.name)
+
+
+def test_fp8_dot_alignment_model():
+    """Pins the FP8 matrix-core behaviour the allowance models: within an
+    aligned group of 8 k, a product more than 2^13 below the group's largest
+    loses the bits below 2^(E-13); products in other groups, and products
+    within 2^6 of the maximum, are exact."""
+    say("fp8 dot alignment model")
+    M, N, K = 64, 64, 128   # tile kernel (M > 16)
+    ca = np.zeros((M, K), np.uint8)
+    cb = np.zeros((K, N), np.uint8)
+    cb[:, :] = 0x38                     # 1.0
+    ca[:, 0] = 0x78                     # 256 -> product 256 at k = 0
+    for i in range(M):
+        kk = [1, 7, 8, 9, 64, 127][i % 6]
+        ca[i, kk] = [0x20, 0x21, 0x27, 0x0F, 0x17, 0x03][i // 6 % 6]   # small products
+    got = run_fp8(dev(ca), dev(cb), scalar(1.0), scalar(1.0), g.OUT_F32)
+    A = orc.e4m3_decode(ca)
+    for i in range(M):
+        k1 = int(np.nonzero(ca[i, 1:])[0][0]) + 1
+        p1 = A[i, k1]
+        q = 2.0 ** (8 - 13)
+        expect = 256.0 + (np.trunc(p1 / q) * q if k1 < 8 else p1)
+        assert np.all(got[i] == expect), (i, k1, p1, got[i, 0], expect)
+    # the window follows the exponent SUM of the factors: (-40) x (-3*2^-9, a
+    # subnormal) = 0.234375 aligns on 2^(5-6) = 2^-1, so 2^-6 x 1.875*2^-6 =
+    # 7.5*2^-14 keeps only bits >= 2^(-1-13): 7*2^-14
+    ca = np.zeros((32, 128), np.uint8)
+    cb = np.zeros((128, 32), np.uint8)
+    ca[:, 0], ca[:, 2] = 0xE2, 0x08
+    cb[0, :], cb[2, :] = 0x83, 0x0F
+    got = run_fp8(dev(ca), dev(cb), scalar(1.0), scalar(1.0), g.OUT_F32)
+    assert np.all(got == np.float32(0.234375 + 7 * 2.0 ** -14)), got[0, 0]
+
+
+# ----------------------------------------------------- structure / edge cases
+
+def test_identity_and_permutation_exact():
+    say("identity / permutation")
+    a16 = wl.random_f16((200, 136), 1)
+    eye16 = np.eye(136, dtype=np.float16)
+    assert np.array_equal(run_f16(a16, eye16, g.OUT_F32), a16.astype(np.float32))
+    perm = np.random.default_rng(3).permutation(200)
+    P = np.eye(200, dtype=np.float16)[perm]
+    assert np.array_equal(run_f16(P, a16, g.OUT_F16), a16[perm])
+    ca = wl.random_e4m3_codes((200, 256), 2)
+    eye8 = np.where(np.eye(256, dtype=bool), np.uint8(0x38), np.uint8(0))
+    one = scalar(1.0)
+    assert np.array_equal(run_fp8(dev(ca), dev(eye8), one, one, g.OUT_F32), orc.e4m3_decode(ca).astype(np.float32))
+    P8 = np.where(np.eye(200, dtype=bool)[perm], np.uint8(0x38), np.uint8(0))
+    expect = ca[perm].copy()
+    expect[expect == 0x80] = 0x00       # a sum of +0 and -0 terms is +0
+    assert np.array_equal(run_fp8(dev(P8), dev(ca), one, one, g.OUT_E4M3, 1.0), expect)
+
+
+def test_all_ones_gives_K():
+    say("all ones")
+    for M, N, K in [(130, 70, 4096), (1, 300, 777)]:
+        assert np.all(run_f16(np.ones((M, K), np.float16), np.ones((K, N), np.float16), g.OUT_F32) == K)
+        (qa, sa, _, osa), (qb, sb, _, osb) = fp8_chain(np.ones((M, K), np.float32), np.ones((K, N), np.float32))
+        got = run_fp8(qa, qb, sa, sb, g.OUT_F32)
+        R = np.full((M, N), K * 448.0 * 448.0)
+        check_f32(got, R, R, osa, osb, what="all ones")
+        assert np.allclose(got, K, rtol=1e-5)
+
+
+@pytest.mark.parametrize("kind,M,N,K", [("f16", 129, 520, 300), ("f16", 3, 1000, 512), ("fp8", 65, 1000, 640),
+                                        ("fp8", 1, 700, 256)])
+def test_guard_bands_and_poison(kind, M, N, K):
+    """Outputs surrounded by guard bands and pre-filled with NaN: every output
+    is written, nothing outside is."""
+    say(f"guard/poison {kind} {M}x{N}x{K}")
+    G = 4096
+    buf = torch.full((M * N + 2 * G,), float("nan"), dtype=torch.float32, device=DEV)
+    C = buf[G:G + M * N].view(M, N)
+    if kind == "f16":
+        a16, b16 = wl.random_f16((M, K), 1), wl.random_f16((K, N), 2)
+        g.gemm_f16(dev(a16), dev(b16), C)
+        R, S = orc.gemm(orc.FMT_F16, a16.view(np.uint16), b16.view(np.uint16))
+        sc = 1.0
+    else:
+        ca, cb = wl.random_e4m3_codes((M, K), 3), wl.random_e4m3_codes((K, N), 4)
+        g.gemm_fp8_scaled(dev(ca), dev(cb), scalar(0.5), scalar(0.25), C)
+        R, S = orc.gemm(orc.FMT_E4M3, ca, cb)
+        sc = 0.125
+    b = host(buf)
+    assert np.all(np.isnan(b[:G])) and np.all(np.isnan(b[G + M * N:])), "guard band written"
+    T = fp8_dot_allowance(ca, cb) if kind == "fp8" and M > 16 else None
+    check_f32(b[G:G + M * N].reshape(M, N), R, S, sc, 1.0, T=T)
+
+
+@pytest.mark.parametrize("M", [1, 16, 200, 4096])
+def test_bitwise_deterministic(M):
+    say(f"determinism M={M}")
+    a16, b16 = wl.random_f16((M, 1024), 5), wl.random_f16((1024, 2048), 6)
+    ta, tb = dev(a16), dev(b16)
+    outs = []
+    for _ in range(3):
+        C = torch.empty((M, 2048), dtype=torch.float32, device=DEV)
+        g.gemm_f16(ta, tb, C)
+        outs.append(host(C))
+    assert all(np.array_equal(outs[0].view(np.uint32), o.view(np.uint32)) for o in outs[1:])
+
+
+def test_k0_and_empty_shapes():
+    say("K=0, M=0, N=0")
+    for out, dt in [(g.OUT_F32, torch.float32), (g.OUT_F16, torch.float16)]:
+        C = torch.full((5, 7), 3.0, dtype=dt, device=DEV)
+        g.gemm_f16(torch.empty((5, 0), dtype=torch.float16, device=DEV),
+                   torch.empty((0, 7), dtype=torch.float16, device=DEV), C)
+        assert np.all(host(C) == 0)
+    C = torch.full((5, 7), 9, dtype=torch.uint8, device=DEV)
+    g.gemm_fp8_scaled(torch.empty((5, 0), dtype=torch.uint8, device=DEV), torch.empty((0, 7), dtype=torch.uint8, device=DEV),
+                      scalar(1), scalar(1), C, scalar(1))
+    assert np.all(host(C) == 0)
+    C = torch.full((0, 7), 3.0, dtype=torch.float32, device=DEV)
+    g.gemm_f16(torch.empty((0, 4), dtype=torch.float16, device=DEV), torch.ones((4, 7), dtype=torch.float16, device=DEV), C)
+    C = torch.full((3, 4), 3.0, dtype=torch.float32, device=DEV)
+    g.gemm_f16(torch.ones((3, 4), dtype=torch.float16, device=DEV), torch.ones((4, 4), dtype=torch.float16, device=DEV)[:, :0].contiguous(),
+               C[:, :0].contiguous())
+    assert np.all(host(C) == 3.0)
+
+
+def test_f16_output_overflow_and_e4m3_saturation():
+    say("overflow / saturation")
+    ca = np.full((20, 256), 0x7E, np.uint8)      # 448
+    cb = np.full((256, 30), 0x7E, np.uint8)
+    cb[:, 1] = 0xFE                               # -448
+    R, S = orc.gemm(orc.FMT_E4M3, ca, cb)
+    got = run_fp8(dev(ca), dev(cb), scalar(1.0), scalar(1.0), g.OUT_F16)   # 256 * 448^2 > 65504
+    assert np.all(np.isposinf(got[:, 0])) and np.all(np.isneginf(got[:, 1]))
+    check_f16(got, R, S)
+    codes = run_fp8(dev(ca), dev(cb), scalar(1.0), scalar(1.0), g.OUT_E4M3, 1.0)
+    assert np.all(codes[:, 0] == 0x7E) and np.all(codes[:, 1] == 0xFE)
+
+
+def test_nondefault_stream():
+    say("non-default stream")
+    a16, b16 = wl.random_f16((300, 512), 8), wl.random_f16((512, 260), 9)
+    ta, tb = dev(a16), dev(b16)
+    s = torch.cuda.Stream()
+    C = torch.empty((300, 260), dtype=torch.float32, device=DEV)
+    torch.cuda.synchronize()
+    with torch.cuda.stream(s):
+        g.gemm_f16(ta, tb, C, stream=s)
+    s.synchronize()
+    R, S = orc.gemm(orc.FMT_F16, a16.view(np.uint16), b16.view(np.uint16))
+    check_f32(C.cpu().numpy(), R, S)
+
+
+def test_error_status_on_gpu():
+    say("error statuses")
+    A = torch.ones((4, 4), dtype=torch.float16, device=DEV)
+    with pytest.raises(g.GemmError) as e:
+        g.lib()
+        g._check(g.lib().gemm_f16(A.data_ptr(), None, A.data_ptr(), 0, 4, 4, 4, None), "x")
+    assert e.value.status == -1
