@@ -41,7 +41,28 @@ def parse():
     p.add_argument("--no-cpu-baseline", action="store_true")
     p.add_argument("--cpu-seconds", type=float, default=15.0, help="target oracle sample time")
     p.add_argument("--rows-reps", type=int, default=200, help="launches per single-row timing")
+    p.add_argument("--calib-copy", action="store_true",
+                   help="run one 256 MiB device-to-device copy first (a known-size kernel that calibrates "
+                        "HBM byte counters in a profiler run)")
     return p.parse_args()
+
+
+def traffic_record(config):
+    """HBM bytes per launch of `config` from the committed counter summary, or
+    None when the kernel source has changed since the counters were taken."""
+    import hashlib
+    path = os.path.join(ROOT, "profiles", "hbm_traffic.json")
+    if not os.path.exists(path):
+        return None
+    rec = json.load(open(path)).get(config)
+    if not rec:
+        return None
+    h = hashlib.sha256()
+    for f in rec["sources"]:
+        h.update(open(os.path.join(ROOT, f), "rb").read())
+    if h.hexdigest() != rec["source_sha256"]:
+        return None
+    return rec
 
 
 def time_launches(torch, fn, reps, warm=10):
@@ -126,6 +147,13 @@ def main():
 
     def to(x):
         return torch.from_numpy(np.ascontiguousarray(x)).to(dev)
+
+    if args.calib_copy:
+        src = torch.ones(64 << 20, dtype=torch.float32, device=dev)
+        dst = torch.empty_like(src)
+        dst.copy_(src)
+        torch.cuda.synchronize()
+        del src, dst
 
     w8, w16, wd = wl.C4[-1], wl.M0, wl.C3[0]
     log(f"inputs: {w8.name}, {w16.name}, {wd.name}")
@@ -218,9 +246,12 @@ def main():
                       "config": g.select_config(g.KIND_F16, g.OUT_F16, wd.M, wd.N, wd.K)},
     }
     achieved = flops8 / ms_gemm8 / 1e9
+    rec = traffic_record(rows["fp8_gemm_4096"]["config"])
     roofline = {"bound": "mfma", "kernel": "FP8 GEMM 4096^3 (" + rows["fp8_gemm_4096"]["config"] + ")",
                 "achieved": achieved, "peak": PEAK_FP8_TFLOPS, "unit": "TFLOP/s", "frac": achieved / PEAK_FP8_TFLOPS,
-                "traffic": None}
+                "traffic": None if rec is None else rec["hbm_bytes"],
+                "traffic_unit": "bytes per launch (FETCH_SIZE x2.0 + WRITE_SIZE x1.0, calibrated on a copy kernel)",
+                "algorithmic_bytes": float(w8.M * w8.K + w8.K * w8.N + w8.M * w8.N)}
 
     cpu = None
     if not args.no_cpu_baseline:

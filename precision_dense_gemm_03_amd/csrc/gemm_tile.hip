@@ -7,8 +7,9 @@
 //
 // Data flow per workgroup (one BM x BN output tile, 4 waves in a 2 x 2 grid):
 //   HBM/L2 --16-byte coalesced loads--> registers --ds_write_b128--> LDS
-//   (two LDS stages: the next K tile is fetched while the current one is
-//   consumed; FP8 guide §2.3 "double buffering", HGEMM §3.2/§3.3)
+//   (two LDS stages plus one register stage: tile k+2 is in flight while
+//   tile k is multiplied; FP8 guide §2.3 "double buffering", HGEMM §3.2/§3.3
+//   on prefetch depth)
 //   LDS --ds_read_b128 (A) / ds_read_b64_tr_b16|b8 (B)--> MFMA operands
 // A is row-major [M,K]: its K-contiguous rows are exactly the MFMA A operand.
 // B is row-major [K,N]: N is contiguous, so the B operand (8 or 32 consecutive
@@ -257,15 +258,21 @@ __global__ __launch_bounds__(64 * WM * WN) void gemm_tile_kernel(
         }
     };
 
+    // Pipeline: iteration kt first writes tile kt+1 (fetched into registers
+    // one iteration earlier, so its loads have had a whole iteration to land)
+    // to the stage that iteration kt-1 finished reading, issues the fetch of
+    // tile kt+2, and then multiplies tile kt out of the other stage. One
+    // barrier per iteration separates the readers of a stage from its next
+    // writers.
     if (nk > 0) {
         load_tile(0);
         store_tile(0);
+        if (nk > 1) load_tile(1);
         __syncthreads();
         for (int kt = 0; kt < nk; ++kt) {
-            const bool more = kt + 1 < nk;
-            if (more) load_tile(kt + 1);
+            if (kt + 1 < nk) store_tile((kt + 1) & 1);
+            if (kt + 2 < nk) load_tile(kt + 2);
             compute(kt & 1);
-            if (more) store_tile((kt + 1) & 1);
             __syncthreads();
         }
     }
