@@ -38,6 +38,9 @@ namespace libgemm {
 namespace {
 
 constexpr int kXcds = 8;
+// The fully register-pipelined loop (two B operand sets) needs more registers
+// than a 256x256 tile leaves; it stays compiled out until it fits.
+constexpr bool kRegisterPipeline = false;
 constexpr int kGroupM = 4;
 
 template <int ES, int BM, int BN, int BK, int WM, int WN>
@@ -67,6 +70,53 @@ struct Tile {
     static_assert(BM % A_RPP == 0 && BK % B_RPP == 0, "tile chunks must divide evenly");
     static_assert(WTM % 16 == 0 && WTN % 16 == 0, "wave tile must be whole 16x16 blocks");
     static_assert(2 * STAGE <= 160 * 1024, "two stages must fit in LDS");
+    // LDS map: A stage 0, A stage 1, B stage 0, B stage 1
+    static constexpr int a_stage(int s) { return s * A_BYTES; }
+    static constexpr int b_stage(int s) { return 2 * A_BYTES + s * B_BYTES; }
+};
+
+// MFMA operand type, LDS operand reads and the multiply for each element size.
+template <int ES>
+struct Operand;
+
+template <>
+struct Operand<2> {  // FP16: v_mfma_f32_16x16x32_f16, 8 halves per lane
+    typedef v8h type;
+    static __device__ __forceinline__ v8h read_a(const LDS_AS uint8_t* p) {
+        return __builtin_bit_cast(v8h, *(const LDS_AS v4u*)p);
+    }
+    // two transpose reads give k = 8g + 0..3 and 8g + 4..7 of one column
+    static __device__ __forceinline__ v8h read_b(const LDS_AS uint8_t* p, int sb) {
+        const v4s lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((LDS_AS v4s*)p);
+        const v4s hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((LDS_AS v4s*)(p + 4 * sb));
+        return __builtin_bit_cast(v8h, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
+    }
+    static __device__ __forceinline__ v4f mma(v8h a, v8h b, v4f c) {
+        return __builtin_amdgcn_mfma_f32_16x16x32_f16(a, b, c, 0, 0, 0);
+    }
+};
+
+template <>
+struct Operand<1> {  // E4M3: v_mfma_scale_f32_16x16x128_f8f6f4 (neutral scales), 32 codes per lane
+    typedef v8i type;
+    static __device__ __forceinline__ v8i read_a(const LDS_AS uint8_t* p) {
+        const v4i lo = *(const LDS_AS v4i*)p;
+        const v4i hi = *(const LDS_AS v4i*)(p + 16);
+        return __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
+    }
+    // four transpose reads give k = 32g + 0..7, 8..15, 16..23, 24..31 of one column
+    static __device__ __forceinline__ v8i read_b(const LDS_AS uint8_t* p, int sb) {
+        const v2i t0 = __builtin_amdgcn_ds_read_tr8_b64_v2i32((LDS_AS v2i*)p);
+        const v2i t1 = __builtin_amdgcn_ds_read_tr8_b64_v2i32((LDS_AS v2i*)(p + 8 * sb));
+        const v2i t2 = __builtin_amdgcn_ds_read_tr8_b64_v2i32((LDS_AS v2i*)(p + 16 * sb));
+        const v2i t3 = __builtin_amdgcn_ds_read_tr8_b64_v2i32((LDS_AS v2i*)(p + 24 * sb));
+        const v4i t01 = __builtin_shufflevector(t0, t1, 0, 1, 2, 3);
+        const v4i t23 = __builtin_shufflevector(t2, t3, 0, 1, 2, 3);
+        return __builtin_shufflevector(t01, t23, 0, 1, 2, 3, 4, 5, 6, 7);
+    }
+    static __device__ __forceinline__ v4f mma(v8i a, v8i b, v4f c) {
+        return __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(a, b, c, 0, 0, 0, 127, 0, 127);
+    }
 };
 
 // One 16-byte chunk of `ES`-byte elements starting at element `col` of a row,
@@ -137,10 +187,6 @@ __global__ __launch_bounds__(64 * WM * WN) void gemm_tile_kernel(
     // This thread's chunk coordinates inside a staged tile.
     const int a_row = tid / T::A_CPR, a_col = tid % T::A_CPR;  // + i * A_RPP rows
     const int b_row = tid / T::B_CPR, b_col = tid % T::B_CPR;  // + i * B_RPP rows
-    const uint8_t* a_base = A + ((int64_t)(m0 + a_row) * K + a_col * T::VE) * ES;
-    const uint8_t* b_base = B + ((int64_t)b_row * N + n0 + b_col * T::VE) * ES;
-    const int64_t a_step = (int64_t)T::A_RPP * K * ES;  // bytes between this thread's A chunks
-    const int64_t b_step = (int64_t)T::B_RPP * N * ES;
 
     v4u ra[T::CA];
     v4u rb[T::CB];
@@ -158,121 +204,191 @@ __global__ __launch_bounds__(64 * WM * WN) void gemm_tile_kernel(
     // (16/E)*e + i/E, E = elements per 64 bits).
     const int b_row_in = (ES == 2) ? (j16 >> 2) : (j16 >> 1);
     const int b_col_in = (ES == 2) ? 4 * (j16 & 3) : 8 * (j16 & 1);
-    const int a_lds = (wm * T::WTM + j16) * T::SA + g * T::OPB;                    // + tm*16*SA + ks*KPI*ES
-    const int b_lds = T::A_BYTES + (8 * (ES == 2 ? 1 : 4) * g + b_row_in) * T::SB  // + ks*KPI*SB + ...
+    const int a_lds = (wm * T::WTM + j16) * T::SA + g * T::OPB;          // + stage + tm*16*SA + ks*KPI*ES
+    const int b_lds = (8 * (ES == 2 ? 1 : 4) * g + b_row_in) * T::SB     // + stage + ks*KPI*SB + tn*16*ES
                       + (wn * T::WTN + b_col_in) * ES;
 
     const int nk = (K + BK - 1) / BK;
+    typedef typename Operand<ES>::type Op;
 
-    auto load_tile = [&](int kt) __attribute__((always_inline)) {
-        const int k0 = kt * BK;
-        if (interior_mn && k0 + BK <= K) {
-            const uint8_t* pa = a_base + (int64_t)k0 * ES;
-            const uint8_t* pb = b_base + (int64_t)k0 * N * ES;
+    // ---- global <-> registers <-> LDS (A and B have separate stages) ----
+    // Fast-path loads: a wave-uniform base (kept in SGPRs) plus a 32-bit
+    // per-lane offset, so the 16 loads of a tile need no 64-bit VGPR addresses.
+    // Valid while one tile row block spans less than 2^31 bytes (checked below).
+    const uint8_t* a_tile = A + (int64_t)m0 * K * ES;
+    const uint8_t* b_tile = B + (int64_t)n0 * ES;
+    // Edge tiles (aligned operands) use the same unguarded loads with the
+    // addresses clamped into the matrix: A rows past M re-read row M-1 and B
+    // column chunks past N re-read the last chunk. Those values only reach
+    // output rows/columns that are never stored, and every address is valid.
+    uint32_t a_offs[T::CA], b_offs[T::CB];
 #pragma unroll
-            for (int i = 0; i < T::CA; ++i) ra[i] = *reinterpret_cast<const v4u*>(pa + i * a_step);
+    for (int i = 0; i < T::CA; ++i) {
+        const int r = min(m0 + a_row + i * T::A_RPP, M - 1) - m0;
+        a_offs[i] = (uint32_t)((r * K + a_col * T::VE) * ES);
+    }
 #pragma unroll
-            for (int i = 0; i < T::CB; ++i) rb[i] = *reinterpret_cast<const v4u*>(pb + i * b_step);
-        } else {
+    for (int i = 0; i < T::CB; ++i) {
+        const int c = min(n0 + b_col * T::VE, N - T::VE) - n0;
+        b_offs[i] = (uint32_t)(((b_row + i * T::B_RPP) * N + c) * ES);
+    }
+    auto load_a = [&](int kt) __attribute__((always_inline)) {
+        const uint8_t* pa = a_tile + (int64_t)kt * BK * ES;
 #pragma unroll
-            for (int i = 0; i < T::CA; ++i) {
-                const int gm = m0 + a_row + i * T::A_RPP;
-                const int64_t gk = (int64_t)k0 + a_col * T::VE;
-                const uint8_t* rp = A + (int64_t)gm * K * ES;
-                if (aligned && gm < M && gk + T::VE <= K)
-                    ra[i] = *reinterpret_cast<const v4u*>(rp + gk * ES);
-                else
-                    ra[i] = load_chunk_guarded<ES>(rp, gm < M, gk, K);
-            }
-#pragma unroll
-            for (int i = 0; i < T::CB; ++i) {
-                const int gk = k0 + b_row + i * T::B_RPP;
-                const int64_t gn = (int64_t)n0 + b_col * T::VE;
-                const uint8_t* rp = B + (int64_t)gk * N * ES;
-                if (aligned && gk < K && gn + T::VE <= N)
-                    rb[i] = *reinterpret_cast<const v4u*>(rp + gn * ES);
-                else
-                    rb[i] = load_chunk_guarded<ES>(rp, gk < K, gn, N);
-            }
-        }
+        for (int i = 0; i < T::CA; ++i) ra[i] = *reinterpret_cast<const v4u*>(pa + a_offs[i]);
     };
-
-    auto store_tile = [&](int buf) __attribute__((always_inline)) {
-        LDS_AS uint8_t* As = smem + buf * T::STAGE;
+    auto load_b = [&](int kt) __attribute__((always_inline)) {
+        const uint8_t* pb = b_tile + (int64_t)kt * BK * N * ES;
+#pragma unroll
+        for (int i = 0; i < T::CB; ++i) rb[i] = *reinterpret_cast<const v4u*>(pb + b_offs[i]);
+    };
+    auto store_a = [&](int stage) __attribute__((always_inline)) {
+        LDS_AS uint8_t* As = smem + T::a_stage(stage);
 #pragma unroll
         for (int i = 0; i < T::CA; ++i)
             *(LDS_AS v4u*)(As + (a_row + i * T::A_RPP) * T::SA + a_col * 16) = ra[i];
+    };
+    auto store_b = [&](int stage) __attribute__((always_inline)) {
+        LDS_AS uint8_t* Bs = smem + T::b_stage(stage);
 #pragma unroll
         for (int i = 0; i < T::CB; ++i)
-            *(LDS_AS v4u*)(As + T::A_BYTES + (b_row + i * T::B_RPP) * T::SB + b_col * 16) = rb[i];
+            *(LDS_AS v4u*)(Bs + (b_row + i * T::B_RPP) * T::SB + b_col * 16) = rb[i];
     };
-
-    auto compute = [&](int buf) __attribute__((always_inline)) {
-        const LDS_AS uint8_t* base = smem + buf * T::STAGE;
-#pragma unroll
-        for (int ks = 0; ks < T::KS; ++ks) {
-            if constexpr (ES == 2) {
-                v8h bop[T::TN];
-#pragma unroll
-                for (int tn = 0; tn < T::TN; ++tn) {
-                    // two transpose reads give k = 8g + 0..3 and 8g + 4..7 of column n
-                    const LDS_AS uint8_t* p = base + b_lds + ks * T::KPI * T::SB + tn * 16 * ES;
-                    const v4s lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((LDS_AS v4s*)p);
-                    const v4s hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((LDS_AS v4s*)(p + 4 * T::SB));
-                    bop[tn] = __builtin_bit_cast(v8h, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
-                }
-#pragma unroll
-                for (int tm = 0; tm < T::TM; ++tm) {
-                    const v4u a = *(const LDS_AS v4u*)(base + a_lds + tm * 16 * T::SA + ks * T::KPI * ES);
-                    const v8h aop = __builtin_bit_cast(v8h, a);
-#pragma unroll
-                    for (int tn = 0; tn < T::TN; ++tn)
-                        acc[tm][tn] = __builtin_amdgcn_mfma_f32_16x16x32_f16(aop, bop[tn], acc[tm][tn], 0, 0, 0);
-                }
-            } else {
-                v8i bop[T::TN];
-#pragma unroll
-                for (int tn = 0; tn < T::TN; ++tn) {
-                    // four transpose reads give k = 32g + 0..7, 8..15, 16..23, 24..31 of column n
-                    const LDS_AS uint8_t* p = base + b_lds + ks * T::KPI * T::SB + tn * 16;
-                    const v2i t0 = __builtin_amdgcn_ds_read_tr8_b64_v2i32((LDS_AS v2i*)p);
-                    const v2i t1 = __builtin_amdgcn_ds_read_tr8_b64_v2i32((LDS_AS v2i*)(p + 8 * T::SB));
-                    const v2i t2 = __builtin_amdgcn_ds_read_tr8_b64_v2i32((LDS_AS v2i*)(p + 16 * T::SB));
-                    const v2i t3 = __builtin_amdgcn_ds_read_tr8_b64_v2i32((LDS_AS v2i*)(p + 24 * T::SB));
-                    const v4i t01 = __builtin_shufflevector(t0, t1, 0, 1, 2, 3);
-                    const v4i t23 = __builtin_shufflevector(t2, t3, 0, 1, 2, 3);
-                    bop[tn] = __builtin_shufflevector(t01, t23, 0, 1, 2, 3, 4, 5, 6, 7);
-                }
-#pragma unroll
-                for (int tm = 0; tm < T::TM; ++tm) {
-                    const LDS_AS uint8_t* ap = base + a_lds + tm * 16 * T::SA + ks * T::KPI;
-                    const v4i lo = *(const LDS_AS v4i*)ap;
-                    const v4i hi = *(const LDS_AS v4i*)(ap + 16);
-                    const v8i aop = __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
-#pragma unroll
-                    for (int tn = 0; tn < T::TN; ++tn)
-                        acc[tm][tn] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(aop, bop[tn], acc[tm][tn],
-                                                                                      0, 0, 0, 127, 0, 127);
-                }
-            }
+    // Edge tiles, the K tail and unaligned operands: each 16-byte chunk is
+    // loaded with per-element guards and written straight to LDS (no register
+    // staging, and a rolled loop, so this path costs almost no registers).
+    auto guarded_to_lds = [&](int kt, int stage) __attribute__((always_inline)) {
+        const int k0 = kt * BK;
+        LDS_AS uint8_t* As = smem + T::a_stage(stage);
+        LDS_AS uint8_t* Bs = smem + T::b_stage(stage);
+#pragma unroll 1
+        for (int i = 0; i < T::CA; ++i) {
+            const int gm = m0 + a_row + i * T::A_RPP;
+            const int64_t gk = (int64_t)k0 + a_col * T::VE;
+            const uint8_t* rp = A + (int64_t)gm * K * ES;
+            v4u v;
+            if (aligned && gm < M && gk + T::VE <= K)
+                v = *reinterpret_cast<const v4u*>(rp + gk * ES);
+            else
+                v = load_chunk_guarded<ES>(rp, gm < M, gk, K);
+            *(LDS_AS v4u*)(As + (a_row + i * T::A_RPP) * T::SA + a_col * 16) = v;
+        }
+#pragma unroll 1
+        for (int i = 0; i < T::CB; ++i) {
+            const int gk = k0 + b_row + i * T::B_RPP;
+            const int64_t gn = (int64_t)n0 + b_col * T::VE;
+            const uint8_t* rp = B + (int64_t)gk * N * ES;
+            v4u v;
+            if (aligned && gk < K && gn + T::VE <= N)
+                v = *reinterpret_cast<const v4u*>(rp + gn * ES);
+            else
+                v = load_chunk_guarded<ES>(rp, gk < K, gn, N);
+            *(LDS_AS v4u*)(Bs + (b_row + i * T::B_RPP) * T::SB + b_col * 16) = v;
         }
     };
 
-    // Pipeline: iteration kt first writes tile kt+1 (fetched into registers
-    // one iteration earlier, so its loads have had a whole iteration to land)
-    // to the stage that iteration kt-1 finished reading, issues the fetch of
-    // tile kt+2, and then multiplies tile kt out of the other stage. One
-    // barrier per iteration separates the readers of a stage from its next
-    // writers.
-    if (nk > 0) {
-        load_tile(0);
-        store_tile(0);
-        if (nk > 1) load_tile(1);
+    // ---- LDS -> MFMA operands ----
+    auto read_b = [&](int stage, Op (&bop)[T::KS][T::TN]) __attribute__((always_inline)) {
+        const LDS_AS uint8_t* base = smem + T::b_stage(stage) + b_lds;
+#pragma unroll
+        for (int ks = 0; ks < T::KS; ++ks)
+#pragma unroll
+            for (int tn = 0; tn < T::TN; ++tn)
+                bop[ks][tn] = Operand<ES>::read_b(base + ks * T::KPI * T::SB + tn * 16 * ES, T::SB);
+    };
+    auto mma_tile = [&](int stage, const Op (&bop)[T::KS][T::TN]) __attribute__((always_inline)) {
+        const LDS_AS uint8_t* base = smem + T::a_stage(stage) + a_lds;
+#pragma unroll
+        for (int ks = 0; ks < T::KS; ++ks)
+#pragma unroll
+            for (int tm = 0; tm < T::TM; ++tm) {
+                const Op aop = Operand<ES>::read_a(base + tm * 16 * T::SA + ks * T::KPI * ES);
+#pragma unroll
+                for (int tn = 0; tn < T::TN; ++tn) acc[tm][tn] = Operand<ES>::mma(aop, bop[ks][tn], acc[tm][tn]);
+                // With two waves per SIMD the other wave hides the A read
+                // latency. Pinning this row block's products here (an empty
+                // asm that reads and rewrites its accumulators, after which no
+                // LDS read may be hoisted) keeps one A operand live at a time
+                // instead of letting the compiler sink every MFMA to the loop
+                // end and hold all A operands.
+                if constexpr (T::NT > 256) {
+#pragma unroll
+                    for (int tn = 0; tn < T::TN; ++tn) asm volatile("" : "+v"(acc[tm][tn])::"memory");
+                }
+            }
+    };
+
+    const bool offsets_fit = (int64_t)BM * K * ES < (1ll << 31) && (int64_t)BK * N * ES < (1ll << 31);
+    if (kRegisterPipeline && interior_mn && K % BK == 0 && nk > 0 && offsets_fit) {
+        // Software pipeline, one barrier per K tile. Entering iteration kt:
+        // LDS holds A(kt) in A stage kt%2 and B(kt+1) in B stage (kt+1)%2,
+        // registers hold the B operands of tile kt (bcur) and the global data
+        // of A(kt+1) and B(kt+2). The iteration stores that data to the stages
+        // iteration kt-1 finished reading, issues the loads of A(kt+2) and
+        // B(kt+3), multiplies tile kt and reads the B operands of tile kt+1
+        // into the other register set, so LDS traffic runs under the MFMAs.
+        // Tiles past the end are clamped to the last one (loaded, never used).
+        Op b0[T::KS][T::TN], b1[T::KS][T::TN];
+        const int last = nk - 1;
+        load_a(0);
+        load_b(0);
+        store_a(0);
+        store_b(0);
+        load_b(min(1, last));
+        store_b(1);
+        load_a(min(1, last));
+        load_b(min(2, last));
+        __syncthreads();
+        read_b(0, b0);
+        __syncthreads();
+        auto iteration = [&](int kt, Op (&bcur)[T::KS][T::TN], Op (&bnext)[T::KS][T::TN])
+                             __attribute__((always_inline)) {
+            store_a((kt + 1) & 1);
+            store_b(kt & 1);
+            load_a(min(kt + 2, last));
+            load_b(min(kt + 3, last));
+            mma_tile(kt & 1, bcur);
+            read_b((kt + 1) & 1, bnext);
+            __syncthreads();
+        };
+        int kt = 0;
+        for (; kt + 1 < nk; kt += 2) {
+            iteration(kt, b0, b1);
+            iteration(kt + 1, b1, b0);
+        }
+        if (kt < nk) iteration(kt, b0, b1);
+    } else if (nk > 0) {
+        Op bop[T::KS][T::TN];
+        // Tile kt+1 is fetched into registers while tile kt is multiplied;
+        // the K tail and unaligned operands load each chunk with element
+        // guards straight into LDS.
+        auto fast = [&](int kt) __attribute__((always_inline)) {
+            return aligned && offsets_fit && (kt + 1) * BK <= K;
+        };
+        if (fast(0)) {
+            load_a(0);
+            load_b(0);
+            store_a(0);
+            store_b(0);
+        } else {
+            guarded_to_lds(0, 0);
+        }
         __syncthreads();
         for (int kt = 0; kt < nk; ++kt) {
-            if (kt + 1 < nk) store_tile((kt + 1) & 1);
-            if (kt + 2 < nk) load_tile(kt + 2);
-            compute(kt & 1);
+            const bool more = kt + 1 < nk;
+            const bool fast_next = more && fast(kt + 1);
+            if (fast_next) {
+                load_a(kt + 1);
+                load_b(kt + 1);
+            }
+            read_b(kt & 1, bop);
+            mma_tile(kt & 1, bop);
+            if (fast_next) {
+                store_a((kt + 1) & 1);
+                store_b((kt + 1) & 1);
+            } else if (more) {
+                guarded_to_lds(kt + 1, (kt + 1) & 1);
+            }
             __syncthreads();
         }
     }
@@ -351,6 +467,10 @@ const GemmConfig* tile_configs(int* count) {
         {"tile_fp8_64x64x128_w2x2", KIND_FP8, 0, 64, 64, 128, launch_tile<1, 64, 64, 128, 2, 2>},
         {"tile_fp8_128x128x128_w2x2", KIND_FP8, 0, 128, 128, 128, launch_tile<1, 128, 128, 128, 2, 2>},
         {"tile_fp8_256x256x128_w2x2", KIND_FP8, 0, 256, 256, 128, launch_tile<1, 256, 256, 128, 2, 2>},
+        {"tile_fp8_256x256x128_w2x4", KIND_FP8, 0, 256, 256, 128, launch_tile<1, 256, 256, 128, 2, 4>},
+        {"tile_fp8_256x256x128_w4x2", KIND_FP8, 0, 256, 256, 128, launch_tile<1, 256, 256, 128, 4, 2>},
+        {"tile_f16_256x256x64_w2x4", KIND_F16, 0, 256, 256, 64, launch_tile<2, 256, 256, 64, 2, 4>},
+        {"tile_f16_256x256x64_w4x2", KIND_F16, 0, 256, 256, 64, launch_tile<2, 256, 256, 64, 4, 2>},
     };
     *count = (int)(sizeof(table) / sizeof(table[0]));
     return table;

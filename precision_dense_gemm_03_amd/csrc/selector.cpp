@@ -36,11 +36,15 @@ const GemmConfig* find_named(const char* name, int kind, int64_t M) {
     return nullptr;
 }
 
+// The preferred configuration of each tile size: 256x256 tiles run 8 waves
+// (two per SIMD, wave tile 128x64), smaller tiles 4 waves.
 const GemmConfig* tile_with(int kind, int bm) {
+    const char* want = nullptr;
+    if (bm == 256) want = (kind == KIND_FP8) ? "tile_fp8_256x256x128_w2x4" : "tile_f16_256x256x64_w2x4";
     int nt = 0;
     const GemmConfig* tt = tile_configs(&nt);
     for (int i = 0; i < nt; ++i)
-        if (tt[i].kind == kind && tt[i].bm == bm) return &tt[i];
+        if (tt[i].kind == kind && tt[i].bm == bm && (!want || std::strcmp(tt[i].name, want) == 0)) return &tt[i];
     return nullptr;
 }
 

@@ -124,8 +124,8 @@ def test_select_config_rules():
     assert sel(g.KIND_F16, g.OUT_F16, 5, 12288, 4096).startswith("stream_f16_m8_")
     assert sel(g.KIND_FP8, g.OUT_E4M3, 1, 4096, 4096).startswith("stream_fp8_m1_")
     # 4096^2 fills the chip with 256x256 tiles (256 tiles)
-    assert sel(g.KIND_FP8, g.OUT_E4M3, 4096, 4096, 4096).startswith("tile_fp8_256x256")
-    assert sel(g.KIND_F16, g.OUT_F16, 4096, 4096, 4096).startswith("tile_f16_256x256")
+    assert sel(g.KIND_FP8, g.OUT_E4M3, 4096, 4096, 4096) == "tile_fp8_256x256x128_w2x4"
+    assert sel(g.KIND_F16, g.OUT_F16, 4096, 4096, 4096) == "tile_f16_256x256x64_w2x4"
     # M = 3000 gives 192 tiles of 256 (not enough): one size down
     assert sel(g.KIND_FP8, g.OUT_E4M3, 3000, 4096, 4096).startswith("tile_fp8_128x128")
     # small problems take the smallest tile
