@@ -16,7 +16,7 @@ INCLUDE = os.path.join(ROOT, "include")
 BUILD = os.path.join(PKG, "_build")
 LIB = os.path.join(PKG, "libgemm.so")
 
-SOURCES = ["abi.cpp", "selector.cpp", "amax_quant.hip", "gemm_tile.hip", "gemm_stream.hip"]
+SOURCES = ["abi.cpp", "selector.cpp", "amax_quant.hip", "gemm_tile.hip", "gemm_dma.hip", "gemm_stream.hip"]
 
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 

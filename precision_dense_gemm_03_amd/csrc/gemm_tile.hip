@@ -32,16 +32,15 @@
 // stay in one L2), walked in groups of 4 tile rows.
 #include "device_common.h"
 #include "kernels.h"
+#include "tile_order.h"
 
 namespace libgemm {
 
 namespace {
 
-constexpr int kXcds = 8;
 // The fully register-pipelined loop (two B operand sets) needs more registers
 // than a 256x256 tile leaves; it stays compiled out until it fits.
 constexpr bool kRegisterPipeline = false;
-constexpr int kGroupM = 4;
 
 template <int ES, int BM, int BN, int BK, int WM, int WN>
 struct Tile {
@@ -147,21 +146,6 @@ __device__ __forceinline__ void store_one(void* C, int64_t idx, float y, float s
     } else {
         reinterpret_cast<uint8_t*>(C)[idx] = e4m3_from_f32(y / s_out);
     }
-}
-
-// Workgroup id -> (tile row, tile column), XCD-compact and grouped by kGroupM rows.
-__device__ __forceinline__ void tile_coords(int bid, int tiles_m, int tiles_n, int& tm, int& tn) {
-    const int total = tiles_m * tiles_n;
-    const int full = total - total % kXcds;
-    int id = bid;
-    if (bid < full) id = (bid % kXcds) * (full / kXcds) + bid / kXcds;  // XCD x owns ids [x*per, (x+1)*per)
-    const int group_span = kGroupM * tiles_n;
-    const int group = id / group_span;
-    const int first_m = group * kGroupM;
-    const int rows = min(tiles_m - first_m, kGroupM);
-    const int in_group = id - group * group_span;
-    tm = first_m + in_group % rows;
-    tn = in_group / rows;
 }
 
 template <int ES, int OUT, int BM, int BN, int BK, int WM, int WN>

@@ -27,7 +27,7 @@ typedef hipError_t (*GemmLauncher)(const GemmArgs&);
 struct GemmConfig {
     const char* name;   // e.g. "tile_fp8_256x256x128_w2x2"
     int kind;           // OperandKind
-    int family;         // 0 = MFMA tile kernel, 1 = M<=16 streaming kernel
+    int family;         // 0 = MFMA tile kernel, 1 = M<=16 streaming kernel, 2 = direct-load tile kernel
     int bm, bn, bk;     // tile (stream: bm = max M, bn = columns per block, bk = k-slices)
     GemmLauncher launch;
 };
@@ -35,6 +35,7 @@ struct GemmConfig {
 // Configuration tables, defined next to their kernels.
 const GemmConfig* tile_configs(int* count);
 const GemmConfig* stream_configs(int* count);
+const GemmConfig* dma_configs(int* count);
 
 // Shape -> configuration (host only, no HIP calls). Returns NULL if none fits.
 const GemmConfig* select_config(int kind, int out_dtype, int64_t M, int64_t N, int64_t K);

@@ -33,18 +33,29 @@ const GemmConfig* find_named(const char* name, int kind, int64_t M) {
         if (std::strcmp(st[i].name, name) == 0 && st[i].kind == kind && M <= st[i].bm) return &st[i];
     for (int i = 0; i < nt; ++i)
         if (std::strcmp(tt[i].name, name) == 0 && tt[i].kind == kind) return &tt[i];
+    int nd = 0;
+    const GemmConfig* dt = dma_configs(&nd);
+    for (int i = 0; i < nd; ++i)
+        if (std::strcmp(dt[i].name, name) == 0 && dt[i].kind == kind) return &dt[i];
     return nullptr;
 }
 
-// The preferred configuration of each tile size: 256x256 tiles run 8 waves
-// (two per SIMD, wave tile 128x64), smaller tiles 4 waves.
+// The preferred configuration of each tile size: 256x256 tiles use the
+// direct-load kernel (4 waves of 128x128, 4-stage LDS ring; it hands
+// unaligned operands to the register-staged kernel itself), smaller tiles the
+// register-staged kernel with 4 waves.
 const GemmConfig* tile_with(int kind, int bm) {
-    const char* want = nullptr;
-    if (bm == 256) want = (kind == KIND_FP8) ? "tile_fp8_256x256x128_w2x4" : "tile_f16_256x256x64_w2x4";
+    if (bm == 256) {
+        const char* want = (kind == KIND_FP8) ? "dma_fp8_256x256x64_s4" : "dma_f16_256x256x32_s4";
+        int nd = 0;
+        const GemmConfig* dt = dma_configs(&nd);
+        for (int i = 0; i < nd; ++i)
+            if (std::strcmp(dt[i].name, want) == 0) return &dt[i];
+    }
     int nt = 0;
     const GemmConfig* tt = tile_configs(&nt);
     for (int i = 0; i < nt; ++i)
-        if (tt[i].kind == kind && tt[i].bm == bm && (!want || std::strcmp(tt[i].name, want) == 0)) return &tt[i];
+        if (tt[i].kind == kind && tt[i].bm == bm) return &tt[i];
     return nullptr;
 }
 

@@ -1,0 +1,141 @@
+"""GPU parity per compiled kernel configuration.
+
+The selector sends small problems to small tiles, so the large-tile kernels
+would otherwise only meet sampled checks at full size. Here every tile
+configuration is forced by name (LIBGEMM_CONFIG) on ragged shapes -- M and N
+edges, a K tail, odd and even numbers of K tiles, operands that are not
+16-byte aligned (which the direct-load kernel hands to the register-staged
+kernel) -- and compared element by element with the oracle.
+"""
+import numpy as np
+import pytest
+import torch
+
+import oracle as orc
+import precision_dense_gemm_03_amd as g
+import workloads as wl
+from parity import check_e4m3, check_f16, check_f32, fp8_dot_allowance
+
+pytestmark = pytest.mark.gpu
+
+DEV = torch.device("cuda:0")
+
+
+def say(*a):
+    print(*a, flush=True)
+
+
+@pytest.fixture(scope="module", autouse=True)
+def _gpu():
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    torch.cuda.set_device(DEV)
+    g.lib()
+    yield
+    torch.cuda.synchronize()
+
+
+def dev(x):
+    return torch.from_numpy(np.ascontiguousarray(x)).to(DEV)
+
+
+def host(t):
+    torch.cuda.synchronize()
+    return t.cpu().numpy()
+
+
+def scalar(v):
+    return torch.tensor([float(np.float32(v))], dtype=torch.float32, device=DEV)
+
+
+FP8_CONFIGS = ["dma_fp8_256x256x64_s4", "dma_fp8_256x256x64_s5", "dma_fp8_256x256x64_s3", "tile_fp8_256x256x128_w2x4",
+               "tile_fp8_256x256x128_w4x2", "tile_fp8_256x256x128_w2x2", "tile_fp8_128x128x128_w2x2",
+               "tile_fp8_64x64x128_w2x2"]
+F16_CONFIGS = ["dma_f16_256x256x32_s4", "dma_f16_256x256x32_s5", "dma_f16_256x256x32_s3", "tile_f16_256x256x64_w2x4",
+               "tile_f16_256x256x64_w4x2", "tile_f16_256x256x64_w2x2", "tile_f16_128x128x64_w2x2",
+               "tile_f16_64x64x64_w2x2"]
+
+# (M, N, K): full tiles; M/N edges with a K tail; an odd number of K tiles;
+# a single partial K tile; K and N not multiples of 16 bytes (unaligned rows).
+FP8_SHAPES = [(256, 256, 256), (300, 272, 80), (513, 784, 192), (100, 32, 48), (257, 512, 1088), (130, 200, 100)]
+F16_SHAPES = [(256, 256, 256), (300, 272, 80), (513, 784, 200), (100, 32, 24), (257, 512, 544), (130, 204, 100)]
+
+
+@pytest.mark.parametrize("cfg", FP8_CONFIGS)
+def test_fp8_config_parity(cfg, monkeypatch):
+    monkeypatch.setenv("LIBGEMM_CONFIG", cfg)
+    sa, sb = np.float32(0.02), np.float32(0.003)
+    tsa, tsb = scalar(sa), scalar(sb)
+    for (M, N, K) in FP8_SHAPES:
+        assert g.select_config(g.KIND_FP8, g.OUT_F32, M, N, K) == cfg
+        say(f"{cfg} fp8 {M}x{N}x{K}")
+        ca = wl.random_e4m3_codes((M, K), 31 * M + K)
+        cb = wl.random_e4m3_codes((K, N), 37 * N + K)
+        R, S = orc.gemm(orc.FMT_E4M3, ca, cb)
+        T = fp8_dot_allowance(ca, cb)
+        ta, tb = dev(ca), dev(cb)
+        C = torch.empty((M, N), dtype=torch.float32, device=DEV)
+        g.gemm_fp8_scaled(ta, tb, tsa, tsb, C)
+        check_f32(host(C), R, S, sa, sb, what=f"{cfg} f32 {M}x{N}x{K}", T=T)
+        C = torch.empty((M, N), dtype=torch.float16, device=DEV)
+        g.gemm_fp8_scaled(ta, tb, tsa, tsb, C)
+        check_f16(host(C), R, S, sa, sb, what=f"{cfg} f16 {M}x{N}x{K}", T=T)
+        s_out = orc.scale_from_amax(np.float32(np.max(np.abs(R * float(sa) * float(sb)))))
+        C = torch.empty((M, N), dtype=torch.uint8, device=DEV)
+        g.gemm_fp8_scaled(ta, tb, tsa, tsb, C, scalar(s_out))
+        check_e4m3(host(C), R, S, sa, sb, s_out, what=f"{cfg} e4m3 {M}x{N}x{K}", T=T)
+
+
+@pytest.mark.parametrize("cfg", F16_CONFIGS)
+def test_f16_config_parity(cfg, monkeypatch):
+    monkeypatch.setenv("LIBGEMM_CONFIG", cfg)
+    for (M, N, K) in F16_SHAPES:
+        assert g.select_config(g.KIND_F16, g.OUT_F32, M, N, K) == cfg
+        say(f"{cfg} f16 {M}x{N}x{K}")
+        a16 = wl.random_f16((M, K), 41 * M + K)
+        b16 = wl.random_f16((K, N), 43 * N + K)
+        R, S = orc.gemm(orc.FMT_F16, a16.view(np.uint16), b16.view(np.uint16))
+        ta, tb = dev(a16), dev(b16)
+        C = torch.empty((M, N), dtype=torch.float32, device=DEV)
+        g.gemm_f16(ta, tb, C)
+        check_f32(host(C), R, S, what=f"{cfg} f32 {M}x{N}x{K}")
+        C = torch.empty((M, N), dtype=torch.float16, device=DEV)
+        g.gemm_f16(ta, tb, C)
+        check_f16(host(C), R, S, what=f"{cfg} f16 {M}x{N}x{K}")
+
+
+@pytest.mark.parametrize("kind", ["fp8", "f16"])
+def test_direct_load_kernel_offset_operands(kind, monkeypatch):
+    """Operands starting 16 bytes into an allocation (aligned) and 2 bytes in
+    (unaligned: handed to the register-staged kernel) give the oracle's result."""
+    cfg = "dma_fp8_256x256x64_s4" if kind == "fp8" else "dma_f16_256x256x32_s4"
+    monkeypatch.setenv("LIBGEMM_CONFIG", cfg)
+    M, N, K = 270, 288, 320
+    for shift in (16, 2):
+        say(f"{cfg} operands shifted by {shift} bytes")
+        if kind == "fp8":
+            ca = wl.random_e4m3_codes((M, K), 501)
+            cb = wl.random_e4m3_codes((K, N), 502)
+            ba = torch.zeros(M * K + shift, dtype=torch.uint8, device=DEV)
+            bb = torch.zeros(K * N + shift, dtype=torch.uint8, device=DEV)
+            ta = ba[shift:].view(M, K)
+            tb = bb[shift:].view(K, N)
+            ta.copy_(dev(ca))
+            tb.copy_(dev(cb))
+            R, S = orc.gemm(orc.FMT_E4M3, ca, cb)
+            C = torch.empty((M, N), dtype=torch.float32, device=DEV)
+            g.gemm_fp8_scaled(ta, tb, scalar(1.0), scalar(1.0), C)
+            check_f32(host(C), R, S, what=f"fp8 shift {shift}", T=fp8_dot_allowance(ca, cb))
+        else:
+            a16 = wl.random_f16((M, K), 503)
+            b16 = wl.random_f16((K, N), 504)
+            ba = torch.zeros(M * K + shift // 2, dtype=torch.float16, device=DEV)
+            bb = torch.zeros(K * N + shift // 2, dtype=torch.float16, device=DEV)
+            ta = ba[shift // 2:].view(M, K)
+            tb = bb[shift // 2:].view(K, N)
+            ta.copy_(dev(a16))
+            tb.copy_(dev(b16))
+            R, S = orc.gemm(orc.FMT_F16, a16.view(np.uint16), b16.view(np.uint16))
+            C = torch.empty((M, N), dtype=torch.float32, device=DEV)
+            g.gemm_f16(ta, tb, C)
+            check_f32(host(C), R, S, what=f"f16 shift {shift}")
