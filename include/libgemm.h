@@ -80,7 +80,9 @@ int gemm_f16(const void* A, const void* B, void* C, int out_dtype,
  *   C          device, float / _Float16 / uint8 per out_dtype, [M*N]
  *   out_dtype  GEMM_OUT_F32, GEMM_OUT_F16 or GEMM_OUT_E4M3
  * Element value: y = acc·(sA·sB) with acc the FP32 sum of decoded products;
- * F32 writes y, F16 writes RNE(y), E4M3 writes E4M3(y / sOut).
+ * F32 writes y, F16 writes RNE(y), E4M3 writes E4M3(y / sOut); the kernels
+ * form y / sOut as acc·(sA·sB/sOut), one FP32 factor, which may differ from
+ * the two-step quotient by a few FP32 ulps (within one E4M3 code step).
  */
 int gemm_fp8_scaled(const uint8_t* A, const uint8_t* B, const float* sA, const float* sB,
                     const float* sOut, void* C, int out_dtype,
@@ -107,6 +109,10 @@ int quantize_fp8(const float* x, int64_t n, const float* scale, uint8_t* q, hipS
  *   x      device, float[n]
  *   amax   device pointer to one float, written
  *   scale  device pointer to one float or NULL; written when non-NULL
+ * amax serves as the running maximum while the call's kernels run: both
+ * outputs are defined once that work has completed in stream order, and they
+ * must not overlap x or each other (GEMM_ERR_ALIAS). Up to three launches;
+ * no allocation.
  */
 int amax_f32(const float* x, int64_t n, float* amax, float* scale, hipStream_t stream);
 

@@ -9,6 +9,8 @@
 //
 // Both kernels are HBM-streaming: amax reads 4 B per element, quantize reads
 // 4 B and writes 1 B per element. Loads are 16 B per lane, fully coalesced.
+// amax is a one-thread clear of the result, the reduction, and (when a scale
+// is wanted) a one-thread launch that turns the maximum into the scale.
 #include "device_common.h"
 #include "kernels.h"
 
@@ -34,8 +36,16 @@ __device__ __forceinline__ uint32_t wave_max_u32(uint32_t v) {
 
 __global__ void amax_init_kernel(uint32_t* amax_bits) { *amax_bits = 0u; }
 
-// Each block reduces a grid-strided share of x to one value, then merges it
-// into *amax_bits with one atomic max (order-independent, hence deterministic).
+// Each block reduces a grid-strided share of x (every wave instruction reads
+// 1 KiB contiguous, kUnroll of them in flight per thread) to one value and
+// merges it into *amax_bits with an atomic max, skipped when the running
+// maximum is already at least as large (one shared word, so the atomics
+// serialize; 512 blocks keep that cost small). The maximum is
+// order-independent, hence deterministic. A last-block-finalizes scheme was
+// measured slower here than a separate one-thread launch: the device-scope
+// fence each block would need costs more than the extra launch.
+constexpr int kUnroll = 4;
+
 __global__ __launch_bounds__(kThreads) void amax_reduce_kernel(const float* __restrict__ x, int64_t n,
                                                                uint32_t* amax_bits, int vec) {
     uint32_t m = 0u;
@@ -43,21 +53,23 @@ __global__ __launch_bounds__(kThreads) void amax_reduce_kernel(const float* __re
     const int64_t nthreads = (int64_t)gridDim.x * kThreads;
     int64_t done = 0;
     if (vec) {
-        // 16 floats per thread per iteration: four 16-byte loads in flight.
         const v4u* x4 = reinterpret_cast<const v4u*>(x);
-        const int64_t n16 = n / 16;
-        for (int64_t i = tid; i < n16; i += nthreads) {
-            v4u v[4];
+        const int64_t n4 = n / 4;
+        int64_t i = tid;
+        for (; i + (kUnroll - 1) * nthreads < n4; i += kUnroll * nthreads) {
+            v4u v[kUnroll];
 #pragma unroll
-            for (int j = 0; j < 4; ++j) v[j] = __builtin_nontemporal_load(&x4[i * 4 + j]);
+            for (int j = 0; j < kUnroll; ++j) v[j] = __builtin_nontemporal_load(&x4[i + j * nthreads]);
 #pragma unroll
-            for (int j = 0; j < 4; ++j) {
-                const uint32_t a = max(max(v[j].x & 0x7FFFFFFFu, v[j].y & 0x7FFFFFFFu),
-                                       max(v[j].z & 0x7FFFFFFFu, v[j].w & 0x7FFFFFFFu));
-                m = max(m, a);
-            }
+            for (int j = 0; j < kUnroll; ++j)
+                m = max(m, max(max(v[j].x & 0x7FFFFFFFu, v[j].y & 0x7FFFFFFFu),
+                               max(v[j].z & 0x7FFFFFFFu, v[j].w & 0x7FFFFFFFu)));
         }
-        done = n16 * 16;
+        for (; i < n4; i += nthreads) {
+            const v4u v = x4[i];
+            m = max(m, max(max(v.x & 0x7FFFFFFFu, v.y & 0x7FFFFFFFu), max(v.z & 0x7FFFFFFFu, v.w & 0x7FFFFFFFu)));
+        }
+        done = n4 * 4;
     }
     for (int64_t i = done + tid; i < n; i += nthreads) m = max(m, abs_bits(x[i]));
 
@@ -70,15 +82,17 @@ __global__ __launch_bounds__(kThreads) void amax_reduce_kernel(const float* __re
         uint32_t b = part[0];
 #pragma unroll
         for (int w = 1; w < kThreads / 64; ++w) b = max(b, part[w]);
-        atomicMax(amax_bits, b);
+        if (b > __hip_atomic_load(amax_bits, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT)) atomicMax(amax_bits, b);
     }
 }
 
 __global__ void amax_finalize_kernel(const uint32_t* amax_bits, float* scale) {
-    if (scale) *scale = scale_from_amax(bits_f32(*amax_bits));
+    *scale = scale_from_amax(bits_f32(*amax_bits));
 }
 
 // q = E4M3(fl32(x / s)). The FP32 division is the IEEE correctly rounded one.
+// Each thread turns 4 floats (one 16-byte load) into one 32-bit word of codes,
+// so a wave instruction reads 1 KiB and writes 256 bytes, both contiguous.
 __global__ __launch_bounds__(kThreads) void quantize_kernel(const float* __restrict__ x, int64_t n,
                                                             const float* __restrict__ scale,
                                                             uint8_t* __restrict__ q, int vec) {
@@ -88,20 +102,20 @@ __global__ __launch_bounds__(kThreads) void quantize_kernel(const float* __restr
     int64_t done = 0;
     if (vec) {
         const v4f* x4 = reinterpret_cast<const v4f*>(x);
-        v4u* q16 = reinterpret_cast<v4u*>(q);
-        const int64_t n16 = n / 16;
-        for (int64_t i = tid; i < n16; i += nthreads) {
-            v4f v[4];
+        uint32_t* q4 = reinterpret_cast<uint32_t*>(q);
+        const int64_t n4 = n / 4;
+        for (int64_t i = tid; i < n4; i += kUnroll * nthreads) {
+            v4f v[kUnroll];
 #pragma unroll
-            for (int j = 0; j < 4; ++j) v[j] = __builtin_nontemporal_load(&x4[i * 4 + j]);
-            v4u o;
-            o.x = e4m3_pack4(v[0].x / s, v[0].y / s, v[0].z / s, v[0].w / s);
-            o.y = e4m3_pack4(v[1].x / s, v[1].y / s, v[1].z / s, v[1].w / s);
-            o.z = e4m3_pack4(v[2].x / s, v[2].y / s, v[2].z / s, v[2].w / s);
-            o.w = e4m3_pack4(v[3].x / s, v[3].y / s, v[3].z / s, v[3].w / s);
-            __builtin_nontemporal_store(o, &q16[i]);
+            for (int j = 0; j < kUnroll; ++j)
+                if (i + j * nthreads < n4) v[j] = __builtin_nontemporal_load(&x4[i + j * nthreads]);
+#pragma unroll
+            for (int j = 0; j < kUnroll; ++j)
+                if (i + j * nthreads < n4)
+                    __builtin_nontemporal_store(e4m3_pack4(v[j].x / s, v[j].y / s, v[j].z / s, v[j].w / s),
+                                                &q4[i + j * nthreads]);
         }
-        done = n16 * 16;
+        done = n4 * 4;
     }
     for (int64_t i = done + tid; i < n; i += nthreads) q[i] = e4m3_from_f32(x[i] / s);
 }
@@ -128,17 +142,17 @@ hipError_t launch_amax(const float* x, int64_t n, float* amax, float* scale, hip
     amax_init_kernel<<<1, 1, 0, stream>>>(bits);
     if (n > 0) {
         const int vec = aligned16(x) ? 1 : 0;
-        const int grid = grid_for(vec ? (n + 15) / 16 : n, 256 * 8);
+        const int grid = grid_for(vec ? (n / 4 + kUnroll - 1) / kUnroll : n, 512);
         amax_reduce_kernel<<<grid, kThreads, 0, stream>>>(x, n, bits, vec);
     }
-    amax_finalize_kernel<<<1, 1, 0, stream>>>(bits, scale);
+    if (scale) amax_finalize_kernel<<<1, 1, 0, stream>>>(bits, scale);
     return hipGetLastError();
 }
 
 hipError_t launch_quantize(const float* x, int64_t n, const float* scale, uint8_t* q, hipStream_t stream) {
     if (n <= 0) return hipSuccess;
-    const int vec = (aligned16(x) && aligned16(q)) ? 1 : 0;
-    const int grid = grid_for(vec ? (n + 15) / 16 : n, 256 * 8);
+    const int vec = (aligned16(x) && ((uintptr_t)q & 3u) == 0) ? 1 : 0;
+    const int grid = grid_for(vec ? (n / 4 + kUnroll - 1) / kUnroll : n, 4096);
     quantize_kernel<<<grid, kThreads, 0, stream>>>(x, n, scale, q, vec);
     return hipGetLastError();
 }

@@ -54,14 +54,26 @@ __device__ __forceinline__ float scale_from_amax(float a) {
 __device__ __forceinline__ uint32_t f32_bits(float x) { return __builtin_bit_cast(uint32_t, x); }
 __device__ __forceinline__ float bits_f32(uint32_t u) { return __builtin_bit_cast(float, u); }
 
-// Stores one output element of the scaled result y (already multiplied by sA*sB).
-__device__ __forceinline__ void store_out(void* C, int64_t idx, float y, int out_dtype, float s_out) {
+// Multiplier applied to the FP32 accumulator in every epilogue: sA*sB, and
+// for E4M3 output sA*sB / sOut, so that the result is y = acc * m. Folding
+// the output scale into one factor instead of dividing every element by sOut
+// changes y by at most a few FP32 ulps, well inside the one-code-step
+// tolerance of an E4M3 output.
+__device__ __forceinline__ float epilogue_multiplier(const float* sA, const float* sB, const float* sOut,
+                                                     bool e4m3_out) {
+    const float s = (sA ? *sA : 1.0f) * (sB ? *sB : 1.0f);
+    return e4m3_out ? s / *sOut : s;
+}
+
+// Stores one output element of the final value y (already multiplied by the
+// epilogue multiplier).
+__device__ __forceinline__ void store_out(void* C, int64_t idx, float y, int out_dtype) {
     if (out_dtype == OUT_F32) {
         reinterpret_cast<float*>(C)[idx] = y;
     } else if (out_dtype == OUT_F16) {
         reinterpret_cast<_Float16*>(C)[idx] = (_Float16)y;
     } else {
-        reinterpret_cast<uint8_t*>(C)[idx] = e4m3_from_f32(y / s_out);
+        reinterpret_cast<uint8_t*>(C)[idx] = e4m3_from_f32(y);
     }
 }
 

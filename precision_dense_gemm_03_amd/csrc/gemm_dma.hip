@@ -163,13 +163,13 @@ __device__ __forceinline__ void interleave_reads_with_mfma() {
 }
 
 template <int OUT>
-__device__ __forceinline__ void store_one(void* C, int64_t idx, float y, float s_out) {
+__device__ __forceinline__ void store_one(void* C, int64_t idx, float y) {
     if constexpr (OUT == OUT_F32) {
         reinterpret_cast<float*>(C)[idx] = y;
     } else if constexpr (OUT == OUT_F16) {
         reinterpret_cast<_Float16*>(C)[idx] = (_Float16)y;
     } else {
-        reinterpret_cast<uint8_t*>(C)[idx] = e4m3_from_f32(y / s_out);
+        reinterpret_cast<uint8_t*>(C)[idx] = e4m3_from_f32(y);
     }
 }
 
@@ -371,8 +371,7 @@ __global__ __launch_bounds__(256) void gemm_dma_kernel(const uint8_t* __restrict
 
     // ---- epilogue: y = acc * (sA*sB), converted; rows/columns past M/N are not stored ----
     // 32x32 accumulator element r of lane l: row 8*(r/4) + 4*(l/32) + r%4, column l%32.
-    const float scale = (sA ? *sA : 1.0f) * (sB ? *sB : 1.0f);
-    const float s_out = (OUT == OUT_E4M3) ? *sOut : 1.0f;
+    const float scale = epilogue_multiplier(sA, sB, sOut, OUT == OUT_E4M3);
     const int row0 = m0 + wm * 128 + 4 * h;
     const int col0 = n0 + wn * 128 + (lane & 31);
     const bool interior = (m0 + T::BM <= M) && (n0 + T::BN <= N);
@@ -385,7 +384,7 @@ __global__ __launch_bounds__(256) void gemm_dma_kernel(const uint8_t* __restrict
                 const int row = row0 + tm * 32 + 8 * (r >> 2) + (r & 3);
                 const int col = col0 + tn * 32;
                 if (interior || (row < M && col < N))
-                    store_one<OUT>(C, (int64_t)row * N + col, acc[tm][tn][r] * scale, s_out);
+                    store_one<OUT>(C, (int64_t)row * N + col, acc[tm][tn][r] * scale);
             }
 }
 

@@ -172,15 +172,15 @@ __global__ __launch_bounds__(NT) void gemm_stream_kernel(const uint8_t* __restri
             for (int e = 0; e < VE; ++e) red[wave][m][lane * VE + e] = acc[m][e];
     }
     __syncthreads();
-    const float scale = (sA ? *sA : 1.0f) * (sB ? *sB : 1.0f);
-    const float s_out = (out_dtype == OUT_E4M3) ? *sOut : 1.0f;
+    const float scale = epilogue_multiplier(sA, sB, sOut, out_dtype == OUT_E4M3);
+
     for (int o = tid; o < MMAX * COLS; o += NT) {
         const int m = o / COLS, c = o % COLS;
         float s = red[0][m][c];
 #pragma unroll
         for (int w = 1; w < NW; ++w) s += red[w][m][c];
         const int64_t col = n0 + c;
-        if (m < M && col < N) store_out(C, (int64_t)m * N + col, s * scale, out_dtype, s_out);
+        if (m < M && col < N) store_out(C, (int64_t)m * N + col, s * scale, out_dtype);
     }
     (void)SLW;
 }

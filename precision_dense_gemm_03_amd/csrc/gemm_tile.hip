@@ -138,13 +138,13 @@ __device__ __forceinline__ v4u load_chunk_guarded(const uint8_t* row_ptr, bool r
 }
 
 template <int OUT>
-__device__ __forceinline__ void store_one(void* C, int64_t idx, float y, float s_out) {
+__device__ __forceinline__ void store_one(void* C, int64_t idx, float y) {
     if constexpr (OUT == OUT_F32) {
         reinterpret_cast<float*>(C)[idx] = y;
     } else if constexpr (OUT == OUT_F16) {
         reinterpret_cast<_Float16*>(C)[idx] = (_Float16)y;
     } else {
-        reinterpret_cast<uint8_t*>(C)[idx] = e4m3_from_f32(y / s_out);
+        reinterpret_cast<uint8_t*>(C)[idx] = e4m3_from_f32(y);
     }
 }
 
@@ -378,8 +378,7 @@ __global__ __launch_bounds__(64 * WM * WN) void gemm_tile_kernel(
     }
 
     // Epilogue: y = acc * (sA*sB), converted, stored with M/N predication on edge tiles.
-    const float scale = (sA ? *sA : 1.0f) * (sB ? *sB : 1.0f);
-    const float s_out = (OUT == OUT_E4M3) ? *sOut : 1.0f;
+    const float scale = epilogue_multiplier(sA, sB, sOut, OUT == OUT_E4M3);
     const int row0 = m0 + wm * T::WTM + 4 * g;
     const int col0 = n0 + wn * T::WTN + j16;
     if (interior_mn) {
@@ -389,8 +388,7 @@ __global__ __launch_bounds__(64 * WM * WN) void gemm_tile_kernel(
             for (int tn = 0; tn < T::TN; ++tn)
 #pragma unroll
                 for (int r = 0; r < 4; ++r)
-                    store_one<OUT>(C, (int64_t)(row0 + tm * 16 + r) * N + col0 + tn * 16, acc[tm][tn][r] * scale,
-                                   s_out);
+                    store_one<OUT>(C, (int64_t)(row0 + tm * 16 + r) * N + col0 + tn * 16, acc[tm][tn][r] * scale);
     } else {
 #pragma unroll
         for (int tm = 0; tm < T::TM; ++tm)
@@ -400,7 +398,7 @@ __global__ __launch_bounds__(64 * WM * WN) void gemm_tile_kernel(
                 for (int r = 0; r < 4; ++r) {
                     const int row = row0 + tm * 16 + r, col = col0 + tn * 16;
                     if (row < M && col < N)
-                        store_one<OUT>(C, (int64_t)row * N + col, acc[tm][tn][r] * scale, s_out);
+                        store_one<OUT>(C, (int64_t)row * N + col, acc[tm][tn][r] * scale);
                 }
     }
 }

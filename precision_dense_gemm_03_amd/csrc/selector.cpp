@@ -11,7 +11,8 @@
 //   2. Otherwise the MFMA tile kernel: the largest square tile (256, 128, 64)
 //      whose grid still gives every CU a tile (>= 256 tiles) and whose padded
 //      area wastes at most 25 %; if none fills the chip, the tile with the
-//      most tiles (64).
+//      most tiles (64). Which kernel runs a 256x256 tile is chosen in
+//      tile_with below.
 //   3. LIBGEMM_CONFIG=<config name> replaces the choice when that config can
 //      serve the request (same operand kind; streaming configs need M <= bound).
 #include <cstdlib>
@@ -40,17 +41,20 @@ const GemmConfig* find_named(const char* name, int kind, int64_t M) {
     return nullptr;
 }
 
-// The preferred configuration of each tile size: 256x256 tiles use the
+// The preferred configuration of each tile size. 256x256 tiles use the
 // direct-load kernel (4 waves of 128x128, 4-stage LDS ring; it hands
-// unaligned operands to the register-staged kernel itself), smaller tiles the
+// unaligned operands to the register-staged kernel itself), except for FP8
+// when the grid is a single round of tiles (fewer than 2 per CU): there the
+// register-staged 8-wave kernel, whose two waves per SIMD overlap the
+// prologue and epilogue, measured faster. Smaller tiles use the
 // register-staged kernel with 4 waves.
-const GemmConfig* tile_with(int kind, int bm) {
+const GemmConfig* tile_with(int kind, int bm, int64_t tiles) {
     if (bm == 256) {
-        const char* want = (kind == KIND_FP8) ? "dma_fp8_256x256x64_s4" : "dma_f16_256x256x32_s4";
-        int nd = 0;
-        const GemmConfig* dt = dma_configs(&nd);
-        for (int i = 0; i < nd; ++i)
-            if (std::strcmp(dt[i].name, want) == 0) return &dt[i];
+        const bool direct = kind == KIND_F16 || tiles >= 2 * kNumCUs;
+        const char* want = direct ? (kind == KIND_FP8 ? "dma_fp8_256x256x64_s4" : "dma_f16_256x256x32_s4")
+                                  : "tile_fp8_256x256x128_w2x4";
+        const GemmConfig* c = find_named(want, kind, 0);
+        if (c) return c;
     }
     int nt = 0;
     const GemmConfig* tt = tile_configs(&nt);
@@ -83,10 +87,10 @@ const GemmConfig* select_config(int kind, int out_dtype, int64_t M, int64_t N, i
         const double useful = (double)M * (double)N;
         const double padded = (double)(tm * bm) * (double)(tn * bm);
         if (tm * tn >= kNumCUs && useful >= 0.75 * padded) {
-            if (const GemmConfig* c = tile_with(kind, bm)) return c;
+            if (const GemmConfig* c = tile_with(kind, bm, tm * tn)) return c;
         }
     }
-    return tile_with(kind, 64);
+    return tile_with(kind, 64, 0);
 }
 
 }  // namespace libgemm
