@@ -115,23 +115,26 @@ __global__ __launch_bounds__(NT) void gemm_stream_kernel(const uint8_t* __restri
         for (int m = 0; m < MMAX; ++m) {
             if (m < M) {
                 if (a_vec && kb + U <= K) {
-                    if constexpr (ES == 2) {
-                        static_assert(U == 8, "fp16 A vector load covers 8 elements");
-                        const v8h h = __builtin_bit_cast(v8h, *reinterpret_cast<const v4u*>(A + (m * K + kb) * 2));
+                    static_assert(U % 8 == 0, "A vector loads cover 8 elements");
 #pragma unroll
-                        for (int u = 0; u < U; ++u) a[m][u] = (float)h[u];
-                    } else {
-                        static_assert(U == 8, "fp8 A vector load covers 8 elements");
-                        const uint2 w = *reinterpret_cast<const uint2*>(A + m * K + kb);
-                        const uint32_t ww[2] = {w.x, w.y};
+                    for (int g8 = 0; g8 < U / 8; ++g8) {
+                        if constexpr (ES == 2) {
+                            const v8h h = __builtin_bit_cast(
+                                v8h, *reinterpret_cast<const v4u*>(A + (m * K + kb + 8 * g8) * 2));
 #pragma unroll
-                        for (int q = 0; q < 2; ++q) {
-                            auto lo = __builtin_amdgcn_cvt_pk_f32_fp8((int)ww[q], false);
-                            auto hi = __builtin_amdgcn_cvt_pk_f32_fp8((int)ww[q], true);
-                            a[m][4 * q + 0] = lo[0];
-                            a[m][4 * q + 1] = lo[1];
-                            a[m][4 * q + 2] = hi[0];
-                            a[m][4 * q + 3] = hi[1];
+                            for (int u = 0; u < 8; ++u) a[m][8 * g8 + u] = (float)h[u];
+                        } else {
+                            const uint2 w = *reinterpret_cast<const uint2*>(A + m * K + kb + 8 * g8);
+                            const uint32_t ww[2] = {w.x, w.y};
+#pragma unroll
+                            for (int q = 0; q < 2; ++q) {
+                                auto lo = __builtin_amdgcn_cvt_pk_f32_fp8((int)ww[q], false);
+                                auto hi = __builtin_amdgcn_cvt_pk_f32_fp8((int)ww[q], true);
+                                a[m][8 * g8 + 4 * q + 0] = lo[0];
+                                a[m][8 * g8 + 4 * q + 1] = lo[1];
+                                a[m][8 * g8 + 4 * q + 2] = hi[0];
+                                a[m][8 * g8 + 4 * q + 3] = hi[1];
+                            }
                         }
                     }
                 } else {
