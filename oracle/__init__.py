@@ -18,6 +18,7 @@ _lib = None
 
 FMT_E4M3 = 0
 FMT_F16 = 1
+FMT_E5M2 = 2
 
 _c_i64 = ctypes.c_int64
 _vp = ctypes.c_void_p
@@ -39,7 +40,12 @@ def _load():
     lib.orc_f16_decode.argtypes = [ctypes.c_uint16]
     lib.orc_f16_round.restype = ctypes.c_uint16
     lib.orc_f16_round.argtypes = [ctypes.c_double]
+    lib.orc_e5m2_decode.restype = ctypes.c_double
+    lib.orc_e5m2_decode.argtypes = [ctypes.c_uint8]
+    lib.orc_e5m2_encode.restype = ctypes.c_uint8
+    lib.orc_e5m2_encode.argtypes = [ctypes.c_double]
     for name in ("orc_e4m3_decode_n", "orc_e4m3_encode_n", "orc_e4m3_encode_f32bits",
+                 "orc_e5m2_decode_n", "orc_e5m2_encode_n", "orc_e5m2_encode_f32bits",
                  "orc_f16_decode_n", "orc_f16_round_n", "orc_out_f16"):
         getattr(lib, name).restype = None
         getattr(lib, name).argtypes = [_vp, _c_i64, _vp]
@@ -49,8 +55,17 @@ def _load():
     lib.orc_scale_from_amax.argtypes = [ctypes.c_float]
     lib.orc_quantize.restype = None
     lib.orc_quantize.argtypes = [_vp, _c_i64, ctypes.c_float, _vp]
+    lib.orc_scale.restype = ctypes.c_float
+    lib.orc_scale.argtypes = [ctypes.c_float, ctypes.c_int, ctypes.c_int]
+    lib.orc_quantize_fmt.restype = None
+    lib.orc_quantize_fmt.argtypes = [_vp, _c_i64, ctypes.c_float, ctypes.c_int, _vp]
     lib.orc_gemm.restype = ctypes.c_int
     lib.orc_gemm.argtypes = [ctypes.c_int, _vp, _vp, _c_i64, _c_i64, _c_i64, _vp, _c_i64, _vp, _vp]
+    lib.orc_gemm_mixed.restype = ctypes.c_int
+    lib.orc_gemm_mixed.argtypes = [ctypes.c_int, ctypes.c_int, _vp, _vp, _c_i64, _c_i64, _c_i64, _vp, _c_i64,
+                                   _vp, _vp]
+    lib.orc_out_fp8.restype = None
+    lib.orc_out_fp8.argtypes = [_vp, _c_i64, ctypes.c_double, ctypes.c_int, _vp]
     lib.orc_out_e4m3.restype = None
     lib.orc_out_e4m3.argtypes = [_vp, _c_i64, ctypes.c_double, _vp]
     lib.orc_num_threads.restype = ctypes.c_int
@@ -93,6 +108,32 @@ def e4m3_encode_f32bits(bits) -> np.ndarray:
     return out
 
 
+def e5m2_decode(codes) -> np.ndarray:
+    c = _c(codes, np.uint8)
+    out = np.empty(c.shape, np.float64)
+    _load().orc_e5m2_decode_n(_ptr(c), c.size, _ptr(out))
+    return out
+
+
+def e5m2_encode(values) -> np.ndarray:
+    """E5M2 code of each real value (given as float64), RNE, saturating at 57344."""
+    v = _c(values, np.float64)
+    out = np.empty(v.shape, np.uint8)
+    _load().orc_e5m2_encode_n(_ptr(v), v.size, _ptr(out))
+    return out
+
+
+def e5m2_encode_f32bits(bits) -> np.ndarray:
+    b = _c(bits, np.uint32)
+    out = np.empty(b.shape, np.uint8)
+    _load().orc_e5m2_encode_f32bits(_ptr(b), b.size, _ptr(out))
+    return out
+
+
+def fp8_decode(codes, fmt) -> np.ndarray:
+    return e5m2_decode(codes) if fmt == FMT_E5M2 else e4m3_decode(codes)
+
+
 def f16_decode(bits) -> np.ndarray:
     h = _c(bits, np.uint16)
     out = np.empty(h.shape, np.float64)
@@ -117,21 +158,34 @@ def scale_from_amax(a) -> np.float32:
     return np.float32(_load().orc_scale_from_amax(float(np.float32(a))))
 
 
-def quantize(x, s) -> np.ndarray:
+def scale(a, fmt=FMT_E4M3, pow2=False) -> np.float32:
+    """Per-tensor scale of amax a for an FP8 format: a / fmax in FP32 (1 when
+    that is 0), or with pow2 the smallest power of two s with a / s <= fmax."""
+    return np.float32(_load().orc_scale(float(np.float32(a)), int(fmt), 1 if pow2 else 0))
+
+
+def quantize(x, s, fmt=FMT_E4M3) -> np.ndarray:
     a = _c(x, np.float32)
     out = np.empty(a.shape, np.uint8)
-    _load().orc_quantize(_ptr(a), a.size, float(np.float32(s)), _ptr(out))
+    if fmt == FMT_E4M3:
+        _load().orc_quantize(_ptr(a), a.size, float(np.float32(s)), _ptr(out))
+    else:
+        _load().orc_quantize_fmt(_ptr(a), a.size, float(np.float32(s)), int(fmt), _ptr(out))
     return out
 
 
-def gemm(fmt, A, B, rows=None):
+def gemm(fmt, A, B, rows=None, fmt_b=None):
     """Unscaled reference product of row-major A[M,K] and B[K,N].
 
-    A, B: uint8 E4M3 codes (fmt=FMT_E4M3) or uint16 binary16 bits (FMT_F16).
+    A, B: uint8 FP8 codes (fmt=FMT_E4M3 or FMT_E5M2; B may use another FP8
+    format given as fmt_b) or uint16 binary16 bits (FMT_F16).
     Returns (R, S), float64 [len(rows) or M, N]: R = sum_k a*b in ascending k,
     S = sum_k |a*b|. rows: optional list of row indices to compute.
     """
-    dt = np.uint8 if fmt == FMT_E4M3 else np.uint16
+    fb = fmt if fmt_b is None else fmt_b
+    if (fmt == FMT_F16) != (fb == FMT_F16):
+        raise ValueError("FP16 pairs only with FP16")
+    dt = np.uint16 if fmt == FMT_F16 else np.uint8
     A = _c(A, dt)
     B = _c(B, dt)
     M, K = A.shape
@@ -148,7 +202,7 @@ def gemm(fmt, A, B, rows=None):
     R = np.empty((nrows, N), np.float64)
     S = np.empty((nrows, N), np.float64)
     if nrows and N:
-        rc = _load().orc_gemm(fmt, _ptr(A), _ptr(B), M, N, K, rp, nrows, _ptr(R), _ptr(S))
+        rc = _load().orc_gemm_mixed(fmt, fb, _ptr(A), _ptr(B), M, N, K, rp, nrows, _ptr(R), _ptr(S))
         if rc != 0:
             raise MemoryError("oracle gemm: out of memory")
     return R, S
@@ -156,6 +210,13 @@ def gemm(fmt, A, B, rows=None):
 
 def out_f16(V) -> np.ndarray:
     return f16_round(V)
+
+
+def out_fp8(V, s_out, fmt) -> np.ndarray:
+    v = _c(V, np.float64)
+    out = np.empty(v.shape, np.uint8)
+    _load().orc_out_fp8(_ptr(v), v.size, float(s_out), int(fmt), _ptr(out))
+    return out
 
 
 def out_e4m3(V, s_out) -> np.ndarray:

@@ -27,10 +27,18 @@
  *     output, divided by the output scale (P2 §3.2); FP8 output needs its own
  *     output scale (P2 §4.3).
  *   - FP16 GEMM with a 32-bit (here: wider) accumulator (P3 §1.3).
+ *   - E5M2 is the other FP8 format: 5 exponent and 2 mantissa bits, wider
+ *     range, less precision (P2 §2.1); its quantization clamps at 57344
+ *     (P2 §4.3). That maximum identifies the OCP E5M2 variant (IEEE-like:
+ *     bias 15, subnormals, S.11111.00 = inf, S.11111.mm (mm != 0) = NaN).
+ *   - A scale may be a power of two just above the calibrated maximum, so
+ *     that scaling is exponent arithmetic (P2 §2.1). Read as: the smallest
+ *     2^e with max|x| / 2^e <= the format's largest value.
  *
  * Readings where the pages are silent (each is listed with its reason in the
- * design notes): a NaN always encodes to the canonical code 0x7F; +-inf and
- * anything of magnitude >= 448 saturate to +-448; amax == 0 (or a scale that
+ * design notes): a NaN always encodes to the canonical code 0x7F (both
+ * formats); +-inf and anything of magnitude >= 448 (E4M3) or >= 57344 (E5M2)
+ * saturate to the largest finite value; amax == 0 (or a scale that
  * underflows to 0) gives scale 1; NaN propagates through amax; signed zeros
  * keep their sign; FP16 output overflows to +-inf as IEEE rounding does.
  */
@@ -117,6 +125,77 @@ ORC_API void orc_e4m3_encode_f32bits(const uint32_t* bits, int64_t n, uint8_t* o
     }
 }
 
+/* ---------------------------------------------------------------- E5M2 --- */
+
+/* Decode one E5M2 code: s eeeee mm, bias 15. e == 0: m * 2^-16 (subnormal);
+ * 1 <= e <= 30: (1 + m/4) * 2^(e-15); e == 31: inf (m == 0) or NaN. */
+ORC_API double orc_e5m2_decode(uint8_t code) {
+    int s = (code >> 7) & 1;
+    int e = (code >> 2) & 31;
+    int m = code & 3;
+    double mag;
+    if (e == 31) mag = (m == 0) ? INFINITY : NAN;
+    else if (e == 0) mag = ldexp((double)m, -16);
+    else mag = ldexp(4.0 + (double)m, e - 17); /* (1 + m/4) * 2^(e-15) */
+    return s ? -mag : mag;
+}
+
+/* Finite non-negative E5M2 magnitudes, codes 0x00..0x7B (0x7B = 57344). */
+static double e5m2_mag_table[124];
+
+__attribute__((constructor)) static void e5m2_mag_init(void) {
+    for (int c = 0; c < 124; ++c) e5m2_mag_table[c] = orc_e5m2_decode((uint8_t)c);
+}
+
+/* Encode a real value to E5M2: nearest finite magnitude, ties to the code with
+ * even last bit, saturate at 57344 (inf included), NaN -> 0x7F. Bisection over
+ * the 124 sorted magnitudes and the exact midpoint, as for E4M3. */
+ORC_API uint8_t orc_e5m2_encode(double v) {
+    uint8_t sign;
+    double a, mid;
+    int lo, hi;
+    if (isnan(v)) return 0x7F;
+    sign = signbit(v) ? 0x80 : 0x00;
+    a = fabs(v);
+    if (a >= 57344.0) return (uint8_t)(sign | 0x7B);
+    lo = 0;
+    hi = 123;
+    while (hi - lo > 1) {
+        int m = (lo + hi) / 2;
+        if (e5m2_mag_table[m] <= a) lo = m; else hi = m;
+    }
+    if (e5m2_mag_table[lo] == a) return (uint8_t)(sign | lo);
+    mid = 0.5 * (e5m2_mag_table[lo] + e5m2_mag_table[hi]);
+    if (a < mid) return (uint8_t)(sign | lo);
+    if (a > mid) return (uint8_t)(sign | hi);
+    return (uint8_t)(sign | ((lo & 1) == 0 ? lo : hi));
+}
+
+ORC_API void orc_e5m2_decode_n(const uint8_t* c, int64_t n, double* out) {
+    for (int64_t i = 0; i < n; ++i) out[i] = orc_e5m2_decode(c[i]);
+}
+
+ORC_API void orc_e5m2_encode_n(const double* v, int64_t n, uint8_t* out) {
+#pragma omp parallel for schedule(static)
+    for (int64_t i = 0; i < n; ++i) out[i] = orc_e5m2_encode(v[i]);
+}
+
+ORC_API void orc_e5m2_encode_f32bits(const uint32_t* bits, int64_t n, uint8_t* out) {
+#pragma omp parallel for schedule(static)
+    for (int64_t i = 0; i < n; ++i) {
+        float f;
+        memcpy(&f, &bits[i], 4);
+        out[i] = orc_e5m2_encode((double)f);
+    }
+}
+
+/* FP8 formats by number: 0 = E4M3, 2 = E5M2 (1 is FP16 in the GEMM below). */
+enum { ORC_FMT_E4M3 = 0, ORC_FMT_F16 = 1, ORC_FMT_E5M2 = 2 };
+
+static double fp8_decode(int fmt, uint8_t c) { return fmt == ORC_FMT_E5M2 ? orc_e5m2_decode(c) : orc_e4m3_decode(c); }
+static uint8_t fp8_encode(int fmt, double v) { return fmt == ORC_FMT_E5M2 ? orc_e5m2_encode(v) : orc_e4m3_encode(v); }
+static double fp8_max(int fmt) { return fmt == ORC_FMT_E5M2 ? 57344.0 : 448.0; }
+
 /* ---------------------------------------------------------------- FP16 --- */
 
 /* Decode IEEE binary16: s eeeee mmmmmmmmmm, bias 15. */
@@ -185,6 +264,35 @@ ORC_API float orc_scale_from_amax(float a) {
     return s;
 }
 
+/* Scale for format fmt from amax a. pow2 == 0: fl32(a / fmax), 1 when that
+ * is 0 (P2 §3.2). pow2 != 0: the smallest power of two s with a / s <= fmax
+ * (P2 §2.1), found by exact doubling/halving in double, not below 2^-149 (the
+ * smallest FP32 power of two); a == 0 gives 1, inf gives inf, NaN gives NaN. */
+ORC_API float orc_scale(float a, int fmt, int pow2) {
+    const double fmax = fp8_max(fmt);
+    double s;
+    if (!pow2) {
+        float q = (float)((double)a / fmax);
+        return q == 0.0f ? 1.0f : q;
+    }
+    if (isnan(a)) return NAN;
+    if (isinf(a)) return INFINITY;
+    if (a == 0.0f) return 1.0f;
+    s = 1.0;
+    while ((double)a / s > fmax) s *= 2.0;          /* exact: powers of two */
+    while (s > ldexp(1.0, -149) && (double)a / (s * 0.5) <= fmax) s *= 0.5;
+    return (float)s;
+}
+
+/* q_i = FP8_fmt(fl32(x_i / s)) (P2 §4.3) for either format. */
+ORC_API void orc_quantize_fmt(const float* x, int64_t n, float s, int fmt, uint8_t* q) {
+#pragma omp parallel for schedule(static)
+    for (int64_t i = 0; i < n; ++i) {
+        float t = (float)((double)x[i] / (double)s);
+        q[i] = fp8_encode(fmt, (double)t);
+    }
+}
+
 /* q_i = E4M3(fl32(x_i / s)) (P2 §4.3), fl32 being correctly rounded division. */
 ORC_API void orc_quantize(const float* x, int64_t n, float s, uint8_t* q) {
 #pragma omp parallel for schedule(static)
@@ -196,15 +304,13 @@ ORC_API void orc_quantize(const float* x, int64_t n, float s, uint8_t* q) {
 
 /* -------------------------------------------------------------- GEMM ---- */
 
-enum { ORC_FMT_E4M3 = 0, ORC_FMT_F16 = 1 };
-
 static double* decode_matrix(int fmt, const void* p, int64_t n) {
     double* d = (double*)malloc((size_t)(n > 0 ? n : 1) * sizeof(double));
     if (!d) return NULL;
-    if (fmt == ORC_FMT_E4M3) {
+    if (fmt != ORC_FMT_F16) {
         const uint8_t* c = (const uint8_t*)p;
 #pragma omp parallel for schedule(static)
-        for (int64_t i = 0; i < n; ++i) d[i] = orc_e4m3_decode(c[i]);
+        for (int64_t i = 0; i < n; ++i) d[i] = fp8_decode(fmt, c[i]);
     } else {
         const uint16_t* h = (const uint16_t*)p;
 #pragma omp parallel for schedule(static)
@@ -213,18 +319,20 @@ static double* decode_matrix(int fmt, const void* p, int64_t n) {
     return d;
 }
 
-/* Row-major A[M,K] and B[K,N] (both in format fmt), unscaled products summed
- * in double in ascending k:  R[r,j] = sum_k a[i,k] b[k,j],
- *                            S[r,j] = sum_k |a[i,k] b[k,j]|,
+/* Row-major A[M,K] (format fa) and B[K,N] (format fb), unscaled products
+ * summed in double in ascending k:  R[r,j] = sum_k a[i,k] b[k,j],
+ *                                   S[r,j] = sum_k |a[i,k] b[k,j]|,
  * for the rows i = rows[r] (rows == NULL: every row, r == i). R and S are
- * [nrows, N] row-major. Returns 0, or -1 when out of memory. */
-ORC_API int orc_gemm(int fmt, const void* A, const void* B, int64_t M, int64_t N, int64_t K,
-                     const int64_t* rows, int64_t nrows, double* R, double* S) {
+ * [nrows, N] row-major. E4M3 x E4M3 sums are exact (see above); E5M2 spans a
+ * wider range, so its sums are the double-rounded sequential sum. FP16 pairs
+ * only with FP16. Returns 0, or -1 when out of memory. */
+ORC_API int orc_gemm_mixed(int fa, int fb, const void* A, const void* B, int64_t M, int64_t N, int64_t K,
+                           const int64_t* rows, int64_t nrows, double* R, double* S) {
     const uint8_t* a8 = (const uint8_t*)A;
     const uint16_t* a16 = (const uint16_t*)A;
     double* Bd;
     if (rows == NULL) nrows = M;
-    Bd = decode_matrix(fmt, B, K * N);
+    Bd = decode_matrix(fb, B, K * N);
     if (!Bd) return -1;
 #pragma omp parallel for schedule(dynamic, 1)
     for (int64_t r = 0; r < nrows; ++r) {
@@ -233,8 +341,7 @@ ORC_API int orc_gemm(int fmt, const void* A, const void* B, int64_t M, int64_t N
         double* restrict Sr = S + r * N;
         for (int64_t j = 0; j < N; ++j) { Rr[j] = 0.0; Sr[j] = 0.0; }
         for (int64_t k = 0; k < K; ++k) {
-            double a = (fmt == ORC_FMT_E4M3) ? orc_e4m3_decode(a8[i * K + k])
-                                             : orc_f16_decode(a16[i * K + k]);
+            double a = (fa == ORC_FMT_F16) ? orc_f16_decode(a16[i * K + k]) : fp8_decode(fa, a8[i * K + k]);
             const double* restrict Bk = Bd + k * N;
             for (int64_t j = 0; j < N; ++j) {
                 double p = a * Bk[j];
@@ -248,12 +355,23 @@ ORC_API int orc_gemm(int fmt, const void* A, const void* B, int64_t M, int64_t N
     return 0;
 }
 
+/* Both operands in the same format fmt. */
+ORC_API int orc_gemm(int fmt, const void* A, const void* B, int64_t M, int64_t N, int64_t K,
+                     const int64_t* rows, int64_t nrows, double* R, double* S) {
+    return orc_gemm_mixed(fmt, fmt, A, B, M, N, K, rows, nrows, R, S);
+}
+
 /* Output rounding of the scaled result V (P2 §3.2, §4.3). */
 ORC_API void orc_out_f16(const double* V, int64_t n, uint16_t* out) { orc_f16_round_n(V, n, out); }
 
 ORC_API void orc_out_e4m3(const double* V, int64_t n, double sOut, uint8_t* out) {
 #pragma omp parallel for schedule(static)
     for (int64_t i = 0; i < n; ++i) out[i] = orc_e4m3_encode(V[i] / sOut);
+}
+
+ORC_API void orc_out_fp8(const double* V, int64_t n, double sOut, int fmt, uint8_t* out) {
+#pragma omp parallel for schedule(static)
+    for (int64_t i = 0; i < n; ++i) out[i] = fp8_encode(fmt, V[i] / sOut);
 }
 
 ORC_API int orc_num_threads(void) {
