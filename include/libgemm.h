@@ -1,6 +1,6 @@
 /*
- * libgemm — FP8 (E4M3) per-tensor-scaled GEMM and FP16 GEMM for AMD Instinct
- * MI355X (gfx950), with the amax and FP8 quantize steps that feed it.
+ * libgemm — FP8 (E4M3 / E5M2) per-tensor-scaled GEMM and FP16 GEMM for AMD
+ * Instinct MI355X (gfx950), with the amax and FP8 quantize steps that feed it.
  *
  * Sources that define the operations (cited per entry point below):
  *   P1  DeepGEMM deep-dive article (hnwysp.cn, news 84236)
@@ -40,7 +40,7 @@ extern "C" {
 #define GEMM_ERR_NULL (-1)        /* a required pointer is NULL                          */
 #define GEMM_ERR_DIM (-2)         /* a dimension is negative or above 2^31 - 1             */
 #define GEMM_ERR_DTYPE (-3)       /* unknown out_dtype, or one the entry point cannot write */
-#define GEMM_ERR_SCALE (-4)       /* sOut is NULL while out_dtype == GEMM_OUT_E4M3         */
+#define GEMM_ERR_SCALE (-4)       /* sOut is NULL while out_dtype is an FP8 output         */
 #define GEMM_ERR_LAUNCH (-5)      /* the HIP runtime rejected a kernel launch              */
 #define GEMM_ERR_UNSUPPORTED (-6) /* no kernel for this request                            */
 #define GEMM_ERR_DEVICE (-7)      /* no current HIP device, or it is not gfx950            */
@@ -50,6 +50,14 @@ extern "C" {
 #define GEMM_OUT_F32 0  /* float                                                  */
 #define GEMM_OUT_F16 1  /* IEEE binary16, round to nearest even, overflow to inf   */
 #define GEMM_OUT_E4M3 2 /* OCP E4M3 code (uint8), nearest even, saturate at +-448 */
+#define GEMM_OUT_E5M2 3 /* OCP E5M2 code (uint8), nearest even, saturate at +-57344 */
+
+/* ----------------------------------------------------- FP8 formats */
+/* P2 §2.1: E4M3 (4 exponent, 3 mantissa bits; largest value 448) and E5M2
+ * (5 exponent, 2 mantissa bits; wider range, less precision; largest 57344,
+ * P2 §4.3). Both are the OCP variants: E4M3 without infinities, E5M2 IEEE-like. */
+#define GEMM_FMT_E4M3 0
+#define GEMM_FMT_E5M2 1
 
 /*
  * gemm_f16 — C = A·B for FP16 operands with FP32 accumulation.
@@ -80,13 +88,26 @@ int gemm_f16(const void* A, const void* B, void* C, int out_dtype,
  *   C          device, float / _Float16 / uint8 per out_dtype, [M*N]
  *   out_dtype  GEMM_OUT_F32, GEMM_OUT_F16 or GEMM_OUT_E4M3
  * Element value: y = acc·(sA·sB) with acc the FP32 sum of decoded products;
- * F32 writes y, F16 writes RNE(y), E4M3 writes E4M3(y / sOut); the kernels
- * form y / sOut as acc·(sA·sB/sOut), one FP32 factor, which may differ from
- * the two-step quotient by a few FP32 ulps (within one E4M3 code step).
+ * F32 writes y, F16 writes RNE(y), E4M3 / E5M2 write FP8(y / sOut); the
+ * kernels form y / sOut as acc·(sA·sB/sOut), one FP32 factor, which may differ
+ * from the two-step quotient by a few FP32 ulps (within one FP8 code step).
+ * out_dtype GEMM_OUT_E5M2 is accepted as well (sOut required).
  */
 int gemm_fp8_scaled(const uint8_t* A, const uint8_t* B, const float* sA, const float* sB,
                     const float* sOut, void* C, int out_dtype,
                     int64_t M, int64_t N, int64_t K, hipStream_t stream);
+
+/*
+ * gemm_fp8_fmt — gemm_fp8_scaled with a format per operand: A holds codes of
+ * format fmt_a, B of fmt_b (GEMM_FMT_E4M3 or GEMM_FMT_E5M2; P2 §2.1 names both
+ * FP8 formats, each with its own range). Same arguments, element value,
+ * outputs (F32, F16, E4M3, E5M2) and errors as gemm_fp8_scaled; an unknown
+ * format gives GEMM_ERR_DTYPE. Products of E4M3 and E5M2 codes accumulate in
+ * FP32 on the FP8 matrix cores, whose format selectors take both formats.
+ */
+int gemm_fp8_fmt(const uint8_t* A, int fmt_a, const uint8_t* B, int fmt_b,
+                 const float* sA, const float* sB, const float* sOut, void* C, int out_dtype,
+                 int64_t M, int64_t N, int64_t K, hipStream_t stream);
 
 /*
  * quantize_fp8 — q[i] = E4M3(fl32(x[i] / scale)).
@@ -100,6 +121,15 @@ int gemm_fp8_scaled(const uint8_t* A, const uint8_t* B, const float* sA, const f
  *   q      device, uint8[n], written; must not overlap x
  */
 int quantize_fp8(const float* x, int64_t n, const float* scale, uint8_t* q, hipStream_t stream);
+
+/*
+ * quantize_fp8_fmt — quantize_fp8 into FP8 format fmt: E4M3 as above, or E5M2
+ * (P2 §4.3: the clamp bound is 57344 for E5M2): the FP32 quotient rounded to
+ * the nearest E5M2 value (ties to the even code), saturated at +-57344, +-inf
+ * saturating too, NaN giving 0x7F. Unknown fmt: GEMM_ERR_DTYPE. Arguments and
+ * errors otherwise as quantize_fp8.
+ */
+int quantize_fp8_fmt(const float* x, int64_t n, const float* scale, uint8_t* q, int fmt, hipStream_t stream);
 
 /*
  * amax_f32 — *amax = max_i |x[i]| (exact; NaN if any x[i] is NaN; 0 for
@@ -116,6 +146,21 @@ int quantize_fp8(const float* x, int64_t n, const float* scale, uint8_t* q, hipS
  */
 int amax_f32(const float* x, int64_t n, float* amax, float* scale, hipStream_t stream);
 
+/*
+ * amax_scale_f32 — amax_f32 with the scale rule chosen by the caller:
+ *   pow2 == 0: *scale = fl32(*amax / fmax), replaced by 1 when that is 0,
+ *              fmax = 448 (GEMM_FMT_E4M3) or 57344 (GEMM_FMT_E5M2) (P2 §3.2,
+ *              §4.3);
+ *   pow2 != 0: *scale = the smallest power of two s with *amax / s <= fmax
+ *              (P2 §2.1: a power of two just above the calibrated maximum, so
+ *              scaling is exponent arithmetic), not below 2^-149; amax 0 gives
+ *              1, inf gives inf, NaN gives NaN.
+ * Unknown fmt: GEMM_ERR_DTYPE. Arguments, aliasing rules and errors otherwise
+ * as amax_f32 (amax_f32 is this call with GEMM_FMT_E4M3 and pow2 = 0).
+ */
+int amax_scale_f32(const float* x, int64_t n, float* amax, float* scale, int fmt, int pow2,
+                   hipStream_t stream);
+
 /* Human-readable name of a status code (a static string). */
 const char* gemm_status_str(int status);
 
@@ -129,6 +174,11 @@ const char* gemm_status_str(int status);
  */
 int gemm_select_config(int kind, int out_dtype, int64_t M, int64_t N, int64_t K,
                        char* buf, int buflen);
+
+/* gemm_select_config for gemm_fp8_fmt's operand formats (kind 1), or kind 0
+ * with formats ignored; unknown formats give GEMM_ERR_DTYPE. */
+int gemm_select_config_fmt(int kind, int out_dtype, int64_t M, int64_t N, int64_t K,
+                           int fmt_a, int fmt_b, char* buf, int buflen);
 
 #ifdef __cplusplus
 }

@@ -7,12 +7,17 @@ fallback: if libgemm.so is not built, every call raises.
 
 Functions keep the C names:
     gemm_f16(A, B, C, stream=None)
-    gemm_fp8_scaled(A, B, sA, sB, C, sOut=None, stream=None)
+    gemm_fp8_scaled(A, B, sA, sB, C, sOut=None, stream=None, out_fmt=None)
+    gemm_fp8_fmt(A, fmt_a, B, fmt_b, sA, sB, C, sOut=None, stream=None, out_fmt=None)
     quantize_fp8(x, scale, q=None, stream=None) -> q
+    quantize_fp8_fmt(x, scale, fmt, q=None, stream=None) -> q
     amax_f32(x, amax=None, scale=None, stream=None) -> (amax, scale)
+    amax_scale_f32(x, fmt, pow2, amax=None, scale=None, stream=None) -> (amax, scale)
     select_config(kind, out_dtype, M, N, K) -> str   (host-only query)
-The output dtype of a GEMM is taken from C: float32, float16, or uint8
-(E4M3 codes; torch.float8_e4m3fn tensors are accepted and viewed as uint8).
+    select_config_fmt(kind, out_dtype, M, N, K, fmt_a, fmt_b) -> str
+The output dtype of a GEMM is taken from C: float32, float16, or 8-bit codes
+(uint8 or torch.float8_e4m3fn: E4M3; torch.float8_e5m2, or uint8 with
+out_fmt=FMT_E5M2: E5M2). FP8 operands are uint8 codes or torch float8 tensors.
 """
 import ctypes
 import os
@@ -23,6 +28,9 @@ LIB_PATH = os.path.join(PKG_DIR, "libgemm.so")
 OUT_F32 = 0
 OUT_F16 = 1
 OUT_E4M3 = 2
+OUT_E5M2 = 3
+FMT_E4M3 = 0
+FMT_E5M2 = 1
 KIND_F16 = 0
 KIND_FP8 = 1
 
@@ -64,6 +72,14 @@ def lib() -> ctypes.CDLL:
     L.gemm_status_str.argtypes = [i32]
     L.gemm_select_config.restype = i32
     L.gemm_select_config.argtypes = [i32, i32, i64, i64, i64, ctypes.c_char_p, i32]
+    L.gemm_fp8_fmt.restype = i32
+    L.gemm_fp8_fmt.argtypes = [vp, i32, vp, i32, vp, vp, vp, vp, i32, i64, i64, i64, vp]
+    L.quantize_fp8_fmt.restype = i32
+    L.quantize_fp8_fmt.argtypes = [vp, i64, vp, vp, i32, vp]
+    L.amax_scale_f32.restype = i32
+    L.amax_scale_f32.argtypes = [vp, i64, vp, vp, i32, i32, vp]
+    L.gemm_select_config_fmt.restype = i32
+    L.gemm_select_config_fmt.argtypes = [i32, i32, i64, i64, i64, i32, i32, ctypes.c_char_p, i32]
     _lib = L
     return L
 
@@ -100,12 +116,14 @@ def _ptr(t):
     return t.data_ptr()
 
 
-def _out_dtype(C):
+def _out_dtype(C, out_fmt=None):
     torch = _torch()
     if C.dtype == torch.float32:
         return OUT_F32
     if C.dtype == torch.float16:
         return OUT_F16
+    if C.dtype == torch.float8_e5m2 or (C.dtype == torch.uint8 and out_fmt == FMT_E5M2):
+        return OUT_E5M2
     if C.dtype in (torch.uint8, torch.float8_e4m3fn):
         return OUT_E4M3
     raise ValueError(f"unsupported output dtype {C.dtype}")
@@ -133,22 +151,33 @@ def gemm_f16(A, B, C, stream=None):
 
 def _u8(t):
     torch = _torch()
-    if t.dtype == torch.float8_e4m3fn:
+    if t.dtype in (torch.float8_e4m3fn, torch.float8_e5m2):
         return t.view(torch.uint8)
     if t.dtype != torch.uint8:
-        raise ValueError("E4M3 tensors must be uint8 codes or torch.float8_e4m3fn")
+        raise ValueError("FP8 tensors must be uint8 codes or torch float8 tensors")
     return t
 
 
-def gemm_fp8_scaled(A, B, sA, sB, C, sOut=None, stream=None):
+def gemm_fp8_scaled(A, B, sA, sB, C, sOut=None, stream=None, out_fmt=None):
     """C = (sA*A) @ (sB*B) for E4M3 A[M,K], B[K,N]; sA, sB (and sOut for an
-    E4M3 C) are one-element float32 device tensors."""
+    FP8 C) are one-element float32 device tensors."""
     A, B = _u8(A), _u8(B)
-    out = _out_dtype(C)
-    Cv = _u8(C) if out == OUT_E4M3 else C
+    out = _out_dtype(C, out_fmt)
+    Cv = _u8(C) if out in (OUT_E4M3, OUT_E5M2) else C
     M, N, K = _dims(A, B, Cv)
     _check(lib().gemm_fp8_scaled(_ptr(A), _ptr(B), _ptr(sA), _ptr(sB), _ptr(sOut), _ptr(Cv), out, M, N, K,
                                  _stream_handle(stream)), "gemm_fp8_scaled")
+    return C
+
+
+def gemm_fp8_fmt(A, fmt_a, B, fmt_b, sA, sB, C, sOut=None, stream=None, out_fmt=None):
+    """gemm_fp8_scaled with A in FP8 format fmt_a and B in fmt_b (FMT_E4M3 / FMT_E5M2)."""
+    A, B = _u8(A), _u8(B)
+    out = _out_dtype(C, out_fmt)
+    Cv = _u8(C) if out in (OUT_E4M3, OUT_E5M2) else C
+    M, N, K = _dims(A, B, Cv)
+    _check(lib().gemm_fp8_fmt(_ptr(A), int(fmt_a), _ptr(B), int(fmt_b), _ptr(sA), _ptr(sB), _ptr(sOut), _ptr(Cv),
+                              out, M, N, K, _stream_handle(stream)), "gemm_fp8_fmt")
     return C
 
 
@@ -164,6 +193,36 @@ def quantize_fp8(x, scale, q=None, stream=None):
         raise ValueError("q must have as many elements as x")
     _check(lib().quantize_fp8(_ptr(x), x.numel(), _ptr(scale), _ptr(qv), _stream_handle(stream)), "quantize_fp8")
     return q
+
+
+def quantize_fp8_fmt(x, scale, fmt, q=None, stream=None):
+    """FP8 codes (format fmt) of x / scale (uint8, same shape as x)."""
+    torch = _torch()
+    if x.dtype != torch.float32:
+        raise ValueError("quantize_fp8_fmt takes float32 input")
+    if q is None:
+        q = torch.empty(x.shape, dtype=torch.uint8, device=x.device)
+    qv = _u8(q)
+    if qv.numel() != x.numel():
+        raise ValueError("q must have as many elements as x")
+    _check(lib().quantize_fp8_fmt(_ptr(x), x.numel(), _ptr(scale), _ptr(qv), int(fmt), _stream_handle(stream)),
+           "quantize_fp8_fmt")
+    return q
+
+
+def amax_scale_f32(x, fmt, pow2, amax=None, scale=None, stream=None):
+    """(amax, scale) with the scale for FP8 format fmt: amax / fmax, or with pow2
+    the smallest power of two s with amax / s <= fmax."""
+    torch = _torch()
+    if x.dtype != torch.float32:
+        raise ValueError("amax_scale_f32 takes float32 input")
+    if amax is None:
+        amax = torch.empty(1, dtype=torch.float32, device=x.device)
+    if scale is None:
+        scale = torch.empty(1, dtype=torch.float32, device=x.device)
+    _check(lib().amax_scale_f32(_ptr(x), x.numel(), _ptr(amax), _ptr(scale), int(fmt), 1 if pow2 else 0,
+                                _stream_handle(stream)), "amax_scale_f32")
+    return amax, scale
 
 
 def amax_f32(x, amax=None, scale=None, stream=None):
@@ -182,4 +241,11 @@ def amax_f32(x, amax=None, scale=None, stream=None):
 def select_config(kind: int, out_dtype: int, M: int, N: int, K: int) -> str:
     buf = ctypes.create_string_buffer(128)
     _check(lib().gemm_select_config(kind, out_dtype, M, N, K, buf, len(buf)), "gemm_select_config")
+    return buf.value.decode()
+
+
+def select_config_fmt(kind: int, out_dtype: int, M: int, N: int, K: int, fmt_a: int, fmt_b: int) -> str:
+    buf = ctypes.create_string_buffer(128)
+    _check(lib().gemm_select_config_fmt(kind, out_dtype, M, N, K, int(fmt_a), int(fmt_b), buf, len(buf)),
+           "gemm_select_config_fmt")
     return buf.value.decode()

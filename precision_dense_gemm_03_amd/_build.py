@@ -16,7 +16,8 @@ INCLUDE = os.path.join(ROOT, "include")
 BUILD = os.path.join(PKG, "_build")
 LIB = os.path.join(PKG, "libgemm.so")
 
-SOURCES = ["abi.cpp", "selector.cpp", "amax_quant.hip", "gemm_tile.hip", "gemm_dma.hip", "gemm_stream.hip"]
+SOURCES = ["abi.cpp", "selector.cpp", "amax_quant.hip", "gemm_tile.hip", "gemm_tile_mixed.hip", "gemm_dma.hip",
+           "gemm_dma_mixed.hip", "gemm_stream.hip"]
 
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 
@@ -26,7 +27,7 @@ FLAGS = [
     "-O3", "-std=c++17", "-fPIC", "--offload-arch=gfx950",
     "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
     "-fhip-fp32-correctly-rounded-divide-sqrt", "-fno-fast-math",
-    "-Wall", "-Wno-unused-function", "-Wno-unused-command-line-argument",
+    "-Wall", "-Wno-unused-function", "-Wno-unused-command-line-argument", "-Wno-inline-asm",
     "-I", CSRC, "-I", INCLUDE,
 ]
 

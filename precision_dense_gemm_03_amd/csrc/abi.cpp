@@ -59,12 +59,14 @@ int status_of(hipError_t e) {
     return GEMM_ERR_LAUNCH;
 }
 
+bool fp8_out(int out_dtype) { return out_dtype == GEMM_OUT_E4M3 || out_dtype == GEMM_OUT_E5M2; }
+
 int run_gemm(int kind, const GemmArgs& a) {
     int st = check_device();
     if (st != GEMM_OK) return st;
     if (a.M == 0 || a.N == 0) return GEMM_OK;
     if (a.K == 0) return status_of(launch_fill_zero(a.C, a.M * a.N, a.out_dtype, a.stream));
-    const GemmConfig* cfg = select_config(kind, a.out_dtype, a.M, a.N, a.K);
+    const GemmConfig* cfg = select_config(kind, a.out_dtype, a.M, a.N, a.K, a.fmt_a, a.fmt_b);
     if (!cfg) return GEMM_ERR_UNSUPPORTED;
     return status_of(cfg->launch(a));
 }
@@ -87,36 +89,55 @@ int gemm_f16(const void* A, const void* B, void* C, int out_dtype, int64_t M, in
     return run_gemm(KIND_F16, a);
 }
 
-int gemm_fp8_scaled(const uint8_t* A, const uint8_t* B, const float* sA, const float* sB, const float* sOut,
-                    void* C, int out_dtype, int64_t M, int64_t N, int64_t K, hipStream_t stream) {
-    if (out_dtype != GEMM_OUT_F32 && out_dtype != GEMM_OUT_F16 && out_dtype != GEMM_OUT_E4M3)
+// Shared by gemm_fp8_scaled and gemm_fp8_fmt: validation, then the launch.
+static int gemm_fp8_common(const uint8_t* A, int fmt_a, const uint8_t* B, int fmt_b, const float* sA,
+                           const float* sB, const float* sOut, void* C, int out_dtype, int64_t M, int64_t N,
+                           int64_t K, hipStream_t stream) {
+    if (out_dtype < GEMM_OUT_F32 || out_dtype > GEMM_OUT_E5M2) return GEMM_ERR_DTYPE;
+    if ((fmt_a != GEMM_FMT_E4M3 && fmt_a != GEMM_FMT_E5M2) || (fmt_b != GEMM_FMT_E4M3 && fmt_b != GEMM_FMT_E5M2))
         return GEMM_ERR_DTYPE;
     if (!dim_ok(M) || !dim_ok(N) || !dim_ok(K)) return GEMM_ERR_DIM;
     if (M > 0 && N > 0) {
         if (!C || !sA || !sB) return GEMM_ERR_NULL;
-        if (out_dtype == GEMM_OUT_E4M3 && !sOut) return GEMM_ERR_SCALE;
+        if (fp8_out(out_dtype) && !sOut) return GEMM_ERR_SCALE;
         if (K > 0 && (!A || !B)) return GEMM_ERR_NULL;
         const int64_t cbytes = M * N * out_size(out_dtype);
         if (K > 0 && (overlaps(C, cbytes, A, M * K) || overlaps(C, cbytes, B, K * N))) return GEMM_ERR_ALIAS;
         if (overlaps(C, cbytes, sA, 4) || overlaps(C, cbytes, sB, 4) ||
-            (out_dtype == GEMM_OUT_E4M3 && overlaps(C, cbytes, sOut, 4)))
+            (fp8_out(out_dtype) && overlaps(C, cbytes, sOut, 4)))
             return GEMM_ERR_ALIAS;
     }
-    GemmArgs a{A, B, C, sA, sB, out_dtype == GEMM_OUT_E4M3 ? sOut : nullptr, out_dtype, M, N, K, stream};
+    GemmArgs a{A, B, C, sA, sB, fp8_out(out_dtype) ? sOut : nullptr, out_dtype, M, N, K, stream, fmt_a, fmt_b};
     return run_gemm(KIND_FP8, a);
 }
 
-int quantize_fp8(const float* x, int64_t n, const float* scale, uint8_t* q, hipStream_t stream) {
+int gemm_fp8_scaled(const uint8_t* A, const uint8_t* B, const float* sA, const float* sB, const float* sOut,
+                    void* C, int out_dtype, int64_t M, int64_t N, int64_t K, hipStream_t stream) {
+    return gemm_fp8_common(A, GEMM_FMT_E4M3, B, GEMM_FMT_E4M3, sA, sB, sOut, C, out_dtype, M, N, K, stream);
+}
+
+int gemm_fp8_fmt(const uint8_t* A, int fmt_a, const uint8_t* B, int fmt_b, const float* sA, const float* sB,
+                 const float* sOut, void* C, int out_dtype, int64_t M, int64_t N, int64_t K, hipStream_t stream) {
+    return gemm_fp8_common(A, fmt_a, B, fmt_b, sA, sB, sOut, C, out_dtype, M, N, K, stream);
+}
+
+int quantize_fp8_fmt(const float* x, int64_t n, const float* scale, uint8_t* q, int fmt, hipStream_t stream) {
+    if (fmt != GEMM_FMT_E4M3 && fmt != GEMM_FMT_E5M2) return GEMM_ERR_DTYPE;
     if (n < 0) return GEMM_ERR_DIM;
     if (n == 0) return GEMM_OK;
     if (!x || !scale || !q) return GEMM_ERR_NULL;
     if (overlaps(q, n, x, 4 * n) || overlaps(q, n, scale, 4)) return GEMM_ERR_ALIAS;
     const int st = check_device();
     if (st != GEMM_OK) return st;
-    return status_of(launch_quantize(x, n, scale, q, stream));
+    return status_of(launch_quantize(x, n, scale, q, fmt, stream));
 }
 
-int amax_f32(const float* x, int64_t n, float* amax, float* scale, hipStream_t stream) {
+int quantize_fp8(const float* x, int64_t n, const float* scale, uint8_t* q, hipStream_t stream) {
+    return quantize_fp8_fmt(x, n, scale, q, GEMM_FMT_E4M3, stream);
+}
+
+int amax_scale_f32(const float* x, int64_t n, float* amax, float* scale, int fmt, int pow2, hipStream_t stream) {
+    if (fmt != GEMM_FMT_E4M3 && fmt != GEMM_FMT_E5M2) return GEMM_ERR_DTYPE;
     if (n < 0) return GEMM_ERR_DIM;
     if (!amax) return GEMM_ERR_NULL;
     if (n > 0 && !x) return GEMM_ERR_NULL;
@@ -124,7 +145,11 @@ int amax_f32(const float* x, int64_t n, float* amax, float* scale, hipStream_t s
         return GEMM_ERR_ALIAS;
     const int st = check_device();
     if (st != GEMM_OK) return st;
-    return status_of(launch_amax(x, n, amax, scale, stream));
+    return status_of(launch_amax(x, n, amax, scale, fmt, pow2 ? 1 : 0, stream));
+}
+
+int amax_f32(const float* x, int64_t n, float* amax, float* scale, hipStream_t stream) {
+    return amax_scale_f32(x, n, amax, scale, GEMM_FMT_E4M3, 0, stream);
 }
 
 const char* gemm_status_str(int status) {
@@ -133,7 +158,7 @@ const char* gemm_status_str(int status) {
         case GEMM_ERR_NULL: return "a required pointer is NULL";
         case GEMM_ERR_DIM: return "a dimension is negative or above 2^31-1";
         case GEMM_ERR_DTYPE: return "unsupported output dtype";
-        case GEMM_ERR_SCALE: return "sOut is required for E4M3 output";
+        case GEMM_ERR_SCALE: return "sOut is required for FP8 output";
         case GEMM_ERR_LAUNCH: return "kernel launch failed";
         case GEMM_ERR_UNSUPPORTED: return "no kernel for this request";
         case GEMM_ERR_DEVICE: return "no current HIP device, or it is not gfx950";
@@ -142,16 +167,23 @@ const char* gemm_status_str(int status) {
     }
 }
 
-int gemm_select_config(int kind, int out_dtype, int64_t M, int64_t N, int64_t K, char* buf, int buflen) {
+int gemm_select_config_fmt(int kind, int out_dtype, int64_t M, int64_t N, int64_t K, int fmt_a, int fmt_b,
+                           char* buf, int buflen) {
     if (kind != KIND_F16 && kind != KIND_FP8) return GEMM_ERR_DTYPE;
-    if (out_dtype < GEMM_OUT_F32 || out_dtype > GEMM_OUT_E4M3 || (kind == KIND_F16 && out_dtype == GEMM_OUT_E4M3))
+    if (out_dtype < GEMM_OUT_F32 || out_dtype > GEMM_OUT_E5M2 || (kind == KIND_F16 && fp8_out(out_dtype)))
+        return GEMM_ERR_DTYPE;
+    if ((fmt_a != GEMM_FMT_E4M3 && fmt_a != GEMM_FMT_E5M2) || (fmt_b != GEMM_FMT_E4M3 && fmt_b != GEMM_FMT_E5M2))
         return GEMM_ERR_DTYPE;
     if (!dim_ok(M) || !dim_ok(N) || !dim_ok(K)) return GEMM_ERR_DIM;
     if (!buf || buflen <= 0) return GEMM_ERR_NULL;
-    const GemmConfig* cfg = select_config(kind, out_dtype, M, N, K);
+    const GemmConfig* cfg = select_config(kind, out_dtype, M, N, K, fmt_a, fmt_b);
     if (!cfg) return GEMM_ERR_UNSUPPORTED;
     std::snprintf(buf, (size_t)buflen, "%s", cfg->name);
     return GEMM_OK;
+}
+
+int gemm_select_config(int kind, int out_dtype, int64_t M, int64_t N, int64_t K, char* buf, int buflen) {
+    return gemm_select_config_fmt(kind, out_dtype, M, N, K, GEMM_FMT_E4M3, GEMM_FMT_E4M3, buf, buflen);
 }
 
 }  // extern "C"

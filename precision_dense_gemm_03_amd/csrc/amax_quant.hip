@@ -86,13 +86,15 @@ __global__ __launch_bounds__(kThreads) void amax_reduce_kernel(const float* __re
     }
 }
 
-__global__ void amax_finalize_kernel(const uint32_t* amax_bits, float* scale) {
-    *scale = scale_from_amax(bits_f32(*amax_bits));
+__global__ void amax_finalize_kernel(const uint32_t* amax_bits, float* scale, int fmt, int pow2) {
+    *scale = scale_for_format(bits_f32(*amax_bits), fmt, pow2);
 }
 
-// q = E4M3(fl32(x / s)). The FP32 division is the IEEE correctly rounded one.
+// q = FP8(fl32(x / s)) in format FMT (E4M3 or E5M2). The FP32 division is the
+// IEEE correctly rounded one.
 // Each thread turns 4 floats (one 16-byte load) into one 32-bit word of codes,
 // so a wave instruction reads 1 KiB and writes 256 bytes, both contiguous.
+template <int FMT>
 __global__ __launch_bounds__(kThreads) void quantize_kernel(const float* __restrict__ x, int64_t n,
                                                             const float* __restrict__ scale,
                                                             uint8_t* __restrict__ q, int vec) {
@@ -112,12 +114,13 @@ __global__ __launch_bounds__(kThreads) void quantize_kernel(const float* __restr
 #pragma unroll
             for (int j = 0; j < kUnroll; ++j)
                 if (i + j * nthreads < n4)
-                    __builtin_nontemporal_store(e4m3_pack4(v[j].x / s, v[j].y / s, v[j].z / s, v[j].w / s),
+                    __builtin_nontemporal_store(fp8_pack4<FMT>(v[j].x / s, v[j].y / s, v[j].z / s, v[j].w / s),
                                                 &q4[i + j * nthreads]);
         }
         done = n4 * 4;
     }
-    for (int64_t i = done + tid; i < n; i += nthreads) q[i] = e4m3_from_f32(x[i] / s);
+    for (int64_t i = done + tid; i < n; i += nthreads)
+        q[i] = FMT == FMT_E5M2 ? e5m2_from_f32(x[i] / s) : e4m3_from_f32(x[i] / s);
 }
 
 __global__ __launch_bounds__(kThreads) void fill_zero_kernel(uint8_t* C, int64_t nbytes) {
@@ -137,7 +140,7 @@ bool aligned16(const void* p) { return ((uintptr_t)p & 15u) == 0; }
 
 }  // namespace
 
-hipError_t launch_amax(const float* x, int64_t n, float* amax, float* scale, hipStream_t stream) {
+hipError_t launch_amax(const float* x, int64_t n, float* amax, float* scale, int fmt, int pow2, hipStream_t stream) {
     uint32_t* bits = reinterpret_cast<uint32_t*>(amax);
     amax_init_kernel<<<1, 1, 0, stream>>>(bits);
     if (n > 0) {
@@ -145,20 +148,21 @@ hipError_t launch_amax(const float* x, int64_t n, float* amax, float* scale, hip
         const int grid = grid_for(vec ? (n / 4 + kUnroll - 1) / kUnroll : n, 512);
         amax_reduce_kernel<<<grid, kThreads, 0, stream>>>(x, n, bits, vec);
     }
-    if (scale) amax_finalize_kernel<<<1, 1, 0, stream>>>(bits, scale);
+    if (scale) amax_finalize_kernel<<<1, 1, 0, stream>>>(bits, scale, fmt, pow2);
     return hipGetLastError();
 }
 
-hipError_t launch_quantize(const float* x, int64_t n, const float* scale, uint8_t* q, hipStream_t stream) {
+hipError_t launch_quantize(const float* x, int64_t n, const float* scale, uint8_t* q, int fmt, hipStream_t stream) {
     if (n <= 0) return hipSuccess;
     const int vec = (aligned16(x) && ((uintptr_t)q & 3u) == 0) ? 1 : 0;
     const int grid = grid_for(vec ? (n / 4 + kUnroll - 1) / kUnroll : n, 4096);
-    quantize_kernel<<<grid, kThreads, 0, stream>>>(x, n, scale, q, vec);
+    if (fmt == FMT_E5M2) quantize_kernel<FMT_E5M2><<<grid, kThreads, 0, stream>>>(x, n, scale, q, vec);
+    else quantize_kernel<FMT_E4M3><<<grid, kThreads, 0, stream>>>(x, n, scale, q, vec);
     return hipGetLastError();
 }
 
 hipError_t launch_fill_zero(void* C, int64_t count, int out_dtype, hipStream_t stream) {
-    const int64_t es = out_dtype == OUT_F32 ? 4 : (out_dtype == OUT_F16 ? 2 : 1);
+    const int64_t es = out_dtype == OUT_F32 ? 4 : (out_dtype == OUT_F16 ? 2 : 1);  // FP8 outputs: 1 byte
     const int64_t nbytes = count * es;
     if (nbytes <= 0) return hipSuccess;
     fill_zero_kernel<<<grid_for(nbytes, 256 * 8), kThreads, 0, stream>>>(reinterpret_cast<uint8_t*>(C), nbytes);

@@ -21,7 +21,10 @@ typedef float v16f __attribute__((ext_vector_type(16)));
 
 #define LDS_AS __attribute__((address_space(3)))
 
-enum OutDtype { OUT_F32 = 0, OUT_F16 = 1, OUT_E4M3 = 2 };
+enum OutDtype { OUT_F32 = 0, OUT_F16 = 1, OUT_E4M3 = 2, OUT_E5M2 = 3 };
+
+// FP8 element formats (operands and quantize): OCP E4M3 ("FN") and OCP E5M2.
+enum Fp8Format { FMT_E4M3 = 0, FMT_E5M2 = 1 };
 
 // E4M3 (OCP "FN" variant) code of an FP32 value: round to nearest, ties to the
 // even code; |w| >= 448 and +-inf saturate to +-448 (0x7E / 0xFE); NaN -> 0x7F.
@@ -43,6 +46,33 @@ __device__ __forceinline__ uint32_t e4m3_pack4(float a, float b, float c, float 
 
 __device__ __forceinline__ uint8_t e4m3_from_f32(float w) { return (uint8_t)(e4m3_pack2(w, 0.0f) & 0xFFu); }
 
+// E5M2 code of an FP32 value: round to nearest, ties to the even code;
+// |w| >= 57344 and +-inf saturate to +-57344 (0x7B / 0xFB); NaN -> 0x7F. The
+// value is clamped before v_cvt_pk_bf8_f32 (which would otherwise round large
+// values to inf); the NaN test comes first, as for E4M3.
+__device__ __forceinline__ uint32_t e5m2_pack2(float a, float b) {
+    float ca = fminf(fmaxf(a, -57344.0f), 57344.0f);
+    float cb = fminf(fmaxf(b, -57344.0f), 57344.0f);
+    uint32_t pk = (uint32_t)__builtin_amdgcn_cvt_pk_bf8_f32(ca, cb, 0, false) & 0xFFFFu;
+    if (a != a) pk = (pk & 0xFF00u) | 0x7Fu;
+    if (b != b) pk = (pk & 0x00FFu) | 0x7F00u;
+    return pk;
+}
+
+__device__ __forceinline__ uint32_t e5m2_pack4(float a, float b, float c, float d) {
+    return e5m2_pack2(a, b) | (e5m2_pack2(c, d) << 16);
+}
+
+__device__ __forceinline__ uint8_t e5m2_from_f32(float w) { return (uint8_t)(e5m2_pack2(w, 0.0f) & 0xFFu); }
+
+template <int FMT>
+__device__ __forceinline__ uint32_t fp8_pack4(float a, float b, float c, float d) {
+    return FMT == FMT_E5M2 ? e5m2_pack4(a, b, c, d) : e4m3_pack4(a, b, c, d);
+}
+
+// Largest finite value of an FP8 format (E4M3 448, E5M2 57344).
+__device__ __forceinline__ float fp8_max(int fmt) { return fmt == FMT_E5M2 ? 57344.0f : 448.0f; }
+
 // Per-tensor scale from amax: fl32(amax / 448), and 1 when that is zero.
 // Division is IEEE correctly rounded (the library is built without fast-math
 // and with correctly rounded FP32 divide).
@@ -51,18 +81,41 @@ __device__ __forceinline__ float scale_from_amax(float a) {
     return (s == 0.0f) ? 1.0f : s;
 }
 
+// Scale of amax a for an FP8 format. pow2 == 0: fl32(a / fmax), 1 when that is
+// 0. pow2 != 0: the smallest power of two s with a / s <= fmax, not below
+// 2^-149; 0 -> 1, inf -> inf, NaN -> NaN. With a = ma * 2^ea and fmax =
+// mf * 2^ef (mantissas in [0.5, 1)), a / fmax lies in (2^(ea-ef-1), 2^(ea-ef)]
+// when ma <= mf and in (2^(ea-ef), 2^(ea-ef+1)) otherwise; both comparisons
+// and the exponent arithmetic are exact.
+__device__ __forceinline__ float scale_for_format(float a, int fmt, int pow2) {
+    const float fmax = fp8_max(fmt);
+    if (!pow2) {
+        const float s = a / fmax;
+        return (s == 0.0f) ? 1.0f : s;
+    }
+    if (a != a) return a;
+    if (a == 0.0f) return 1.0f;
+    if (__builtin_isinf(a)) return a;
+    int ea, ef;
+    const float ma = __builtin_frexpf(a, &ea);
+    const float mf = __builtin_frexpf(fmax, &ef);
+    int e = ea - ef + (ma > mf ? 1 : 0);
+    if (e < -149) e = -149;
+    return __builtin_ldexpf(1.0f, e);
+}
+
 __device__ __forceinline__ uint32_t f32_bits(float x) { return __builtin_bit_cast(uint32_t, x); }
 __device__ __forceinline__ float bits_f32(uint32_t u) { return __builtin_bit_cast(float, u); }
 
 // Multiplier applied to the FP32 accumulator in every epilogue: sA*sB, and
-// for E4M3 output sA*sB / sOut, so that the result is y = acc * m. Folding
+// for FP8 output sA*sB / sOut, so that the result is y = acc * m. Folding
 // the output scale into one factor instead of dividing every element by sOut
 // changes y by at most a few FP32 ulps, well inside the one-code-step
-// tolerance of an E4M3 output.
+// tolerance of an FP8 output.
 __device__ __forceinline__ float epilogue_multiplier(const float* sA, const float* sB, const float* sOut,
-                                                     bool e4m3_out) {
+                                                     bool fp8_out) {
     const float s = (sA ? *sA : 1.0f) * (sB ? *sB : 1.0f);
-    return e4m3_out ? s / *sOut : s;
+    return fp8_out ? s / *sOut : s;
 }
 
 // Stores one output element of the final value y (already multiplied by the
@@ -72,6 +125,8 @@ __device__ __forceinline__ void store_out(void* C, int64_t idx, float y, int out
         reinterpret_cast<float*>(C)[idx] = y;
     } else if (out_dtype == OUT_F16) {
         reinterpret_cast<_Float16*>(C)[idx] = (_Float16)y;
+    } else if (out_dtype == OUT_E5M2) {
+        reinterpret_cast<uint8_t*>(C)[idx] = e5m2_from_f32(y);
     } else {
         reinterpret_cast<uint8_t*>(C)[idx] = e4m3_from_f32(y);
     }

@@ -21,7 +21,14 @@ namespace libgemm {
 
 namespace {
 
-template <int ES>
+// Two FP8 codes (the low or high half HI of a 32-bit word) to floats, in format F.
+template <int F, bool HI>
+__device__ __forceinline__ auto fp8x2_to_f32(uint32_t w) {
+    if constexpr (F == FMT_E5M2) return __builtin_amdgcn_cvt_pk_f32_bf8((int)w, HI);
+    else return __builtin_amdgcn_cvt_pk_f32_fp8((int)w, HI);
+}
+
+template <int ES, int F>
 __device__ __forceinline__ void decode16(const v4u& v, float (&out)[16 / ES]) {
     if constexpr (ES == 2) {
         const v8h h = __builtin_bit_cast(v8h, v);
@@ -31,8 +38,8 @@ __device__ __forceinline__ void decode16(const v4u& v, float (&out)[16 / ES]) {
         const uint32_t w[4] = {v.x, v.y, v.z, v.w};
 #pragma unroll
         for (int q = 0; q < 4; ++q) {
-            auto lo = __builtin_amdgcn_cvt_pk_f32_fp8((int)w[q], false);
-            auto hi = __builtin_amdgcn_cvt_pk_f32_fp8((int)w[q], true);
+            auto lo = fp8x2_to_f32<F, false>(w[q]);
+            auto hi = fp8x2_to_f32<F, true>(w[q]);
             out[4 * q + 0] = lo[0];
             out[4 * q + 1] = lo[1];
             out[4 * q + 2] = hi[0];
@@ -41,12 +48,12 @@ __device__ __forceinline__ void decode16(const v4u& v, float (&out)[16 / ES]) {
     }
 }
 
-template <int ES>
+template <int ES, int F>
 __device__ __forceinline__ float decode1(const uint8_t* p, int64_t idx) {
     if constexpr (ES == 2) {
         return (float)reinterpret_cast<const _Float16*>(p)[idx];
     } else {
-        auto v = __builtin_amdgcn_cvt_pk_f32_fp8((int)p[idx], false);
+        auto v = fp8x2_to_f32<F, false>((uint32_t)p[idx]);
         return v[0];
     }
 }
@@ -55,7 +62,7 @@ __device__ __forceinline__ float decode1(const uint8_t* p, int64_t idx) {
 // CX = COLS / VE chunks across, KY = NT / CX slices down. Lane order inside a
 // wave is cx fastest, so one wave covers (64 / CX) slices of a full
 // COLS-wide row segment.
-template <int ES, int MMAX, int COLS, int NT, int U>
+template <int ES, int MMAX, int COLS, int NT, int U, int FA, int FB>
 __global__ __launch_bounds__(NT) void gemm_stream_kernel(const uint8_t* __restrict__ A,
                                                          const uint8_t* __restrict__ B, void* __restrict__ C,
                                                          int64_t M, int64_t N, int64_t K,
@@ -128,8 +135,8 @@ __global__ __launch_bounds__(NT) void gemm_stream_kernel(const uint8_t* __restri
                             const uint32_t ww[2] = {w.x, w.y};
 #pragma unroll
                             for (int q = 0; q < 2; ++q) {
-                                auto lo = __builtin_amdgcn_cvt_pk_f32_fp8((int)ww[q], false);
-                                auto hi = __builtin_amdgcn_cvt_pk_f32_fp8((int)ww[q], true);
+                                auto lo = fp8x2_to_f32<FA, false>(ww[q]);
+                                auto hi = fp8x2_to_f32<FA, true>(ww[q]);
                                 a[m][8 * g8 + 4 * q + 0] = lo[0];
                                 a[m][8 * g8 + 4 * q + 1] = lo[1];
                                 a[m][8 * g8 + 4 * q + 2] = hi[0];
@@ -139,7 +146,7 @@ __global__ __launch_bounds__(NT) void gemm_stream_kernel(const uint8_t* __restri
                     }
                 } else {
 #pragma unroll
-                    for (int u = 0; u < U; ++u) a[m][u] = (kb + u < K) ? decode1<ES>(A, m * K + kb + u) : 0.0f;
+                    for (int u = 0; u < U; ++u) a[m][u] = (kb + u < K) ? decode1<ES, FA>(A, m * K + kb + u) : 0.0f;
                 }
             } else {
 #pragma unroll
@@ -149,7 +156,7 @@ __global__ __launch_bounds__(NT) void gemm_stream_kernel(const uint8_t* __restri
 #pragma unroll
         for (int u = 0; u < U; ++u) {
             float b[VE];
-            decode16<ES>(braw[u], b);
+            decode16<ES, FB>(braw[u], b);
 #pragma unroll
             for (int m = 0; m < MMAX; ++m)
 #pragma unroll
@@ -175,7 +182,7 @@ __global__ __launch_bounds__(NT) void gemm_stream_kernel(const uint8_t* __restri
             for (int e = 0; e < VE; ++e) red[wave][m][lane * VE + e] = acc[m][e];
     }
     __syncthreads();
-    const float scale = epilogue_multiplier(sA, sB, sOut, out_dtype == OUT_E4M3);
+    const float scale = epilogue_multiplier(sA, sB, sOut, out_dtype == OUT_E4M3 || out_dtype == OUT_E5M2);
 
     for (int o = tid; o < MMAX * COLS; o += NT) {
         const int m = o / COLS, c = o % COLS;
@@ -190,17 +197,28 @@ __global__ __launch_bounds__(NT) void gemm_stream_kernel(const uint8_t* __restri
 
 bool aligned16(const void* p) { return ((uintptr_t)p & 15u) == 0; }
 
-template <int ES, int MMAX, int COLS, int NT, int U>
+template <int ES, int MMAX, int COLS, int NT, int U, int FA = 0, int FB = 0>
 hipError_t launch_stream(const GemmArgs& a) {
     const int64_t blocks = (a.N + COLS - 1) / COLS;
     if (blocks <= 0 || a.M <= 0) return hipSuccess;
     if (blocks > 0x7FFFFFFF || a.M > MMAX) return hipErrorInvalidValue;
     const int a_vec = aligned16(a.A) && ((a.K * ES) % 16 == 0);
     const int b_vec = aligned16(a.B) && ((a.N * ES) % 16 == 0);
-    gemm_stream_kernel<ES, MMAX, COLS, NT, U><<<(unsigned)blocks, NT, 0, a.stream>>>(
+    gemm_stream_kernel<ES, MMAX, COLS, NT, U, FA, FB><<<(unsigned)blocks, NT, 0, a.stream>>>(
         reinterpret_cast<const uint8_t*>(a.A), reinterpret_cast<const uint8_t*>(a.B), a.C, a.M, a.N, a.K, a.sA,
         a.sB, a.sOut, a.out_dtype, a_vec, b_vec);
     return hipGetLastError();
+}
+
+// FP8 operand-format dispatch.
+template <int MMAX, int COLS, int NT, int U>
+hipError_t launch_stream_fp8_any(const GemmArgs& a) {
+    switch (a.fmt_a * 2 + a.fmt_b) {
+        case 0: return launch_stream<1, MMAX, COLS, NT, U, 0, 0>(a);
+        case 1: return launch_stream<1, MMAX, COLS, NT, U, 0, 1>(a);
+        case 2: return launch_stream<1, MMAX, COLS, NT, U, 1, 0>(a);
+        default: return launch_stream<1, MMAX, COLS, NT, U, 1, 1>(a);
+    }
 }
 
 }  // namespace
@@ -214,8 +232,8 @@ const GemmConfig* stream_configs(int* count) {
     {"stream_f16_m4_c64_t512", KIND_F16, 1, 4, 64, 512, launch_stream<2, 4, 64, 512, 8>},
     {"stream_f16_m8_c64_t256", KIND_F16, 1, 8, 64, 256, launch_stream<2, 8, 64, 256, 8>},
     {"stream_f16_m16_c64_t256", KIND_F16, 1, 16, 64, 256, launch_stream<2, 16, 64, 256, 8>},
-    {"stream_fp8_m1_c64_t1024", KIND_FP8, 1, 1, 64, 1024, launch_stream<1, 1, 64, 1024, 8>},
-    {"stream_fp8_m4_c64_t512", KIND_FP8, 1, 4, 64, 512, launch_stream<1, 4, 64, 512, 8>},
+    {"stream_fp8_m1_c64_t1024", KIND_FP8, 1, 1, 64, 1024, launch_stream_fp8_any<1, 64, 1024, 8>, kAllFp8Pairs},
+    {"stream_fp8_m4_c64_t512", KIND_FP8, 1, 4, 64, 512, launch_stream_fp8_any<4, 64, 512, 8>, kAllFp8Pairs},
     };
     *count = (int)(sizeof(table) / sizeof(table[0]));
     return table;

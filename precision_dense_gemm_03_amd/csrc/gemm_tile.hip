@@ -1,458 +1,29 @@
-// MFMA tile GEMM for gfx950: C[M,N] = (sA*A[M,K]) (sB*B[K,N]), all row-major.
-//
-// Operands are FP16 (v_mfma_f32_16x16x32_f16) or OCP E4M3 codes
-// (v_mfma_scale_f32_16x16x128_f8f6f4 with neutral block scales), always with
-// FP32 accumulation ("DeepGEMM实战：FP8矩阵乘法与JIT编译优化指南" §2.1;
-// "HGEMM优化：深度学习中的矩阵乘法性能提升策略" §1.3).
-//
-// Data flow per workgroup (one BM x BN output tile, 4 waves in a 2 x 2 grid):
-//   HBM/L2 --16-byte coalesced loads--> registers --ds_write_b128--> LDS
-//   (two LDS stages plus one register stage: tile k+2 is in flight while
-//   tile k is multiplied; FP8 guide §2.3 "double buffering", HGEMM §3.2/§3.3
-//   on prefetch depth)
-//   LDS --ds_read_b128 (A) / ds_read_b64_tr_b16|b8 (B)--> MFMA operands
-// A is row-major [M,K]: its K-contiguous rows are exactly the MFMA A operand.
-// B is row-major [K,N]: N is contiguous, so the B operand (8 or 32 consecutive
-// k for one column per lane) comes from gfx950's LDS transpose reads instead of
-// a transposing copy. LDS rows are padded (A: +16 B, B: +16/32 B) so that the
-// lanes served by one LDS pass hit distinct banks (the bank-aware layout the
-// DeepGEMM deep-dive article, §3.2, argues for).
-//
-// Edges (FP8 guide §3.3): rows >= M and columns >= N are neither loaded nor
-// stored, the K tail is zero-filled in the staged tile, so one kernel serves
-// every shape. Interior tiles take a branch-free path; only edge tiles (and
-// unaligned operands) run the guarded element loads. The epilogue multiplies
-// by sA*sB once and converts to the output type, which is a template
-// parameter so that every accumulator index is a compile-time constant and
-// the accumulators stay in registers.
-//
-// Tile order: consecutive workgroups are dispatched round-robin over the 8
-// XCDs, each with its own L2. Workgroup ids are remapped so that every XCD
-// receives a compact block of tiles (shared A row-blocks and B column-blocks
-// stay in one L2), walked in groups of 4 tile rows.
-#include "device_common.h"
-#include "kernels.h"
-#include "tile_order.h"
+// MFMA tile GEMM for gfx950 (register-staged loads): the configuration table
+// and the E4M3 x E4M3 and FP16 instantiations. The kernel itself, its data
+// flow and its citations are in gemm_tile_impl.h.
+#include "gemm_tile_impl.h"
 
 namespace libgemm {
-
-namespace {
-
-// The fully register-pipelined loop (two B operand sets) needs more registers
-// than a 256x256 tile leaves; it stays compiled out until it fits.
-constexpr bool kRegisterPipeline = false;
-
-template <int ES, int BM, int BN, int BK, int WM, int WN>
-struct Tile {
-    static constexpr int NT = 64 * WM * WN;           // threads per workgroup
-    static constexpr int KPI = ES == 2 ? 32 : 128;    // k per MFMA instruction
-    static constexpr int OPB = ES == 2 ? 16 : 32;     // operand bytes per lane
-    static constexpr int VE = 16 / ES;                // elements per 16-byte chunk
-    static constexpr int BKB = BK * ES;               // bytes of one A tile row
-    static constexpr int BNB = BN * ES;               // bytes of one B tile row
-    static constexpr int SA = BKB + 16;               // padded LDS row strides
-    static constexpr int SB = BNB + (ES == 2 ? 32 : 16);
-    static constexpr int A_BYTES = BM * SA;
-    static constexpr int B_BYTES = BK * SB;
-    static constexpr int STAGE = A_BYTES + B_BYTES;
-    static constexpr int A_CPR = BKB / 16;            // 16-byte chunks per A row
-    static constexpr int B_CPR = BNB / 16;
-    static constexpr int A_RPP = NT / A_CPR;          // A rows covered per pass of all threads
-    static constexpr int B_RPP = NT / B_CPR;
-    static constexpr int CA = BM / A_RPP;             // A chunks per thread
-    static constexpr int CB = BK / B_RPP;
-    static constexpr int WTM = BM / WM, WTN = BN / WN;
-    static constexpr int TM = WTM / 16, TN = WTN / 16;
-    static constexpr int KS = BK / KPI;
-    static_assert(BK % KPI == 0, "BK must be a multiple of the MFMA depth");
-    static_assert(NT % A_CPR == 0 && NT % B_CPR == 0, "chunk rows must tile the workgroup");
-    static_assert(BM % A_RPP == 0 && BK % B_RPP == 0, "tile chunks must divide evenly");
-    static_assert(WTM % 16 == 0 && WTN % 16 == 0, "wave tile must be whole 16x16 blocks");
-    static_assert(2 * STAGE <= 160 * 1024, "two stages must fit in LDS");
-    // LDS map: A stage 0, A stage 1, B stage 0, B stage 1
-    static constexpr int a_stage(int s) { return s * A_BYTES; }
-    static constexpr int b_stage(int s) { return 2 * A_BYTES + s * B_BYTES; }
-};
-
-// MFMA operand type, LDS operand reads and the multiply for each element size.
-template <int ES>
-struct Operand;
-
-template <>
-struct Operand<2> {  // FP16: v_mfma_f32_16x16x32_f16, 8 halves per lane
-    typedef v8h type;
-    static __device__ __forceinline__ v8h read_a(const LDS_AS uint8_t* p) {
-        return __builtin_bit_cast(v8h, *(const LDS_AS v4u*)p);
-    }
-    // two transpose reads give k = 8g + 0..3 and 8g + 4..7 of one column
-    static __device__ __forceinline__ v8h read_b(const LDS_AS uint8_t* p, int sb) {
-        const v4s lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((LDS_AS v4s*)p);
-        const v4s hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((LDS_AS v4s*)(p + 4 * sb));
-        return __builtin_bit_cast(v8h, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
-    }
-    static __device__ __forceinline__ v4f mma(v8h a, v8h b, v4f c) {
-        return __builtin_amdgcn_mfma_f32_16x16x32_f16(a, b, c, 0, 0, 0);
-    }
-};
-
-template <>
-struct Operand<1> {  // E4M3: v_mfma_scale_f32_16x16x128_f8f6f4 (neutral scales), 32 codes per lane
-    typedef v8i type;
-    static __device__ __forceinline__ v8i read_a(const LDS_AS uint8_t* p) {
-        const v4i lo = *(const LDS_AS v4i*)p;
-        const v4i hi = *(const LDS_AS v4i*)(p + 16);
-        return __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
-    }
-    // four transpose reads give k = 32g + 0..7, 8..15, 16..23, 24..31 of one column
-    static __device__ __forceinline__ v8i read_b(const LDS_AS uint8_t* p, int sb) {
-        const v2i t0 = __builtin_amdgcn_ds_read_tr8_b64_v2i32((LDS_AS v2i*)p);
-        const v2i t1 = __builtin_amdgcn_ds_read_tr8_b64_v2i32((LDS_AS v2i*)(p + 8 * sb));
-        const v2i t2 = __builtin_amdgcn_ds_read_tr8_b64_v2i32((LDS_AS v2i*)(p + 16 * sb));
-        const v2i t3 = __builtin_amdgcn_ds_read_tr8_b64_v2i32((LDS_AS v2i*)(p + 24 * sb));
-        const v4i t01 = __builtin_shufflevector(t0, t1, 0, 1, 2, 3);
-        const v4i t23 = __builtin_shufflevector(t2, t3, 0, 1, 2, 3);
-        return __builtin_shufflevector(t01, t23, 0, 1, 2, 3, 4, 5, 6, 7);
-    }
-    static __device__ __forceinline__ v4f mma(v8i a, v8i b, v4f c) {
-        return __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(a, b, c, 0, 0, 0, 127, 0, 127);
-    }
-};
-
-// One 16-byte chunk of `ES`-byte elements starting at element `col` of a row,
-// zero beyond `limit` and for rows out of range (edges and unaligned operands).
-template <int ES>
-__device__ __forceinline__ v4u load_chunk_guarded(const uint8_t* row_ptr, bool row_ok, int64_t col, int64_t limit) {
-    uint32_t w[4] = {0u, 0u, 0u, 0u};
-    if (row_ok) {
-#pragma unroll
-        for (int e = 0; e < 16 / ES; ++e) {
-            if (col + e < limit) {
-                uint32_t v = (ES == 1) ? (uint32_t)row_ptr[col + e]
-                                       : (uint32_t)reinterpret_cast<const uint16_t*>(row_ptr)[col + e];
-                const int bit = e * ES * 8;
-                w[bit >> 5] |= v << (bit & 31);
-            }
-        }
-    }
-    return v4u{w[0], w[1], w[2], w[3]};
-}
-
-template <int OUT>
-__device__ __forceinline__ void store_one(void* C, int64_t idx, float y) {
-    if constexpr (OUT == OUT_F32) {
-        reinterpret_cast<float*>(C)[idx] = y;
-    } else if constexpr (OUT == OUT_F16) {
-        reinterpret_cast<_Float16*>(C)[idx] = (_Float16)y;
-    } else {
-        reinterpret_cast<uint8_t*>(C)[idx] = e4m3_from_f32(y);
-    }
-}
-
-template <int ES, int OUT, int BM, int BN, int BK, int WM, int WN>
-__global__ __launch_bounds__(64 * WM * WN) void gemm_tile_kernel(
-    const uint8_t* __restrict__ A, const uint8_t* __restrict__ B, void* __restrict__ C, int M, int N, int K,
-    const float* __restrict__ sA, const float* __restrict__ sB, const float* __restrict__ sOut, int tiles_m,
-    int tiles_n, int aligned) {
-    using T = Tile<ES, BM, BN, BK, WM, WN>;
-    __shared__ __attribute__((aligned(16))) uint8_t smem_raw[2 * T::STAGE];
-    LDS_AS uint8_t* smem = (LDS_AS uint8_t*)smem_raw;
-
-    const int tid = threadIdx.x;
-    const int lane = tid & 63;
-    const int wave = tid >> 6;
-    const int wm = wave / WN, wn = wave % WN;
-
-    int tile_m, tile_n;
-    tile_coords(blockIdx.x, tiles_m, tiles_n, tile_m, tile_n);
-    const int m0 = tile_m * BM;
-    const int n0 = tile_n * BN;
-    const bool interior_mn = aligned && (m0 + BM <= M) && (n0 + BN <= N);
-
-    // This thread's chunk coordinates inside a staged tile.
-    const int a_row = tid / T::A_CPR, a_col = tid % T::A_CPR;  // + i * A_RPP rows
-    const int b_row = tid / T::B_CPR, b_col = tid % T::B_CPR;  // + i * B_RPP rows
-
-    v4u ra[T::CA];
-    v4u rb[T::CB];
-
-    v4f acc[T::TM][T::TN];
-#pragma unroll
-    for (int i = 0; i < T::TM; ++i)
-#pragma unroll
-        for (int j = 0; j < T::TN; ++j) acc[i][j] = v4f{0.f, 0.f, 0.f, 0.f};
-
-    const int g = lane >> 4;    // 16-lane group: selects the k sub-range of an operand
-    const int j16 = lane & 15;  // lane within its group
-    // B transpose-read pattern (lane maps measured for ds_read_b64_tr_b16 /
-    // _b8: lane i of a 16-lane group receives element i % E of lanes
-    // (16/E)*e + i/E, E = elements per 64 bits).
-    const int b_row_in = (ES == 2) ? (j16 >> 2) : (j16 >> 1);
-    const int b_col_in = (ES == 2) ? 4 * (j16 & 3) : 8 * (j16 & 1);
-    const int a_lds = (wm * T::WTM + j16) * T::SA + g * T::OPB;          // + stage + tm*16*SA + ks*KPI*ES
-    const int b_lds = (8 * (ES == 2 ? 1 : 4) * g + b_row_in) * T::SB     // + stage + ks*KPI*SB + tn*16*ES
-                      + (wn * T::WTN + b_col_in) * ES;
-
-    const int nk = (K + BK - 1) / BK;
-    typedef typename Operand<ES>::type Op;
-
-    // ---- global <-> registers <-> LDS (A and B have separate stages) ----
-    // Fast-path loads: a wave-uniform base (kept in SGPRs) plus a 32-bit
-    // per-lane offset, so the 16 loads of a tile need no 64-bit VGPR addresses.
-    // Valid while one tile row block spans less than 2^31 bytes (checked below).
-    const uint8_t* a_tile = A + (int64_t)m0 * K * ES;
-    const uint8_t* b_tile = B + (int64_t)n0 * ES;
-    // Edge tiles (aligned operands) use the same unguarded loads with the
-    // addresses clamped into the matrix: A rows past M re-read row M-1 and B
-    // column chunks past N re-read the last chunk. Those values only reach
-    // output rows/columns that are never stored, and every address is valid.
-    uint32_t a_offs[T::CA], b_offs[T::CB];
-#pragma unroll
-    for (int i = 0; i < T::CA; ++i) {
-        const int r = min(m0 + a_row + i * T::A_RPP, M - 1) - m0;
-        a_offs[i] = (uint32_t)((r * K + a_col * T::VE) * ES);
-    }
-#pragma unroll
-    for (int i = 0; i < T::CB; ++i) {
-        const int c = min(n0 + b_col * T::VE, N - T::VE) - n0;
-        b_offs[i] = (uint32_t)(((b_row + i * T::B_RPP) * N + c) * ES);
-    }
-    auto load_a = [&](int kt) __attribute__((always_inline)) {
-        const uint8_t* pa = a_tile + (int64_t)kt * BK * ES;
-#pragma unroll
-        for (int i = 0; i < T::CA; ++i) ra[i] = *reinterpret_cast<const v4u*>(pa + a_offs[i]);
-    };
-    auto load_b = [&](int kt) __attribute__((always_inline)) {
-        const uint8_t* pb = b_tile + (int64_t)kt * BK * N * ES;
-#pragma unroll
-        for (int i = 0; i < T::CB; ++i) rb[i] = *reinterpret_cast<const v4u*>(pb + b_offs[i]);
-    };
-    auto store_a = [&](int stage) __attribute__((always_inline)) {
-        LDS_AS uint8_t* As = smem + T::a_stage(stage);
-#pragma unroll
-        for (int i = 0; i < T::CA; ++i)
-            *(LDS_AS v4u*)(As + (a_row + i * T::A_RPP) * T::SA + a_col * 16) = ra[i];
-    };
-    auto store_b = [&](int stage) __attribute__((always_inline)) {
-        LDS_AS uint8_t* Bs = smem + T::b_stage(stage);
-#pragma unroll
-        for (int i = 0; i < T::CB; ++i)
-            *(LDS_AS v4u*)(Bs + (b_row + i * T::B_RPP) * T::SB + b_col * 16) = rb[i];
-    };
-    // Edge tiles, the K tail and unaligned operands: each 16-byte chunk is
-    // loaded with per-element guards and written straight to LDS (no register
-    // staging, and a rolled loop, so this path costs almost no registers).
-    auto guarded_to_lds = [&](int kt, int stage) __attribute__((always_inline)) {
-        const int k0 = kt * BK;
-        LDS_AS uint8_t* As = smem + T::a_stage(stage);
-        LDS_AS uint8_t* Bs = smem + T::b_stage(stage);
-#pragma unroll 1
-        for (int i = 0; i < T::CA; ++i) {
-            const int gm = m0 + a_row + i * T::A_RPP;
-            const int64_t gk = (int64_t)k0 + a_col * T::VE;
-            const uint8_t* rp = A + (int64_t)gm * K * ES;
-            v4u v;
-            if (aligned && gm < M && gk + T::VE <= K)
-                v = *reinterpret_cast<const v4u*>(rp + gk * ES);
-            else
-                v = load_chunk_guarded<ES>(rp, gm < M, gk, K);
-            *(LDS_AS v4u*)(As + (a_row + i * T::A_RPP) * T::SA + a_col * 16) = v;
-        }
-#pragma unroll 1
-        for (int i = 0; i < T::CB; ++i) {
-            const int gk = k0 + b_row + i * T::B_RPP;
-            const int64_t gn = (int64_t)n0 + b_col * T::VE;
-            const uint8_t* rp = B + (int64_t)gk * N * ES;
-            v4u v;
-            if (aligned && gk < K && gn + T::VE <= N)
-                v = *reinterpret_cast<const v4u*>(rp + gn * ES);
-            else
-                v = load_chunk_guarded<ES>(rp, gk < K, gn, N);
-            *(LDS_AS v4u*)(Bs + (b_row + i * T::B_RPP) * T::SB + b_col * 16) = v;
-        }
-    };
-
-    // ---- LDS -> MFMA operands ----
-    auto read_b = [&](int stage, Op (&bop)[T::KS][T::TN]) __attribute__((always_inline)) {
-        const LDS_AS uint8_t* base = smem + T::b_stage(stage) + b_lds;
-#pragma unroll
-        for (int ks = 0; ks < T::KS; ++ks)
-#pragma unroll
-            for (int tn = 0; tn < T::TN; ++tn)
-                bop[ks][tn] = Operand<ES>::read_b(base + ks * T::KPI * T::SB + tn * 16 * ES, T::SB);
-    };
-    auto mma_tile = [&](int stage, const Op (&bop)[T::KS][T::TN]) __attribute__((always_inline)) {
-        const LDS_AS uint8_t* base = smem + T::a_stage(stage) + a_lds;
-#pragma unroll
-        for (int ks = 0; ks < T::KS; ++ks)
-#pragma unroll
-            for (int tm = 0; tm < T::TM; ++tm) {
-                const Op aop = Operand<ES>::read_a(base + tm * 16 * T::SA + ks * T::KPI * ES);
-#pragma unroll
-                for (int tn = 0; tn < T::TN; ++tn) acc[tm][tn] = Operand<ES>::mma(aop, bop[ks][tn], acc[tm][tn]);
-                // With two waves per SIMD the other wave hides the A read
-                // latency. Pinning this row block's products here (an empty
-                // asm that reads and rewrites its accumulators, after which no
-                // LDS read may be hoisted) keeps one A operand live at a time
-                // instead of letting the compiler sink every MFMA to the loop
-                // end and hold all A operands.
-                if constexpr (T::NT > 256) {
-#pragma unroll
-                    for (int tn = 0; tn < T::TN; ++tn) asm volatile("" : "+v"(acc[tm][tn])::"memory");
-                }
-            }
-    };
-
-    const bool offsets_fit = (int64_t)BM * K * ES < (1ll << 31) && (int64_t)BK * N * ES < (1ll << 31);
-    if (kRegisterPipeline && interior_mn && K % BK == 0 && nk > 0 && offsets_fit) {
-        // Software pipeline, one barrier per K tile. Entering iteration kt:
-        // LDS holds A(kt) in A stage kt%2 and B(kt+1) in B stage (kt+1)%2,
-        // registers hold the B operands of tile kt (bcur) and the global data
-        // of A(kt+1) and B(kt+2). The iteration stores that data to the stages
-        // iteration kt-1 finished reading, issues the loads of A(kt+2) and
-        // B(kt+3), multiplies tile kt and reads the B operands of tile kt+1
-        // into the other register set, so LDS traffic runs under the MFMAs.
-        // Tiles past the end are clamped to the last one (loaded, never used).
-        Op b0[T::KS][T::TN], b1[T::KS][T::TN];
-        const int last = nk - 1;
-        load_a(0);
-        load_b(0);
-        store_a(0);
-        store_b(0);
-        load_b(min(1, last));
-        store_b(1);
-        load_a(min(1, last));
-        load_b(min(2, last));
-        __syncthreads();
-        read_b(0, b0);
-        __syncthreads();
-        auto iteration = [&](int kt, Op (&bcur)[T::KS][T::TN], Op (&bnext)[T::KS][T::TN])
-                             __attribute__((always_inline)) {
-            store_a((kt + 1) & 1);
-            store_b(kt & 1);
-            load_a(min(kt + 2, last));
-            load_b(min(kt + 3, last));
-            mma_tile(kt & 1, bcur);
-            read_b((kt + 1) & 1, bnext);
-            __syncthreads();
-        };
-        int kt = 0;
-        for (; kt + 1 < nk; kt += 2) {
-            iteration(kt, b0, b1);
-            iteration(kt + 1, b1, b0);
-        }
-        if (kt < nk) iteration(kt, b0, b1);
-    } else if (nk > 0) {
-        Op bop[T::KS][T::TN];
-        // Tile kt+1 is fetched into registers while tile kt is multiplied;
-        // the K tail and unaligned operands load each chunk with element
-        // guards straight into LDS.
-        auto fast = [&](int kt) __attribute__((always_inline)) {
-            return aligned && offsets_fit && (kt + 1) * BK <= K;
-        };
-        if (fast(0)) {
-            load_a(0);
-            load_b(0);
-            store_a(0);
-            store_b(0);
-        } else {
-            guarded_to_lds(0, 0);
-        }
-        __syncthreads();
-        for (int kt = 0; kt < nk; ++kt) {
-            const bool more = kt + 1 < nk;
-            const bool fast_next = more && fast(kt + 1);
-            if (fast_next) {
-                load_a(kt + 1);
-                load_b(kt + 1);
-            }
-            read_b(kt & 1, bop);
-            mma_tile(kt & 1, bop);
-            if (fast_next) {
-                store_a((kt + 1) & 1);
-                store_b((kt + 1) & 1);
-            } else if (more) {
-                guarded_to_lds(kt + 1, (kt + 1) & 1);
-            }
-            __syncthreads();
-        }
-    }
-
-    // Epilogue: y = acc * (sA*sB), converted, stored with M/N predication on edge tiles.
-    const float scale = epilogue_multiplier(sA, sB, sOut, OUT == OUT_E4M3);
-    const int row0 = m0 + wm * T::WTM + 4 * g;
-    const int col0 = n0 + wn * T::WTN + j16;
-    if (interior_mn) {
-#pragma unroll
-        for (int tm = 0; tm < T::TM; ++tm)
-#pragma unroll
-            for (int tn = 0; tn < T::TN; ++tn)
-#pragma unroll
-                for (int r = 0; r < 4; ++r)
-                    store_one<OUT>(C, (int64_t)(row0 + tm * 16 + r) * N + col0 + tn * 16, acc[tm][tn][r] * scale);
-    } else {
-#pragma unroll
-        for (int tm = 0; tm < T::TM; ++tm)
-#pragma unroll
-            for (int tn = 0; tn < T::TN; ++tn)
-#pragma unroll
-                for (int r = 0; r < 4; ++r) {
-                    const int row = row0 + tm * 16 + r, col = col0 + tn * 16;
-                    if (row < M && col < N)
-                        store_one<OUT>(C, (int64_t)row * N + col, acc[tm][tn][r] * scale);
-                }
-    }
-}
-
-bool aligned16(const void* p) { return ((uintptr_t)p & 15u) == 0; }
-
-template <int ES, int BM, int BN, int BK, int WM, int WN>
-hipError_t launch_tile(const GemmArgs& a) {
-    const int64_t tiles_m = (a.M + BM - 1) / BM;
-    const int64_t tiles_n = (a.N + BN - 1) / BN;
-    const int64_t blocks = tiles_m * tiles_n;
-    if (blocks <= 0) return hipSuccess;
-    if (blocks > 0x7FFFFFFF) return hipErrorInvalidValue;
-    const int aligned = aligned16(a.A) && aligned16(a.B) && ((a.K * ES) % 16 == 0) && ((a.N * ES) % 16 == 0);
-    const uint8_t* A = reinterpret_cast<const uint8_t*>(a.A);
-    const uint8_t* B = reinterpret_cast<const uint8_t*>(a.B);
-    const int M = (int)a.M, N = (int)a.N, K = (int)a.K;
-    const dim3 grid((unsigned)blocks), block(64 * WM * WN);
-    switch (a.out_dtype) {
-        case OUT_F32:
-            gemm_tile_kernel<ES, OUT_F32, BM, BN, BK, WM, WN><<<grid, block, 0, a.stream>>>(
-                A, B, a.C, M, N, K, a.sA, a.sB, a.sOut, (int)tiles_m, (int)tiles_n, aligned);
-            break;
-        case OUT_F16:
-            gemm_tile_kernel<ES, OUT_F16, BM, BN, BK, WM, WN><<<grid, block, 0, a.stream>>>(
-                A, B, a.C, M, N, K, a.sA, a.sB, a.sOut, (int)tiles_m, (int)tiles_n, aligned);
-            break;
-        default:
-            if constexpr (ES == 1) {
-                gemm_tile_kernel<ES, OUT_E4M3, BM, BN, BK, WM, WN><<<grid, block, 0, a.stream>>>(
-                    A, B, a.C, M, N, K, a.sA, a.sB, a.sOut, (int)tiles_m, (int)tiles_n, aligned);
-            } else {
-                return hipErrorInvalidValue;
-            }
-    }
-    return hipGetLastError();
-}
-
-}  // namespace
+namespace tile {
+// The other FP8 operand pairs are compiled in gemm_tile_mixed.hip.
+#define LIBGEMM_TILE_EXTERN(BM, BN, BK, WM, WN)                                         \
+    extern template hipError_t launch_tile<1, BM, BN, BK, WM, WN, 0, 1>(const GemmArgs&); \
+    extern template hipError_t launch_tile<1, BM, BN, BK, WM, WN, 1, 0>(const GemmArgs&); \
+    extern template hipError_t launch_tile<1, BM, BN, BK, WM, WN, 1, 1>(const GemmArgs&);
+LIBGEMM_TILE_MIXED_CONFIGS(LIBGEMM_TILE_EXTERN)
+#undef LIBGEMM_TILE_EXTERN
+}  // namespace tile
 
 // The table lives in a host function so that the kernels it names are
 // instantiated for the device while the table itself stays host data.
 const GemmConfig* tile_configs(int* count) {
     static const GemmConfig table[] = {
-        {"tile_f16_64x64x64_w2x2", KIND_F16, 0, 64, 64, 64, launch_tile<2, 64, 64, 64, 2, 2>},
-        {"tile_f16_128x128x64_w2x2", KIND_F16, 0, 128, 128, 64, launch_tile<2, 128, 128, 64, 2, 2>},
-        {"tile_f16_256x256x64_w2x2", KIND_F16, 0, 256, 256, 64, launch_tile<2, 256, 256, 64, 2, 2>},
-        {"tile_fp8_64x64x128_w2x2", KIND_FP8, 0, 64, 64, 128, launch_tile<1, 64, 64, 128, 2, 2>},
-        {"tile_fp8_128x128x128_w2x2", KIND_FP8, 0, 128, 128, 128, launch_tile<1, 128, 128, 128, 2, 2>},
-        {"tile_fp8_256x256x128_w2x2", KIND_FP8, 0, 256, 256, 128, launch_tile<1, 256, 256, 128, 2, 2>},
-        {"tile_fp8_256x256x128_w2x4", KIND_FP8, 0, 256, 256, 128, launch_tile<1, 256, 256, 128, 2, 4>},
-        {"tile_fp8_256x256x128_w4x2", KIND_FP8, 0, 256, 256, 128, launch_tile<1, 256, 256, 128, 4, 2>},
-        {"tile_f16_256x256x64_w2x4", KIND_F16, 0, 256, 256, 64, launch_tile<2, 256, 256, 64, 2, 4>},
-        {"tile_f16_256x256x64_w4x2", KIND_F16, 0, 256, 256, 64, launch_tile<2, 256, 256, 64, 4, 2>},
+        {"tile_f16_64x64x64_w2x2", KIND_F16, 0, 64, 64, 64, tile::launch_tile<2, 64, 64, 64, 2, 2, 0, 0>},
+        {"tile_f16_128x128x64_w2x2", KIND_F16, 0, 128, 128, 64, tile::launch_tile<2, 128, 128, 64, 2, 2, 0, 0>},
+        {"tile_fp8_64x64x128_w2x2", KIND_FP8, 0, 64, 64, 128, tile::launch_tile_fp8_any<64, 64, 128, 2, 2>, kAllFp8Pairs},
+        {"tile_fp8_128x128x128_w2x2", KIND_FP8, 0, 128, 128, 128, tile::launch_tile_fp8_any<128, 128, 128, 2, 2>, kAllFp8Pairs},
+        {"tile_fp8_256x256x128_w2x4", KIND_FP8, 0, 256, 256, 128, tile::launch_tile_fp8_any<256, 256, 128, 2, 4>, kAllFp8Pairs},
+        {"tile_f16_256x256x64_w2x4", KIND_F16, 0, 256, 256, 64, tile::launch_tile<2, 256, 256, 64, 2, 4, 0, 0>},
     };
     *count = (int)(sizeof(table) / sizeof(table[0]));
     return table;

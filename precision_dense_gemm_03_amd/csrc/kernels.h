@@ -19,6 +19,8 @@ struct GemmArgs {
     int out_dtype;
     int64_t M, N, K;
     hipStream_t stream;
+    int fmt_a = 0;     // FP8 operand formats (Fp8Format: 0 = E4M3, 1 = E5M2); 0 for FP16
+    int fmt_b = 0;
 };
 
 typedef hipError_t (*GemmLauncher)(const GemmArgs&);
@@ -30,19 +32,32 @@ struct GemmConfig {
     int family;         // 0 = MFMA tile kernel, 1 = M<=16 streaming kernel, 2 = direct-load tile kernel
     int bm, bn, bk;     // tile (stream: bm = max M, bn = columns per block, bk = k-slices)
     GemmLauncher launch;
+    int fmt_mask = 0;   // FP8 operand pairs served: bit (2*fmt_a + fmt_b); 0 means E4M3 x E4M3 only
 };
+
+constexpr int kAllFp8Pairs = 15;
+
+// Whether configuration c serves FP8 operand formats (fa, fb).
+inline bool serves_formats(const GemmConfig& c, int fa, int fb) {
+    const int mask = c.fmt_mask ? c.fmt_mask : 1;
+    return (mask >> (2 * fa + fb)) & 1;
+}
 
 // Configuration tables, defined next to their kernels.
 const GemmConfig* tile_configs(int* count);
 const GemmConfig* stream_configs(int* count);
 const GemmConfig* dma_configs(int* count);
 
-// Shape -> configuration (host only, no HIP calls). Returns NULL if none fits.
-const GemmConfig* select_config(int kind, int out_dtype, int64_t M, int64_t N, int64_t K);
+// Shape (and FP8 operand formats) -> configuration (host only, no HIP calls).
+// Returns NULL if none fits.
+const GemmConfig* select_config(int kind, int out_dtype, int64_t M, int64_t N, int64_t K, int fmt_a = 0,
+                                int fmt_b = 0);
 
 // amax / quantize launchers.
-hipError_t launch_amax(const float* x, int64_t n, float* amax, float* scale, hipStream_t stream);
-hipError_t launch_quantize(const float* x, int64_t n, const float* scale, uint8_t* q, hipStream_t stream);
+// amax and (scale != NULL) the scale for FP8 format fmt, pow2 != 0 for a
+// power-of-two scale.
+hipError_t launch_amax(const float* x, int64_t n, float* amax, float* scale, int fmt, int pow2, hipStream_t stream);
+hipError_t launch_quantize(const float* x, int64_t n, const float* scale, uint8_t* q, int fmt, hipStream_t stream);
 // Writes zeros to an [M,N] output of the given dtype (the K = 0 empty sum).
 hipError_t launch_fill_zero(void* C, int64_t count, int out_dtype, hipStream_t stream);
 

@@ -14,7 +14,10 @@
 //      most tiles (64). Which kernel runs a 256x256 tile is chosen in
 //      tile_with below.
 //   3. LIBGEMM_CONFIG=<config name> replaces the choice when that config can
-//      serve the request (same operand kind; streaming configs need M <= bound).
+//      serve the request (same operand kind and FP8 operand formats; streaming
+//      configs need M <= bound).
+//   Every rule only considers configurations compiled for the requested FP8
+//   operand formats (E4M3 / E5M2 for A and for B).
 #include <cstdlib>
 #include <cstring>
 
@@ -26,18 +29,20 @@ namespace {
 
 constexpr int64_t kNumCUs = 256;
 
-const GemmConfig* find_named(const char* name, int kind, int64_t M) {
+const GemmConfig* find_named(const char* name, int kind, int64_t M, int fa = 0, int fb = 0) {
     int ns = 0, nt = 0;
     const GemmConfig* st = stream_configs(&ns);
     const GemmConfig* tt = tile_configs(&nt);
     for (int i = 0; i < ns; ++i)
-        if (std::strcmp(st[i].name, name) == 0 && st[i].kind == kind && M <= st[i].bm) return &st[i];
+        if (std::strcmp(st[i].name, name) == 0 && st[i].kind == kind && M <= st[i].bm &&
+            serves_formats(st[i], fa, fb))
+            return &st[i];
     for (int i = 0; i < nt; ++i)
-        if (std::strcmp(tt[i].name, name) == 0 && tt[i].kind == kind) return &tt[i];
+        if (std::strcmp(tt[i].name, name) == 0 && tt[i].kind == kind && serves_formats(tt[i], fa, fb)) return &tt[i];
     int nd = 0;
     const GemmConfig* dt = dma_configs(&nd);
     for (int i = 0; i < nd; ++i)
-        if (std::strcmp(dt[i].name, name) == 0 && dt[i].kind == kind) return &dt[i];
+        if (std::strcmp(dt[i].name, name) == 0 && dt[i].kind == kind && serves_formats(dt[i], fa, fb)) return &dt[i];
     return nullptr;
 }
 
@@ -48,28 +53,29 @@ const GemmConfig* find_named(const char* name, int kind, int64_t M) {
 // register-staged 8-wave kernel, whose two waves per SIMD overlap the
 // prologue and epilogue, measured faster. Smaller tiles use the
 // register-staged kernel with 4 waves.
-const GemmConfig* tile_with(int kind, int bm, int64_t tiles) {
+const GemmConfig* tile_with(int kind, int bm, int64_t tiles, int fa, int fb) {
     if (bm == 256) {
         const bool direct = kind == KIND_F16 || tiles >= 2 * kNumCUs;
         const char* want = direct ? (kind == KIND_FP8 ? "dma_fp8_256x256x64_s4" : "dma_f16_256x256x32_s4")
                                   : "tile_fp8_256x256x128_w2x4";
-        const GemmConfig* c = find_named(want, kind, 0);
+        const GemmConfig* c = find_named(want, kind, 0, fa, fb);
         if (c) return c;
     }
     int nt = 0;
     const GemmConfig* tt = tile_configs(&nt);
     for (int i = 0; i < nt; ++i)
-        if (tt[i].kind == kind && tt[i].bm == bm) return &tt[i];
+        if (tt[i].kind == kind && tt[i].bm == bm && serves_formats(tt[i], fa, fb)) return &tt[i];
     return nullptr;
 }
 
 }  // namespace
 
-const GemmConfig* select_config(int kind, int out_dtype, int64_t M, int64_t N, int64_t K) {
+const GemmConfig* select_config(int kind, int out_dtype, int64_t M, int64_t N, int64_t K, int fa, int fb) {
     (void)out_dtype;
     (void)K;
+    if (kind == KIND_F16) fa = fb = 0;
     if (const char* env = std::getenv("LIBGEMM_CONFIG")) {
-        if (const GemmConfig* c = find_named(env, kind, M)) return c;
+        if (const GemmConfig* c = find_named(env, kind, M, fa, fb)) return c;
     }
     if (M <= 16) {
         const GemmConfig* best = nullptr;
@@ -77,7 +83,7 @@ const GemmConfig* select_config(int kind, int out_dtype, int64_t M, int64_t N, i
         const GemmConfig* st = stream_configs(&ns);
         for (int i = 0; i < ns; ++i) {
             const GemmConfig& c = st[i];
-            if (c.kind == kind && M <= c.bm && (!best || c.bm < best->bm)) best = &c;
+            if (c.kind == kind && M <= c.bm && serves_formats(c, fa, fb) && (!best || c.bm < best->bm)) best = &c;
         }
         if (best) return best;
     }
@@ -87,10 +93,10 @@ const GemmConfig* select_config(int kind, int out_dtype, int64_t M, int64_t N, i
         const double useful = (double)M * (double)N;
         const double padded = (double)(tm * bm) * (double)(tn * bm);
         if (tm * tn >= kNumCUs && useful >= 0.75 * padded) {
-            if (const GemmConfig* c = tile_with(kind, bm, tm * tn)) return c;
+            if (const GemmConfig* c = tile_with(kind, bm, tm * tn, fa, fb)) return c;
         }
     }
-    return tile_with(kind, 64, 0);
+    return tile_with(kind, 64, 0, fa, fb);
 }
 
 }  // namespace libgemm

@@ -38,7 +38,8 @@ def header_defines():
 def test_header_declares_the_entry_points():
     names = set(header_functions())
     assert {"gemm_f16", "gemm_fp8_scaled", "quantize_fp8", "amax_f32", "gemm_status_str",
-            "gemm_select_config"} <= names
+            "gemm_select_config", "gemm_fp8_fmt", "quantize_fp8_fmt", "amax_scale_f32",
+            "gemm_select_config_fmt"} <= names
 
 
 def test_library_exports_every_declared_symbol():
@@ -53,6 +54,7 @@ def test_library_exports_every_declared_symbol():
 def test_binding_constants_match_header():
     d = header_defines()
     assert d["GEMM_OUT_F32"] == g.OUT_F32 and d["GEMM_OUT_F16"] == g.OUT_F16 and d["GEMM_OUT_E4M3"] == g.OUT_E4M3
+    assert d["GEMM_OUT_E5M2"] == g.OUT_E5M2 and d["GEMM_FMT_E4M3"] == g.FMT_E4M3 and d["GEMM_FMT_E5M2"] == g.FMT_E5M2
     for code, name in g.STATUS_NAMES.items():
         assert d[name] == code
 
@@ -87,9 +89,42 @@ def test_gemm_fp8_argument_validation():
     assert L.gemm_fp8_scaled(FAKE, FAKE2, s, s + 4, None, FAKE3, 2, 4, 4, 4, None) == -4   # E4M3 needs sOut
     assert L.gemm_fp8_scaled(FAKE, FAKE2, None, s, None, FAKE3, 0, 4, 4, 4, None) == -1
     assert L.gemm_fp8_scaled(FAKE, FAKE2, s, None, None, FAKE3, 0, 4, 4, 4, None) == -1
-    assert L.gemm_fp8_scaled(FAKE, FAKE2, s, s, None, FAKE3, 3, 4, 4, 4, None) == -3
+    assert L.gemm_fp8_scaled(FAKE, FAKE2, s, s, None, FAKE3, 3, 4, 4, 4, None) == -4   # E5M2 needs sOut too
+    assert L.gemm_fp8_scaled(FAKE, FAKE2, s, s, None, FAKE3, 4, 4, 4, 4, None) == -3
     assert L.gemm_fp8_scaled(FAKE, FAKE2, s, s, None, FAKE3, 0, 4, -4, 4, None) == -2
     assert L.gemm_fp8_scaled(FAKE, FAKE2, FAKE3 + 8, s, None, FAKE3, 0, 4, 4, 4, None) == -8  # C covers sA
+
+
+def test_format_entry_points_argument_validation():
+    L = g.lib()
+    s = FAKE3 + 4096
+    # unknown operand or quantize formats
+    assert L.gemm_fp8_fmt(FAKE, 2, FAKE2, 0, s, s + 4, None, FAKE3, 0, 4, 4, 4, None) == -3
+    assert L.gemm_fp8_fmt(FAKE, 0, FAKE2, -1, s, s + 4, None, FAKE3, 0, 4, 4, 4, None) == -3
+    assert L.gemm_fp8_fmt(FAKE, 1, FAKE2, 1, s, s + 4, None, FAKE3, 3, 4, 4, 4, None) == -4   # E5M2 out, no sOut
+    assert L.gemm_fp8_fmt(FAKE, 1, FAKE2, 0, s, None, None, FAKE3, 0, 4, 4, 4, None) == -1
+    assert L.gemm_fp8_fmt(FAKE, 1, FAKE2, 0, s, s + 4, None, FAKE + 2, 0, 4, 4, 4, None) == -8
+    assert L.quantize_fp8_fmt(FAKE, 10, FAKE2, FAKE3, 2, None) == -3
+    assert L.quantize_fp8_fmt(FAKE, 10, FAKE2, FAKE + 8, 1, None) == -8
+    assert L.quantize_fp8_fmt(None, 0, None, None, 1, None) == 0
+    assert L.amax_scale_f32(FAKE, 3, FAKE2, FAKE2 + 64, 5, 0, None) == -3
+    assert L.amax_scale_f32(FAKE, 3, None, None, 1, 1, None) == -1
+    assert L.amax_scale_f32(FAKE, 3, FAKE2, FAKE2, 1, 1, None) == -8
+    buf = ctypes.create_string_buffer(64)
+    assert L.gemm_select_config_fmt(1, 0, 8, 8, 8, 3, 0, buf, 64) == -3
+    assert L.gemm_select_config_fmt(0, 3, 8, 8, 8, 0, 0, buf, 64) == -3          # FP16 cannot write FP8
+
+
+def test_select_config_formats():
+    # every FP8 shape class has a configuration for every operand-format pair
+    for fa in (g.FMT_E4M3, g.FMT_E5M2):
+        for fb in (g.FMT_E4M3, g.FMT_E5M2):
+            for (M, N, K) in [(1, 4096, 4096), (4, 4096, 4096), (16, 4096, 4096), (65, 4096, 4096),
+                              (3000, 4096, 4096), (4096, 4096, 4096), (16384, 12288, 4096)]:
+                name = g.select_config_fmt(g.KIND_FP8, g.OUT_E5M2, M, N, K, fa, fb)
+                assert name.startswith(("stream_fp8", "tile_fp8", "dma_fp8")), name
+    assert g.select_config_fmt(g.KIND_FP8, g.OUT_F16, 4096, 4096, 4096, 0, 0) == \
+        g.select_config(g.KIND_FP8, g.OUT_F16, 4096, 4096, 4096)
 
 
 def test_quantize_and_amax_argument_validation():

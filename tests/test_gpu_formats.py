@@ -1,0 +1,187 @@
+"""GPU parity for the second FP8 format and power-of-two scales.
+
+E5M2 quantize (all 2^32 FP32 inputs), the amax scale rules (max/448,
+max/57344 and the power-of-two scales) bit-exact against the oracle, and the
+GEMM with every pair of operand formats and every output type on each kernel
+family, element by element against the oracle.
+"""
+import numpy as np
+import pytest
+import torch
+
+import oracle as orc
+import precision_dense_gemm_03_amd as g
+import workloads as wl
+from parity import check_f16, check_f32, check_fp8, fp8_dot_allowance
+
+pytestmark = pytest.mark.gpu
+
+DEV = torch.device("cuda:0")
+# library format number -> oracle format number
+ORC_FMT = {g.FMT_E4M3: orc.FMT_E4M3, g.FMT_E5M2: orc.FMT_E5M2}
+
+
+def say(*a):
+    print(*a, flush=True)
+
+
+@pytest.fixture(scope="module", autouse=True)
+def _gpu():
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    torch.cuda.set_device(DEV)
+    g.lib()
+    yield
+    torch.cuda.synchronize()
+
+
+def dev(x):
+    return torch.from_numpy(np.ascontiguousarray(x)).to(DEV)
+
+
+def host(t):
+    torch.cuda.synchronize()
+    return t.cpu().numpy()
+
+
+def scalar(v):
+    return torch.tensor([float(np.float32(v))], dtype=torch.float32, device=DEV)
+
+
+def codes(fmt, shape, seed):
+    return wl.random_e5m2_codes(shape, seed) if fmt == g.FMT_E5M2 else wl.random_e4m3_codes(shape, seed)
+
+
+# ------------------------------------------------------------- quantize
+
+def test_quantize_e5m2_all_fp32_bit_patterns():
+    """All 2^32 inputs with scale 1 (so the E5M2 codec alone is under test)."""
+    chunk = 1 << 28
+    one = scalar(1.0)
+    q = torch.empty(chunk, dtype=torch.uint8, device=DEV)
+    for start in range(0, 1 << 32, chunk):
+        say(f"quantize e5m2 exhaustive chunk {start:#x}")
+        v = torch.arange(start, start + chunk, dtype=torch.int64, device=DEV)
+        v = torch.where(v >= 2 ** 31, v - 2 ** 32, v)
+        xs = v.to(torch.int32).view(torch.float32)
+        del v
+        g.quantize_fp8_fmt(xs, one, g.FMT_E5M2, q)
+        ref = orc.e5m2_encode_f32bits(np.arange(chunk, dtype=np.uint32) + np.uint32(start))
+        got = host(q)
+        if not np.array_equal(got, ref):
+            i = int(np.argmax(got != ref))
+            raise AssertionError(f"bits {start + i:#010x}: got {got[i]:#04x} ref {ref[i]:#04x}")
+        del xs
+
+
+@pytest.mark.parametrize("fmt", [g.FMT_E4M3, g.FMT_E5M2])
+@pytest.mark.parametrize("pow2", [False, True])
+def test_quantize_with_each_scale_rule(fmt, pow2):
+    for n, mag in [(100003, 1.0), (4096 * 37, 3.0e4), (777, 1e-30), (16, 1e30)]:
+        say(f"quantize fmt={fmt} pow2={pow2} n={n} mag={mag}")
+        x = wl.random_normal_f32((n,), n) * np.float32(mag)
+        x[n // 2] = -x[n // 2] * 3
+        tx = dev(x)
+        amax, s = g.amax_scale_f32(tx, fmt, pow2)
+        oa = orc.amax(x)
+        os_ = orc.scale(oa, ORC_FMT[fmt], pow2)
+        assert host(amax)[0] == oa
+        assert host(s).view(np.uint32)[0] == np.float32(os_).view(np.uint32), (host(s)[0], os_)
+        q = g.quantize_fp8_fmt(tx, s, fmt)
+        assert np.array_equal(host(q), orc.quantize(x, os_, ORC_FMT[fmt]))
+
+
+def test_scale_rules_special_values():
+    cases = [np.zeros(1000, np.float32), np.array([1.4e-45, -2.8e-45], np.float32),
+             np.array([448.0], np.float32), np.array([448.00003], np.float32),
+             np.array([57344.0, 1.0], np.float32), np.array([3.3e38, -1.0], np.float32),
+             np.array([1.0, np.inf], np.float32), np.array([1.0, np.nan], np.float32)]
+    for x in cases:
+        for fmt in (g.FMT_E4M3, g.FMT_E5M2):
+            for pow2 in (False, True):
+                say(f"scale rule {x[:2]} fmt={fmt} pow2={pow2}")
+                _, s = g.amax_scale_f32(dev(x), fmt, pow2)
+                ref = orc.scale(orc.amax(x), ORC_FMT[fmt], pow2)
+                got = host(s)[0]
+                assert (np.isnan(got) and np.isnan(ref)) or np.float32(got).view(np.uint32) == \
+                    np.float32(ref).view(np.uint32), (x, fmt, pow2, got, ref)
+
+
+# ----------------------------------------------------------------- GEMM
+
+PAIRS = [(g.FMT_E4M3, g.FMT_E4M3), (g.FMT_E4M3, g.FMT_E5M2), (g.FMT_E5M2, g.FMT_E4M3), (g.FMT_E5M2, g.FMT_E5M2)]
+# (config forced, M, N, K): each kernel family that serves every operand pair
+SHAPES = [(None, 1, 1000, 512), (None, 4, 520, 640), ("tile_fp8_64x64x128_w2x2", 100, 200, 256),
+          ("tile_fp8_128x128x128_w2x2", 300, 272, 384), ("tile_fp8_256x256x128_w2x4", 257, 512, 320),
+          ("dma_fp8_256x256x64_s4", 300, 272, 192)]
+
+
+@pytest.mark.parametrize("fa,fb", PAIRS)
+@pytest.mark.parametrize("cfg,M,N,K", SHAPES)
+def test_gemm_operand_formats(fa, fb, cfg, M, N, K, monkeypatch):
+    if cfg:
+        monkeypatch.setenv("LIBGEMM_CONFIG", cfg)
+        assert g.select_config_fmt(g.KIND_FP8, g.OUT_F32, M, N, K, fa, fb) == cfg
+    say(f"gemm formats a={fa} b={fb} {cfg} {M}x{N}x{K}")
+    ca = codes(fa, (M, K), 7 * M + K + fa)
+    cb = codes(fb, (K, N), 11 * N + K + fb)
+    ofa, ofb = ORC_FMT[fa], ORC_FMT[fb]
+    R, S = orc.gemm(ofa, ca, cb, fmt_b=ofb)
+    T = fp8_dot_allowance(ca, cb, fmt_a=ofa, fmt_b=ofb)
+    sa, sb = np.float32(0.5), np.float32(0.25)      # powers of two: no extra rounding in sA*sB
+    ta, tb, tsa, tsb = dev(ca), dev(cb), scalar(sa), scalar(sb)
+    C = torch.empty((M, N), dtype=torch.float32, device=DEV)
+    g.gemm_fp8_fmt(ta, fa, tb, fb, tsa, tsb, C)
+    check_f32(host(C), R, S, sa, sb, what="f32", T=T)
+    C = torch.empty((M, N), dtype=torch.float16, device=DEV)
+    g.gemm_fp8_fmt(ta, fa, tb, fb, tsa, tsb, C)
+    V = R * float(sa) * float(sb)
+    # E5M2 products can overflow FP16: compare the elements whose whole
+    # tolerance interval stays below 65520 (where RNE to FP16 turns into inf)
+    slack = (1e-5 * S + T) * float(sa) * float(sb)
+    fin = np.abs(V) + slack < 65520.0
+    got16 = host(C).astype(np.float64)
+    check_f16(got16[fin], R[fin], S[fin], sa, sb, what="f16", T=T[fin])
+    for out_fmt in (g.FMT_E4M3, g.FMT_E5M2):
+        s_out = orc.scale(np.float32(np.max(np.abs(V))), ORC_FMT[out_fmt])
+        C = torch.empty((M, N), dtype=torch.uint8, device=DEV)
+        g.gemm_fp8_fmt(ta, fa, tb, fb, tsa, tsb, C, scalar(s_out), out_fmt=out_fmt)
+        check_fp8(host(C), R, S, sa, sb, s_out, ORC_FMT[out_fmt], what=f"fp8 out {out_fmt}", T=T)
+
+
+def test_gemm_fp8_scaled_e5m2_output():
+    """The original entry point writes E5M2 as well (out_dtype GEMM_OUT_E5M2)."""
+    M, N, K = 129, 300, 256
+    ca, cb = codes(g.FMT_E4M3, (M, K), 1), codes(g.FMT_E4M3, (K, N), 2)
+    R, S = orc.gemm(orc.FMT_E4M3, ca, cb)
+    T = fp8_dot_allowance(ca, cb)
+    s_out = orc.scale(np.float32(np.max(np.abs(R))), orc.FMT_E5M2)
+    C = torch.empty((M, N), dtype=torch.float8_e5m2, device=DEV)
+    g.gemm_fp8_scaled(dev(ca), dev(cb), scalar(1.0), scalar(1.0), C, scalar(s_out))
+    check_fp8(host(C.view(torch.uint8)), R, S, 1.0, 1.0, s_out, orc.FMT_E5M2, T=T)
+
+
+@pytest.mark.parametrize("M", [4, 3000])
+def test_pow2_e5m2_chain_against_oracle(M):
+    """FP32 data -> power-of-two E5M2 scale for A, E4M3 for B -> quantize ->
+    mixed GEMM -> F16 output; every step against the oracle's chain."""
+    N, K = 1024, 512
+    xa = wl.random_normal_f32((M, K), 41) * np.float32(1000.0)
+    xb = wl.random_normal_f32((K, N), 42)
+    ta, tb = dev(xa), dev(xb)
+    _, s_a = g.amax_scale_f32(ta, g.FMT_E5M2, True)
+    _, s_b = g.amax_scale_f32(tb, g.FMT_E4M3, True)
+    qa = g.quantize_fp8_fmt(ta, s_a, g.FMT_E5M2)
+    qb = g.quantize_fp8_fmt(tb, s_b, g.FMT_E4M3)
+    osa = orc.scale(orc.amax(xa), orc.FMT_E5M2, True)
+    osb = orc.scale(orc.amax(xb), orc.FMT_E4M3, True)
+    assert host(s_a)[0] == osa and host(s_b)[0] == osb
+    cqa, cqb = orc.quantize(xa, osa, orc.FMT_E5M2), orc.quantize(xb, osb, orc.FMT_E4M3)
+    assert np.array_equal(host(qa), cqa) and np.array_equal(host(qb), cqb)
+    C = torch.empty((M, N), dtype=torch.float16, device=DEV)
+    g.gemm_fp8_fmt(qa, g.FMT_E5M2, qb, g.FMT_E4M3, s_a, s_b, C)
+    rows = None if M <= 64 else list(range(0, M, 97)) + [M - 1]
+    R, S = orc.gemm(orc.FMT_E5M2, cqa, cqb, rows=rows, fmt_b=orc.FMT_E4M3)
+    T = fp8_dot_allowance(cqa, cqb, rows=rows, fmt_a=orc.FMT_E5M2, fmt_b=orc.FMT_E4M3)
+    got = host(C)
+    check_f16(got if rows is None else got[rows], R, S, osa, osb, what="pow2 chain", T=T)

@@ -48,12 +48,10 @@ def scalar(v):
     return torch.tensor([float(np.float32(v))], dtype=torch.float32, device=DEV)
 
 
-FP8_CONFIGS = ["dma_fp8_256x256x64_s4", "dma_fp8_256x256x64_s5", "dma_fp8_256x256x64_s3", "tile_fp8_256x256x128_w2x4",
-               "tile_fp8_256x256x128_w4x2", "tile_fp8_256x256x128_w2x2", "tile_fp8_128x128x128_w2x2",
-               "tile_fp8_64x64x128_w2x2"]
-F16_CONFIGS = ["dma_f16_256x256x32_s4", "dma_f16_256x256x32_s5", "dma_f16_256x256x32_s3", "tile_f16_256x256x64_w2x4",
-               "tile_f16_256x256x64_w4x2", "tile_f16_256x256x64_w2x2", "tile_f16_128x128x64_w2x2",
-               "tile_f16_64x64x64_w2x2"]
+FP8_CONFIGS = ["dma_fp8_256x256x64_s4", "dma_fp8_256x256x64_s5", "tile_fp8_256x256x128_w2x4",
+               "tile_fp8_128x128x128_w2x2", "tile_fp8_64x64x128_w2x2"]
+F16_CONFIGS = ["dma_f16_256x256x32_s4", "dma_f16_256x256x32_s5", "tile_f16_256x256x64_w2x4",
+               "tile_f16_128x128x64_w2x2", "tile_f16_64x64x64_w2x2"]
 
 # (M, N, K): full tiles; M/N edges with a K tail; an odd number of K tiles;
 # a single partial K tile; K and N not multiples of 16 bytes (unaligned rows).

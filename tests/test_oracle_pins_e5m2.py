@@ -184,10 +184,7 @@ def _exact(Ad, Bd):
     return R, S
 
 
-def random_e5m2_codes(shape, seed):
-    g = np.random.default_rng([9100, seed])
-    c = g.integers(0, 256, size=shape, dtype=np.uint8)
-    return np.where((c & 0x7F) > 0x7B, c & 0xBB, c).astype(np.uint8)   # finite codes only
+random_e5m2_codes = wl.random_e5m2_codes
 
 
 def test_gemm_mixed_formats_brute_force():

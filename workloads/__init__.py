@@ -108,6 +108,13 @@ def random_e4m3_codes(shape, seed, finite=True) -> np.ndarray:
     return c
 
 
+def random_e5m2_codes(shape, seed):
+    """Uniformly random finite E5M2 codes (infinities and NaNs excluded)."""
+    g = np.random.default_rng([9100, seed])
+    c = g.integers(0, 256, size=shape, dtype=np.uint8)
+    return np.where((c & 0x7F) > 0x7B, c & 0xBB, c).astype(np.uint8)
+
+
 def random_f16(shape, seed, lo=-1.0, hi=1.0) -> np.ndarray:
     g = np.random.default_rng([9001, seed])
     return g.uniform(lo, hi, size=shape).astype(np.float16)
