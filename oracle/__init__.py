@@ -68,6 +68,12 @@ def _load():
     lib.orc_out_fp8.argtypes = [_vp, _c_i64, ctypes.c_double, ctypes.c_int, _vp]
     lib.orc_out_e4m3.restype = None
     lib.orc_out_e4m3.argtypes = [_vp, _c_i64, ctypes.c_double, _vp]
+    lib.orc_amax_channel.restype = None
+    lib.orc_amax_channel.argtypes = [_vp, _c_i64, _c_i64, ctypes.c_int, _vp]
+    lib.orc_scale_n.restype = None
+    lib.orc_scale_n.argtypes = [_vp, _c_i64, ctypes.c_int, ctypes.c_int, _vp]
+    lib.orc_quantize_channel.restype = None
+    lib.orc_quantize_channel.argtypes = [_vp, _c_i64, _c_i64, ctypes.c_int, _vp, ctypes.c_int, _vp]
     lib.orc_num_threads.restype = ctypes.c_int
     lib.orc_num_threads.argtypes = []
     _lib = lib
@@ -171,6 +177,36 @@ def quantize(x, s, fmt=FMT_E4M3) -> np.ndarray:
         _load().orc_quantize(_ptr(a), a.size, float(np.float32(s)), _ptr(out))
     else:
         _load().orc_quantize_fmt(_ptr(a), a.size, float(np.float32(s)), int(fmt), _ptr(out))
+    return out
+
+
+def amax_channel(x, axis) -> np.ndarray:
+    """max|x| per row (axis 0) or per column (axis 1) of a 2-D float32 array;
+    NaN in a channel makes its value NaN."""
+    a = _c(x, np.float32)
+    rows, cols = a.shape
+    out = np.empty(rows if axis == 0 else cols, np.float32)
+    _load().orc_amax_channel(_ptr(a), rows, cols, int(axis), _ptr(out))
+    return out
+
+
+def scale_channel(a, fmt=FMT_E4M3, pow2=False) -> np.ndarray:
+    """The per-tensor scale rule applied to each channel's amax."""
+    v = _c(a, np.float32)
+    out = np.empty(v.shape, np.float32)
+    _load().orc_scale_n(_ptr(v), v.size, int(fmt), 1 if pow2 else 0, _ptr(out))
+    return out
+
+
+def quantize_channel(x, s, axis, fmt=FMT_E4M3) -> np.ndarray:
+    """FP8 codes of x[i,j] / s[i] (axis 0) or x[i,j] / s[j] (axis 1)."""
+    a = _c(x, np.float32)
+    rows, cols = a.shape
+    sv = _c(s, np.float32)
+    if sv.shape != ((rows,) if axis == 0 else (cols,)):
+        raise ValueError("one scale per channel")
+    out = np.empty(a.shape, np.uint8)
+    _load().orc_quantize_channel(_ptr(a), rows, cols, int(axis), _ptr(sv), int(fmt), _ptr(out))
     return out
 
 

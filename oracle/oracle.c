@@ -34,6 +34,10 @@
  *   - A scale may be a power of two just above the calibrated maximum, so
  *     that scaling is exponent arithmetic (P2 §2.1). Read as: the smallest
  *     2^e with max|x| / 2^e <= the format's largest value.
+ *   - Per-channel scaling is the named alternative to per-tensor scales
+ *     (P2 §2.1, §3.2): one scale per row of A and per column of B, the
+ *     per-tensor rule applied to each channel; the write-back multiplies the
+ *     accumulator by sA[i] * sB[j].
  *
  * Readings where the pages are silent (each is listed with its reason in the
  * design notes): a NaN always encodes to the canonical code 0x7F (both
@@ -291,6 +295,47 @@ ORC_API void orc_quantize_fmt(const float* x, int64_t n, float s, int fmt, uint8
         float t = (float)((double)x[i] / (double)s);
         q[i] = fp8_encode(fmt, (double)t);
     }
+}
+
+/* Per-channel scaling, named in P2 §2.1 and §3.2 as the finer alternative to
+ * one scale per tensor. Read as: a scale must be constant along K to be
+ * applied to the accumulator at write-back (P2 §3.2), so A[M,K] gets one scale
+ * per row and B[K,N] one per column; each channel's scale is the per-tensor
+ * rule applied to that channel's max|x|. axis 0: one value per row of the
+ * row-major x[rows, cols]; axis 1: one value per column. */
+ORC_API void orc_amax_channel(const float* x, int64_t rows, int64_t cols, int axis, float* out) {
+    if (axis == 0) {
+#pragma omp parallel for schedule(static)
+        for (int64_t i = 0; i < rows; ++i) out[i] = orc_amax(x + i * cols, cols);
+        return;
+    }
+    for (int64_t j = 0; j < cols; ++j) {
+        float m = 0.0f;
+        int saw_nan = 0;
+        for (int64_t i = 0; i < rows; ++i) {
+            float a = fabsf(x[i * cols + j]);
+            if (isnan(a)) saw_nan = 1;
+            else if (a > m) m = a;
+        }
+        out[j] = saw_nan ? NAN : m;
+    }
+}
+
+/* out_c = the scale of channel c from its amax a_c (orc_scale, per channel). */
+ORC_API void orc_scale_n(const float* a, int64_t n, int fmt, int pow2, float* out) {
+    for (int64_t i = 0; i < n; ++i) out[i] = orc_scale(a[i], fmt, pow2);
+}
+
+/* q[i,j] = FP8_fmt(fl32(x[i,j] / s_c)) with c = i (axis 0) or c = j (axis 1). */
+ORC_API void orc_quantize_channel(const float* x, int64_t rows, int64_t cols, int axis, const float* s, int fmt,
+                                  uint8_t* q) {
+#pragma omp parallel for schedule(static)
+    for (int64_t i = 0; i < rows; ++i)
+        for (int64_t j = 0; j < cols; ++j) {
+            double sc = (double)s[axis == 0 ? i : j];
+            float t = (float)((double)x[i * cols + j] / sc);
+            q[i * cols + j] = fp8_encode(fmt, (double)t);
+        }
 }
 
 /* q_i = E4M3(fl32(x_i / s)) (P2 §4.3), fl32 being correctly rounded division. */

@@ -1,7 +1,8 @@
 """Parity criteria between the HIP path and the oracle (per element).
 
-V = R * sA * sB is the oracle's exact-order double result, S = sum_k |a*b|
-(unscaled), so the FP32-accumulation allowance is 1e-5 * S * sA * sB:
+V = R * sA * sB is the oracle's exact-order double result (sA[i] * sB[j] for
+per-channel scales), S = sum_k |a*b| (unscaled), so the FP32-accumulation
+allowance is 1e-5 * S * sA * sB:
   F32 output:   |C - V| <= 1e-5 * S * sA * sB
   F16 output:   |C - V| <= 1e-5 * S * sA * sB + ulp16(V)
   E4M3 output:  |dec(C) - sat448(V / sOut)| <= 1e-5 * S * sA * sB / sOut + ulpE4M3(V / sOut)
@@ -28,6 +29,16 @@ import numpy as np
 import oracle as orc
 
 REL = 1e-5
+
+
+def scale_grid(sA, sB):
+    """sA*sB per output element: a scalar for per-tensor scales, the outer
+    product sA[i]*sB[j] (float64) when either is a per-channel vector."""
+    a = np.asarray(sA, np.float64)
+    b = np.asarray(sB, np.float64)
+    if a.size == 1 and b.size == 1:
+        return float(a.reshape(-1)[0]) * float(b.reshape(-1)[0])
+    return a.reshape(-1, 1) * b.reshape(1, -1)
 
 
 def ulp16(x):
@@ -105,7 +116,7 @@ def fp8_dot_allowance(codes_a, codes_b, rows=None, group=8, fmt_a=orc.FMT_E4M3, 
 
 def check_f32(C, R, S, sA=1.0, sB=1.0, what="F32 output", T=None):
     C = np.asarray(C, np.float64)
-    sc = float(sA) * float(sB)
+    sc = scale_grid(sA, sB)
     V = R * sc
     bound = REL * S * sc + (0.0 if T is None else T * sc)
     finite_ref = np.isfinite(V)
@@ -116,7 +127,7 @@ def check_f32(C, R, S, sA=1.0, sB=1.0, what="F32 output", T=None):
 
 def check_f16(C, R, S, sA=1.0, sB=1.0, what="F16 output", T=None):
     C = np.asarray(C).astype(np.float64)
-    sc = float(sA) * float(sB)
+    sc = scale_grid(sA, sB)
     V = R * sc
     ref16 = orc.f16_decode(orc.out_f16(V))           # the oracle's rounded output
     finite_ref = np.isfinite(ref16)
@@ -132,7 +143,7 @@ def check_fp8(codes, R, S, sA, sB, sOut, fmt, what="FP8 output", T=None):
     codes = np.asarray(codes, np.uint8)
     dec = orc.fp8_decode(codes, fmt)
     fmax, ulp = (57344.0, ulp_e5m2) if fmt == orc.FMT_E5M2 else (448.0, ulp_e4m3)
-    sc = float(sA) * float(sB)
+    sc = scale_grid(sA, sB)
     w = R * sc / float(sOut)
     bound = REL * S * sc / float(sOut) + ulp(w) + (0.0 if T is None else T * sc / float(sOut))
     bad = ~np.isfinite(dec) | (np.abs(dec - np.clip(w, -fmax, fmax)) > bound)

@@ -123,3 +123,10 @@ def random_f16(shape, seed, lo=-1.0, hi=1.0) -> np.ndarray:
 def random_normal_f32(shape, seed) -> np.ndarray:
     g = np.random.default_rng([9002, seed])
     return g.standard_normal(shape, dtype=np.float32)
+
+
+def normal_with_outliers_f32(shape, seed) -> np.ndarray:
+    """N(0,1) FP32 with 0.1% of the positions multiplied by 50 (the outlier
+    mix of the M-sweep workload)."""
+    g = np.random.default_rng([9003, seed])
+    return _outliers(g.standard_normal(shape, dtype=np.float32), g)
