@@ -161,6 +161,61 @@ int amax_f32(const float* x, int64_t n, float* amax, float* scale, hipStream_t s
 int amax_scale_f32(const float* x, int64_t n, float* amax, float* scale, int fmt, int pow2,
                    hipStream_t stream);
 
+/* ------------------------------------------------ per-channel scaling */
+/* P2 §2.1 and §3.2 name per-channel scaling as the finer alternative to one
+ * scale per tensor. A scale applied to the accumulator at write-back (P2 §3.2)
+ * must be constant along K, so the channels are the rows of A[M,K] and the
+ * columns of B[K,N]. The channel calls take a row-major x[rows, cols] and an
+ * axis: GEMM_AXIS_ROW gives one value per row (rows values; use it for A),
+ * GEMM_AXIS_COL one per column (cols values; use it for B). */
+#define GEMM_AXIS_ROW 0
+#define GEMM_AXIS_COL 1
+
+/*
+ * gemm_fp8_channel — gemm_fp8_fmt with a scale per channel:
+ *   C[i,j] = acc[i,j] · sA[i] · sB[j]   (F32, F16 outputs)
+ *   C[i,j] = FP8(acc[i,j] · (1/sOut) · sA[i] · sB[j])   (E4M3 / E5M2 outputs)
+ *   sA     device, float[M]: one scale per row of A
+ *   sB     device, float[N]: one scale per column of B
+ *   sOut   device pointer to one float (per-tensor output scale), required
+ *          iff out_dtype is an FP8 output
+ * Every other argument, output and error as gemm_fp8_fmt. The kernels read
+ * sA[i] and sB[j] only for the elements they store, and form the element's
+ * value as three FP32 products (a few FP32 ulps from the exact product).
+ */
+int gemm_fp8_channel(const uint8_t* A, int fmt_a, const uint8_t* B, int fmt_b,
+                     const float* sA, const float* sB, const float* sOut, void* C, int out_dtype,
+                     int64_t M, int64_t N, int64_t K, hipStream_t stream);
+
+/*
+ * amax_scale_channel_f32 — per channel c of x[rows, cols] (axis as above):
+ *   amax[c]  = max |x| over the channel (exact; NaN if the channel holds a
+ *              NaN; 0 for an empty channel)
+ *   scale[c] = the rule of amax_scale_f32 (fmt, pow2) applied to amax[c];
+ *              written when scale != NULL
+ *   x       device, float[rows*cols] row-major (may be NULL when it is empty)
+ *   amax    device, float[rows] (GEMM_AXIS_ROW) or float[cols] (GEMM_AXIS_COL)
+ *   scale   device, the same length as amax, or NULL
+ * With GEMM_AXIS_COL, amax serves as the running maximum while the call's
+ * kernels run (three launches; one launch for GEMM_AXIS_ROW). Outputs must
+ * not overlap x or each other (GEMM_ERR_ALIAS). Unknown fmt: GEMM_ERR_DTYPE;
+ * an axis other than the two: GEMM_ERR_DIM. No allocation.
+ */
+int amax_scale_channel_f32(const float* x, int64_t rows, int64_t cols, int axis, float* amax,
+                           float* scale, int fmt, int pow2, hipStream_t stream);
+
+/*
+ * quantize_fp8_channel — q[i,j] = FP8_fmt(fl32(x[i,j] / scale[c])) with c = i
+ * (GEMM_AXIS_ROW) or c = j (GEMM_AXIS_COL); rounding, saturation and NaN as
+ * quantize_fp8_fmt (P2 §4.3).
+ *   x      device, float[rows*cols] row-major
+ *   scale  device, float[rows] or float[cols] per the axis
+ *   q      device, uint8[rows*cols], written; must not overlap x or scale
+ * Errors as quantize_fp8_fmt, plus GEMM_ERR_DIM for an unknown axis.
+ */
+int quantize_fp8_channel(const float* x, int64_t rows, int64_t cols, int axis,
+                         const float* scale, uint8_t* q, int fmt, hipStream_t stream);
+
 /* Human-readable name of a status code (a static string). */
 const char* gemm_status_str(int status);
 

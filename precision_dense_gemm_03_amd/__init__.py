@@ -13,6 +13,9 @@ Functions keep the C names:
     quantize_fp8_fmt(x, scale, fmt, q=None, stream=None) -> q
     amax_f32(x, amax=None, scale=None, stream=None) -> (amax, scale)
     amax_scale_f32(x, fmt, pow2, amax=None, scale=None, stream=None) -> (amax, scale)
+    gemm_fp8_channel(A, fmt_a, B, fmt_b, sA, sB, C, sOut=None, stream=None, out_fmt=None)
+    quantize_fp8_channel(x, scale, axis, fmt, q=None, stream=None) -> q
+    amax_scale_channel_f32(x, axis, fmt, pow2, amax=None, scale=None, stream=None) -> (amax, scale)
     select_config(kind, out_dtype, M, N, K) -> str   (host-only query)
     select_config_fmt(kind, out_dtype, M, N, K, fmt_a, fmt_b) -> str
 The output dtype of a GEMM is taken from C: float32, float16, or 8-bit codes
@@ -33,6 +36,8 @@ FMT_E4M3 = 0
 FMT_E5M2 = 1
 KIND_F16 = 0
 KIND_FP8 = 1
+AXIS_ROW = 0
+AXIS_COL = 1
 
 GEMM_OK = 0
 STATUS_NAMES = {
@@ -78,6 +83,12 @@ def lib() -> ctypes.CDLL:
     L.quantize_fp8_fmt.argtypes = [vp, i64, vp, vp, i32, vp]
     L.amax_scale_f32.restype = i32
     L.amax_scale_f32.argtypes = [vp, i64, vp, vp, i32, i32, vp]
+    L.gemm_fp8_channel.restype = i32
+    L.gemm_fp8_channel.argtypes = [vp, i32, vp, i32, vp, vp, vp, vp, i32, i64, i64, i64, vp]
+    L.amax_scale_channel_f32.restype = i32
+    L.amax_scale_channel_f32.argtypes = [vp, i64, i64, i32, vp, vp, i32, i32, vp]
+    L.quantize_fp8_channel.restype = i32
+    L.quantize_fp8_channel.argtypes = [vp, i64, i64, i32, vp, vp, i32, vp]
     L.gemm_select_config_fmt.restype = i32
     L.gemm_select_config_fmt.argtypes = [i32, i32, i64, i64, i64, i32, i32, ctypes.c_char_p, i32]
     _lib = L
@@ -179,6 +190,64 @@ def gemm_fp8_fmt(A, fmt_a, B, fmt_b, sA, sB, C, sOut=None, stream=None, out_fmt=
     _check(lib().gemm_fp8_fmt(_ptr(A), int(fmt_a), _ptr(B), int(fmt_b), _ptr(sA), _ptr(sB), _ptr(sOut), _ptr(Cv),
                               out, M, N, K, _stream_handle(stream)), "gemm_fp8_fmt")
     return C
+
+
+def gemm_fp8_channel(A, fmt_a, B, fmt_b, sA, sB, C, sOut=None, stream=None, out_fmt=None):
+    """gemm_fp8_fmt with per-channel scales: sA float32[M] (one per row of A),
+    sB float32[N] (one per column of B); sOut stays one element."""
+    A, B = _u8(A), _u8(B)
+    out = _out_dtype(C, out_fmt)
+    Cv = _u8(C) if out in (OUT_E4M3, OUT_E5M2) else C
+    M, N, K = _dims(A, B, Cv)
+    torch = _torch()
+    for name, s, n in (("sA", sA, M), ("sB", sB, N)):
+        if s.dtype != torch.float32 or s.numel() != n:
+            raise ValueError(f"{name} must be float32 with one scale per channel ({n})")
+    _check(lib().gemm_fp8_channel(_ptr(A), int(fmt_a), _ptr(B), int(fmt_b), _ptr(sA), _ptr(sB), _ptr(sOut),
+                                  _ptr(Cv), out, M, N, K, _stream_handle(stream)), "gemm_fp8_channel")
+    return C
+
+
+def _rows_cols(x):
+    if x.dim() != 2:
+        raise ValueError("per-channel calls take a 2-D x")
+    return int(x.shape[0]), int(x.shape[1])
+
+
+def quantize_fp8_channel(x, scale, axis, fmt, q=None, stream=None):
+    """FP8 codes of x[i,j] / scale[i] (axis AXIS_ROW) or / scale[j] (AXIS_COL)."""
+    torch = _torch()
+    if x.dtype != torch.float32:
+        raise ValueError("quantize_fp8_channel takes float32 input")
+    rows, cols = _rows_cols(x)
+    if scale.dtype != torch.float32 or scale.numel() != (rows if axis == AXIS_ROW else cols):
+        raise ValueError("one float32 scale per channel")
+    if q is None:
+        q = torch.empty(x.shape, dtype=torch.uint8, device=x.device)
+    qv = _u8(q)
+    if qv.numel() != x.numel():
+        raise ValueError("q must have as many elements as x")
+    _check(lib().quantize_fp8_channel(_ptr(x), rows, cols, int(axis), _ptr(scale), _ptr(qv), int(fmt),
+                                      _stream_handle(stream)), "quantize_fp8_channel")
+    return q
+
+
+def amax_scale_channel_f32(x, axis, fmt, pow2, amax=None, scale=None, stream=None):
+    """(amax, scale) per row (axis AXIS_ROW) or per column (AXIS_COL) of x."""
+    torch = _torch()
+    if x.dtype != torch.float32:
+        raise ValueError("amax_scale_channel_f32 takes float32 input")
+    rows, cols = _rows_cols(x)
+    n = rows if axis == AXIS_ROW else cols
+    if amax is None:
+        amax = torch.empty(n, dtype=torch.float32, device=x.device)
+    if scale is None:
+        scale = torch.empty(n, dtype=torch.float32, device=x.device)
+    if amax.numel() != n or scale.numel() != n:
+        raise ValueError("amax and scale need one element per channel")
+    _check(lib().amax_scale_channel_f32(_ptr(x), rows, cols, int(axis), _ptr(amax), _ptr(scale), int(fmt),
+                                        1 if pow2 else 0, _stream_handle(stream)), "amax_scale_channel_f32")
+    return amax, scale
 
 
 def quantize_fp8(x, scale, q=None, stream=None):

@@ -89,10 +89,11 @@ int gemm_f16(const void* A, const void* B, void* C, int out_dtype, int64_t M, in
     return run_gemm(KIND_F16, a);
 }
 
-// Shared by gemm_fp8_scaled and gemm_fp8_fmt: validation, then the launch.
+// Shared by gemm_fp8_scaled, gemm_fp8_fmt and gemm_fp8_channel: validation,
+// then the launch. channel: sA holds M floats and sB N floats.
 static int gemm_fp8_common(const uint8_t* A, int fmt_a, const uint8_t* B, int fmt_b, const float* sA,
                            const float* sB, const float* sOut, void* C, int out_dtype, int64_t M, int64_t N,
-                           int64_t K, hipStream_t stream) {
+                           int64_t K, hipStream_t stream, int channel = 0) {
     if (out_dtype < GEMM_OUT_F32 || out_dtype > GEMM_OUT_E5M2) return GEMM_ERR_DTYPE;
     if ((fmt_a != GEMM_FMT_E4M3 && fmt_a != GEMM_FMT_E5M2) || (fmt_b != GEMM_FMT_E4M3 && fmt_b != GEMM_FMT_E5M2))
         return GEMM_ERR_DTYPE;
@@ -103,11 +104,13 @@ static int gemm_fp8_common(const uint8_t* A, int fmt_a, const uint8_t* B, int fm
         if (K > 0 && (!A || !B)) return GEMM_ERR_NULL;
         const int64_t cbytes = M * N * out_size(out_dtype);
         if (K > 0 && (overlaps(C, cbytes, A, M * K) || overlaps(C, cbytes, B, K * N))) return GEMM_ERR_ALIAS;
-        if (overlaps(C, cbytes, sA, 4) || overlaps(C, cbytes, sB, 4) ||
+        const int64_t sa_bytes = channel ? 4 * M : 4, sb_bytes = channel ? 4 * N : 4;
+        if (overlaps(C, cbytes, sA, sa_bytes) || overlaps(C, cbytes, sB, sb_bytes) ||
             (fp8_out(out_dtype) && overlaps(C, cbytes, sOut, 4)))
             return GEMM_ERR_ALIAS;
     }
-    GemmArgs a{A, B, C, sA, sB, fp8_out(out_dtype) ? sOut : nullptr, out_dtype, M, N, K, stream, fmt_a, fmt_b};
+    GemmArgs a{A, B, C, sA, sB, fp8_out(out_dtype) ? sOut : nullptr, out_dtype, M, N, K, stream, fmt_a, fmt_b,
+               channel};
     return run_gemm(KIND_FP8, a);
 }
 
@@ -119,6 +122,44 @@ int gemm_fp8_scaled(const uint8_t* A, const uint8_t* B, const float* sA, const f
 int gemm_fp8_fmt(const uint8_t* A, int fmt_a, const uint8_t* B, int fmt_b, const float* sA, const float* sB,
                  const float* sOut, void* C, int out_dtype, int64_t M, int64_t N, int64_t K, hipStream_t stream) {
     return gemm_fp8_common(A, fmt_a, B, fmt_b, sA, sB, sOut, C, out_dtype, M, N, K, stream);
+}
+
+int gemm_fp8_channel(const uint8_t* A, int fmt_a, const uint8_t* B, int fmt_b, const float* sA, const float* sB,
+                     const float* sOut, void* C, int out_dtype, int64_t M, int64_t N, int64_t K, hipStream_t stream) {
+    return gemm_fp8_common(A, fmt_a, B, fmt_b, sA, sB, sOut, C, out_dtype, M, N, K, stream, 1);
+}
+
+int amax_scale_channel_f32(const float* x, int64_t rows, int64_t cols, int axis, float* amax, float* scale, int fmt,
+                           int pow2, hipStream_t stream) {
+    if (fmt != GEMM_FMT_E4M3 && fmt != GEMM_FMT_E5M2) return GEMM_ERR_DTYPE;
+    if (axis != GEMM_AXIS_ROW && axis != GEMM_AXIS_COL) return GEMM_ERR_DIM;
+    if (!dim_ok(rows) || !dim_ok(cols)) return GEMM_ERR_DIM;
+    const int64_t nch = axis == GEMM_AXIS_ROW ? rows : cols;
+    if (nch == 0) return GEMM_OK;
+    if (!amax) return GEMM_ERR_NULL;
+    const int64_t xbytes = 4 * rows * cols;
+    if (xbytes > 0 && !x) return GEMM_ERR_NULL;
+    if (overlaps(amax, 4 * nch, x, xbytes) || overlaps(scale, 4 * nch, x, xbytes) ||
+        overlaps(amax, 4 * nch, scale, 4 * nch))
+        return GEMM_ERR_ALIAS;
+    const int st = check_device();
+    if (st != GEMM_OK) return st;
+    return status_of(launch_amax_channel(x, rows, cols, axis, amax, scale, fmt, pow2 ? 1 : 0, stream));
+}
+
+int quantize_fp8_channel(const float* x, int64_t rows, int64_t cols, int axis, const float* scale, uint8_t* q,
+                         int fmt, hipStream_t stream) {
+    if (fmt != GEMM_FMT_E4M3 && fmt != GEMM_FMT_E5M2) return GEMM_ERR_DTYPE;
+    if (axis != GEMM_AXIS_ROW && axis != GEMM_AXIS_COL) return GEMM_ERR_DIM;
+    if (!dim_ok(rows) || !dim_ok(cols)) return GEMM_ERR_DIM;
+    const int64_t n = rows * cols;
+    if (n == 0) return GEMM_OK;
+    if (!x || !scale || !q) return GEMM_ERR_NULL;
+    const int64_t nch = axis == GEMM_AXIS_ROW ? rows : cols;
+    if (overlaps(q, n, x, 4 * n) || overlaps(q, n, scale, 4 * nch)) return GEMM_ERR_ALIAS;
+    const int st = check_device();
+    if (st != GEMM_OK) return st;
+    return status_of(launch_quantize_channel(x, rows, cols, axis, scale, q, fmt, stream));
 }
 
 int quantize_fp8_fmt(const float* x, int64_t n, const float* scale, uint8_t* q, int fmt, hipStream_t stream) {

@@ -118,6 +118,18 @@ __device__ __forceinline__ float epilogue_multiplier(const float* sA, const floa
     return fp8_out ? s / *sOut : s;
 }
 
+// Epilogue options passed to the tile kernels as one uniform integer.
+enum EpilogueFlags { EPI_E5M2 = 1, EPI_CHANNEL = 2 };
+
+// Per-tensor multiplier, or with per-channel scales (sA[M], sB[N]) the part
+// common to every element: 1 / sOut for an FP8 output, else 1; the element
+// (i, j) is then multiplied by sA[i] * sB[j] as it is stored.
+__device__ __forceinline__ float epilogue_base(const float* sA, const float* sB, const float* sOut, bool fp8_out,
+                                               bool channel) {
+    if (channel) return fp8_out ? 1.0f / *sOut : 1.0f;
+    return epilogue_multiplier(sA, sB, sOut, fp8_out);
+}
+
 // Stores one output element of the final value y (already multiplied by the
 // epilogue multiplier).
 __device__ __forceinline__ void store_out(void* C, int64_t idx, float y, int out_dtype) {

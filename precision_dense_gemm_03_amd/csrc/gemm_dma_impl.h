@@ -171,15 +171,16 @@ __device__ __forceinline__ void interleave_reads_with_mfma() {
     }
 }
 
-// OUT_E4M3 stands for both FP8 outputs; out_e5m2 (uniform) picks the format.
+// OUT_E4M3 stands for both FP8 outputs; EPI_E5M2 in eflags (uniform) picks the
+// format.
 template <int OUT>
-__device__ __forceinline__ void store_one(void* C, int64_t idx, float y, int out_e5m2) {
+__device__ __forceinline__ void store_one(void* C, int64_t idx, float y, int eflags) {
     if constexpr (OUT == OUT_F32) {
         reinterpret_cast<float*>(C)[idx] = y;
     } else if constexpr (OUT == OUT_F16) {
         reinterpret_cast<_Float16*>(C)[idx] = (_Float16)y;
     } else {
-        reinterpret_cast<uint8_t*>(C)[idx] = out_e5m2 ? e5m2_from_f32(y) : e4m3_from_f32(y);
+        reinterpret_cast<uint8_t*>(C)[idx] = (eflags & EPI_E5M2) ? e5m2_from_f32(y) : e4m3_from_f32(y);
     }
 }
 
@@ -188,7 +189,7 @@ __global__ __launch_bounds__(256) void gemm_dma_kernel(const uint8_t* __restrict
                                                        void* __restrict__ C, int M, int N, int K,
                                                        const float* __restrict__ sA, const float* __restrict__ sB,
                                                        const float* __restrict__ sOut, int tiles_m, int tiles_n,
-                                                       int out_e5m2) {
+                                                       int eflags) {
     using T = Dma<ES, STAGES>;
     using Op = typename Mfma32<ES>::op;
     static_assert(STAGES - 2 <= 3, "wait_outstanding_tiles covers at most three tiles in flight");
@@ -382,7 +383,11 @@ __global__ __launch_bounds__(256) void gemm_dma_kernel(const uint8_t* __restrict
 
     // ---- epilogue: y = acc * (sA*sB), converted; rows/columns past M/N are not stored ----
     // 32x32 accumulator element r of lane l: row 8*(r/4) + 4*(l/32) + r%4, column l%32.
-    const float scale = epilogue_multiplier(sA, sB, sOut, OUT == OUT_E4M3);
+    // Per-tensor: y = acc * sA*sB (/ sOut). Per-channel (EPI_CHANNEL, sA[M] and
+    // sB[N]): y = acc * (1/sOut) * sA[row] * sB[col], loaded only for stored
+    // elements.
+    const bool chan = (eflags & EPI_CHANNEL) != 0;
+    const float scale = epilogue_base(sA, sB, sOut, OUT == OUT_E4M3, chan);
     const int row0 = m0 + wm * 128 + 4 * h;
     const int col0 = n0 + wn * 128 + (lane & 31);
     const bool interior = (m0 + T::BM <= M) && (n0 + T::BN <= N);
@@ -394,8 +399,11 @@ __global__ __launch_bounds__(256) void gemm_dma_kernel(const uint8_t* __restrict
             for (int r = 0; r < 16; ++r) {
                 const int row = row0 + tm * 32 + 8 * (r >> 2) + (r & 3);
                 const int col = col0 + tn * 32;
-                if (interior || (row < M && col < N))
-                    store_one<OUT>(C, (int64_t)row * N + col, acc[tm][tn][r] * scale, out_e5m2);
+                if (interior || (row < M && col < N)) {
+                    float y = acc[tm][tn][r] * scale;
+                    if (chan) y *= sA[row] * sB[col];
+                    store_one<OUT>(C, (int64_t)row * N + col, y, eflags);
+                }
             }
 }
 
@@ -427,20 +435,21 @@ hipError_t launch_dma(const GemmArgs& a) {
     const uint8_t* B = reinterpret_cast<const uint8_t*>(a.B);
     const int M = (int)a.M, N = (int)a.N, K = (int)a.K;
     const dim3 grid((unsigned)blocks), block(T::NT);
+    const int eflags = (a.out_dtype == OUT_E5M2 ? EPI_E5M2 : 0) | (a.channel ? EPI_CHANNEL : 0);
     switch (a.out_dtype) {
         case OUT_F32:
             gemm_dma_kernel<ES, OUT_F32, STAGES, FA, FB><<<grid, block, 0, a.stream>>>(
-                A, B, a.C, M, N, K, a.sA, a.sB, a.sOut, (int)tiles_m, (int)tiles_n, 0);
+                A, B, a.C, M, N, K, a.sA, a.sB, a.sOut, (int)tiles_m, (int)tiles_n, eflags);
             break;
         case OUT_F16:
             gemm_dma_kernel<ES, OUT_F16, STAGES, FA, FB><<<grid, block, 0, a.stream>>>(
-                A, B, a.C, M, N, K, a.sA, a.sB, a.sOut, (int)tiles_m, (int)tiles_n, 0);
+                A, B, a.C, M, N, K, a.sA, a.sB, a.sOut, (int)tiles_m, (int)tiles_n, eflags);
             break;
         default:
             if constexpr (ES == 1) {
                 gemm_dma_kernel<ES, OUT_E4M3, STAGES, FA, FB><<<grid, block, 0, a.stream>>>(
                     A, B, a.C, M, N, K, a.sA, a.sB, a.sOut, (int)tiles_m, (int)tiles_n,
-                    a.out_dtype == OUT_E5M2 ? 1 : 0);
+                    eflags);
             } else {
                 return hipErrorInvalidValue;
             }

@@ -68,7 +68,7 @@ __global__ __launch_bounds__(NT) void gemm_stream_kernel(const uint8_t* __restri
                                                          int64_t M, int64_t N, int64_t K,
                                                          const float* __restrict__ sA, const float* __restrict__ sB,
                                                          const float* __restrict__ sOut, int out_dtype, int a_vec,
-                                                         int b_vec) {
+                                                         int b_vec, int channel) {
     constexpr int VE = 16 / ES;
     constexpr int CX = COLS / VE;
     constexpr int KY = NT / CX;
@@ -182,7 +182,8 @@ __global__ __launch_bounds__(NT) void gemm_stream_kernel(const uint8_t* __restri
             for (int e = 0; e < VE; ++e) red[wave][m][lane * VE + e] = acc[m][e];
     }
     __syncthreads();
-    const float scale = epilogue_multiplier(sA, sB, sOut, out_dtype == OUT_E4M3 || out_dtype == OUT_E5M2);
+    // per-channel scales (sA[M], sB[N]) are applied per stored element
+    const float scale = epilogue_base(sA, sB, sOut, out_dtype == OUT_E4M3 || out_dtype == OUT_E5M2, channel != 0);
 
     for (int o = tid; o < MMAX * COLS; o += NT) {
         const int m = o / COLS, c = o % COLS;
@@ -190,7 +191,11 @@ __global__ __launch_bounds__(NT) void gemm_stream_kernel(const uint8_t* __restri
 #pragma unroll
         for (int w = 1; w < NW; ++w) s += red[w][m][c];
         const int64_t col = n0 + c;
-        if (m < M && col < N) store_out(C, (int64_t)m * N + col, s * scale, out_dtype);
+        if (m < M && col < N) {
+            float y = s * scale;
+            if (channel) y *= sA[m] * sB[col];
+            store_out(C, (int64_t)m * N + col, y, out_dtype);
+        }
     }
     (void)SLW;
 }
@@ -206,7 +211,7 @@ hipError_t launch_stream(const GemmArgs& a) {
     const int b_vec = aligned16(a.B) && ((a.N * ES) % 16 == 0);
     gemm_stream_kernel<ES, MMAX, COLS, NT, U, FA, FB><<<(unsigned)blocks, NT, 0, a.stream>>>(
         reinterpret_cast<const uint8_t*>(a.A), reinterpret_cast<const uint8_t*>(a.B), a.C, a.M, a.N, a.K, a.sA,
-        a.sB, a.sOut, a.out_dtype, a_vec, b_vec);
+        a.sB, a.sOut, a.out_dtype, a_vec, b_vec, a.channel ? 1 : 0);
     return hipGetLastError();
 }
 

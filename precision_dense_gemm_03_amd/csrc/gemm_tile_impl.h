@@ -146,15 +146,16 @@ __device__ __forceinline__ v4u load_chunk_guarded(const uint8_t* row_ptr, bool r
     return v4u{w[0], w[1], w[2], w[3]};
 }
 
-// OUT_E4M3 stands for both FP8 outputs; out_e5m2 (uniform) picks the format.
+// OUT_E4M3 stands for both FP8 outputs; EPI_E5M2 in eflags (uniform) picks the
+// format.
 template <int OUT>
-__device__ __forceinline__ void store_one(void* C, int64_t idx, float y, int out_e5m2) {
+__device__ __forceinline__ void store_one(void* C, int64_t idx, float y, int eflags) {
     if constexpr (OUT == OUT_F32) {
         reinterpret_cast<float*>(C)[idx] = y;
     } else if constexpr (OUT == OUT_F16) {
         reinterpret_cast<_Float16*>(C)[idx] = (_Float16)y;
     } else {
-        reinterpret_cast<uint8_t*>(C)[idx] = out_e5m2 ? e5m2_from_f32(y) : e4m3_from_f32(y);
+        reinterpret_cast<uint8_t*>(C)[idx] = (eflags & EPI_E5M2) ? e5m2_from_f32(y) : e4m3_from_f32(y);
     }
 }
 
@@ -162,7 +163,7 @@ template <int ES, int OUT, int BM, int BN, int BK, int WM, int WN, int FA, int F
 __global__ __launch_bounds__(64 * WM * WN) void gemm_tile_kernel(
     const uint8_t* __restrict__ A, const uint8_t* __restrict__ B, void* __restrict__ C, int M, int N, int K,
     const float* __restrict__ sA, const float* __restrict__ sB, const float* __restrict__ sOut, int tiles_m,
-    int tiles_n, int aligned, int out_e5m2) {
+    int tiles_n, int aligned, int eflags) {
     using T = Tile<ES, BM, BN, BK, WM, WN>;
     __shared__ __attribute__((aligned(16))) uint8_t smem_raw[2 * T::STAGE];
     LDS_AS uint8_t* smem = (LDS_AS uint8_t*)smem_raw;
@@ -388,7 +389,11 @@ __global__ __launch_bounds__(64 * WM * WN) void gemm_tile_kernel(
     }
 
     // Epilogue: y = acc * (sA*sB), converted, stored with M/N predication on edge tiles.
-    const float scale = epilogue_multiplier(sA, sB, sOut, OUT == OUT_E4M3);  // both FP8 outputs
+    // Per-tensor: y = acc * sA*sB (/ sOut). Per-channel (EPI_CHANNEL, sA[M] and
+    // sB[N]): y = acc * (1/sOut) * sA[row] * sB[col], loaded only for stored
+    // elements.
+    const bool chan = (eflags & EPI_CHANNEL) != 0;
+    const float scale = epilogue_base(sA, sB, sOut, OUT == OUT_E4M3, chan);  // both FP8 outputs
     const int row0 = m0 + wm * T::WTM + 4 * g;
     const int col0 = n0 + wn * T::WTN + j16;
     if (interior_mn) {
@@ -397,8 +402,12 @@ __global__ __launch_bounds__(64 * WM * WN) void gemm_tile_kernel(
 #pragma unroll
             for (int tn = 0; tn < T::TN; ++tn)
 #pragma unroll
-                for (int r = 0; r < 4; ++r)
-                    store_one<OUT>(C, (int64_t)(row0 + tm * 16 + r) * N + col0 + tn * 16, acc[tm][tn][r] * scale, out_e5m2);
+                for (int r = 0; r < 4; ++r) {
+                    const int row = row0 + tm * 16 + r, col = col0 + tn * 16;
+                    float y = acc[tm][tn][r] * scale;
+                    if (chan) y *= sA[row] * sB[col];
+                    store_one<OUT>(C, (int64_t)row * N + col, y, eflags);
+                }
     } else {
 #pragma unroll
         for (int tm = 0; tm < T::TM; ++tm)
@@ -407,8 +416,11 @@ __global__ __launch_bounds__(64 * WM * WN) void gemm_tile_kernel(
 #pragma unroll
                 for (int r = 0; r < 4; ++r) {
                     const int row = row0 + tm * 16 + r, col = col0 + tn * 16;
-                    if (row < M && col < N)
-                        store_one<OUT>(C, (int64_t)row * N + col, acc[tm][tn][r] * scale, out_e5m2);
+                    if (row < M && col < N) {
+                        float y = acc[tm][tn][r] * scale;
+                        if (chan) y *= sA[row] * sB[col];
+                        store_one<OUT>(C, (int64_t)row * N + col, y, eflags);
+                    }
                 }
     }
 }
@@ -429,20 +441,21 @@ hipError_t launch_tile(const GemmArgs& a) {
     const uint8_t* B = reinterpret_cast<const uint8_t*>(a.B);
     const int M = (int)a.M, N = (int)a.N, K = (int)a.K;
     const dim3 grid((unsigned)blocks), block(64 * WM * WN);
+    const int eflags = (a.out_dtype == OUT_E5M2 ? EPI_E5M2 : 0) | (a.channel ? EPI_CHANNEL : 0);
     switch (a.out_dtype) {
         case OUT_F32:
             gemm_tile_kernel<ES, OUT_F32, BM, BN, BK, WM, WN, FA, FB><<<grid, block, 0, a.stream>>>(
-                A, B, a.C, M, N, K, a.sA, a.sB, a.sOut, (int)tiles_m, (int)tiles_n, aligned, 0);
+                A, B, a.C, M, N, K, a.sA, a.sB, a.sOut, (int)tiles_m, (int)tiles_n, aligned, eflags);
             break;
         case OUT_F16:
             gemm_tile_kernel<ES, OUT_F16, BM, BN, BK, WM, WN, FA, FB><<<grid, block, 0, a.stream>>>(
-                A, B, a.C, M, N, K, a.sA, a.sB, a.sOut, (int)tiles_m, (int)tiles_n, aligned, 0);
+                A, B, a.C, M, N, K, a.sA, a.sB, a.sOut, (int)tiles_m, (int)tiles_n, aligned, eflags);
             break;
         default:
             if constexpr (ES == 1) {
                 gemm_tile_kernel<ES, OUT_E4M3, BM, BN, BK, WM, WN, FA, FB><<<grid, block, 0, a.stream>>>(
                     A, B, a.C, M, N, K, a.sA, a.sB, a.sOut, (int)tiles_m, (int)tiles_n, aligned,
-                    a.out_dtype == OUT_E5M2 ? 1 : 0);
+                    eflags);
             } else {
                 return hipErrorInvalidValue;
             }

@@ -13,14 +13,15 @@ struct GemmArgs {
     const void* A;
     const void* B;
     void* C;
-    const float* sA;   // device scalars; NULL for FP16 (scale 1)
+    const float* sA;   // device scalars (per-channel: sA[M], sB[N]); NULL for FP16
     const float* sB;
-    const float* sOut; // device scalar; only read for E4M3 output
+    const float* sOut; // device scalar; only read for FP8 outputs
     int out_dtype;
     int64_t M, N, K;
     hipStream_t stream;
     int fmt_a = 0;     // FP8 operand formats (Fp8Format: 0 = E4M3, 1 = E5M2); 0 for FP16
     int fmt_b = 0;
+    int channel = 0;   // 1: sA holds M per-row scales and sB N per-column scales
 };
 
 typedef hipError_t (*GemmLauncher)(const GemmArgs&);
@@ -58,6 +59,13 @@ const GemmConfig* select_config(int kind, int out_dtype, int64_t M, int64_t N, i
 // power-of-two scale.
 hipError_t launch_amax(const float* x, int64_t n, float* amax, float* scale, int fmt, int pow2, hipStream_t stream);
 hipError_t launch_quantize(const float* x, int64_t n, const float* scale, uint8_t* q, int fmt, hipStream_t stream);
+// Per-channel amax / scale / quantize over a row-major x[rows, cols]: axis 0
+// one channel per row, axis 1 one per column. For axis 1, amax doubles as the
+// running maximum while the launches run.
+hipError_t launch_amax_channel(const float* x, int64_t rows, int64_t cols, int axis, float* amax, float* scale,
+                               int fmt, int pow2, hipStream_t stream);
+hipError_t launch_quantize_channel(const float* x, int64_t rows, int64_t cols, int axis, const float* scale,
+                                   uint8_t* q, int fmt, hipStream_t stream);
 // Writes zeros to an [M,N] output of the given dtype (the K = 0 empty sum).
 hipError_t launch_fill_zero(void* C, int64_t count, int out_dtype, hipStream_t stream);
 

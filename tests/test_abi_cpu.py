@@ -39,7 +39,8 @@ def test_header_declares_the_entry_points():
     names = set(header_functions())
     assert {"gemm_f16", "gemm_fp8_scaled", "quantize_fp8", "amax_f32", "gemm_status_str",
             "gemm_select_config", "gemm_fp8_fmt", "quantize_fp8_fmt", "amax_scale_f32",
-            "gemm_select_config_fmt"} <= names
+            "gemm_select_config_fmt", "gemm_fp8_channel", "amax_scale_channel_f32",
+            "quantize_fp8_channel"} <= names
 
 
 def test_library_exports_every_declared_symbol():
@@ -55,6 +56,7 @@ def test_binding_constants_match_header():
     d = header_defines()
     assert d["GEMM_OUT_F32"] == g.OUT_F32 and d["GEMM_OUT_F16"] == g.OUT_F16 and d["GEMM_OUT_E4M3"] == g.OUT_E4M3
     assert d["GEMM_OUT_E5M2"] == g.OUT_E5M2 and d["GEMM_FMT_E4M3"] == g.FMT_E4M3 and d["GEMM_FMT_E5M2"] == g.FMT_E5M2
+    assert d["GEMM_AXIS_ROW"] == g.AXIS_ROW and d["GEMM_AXIS_COL"] == g.AXIS_COL
     for code, name in g.STATUS_NAMES.items():
         assert d[name] == code
 
@@ -113,6 +115,34 @@ def test_format_entry_points_argument_validation():
     buf = ctypes.create_string_buffer(64)
     assert L.gemm_select_config_fmt(1, 0, 8, 8, 8, 3, 0, buf, 64) == -3
     assert L.gemm_select_config_fmt(0, 3, 8, 8, 8, 0, 0, buf, 64) == -3          # FP16 cannot write FP8
+
+
+def test_channel_entry_points_argument_validation():
+    L = g.lib()
+    s = FAKE3 + (1 << 20)
+    # gemm_fp8_channel: sA covers M floats and sB N floats for the overlap check
+    assert L.gemm_fp8_channel(FAKE, 0, FAKE2, 0, s, s + 64, None, FAKE3, 2, 4, 4, 4, None) == -4
+    assert L.gemm_fp8_channel(FAKE, 3, FAKE2, 0, s, s + 64, None, FAKE3, 0, 4, 4, 4, None) == -3
+    assert L.gemm_fp8_channel(FAKE, 0, FAKE2, 0, None, s, None, FAKE3, 0, 4, 4, 4, None) == -1
+    assert L.gemm_fp8_channel(FAKE, 0, FAKE2, 0, FAKE3 - 12, s, None, FAKE3, 0, 4, 4, 4, None) == -8  # sA[3] in C
+    assert L.gemm_fp8_channel(FAKE, 0, FAKE2, 0, s, FAKE3 + 60, None, FAKE3, 0, 4, 4, 4, None) == -8  # C[15] in sB
+    assert L.gemm_fp8_channel(FAKE, 0, FAKE2, 0, s, s, None, FAKE3, 0, 4, -1, 4, None) == -2
+    # amax_scale_channel_f32(x, rows, cols, axis, amax, scale, fmt, pow2, stream)
+    assert L.amax_scale_channel_f32(FAKE, 4, 8, 2, FAKE2, FAKE3, 0, 0, None) == -2        # unknown axis
+    assert L.amax_scale_channel_f32(FAKE, 4, 8, 0, FAKE2, FAKE3, 4, 0, None) == -3
+    assert L.amax_scale_channel_f32(FAKE, -4, 8, 0, FAKE2, FAKE3, 0, 0, None) == -2
+    assert L.amax_scale_channel_f32(FAKE, 4, 8, 1, None, FAKE3, 0, 0, None) == -1
+    assert L.amax_scale_channel_f32(None, 4, 8, 1, FAKE2, FAKE3, 0, 0, None) == -1
+    assert L.amax_scale_channel_f32(FAKE, 4, 8, 0, FAKE + 100, None, 0, 0, None) == -8   # amax inside x
+    assert L.amax_scale_channel_f32(FAKE, 4, 8, 1, FAKE2, FAKE2 + 28, 0, 0, None) == -8  # amax[7] = scale[0]
+    assert L.amax_scale_channel_f32(None, 0, 8, 0, None, None, 0, 0, None) == 0          # no channels
+    # quantize_fp8_channel(x, rows, cols, axis, scale, q, fmt, stream)
+    assert L.quantize_fp8_channel(FAKE, 4, 8, 5, FAKE2, FAKE3, 0, None) == -2
+    assert L.quantize_fp8_channel(FAKE, 4, 8, 0, FAKE2, FAKE3, 2, None) == -3
+    assert L.quantize_fp8_channel(FAKE, 4, 8, 0, None, FAKE3, 0, None) == -1
+    assert L.quantize_fp8_channel(FAKE, 4, 8, 1, FAKE2, FAKE2 + 16, 0, None) == -8       # q over scale[4..]
+    assert L.quantize_fp8_channel(FAKE, 4, 8, 0, FAKE2, FAKE + 127, 0, None) == -8
+    assert L.quantize_fp8_channel(None, 0, 8, 0, None, None, 0, None) == 0
 
 
 def test_select_config_formats():

@@ -1,0 +1,243 @@
+"""GPU parity for per-channel scaling: per-row and per-column amax and scales
+(bit-exact), per-channel quantization (bit-exact), and the GEMM with a scale
+per row of A and per column of B on every kernel family and output type,
+element by element against the oracle; then the whole FP32 -> scales ->
+quantize -> GEMM chain at 4096 x 4096 x 4096 on sampled rows."""
+import numpy as np
+import pytest
+import torch
+
+import oracle as orc
+import precision_dense_gemm_03_amd as g
+import workloads as wl
+from parity import REL, check_f16, check_f32, check_fp8, fp8_dot_allowance, scale_grid, ulp16
+
+pytestmark = pytest.mark.gpu
+
+DEV = torch.device("cuda:0")
+ORC_FMT = {g.FMT_E4M3: orc.FMT_E4M3, g.FMT_E5M2: orc.FMT_E5M2}
+
+
+def say(*a):
+    print(*a, flush=True)
+
+
+@pytest.fixture(scope="module", autouse=True)
+def _gpu():
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    torch.cuda.set_device(DEV)
+    g.lib()
+    yield
+    torch.cuda.synchronize()
+
+
+def dev(x):
+    return torch.from_numpy(np.ascontiguousarray(x)).to(DEV)
+
+
+def host(t):
+    torch.cuda.synchronize()
+    return t.cpu().numpy()
+
+
+def scalar(v):
+    return torch.tensor([float(np.float32(v))], dtype=torch.float32, device=DEV)
+
+
+def same_f32(a, b):
+    """Bitwise equality, any NaN matching any NaN."""
+    a, b = np.asarray(a, np.float32), np.asarray(b, np.float32)
+    nan = np.isnan(a)
+    return np.array_equal(nan, np.isnan(b)) and np.array_equal(a[~nan].view(np.uint32), b[~nan].view(np.uint32))
+
+
+def channel_data(rows, cols, seed, specials=False):
+    x = wl.random_normal_f32((rows, cols), seed)
+    e = np.random.default_rng(seed + 1).integers(-20, 21, size=(rows, 1))
+    x = (x * np.exp2(e)).astype(np.float32)
+    if specials and rows > 3 and cols > 3:
+        x[1, 2] = np.inf
+        x[2, 3] = np.nan
+        x[3, :] = 0.0
+    return x
+
+
+# rows x cols: single element, unaligned row length, wide rows, tall columns,
+# vector-path aligned, ragged column block, many short rows.
+SHAPES = [(1, 1), (37, 53), (64, 4096), (4096, 64), (300, 1024), (129, 260), (2049, 12)]
+
+
+@pytest.mark.parametrize("axis", [g.AXIS_ROW, g.AXIS_COL])
+@pytest.mark.parametrize("rows,cols", SHAPES)
+def test_amax_scale_quantize_per_channel(axis, rows, cols):
+    x = channel_data(rows, cols, rows * 7 + cols, specials=True)
+    tx = dev(x)
+    oa = orc.amax_channel(x, axis)
+    for fmt in (g.FMT_E4M3, g.FMT_E5M2):
+        for pow2 in (False, True):
+            say(f"channel amax axis={axis} {rows}x{cols} fmt={fmt} pow2={pow2}")
+            amax, s = g.amax_scale_channel_f32(tx, axis, fmt, pow2)
+            os_ = orc.scale_channel(oa, ORC_FMT[fmt], pow2)
+            assert same_f32(host(amax), oa)
+            assert same_f32(host(s), os_)
+            say(f"channel quantize axis={axis} {rows}x{cols} fmt={fmt} pow2={pow2}")
+            q = g.quantize_fp8_channel(tx, s, axis, fmt)
+            assert np.array_equal(host(q), orc.quantize_channel(x, os_, axis, ORC_FMT[fmt]))
+
+
+@pytest.mark.parametrize("axis", [g.AXIS_ROW, g.AXIS_COL])
+def test_per_channel_unaligned_pointers(axis):
+    """x starting 4 bytes into an allocation and q 1 byte in: the scalar paths."""
+    rows, cols = 70, 132
+    x = channel_data(rows, cols, 91)
+    bx = torch.zeros(rows * cols + 1, dtype=torch.float32, device=DEV)
+    tx = bx[1:].view(rows, cols)
+    tx.copy_(dev(x))
+    bq = torch.zeros(rows * cols + 1, dtype=torch.uint8, device=DEV)
+    tq = bq[1:].view(rows, cols)
+    say(f"channel unaligned axis={axis}")
+    amax, s = g.amax_scale_channel_f32(tx, axis, g.FMT_E4M3, False)
+    oa = orc.amax_channel(x, axis)
+    os_ = orc.scale_channel(oa, orc.FMT_E4M3, False)
+    assert same_f32(host(amax), oa) and same_f32(host(s), os_)
+    g.quantize_fp8_channel(tx, s, axis, g.FMT_E4M3, q=tq)
+    assert np.array_equal(host(tq), orc.quantize_channel(x, os_, axis, orc.FMT_E4M3))
+    assert host(bq)[0] == 0
+
+
+def test_per_channel_empty():
+    say("channel empty shapes")
+    e = torch.empty((0, 5), dtype=torch.float32, device=DEV)
+    amax, s = g.amax_scale_channel_f32(e, g.AXIS_COL, g.FMT_E4M3, False)
+    assert np.array_equal(host(amax), np.zeros(5, np.float32)) and np.array_equal(host(s), np.ones(5, np.float32))
+    amax, s = g.amax_scale_channel_f32(e, g.AXIS_ROW, g.FMT_E4M3, False)
+    assert amax.numel() == 0
+    z = torch.empty((4, 0), dtype=torch.float32, device=DEV)
+    amax, s = g.amax_scale_channel_f32(z, g.AXIS_ROW, g.FMT_E5M2, True)
+    assert np.array_equal(host(amax), np.zeros(4, np.float32)) and np.array_equal(host(s), np.ones(4, np.float32))
+    q = g.quantize_fp8_channel(z, s, g.AXIS_ROW, g.FMT_E5M2)
+    assert q.numel() == 0
+
+
+# ----------------------------------------------------------------- GEMM
+
+SHAPES_GEMM = [(None, 1, 1000, 512), (None, 4, 520, 640), ("tile_fp8_64x64x128_w2x2", 100, 200, 256),
+               ("tile_fp8_128x128x128_w2x2", 300, 272, 384), ("tile_fp8_256x256x128_w2x4", 257, 512, 320),
+               ("dma_fp8_256x256x64_s4", 300, 272, 192), ("dma_fp8_256x256x64_s5", 513, 784, 192)]
+
+
+# the 5-stage direct-load configuration is built for E4M3 x E4M3 only
+GEMM_CASES = [(fa, fb, *shape) for shape in SHAPES_GEMM
+              for (fa, fb) in [(g.FMT_E4M3, g.FMT_E4M3), (g.FMT_E5M2, g.FMT_E4M3)]
+              if not (shape[0] == "dma_fp8_256x256x64_s5" and fa != g.FMT_E4M3)]
+
+
+@pytest.mark.parametrize("fa,fb,cfg,M,N,K", GEMM_CASES)
+def test_gemm_per_channel_scales(fa, fb, cfg, M, N, K, monkeypatch):
+    if cfg:
+        monkeypatch.setenv("LIBGEMM_CONFIG", cfg)
+        assert g.select_config_fmt(g.KIND_FP8, g.OUT_F32, M, N, K, fa, fb) == cfg
+    say(f"gemm per-channel a={fa} b={fb} {cfg} {M}x{N}x{K}")
+    enc = {g.FMT_E4M3: wl.random_e4m3_codes, g.FMT_E5M2: wl.random_e5m2_codes}
+    ca = enc[fa]((M, K), 3 * M + K + fa)
+    cb = enc[fb]((K, N), 5 * N + K + fb)
+    rng = np.random.default_rng(M + N + K)
+    # per-channel scales spread over 2^-6 .. 2^6, not powers of two
+    sA = (np.exp2(rng.uniform(-6, 6, M)) * 0.37).astype(np.float32)
+    sB = (np.exp2(rng.uniform(-6, 6, N)) * 0.11).astype(np.float32)
+    ofa, ofb = ORC_FMT[fa], ORC_FMT[fb]
+    R, S = orc.gemm(ofa, ca, cb, fmt_b=ofb)
+    T = fp8_dot_allowance(ca, cb, fmt_a=ofa, fmt_b=ofb)
+    ta, tb, tsa, tsb = dev(ca), dev(cb), dev(sA), dev(sB)
+    C = torch.empty((M, N), dtype=torch.float32, device=DEV)
+    g.gemm_fp8_channel(ta, fa, tb, fb, tsa, tsb, C)
+    check_f32(host(C), R, S, sA, sB, what="f32 per-channel", T=T)
+    C = torch.empty((M, N), dtype=torch.float16, device=DEV)
+    g.gemm_fp8_channel(ta, fa, tb, fb, tsa, tsb, C)
+    sc = scale_grid(sA, sB)
+    V = R * sc
+    fin = np.abs(V) + (1e-5 * S + T) * sc < 65520.0
+    got16 = host(C).astype(np.float64)
+    check_f16_channel(got16, R, S, sA, sB, T, fin)
+    for out_fmt in (g.FMT_E4M3, g.FMT_E5M2):
+        s_out = orc.scale(np.float32(np.max(np.abs(V))), ORC_FMT[out_fmt])
+        C = torch.empty((M, N), dtype=torch.uint8, device=DEV)
+        g.gemm_fp8_channel(ta, fa, tb, fb, tsa, tsb, C, scalar(s_out), out_fmt=out_fmt)
+        check_fp8(host(C), R, S, sA, sB, s_out, ORC_FMT[out_fmt], what=f"fp8 out {out_fmt} per-channel", T=T)
+
+
+def check_f16_channel(got16, R, S, sA, sB, T, fin):
+    """The F16 bound over the elements whose tolerance interval stays below
+    the FP16 overflow threshold (65520, where RNE turns into inf)."""
+    sc = scale_grid(sA, sB)
+    V = R * sc
+    bound = REL * S * sc + ulp16(V) + T * sc
+    bad = fin & (~np.isfinite(got16) | (np.abs(got16 - V) > bound))
+    if np.any(bad):
+        i = tuple(np.argwhere(bad)[0])
+        raise AssertionError(f"f16 per-channel: {int(bad.sum())} bad; first {i}: got {got16[i]} ref {V[i]}")
+
+
+def test_gemm_per_channel_equal_scales_match_per_tensor():
+    """All sA[i] = a and sB[j] = b: the same values as the per-tensor call
+    within the F32 bound (the products are formed in another order)."""
+    M, N, K = 200, 300, 256
+    ca, cb = wl.random_e4m3_codes((M, K), 61), wl.random_e4m3_codes((K, N), 62)
+    R, S = orc.gemm(orc.FMT_E4M3, ca, cb)
+    a, b = np.float32(0.02), np.float32(0.003)
+    say("gemm per-channel equal scales")
+    C1 = torch.empty((M, N), dtype=torch.float32, device=DEV)
+    g.gemm_fp8_channel(dev(ca), g.FMT_E4M3, dev(cb), g.FMT_E4M3, dev(np.full(M, a, np.float32)),
+                       dev(np.full(N, b, np.float32)), C1)
+    check_f32(host(C1), R, S, a, b, what="equal per-channel scales", T=fp8_dot_allowance(ca, cb))
+
+
+def test_gemm_per_channel_k0_and_validation():
+    say("gemm per-channel K=0")
+    M, N = 5, 7
+    C = torch.full((M, N), 3.0, dtype=torch.float32, device=DEV)
+    A = torch.empty((M, 0), dtype=torch.uint8, device=DEV)
+    B = torch.empty((0, N), dtype=torch.uint8, device=DEV)
+    g.gemm_fp8_channel(A, g.FMT_E4M3, B, g.FMT_E4M3, torch.ones(M, device=DEV), torch.ones(N, device=DEV), C)
+    assert np.array_equal(host(C), np.zeros((M, N), np.float32))
+    with pytest.raises(ValueError):
+        g.gemm_fp8_channel(A, g.FMT_E4M3, B, g.FMT_E4M3, torch.ones(1, device=DEV), torch.ones(N, device=DEV), C)
+
+
+# -------------------------------------------------------- full-size chain
+
+@pytest.mark.parametrize("M", [4096, 3000, 1])
+def test_per_channel_chain_full_size(M):
+    """FP32 A[M,4096] and B[4096,4096] with 0.1% outliers x50 -> per-row and
+    per-column scales -> quantize -> GEMM (FP32 and FP16 outputs) in the
+    launch configuration the selector picks; every code and scale against the
+    oracle, the products on sampled rows."""
+    N = K = 4096
+    say(f"per-channel chain M={M}")
+    xa = wl.normal_with_outliers_f32((M, K), 1201)
+    xb = wl.normal_with_outliers_f32((K, N), 1202)
+    ta, tb = dev(xa), dev(xb)
+    _, s_a = g.amax_scale_channel_f32(ta, g.AXIS_ROW, g.FMT_E4M3, False)
+    _, s_b = g.amax_scale_channel_f32(tb, g.AXIS_COL, g.FMT_E4M3, False)
+    qa = g.quantize_fp8_channel(ta, s_a, g.AXIS_ROW, g.FMT_E4M3)
+    qb = g.quantize_fp8_channel(tb, s_b, g.AXIS_COL, g.FMT_E4M3)
+    osa = orc.scale_channel(orc.amax_channel(xa, 0), orc.FMT_E4M3)
+    osb = orc.scale_channel(orc.amax_channel(xb, 1), orc.FMT_E4M3)
+    assert same_f32(host(s_a), osa) and same_f32(host(s_b), osb)
+    cqa = orc.quantize_channel(xa, osa, 0, orc.FMT_E4M3)
+    cqb = orc.quantize_channel(xb, osb, 1, orc.FMT_E4M3)
+    assert np.array_equal(host(qa), cqa) and np.array_equal(host(qb), cqb)
+    rows = sorted(set([0, M - 1] + list(range(0, M, max(1, M // 24)))))
+    R, S = orc.gemm(orc.FMT_E4M3, cqa, cqb, rows=rows)
+    # outliers put products far apart within one 8-wide k group: the matrix
+    # cores' alignment allowance applies
+    T = fp8_dot_allowance(cqa, cqb, rows=rows)
+    for dt in (torch.float32, torch.float16):
+        C = torch.empty((M, N), dtype=dt, device=DEV)
+        g.gemm_fp8_channel(qa, g.FMT_E4M3, qb, g.FMT_E4M3, s_a, s_b, C)
+        got = host(C)[rows]
+        if dt == torch.float32:
+            check_f32(got, R, S, osa[rows], osb, what=f"chain f32 M={M}", T=T)
+        else:
+            check_f16(got, R, S, osa[rows], osb, what=f"chain f16 M={M}", T=T)
