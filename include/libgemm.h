@@ -45,6 +45,7 @@ extern "C" {
 #define GEMM_ERR_UNSUPPORTED (-6) /* no kernel for this request                            */
 #define GEMM_ERR_DEVICE (-7)      /* no current HIP device, or it is not gfx950            */
 #define GEMM_ERR_ALIAS (-8)       /* the output overlaps an input                          */
+#define GEMM_ERR_WORKSPACE (-9)   /* a split-K workspace too small or not 16-byte aligned   */
 
 /* ------------------------------------------------------- output types */
 #define GEMM_OUT_F32 0  /* float                                                  */
@@ -215,6 +216,55 @@ int amax_scale_channel_f32(const float* x, int64_t rows, int64_t cols, int axis,
  */
 int quantize_fp8_channel(const float* x, int64_t rows, int64_t cols, int axis,
                          const float* scale, uint8_t* q, int fmt, hipStream_t stream);
+
+/* ------------------------------------------------------------ split-K */
+/* Decode and mid-M shapes (e.g. M <= 256 with N = K = 4096) have too few
+ * output tiles to occupy 256 compute units while B streams from HBM. The
+ * workspace entry points then cut K into ranges summed by separate
+ * workgroups into FP32 slices of a caller-provided workspace, and a second
+ * launch adds the slices in a fixed order and applies the epilogue once to
+ * the full sum (P3 §6 names splitting K as the way to spread one GEMM over
+ * more compute; P2 §3.2: scale, then convert, at write-back). */
+
+/*
+ * gemm_splitk_plan — host-only query: the configuration, the number of K
+ * ranges (*splits; 1 = no split) and the workspace size in bytes
+ * (*workspace_bytes = splits * M * N * 4, or 0) that gemm_fp8_splitk (kind 1)
+ * or gemm_f16_splitk (kind 0) would use for this request. buf receives the
+ * configuration name (NUL-terminated, truncated to buflen); buf, splits and
+ * workspace_bytes may each be NULL. Returns GEMM_OK or a negative status for
+ * invalid arguments; makes no HIP call. The plan depends only on the shape,
+ * the kinds, formats and output type (and the LIBGEMM_CONFIG / LIBGEMM_SPLITS
+ * overrides).
+ */
+int gemm_splitk_plan(int kind, int out_dtype, int64_t M, int64_t N, int64_t K,
+                     int fmt_a, int fmt_b, char* buf, int buflen, int* splits,
+                     int64_t* workspace_bytes);
+
+/*
+ * gemm_fp8_splitk — gemm_fp8_fmt (per-tensor scales) that may split K.
+ *   workspace        device memory of workspace_bytes bytes, 16-byte aligned,
+ *                    used as FP32 scratch; or NULL: no split (the plain call)
+ *   workspace_bytes  at least what gemm_splitk_plan reports for the request
+ * When the plan splits, the workspace must be large enough and 16-byte
+ * aligned (else GEMM_ERR_WORKSPACE) and must not overlap A, B, C or the
+ * scales (GEMM_ERR_ALIAS); its contents on entry do not matter and on return
+ * are unspecified. Two launches on `stream`; calls that share a workspace
+ * must not run concurrently. Element values, outputs and other errors as
+ * gemm_fp8_fmt; the FP32 sum is formed in another order (per K range, then
+ * across ranges in range order), so results are deterministic and within the
+ * same bounds.
+ */
+int gemm_fp8_splitk(const uint8_t* A, int fmt_a, const uint8_t* B, int fmt_b,
+                    const float* sA, const float* sB, const float* sOut, void* C, int out_dtype,
+                    int64_t M, int64_t N, int64_t K, void* workspace, int64_t workspace_bytes,
+                    hipStream_t stream);
+
+/* gemm_f16_splitk — gemm_f16 that may split K, with the workspace rules of
+ * gemm_fp8_splitk (the M = 1 decode of P1 §4.1 is such a shape). */
+int gemm_f16_splitk(const void* A, const void* B, void* C, int out_dtype,
+                    int64_t M, int64_t N, int64_t K, void* workspace, int64_t workspace_bytes,
+                    hipStream_t stream);
 
 /* Human-readable name of a status code (a static string). */
 const char* gemm_status_str(int status);

@@ -16,6 +16,9 @@ Functions keep the C names:
     gemm_fp8_channel(A, fmt_a, B, fmt_b, sA, sB, C, sOut=None, stream=None, out_fmt=None)
     quantize_fp8_channel(x, scale, axis, fmt, q=None, stream=None) -> q
     amax_scale_channel_f32(x, axis, fmt, pow2, amax=None, scale=None, stream=None) -> (amax, scale)
+    gemm_fp8_splitk(A, fmt_a, B, fmt_b, sA, sB, C, sOut=None, workspace=None, stream=None, out_fmt=None)
+    gemm_f16_splitk(A, B, C, workspace=None, stream=None)
+    splitk_plan(kind, out_dtype, M, N, K, fmt_a=0, fmt_b=0) -> (config, splits, workspace_bytes)
     select_config(kind, out_dtype, M, N, K) -> str   (host-only query)
     select_config_fmt(kind, out_dtype, M, N, K, fmt_a, fmt_b) -> str
 The output dtype of a GEMM is taken from C: float32, float16, or 8-bit codes
@@ -43,7 +46,7 @@ GEMM_OK = 0
 STATUS_NAMES = {
     0: "GEMM_OK", -1: "GEMM_ERR_NULL", -2: "GEMM_ERR_DIM", -3: "GEMM_ERR_DTYPE",
     -4: "GEMM_ERR_SCALE", -5: "GEMM_ERR_LAUNCH", -6: "GEMM_ERR_UNSUPPORTED",
-    -7: "GEMM_ERR_DEVICE", -8: "GEMM_ERR_ALIAS",
+    -7: "GEMM_ERR_DEVICE", -8: "GEMM_ERR_ALIAS", -9: "GEMM_ERR_WORKSPACE",
 }
 
 _lib = None
@@ -89,6 +92,13 @@ def lib() -> ctypes.CDLL:
     L.amax_scale_channel_f32.argtypes = [vp, i64, i64, i32, vp, vp, i32, i32, vp]
     L.quantize_fp8_channel.restype = i32
     L.quantize_fp8_channel.argtypes = [vp, i64, i64, i32, vp, vp, i32, vp]
+    L.gemm_fp8_splitk.restype = i32
+    L.gemm_fp8_splitk.argtypes = [vp, i32, vp, i32, vp, vp, vp, vp, i32, i64, i64, i64, vp, i64, vp]
+    L.gemm_f16_splitk.restype = i32
+    L.gemm_f16_splitk.argtypes = [vp, vp, vp, i32, i64, i64, i64, vp, i64, vp]
+    L.gemm_splitk_plan.restype = i32
+    L.gemm_splitk_plan.argtypes = [i32, i32, i64, i64, i64, i32, i32, ctypes.c_char_p, i32,
+                                   ctypes.POINTER(i32), ctypes.POINTER(i64)]
     L.gemm_select_config_fmt.restype = i32
     L.gemm_select_config_fmt.argtypes = [i32, i32, i64, i64, i64, i32, i32, ctypes.c_char_p, i32]
     _lib = L
@@ -248,6 +258,58 @@ def amax_scale_channel_f32(x, axis, fmt, pow2, amax=None, scale=None, stream=Non
     _check(lib().amax_scale_channel_f32(_ptr(x), rows, cols, int(axis), _ptr(amax), _ptr(scale), int(fmt),
                                         1 if pow2 else 0, _stream_handle(stream)), "amax_scale_channel_f32")
     return amax, scale
+
+
+def splitk_plan(kind: int, out_dtype: int, M: int, N: int, K: int, fmt_a: int = 0, fmt_b: int = 0):
+    """(configuration name, number of K ranges, workspace bytes) of the
+    split-K entry points for this request (host-only query)."""
+    buf = ctypes.create_string_buffer(64)
+    sp = ctypes.c_int(0)
+    wb = ctypes.c_int64(0)
+    _check(lib().gemm_splitk_plan(kind, out_dtype, M, N, K, fmt_a, fmt_b, buf, 64, ctypes.byref(sp),
+                                  ctypes.byref(wb)), "gemm_splitk_plan")
+    return buf.value.decode(), sp.value, wb.value
+
+
+def _workspace(kind, out, M, N, K, fa, fb, workspace, device):
+    if workspace is not None:
+        return workspace
+    _, _, nbytes = splitk_plan(kind, out, M, N, K, fa, fb)
+    if nbytes == 0:
+        return None
+    return _torch().empty(nbytes, dtype=_torch().uint8, device=device)
+
+
+def _ws_args(workspace):
+    if workspace is None:
+        return None, 0
+    return _ptr(workspace), workspace.numel() * workspace.element_size()
+
+
+def gemm_fp8_splitk(A, fmt_a, B, fmt_b, sA, sB, C, sOut=None, workspace=None, stream=None, out_fmt=None):
+    """gemm_fp8_fmt that splits K over a workspace when the shape has too few
+    output tiles; workspace=None allocates one of the planned size."""
+    A, B = _u8(A), _u8(B)
+    out = _out_dtype(C, out_fmt)
+    Cv = _u8(C) if out in (OUT_E4M3, OUT_E5M2) else C
+    M, N, K = _dims(A, B, Cv)
+    ws, nbytes = _ws_args(_workspace(KIND_FP8, out, M, N, K, int(fmt_a), int(fmt_b), workspace, C.device))
+    _check(lib().gemm_fp8_splitk(_ptr(A), int(fmt_a), _ptr(B), int(fmt_b), _ptr(sA), _ptr(sB), _ptr(sOut), _ptr(Cv),
+                                 out, M, N, K, ws, nbytes, _stream_handle(stream)), "gemm_fp8_splitk")
+    return C
+
+
+def gemm_f16_splitk(A, B, C, workspace=None, stream=None):
+    """gemm_f16 that splits K over a workspace when the shape has too few
+    output tiles; workspace=None allocates one of the planned size."""
+    out = _out_dtype(C)
+    if out not in (OUT_F32, OUT_F16):
+        raise ValueError("gemm_f16 writes float32 or float16")
+    M, N, K = _dims(A, B, C)
+    ws, nbytes = _ws_args(_workspace(KIND_F16, out, M, N, K, 0, 0, workspace, C.device))
+    _check(lib().gemm_f16_splitk(_ptr(A), _ptr(B), _ptr(C), out, M, N, K, ws, nbytes, _stream_handle(stream)),
+           "gemm_f16_splitk")
+    return C
 
 
 def quantize_fp8(x, scale, q=None, stream=None):

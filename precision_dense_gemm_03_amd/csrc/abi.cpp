@@ -71,6 +71,33 @@ int run_gemm(int kind, const GemmArgs& a) {
     return status_of(cfg->launch(a));
 }
 
+int64_t splitk_bytes(const SplitPlan& p, int64_t M, int64_t N) { return p.splits > 1 ? p.splits * M * N * 4 : 0; }
+
+// Workspace entry points: after the caller's arguments were validated, the
+// workspace is checked (host only), then the split launch and the reduce run,
+// or the plain launch when the plan does not split or no workspace was given.
+// `inputs` lists the byte ranges the workspace must not overlap.
+int run_gemm_splitk(int kind, GemmArgs a, void* ws, int64_t ws_bytes, const void* const* in_ptr,
+                    const int64_t* in_bytes, int n_in) {
+    if (a.M == 0 || a.N == 0 || a.K == 0 || !ws) return run_gemm(kind, a);
+    if (ws_bytes < 0) return GEMM_ERR_WORKSPACE;
+    const SplitPlan p = plan_splitk(kind, a.out_dtype, a.M, a.N, a.K, a.fmt_a, a.fmt_b);
+    if (!p.cfg) return GEMM_ERR_UNSUPPORTED;
+    const int64_t need = splitk_bytes(p, a.M, a.N);
+    if (need == 0) return run_gemm(kind, a);
+    if (ws_bytes < need || ((uintptr_t)ws & 15u) != 0) return GEMM_ERR_WORKSPACE;
+    for (int i = 0; i < n_in; ++i)
+        if (overlaps(ws, need, in_ptr[i], in_bytes[i])) return GEMM_ERR_ALIAS;
+    const int st = check_device();
+    if (st != GEMM_OK) return st;
+    a.ws = reinterpret_cast<float*>(ws);
+    a.splits = p.splits;
+    a.k_chunk = p.k_chunk;
+    const int s1 = status_of(p.cfg->launch(a));
+    if (s1 != GEMM_OK) return s1;
+    return status_of(launch_splitk_reduce(a));
+}
+
 }  // namespace
 
 extern "C" {
@@ -89,11 +116,13 @@ int gemm_f16(const void* A, const void* B, void* C, int out_dtype, int64_t M, in
     return run_gemm(KIND_F16, a);
 }
 
-// Shared by gemm_fp8_scaled, gemm_fp8_fmt and gemm_fp8_channel: validation,
-// then the launch. channel: sA holds M floats and sB N floats.
+// Shared by gemm_fp8_scaled, gemm_fp8_fmt, gemm_fp8_channel and
+// gemm_fp8_splitk: validation, then the launch. channel: sA holds M floats and
+// sB N floats. ws: the split-K workspace (NULL: none).
 static int gemm_fp8_common(const uint8_t* A, int fmt_a, const uint8_t* B, int fmt_b, const float* sA,
                            const float* sB, const float* sOut, void* C, int out_dtype, int64_t M, int64_t N,
-                           int64_t K, hipStream_t stream, int channel = 0) {
+                           int64_t K, hipStream_t stream, int channel = 0, void* ws = nullptr,
+                           int64_t ws_bytes = 0) {
     if (out_dtype < GEMM_OUT_F32 || out_dtype > GEMM_OUT_E5M2) return GEMM_ERR_DTYPE;
     if ((fmt_a != GEMM_FMT_E4M3 && fmt_a != GEMM_FMT_E5M2) || (fmt_b != GEMM_FMT_E4M3 && fmt_b != GEMM_FMT_E5M2))
         return GEMM_ERR_DTYPE;
@@ -111,7 +140,11 @@ static int gemm_fp8_common(const uint8_t* A, int fmt_a, const uint8_t* B, int fm
     }
     GemmArgs a{A, B, C, sA, sB, fp8_out(out_dtype) ? sOut : nullptr, out_dtype, M, N, K, stream, fmt_a, fmt_b,
                channel};
-    return run_gemm(KIND_FP8, a);
+    if (!ws) return run_gemm(KIND_FP8, a);
+    const void* in_ptr[6] = {A, B, C, sA, sB, fp8_out(out_dtype) ? sOut : nullptr};
+    const int64_t in_bytes[6] = {M * K, K * N, M * N * out_size(out_dtype), channel ? 4 * M : 4, channel ? 4 * N : 4,
+                                 4};
+    return run_gemm_splitk(KIND_FP8, a, ws, ws_bytes, in_ptr, in_bytes, 6);
 }
 
 int gemm_fp8_scaled(const uint8_t* A, const uint8_t* B, const float* sA, const float* sB, const float* sOut,
@@ -122,6 +155,48 @@ int gemm_fp8_scaled(const uint8_t* A, const uint8_t* B, const float* sA, const f
 int gemm_fp8_fmt(const uint8_t* A, int fmt_a, const uint8_t* B, int fmt_b, const float* sA, const float* sB,
                  const float* sOut, void* C, int out_dtype, int64_t M, int64_t N, int64_t K, hipStream_t stream) {
     return gemm_fp8_common(A, fmt_a, B, fmt_b, sA, sB, sOut, C, out_dtype, M, N, K, stream);
+}
+
+int gemm_fp8_splitk(const uint8_t* A, int fmt_a, const uint8_t* B, int fmt_b, const float* sA, const float* sB,
+                    const float* sOut, void* C, int out_dtype, int64_t M, int64_t N, int64_t K, void* workspace,
+                    int64_t workspace_bytes, hipStream_t stream) {
+    return gemm_fp8_common(A, fmt_a, B, fmt_b, sA, sB, sOut, C, out_dtype, M, N, K, stream, 0, workspace,
+                           workspace_bytes);
+}
+
+int gemm_f16_splitk(const void* A, const void* B, void* C, int out_dtype, int64_t M, int64_t N, int64_t K,
+                    void* workspace, int64_t workspace_bytes, hipStream_t stream) {
+    if (out_dtype != GEMM_OUT_F32 && out_dtype != GEMM_OUT_F16) return GEMM_ERR_DTYPE;
+    if (!dim_ok(M) || !dim_ok(N) || !dim_ok(K)) return GEMM_ERR_DIM;
+    if (M > 0 && N > 0) {
+        if (!C) return GEMM_ERR_NULL;
+        if (K > 0 && (!A || !B)) return GEMM_ERR_NULL;
+        const int64_t cbytes = M * N * out_size(out_dtype);
+        if (K > 0 && (overlaps(C, cbytes, A, M * K * 2) || overlaps(C, cbytes, B, K * N * 2))) return GEMM_ERR_ALIAS;
+    }
+    GemmArgs a{A, B, C, nullptr, nullptr, nullptr, out_dtype, M, N, K, stream};
+    const void* in_ptr[3] = {A, B, C};
+    const int64_t in_bytes[3] = {M * K * 2, K * N * 2, M * N * out_size(out_dtype)};
+    return run_gemm_splitk(KIND_F16, a, workspace, workspace_bytes, in_ptr, in_bytes, 3);
+}
+
+int gemm_splitk_plan(int kind, int out_dtype, int64_t M, int64_t N, int64_t K, int fmt_a, int fmt_b, char* buf,
+                     int buflen, int* splits, int64_t* workspace_bytes) {
+    if (kind != KIND_F16 && kind != KIND_FP8) return GEMM_ERR_DTYPE;
+    if (out_dtype < GEMM_OUT_F32 || out_dtype > GEMM_OUT_E5M2 || (kind == KIND_F16 && fp8_out(out_dtype)))
+        return GEMM_ERR_DTYPE;
+    if ((fmt_a != GEMM_FMT_E4M3 && fmt_a != GEMM_FMT_E5M2) || (fmt_b != GEMM_FMT_E4M3 && fmt_b != GEMM_FMT_E5M2))
+        return GEMM_ERR_DTYPE;
+    if (!dim_ok(M) || !dim_ok(N) || !dim_ok(K)) return GEMM_ERR_DIM;
+    const SplitPlan p = plan_splitk(kind, out_dtype, M, N, K, fmt_a, fmt_b);
+    if (!p.cfg) return GEMM_ERR_UNSUPPORTED;
+    if (buf && buflen > 0) {
+        std::strncpy(buf, p.cfg->name, (size_t)buflen - 1);
+        buf[buflen - 1] = '\0';
+    }
+    if (splits) *splits = p.splits;
+    if (workspace_bytes) *workspace_bytes = splitk_bytes(p, M, N);
+    return GEMM_OK;
 }
 
 int gemm_fp8_channel(const uint8_t* A, int fmt_a, const uint8_t* B, int fmt_b, const float* sA, const float* sB,
@@ -204,6 +279,7 @@ const char* gemm_status_str(int status) {
         case GEMM_ERR_UNSUPPORTED: return "no kernel for this request";
         case GEMM_ERR_DEVICE: return "no current HIP device, or it is not gfx950";
         case GEMM_ERR_ALIAS: return "output overlaps an input";
+        case GEMM_ERR_WORKSPACE: return "workspace too small or not 16-byte aligned";
         default: return "unknown status";
     }
 }

@@ -118,8 +118,11 @@ __device__ __forceinline__ float epilogue_multiplier(const float* sA, const floa
     return fp8_out ? s / *sOut : s;
 }
 
-// Epilogue options passed to the tile kernels as one uniform integer.
-enum EpilogueFlags { EPI_E5M2 = 1, EPI_CHANNEL = 2 };
+// Epilogue options passed to the kernels as one uniform integer. EPI_PARTIAL:
+// the workgroup stores the raw FP32 sum over its K range (no scale, no
+// conversion) into its split's [M, N] slice of the workspace; a reduce kernel
+// then applies the epilogue to the sum of the slices.
+enum EpilogueFlags { EPI_E5M2 = 1, EPI_CHANNEL = 2, EPI_PARTIAL = 4 };
 
 // Per-tensor multiplier, or with per-channel scales (sA[M], sB[N]) the part
 // common to every element: 1 / sOut for an FP8 output, else 1; the element

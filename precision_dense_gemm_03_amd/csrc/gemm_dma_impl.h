@@ -423,6 +423,7 @@ inline hipError_t fallback(int kind, const GemmArgs& a) {
 template <int ES, int STAGES, int FA, int FB>
 hipError_t launch_dma(const GemmArgs& a) {
     using T = Dma<ES, STAGES>;
+    if (a.splits > 1) return hipErrorInvalidValue;   // no split-K here (kgran 0 in the table)
     const int64_t tiles_m = (a.M + T::BM - 1) / T::BM;
     const int64_t tiles_n = (a.N + T::BN - 1) / T::BN;
     const int64_t blocks = tiles_m * tiles_n;

@@ -68,7 +68,7 @@ __global__ __launch_bounds__(NT) void gemm_stream_kernel(const uint8_t* __restri
                                                          int64_t M, int64_t N, int64_t K,
                                                          const float* __restrict__ sA, const float* __restrict__ sB,
                                                          const float* __restrict__ sOut, int out_dtype, int a_vec,
-                                                         int b_vec, int channel) {
+                                                         int b_vec, int eflags, int64_t kchunk) {
     constexpr int VE = 16 / ES;
     constexpr int CX = COLS / VE;
     constexpr int KY = NT / CX;
@@ -81,6 +81,10 @@ __global__ __launch_bounds__(NT) void gemm_stream_kernel(const uint8_t* __restri
     const int ky = tid / CX;
     const int64_t n0 = (int64_t)blockIdx.x * COLS;
     const int64_t ncol = n0 + (int64_t)cx * VE;  // first column of this lane's chunk
+    // Split-K: workgroup row blockIdx.y sums K range [kbeg, kend) (all of K
+    // when the launch is not split); kbeg is a multiple of KY * U.
+    const int64_t kbeg = (int64_t)blockIdx.y * kchunk;
+    const int64_t kend = min(K, kbeg + kchunk);
 
     float acc[MMAX][VE];
 #pragma unroll
@@ -89,13 +93,13 @@ __global__ __launch_bounds__(NT) void gemm_stream_kernel(const uint8_t* __restri
         for (int e = 0; e < VE; ++e) acc[m][e] = 0.0f;
 
     const bool chunk_full = b_vec && (ncol + VE <= N);
-    for (int64_t kb = (int64_t)ky * U; kb < K; kb += (int64_t)KY * U) {
+    for (int64_t kb = kbeg + (int64_t)ky * U; kb < kend; kb += (int64_t)KY * U) {
         // B rows kb .. kb+U-1 of this lane's chunk (zero beyond K / N).
         v4u braw[U];
 #pragma unroll
         for (int u = 0; u < U; ++u) {
             const int64_t k = kb + u;
-            if (chunk_full && k < K) {
+            if (chunk_full && k < kend) {
                 braw[u] = __builtin_nontemporal_load(reinterpret_cast<const v4u*>(B + (k * N + ncol) * ES));
             } else {
                 union {
@@ -104,7 +108,7 @@ __global__ __launch_bounds__(NT) void gemm_stream_kernel(const uint8_t* __restri
                     uint16_t h[8];
                 } t;
                 t.v = v4u{0u, 0u, 0u, 0u};
-                if (k < K) {
+                if (k < kend) {
 #pragma unroll
                     for (int e = 0; e < VE; ++e) {
                         if (ncol + e < N) {
@@ -121,7 +125,7 @@ __global__ __launch_bounds__(NT) void gemm_stream_kernel(const uint8_t* __restri
 #pragma unroll
         for (int m = 0; m < MMAX; ++m) {
             if (m < M) {
-                if (a_vec && kb + U <= K) {
+                if (a_vec && kb + U <= kend) {
                     static_assert(U % 8 == 0, "A vector loads cover 8 elements");
 #pragma unroll
                     for (int g8 = 0; g8 < U / 8; ++g8) {
@@ -146,7 +150,7 @@ __global__ __launch_bounds__(NT) void gemm_stream_kernel(const uint8_t* __restri
                     }
                 } else {
 #pragma unroll
-                    for (int u = 0; u < U; ++u) a[m][u] = (kb + u < K) ? decode1<ES, FA>(A, m * K + kb + u) : 0.0f;
+                    for (int u = 0; u < U; ++u) a[m][u] = (kb + u < kend) ? decode1<ES, FA>(A, m * K + kb + u) : 0.0f;
                 }
             } else {
 #pragma unroll
@@ -182,8 +186,17 @@ __global__ __launch_bounds__(NT) void gemm_stream_kernel(const uint8_t* __restri
             for (int e = 0; e < VE; ++e) red[wave][m][lane * VE + e] = acc[m][e];
     }
     __syncthreads();
-    // per-channel scales (sA[M], sB[N]) are applied per stored element
-    const float scale = epilogue_base(sA, sB, sOut, out_dtype == OUT_E4M3 || out_dtype == OUT_E5M2, channel != 0);
+    // per-channel scales (sA[M], sB[N]) are applied per stored element; a
+    // split-K partial (EPI_PARTIAL) stores the raw FP32 sum into its split's
+    // [M, N] slice of the workspace C
+    const bool partial = (eflags & EPI_PARTIAL) != 0;
+    if (partial) {
+        C = reinterpret_cast<float*>(C) + (int64_t)blockIdx.y * M * N;
+        out_dtype = OUT_F32;
+    }
+    const bool channel = !partial && (eflags & EPI_CHANNEL) != 0;
+    const float scale = partial ? 1.0f
+                                : epilogue_base(sA, sB, sOut, out_dtype == OUT_E4M3 || out_dtype == OUT_E5M2, channel);
 
     for (int o = tid; o < MMAX * COLS; o += NT) {
         const int m = o / COLS, c = o % COLS;
@@ -202,16 +215,29 @@ __global__ __launch_bounds__(NT) void gemm_stream_kernel(const uint8_t* __restri
 
 bool aligned16(const void* p) { return ((uintptr_t)p & 15u) == 0; }
 
+// K rows one pass of a workgroup covers: the split-K granularity.
+template <int ES, int COLS, int NT, int U>
+constexpr int stream_kgran() {
+    return NT / (COLS / (16 / ES)) * U;
+}
+
 template <int ES, int MMAX, int COLS, int NT, int U, int FA = 0, int FB = 0>
 hipError_t launch_stream(const GemmArgs& a) {
     const int64_t blocks = (a.N + COLS - 1) / COLS;
     if (blocks <= 0 || a.M <= 0) return hipSuccess;
     if (blocks > 0x7FFFFFFF || a.M > MMAX) return hipErrorInvalidValue;
+    const int splits = a.splits > 1 ? a.splits : 1;
+    constexpr int kgran = stream_kgran<ES, COLS, NT, U>();
+    if (splits > 1 && (a.k_chunk % kgran != 0 || a.k_chunk <= 0 || (int64_t)(splits - 1) * a.k_chunk >= a.K ||
+                       splits > 65535 || !a.ws))
+        return hipErrorInvalidValue;
     const int a_vec = aligned16(a.A) && ((a.K * ES) % 16 == 0);
     const int b_vec = aligned16(a.B) && ((a.N * ES) % 16 == 0);
-    gemm_stream_kernel<ES, MMAX, COLS, NT, U, FA, FB><<<(unsigned)blocks, NT, 0, a.stream>>>(
-        reinterpret_cast<const uint8_t*>(a.A), reinterpret_cast<const uint8_t*>(a.B), a.C, a.M, a.N, a.K, a.sA,
-        a.sB, a.sOut, a.out_dtype, a_vec, b_vec, a.channel ? 1 : 0);
+    const int eflags = splits > 1 ? EPI_PARTIAL : (a.channel ? EPI_CHANNEL : 0);
+    const dim3 grid((unsigned)blocks, (unsigned)splits);
+    gemm_stream_kernel<ES, MMAX, COLS, NT, U, FA, FB><<<grid, NT, 0, a.stream>>>(
+        reinterpret_cast<const uint8_t*>(a.A), reinterpret_cast<const uint8_t*>(a.B), splits > 1 ? a.ws : a.C, a.M,
+        a.N, a.K, a.sA, a.sB, a.sOut, a.out_dtype, a_vec, b_vec, eflags, splits > 1 ? a.k_chunk : a.K);
     return hipGetLastError();
 }
 
@@ -232,13 +258,29 @@ hipError_t launch_stream_fp8_any(const GemmArgs& a) {
 // The table lives in a host function so that the kernels it names are
 // instantiated for the device while the table itself stays host data.
 const GemmConfig* stream_configs(int* count) {
+    // The last field is the split-K granularity (K rows per workgroup pass).
+    // For one bound M the first entry is the plain choice; the split-K plan
+    // takes the one with the smallest granularity (fewer threads, so a K
+    // range of a few hundred rows still keeps every lane busy).
     static const GemmConfig table[] = {
-    {"stream_f16_m1_c64_t1024", KIND_F16, 1, 1, 64, 1024, launch_stream<2, 1, 64, 1024, 8>},
-    {"stream_f16_m4_c64_t512", KIND_F16, 1, 4, 64, 512, launch_stream<2, 4, 64, 512, 8>},
-    {"stream_f16_m8_c64_t256", KIND_F16, 1, 8, 64, 256, launch_stream<2, 8, 64, 256, 8>},
-    {"stream_f16_m16_c64_t256", KIND_F16, 1, 16, 64, 256, launch_stream<2, 16, 64, 256, 8>},
-    {"stream_fp8_m1_c64_t1024", KIND_FP8, 1, 1, 64, 1024, launch_stream_fp8_any<1, 64, 1024, 8>, kAllFp8Pairs},
-    {"stream_fp8_m4_c64_t512", KIND_FP8, 1, 4, 64, 512, launch_stream_fp8_any<4, 64, 512, 8>, kAllFp8Pairs},
+    {"stream_f16_m1_c64_t1024", KIND_F16, 1, 1, 64, 1024, launch_stream<2, 1, 64, 1024, 8>, 0,
+     stream_kgran<2, 64, 1024, 8>()},
+    {"stream_f16_m4_c64_t512", KIND_F16, 1, 4, 64, 512, launch_stream<2, 4, 64, 512, 8>, 0,
+     stream_kgran<2, 64, 512, 8>()},
+    {"stream_f16_m8_c64_t256", KIND_F16, 1, 8, 64, 256, launch_stream<2, 8, 64, 256, 8>, 0,
+     stream_kgran<2, 64, 256, 8>()},
+    {"stream_f16_m16_c64_t256", KIND_F16, 1, 16, 64, 256, launch_stream<2, 16, 64, 256, 8>, 0,
+     stream_kgran<2, 64, 256, 8>()},
+    {"stream_fp8_m1_c64_t1024", KIND_FP8, 1, 1, 64, 1024, launch_stream_fp8_any<1, 64, 1024, 8>, kAllFp8Pairs,
+     stream_kgran<1, 64, 1024, 8>()},
+    {"stream_fp8_m4_c64_t512", KIND_FP8, 1, 4, 64, 512, launch_stream_fp8_any<4, 64, 512, 8>, kAllFp8Pairs,
+     stream_kgran<1, 64, 512, 8>()},
+    {"stream_f16_m1_c64_t256", KIND_F16, 1, 1, 64, 256, launch_stream<2, 1, 64, 256, 8>, 0,
+     stream_kgran<2, 64, 256, 8>()},
+    {"stream_fp8_m1_c128_t256", KIND_FP8, 1, 1, 128, 256, launch_stream_fp8_any<1, 128, 256, 8>, kAllFp8Pairs,
+     stream_kgran<1, 128, 256, 8>()},
+    {"stream_fp8_m4_c128_t256", KIND_FP8, 1, 4, 128, 256, launch_stream_fp8_any<4, 128, 256, 8>, kAllFp8Pairs,
+     stream_kgran<1, 128, 256, 8>()},
     };
     *count = (int)(sizeof(table) / sizeof(table[0]));
     return table;

@@ -18,12 +18,12 @@ LIBGEMM_TILE_MIXED_CONFIGS(LIBGEMM_TILE_EXTERN)
 // instantiated for the device while the table itself stays host data.
 const GemmConfig* tile_configs(int* count) {
     static const GemmConfig table[] = {
-        {"tile_f16_64x64x64_w2x2", KIND_F16, 0, 64, 64, 64, tile::launch_tile<2, 64, 64, 64, 2, 2, 0, 0>},
-        {"tile_f16_128x128x64_w2x2", KIND_F16, 0, 128, 128, 64, tile::launch_tile<2, 128, 128, 64, 2, 2, 0, 0>},
-        {"tile_fp8_64x64x128_w2x2", KIND_FP8, 0, 64, 64, 128, tile::launch_tile_fp8_any<64, 64, 128, 2, 2>, kAllFp8Pairs},
-        {"tile_fp8_128x128x128_w2x2", KIND_FP8, 0, 128, 128, 128, tile::launch_tile_fp8_any<128, 128, 128, 2, 2>, kAllFp8Pairs},
-        {"tile_fp8_256x256x128_w2x4", KIND_FP8, 0, 256, 256, 128, tile::launch_tile_fp8_any<256, 256, 128, 2, 4>, kAllFp8Pairs},
-        {"tile_f16_256x256x64_w2x4", KIND_F16, 0, 256, 256, 64, tile::launch_tile<2, 256, 256, 64, 2, 4, 0, 0>},
+        {"tile_f16_64x64x64_w2x2", KIND_F16, 0, 64, 64, 64, tile::launch_tile<2, 64, 64, 64, 2, 2, 0, 0>, 0, 64},
+        {"tile_f16_128x128x64_w2x2", KIND_F16, 0, 128, 128, 64, tile::launch_tile<2, 128, 128, 64, 2, 2, 0, 0>, 0, 64},
+        {"tile_fp8_64x64x128_w2x2", KIND_FP8, 0, 64, 64, 128, tile::launch_tile_fp8_any<64, 64, 128, 2, 2>, kAllFp8Pairs, 128},
+        {"tile_fp8_128x128x128_w2x2", KIND_FP8, 0, 128, 128, 128, tile::launch_tile_fp8_any<128, 128, 128, 2, 2>, kAllFp8Pairs, 128},
+        {"tile_fp8_256x256x128_w2x4", KIND_FP8, 0, 256, 256, 128, tile::launch_tile_fp8_any<256, 256, 128, 2, 4>, kAllFp8Pairs, 128},
+        {"tile_f16_256x256x64_w2x4", KIND_F16, 0, 256, 256, 64, tile::launch_tile<2, 256, 256, 64, 2, 4, 0, 0>, 0, 64},
     };
     *count = (int)(sizeof(table) / sizeof(table[0]));
     return table;

@@ -163,7 +163,7 @@ template <int ES, int OUT, int BM, int BN, int BK, int WM, int WN, int FA, int F
 __global__ __launch_bounds__(64 * WM * WN) void gemm_tile_kernel(
     const uint8_t* __restrict__ A, const uint8_t* __restrict__ B, void* __restrict__ C, int M, int N, int K,
     const float* __restrict__ sA, const float* __restrict__ sB, const float* __restrict__ sOut, int tiles_m,
-    int tiles_n, int aligned, int eflags) {
+    int tiles_n, int aligned, int eflags, int kchunk) {
     using T = Tile<ES, BM, BN, BK, WM, WN>;
     __shared__ __attribute__((aligned(16))) uint8_t smem_raw[2 * T::STAGE];
     LDS_AS uint8_t* smem = (LDS_AS uint8_t*)smem_raw;
@@ -178,6 +178,12 @@ __global__ __launch_bounds__(64 * WM * WN) void gemm_tile_kernel(
     const int m0 = tile_m * BM;
     const int n0 = tile_n * BN;
     const bool interior_mn = aligned && (m0 + BM <= M) && (n0 + BN <= N);
+    // Split-K: workgroup row blockIdx.y sums K range [kbeg, kend) (the whole
+    // of K when the launch is not split). kbeg is a multiple of BK.
+    const int split = blockIdx.y;
+    const int kbeg = split * kchunk;
+    const int klen = min(K - kbeg, kchunk);
+    const int kend = kbeg + klen;
 
     // This thread's chunk coordinates inside a staged tile.
     const int a_row = tid / T::A_CPR, a_col = tid % T::A_CPR;  // + i * A_RPP rows
@@ -203,15 +209,15 @@ __global__ __launch_bounds__(64 * WM * WN) void gemm_tile_kernel(
     const int b_lds = (8 * (ES == 2 ? 1 : 4) * g + b_row_in) * T::SB     // + stage + ks*KPI*SB + tn*16*ES
                       + (wn * T::WTN + b_col_in) * ES;
 
-    const int nk = (K + BK - 1) / BK;
+    const int nk = (klen + BK - 1) / BK;
     typedef typename Operand<ES>::type Op;
 
     // ---- global <-> registers <-> LDS (A and B have separate stages) ----
     // Fast-path loads: a wave-uniform base (kept in SGPRs) plus a 32-bit
     // per-lane offset, so the 16 loads of a tile need no 64-bit VGPR addresses.
     // Valid while one tile row block spans less than 2^31 bytes (checked below).
-    const uint8_t* a_tile = A + (int64_t)m0 * K * ES;
-    const uint8_t* b_tile = B + (int64_t)n0 * ES;
+    const uint8_t* a_tile = A + ((int64_t)m0 * K + kbeg) * ES;
+    const uint8_t* b_tile = B + ((int64_t)kbeg * N + n0) * ES;
     // Edge tiles (aligned operands) use the same unguarded loads with the
     // addresses clamped into the matrix: A rows past M re-read row M-1 and B
     // column chunks past N re-read the last chunk. Those values only reach
@@ -253,7 +259,7 @@ __global__ __launch_bounds__(64 * WM * WN) void gemm_tile_kernel(
     // loaded with per-element guards and written straight to LDS (no register
     // staging, and a rolled loop, so this path costs almost no registers).
     auto guarded_to_lds = [&](int kt, int stage) __attribute__((always_inline)) {
-        const int k0 = kt * BK;
+        const int k0 = kbeg + kt * BK;
         LDS_AS uint8_t* As = smem + T::a_stage(stage);
         LDS_AS uint8_t* Bs = smem + T::b_stage(stage);
 #pragma unroll 1
@@ -262,10 +268,10 @@ __global__ __launch_bounds__(64 * WM * WN) void gemm_tile_kernel(
             const int64_t gk = (int64_t)k0 + a_col * T::VE;
             const uint8_t* rp = A + (int64_t)gm * K * ES;
             v4u v;
-            if (aligned && gm < M && gk + T::VE <= K)
+            if (aligned && gm < M && gk + T::VE <= kend)
                 v = *reinterpret_cast<const v4u*>(rp + gk * ES);
             else
-                v = load_chunk_guarded<ES>(rp, gm < M, gk, K);
+                v = load_chunk_guarded<ES>(rp, gm < M, gk, kend);
             *(LDS_AS v4u*)(As + (a_row + i * T::A_RPP) * T::SA + a_col * 16) = v;
         }
 #pragma unroll 1
@@ -274,10 +280,10 @@ __global__ __launch_bounds__(64 * WM * WN) void gemm_tile_kernel(
             const int64_t gn = (int64_t)n0 + b_col * T::VE;
             const uint8_t* rp = B + (int64_t)gk * N * ES;
             v4u v;
-            if (aligned && gk < K && gn + T::VE <= N)
+            if (aligned && gk < kend && gn + T::VE <= N)
                 v = *reinterpret_cast<const v4u*>(rp + gn * ES);
             else
-                v = load_chunk_guarded<ES>(rp, gk < K, gn, N);
+                v = load_chunk_guarded<ES>(rp, gk < kend, gn, N);
             *(LDS_AS v4u*)(Bs + (b_row + i * T::B_RPP) * T::SB + b_col * 16) = v;
         }
     };
@@ -314,7 +320,7 @@ __global__ __launch_bounds__(64 * WM * WN) void gemm_tile_kernel(
     };
 
     const bool offsets_fit = (int64_t)BM * K * ES < (1ll << 31) && (int64_t)BK * N * ES < (1ll << 31);
-    if (kRegisterPipeline && interior_mn && K % BK == 0 && nk > 0 && offsets_fit) {
+    if (kRegisterPipeline && interior_mn && klen % BK == 0 && nk > 0 && offsets_fit) {
         // Software pipeline, one barrier per K tile. Entering iteration kt:
         // LDS holds A(kt) in A stage kt%2 and B(kt+1) in B stage (kt+1)%2,
         // registers hold the B operands of tile kt (bcur) and the global data
@@ -358,7 +364,7 @@ __global__ __launch_bounds__(64 * WM * WN) void gemm_tile_kernel(
         // the K tail and unaligned operands load each chunk with element
         // guards straight into LDS.
         auto fast = [&](int kt) __attribute__((always_inline)) {
-            return aligned && offsets_fit && (kt + 1) * BK <= K;
+            return aligned && offsets_fit && (kt + 1) * BK <= klen;
         };
         if (fast(0)) {
             load_a(0);
@@ -392,8 +398,12 @@ __global__ __launch_bounds__(64 * WM * WN) void gemm_tile_kernel(
     // Per-tensor: y = acc * sA*sB (/ sOut). Per-channel (EPI_CHANNEL, sA[M] and
     // sB[N]): y = acc * (1/sOut) * sA[row] * sB[col], loaded only for stored
     // elements.
-    const bool chan = (eflags & EPI_CHANNEL) != 0;
-    const float scale = epilogue_base(sA, sB, sOut, OUT == OUT_E4M3, chan);  // both FP8 outputs
+    // A split-K partial (EPI_PARTIAL, OUT_F32) stores the raw sum into the
+    // split's [M, N] slice of the workspace C.
+    const bool partial = (eflags & EPI_PARTIAL) != 0;
+    if (partial) C = reinterpret_cast<float*>(C) + (int64_t)split * M * N;
+    const bool chan = !partial && (eflags & EPI_CHANNEL) != 0;
+    const float scale = partial ? 1.0f : epilogue_base(sA, sB, sOut, OUT == OUT_E4M3, chan);  // both FP8 outputs
     const int row0 = m0 + wm * T::WTM + 4 * g;
     const int col0 = n0 + wn * T::WTN + j16;
     if (interior_mn) {
@@ -436,26 +446,36 @@ hipError_t launch_tile(const GemmArgs& a) {
     const int64_t blocks = tiles_m * tiles_n;
     if (blocks <= 0) return hipSuccess;
     if (blocks > 0x7FFFFFFF) return hipErrorInvalidValue;
+    const int splits = a.splits > 1 ? a.splits : 1;
+    if (splits > 1 && (a.k_chunk % BK != 0 || a.k_chunk <= 0 || (int64_t)(splits - 1) * a.k_chunk >= a.K ||
+                       splits > 65535 || !a.ws))
+        return hipErrorInvalidValue;
+    const int kchunk = splits > 1 ? (int)a.k_chunk : (int)a.K;
     const int aligned = aligned16(a.A) && aligned16(a.B) && ((a.K * ES) % 16 == 0) && ((a.N * ES) % 16 == 0);
     const uint8_t* A = reinterpret_cast<const uint8_t*>(a.A);
     const uint8_t* B = reinterpret_cast<const uint8_t*>(a.B);
     const int M = (int)a.M, N = (int)a.N, K = (int)a.K;
-    const dim3 grid((unsigned)blocks), block(64 * WM * WN);
+    const dim3 grid((unsigned)blocks, (unsigned)splits), block(64 * WM * WN);
+    if (splits > 1) {   // FP32 partial sums into the workspace
+        gemm_tile_kernel<ES, OUT_F32, BM, BN, BK, WM, WN, FA, FB><<<grid, block, 0, a.stream>>>(
+            A, B, a.ws, M, N, K, nullptr, nullptr, nullptr, (int)tiles_m, (int)tiles_n, aligned, EPI_PARTIAL, kchunk);
+        return hipGetLastError();
+    }
     const int eflags = (a.out_dtype == OUT_E5M2 ? EPI_E5M2 : 0) | (a.channel ? EPI_CHANNEL : 0);
     switch (a.out_dtype) {
         case OUT_F32:
             gemm_tile_kernel<ES, OUT_F32, BM, BN, BK, WM, WN, FA, FB><<<grid, block, 0, a.stream>>>(
-                A, B, a.C, M, N, K, a.sA, a.sB, a.sOut, (int)tiles_m, (int)tiles_n, aligned, eflags);
+                A, B, a.C, M, N, K, a.sA, a.sB, a.sOut, (int)tiles_m, (int)tiles_n, aligned, eflags, kchunk);
             break;
         case OUT_F16:
             gemm_tile_kernel<ES, OUT_F16, BM, BN, BK, WM, WN, FA, FB><<<grid, block, 0, a.stream>>>(
-                A, B, a.C, M, N, K, a.sA, a.sB, a.sOut, (int)tiles_m, (int)tiles_n, aligned, eflags);
+                A, B, a.C, M, N, K, a.sA, a.sB, a.sOut, (int)tiles_m, (int)tiles_n, aligned, eflags, kchunk);
             break;
         default:
             if constexpr (ES == 1) {
                 gemm_tile_kernel<ES, OUT_E4M3, BM, BN, BK, WM, WN, FA, FB><<<grid, block, 0, a.stream>>>(
                     A, B, a.C, M, N, K, a.sA, a.sB, a.sOut, (int)tiles_m, (int)tiles_n, aligned,
-                    eflags);
+                    eflags, kchunk);
             } else {
                 return hipErrorInvalidValue;
             }

@@ -22,6 +22,12 @@ struct GemmArgs {
     int fmt_a = 0;     // FP8 operand formats (Fp8Format: 0 = E4M3, 1 = E5M2); 0 for FP16
     int fmt_b = 0;
     int channel = 0;   // 1: sA holds M per-row scales and sB N per-column scales
+    // Split-K: with splits > 1 the launch covers K in ranges of k_chunk and
+    // writes FP32 partial sums to ws[split][M][N] instead of C; the reduce
+    // launch (launch_splitk_reduce) then writes C.
+    float* ws = nullptr;
+    int splits = 1;
+    int64_t k_chunk = 0;
 };
 
 typedef hipError_t (*GemmLauncher)(const GemmArgs&);
@@ -34,6 +40,7 @@ struct GemmConfig {
     int bm, bn, bk;     // tile (stream: bm = max M, bn = columns per block, bk = k-slices)
     GemmLauncher launch;
     int fmt_mask = 0;   // FP8 operand pairs served: bit (2*fmt_a + fmt_b); 0 means E4M3 x E4M3 only
+    int kgran = 0;      // split-K: K ranges are multiples of kgran; 0 = this config does not split
 };
 
 constexpr int kAllFp8Pairs = 15;
@@ -53,6 +60,18 @@ const GemmConfig* dma_configs(int* count);
 // Returns NULL if none fits.
 const GemmConfig* select_config(int kind, int out_dtype, int64_t M, int64_t N, int64_t K, int fmt_a = 0,
                                 int fmt_b = 0);
+
+// Split-K plan for the workspace entry points: the configuration, the number
+// of K ranges and their length (splits == 1: no split, the plain launch).
+struct SplitPlan {
+    const GemmConfig* cfg;
+    int splits;
+    int64_t k_chunk;
+};
+SplitPlan plan_splitk(int kind, int out_dtype, int64_t M, int64_t N, int64_t K, int fmt_a = 0, int fmt_b = 0);
+
+// C = epilogue(sum over a.splits slices of a.ws), in slice order.
+hipError_t launch_splitk_reduce(const GemmArgs& a);
 
 // amax / quantize launchers.
 // amax and (scale != NULL) the scale for FP8 format fmt, pow2 != 0 for a

@@ -18,6 +18,14 @@
 //      configs need M <= bound).
 //   Every rule only considers configurations compiled for the requested FP8
 //   operand formats (E4M3 / E5M2 for A and for B).
+// Split-K plan (workspace entry points): for M <= 256 (with N = K = 4096 that
+// is the HBM-bound side of the FP8 ridge point, about 600 flop per byte), when
+// the chosen configuration's grid has fewer than two workgroups per CU, so
+// too few loads are in flight to stream B at HBM speed, K is cut into 2, 4, 8, ...
+// ranges (multiples of the configuration's K granularity) until the grid
+// reaches that, or K runs out. Decode shapes switch to the streaming variant
+// with the smallest K granularity. LIBGEMM_SPLITS=<n> forces the number of
+// ranges (clamped to what K allows).
 #include <cstdlib>
 #include <cstring>
 
@@ -28,6 +36,7 @@ namespace libgemm {
 namespace {
 
 constexpr int64_t kNumCUs = 256;
+constexpr int64_t kSplitMaxM = 256;
 
 const GemmConfig* find_named(const char* name, int kind, int64_t M, int fa = 0, int fb = 0) {
     int ns = 0, nt = 0;
@@ -97,6 +106,37 @@ const GemmConfig* select_config(int kind, int out_dtype, int64_t M, int64_t N, i
         }
     }
     return tile_with(kind, 64, 0, fa, fb);
+}
+
+SplitPlan plan_splitk(int kind, int out_dtype, int64_t M, int64_t N, int64_t K, int fa, int fb) {
+    if (kind == KIND_F16) fa = fb = 0;
+    SplitPlan p{select_config(kind, out_dtype, M, N, K, fa, fb), 1, K};
+    const GemmConfig* c = p.cfg;
+    if (!c || M <= 0 || N <= 0 || K <= 0 || M > kSplitMaxM) return p;
+    if (c->family == 1 && !std::getenv("LIBGEMM_CONFIG")) {
+        int ns = 0;
+        const GemmConfig* st = stream_configs(&ns);
+        for (int i = 0; i < ns; ++i) {
+            const GemmConfig& d = st[i];
+            if (d.kind == kind && d.bm == c->bm && serves_formats(d, fa, fb) && d.kgran > 0 && d.kgran < c->kgran)
+                c = &d;
+        }
+    }
+    if (c->kgran <= 0) return p;
+    const int64_t base = c->family == 1 ? (N + c->bn - 1) / c->bn : ((M + c->bm - 1) / c->bm) * ((N + c->bn - 1) / c->bn);
+    const int64_t max_splits = K / c->kgran;
+    int64_t splits = 1;
+    while (base * splits < 2 * kNumCUs && splits * 2 <= max_splits && splits < 64) splits *= 2;
+    if (const char* env = std::getenv("LIBGEMM_SPLITS")) {
+        const int64_t want = std::atoll(env);
+        if (want >= 1) splits = want < max_splits ? want : (max_splits > 1 ? max_splits : 1);
+    }
+    if (splits <= 1) return p;
+    const int64_t per = (K + splits - 1) / splits;
+    const int64_t chunk = (per + c->kgran - 1) / c->kgran * c->kgran;
+    const int64_t n = (K + chunk - 1) / chunk;
+    if (n <= 1 || n > 65535) return p;
+    return SplitPlan{c, (int)n, chunk};
 }
 
 }  // namespace libgemm

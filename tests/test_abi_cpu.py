@@ -40,7 +40,7 @@ def test_header_declares_the_entry_points():
     assert {"gemm_f16", "gemm_fp8_scaled", "quantize_fp8", "amax_f32", "gemm_status_str",
             "gemm_select_config", "gemm_fp8_fmt", "quantize_fp8_fmt", "amax_scale_f32",
             "gemm_select_config_fmt", "gemm_fp8_channel", "amax_scale_channel_f32",
-            "quantize_fp8_channel"} <= names
+            "quantize_fp8_channel", "gemm_fp8_splitk", "gemm_f16_splitk", "gemm_splitk_plan"} <= names
 
 
 def test_library_exports_every_declared_symbol():
@@ -143,6 +143,61 @@ def test_channel_entry_points_argument_validation():
     assert L.quantize_fp8_channel(FAKE, 4, 8, 1, FAKE2, FAKE2 + 16, 0, None) == -8       # q over scale[4..]
     assert L.quantize_fp8_channel(FAKE, 4, 8, 0, FAKE2, FAKE + 127, 0, None) == -8
     assert L.quantize_fp8_channel(None, 0, 8, 0, None, None, 0, None) == 0
+
+
+def test_splitk_plan_rules():
+    plan = g.splitk_plan
+    # decode: the 256-thread streaming variants, K cut until >= 512 workgroups
+    assert plan(g.KIND_FP8, g.OUT_E4M3, 1, 4096, 4096) == ("stream_fp8_m1_c128_t256", 16, 16 * 4096 * 4)
+    assert plan(g.KIND_F16, g.OUT_F16, 1, 12288, 4096) == ("stream_f16_m1_c64_t256", 4, 4 * 12288 * 4)
+    # mid-M: 64x64 tiles, 2 x 64 tiles -> 4 ranges of 1024
+    assert plan(g.KIND_FP8, g.OUT_E4M3, 65, 4096, 4096) == ("tile_fp8_64x64x128_w2x2", 4, 4 * 65 * 4096 * 4)
+    assert plan(g.KIND_FP8, g.OUT_F32, 16, 4096, 4096)[1] == 8
+    # enough tiles, or large M: no split, no workspace
+    assert plan(g.KIND_FP8, g.OUT_E4M3, 512, 4096, 4096)[1:] == (1, 0)
+    assert plan(g.KIND_FP8, g.OUT_E4M3, 4096, 4096, 4096)[1:] == (1, 0)
+    # K shorter than two granules: no split
+    assert plan(g.KIND_FP8, g.OUT_F32, 65, 4096, 200)[1:] == (1, 0)
+    # ragged K: ranges are granule multiples and none is empty
+    name, splits, nbytes = plan(g.KIND_FP8, g.OUT_F32, 65, 4096, 300)
+    assert (name, splits, nbytes) == ("tile_fp8_64x64x128_w2x2", 2, 2 * 65 * 4096 * 4)
+
+
+def test_splitk_plan_overrides(monkeypatch):
+    monkeypatch.setenv("LIBGEMM_SPLITS", "3")
+    assert g.splitk_plan(g.KIND_FP8, g.OUT_F32, 65, 4096, 4096)[1] == 3
+    monkeypatch.setenv("LIBGEMM_SPLITS", "1000")        # clamped to K / granule
+    assert g.splitk_plan(g.KIND_FP8, g.OUT_F32, 65, 4096, 4096)[1] == 4096 // 128
+    monkeypatch.setenv("LIBGEMM_SPLITS", "1")
+    assert g.splitk_plan(g.KIND_FP8, g.OUT_F32, 65, 4096, 4096)[1:] == (1, 0)
+    monkeypatch.delenv("LIBGEMM_SPLITS")
+    monkeypatch.setenv("LIBGEMM_CONFIG", "tile_fp8_128x128x128_w2x2")
+    name, splits, _ = g.splitk_plan(g.KIND_FP8, g.OUT_F32, 65, 4096, 4096)
+    assert name == "tile_fp8_128x128x128_w2x2" and splits == 16
+    monkeypatch.setenv("LIBGEMM_CONFIG", "dma_fp8_256x256x64_s4")   # cannot split
+    assert g.splitk_plan(g.KIND_FP8, g.OUT_F32, 65, 4096, 4096)[1:] == (1, 0)
+
+
+def test_splitk_argument_validation():
+    L = g.lib()
+    s = FAKE3 + (1 << 24)
+    W = 5 << 40
+    need = 4 * 65 * 4096 * 4
+    args = (FAKE, 0, FAKE2, 0, s, s + 4, None, FAKE3, 0, 65, 4096, 4096)
+    assert L.gemm_fp8_splitk(*args, W, need - 1, None) == -9          # too small
+    assert L.gemm_fp8_splitk(*args, W + 4, need, None) == -9          # not 16-byte aligned
+    assert L.gemm_fp8_splitk(*args, W, -1, None) == -9
+    assert L.gemm_fp8_splitk(*args, FAKE3 - 16, need, None) == -8     # covers C
+    assert L.gemm_fp8_splitk(*args, FAKE + 65 * 4096 - 16, need, None) == -8   # covers the end of A
+    assert L.gemm_fp8_splitk(FAKE, 0, FAKE2, 0, s, s + 4, None, FAKE3, 2, 65, 4096, 4096, W, need, None) == -4
+    assert L.gemm_fp8_splitk(FAKE, 0, FAKE2, 7, s, s + 4, None, FAKE3, 0, 65, 4096, 4096, W, need, None) == -3
+    assert L.gemm_f16_splitk(FAKE, FAKE2, FAKE3, 1, 1, 12288, 4096, W, 4 * 12288 * 4 - 4, None) == -9
+    assert L.gemm_f16_splitk(FAKE, FAKE2, FAKE3, 2, 1, 12288, 4096, W, 1 << 30, None) == -3
+    assert L.gemm_f16_splitk(FAKE, FAKE2, FAKE3, 1, 1, 12288, 4096, FAKE2 + 64, 1 << 30, None) == -8   # inside B
+    assert L.gemm_splitk_plan(5, 0, 1, 1, 1, 0, 0, None, 0, None, None) == -3
+    assert L.gemm_splitk_plan(1, 0, 1, -1, 1, 0, 0, None, 0, None, None) == -2
+    assert L.gemm_splitk_plan(1, 0, 1, 1, 1, 0, 0, None, 0, None, None) == 0   # every output may be NULL
+    assert g.STATUS_NAMES[-9] == "GEMM_ERR_WORKSPACE" and g.status_str(-9).startswith("workspace")
 
 
 def test_select_config_formats():

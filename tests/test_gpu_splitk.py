@@ -1,0 +1,189 @@
+"""GPU parity for the split-K entry points (gemm_fp8_splitk, gemm_f16_splitk):
+forced numbers of K ranges on ragged shapes for every kernel family that
+splits and every output type, the M sweep at N = K = 4096 in its planned
+configuration (every element against the oracle), the FP16 decode shapes,
+and the workspace rules (determinism, reuse, NULL workspace, too small)."""
+import numpy as np
+import pytest
+import torch
+
+import oracle as orc
+import precision_dense_gemm_03_amd as g
+import workloads as wl
+from parity import check_f16, check_f32, check_fp8, fp8_dot_allowance
+
+pytestmark = pytest.mark.gpu
+
+DEV = torch.device("cuda:0")
+ORC_FMT = {g.FMT_E4M3: orc.FMT_E4M3, g.FMT_E5M2: orc.FMT_E5M2}
+
+
+def say(*a):
+    print(*a, flush=True)
+
+
+@pytest.fixture(scope="module", autouse=True)
+def _gpu():
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    torch.cuda.set_device(DEV)
+    g.lib()
+    yield
+    torch.cuda.synchronize()
+
+
+def dev(x):
+    return torch.from_numpy(np.ascontiguousarray(x)).to(DEV)
+
+
+def host(t):
+    torch.cuda.synchronize()
+    return t.cpu().numpy()
+
+
+def scalar(v):
+    return torch.tensor([float(np.float32(v))], dtype=torch.float32, device=DEV)
+
+
+def workspace_for(kind, out, M, N, K, fa=0, fb=0):
+    name, splits, nbytes = g.splitk_plan(kind, out, M, N, K, fa, fb)
+    return name, splits, torch.empty(max(nbytes, 16), dtype=torch.uint8, device=DEV)
+
+
+# (config forced or None, forced splits, M, N, K): the streaming variants, the
+# 64 and 128 tiles; K not a multiple of the range length; N not a multiple
+# of 4 (scalar reduce); K shorter than the ranges need (fewer ranges).
+FP8_CASES = [(None, 16, 1, 4096, 4096), ("stream_fp8_m4_c128_t256", 5, 3, 1000, 1500),
+             ("stream_fp8_m1_c64_t1024", 2, 1, 777, 4100), (None, 4, 65, 1000, 4096),
+             ("tile_fp8_64x64x128_w2x2", 3, 100, 203, 1000), ("tile_fp8_128x128x128_w2x2", 7, 129, 384, 2000),
+             ("tile_fp8_256x256x128_w2x4", 2, 200, 300, 700), (None, 8, 16, 520, 640)]
+
+
+@pytest.mark.parametrize("cfg,splits,M,N,K", FP8_CASES)
+@pytest.mark.parametrize("fa,fb", [(g.FMT_E4M3, g.FMT_E4M3), (g.FMT_E5M2, g.FMT_E4M3)])
+def test_fp8_splitk_forced(cfg, splits, M, N, K, fa, fb, monkeypatch):
+    if cfg:
+        monkeypatch.setenv("LIBGEMM_CONFIG", cfg)
+    monkeypatch.setenv("LIBGEMM_SPLITS", str(splits))
+    name, got_splits, ws = workspace_for(g.KIND_FP8, g.OUT_F32, M, N, K, fa, fb)
+    assert got_splits > 1 and (cfg is None or name == cfg)
+    say(f"fp8 split-K {name} splits={got_splits} {M}x{N}x{K} a={fa} b={fb}")
+    enc = {g.FMT_E4M3: wl.random_e4m3_codes, g.FMT_E5M2: wl.random_e5m2_codes}
+    ca, cb = enc[fa]((M, K), 3 * M + K), enc[fb]((K, N), 7 * N + K)
+    ofa, ofb = ORC_FMT[fa], ORC_FMT[fb]
+    R, S = orc.gemm(ofa, ca, cb, fmt_b=ofb)
+    T = fp8_dot_allowance(ca, cb, fmt_a=ofa, fmt_b=ofb) if M > 16 or name.startswith("tile") else None
+    sa, sb = np.float32(0.125), np.float32(0.5)
+    ta, tb, tsa, tsb = dev(ca), dev(cb), scalar(sa), scalar(sb)
+    C = torch.empty((M, N), dtype=torch.float32, device=DEV)
+    g.gemm_fp8_splitk(ta, fa, tb, fb, tsa, tsb, C, workspace=ws)
+    check_f32(host(C), R, S, sa, sb, what=f"{name} f32", T=T)
+    V = R * float(sa) * float(sb)
+    C16 = torch.empty((M, N), dtype=torch.float16, device=DEV)
+    g.gemm_fp8_splitk(ta, fa, tb, fb, tsa, tsb, C16, workspace=ws)
+    slack = (1e-5 * S + (0 if T is None else T)) * float(sa) * float(sb)
+    fin = np.abs(V) + slack < 65520.0
+    check_f16(host(C16).astype(np.float64)[fin], R[fin], S[fin], sa, sb, what=f"{name} f16",
+              T=None if T is None else T[fin])
+    for out_fmt in (g.FMT_E4M3, g.FMT_E5M2):
+        s_out = orc.scale(np.float32(np.max(np.abs(V))), ORC_FMT[out_fmt])
+        C8 = torch.empty((M, N), dtype=torch.uint8, device=DEV)
+        g.gemm_fp8_splitk(ta, fa, tb, fb, tsa, tsb, C8, scalar(s_out), workspace=ws, out_fmt=out_fmt)
+        check_fp8(host(C8), R, S, sa, sb, s_out, ORC_FMT[out_fmt], what=f"{name} fp8 out {out_fmt}", T=T)
+
+
+@pytest.mark.parametrize("M", [1, 63, 65, 127, 129, 256])
+def test_fp8_splitk_m_sweep_full_size(M):
+    """N = K = 4096, inputs N(0,1) with 0.1% outliers x50, per-tensor amax
+    scales, FP8 output with sOut = amax(C_ref)/448, in the planned
+    configuration; every element against the oracle."""
+    N = K = 4096
+    name, splits, ws = workspace_for(g.KIND_FP8, g.OUT_E4M3, M, N, K)
+    say(f"fp8 split-K sweep M={M}: {name} splits={splits}")
+    assert splits > 1
+    xa = wl.normal_with_outliers_f32((M, K), 2000 + M)
+    xb = wl.normal_with_outliers_f32((K, N), 2001)
+    sa = orc.scale_from_amax(orc.amax(xa))
+    sb = orc.scale_from_amax(orc.amax(xb))
+    ca, cb = orc.quantize(xa, sa), orc.quantize(xb, sb)
+    R, S = orc.gemm(orc.FMT_E4M3, ca, cb)
+    T = fp8_dot_allowance(ca, cb)
+    V = R * float(sa) * float(sb)
+    s_out = orc.scale_from_amax(np.float32(np.max(np.abs(V))))
+    ta, tb = dev(ca), dev(cb)
+    C8 = torch.empty((M, N), dtype=torch.uint8, device=DEV)
+    g.gemm_fp8_splitk(ta, g.FMT_E4M3, tb, g.FMT_E4M3, scalar(sa), scalar(sb), C8, scalar(s_out), workspace=ws)
+    check_fp8(host(C8), R, S, sa, sb, s_out, orc.FMT_E4M3, what=f"sweep M={M} e4m3", T=T)
+    C = torch.empty((M, N), dtype=torch.float32, device=DEV)
+    g.gemm_fp8_splitk(ta, g.FMT_E4M3, tb, g.FMT_E4M3, scalar(sa), scalar(sb), C, workspace=ws)
+    check_f32(host(C), R, S, sa, sb, what=f"sweep M={M} f32", T=T)
+
+
+@pytest.mark.parametrize("M", [1, 4, 16])
+def test_f16_splitk_decode(M):
+    """[M,4096] x [4096,12288]: B ~ N(0, 0.02), A ~ N(0, 1), FP16 output."""
+    N, K = 12288, 4096
+    name, splits, ws = workspace_for(g.KIND_F16, g.OUT_F16, M, N, K)
+    say(f"f16 split-K decode M={M}: {name} splits={splits}")
+    assert splits > 1
+    a16 = wl.random_normal_f32((M, K), 31).astype(np.float16)
+    b16 = (wl.random_normal_f32((K, N), 32) * np.float32(0.02)).astype(np.float16)
+    R, S = orc.gemm(orc.FMT_F16, a16.view(np.uint16), b16.view(np.uint16))
+    C = torch.empty((M, N), dtype=torch.float16, device=DEV)
+    g.gemm_f16_splitk(dev(a16), dev(b16), C, workspace=ws)
+    check_f16(host(C), R, S, what=f"decode M={M}")
+    C32 = torch.empty((M, N), dtype=torch.float32, device=DEV)
+    g.gemm_f16_splitk(dev(a16), dev(b16), C32, workspace=ws)
+    check_f32(host(C32), R, S, what=f"decode M={M} f32")
+
+
+@pytest.mark.parametrize("cfg,splits,M,N,K", [("stream_f16_m8_c64_t256", 3, 7, 1000, 900),
+                                              ("tile_f16_64x64x64_w2x2", 5, 100, 300, 700),
+                                              ("tile_f16_128x128x64_w2x2", 2, 130, 202, 333)])
+def test_f16_splitk_forced(cfg, splits, M, N, K, monkeypatch):
+    monkeypatch.setenv("LIBGEMM_CONFIG", cfg)
+    monkeypatch.setenv("LIBGEMM_SPLITS", str(splits))
+    name, got, ws = workspace_for(g.KIND_F16, g.OUT_F32, M, N, K)
+    assert name == cfg and got > 1
+    say(f"f16 split-K {name} splits={got} {M}x{N}x{K}")
+    a16, b16 = wl.random_f16((M, K), 41 + M), wl.random_f16((K, N), 43 + N)
+    R, S = orc.gemm(orc.FMT_F16, a16.view(np.uint16), b16.view(np.uint16))
+    C = torch.empty((M, N), dtype=torch.float32, device=DEV)
+    g.gemm_f16_splitk(dev(a16), dev(b16), C, workspace=ws)
+    check_f32(host(C), R, S, what=f"{cfg} f32")
+    C16 = torch.empty((M, N), dtype=torch.float16, device=DEV)
+    g.gemm_f16_splitk(dev(a16), dev(b16), C16, workspace=ws)
+    check_f16(host(C16), R, S, what=f"{cfg} f16")
+
+
+def test_splitk_workspace_rules():
+    M, N, K = 65, 4096, 4096
+    ca, cb = wl.random_e4m3_codes((M, K), 5), wl.random_e4m3_codes((K, N), 6)
+    R, S = orc.gemm(orc.FMT_E4M3, ca, cb)
+    T = fp8_dot_allowance(ca, cb)
+    ta, tb, one = dev(ca), dev(cb), scalar(1.0)
+    name, splits, ws = workspace_for(g.KIND_FP8, g.OUT_F32, M, N, K)
+    say(f"split-K workspace rules: {name} splits={splits}")
+    # deterministic: the same bits twice, with garbage left in the workspace
+    ws.fill_(0xA5)
+    C1 = torch.empty((M, N), dtype=torch.float32, device=DEV)
+    C2 = torch.empty((M, N), dtype=torch.float32, device=DEV)
+    g.gemm_fp8_splitk(ta, 0, tb, 0, one, one, C1, workspace=ws)
+    g.gemm_fp8_splitk(ta, 0, tb, 0, one, one, C2, workspace=ws)
+    assert np.array_equal(host(C1).view(np.uint32), host(C2).view(np.uint32))
+    check_f32(host(C1), R, S, what="split", T=T)
+    # a workspace from a larger request serves a smaller one (reuse)
+    Cs = torch.empty((3, N), dtype=torch.float32, device=DEV)
+    g.gemm_fp8_splitk(ta[:3].contiguous(), 0, tb, 0, one, one, Cs, workspace=ws)
+    check_f32(host(Cs), R[:3], S[:3], what="reused workspace", T=T[:3])
+    # the library's NULL-workspace path is the plain kernel
+    L = g.lib()
+    C3 = torch.empty((M, N), dtype=torch.float32, device=DEV)
+    rc = L.gemm_fp8_splitk(ta.data_ptr(), 0, tb.data_ptr(), 0, one.data_ptr(), one.data_ptr(), None, C3.data_ptr(),
+                           g.OUT_F32, M, N, K, None, 0, torch.cuda.current_stream().cuda_stream)
+    assert rc == 0
+    check_f32(host(C3), R, S, what="null workspace", T=T)
+    # too small: an error, nothing launched
+    small = torch.empty(1024, dtype=torch.uint8, device=DEV)
+    with pytest.raises(g.GemmError):
+        g.gemm_fp8_splitk(ta, 0, tb, 0, one, one, C3, workspace=small)
