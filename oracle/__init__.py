@@ -74,6 +74,10 @@ def _load():
     lib.orc_scale_n.argtypes = [_vp, _c_i64, ctypes.c_int, ctypes.c_int, _vp]
     lib.orc_quantize_channel.restype = None
     lib.orc_quantize_channel.argtypes = [_vp, _c_i64, _c_i64, ctypes.c_int, _vp, ctypes.c_int, _vp]
+    lib.orc_guard_scale.restype = ctypes.c_float
+    lib.orc_guard_scale.argtypes = [ctypes.c_float, ctypes.c_float]
+    lib.orc_guard_to_f16.restype = None
+    lib.orc_guard_to_f16.argtypes = [_vp, _c_i64, ctypes.c_float, _vp]
     lib.orc_num_threads.restype = ctypes.c_int
     lib.orc_num_threads.argtypes = []
     _lib = lib
@@ -207,6 +211,19 @@ def quantize_channel(x, s, axis, fmt=FMT_E4M3) -> np.ndarray:
         raise ValueError("one scale per channel")
     out = np.empty(a.shape, np.uint8)
     _load().orc_quantize_channel(_ptr(a), rows, cols, int(axis), _ptr(sv), int(fmt), _ptr(out))
+    return out
+
+
+def guard_scale(amax_a, amax_b) -> np.float32:
+    """FP16 dynamic-range guard scale min(1, 65504 / (amax_a * amax_b))."""
+    return np.float32(_load().orc_guard_scale(float(np.float32(amax_a)), float(np.float32(amax_b))))
+
+
+def guard_to_f16(x, s) -> np.ndarray:
+    """binary16 bits (uint16) of x * sqrt(s), each rounded to FP32 and then FP16."""
+    a = _c(x, np.float32)
+    out = np.empty(a.shape, np.uint16)
+    _load().orc_guard_to_f16(_ptr(a), a.size, float(np.float32(s)), _ptr(out))
     return out
 
 

@@ -34,6 +34,11 @@
  *   - A scale may be a power of two just above the calibrated maximum, so
  *     that scaling is exponent arithmetic (P2 §2.1). Read as: the smallest
  *     2^e with max|x| / 2^e <= the format's largest value.
+ *   - FP16 dynamic-range guard (P1, mixed-precision section): with max|A|
+ *     and max|B| taken on the GPU before the GEMM, s = min(1, 65504 /
+ *     (max|A| max|B|)); A and B are multiplied by sqrt(s) before they enter
+ *     the FP16 GEMM and the result is divided by s, so that no product of
+ *     the scaled FP16 operands exceeds the FP16 range.
  *   - Per-channel scaling is the named alternative to per-tensor scales
  *     (P2 §2.1, §3.2): one scale per row of A and per column of B, the
  *     per-tensor rule applied to each channel; the write-back multiplies the
@@ -344,6 +349,32 @@ ORC_API void orc_quantize(const float* x, int64_t n, float s, uint8_t* q) {
     for (int64_t i = 0; i < n; ++i) {
         float t = (float)((double)x[i] / (double)s);
         q[i] = orc_e4m3_encode((double)t);
+    }
+}
+
+/* --------------------------------------------- FP16 dynamic-range guard --- */
+
+/* s = min(1, 65504 / (aA * aB)) (P1, mixed-precision section). Read as: the
+ * product and the quotient in double (exact product of two floats; the
+ * quotient correctly rounded), the result rounded once to FP32. aA * aB == 0
+ * gives 65504/0 = inf, so s = 1; a NaN maximum also gives 1 (the NaN
+ * element poisons the GEMM by itself); a product so large that s rounds to 0
+ * in FP32 (inputs holding inf included) gives 0. */
+ORC_API float orc_guard_scale(float aA, float aB) {
+    const double q = 65504.0 / ((double)aA * (double)aB);
+    return q < 1.0 ? (float)q : 1.0f;
+}
+
+/* binary16 bits of fl32(x_i * fl32(sqrt(s))): the operand scaled by the
+ * square root of the guard scale in FP32, then rounded to FP16 (RNE, IEEE
+ * overflow to inf). sqrt and the product are formed in double and rounded to
+ * FP32 once, which is the correctly rounded FP32 result for both. */
+ORC_API void orc_guard_to_f16(const float* x, int64_t n, float s, uint16_t* out) {
+    const float r = (float)sqrt((double)s);
+#pragma omp parallel for schedule(static)
+    for (int64_t i = 0; i < n; ++i) {
+        const float t = (float)((double)x[i] * (double)r);
+        out[i] = orc_f16_round((double)t);
     }
 }
 
