@@ -266,6 +266,45 @@ int gemm_f16_splitk(const void* A, const void* B, void* C, int out_dtype,
                     int64_t M, int64_t N, int64_t K, void* workspace, int64_t workspace_bytes,
                     hipStream_t stream);
 
+/* ------------------------------------------- FP16 dynamic-range guard */
+
+/*
+ * gemm_f16_guarded — C = A·B for FP32 inputs computed as an FP16 GEMM under
+ * P1's dynamic-range guard (mixed-precision section): FP16 holds at most
+ * ±65504, so max|A| and max|B| are taken on the GPU first, then
+ *   s  = min(1, 65504 / (max|A| · max|B|))   (product and quotient in double,
+ *        rounded once to FP32; 1 when A or B is all zero)
+ *   A' = FP16(fl32(A · fl32(sqrt(s)))),  B' likewise   (RNE, IEEE overflow)
+ *   C  = (A'·B', FP32 accumulation) · fl32(1/s)   (F32, or RNE to F16)
+ * so every product of the scaled operands stays within the FP16 range. Both
+ * operands stay finite when max|A| / max|B| (and its inverse) is at most
+ * 65504; beyond that the larger one can still overflow to inf, as the
+ * formula stands.
+ *   A          device, float[M*K], row-major
+ *   B          device, float[K*N], row-major
+ *   C          device, float or _Float16 [M*N] per out_dtype (GEMM_OUT_F32 or
+ *              GEMM_OUT_F16)
+ *   scale      device pointer to one float receiving s, or NULL
+ *   workspace  device memory, 16-byte aligned, of at least
+ *              gemm_f16_guarded_workspace_size(M, N, K) bytes. On return it
+ *              holds at offset 0 the floats max|A|, max|B|, s, sqrt(s), 1/s;
+ *              at offset 256 the scaled FP16 A' (M*K halves, row-major); and
+ *              at offset 256 + M*K*2 rounded up to a multiple of 256 the
+ *              scaled FP16 B' (K*N halves).
+ * Errors: GEMM_ERR_NULL (C or workspace NULL, or A/B NULL with K > 0),
+ * GEMM_ERR_WORKSPACE (too small or misaligned), GEMM_ERR_ALIAS (C, the
+ * workspace, scale, A and B must not overlap), and those of gemm_f16.
+ * M = 0 or N = 0 is a no-op; K = 0 writes zeros (and s = 1). Eight launches
+ * on `stream` (amax x2 with their clears, the scale, two conversions, the
+ * GEMM); calls that share a workspace must not run concurrently.
+ */
+int gemm_f16_guarded(const float* A, const float* B, void* C, int out_dtype,
+                     int64_t M, int64_t N, int64_t K, float* scale,
+                     void* workspace, int64_t workspace_bytes, hipStream_t stream);
+
+/* Bytes of workspace gemm_f16_guarded needs (GEMM_ERR_DIM for a bad size). */
+int64_t gemm_f16_guarded_workspace_size(int64_t M, int64_t N, int64_t K);
+
 /* Human-readable name of a status code (a static string). */
 const char* gemm_status_str(int status);
 

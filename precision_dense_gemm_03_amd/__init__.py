@@ -19,6 +19,8 @@ Functions keep the C names:
     gemm_fp8_splitk(A, fmt_a, B, fmt_b, sA, sB, C, sOut=None, workspace=None, stream=None, out_fmt=None)
     gemm_f16_splitk(A, B, C, workspace=None, stream=None)
     splitk_plan(kind, out_dtype, M, N, K, fmt_a=0, fmt_b=0) -> (config, splits, workspace_bytes)
+    gemm_f16_guarded(A, B, C, scale=None, workspace=None, stream=None) -> (C, scale)
+    guarded_workspace_size(M, N, K) -> int
     select_config(kind, out_dtype, M, N, K) -> str   (host-only query)
     select_config_fmt(kind, out_dtype, M, N, K, fmt_a, fmt_b) -> str
 The output dtype of a GEMM is taken from C: float32, float16, or 8-bit codes
@@ -99,6 +101,10 @@ def lib() -> ctypes.CDLL:
     L.gemm_splitk_plan.restype = i32
     L.gemm_splitk_plan.argtypes = [i32, i32, i64, i64, i64, i32, i32, ctypes.c_char_p, i32,
                                    ctypes.POINTER(i32), ctypes.POINTER(i64)]
+    L.gemm_f16_guarded.restype = i32
+    L.gemm_f16_guarded.argtypes = [vp, vp, vp, i32, i64, i64, i64, vp, vp, i64, vp]
+    L.gemm_f16_guarded_workspace_size.restype = i64
+    L.gemm_f16_guarded_workspace_size.argtypes = [i64, i64, i64]
     L.gemm_select_config_fmt.restype = i32
     L.gemm_select_config_fmt.argtypes = [i32, i32, i64, i64, i64, i32, i32, ctypes.c_char_p, i32]
     _lib = L
@@ -310,6 +316,32 @@ def gemm_f16_splitk(A, B, C, workspace=None, stream=None):
     _check(lib().gemm_f16_splitk(_ptr(A), _ptr(B), _ptr(C), out, M, N, K, ws, nbytes, _stream_handle(stream)),
            "gemm_f16_splitk")
     return C
+
+
+def guarded_workspace_size(M: int, N: int, K: int) -> int:
+    n = int(lib().gemm_f16_guarded_workspace_size(M, N, K))
+    _check(n if n < 0 else 0, "gemm_f16_guarded_workspace_size")
+    return n
+
+
+def gemm_f16_guarded(A, B, C, scale=None, workspace=None, stream=None):
+    """C = A @ B for float32 A[M,K], B[K,N] through the FP16 GEMM under the
+    dynamic-range guard; returns (C, scale) with scale the one-element s."""
+    torch = _torch()
+    if A.dtype != torch.float32 or B.dtype != torch.float32:
+        raise ValueError("gemm_f16_guarded takes float32 A and B")
+    out = _out_dtype(C)
+    if out not in (OUT_F32, OUT_F16):
+        raise ValueError("gemm_f16_guarded writes float32 or float16")
+    M, N, K = _dims(A, B, C)
+    if scale is None:
+        scale = torch.empty(1, dtype=torch.float32, device=C.device)
+    if workspace is None:
+        workspace = torch.empty(guarded_workspace_size(M, N, K), dtype=torch.uint8, device=C.device)
+    _check(lib().gemm_f16_guarded(_ptr(A), _ptr(B), _ptr(C), out, M, N, K, _ptr(scale), _ptr(workspace),
+                                  workspace.numel() * workspace.element_size(), _stream_handle(stream)),
+           "gemm_f16_guarded")
+    return C, scale
 
 
 def quantize_fp8(x, scale, q=None, stream=None):

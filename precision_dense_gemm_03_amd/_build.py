@@ -17,7 +17,8 @@ BUILD = os.path.join(PKG, "_build")
 LIB = os.path.join(PKG, "libgemm.so")
 
 SOURCES = ["abi.cpp", "selector.cpp", "amax_quant.hip", "amax_quant_channel.hip", "splitk_reduce.hip",
-           "gemm_tile.hip", "gemm_tile_mixed.hip", "gemm_dma.hip", "gemm_dma_mixed.hip", "gemm_stream.hip"]
+           "guard_f16.hip", "gemm_tile.hip", "gemm_tile_mixed.hip", "gemm_dma.hip", "gemm_dma_mixed.hip",
+           "gemm_stream.hip"]
 
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 

@@ -180,6 +180,54 @@ int gemm_f16_splitk(const void* A, const void* B, void* C, int out_dtype, int64_
     return run_gemm_splitk(KIND_F16, a, workspace, workspace_bytes, in_ptr, in_bytes, 3);
 }
 
+// Workspace of gemm_f16_guarded: 256 bytes of scalars (amax of A and B, s,
+// sqrt(s), 1/s), then the scaled FP16 copies of A and of B, each starting on
+// a 256-byte boundary.
+static int64_t round256(int64_t b) { return (b + 255) / 256 * 256; }
+static int64_t guard_ws_a16(int64_t, int64_t, int64_t) { return 256; }
+static int64_t guard_ws_b16(int64_t M, int64_t, int64_t K) { return 256 + round256(M * K * 2); }
+
+int64_t gemm_f16_guarded_workspace_size(int64_t M, int64_t N, int64_t K) {
+    if (!dim_ok(M) || !dim_ok(N) || !dim_ok(K)) return GEMM_ERR_DIM;
+    return guard_ws_b16(M, N, K) + round256(K * N * 2);
+}
+
+int gemm_f16_guarded(const float* A, const float* B, void* C, int out_dtype, int64_t M, int64_t N, int64_t K,
+                     float* scale, void* workspace, int64_t workspace_bytes, hipStream_t stream) {
+    if (out_dtype != GEMM_OUT_F32 && out_dtype != GEMM_OUT_F16) return GEMM_ERR_DTYPE;
+    if (!dim_ok(M) || !dim_ok(N) || !dim_ok(K)) return GEMM_ERR_DIM;
+    if (M == 0 || N == 0) return GEMM_OK;
+    if (!C || !workspace) return GEMM_ERR_NULL;
+    if (K > 0 && (!A || !B)) return GEMM_ERR_NULL;
+    const int64_t need = gemm_f16_guarded_workspace_size(M, N, K);
+    if (workspace_bytes < need || ((uintptr_t)workspace & 15u) != 0) return GEMM_ERR_WORKSPACE;
+    const int64_t cbytes = M * N * out_size(out_dtype);
+    const void* in_ptr[3] = {A, B, scale};
+    const int64_t in_bytes[3] = {M * K * 4, K * N * 4, 4};
+    for (int i = 0; i < 3; ++i)
+        if (overlaps(C, cbytes, in_ptr[i], in_bytes[i]) || overlaps(workspace, need, in_ptr[i], in_bytes[i]))
+            return GEMM_ERR_ALIAS;
+    if (overlaps(workspace, need, C, cbytes) || overlaps(scale, 4, A, M * K * 4) || overlaps(scale, 4, B, K * N * 4))
+        return GEMM_ERR_ALIAS;
+    const int st = check_device();
+    if (st != GEMM_OK) return st;
+    uint8_t* ws = reinterpret_cast<uint8_t*>(workspace);
+    float* amax_a = reinterpret_cast<float*>(ws);
+    float* amax_b = amax_a + 1;
+    float* scalars = amax_a + 2;   // s, sqrt(s), 1/s
+    _Float16* a16 = reinterpret_cast<_Float16*>(ws + guard_ws_a16(M, N, K));
+    _Float16* b16 = reinterpret_cast<_Float16*>(ws + guard_ws_b16(M, N, K));
+    int s1 = status_of(launch_amax(A, M * K, amax_a, nullptr, GEMM_FMT_E4M3, 0, stream));
+    if (s1 == GEMM_OK) s1 = status_of(launch_amax(B, K * N, amax_b, nullptr, GEMM_FMT_E4M3, 0, stream));
+    if (s1 == GEMM_OK) s1 = status_of(launch_guard_scale(amax_a, amax_b, scalars, scale, stream));
+    if (s1 == GEMM_OK) s1 = status_of(launch_guard_to_f16(A, M * K, scalars, a16, stream));
+    if (s1 == GEMM_OK) s1 = status_of(launch_guard_to_f16(B, K * N, scalars, b16, stream));
+    if (s1 != GEMM_OK) return s1;
+    // The FP16 GEMM; its epilogue multiplies the FP32 sum by *sA = 1/s.
+    GemmArgs a{a16, b16, C, scalars + 2, nullptr, nullptr, out_dtype, M, N, K, stream};
+    return run_gemm(KIND_F16, a);
+}
+
 int gemm_splitk_plan(int kind, int out_dtype, int64_t M, int64_t N, int64_t K, int fmt_a, int fmt_b, char* buf,
                      int buflen, int* splits, int64_t* workspace_bytes) {
     if (kind != KIND_F16 && kind != KIND_FP8) return GEMM_ERR_DTYPE;

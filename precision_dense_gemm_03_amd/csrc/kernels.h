@@ -85,6 +85,11 @@ hipError_t launch_amax_channel(const float* x, int64_t rows, int64_t cols, int a
                                int fmt, int pow2, hipStream_t stream);
 hipError_t launch_quantize_channel(const float* x, int64_t rows, int64_t cols, int axis, const float* scale,
                                    uint8_t* q, int fmt, hipStream_t stream);
+// FP16 dynamic-range guard: scalars[0..2] = s, sqrt(s), 1/s from the two
+// maxima (scale_out, if not NULL, receives s); y = FP16(fl32(x * sqrt(s))).
+hipError_t launch_guard_scale(const float* amax_a, const float* amax_b, float* scalars, float* scale_out,
+                              hipStream_t stream);
+hipError_t launch_guard_to_f16(const float* x, int64_t n, const float* scalars, _Float16* y, hipStream_t stream);
 // Writes zeros to an [M,N] output of the given dtype (the K = 0 empty sum).
 hipError_t launch_fill_zero(void* C, int64_t count, int out_dtype, hipStream_t stream);
 

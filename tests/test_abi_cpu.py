@@ -40,7 +40,8 @@ def test_header_declares_the_entry_points():
     assert {"gemm_f16", "gemm_fp8_scaled", "quantize_fp8", "amax_f32", "gemm_status_str",
             "gemm_select_config", "gemm_fp8_fmt", "quantize_fp8_fmt", "amax_scale_f32",
             "gemm_select_config_fmt", "gemm_fp8_channel", "amax_scale_channel_f32",
-            "quantize_fp8_channel", "gemm_fp8_splitk", "gemm_f16_splitk", "gemm_splitk_plan"} <= names
+            "quantize_fp8_channel", "gemm_fp8_splitk", "gemm_f16_splitk", "gemm_splitk_plan",
+            "gemm_f16_guarded", "gemm_f16_guarded_workspace_size"} <= names
 
 
 def test_library_exports_every_declared_symbol():
@@ -198,6 +199,26 @@ def test_splitk_argument_validation():
     assert L.gemm_splitk_plan(1, 0, 1, -1, 1, 0, 0, None, 0, None, None) == -2
     assert L.gemm_splitk_plan(1, 0, 1, 1, 1, 0, 0, None, 0, None, None) == 0   # every output may be NULL
     assert g.STATUS_NAMES[-9] == "GEMM_ERR_WORKSPACE" and g.status_str(-9).startswith("workspace")
+
+
+def test_guarded_entry_point_validation():
+    L = g.lib()
+    M, N, K = 64, 80, 96
+    need = 256 + (M * K * 2 + 255) // 256 * 256 + (K * N * 2 + 255) // 256 * 256
+    assert g.guarded_workspace_size(M, N, K) == need
+    assert L.gemm_f16_guarded_workspace_size(-1, 2, 3) == -2
+    W = 5 << 40
+    args = (FAKE, FAKE2, FAKE3, 0, M, N, K, None)
+    assert L.gemm_f16_guarded(*args, None, 0, None) == -1                 # workspace required
+    assert L.gemm_f16_guarded(*args, W, need - 1, None) == -9
+    assert L.gemm_f16_guarded(*args, W + 8, need, None) == -9             # misaligned
+    assert L.gemm_f16_guarded(*args, FAKE2 + 16, need, None) == -8        # overlaps B
+    assert L.gemm_f16_guarded(*args, FAKE3 + 64, need, None) == -8        # overlaps C
+    assert L.gemm_f16_guarded(FAKE, FAKE2, FAKE3, 2, M, N, K, None, W, need, None) == -3   # no FP8 output
+    assert L.gemm_f16_guarded(FAKE, FAKE2, FAKE + 100, 0, M, N, K, None, W, need, None) == -8   # C inside A
+    assert L.gemm_f16_guarded(FAKE, FAKE2, FAKE3, 0, M, N, K, FAKE + 8, W, need, None) == -8    # scale inside A
+    assert L.gemm_f16_guarded(None, FAKE2, FAKE3, 0, M, N, K, None, W, need, None) == -1
+    assert L.gemm_f16_guarded(None, None, None, 0, 0, N, K, None, None, 0, None) == 0      # M = 0: no-op
 
 
 def test_select_config_formats():
