@@ -56,17 +56,19 @@ const GemmConfig* find_named(const char* name, int kind, int64_t M, int fa = 0, 
 }
 
 // The preferred configuration of each tile size. 256x256 tiles use the
-// direct-load kernel (4 waves of 128x128, 4-stage LDS ring; it hands
-// unaligned operands to the register-staged kernel itself), except for FP8
-// when the grid is a single round of tiles (fewer than 2 per CU): there the
-// register-staged 8-wave kernel, whose two waves per SIMD overlap the
-// prologue and epilogue, measured faster. Smaller tiles use the
+// register-staged 8-wave kernel (two waves per SIMD overlap one another's
+// loads, prologue and epilogue), except for FP16 grids of several rounds of
+// tiles (at least 2 per CU), where the direct-load kernel (4 waves of
+// 128x128, 4-stage LDS ring) measured faster. Measured on two MI355X boxes,
+// same box per row (us): FP8 4096^3 78.4 vs 79.6, FP8 16384x12288x4096 774
+// vs 877, FP8 8192^3 481 vs 492; FP16 4096^3 144 vs 153; FP16 8192^3 1051
+// vs 1022 (register-staged vs direct-load). Smaller tiles use the
 // register-staged kernel with 4 waves.
 const GemmConfig* tile_with(int kind, int bm, int64_t tiles, int fa, int fb) {
     if (bm == 256) {
-        const bool direct = kind == KIND_F16 || tiles >= 2 * kNumCUs;
-        const char* want = direct ? (kind == KIND_FP8 ? "dma_fp8_256x256x64_s4" : "dma_f16_256x256x32_s4")
-                                  : "tile_fp8_256x256x128_w2x4";
+        const bool direct = kind == KIND_F16 && tiles >= 2 * kNumCUs;
+        const char* want = direct ? "dma_f16_256x256x32_s4"
+                                  : (kind == KIND_FP8 ? "tile_fp8_256x256x128_w2x4" : "tile_f16_256x256x64_w2x4");
         const GemmConfig* c = find_named(want, kind, 0, fa, fb);
         if (c) return c;
     }

@@ -264,12 +264,12 @@ def test_select_config_rules():
     assert sel(g.KIND_F16, g.OUT_F16, 16, 12288, 4096).startswith("stream_f16_m16_")
     assert sel(g.KIND_F16, g.OUT_F16, 5, 12288, 4096).startswith("stream_f16_m8_")
     assert sel(g.KIND_FP8, g.OUT_E4M3, 1, 4096, 4096).startswith("stream_fp8_m1_")
-    # 4096^2 fills the chip with 256x256 tiles (256 tiles): one round of FP8
-    # tiles runs on the 8-wave register-staged kernel, FP16 and larger grids
-    # on the direct-load kernel
+    # 4096^2 fills the chip with 256x256 tiles (256 tiles): FP8 always runs
+    # them on the 8-wave register-staged kernel, FP16 too for one round of
+    # tiles and on the direct-load kernel for larger grids
     assert sel(g.KIND_FP8, g.OUT_E4M3, 4096, 4096, 4096) == "tile_fp8_256x256x128_w2x4"
-    assert sel(g.KIND_F16, g.OUT_F16, 4096, 4096, 4096) == "dma_f16_256x256x32_s4"
-    assert sel(g.KIND_FP8, g.OUT_F16, 16384, 12288, 4096) == "dma_fp8_256x256x64_s4"
+    assert sel(g.KIND_F16, g.OUT_F16, 4096, 4096, 4096) == "tile_f16_256x256x64_w2x4"
+    assert sel(g.KIND_FP8, g.OUT_F16, 16384, 12288, 4096) == "tile_fp8_256x256x128_w2x4"
     assert sel(g.KIND_F16, g.OUT_F16, 8192, 8192, 8192) == "dma_f16_256x256x32_s4"
     # M = 3000 gives 192 tiles of 256 (not enough): one size down
     assert sel(g.KIND_FP8, g.OUT_E4M3, 3000, 4096, 4096).startswith("tile_fp8_128x128")
@@ -283,7 +283,7 @@ def test_select_config_override(monkeypatch):
     monkeypatch.setenv("LIBGEMM_CONFIG", "tile_fp8_128x128x128_w2x2")
     assert g.select_config(g.KIND_FP8, g.OUT_F32, 4096, 4096, 4096) == "tile_fp8_128x128x128_w2x2"
     # an override that cannot serve the request is ignored
-    assert g.select_config(g.KIND_F16, g.OUT_F32, 4096, 4096, 4096).startswith("dma_f16_256x256")
+    assert g.select_config(g.KIND_F16, g.OUT_F32, 4096, 4096, 4096) == "tile_f16_256x256x64_w2x4"
     monkeypatch.setenv("LIBGEMM_CONFIG", "stream_f16_m1_c64_t1024")
     assert g.select_config(g.KIND_F16, g.OUT_F16, 8, 100, 100).startswith("stream_f16_m8_")
 
