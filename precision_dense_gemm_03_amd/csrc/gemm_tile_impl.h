@@ -57,8 +57,14 @@ struct Tile {
     static constexpr int BNB = BN * ES;               // bytes of one B tile row
     static constexpr int SA = BKB + 16;               // padded LDS row strides
     static constexpr int SB = BNB + (ES == 2 ? 32 : 16);
+    // B rows come in groups of RB (the rows one 16-lane group of a transpose
+    // read spans: 32 for FP8, 8 for FP16) and each group starts 128 bytes
+    // further: without that, the row stride times RB is a multiple of the 64
+    // banks' 256 bytes and the lane groups that LDS serves together (groups
+    // g and g+1 start RB rows apart) read the same 32 banks.
+    static constexpr int RB = ES == 2 ? 8 : 32;
     static constexpr int A_BYTES = BM * SA;
-    static constexpr int B_BYTES = BK * SB;
+    static constexpr int B_BYTES = BK * SB + (BK / RB) * 128;
     static constexpr int STAGE = A_BYTES + B_BYTES;
     static constexpr int A_CPR = BKB / 16;            // 16-byte chunks per A row
     static constexpr int B_CPR = BNB / 16;
@@ -77,6 +83,7 @@ struct Tile {
     // LDS map: A stage 0, A stage 1, B stage 0, B stage 1
     static constexpr int a_stage(int s) { return s * A_BYTES; }
     static constexpr int b_stage(int s) { return 2 * A_BYTES + s * B_BYTES; }
+    static __device__ __forceinline__ int b_row(int r) { return r * SB + (r / RB) * 128; }
 };
 
 // MFMA operand type, LDS operand reads and the multiply for each element size.
@@ -206,7 +213,7 @@ __global__ __launch_bounds__(64 * WM * WN) void gemm_tile_kernel(
     const int b_row_in = (ES == 2) ? (j16 >> 2) : (j16 >> 1);
     const int b_col_in = (ES == 2) ? 4 * (j16 & 3) : 8 * (j16 & 1);
     const int a_lds = (wm * T::WTM + j16) * T::SA + g * T::OPB;          // + stage + tm*16*SA + ks*KPI*ES
-    const int b_lds = (8 * (ES == 2 ? 1 : 4) * g + b_row_in) * T::SB     // + stage + ks*KPI*SB + tn*16*ES
+    const int b_lds = T::b_row(8 * (ES == 2 ? 1 : 4) * g + b_row_in)    // + stage + b_row(ks*KPI) + tn*16*ES
                       + (wn * T::WTN + b_col_in) * ES;
 
     const int nk = (klen + BK - 1) / BK;
@@ -253,7 +260,7 @@ __global__ __launch_bounds__(64 * WM * WN) void gemm_tile_kernel(
         LDS_AS uint8_t* Bs = smem + T::b_stage(stage);
 #pragma unroll
         for (int i = 0; i < T::CB; ++i)
-            *(LDS_AS v4u*)(Bs + (b_row + i * T::B_RPP) * T::SB + b_col * 16) = rb[i];
+            *(LDS_AS v4u*)(Bs + T::b_row(b_row + i * T::B_RPP) + b_col * 16) = rb[i];
     };
     // Edge tiles, the K tail and unaligned operands: each 16-byte chunk is
     // loaded with per-element guards and written straight to LDS (no register
@@ -284,7 +291,7 @@ __global__ __launch_bounds__(64 * WM * WN) void gemm_tile_kernel(
                 v = *reinterpret_cast<const v4u*>(rp + gn * ES);
             else
                 v = load_chunk_guarded<ES>(rp, gk < kend, gn, N);
-            *(LDS_AS v4u*)(Bs + (b_row + i * T::B_RPP) * T::SB + b_col * 16) = v;
+            *(LDS_AS v4u*)(Bs + T::b_row(b_row + i * T::B_RPP) + b_col * 16) = v;
         }
     };
 
@@ -295,7 +302,7 @@ __global__ __launch_bounds__(64 * WM * WN) void gemm_tile_kernel(
         for (int ks = 0; ks < T::KS; ++ks)
 #pragma unroll
             for (int tn = 0; tn < T::TN; ++tn)
-                bop[ks][tn] = Operand<ES>::read_b(base + ks * T::KPI * T::SB + tn * 16 * ES, T::SB);
+                bop[ks][tn] = Operand<ES>::read_b(base + T::b_row(ks * T::KPI) + tn * 16 * ES, T::SB);
     };
     auto mma_tile = [&](int stage, const Op (&bop)[T::KS][T::TN]) __attribute__((always_inline)) {
         const LDS_AS uint8_t* base = smem + T::a_stage(stage) + a_lds;
