@@ -70,7 +70,7 @@ extern "C" {
  *              (GEMM_OUT_F16); written, never read
  *   out_dtype  GEMM_OUT_F32 or GEMM_OUT_F16 (anything else: GEMM_ERR_DTYPE)
  *   M, N, K    M = 0 or N = 0 is a no-op; K = 0 writes zeros (the empty sum)
- * M <= 16 runs an HBM-streaming kernel, larger M an MFMA tile kernel; the
+ * M <= 4 runs an HBM-streaming kernel, larger M an MFMA tile kernel; the
  * choice never changes which outputs are written.
  */
 int gemm_f16(const void* A, const void* B, void* C, int out_dtype,

@@ -263,6 +263,8 @@ const GemmConfig* stream_configs(int* count) {
     // takes the one with the smallest granularity (fewer threads, so a K
     // range of a few hundred rows still keeps every lane busy).
     static const GemmConfig table[] = {
+    {"stream_f16_m1_c64_t512", KIND_F16, 1, 1, 64, 512, launch_stream<2, 1, 64, 512, 8>, 0,
+     stream_kgran<2, 64, 512, 8>()},
     {"stream_f16_m1_c64_t1024", KIND_F16, 1, 1, 64, 1024, launch_stream<2, 1, 64, 1024, 8>, 0,
      stream_kgran<2, 64, 1024, 8>()},
     {"stream_f16_m4_c64_t512", KIND_F16, 1, 4, 64, 512, launch_stream<2, 4, 64, 512, 8>, 0,
@@ -277,6 +279,7 @@ const GemmConfig* stream_configs(int* count) {
      stream_kgran<1, 64, 512, 8>()},
     {"stream_f16_m1_c64_t256", KIND_F16, 1, 1, 64, 256, launch_stream<2, 1, 64, 256, 8>, 0,
      stream_kgran<2, 64, 256, 8>()},
+
     {"stream_fp8_m1_c128_t256", KIND_FP8, 1, 1, 128, 256, launch_stream_fp8_any<1, 128, 256, 8>, kAllFp8Pairs,
      stream_kgran<1, 128, 256, 8>()},
     {"stream_fp8_m4_c128_t256", KIND_FP8, 1, 4, 128, 256, launch_stream_fp8_any<4, 128, 256, 8>, kAllFp8Pairs,

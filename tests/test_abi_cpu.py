@@ -261,8 +261,9 @@ def test_select_config_rules():
     # decode shapes go to the streaming kernel sized for M
     assert sel(g.KIND_F16, g.OUT_F16, 1, 12288, 4096).startswith("stream_f16_m1_")
     assert sel(g.KIND_F16, g.OUT_F16, 4, 12288, 4096).startswith("stream_f16_m4_")
-    assert sel(g.KIND_F16, g.OUT_F16, 16, 12288, 4096).startswith("stream_f16_m16_")
-    assert sel(g.KIND_F16, g.OUT_F16, 5, 12288, 4096).startswith("stream_f16_m8_")
+    # from M = 5 the 64x64 MFMA tile reads the weight faster than streaming
+    assert sel(g.KIND_F16, g.OUT_F16, 16, 12288, 4096) == "tile_f16_64x64x64_w2x2"
+    assert sel(g.KIND_F16, g.OUT_F16, 5, 12288, 4096) == "tile_f16_64x64x64_w2x2"
     assert sel(g.KIND_FP8, g.OUT_E4M3, 1, 4096, 4096).startswith("stream_fp8_m1_")
     # 4096^2 fills the chip with 256x256 tiles (256 tiles): FP8 always runs
     # them on the 8-wave register-staged kernel, FP16 too for one round of
@@ -285,7 +286,9 @@ def test_select_config_override(monkeypatch):
     # an override that cannot serve the request is ignored
     assert g.select_config(g.KIND_F16, g.OUT_F32, 4096, 4096, 4096) == "tile_f16_256x256x64_w2x4"
     monkeypatch.setenv("LIBGEMM_CONFIG", "stream_f16_m1_c64_t1024")
-    assert g.select_config(g.KIND_F16, g.OUT_F16, 8, 100, 100).startswith("stream_f16_m8_")
+    assert g.select_config(g.KIND_F16, g.OUT_F16, 8, 100, 100) == "tile_f16_64x64x64_w2x2"
+    monkeypatch.setenv("LIBGEMM_CONFIG", "stream_f16_m8_c64_t256")      # still selectable by name
+    assert g.select_config(g.KIND_F16, g.OUT_F16, 8, 100, 100) == "stream_f16_m8_c64_t256"
 
 
 def test_select_config_validation():

@@ -137,3 +137,45 @@ def test_direct_load_kernel_offset_operands(kind, monkeypatch):
             C = torch.empty((M, N), dtype=torch.float32, device=DEV)
             g.gemm_f16(ta, tb, C)
             check_f32(host(C), R, S, what=f"f16 shift {shift}")
+
+
+# Every streaming (M <= 16) configuration, forced by name: the selector only
+# picks some of them by default (M <= 4), the rest stay selectable.
+STREAM_CONFIGS = [("stream_f16_m1_c64_t512", 1), ("stream_f16_m1_c64_t1024", 1), ("stream_f16_m1_c64_t256", 1),
+                  ("stream_f16_m4_c64_t512", 4), ("stream_f16_m8_c64_t256", 8), ("stream_f16_m16_c64_t256", 16),
+                  ("stream_fp8_m1_c64_t1024", 1), ("stream_fp8_m1_c128_t256", 1), ("stream_fp8_m4_c64_t512", 4),
+                  ("stream_fp8_m4_c128_t256", 4)]
+
+
+@pytest.mark.parametrize("cfg,bm", STREAM_CONFIGS)
+def test_stream_config_parity(cfg, bm, monkeypatch):
+    """Ragged N (not a multiple of the column block), a K tail, every M up to
+    the configuration's bound; F32 and F16 (FP8 also E4M3) outputs."""
+    monkeypatch.setenv("LIBGEMM_CONFIG", cfg)
+    fp8 = "_fp8_" in cfg
+    N, K = 1000, 1500
+    for M in sorted({1, (bm + 1) // 2, bm}):
+        kind = g.KIND_FP8 if fp8 else g.KIND_F16
+        assert g.select_config(kind, g.OUT_F32, M, N, K) == cfg
+        say(f"{cfg} {M}x{N}x{K}")
+        if fp8:
+            ca, cb = wl.random_e4m3_codes((M, K), 61 + M), wl.random_e4m3_codes((K, N), 62)
+            R, S = orc.gemm(orc.FMT_E4M3, ca, cb)
+            ta, tb, one = dev(ca), dev(cb), scalar(1.0)
+            C = torch.empty((M, N), dtype=torch.float32, device=DEV)
+            g.gemm_fp8_scaled(ta, tb, one, one, C)
+            check_f32(host(C), R, S, what=f"{cfg} f32 M={M}")
+            s_out = orc.scale_from_amax(np.float32(np.max(np.abs(R))))
+            C8 = torch.empty((M, N), dtype=torch.uint8, device=DEV)
+            g.gemm_fp8_scaled(ta, tb, one, one, C8, scalar(s_out))
+            check_e4m3(host(C8), R, S, 1.0, 1.0, s_out, what=f"{cfg} e4m3 M={M}")
+        else:
+            a16, b16 = wl.random_f16((M, K), 63 + M), wl.random_f16((K, N), 64)
+            R, S = orc.gemm(orc.FMT_F16, a16.view(np.uint16), b16.view(np.uint16))
+            ta, tb = dev(a16), dev(b16)
+            C = torch.empty((M, N), dtype=torch.float32, device=DEV)
+            g.gemm_f16(ta, tb, C)
+            check_f32(host(C), R, S, what=f"{cfg} f32 M={M}")
+            C16 = torch.empty((M, N), dtype=torch.float16, device=DEV)
+            g.gemm_f16(ta, tb, C16)
+            check_f16(host(C16), R, S, what=f"{cfg} f16 M={M}")
