@@ -27,9 +27,9 @@
 // the chosen configuration's grid has fewer than two workgroups per CU, so
 // too few loads are in flight to stream B at HBM speed, K is cut into 2, 4, 8, ...
 // ranges (multiples of the configuration's K granularity) until the grid
-// reaches that, or K runs out. Decode shapes switch to the streaming variant
-// with the smallest K granularity. LIBGEMM_SPLITS=<n> forces the number of
-// ranges (clamped to what K allows).
+// reaches that, or K runs out. Decode shapes are split over 64x64 tiles
+// (below). LIBGEMM_SPLITS=<n> forces the number of ranges (clamped to what K
+// allows).
 #include <cstdlib>
 #include <cstring>
 
@@ -121,13 +121,13 @@ SplitPlan plan_splitk(int kind, int out_dtype, int64_t M, int64_t N, int64_t K, 
     const GemmConfig* c = p.cfg;
     if (!c || M <= 0 || N <= 0 || K <= 0 || M > kSplitMaxM) return p;
     if (c->family == 1 && !std::getenv("LIBGEMM_CONFIG")) {
-        int ns = 0;
-        const GemmConfig* st = stream_configs(&ns);
-        for (int i = 0; i < ns; ++i) {
-            const GemmConfig& d = st[i];
-            if (d.kind == kind && d.bm == c->bm && serves_formats(d, fa, fb) && d.kgran > 0 && d.kgran < c->kgran)
-                c = &d;
-        }
+        // Decode shapes split over 64x64 MFMA tiles (two launches, measured
+        // against the streaming kernels' own split: FP8 N = K = 4096 M = 1
+        // 13.3 vs 13.7 us, M = 4 12.9 vs 16.9 us; FP16 [M,4096]x[4096,12288]
+        // M = 8 23.3 us vs 53.3 us plain), except the FP16 M = 1 decode,
+        // whose plain streaming kernel (21.5 us) beats every split tried.
+        if (kind == KIND_F16 && M == 1) return p;
+        if (const GemmConfig* t = tile_with(kind, 64, 0, fa, fb)) c = t;
     }
     if (c->kgran <= 0) return p;
     const int64_t base = c->family == 1 ? (N + c->bn - 1) / c->bn : ((M + c->bm - 1) / c->bm) * ((N + c->bn - 1) / c->bn);

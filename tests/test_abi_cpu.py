@@ -148,9 +148,12 @@ def test_channel_entry_points_argument_validation():
 
 def test_splitk_plan_rules():
     plan = g.splitk_plan
-    # decode: the 256-thread streaming variants, K cut until >= 512 workgroups
-    assert plan(g.KIND_FP8, g.OUT_E4M3, 1, 4096, 4096) == ("stream_fp8_m1_c128_t256", 16, 16 * 4096 * 4)
-    assert plan(g.KIND_F16, g.OUT_F16, 1, 12288, 4096) == ("stream_f16_m1_c64_t256", 4, 4 * 12288 * 4)
+    # decode shapes split over 64x64 tiles, K cut until >= 512 workgroups;
+    # the FP16 M = 1 decode keeps its plain streaming kernel
+    assert plan(g.KIND_FP8, g.OUT_E4M3, 1, 4096, 4096) == ("tile_fp8_64x64x128_w2x2", 8, 8 * 4096 * 4)
+    assert plan(g.KIND_FP8, g.OUT_E4M3, 4, 4096, 4096) == ("tile_fp8_64x64x128_w2x2", 8, 8 * 4 * 4096 * 4)
+    assert plan(g.KIND_F16, g.OUT_F16, 1, 12288, 4096) == ("stream_f16_m1_c64_t512", 1, 0)
+    assert plan(g.KIND_F16, g.OUT_F16, 4, 12288, 4096) == ("tile_f16_64x64x64_w2x2", 4, 4 * 4 * 12288 * 4)
     # mid-M: 64x64 tiles, 2 x 64 tiles -> 4 ranges of 1024
     assert plan(g.KIND_FP8, g.OUT_E4M3, 65, 4096, 4096) == ("tile_fp8_64x64x128_w2x2", 4, 4 * 65 * 4096 * 4)
     assert plan(g.KIND_FP8, g.OUT_F32, 16, 4096, 4096)[1] == 8
@@ -192,9 +195,9 @@ def test_splitk_argument_validation():
     assert L.gemm_fp8_splitk(*args, FAKE + 65 * 4096 - 16, need, None) == -8   # covers the end of A
     assert L.gemm_fp8_splitk(FAKE, 0, FAKE2, 0, s, s + 4, None, FAKE3, 2, 65, 4096, 4096, W, need, None) == -4
     assert L.gemm_fp8_splitk(FAKE, 0, FAKE2, 7, s, s + 4, None, FAKE3, 0, 65, 4096, 4096, W, need, None) == -3
-    assert L.gemm_f16_splitk(FAKE, FAKE2, FAKE3, 1, 1, 12288, 4096, W, 4 * 12288 * 4 - 4, None) == -9
+    assert L.gemm_f16_splitk(FAKE, FAKE2, FAKE3, 1, 4, 12288, 4096, W, 4 * 4 * 12288 * 4 - 4, None) == -9
     assert L.gemm_f16_splitk(FAKE, FAKE2, FAKE3, 2, 1, 12288, 4096, W, 1 << 30, None) == -3
-    assert L.gemm_f16_splitk(FAKE, FAKE2, FAKE3, 1, 1, 12288, 4096, FAKE2 + 64, 1 << 30, None) == -8   # inside B
+    assert L.gemm_f16_splitk(FAKE, FAKE2, FAKE3, 1, 4, 12288, 4096, FAKE2 + 64, 1 << 30, None) == -8   # inside B
     assert L.gemm_splitk_plan(5, 0, 1, 1, 1, 0, 0, None, 0, None, None) == -3
     assert L.gemm_splitk_plan(1, 0, 1, -1, 1, 0, 0, None, 0, None, None) == -2
     assert L.gemm_splitk_plan(1, 0, 1, 1, 1, 0, 0, None, 0, None, None) == 0   # every output may be NULL

@@ -125,7 +125,7 @@ def test_f16_splitk_decode(M):
     N, K = 12288, 4096
     name, splits, ws = workspace_for(g.KIND_F16, g.OUT_F16, M, N, K)
     say(f"f16 split-K decode M={M}: {name} splits={splits}")
-    assert splits > 1
+    assert (splits == 1) if M == 1 else (splits > 1)   # M = 1 keeps the plain streaming kernel
     a16 = wl.random_normal_f32((M, K), 31).astype(np.float16)
     b16 = (wl.random_normal_f32((K, N), 32) * np.float32(0.02)).astype(np.float16)
     R, S = orc.gemm(orc.FMT_F16, a16.view(np.uint16), b16.view(np.uint16))
