@@ -6,11 +6,16 @@ already resident in HBM:
                    E4M3 GEMM with FP8 output and its own output scale
   FP16 4096^3:     FP16 GEMM, FP16 output
   FP16 decode:     [1,4096] x [4096,12288], FP16 output (HBM-bound kernel)
+With --b-layout kmajor (the default) B is held K-major, as Bt[N,K] (the layout
+a linear layer keeps its weight in): the FP8 job quantizes B straight into that
+layout and the GEMMs take it; with rowmajor every B is B[K,N]. The results are
+the same either way.
 value = all GEMM flops of a step / step time (TFLOPS). The same run also times
-each row on its own (TFLOPS and % of MFMA peak for the two 4096^3 GEMMs; HBM
-GB/s at M = 1 with the weights rotated over 6 copies, 604 MB, so the 256 MB
-Infinity Cache cannot serve them), the dominant kernel's roofline figure, and
-the oracle on a bounded sample of the same step on the host cores.
+each row on its own, for both layouts (TFLOPS and % of MFMA peak for the two
+4096^3 GEMMs; HBM GB/s at M = 1 with the weights rotated over 6 copies, 604 MB,
+so the 256 MB Infinity Cache cannot serve them), the dominant kernel's
+roofline figure, and the oracle on a bounded sample of the same step on the
+host cores.
 
 Prints ONE JSON line. Usage: python bench.py [--gpus 1] [--steps K] [--warmup W]
 """
@@ -41,6 +46,9 @@ def parse():
     p.add_argument("--no-cpu-baseline", action="store_true")
     p.add_argument("--cpu-seconds", type=float, default=15.0, help="target oracle sample time")
     p.add_argument("--rows-reps", type=int, default=200, help="launches per single-row timing")
+    p.add_argument("--b-layout", choices=("kmajor", "rowmajor"), default="kmajor",
+                   help="layout of B in the timed step: kmajor (Bt[N,K], a linear layer's weight layout; the FP8 "
+                        "job quantizes B straight into it) or rowmajor (B[K,N])")
     p.add_argument("--calib-copy", action="store_true",
                    help="run one 256 MiB device-to-device copy first (a known-size kernel that calibrates "
                         "HBM byte counters in a profiler run)")
@@ -170,6 +178,11 @@ def main():
     for _ in range(5):
         db_copies.append(db_copies[0].clone())
     cd = torch.empty((wd.M, wd.N), dtype=torch.float16, device=dev)
+    # K-major copies of the B operands (Bt[N,K]); the FP8 job writes its own
+    # K-major codes with the transposed quantize
+    qbt = torch.empty((w8.N, w8.K), dtype=torch.uint8, device=dev)
+    hbt = hb.t().contiguous()
+    dbt_copies = [b.t().contiguous() for b in db_copies]
 
     # output scale of the FP8 job: amax of the FP32-output product / 448 (computed once, on the GPU)
     g.amax_f32(xa, amax_a, s_a)
@@ -183,8 +196,9 @@ def main():
     torch.cuda.synchronize()
 
     rot = [0]
+    kmajor = args.b_layout == "kmajor"
 
-    def fp8_job(ev=None):
+    def fp8_job_rm(ev=None):
         g.amax_f32(xa, amax_a, s_a)
         g.amax_f32(xb, amax_b, s_b)
         g.quantize_fp8(xa, s_a, qa)
@@ -195,12 +209,33 @@ def main():
         if ev is not None:
             ev[1].record()
 
-    def f16_gemm():
+    def fp8_job_km(ev=None):
+        g.amax_f32(xa, amax_a, s_a)
+        g.amax_f32(xb, amax_b, s_b)
+        g.quantize_fp8(xa, s_a, qa)
+        g.quantize_fp8_transposed(xb, s_b, qbt)
+        if ev is not None:
+            ev[0].record()
+        g.gemm_fp8_scaled_bt(qa, qbt, s_a, s_b, c8, s_out)
+        if ev is not None:
+            ev[1].record()
+
+    def f16_gemm_rm():
         g.gemm_f16(ha, hb, c16)
 
-    def decode():
+    def f16_gemm_km():
+        g.gemm_f16_bt(ha, hbt, c16)
+
+    def decode_rm():
         g.gemm_f16(da, db_copies[rot[0] % len(db_copies)], cd)
         rot[0] += 1
+
+    def decode_km():
+        g.gemm_f16_bt(da, dbt_copies[rot[0] % len(dbt_copies)], cd)
+        rot[0] += 1
+
+    fp8_job, f16_gemm, decode = (fp8_job_km, f16_gemm_km, decode_km) if kmajor else (fp8_job_rm, f16_gemm_rm,
+                                                                                     decode_rm)
 
     def step(ev=None):
         fp8_job(ev)
@@ -232,32 +267,48 @@ def main():
     # Each row on its own (HIP events on the launch stream).
     log("timing rows")
     reps = args.rows_reps
-    ms_gemm8 = time_launches(torch, lambda: g.gemm_fp8_scaled(qa, qb, s_a, s_b, c8, s_out), reps)
-    ms_job8 = time_launches(torch, fp8_job, max(20, reps // 4))
-    ms_amax = time_launches(torch, lambda: g.amax_f32(xa, amax_a, s_a), reps)
-    ms_quant = time_launches(torch, lambda: g.quantize_fp8(xa, s_a, qa), reps)
-    ms_gemm16 = time_launches(torch, f16_gemm, reps)
-    ms_dec = time_launches(torch, decode, reps * 2)
     dec_bytes = 2.0 * (wd.M * wd.K + wd.K * wd.N + wd.M * wd.N)
     n_x = xa.numel()
-    rows = {
-        "fp8_gemm_4096": {"tflops": flops8 / ms_gemm8 / 1e9, "pct_peak": 100 * flops8 / ms_gemm8 / 1e9 / PEAK_FP8_TFLOPS,
-                          "us": ms_gemm8 * 1e3, "config": g.select_config(g.KIND_FP8, g.OUT_E4M3, w8.M, w8.N, w8.K)},
-        "fp8_job_4096": {"tflops": flops8 / ms_job8 / 1e9, "us": ms_job8 * 1e3,
-                         "what": "amax x2 + quantize x2 + FP8 GEMM (E4M3 out)"},
-        "amax_64MiB": {"gbs": 4.0 * n_x / ms_amax / 1e6, "us": ms_amax * 1e3},
-        "quantize_64MiB": {"gbs": 5.0 * n_x / ms_quant / 1e6, "us": ms_quant * 1e3},
-        "f16_gemm_4096": {"tflops": flops16 / ms_gemm16 / 1e9,
-                          "pct_peak": 100 * flops16 / ms_gemm16 / 1e9 / PEAK_F16_TFLOPS, "us": ms_gemm16 * 1e3,
-                          "config": g.select_config(g.KIND_F16, g.OUT_F16, w16.M, w16.N, w16.K)},
-        "decode_m1": {"gbs": dec_bytes / ms_dec / 1e6, "pct_hbm": 100 * dec_bytes / ms_dec / 1e6 / PEAK_HBM_GBS,
-                      "us": ms_dec * 1e3, "cold": "B rotated over 6 copies (604 MB)",
-                      "config": g.select_config(g.KIND_F16, g.OUT_F16, wd.M, wd.N, wd.K)},
-    }
-    rows["fp8_gemm_4096"]["us_in_step"] = ms_gemm8_step * 1e3
+    rows = {}
+    for lay, sfx in (("kmajor", "_bt"), ("rowmajor", "")):
+        km = lay == "kmajor"
+        if km:
+            gemm8 = lambda: g.gemm_fp8_scaled_bt(qa, qbt, s_a, s_b, c8, s_out)  # noqa: E731
+            sel8 = g.select_config_bt(g.KIND_FP8, g.OUT_E4M3, w8.M, w8.N, w8.K)
+            sel16 = g.select_config_bt(g.KIND_F16, g.OUT_F16, w16.M, w16.N, w16.K)
+            seld = g.select_config_bt(g.KIND_F16, g.OUT_F16, wd.M, wd.N, wd.K)
+        else:
+            gemm8 = lambda: g.gemm_fp8_scaled(qa, qb, s_a, s_b, c8, s_out)  # noqa: E731
+            sel8 = g.select_config(g.KIND_FP8, g.OUT_E4M3, w8.M, w8.N, w8.K)
+            sel16 = g.select_config(g.KIND_F16, g.OUT_F16, w16.M, w16.N, w16.K)
+            seld = g.select_config(g.KIND_F16, g.OUT_F16, wd.M, wd.N, wd.K)
+        ms_gemm8 = time_launches(torch, gemm8, reps)
+        ms_job8 = time_launches(torch, fp8_job_km if km else fp8_job_rm, max(20, reps // 4))
+        ms_gemm16 = time_launches(torch, f16_gemm_km if km else f16_gemm_rm, reps)
+        ms_dec = time_launches(torch, decode_km if km else decode_rm, reps * 2)
+        rows["fp8_gemm_4096" + sfx] = {
+            "tflops": flops8 / ms_gemm8 / 1e9, "pct_peak": 100 * flops8 / ms_gemm8 / 1e9 / PEAK_FP8_TFLOPS,
+            "us": ms_gemm8 * 1e3, "config": sel8, "b_layout": lay}
+        rows["fp8_job_4096" + sfx] = {
+            "tflops": flops8 / ms_job8 / 1e9, "us": ms_job8 * 1e3,
+            "what": "amax x2 + quantize x2 " + ("(B transposed into Bt[N,K]) " if km else "") + "+ FP8 GEMM (E4M3 out)"}
+        rows["f16_gemm_4096" + sfx] = {
+            "tflops": flops16 / ms_gemm16 / 1e9, "pct_peak": 100 * flops16 / ms_gemm16 / 1e9 / PEAK_F16_TFLOPS,
+            "us": ms_gemm16 * 1e3, "config": sel16, "b_layout": lay}
+        rows["decode_m1" + sfx] = {
+            "gbs": dec_bytes / ms_dec / 1e6, "pct_hbm": 100 * dec_bytes / ms_dec / 1e6 / PEAK_HBM_GBS,
+            "us": ms_dec * 1e3, "cold": "B rotated over 6 copies (604 MB)", "config": seld, "b_layout": lay}
+    ms_amax = time_launches(torch, lambda: g.amax_f32(xa, amax_a, s_a), reps)
+    ms_quant = time_launches(torch, lambda: g.quantize_fp8(xa, s_a, qa), reps)
+    ms_quant_t = time_launches(torch, lambda: g.quantize_fp8_transposed(xb, s_b, qbt), reps)
+    rows["amax_64MiB"] = {"gbs": 4.0 * n_x / ms_amax / 1e6, "us": ms_amax * 1e3}
+    rows["quantize_64MiB"] = {"gbs": 5.0 * n_x / ms_quant / 1e6, "us": ms_quant * 1e3}
+    rows["quantize_transposed_64MiB"] = {"gbs": 5.0 * n_x / ms_quant_t / 1e6, "us": ms_quant_t * 1e3}
+    key8 = "fp8_gemm_4096" + ("_bt" if kmajor else "")
+    rows[key8]["us_in_step"] = ms_gemm8_step * 1e3
     achieved = flops8 / ms_gemm8_step / 1e9
-    rec = traffic_record(rows["fp8_gemm_4096"]["config"])
-    roofline = {"bound": "mfma", "kernel": "FP8 GEMM 4096^3 (" + rows["fp8_gemm_4096"]["config"] + ")",
+    rec = traffic_record(rows[key8]["config"])
+    roofline = {"bound": "mfma", "kernel": "FP8 GEMM 4096^3 (" + rows[key8]["config"] + ")",
                 "kernel_us": ms_gemm8_step * 1e3,
                 "achieved": achieved, "peak": PEAK_FP8_TFLOPS, "unit": "TFLOP/s", "frac": achieved / PEAK_FP8_TFLOPS,
                 "traffic": None if rec is None else rec["hbm_bytes"],
@@ -275,7 +326,7 @@ def main():
         "scaling": "weak", "vs_baseline": None, "dtype": "fp8_e4m3+f16 (f32 accumulate)", "data": "synthetic",
         "config": {"workload": "fp8 e4m3 job 4096^3 (amax, quantize, GEMM, fp8 out) + fp16 GEMM 4096^3 + "
                                "fp16 decode 1x4096x12288", "M": 4096, "N": 4096, "K": 4096,
-                   "decode": [1, 4096, 12288]},
+                   "decode": [1, 4096, 12288], "b_layout": args.b_layout},
         "rows": rows, "roofline": roofline, "cpu_baseline": cpu,
     }
     print(json.dumps(out), flush=True)

@@ -324,6 +324,54 @@ int gemm_select_config(int kind, int out_dtype, int64_t M, int64_t N, int64_t K,
 int gemm_select_config_fmt(int kind, int out_dtype, int64_t M, int64_t N, int64_t K,
                            int fmt_a, int fmt_b, char* buf, int buflen);
 
+/* ------------------------------------------------ K-major B (weight layout) */
+/* P1 §3.2 ("Data Layout"): the weight matrix B need not be kept row-major;
+ * it may be stored in a layout chosen for the kernel. The calls below take B
+ * K-major, as Bt[N,K] row-major (element (k, n) of B at Bt[n*K + k]), which is
+ * how a linear layer keeps its weight. Every B row is then a contiguous K
+ * vector: the MFMA tile kernels stage B exactly like A (no LDS transpose
+ * reads), and decode shapes (M <= 8) read each weight row once as a dot
+ * product (P1 §2.1, §4.1: the [1,4096]x[4096,12288] projection reads each
+ * weight once). The results are those of gemm_f16 / gemm_fp8_scaled on
+ * B = transpose(Bt). */
+
+/*
+ * gemm_f16_bt — gemm_f16 with B given as Bt[N,K]:
+ *   A          device, _Float16[M*K], row-major
+ *   Bt         device, _Float16[N*K], row-major (B transposed)
+ *   C, out_dtype, M, N, K, stream, errors: as gemm_f16.
+ * M <= 8 runs the K-major decode kernel, larger M the MFMA tile kernel.
+ */
+int gemm_f16_bt(const void* A, const void* Bt, void* C, int out_dtype,
+                int64_t M, int64_t N, int64_t K, hipStream_t stream);
+
+/*
+ * gemm_fp8_scaled_bt — gemm_fp8_scaled (E4M3 operands, per-tensor scales,
+ * outputs F32, F16, E4M3 or E5M2) with B given as Bt[N,K] E4M3 codes,
+ * row-major. Arguments, element value and errors as gemm_fp8_scaled.
+ */
+int gemm_fp8_scaled_bt(const uint8_t* A, const uint8_t* Bt, const float* sA, const float* sB,
+                       const float* sOut, void* C, int out_dtype,
+                       int64_t M, int64_t N, int64_t K, hipStream_t stream);
+
+/*
+ * quantize_fp8_transposed — quantize_fp8 of a row-major x[rows, cols] written
+ * transposed: q[c*rows + r] = E4M3(fl32(x[r*cols + c] / scale)) (same
+ * rounding, saturation and NaN rules as quantize_fp8, P2 §4.3). Quantizing a
+ * row-major FP32 B[K,N] this way gives the Bt[N,K] codes gemm_fp8_scaled_bt
+ * takes, in the same pass over B.
+ *   x      device, float[rows*cols], row-major
+ *   rows, cols  sizes (either 0: no-op; each at most 2^31 - 1)
+ *   scale  device pointer to one float
+ *   q      device, uint8[cols*rows], written; must not overlap x or scale
+ */
+int quantize_fp8_transposed(const float* x, int64_t rows, int64_t cols, const float* scale,
+                            uint8_t* q, hipStream_t stream);
+
+/* gemm_select_config for gemm_f16_bt (kind 0) and gemm_fp8_scaled_bt (kind 1). */
+int gemm_select_config_bt(int kind, int out_dtype, int64_t M, int64_t N, int64_t K,
+                          char* buf, int buflen);
+
 #ifdef __cplusplus
 }
 #endif

@@ -23,6 +23,11 @@ Functions keep the C names:
     guarded_workspace_size(M, N, K) -> int
     select_config(kind, out_dtype, M, N, K) -> str   (host-only query)
     select_config_fmt(kind, out_dtype, M, N, K, fmt_a, fmt_b) -> str
+  K-major B (Bt[N,K], the layout of a linear layer's weight):
+    gemm_f16_bt(A, Bt, C, stream=None)
+    gemm_fp8_scaled_bt(A, Bt, sA, sB, C, sOut=None, stream=None, out_fmt=None)
+    quantize_fp8_transposed(x, scale, q=None, stream=None) -> q[cols, rows]
+    select_config_bt(kind, out_dtype, M, N, K) -> str
 The output dtype of a GEMM is taken from C: float32, float16, or 8-bit codes
 (uint8 or torch.float8_e4m3fn: E4M3; torch.float8_e5m2, or uint8 with
 out_fmt=FMT_E5M2: E5M2). FP8 operands are uint8 codes or torch float8 tensors.
@@ -107,6 +112,14 @@ def lib() -> ctypes.CDLL:
     L.gemm_f16_guarded_workspace_size.argtypes = [i64, i64, i64]
     L.gemm_select_config_fmt.restype = i32
     L.gemm_select_config_fmt.argtypes = [i32, i32, i64, i64, i64, i32, i32, ctypes.c_char_p, i32]
+    L.gemm_f16_bt.restype = i32
+    L.gemm_f16_bt.argtypes = [vp, vp, vp, i32, i64, i64, i64, vp]
+    L.gemm_fp8_scaled_bt.restype = i32
+    L.gemm_fp8_scaled_bt.argtypes = [vp, vp, vp, vp, vp, vp, i32, i64, i64, i64, vp]
+    L.quantize_fp8_transposed.restype = i32
+    L.quantize_fp8_transposed.argtypes = [vp, i64, i64, vp, vp, vp]
+    L.gemm_select_config_bt.restype = i32
+    L.gemm_select_config_bt.argtypes = [i32, i32, i64, i64, i64, ctypes.c_char_p, i32]
     _lib = L
     return L
 
@@ -166,6 +179,27 @@ def _dims(A, B, C):
     return M, N, K
 
 
+def _dims_bt(A, Bt, C):
+    if A.dim() != 2 or Bt.dim() != 2 or C.dim() != 2:
+        raise ValueError("A, Bt and C must be 2-D")
+    M, K = A.shape
+    N, K2 = Bt.shape
+    if K2 != K or tuple(C.shape) != (M, N):
+        raise ValueError(f"shape mismatch: A{tuple(A.shape)} Bt{tuple(Bt.shape)} C{tuple(C.shape)}")
+    return M, N, K
+
+
+def gemm_f16_bt(A, Bt, C, stream=None):
+    """C = A @ Bt.T for float16 A[M,K] and a K-major weight Bt[N,K]; C float32 or float16 [M,N]."""
+    torch = _torch()
+    if A.dtype != torch.float16 or Bt.dtype != torch.float16:
+        raise ValueError("gemm_f16_bt takes float16 operands")
+    M, N, K = _dims_bt(A, Bt, C)
+    _check(lib().gemm_f16_bt(_ptr(A), _ptr(Bt), _ptr(C), _out_dtype(C), M, N, K, _stream_handle(stream)),
+           "gemm_f16_bt")
+    return C
+
+
 def gemm_f16(A, B, C, stream=None):
     """C = A @ B for float16 A[M,K], B[K,N]; C float32 or float16 [M,N]."""
     torch = _torch()
@@ -195,6 +229,35 @@ def gemm_fp8_scaled(A, B, sA, sB, C, sOut=None, stream=None, out_fmt=None):
     _check(lib().gemm_fp8_scaled(_ptr(A), _ptr(B), _ptr(sA), _ptr(sB), _ptr(sOut), _ptr(Cv), out, M, N, K,
                                  _stream_handle(stream)), "gemm_fp8_scaled")
     return C
+
+
+def gemm_fp8_scaled_bt(A, Bt, sA, sB, C, sOut=None, stream=None, out_fmt=None):
+    """gemm_fp8_scaled with B given K-major: C = (sA*A) @ (sB*Bt).T for E4M3
+    A[M,K] and Bt[N,K]."""
+    A, Bt = _u8(A), _u8(Bt)
+    out = _out_dtype(C, out_fmt)
+    Cv = _u8(C) if out in (OUT_E4M3, OUT_E5M2) else C
+    M, N, K = _dims_bt(A, Bt, Cv)
+    _check(lib().gemm_fp8_scaled_bt(_ptr(A), _ptr(Bt), _ptr(sA), _ptr(sB), _ptr(sOut), _ptr(Cv), out, M, N, K,
+                                    _stream_handle(stream)), "gemm_fp8_scaled_bt")
+    return C
+
+
+def quantize_fp8_transposed(x, scale, q=None, stream=None):
+    """E4M3 codes of x / scale for a 2-D float32 x[rows, cols], written
+    transposed: q[cols, rows] (uint8)."""
+    torch = _torch()
+    if x.dtype != torch.float32:
+        raise ValueError("quantize_fp8_transposed takes float32 input")
+    rows, cols = _rows_cols(x)
+    if q is None:
+        q = torch.empty((cols, rows), dtype=torch.uint8, device=x.device)
+    qv = _u8(q)
+    if qv.numel() != x.numel():
+        raise ValueError("q must have as many elements as x")
+    _check(lib().quantize_fp8_transposed(_ptr(x), rows, cols, _ptr(scale), _ptr(qv), _stream_handle(stream)),
+           "quantize_fp8_transposed")
+    return q
 
 
 def gemm_fp8_fmt(A, fmt_a, B, fmt_b, sA, sB, C, sOut=None, stream=None, out_fmt=None):
@@ -411,4 +474,11 @@ def select_config_fmt(kind: int, out_dtype: int, M: int, N: int, K: int, fmt_a: 
     buf = ctypes.create_string_buffer(128)
     _check(lib().gemm_select_config_fmt(kind, out_dtype, M, N, K, int(fmt_a), int(fmt_b), buf, len(buf)),
            "gemm_select_config_fmt")
+    return buf.value.decode()
+
+
+def select_config_bt(kind: int, out_dtype: int, M: int, N: int, K: int) -> str:
+    """The configuration gemm_f16_bt (kind 0) or gemm_fp8_scaled_bt (kind 1) would launch."""
+    buf = ctypes.create_string_buffer(128)
+    _check(lib().gemm_select_config_bt(kind, out_dtype, M, N, K, buf, len(buf)), "gemm_select_config_bt")
     return buf.value.decode()

@@ -66,7 +66,7 @@ int run_gemm(int kind, const GemmArgs& a) {
     if (st != GEMM_OK) return st;
     if (a.M == 0 || a.N == 0) return GEMM_OK;
     if (a.K == 0) return status_of(launch_fill_zero(a.C, a.M * a.N, a.out_dtype, a.stream));
-    const GemmConfig* cfg = select_config(kind, a.out_dtype, a.M, a.N, a.K, a.fmt_a, a.fmt_b);
+    const GemmConfig* cfg = select_config(kind, a.out_dtype, a.M, a.N, a.K, a.fmt_a, a.fmt_b, a.b_kmajor);
     if (!cfg) return GEMM_ERR_UNSUPPORTED;
     return status_of(cfg->launch(a));
 }
@@ -102,8 +102,9 @@ int run_gemm_splitk(int kind, GemmArgs a, void* ws, int64_t ws_bytes, const void
 
 extern "C" {
 
-int gemm_f16(const void* A, const void* B, void* C, int out_dtype, int64_t M, int64_t N, int64_t K,
-             hipStream_t stream) {
+// gemm_f16 and gemm_f16_bt: b_kmajor = 1 when B is given as Bt[N,K].
+static int gemm_f16_common(const void* A, const void* B, void* C, int out_dtype, int64_t M, int64_t N, int64_t K,
+                           hipStream_t stream, int b_kmajor) {
     if (out_dtype != GEMM_OUT_F32 && out_dtype != GEMM_OUT_F16) return GEMM_ERR_DTYPE;
     if (!dim_ok(M) || !dim_ok(N) || !dim_ok(K)) return GEMM_ERR_DIM;
     if (M > 0 && N > 0) {
@@ -113,7 +114,18 @@ int gemm_f16(const void* A, const void* B, void* C, int out_dtype, int64_t M, in
         if (K > 0 && (overlaps(C, cbytes, A, M * K * 2) || overlaps(C, cbytes, B, K * N * 2))) return GEMM_ERR_ALIAS;
     }
     GemmArgs a{A, B, C, nullptr, nullptr, nullptr, out_dtype, M, N, K, stream};
+    a.b_kmajor = b_kmajor;
     return run_gemm(KIND_F16, a);
+}
+
+int gemm_f16(const void* A, const void* B, void* C, int out_dtype, int64_t M, int64_t N, int64_t K,
+             hipStream_t stream) {
+    return gemm_f16_common(A, B, C, out_dtype, M, N, K, stream, 0);
+}
+
+int gemm_f16_bt(const void* A, const void* Bt, void* C, int out_dtype, int64_t M, int64_t N, int64_t K,
+                hipStream_t stream) {
+    return gemm_f16_common(A, Bt, C, out_dtype, M, N, K, stream, 1);
 }
 
 // Shared by gemm_fp8_scaled, gemm_fp8_fmt, gemm_fp8_channel and
@@ -122,7 +134,7 @@ int gemm_f16(const void* A, const void* B, void* C, int out_dtype, int64_t M, in
 static int gemm_fp8_common(const uint8_t* A, int fmt_a, const uint8_t* B, int fmt_b, const float* sA,
                            const float* sB, const float* sOut, void* C, int out_dtype, int64_t M, int64_t N,
                            int64_t K, hipStream_t stream, int channel = 0, void* ws = nullptr,
-                           int64_t ws_bytes = 0) {
+                           int64_t ws_bytes = 0, int b_kmajor = 0) {
     if (out_dtype < GEMM_OUT_F32 || out_dtype > GEMM_OUT_E5M2) return GEMM_ERR_DTYPE;
     if ((fmt_a != GEMM_FMT_E4M3 && fmt_a != GEMM_FMT_E5M2) || (fmt_b != GEMM_FMT_E4M3 && fmt_b != GEMM_FMT_E5M2))
         return GEMM_ERR_DTYPE;
@@ -140,6 +152,7 @@ static int gemm_fp8_common(const uint8_t* A, int fmt_a, const uint8_t* B, int fm
     }
     GemmArgs a{A, B, C, sA, sB, fp8_out(out_dtype) ? sOut : nullptr, out_dtype, M, N, K, stream, fmt_a, fmt_b,
                channel};
+    a.b_kmajor = b_kmajor;
     if (!ws) return run_gemm(KIND_FP8, a);
     const void* in_ptr[6] = {A, B, C, sA, sB, fp8_out(out_dtype) ? sOut : nullptr};
     const int64_t in_bytes[6] = {M * K, K * N, M * N * out_size(out_dtype), channel ? 4 * M : 4, channel ? 4 * N : 4,
@@ -150,6 +163,12 @@ static int gemm_fp8_common(const uint8_t* A, int fmt_a, const uint8_t* B, int fm
 int gemm_fp8_scaled(const uint8_t* A, const uint8_t* B, const float* sA, const float* sB, const float* sOut,
                     void* C, int out_dtype, int64_t M, int64_t N, int64_t K, hipStream_t stream) {
     return gemm_fp8_common(A, GEMM_FMT_E4M3, B, GEMM_FMT_E4M3, sA, sB, sOut, C, out_dtype, M, N, K, stream);
+}
+
+int gemm_fp8_scaled_bt(const uint8_t* A, const uint8_t* Bt, const float* sA, const float* sB, const float* sOut,
+                       void* C, int out_dtype, int64_t M, int64_t N, int64_t K, hipStream_t stream) {
+    return gemm_fp8_common(A, GEMM_FMT_E4M3, Bt, GEMM_FMT_E4M3, sA, sB, sOut, C, out_dtype, M, N, K, stream, 0,
+                           nullptr, 0, 1);
 }
 
 int gemm_fp8_fmt(const uint8_t* A, int fmt_a, const uint8_t* B, int fmt_b, const float* sA, const float* sB,
@@ -296,6 +315,18 @@ int quantize_fp8_fmt(const float* x, int64_t n, const float* scale, uint8_t* q, 
     return status_of(launch_quantize(x, n, scale, q, fmt, stream));
 }
 
+int quantize_fp8_transposed(const float* x, int64_t rows, int64_t cols, const float* scale, uint8_t* q,
+                            hipStream_t stream) {
+    if (!dim_ok(rows) || !dim_ok(cols)) return GEMM_ERR_DIM;
+    const int64_t n = rows * cols;
+    if (n == 0) return GEMM_OK;
+    if (!x || !scale || !q) return GEMM_ERR_NULL;
+    if (overlaps(q, n, x, 4 * n) || overlaps(q, n, scale, 4)) return GEMM_ERR_ALIAS;
+    const int st = check_device();
+    if (st != GEMM_OK) return st;
+    return status_of(launch_quantize_transposed(x, rows, cols, scale, q, GEMM_FMT_E4M3, stream));
+}
+
 int quantize_fp8(const float* x, int64_t n, const float* scale, uint8_t* q, hipStream_t stream) {
     return quantize_fp8_fmt(x, n, scale, q, GEMM_FMT_E4M3, stream);
 }
@@ -342,6 +373,18 @@ int gemm_select_config_fmt(int kind, int out_dtype, int64_t M, int64_t N, int64_
     if (!dim_ok(M) || !dim_ok(N) || !dim_ok(K)) return GEMM_ERR_DIM;
     if (!buf || buflen <= 0) return GEMM_ERR_NULL;
     const GemmConfig* cfg = select_config(kind, out_dtype, M, N, K, fmt_a, fmt_b);
+    if (!cfg) return GEMM_ERR_UNSUPPORTED;
+    std::snprintf(buf, (size_t)buflen, "%s", cfg->name);
+    return GEMM_OK;
+}
+
+int gemm_select_config_bt(int kind, int out_dtype, int64_t M, int64_t N, int64_t K, char* buf, int buflen) {
+    if (kind != KIND_F16 && kind != KIND_FP8) return GEMM_ERR_DTYPE;
+    if (out_dtype < GEMM_OUT_F32 || out_dtype > GEMM_OUT_E5M2 || (kind == KIND_F16 && fp8_out(out_dtype)))
+        return GEMM_ERR_DTYPE;
+    if (!dim_ok(M) || !dim_ok(N) || !dim_ok(K)) return GEMM_ERR_DIM;
+    if (!buf || buflen <= 0) return GEMM_ERR_NULL;
+    const GemmConfig* cfg = select_config(kind, out_dtype, M, N, K, GEMM_FMT_E4M3, GEMM_FMT_E4M3, 1);
     if (!cfg) return GEMM_ERR_UNSUPPORTED;
     std::snprintf(buf, (size_t)buflen, "%s", cfg->name);
     return GEMM_OK;

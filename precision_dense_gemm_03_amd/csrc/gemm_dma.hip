@@ -17,6 +17,9 @@ const GemmConfig* dma_configs(int* count) {
         {"dma_f16_256x256x32_s4", KIND_F16, 2, 256, 256, 32, dma::launch_dma<2, 4, 0, 0>},
         {"dma_fp8_256x256x64_s5", KIND_FP8, 2, 256, 256, 64, dma::launch_dma<1, 5, 0, 0>},
         {"dma_f16_256x256x32_s5", KIND_F16, 2, 256, 256, 32, dma::launch_dma<2, 5, 0, 0>},
+        // K-major B (Bt[N,K]), E4M3 x E4M3 and FP16
+        {"dma_fp8_256x256x64_s4_bt", KIND_FP8, 2, 256, 256, 64, dma::launch_dma<1, 4, 0, 0, true>, 0, 0, 1},
+        {"dma_f16_256x256x32_s4_bt", KIND_F16, 2, 256, 256, 32, dma::launch_dma<2, 4, 0, 0, true>, 0, 0, 1},
     };
     *count = (int)(sizeof(table) / sizeof(table[0]));
     return table;

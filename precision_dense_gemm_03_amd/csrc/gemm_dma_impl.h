@@ -35,6 +35,12 @@
 //     rows x 2 chunks of a transpose-read pass, for FP16 its 4 rows x 4
 //     chunks, land in 16 different bank groups.
 
+// K-major B (BT, B given as Bt[N,K] row-major, the layout a linear layer keeps
+// its weight in): B's tile is 256 rows of 64 bytes exactly like A's, loaded,
+// swizzled (swz_a) and read (ds_read_b128) the same way, so no transpose read
+// is needed; the LDS bytes read per MFMA stay the same but every read is a
+// full-width one.
+//
 // Edges: rows past M and column chunks past N are loaded from clamped (valid)
 // addresses and never stored; a partial last K tile is loaded by guarded
 // vector loads with zero fill. Operands that are not 16-byte aligned, or whose
@@ -159,10 +165,10 @@ __device__ __forceinline__ void wait_outstanding_tiles(int tiles) {
 // Scheduling pattern for one iteration: 24 LDS operand reads spread between
 // the MFMAs (16 of 32x32x64 for FP8, 32 of 32x32x16 for FP16), so the matrix
 // core has work queued while the reads are issued.
-template <int ES>
+template <int ES, bool BT>
 __device__ __forceinline__ void interleave_reads_with_mfma() {
     constexpr int kMfma = ES == 1 ? 16 : 32;
-    constexpr int kReads = 24;
+    constexpr int kReads = BT ? 16 : 24;  // K-major B: 8 A and 8 B ds_read_b128
     constexpr int kPer = (kReads + kMfma - 1) / kMfma;  // reads after each MFMA
 #pragma unroll
     for (int i = 0; i < kMfma; ++i) {
@@ -184,7 +190,7 @@ __device__ __forceinline__ void store_one(void* C, int64_t idx, float y, int efl
     }
 }
 
-template <int ES, int OUT, int STAGES, int FA, int FB>
+template <int ES, int OUT, int STAGES, int FA, int FB, bool BT>
 __global__ __launch_bounds__(256) void gemm_dma_kernel(const uint8_t* __restrict__ A, const uint8_t* __restrict__ B,
                                                        void* __restrict__ C, int M, int N, int K,
                                                        const float* __restrict__ sA, const float* __restrict__ sB,
@@ -213,7 +219,7 @@ __global__ __launch_bounds__(256) void gemm_dma_kernel(const uint8_t* __restrict
     // A block q (16 rows) = A_PER_WAVE blocks per wave; lane -> row 16q + lane/4,
     // slot lane%4 holding chunk slot ^ swz_a(row). Rows past M re-read M-1.
     const uint8_t* a_tile = A + (int64_t)m0 * K * ES;
-    const uint8_t* b_tile = B + (int64_t)n0 * ES;
+    const uint8_t* b_tile = BT ? B + (int64_t)n0 * K * ES : B + (int64_t)n0 * ES;
     uint32_t a_off[T::A_PER_WAVE], b_off[T::B_PER_WAVE];
 #pragma unroll
     for (int i = 0; i < T::A_PER_WAVE; ++i) {
@@ -227,17 +233,24 @@ __global__ __launch_bounds__(256) void gemm_dma_kernel(const uint8_t* __restrict
     // chunk of the row.
 #pragma unroll
     for (int i = 0; i < T::B_PER_WAVE; ++i) {
-        const int r = T::B_RPB * (wave * T::B_PER_WAVE + i) + lane / T::B_CPR;
-        const int c = (lane % T::B_CPR) ^ swz_b<ES>(r);
-        const int col = min(n0 + c * T::VE, N - T::VE) - n0;
-        b_off[i] = (uint32_t)(r * N * ES + col * ES);
+        if constexpr (BT) {  // as A: rows of Bt past N re-read row N-1
+            const int r = 16 * (wave * T::B_PER_WAVE + i) + (lane >> 2);
+            const int c = (lane & 3) ^ swz_a(r);
+            const int rr = min(n0 + r, N - 1) - n0;
+            b_off[i] = (uint32_t)(rr * K * ES + c * 16);
+        } else {
+            const int r = T::B_RPB * (wave * T::B_PER_WAVE + i) + lane / T::B_CPR;
+            const int c = (lane % T::B_CPR) ^ swz_b<ES>(r);
+            const int col = min(n0 + c * T::VE, N - T::VE) - n0;
+            b_off[i] = (uint32_t)(r * N * ES + col * ES);
+        }
     }
 
     auto issue_tile = [&](int kt) __attribute__((always_inline)) {
         LDS_AS uint8_t* st = smem + (kt % STAGES) * T::STAGE;
         if (kt < nk_full) {
             const uint8_t* pa = a_tile + (int64_t)kt * T::ROWB;
-            const uint8_t* pb = b_tile + (int64_t)kt * T::BK * N * ES;
+            const uint8_t* pb = b_tile + (BT ? (int64_t)kt * T::ROWB : (int64_t)kt * T::BK * N * ES);
             const uint32_t la = lds_base + (kt % STAGES) * T::STAGE + wave * T::A_PER_WAVE * 1024;
             const uint32_t lb = lds_base + (kt % STAGES) * T::STAGE + T::A_BYTES + wave * T::B_PER_WAVE * 1024;
             dma_tile(pa, pb, la, lb, a_off, b_off);
@@ -254,9 +267,15 @@ __global__ __launch_bounds__(256) void gemm_dma_kernel(const uint8_t* __restrict
             }
 #pragma unroll 1
             for (int i = 0; i < T::B_PER_WAVE; ++i) {
-                const int r = T::B_RPB * (wave * T::B_PER_WAVE + i) + lane / T::B_CPR;
                 v4u v = v4u{0u, 0u, 0u, 0u};
-                if (k0 + r < K) v = *reinterpret_cast<const v4u*>(b_tile + (int64_t)k0 * N * ES + b_off[i]);
+                if constexpr (BT) {
+                    const int r = 16 * (wave * T::B_PER_WAVE + i) + (lane >> 2);
+                    const int c = (lane & 3) ^ swz_a(r);
+                    if (k0 + c * T::VE < K) v = *reinterpret_cast<const v4u*>(b_tile + (int64_t)k0 * ES + b_off[i]);
+                } else {
+                    const int r = T::B_RPB * (wave * T::B_PER_WAVE + i) + lane / T::B_CPR;
+                    if (k0 + r < K) v = *reinterpret_cast<const v4u*>(b_tile + (int64_t)k0 * N * ES + b_off[i]);
+                }
                 *(LDS_AS v4u*)(st + T::A_BYTES + (wave * T::B_PER_WAVE + i) * 1024 + lane * 16) = v;
             }
         }
@@ -267,6 +286,8 @@ __global__ __launch_bounds__(256) void gemm_dma_kernel(const uint8_t* __restrict
     // FP16 k-step u reads chunk 2u + h.
     const int ar = wm * 128 + (lane & 31);
     const int a_sw = swz_a(ar);  // swizzle of rows ar + 32 tm (same for every tm)
+    const int br = wn * 128 + (lane & 31);  // K-major B: Bt row br + 32 tn
+    const int b_sw = swz_a(br);
     const int h = lane >> 5;
     const int j16 = lane & 15, half = (lane >> 4) & 1;
     Op ra0[T::KSUB][4], rb0[T::KSUB][4], ra1[T::KSUB][4], rb1[T::KSUB][4];
@@ -275,12 +296,23 @@ __global__ __launch_bounds__(256) void gemm_dma_kernel(const uint8_t* __restrict
         const LDS_AS uint8_t* st = smem + (kt % STAGES) * T::STAGE;
         const LDS_AS uint8_t* sa = st + ar * T::ROWB;
         const LDS_AS uint8_t* sb = st + T::A_BYTES;
+        const LDS_AS uint8_t* sbt = sb + br * T::ROWB;  // K-major B: this lane's row
         if constexpr (ES == 1) {
 #pragma unroll
             for (int tm = 0; tm < 4; ++tm) {
                 const v4i lo = *(const LDS_AS v4i*)(sa + tm * 32 * T::ROWB + ((2 * h) ^ a_sw) * 16);
                 const v4i hi = *(const LDS_AS v4i*)(sa + tm * 32 * T::ROWB + ((2 * h + 1) ^ a_sw) * 16);
                 ra[0][tm] = __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
+            }
+            if constexpr (BT) {  // as A: Bt row 128 wn + 32 tn + lane%32, chunks 2h, 2h+1
+#pragma unroll
+                for (int tn = 0; tn < 4; ++tn) {
+                    const LDS_AS uint8_t* p = sbt + tn * 32 * T::ROWB;
+                    const v4i lo = *(const LDS_AS v4i*)(p + ((2 * h) ^ b_sw) * 16);
+                    const v4i hi = *(const LDS_AS v4i*)(p + ((2 * h + 1) ^ b_sw) * 16);
+                    rb[0][tn] = __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
+                }
+                return;
             }
             // B: 16-lane group (h, half) covers columns 128 wn + 32 tn + 16 half + 0..15;
             // lane j16 addresses row 32h + 8t + j16/2, bytes 8*(j16%2) of that chunk.
@@ -305,6 +337,13 @@ __global__ __launch_bounds__(256) void gemm_dma_kernel(const uint8_t* __restrict
                 for (int tm = 0; tm < 4; ++tm)
                     ra[u][tm] = __builtin_bit_cast(
                         v8h, *(const LDS_AS v4u*)(sa + tm * 32 * T::ROWB + ((2 * u + h) ^ a_sw) * 16));
+                if constexpr (BT) {
+#pragma unroll
+                    for (int tn = 0; tn < 4; ++tn)
+                        rb[u][tn] = __builtin_bit_cast(
+                            v8h, *(const LDS_AS v4u*)(sbt + tn * 32 * T::ROWB + ((2 * u + h) ^ b_sw) * 16));
+                    continue;
+                }
                 // B: lane j16 addresses row 16u + 8h + 4t + j16/4, columns
                 // 128 wn + 32 tn + 16 half + 4 (j16%4) .. +3.
 #pragma unroll
@@ -366,7 +405,7 @@ __global__ __launch_bounds__(256) void gemm_dma_kernel(const uint8_t* __restrict
             wait_outstanding_tiles<T::LOADS_PER_TILE>(max(min(kt + D - 1, nk - 1) - (kt + 1), 0));
             read_ops(kt + 1, na, nb);
             mma(ca, cb);
-            interleave_reads_with_mfma<ES>();
+            interleave_reads_with_mfma<ES, BT>();
 #pragma unroll
             for (int tm = 0; tm < 4; ++tm)
 #pragma unroll
@@ -412,7 +451,8 @@ inline bool aligned16(const void* p) { return ((uintptr_t)p & 15u) == 0; }
 // Falls back to the register-staged 256x256 kernel when the direct-load
 // kernel's preconditions (16-byte aligned rows, 32-bit tile offsets) fail.
 inline hipError_t fallback(int kind, const GemmArgs& a) {
-    const char* name = kind == KIND_FP8 ? "tile_fp8_256x256x128_w2x4" : "tile_f16_256x256x64_w2x4";
+    const char* name = a.b_kmajor ? (kind == KIND_FP8 ? "tile_fp8_256x256x128_w2x4_bt" : "tile_f16_256x256x64_w2x4_bt")
+                                  : (kind == KIND_FP8 ? "tile_fp8_256x256x128_w2x4" : "tile_f16_256x256x64_w2x4");
     int nt = 0;
     const GemmConfig* tt = tile_configs(&nt);
     for (int i = 0; i < nt; ++i)
@@ -420,16 +460,18 @@ inline hipError_t fallback(int kind, const GemmArgs& a) {
     return hipErrorInvalidValue;
 }
 
-template <int ES, int STAGES, int FA, int FB>
+template <int ES, int STAGES, int FA, int FB, bool BT = false>
 hipError_t launch_dma(const GemmArgs& a) {
     using T = Dma<ES, STAGES>;
     if (a.splits > 1) return hipErrorInvalidValue;   // no split-K here (kgran 0 in the table)
+    if (BT != (a.b_kmajor != 0)) return hipErrorInvalidValue;
     const int64_t tiles_m = (a.M + T::BM - 1) / T::BM;
     const int64_t tiles_n = (a.N + T::BN - 1) / T::BN;
     const int64_t blocks = tiles_m * tiles_n;
     if (blocks <= 0) return hipSuccess;
-    const bool aligned = aligned16(a.A) && aligned16(a.B) && (a.K * ES) % 16 == 0 && (a.N * ES) % 16 == 0;
-    const bool fits = (int64_t)T::BM * a.K * ES < (1ll << 31) && (int64_t)T::BK * a.N * ES < (1ll << 31) &&
+    const bool aligned = aligned16(a.A) && aligned16(a.B) && (a.K * ES) % 16 == 0 && (BT || (a.N * ES) % 16 == 0);
+    const bool fits = (int64_t)T::BM * a.K * ES < (1ll << 31) &&
+                      (BT ? (int64_t)T::BN * a.K * ES : (int64_t)T::BK * a.N * ES) < (1ll << 31) &&
                       blocks <= 0x7FFFFFFF;
     if (!aligned || !fits) return fallback(ES == 1 ? KIND_FP8 : KIND_F16, a);
     const uint8_t* A = reinterpret_cast<const uint8_t*>(a.A);
@@ -439,16 +481,16 @@ hipError_t launch_dma(const GemmArgs& a) {
     const int eflags = (a.out_dtype == OUT_E5M2 ? EPI_E5M2 : 0) | (a.channel ? EPI_CHANNEL : 0);
     switch (a.out_dtype) {
         case OUT_F32:
-            gemm_dma_kernel<ES, OUT_F32, STAGES, FA, FB><<<grid, block, 0, a.stream>>>(
+            gemm_dma_kernel<ES, OUT_F32, STAGES, FA, FB, BT><<<grid, block, 0, a.stream>>>(
                 A, B, a.C, M, N, K, a.sA, a.sB, a.sOut, (int)tiles_m, (int)tiles_n, eflags);
             break;
         case OUT_F16:
-            gemm_dma_kernel<ES, OUT_F16, STAGES, FA, FB><<<grid, block, 0, a.stream>>>(
+            gemm_dma_kernel<ES, OUT_F16, STAGES, FA, FB, BT><<<grid, block, 0, a.stream>>>(
                 A, B, a.C, M, N, K, a.sA, a.sB, a.sOut, (int)tiles_m, (int)tiles_n, eflags);
             break;
         default:
             if constexpr (ES == 1) {
-                gemm_dma_kernel<ES, OUT_E4M3, STAGES, FA, FB><<<grid, block, 0, a.stream>>>(
+                gemm_dma_kernel<ES, OUT_E4M3, STAGES, FA, FB, BT><<<grid, block, 0, a.stream>>>(
                     A, B, a.C, M, N, K, a.sA, a.sB, a.sOut, (int)tiles_m, (int)tiles_n,
                     eflags);
             } else {

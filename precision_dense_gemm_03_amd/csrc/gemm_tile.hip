@@ -24,6 +24,13 @@ const GemmConfig* tile_configs(int* count) {
         {"tile_fp8_128x128x128_w2x2", KIND_FP8, 0, 128, 128, 128, tile::launch_tile_fp8_any<128, 128, 128, 2, 2>, kAllFp8Pairs, 128},
         {"tile_fp8_256x256x128_w2x4", KIND_FP8, 0, 256, 256, 128, tile::launch_tile_fp8_any<256, 256, 128, 2, 4>, kAllFp8Pairs, 128},
         {"tile_f16_256x256x64_w2x4", KIND_F16, 0, 256, 256, 64, tile::launch_tile<2, 256, 256, 64, 2, 4, 0, 0>, 0, 64},
+        // K-major B (Bt[N,K]): B staged and read like A; E4M3 x E4M3 and FP16.
+        {"tile_f16_64x64x64_w2x2_bt", KIND_F16, 0, 64, 64, 64, tile::launch_tile<2, 64, 64, 64, 2, 2, 0, 0, true>, 0, 64, 1},
+        {"tile_f16_128x128x64_w2x2_bt", KIND_F16, 0, 128, 128, 64, tile::launch_tile<2, 128, 128, 64, 2, 2, 0, 0, true>, 0, 64, 1},
+        {"tile_f16_256x256x64_w2x4_bt", KIND_F16, 0, 256, 256, 64, tile::launch_tile<2, 256, 256, 64, 2, 4, 0, 0, true>, 0, 64, 1},
+        {"tile_fp8_64x64x128_w2x2_bt", KIND_FP8, 0, 64, 64, 128, tile::launch_tile<1, 64, 64, 128, 2, 2, 0, 0, true>, 0, 128, 1},
+        {"tile_fp8_128x128x128_w2x2_bt", KIND_FP8, 0, 128, 128, 128, tile::launch_tile<1, 128, 128, 128, 2, 2, 0, 0, true>, 0, 128, 1},
+        {"tile_fp8_256x256x128_w2x4_bt", KIND_FP8, 0, 256, 256, 128, tile::launch_tile<1, 256, 256, 128, 2, 4, 0, 0, true>, 0, 128, 1},
     };
     *count = (int)(sizeof(table) / sizeof(table[0]));
     return table;

@@ -47,7 +47,9 @@ namespace tile {
 // than a 256x256 tile leaves; it stays compiled out until it fits.
 constexpr bool kRegisterPipeline = false;
 
-template <int ES, int BM, int BN, int BK, int WM, int WN>
+// BT: B is stored K-major, as Bt[N,K] row-major (the layout of a linear
+// layer's weight); its tile is then staged and read exactly like A's.
+template <int ES, int BM, int BN, int BK, int WM, int WN, bool BT = false>
 struct Tile {
     static constexpr int NT = 64 * WM * WN;           // threads per workgroup
     static constexpr int KPI = ES == 2 ? 32 : 128;    // k per MFMA instruction
@@ -64,26 +66,27 @@ struct Tile {
     // g and g+1 start RB rows apart) read the same 32 banks.
     static constexpr int RB = ES == 2 ? 8 : 32;
     static constexpr int A_BYTES = BM * SA;
-    static constexpr int B_BYTES = BK * SB + (BK / RB) * 128;
+    static constexpr int B_BYTES = BT ? BN * SA : BK * SB + (BK / RB) * 128;
     static constexpr int STAGE = A_BYTES + B_BYTES;
     static constexpr int A_CPR = BKB / 16;            // 16-byte chunks per A row
-    static constexpr int B_CPR = BNB / 16;
+    static constexpr int B_CPR = BT ? BKB / 16 : BNB / 16;
     static constexpr int A_RPP = NT / A_CPR;          // A rows covered per pass of all threads
     static constexpr int B_RPP = NT / B_CPR;
     static constexpr int CA = BM / A_RPP;             // A chunks per thread
-    static constexpr int CB = BK / B_RPP;
+    static constexpr int CB = (BT ? BN : BK) / B_RPP;  // B chunks per thread
     static constexpr int WTM = BM / WM, WTN = BN / WN;
     static constexpr int TM = WTM / 16, TN = WTN / 16;
     static constexpr int KS = BK / KPI;
     static_assert(BK % KPI == 0, "BK must be a multiple of the MFMA depth");
     static_assert(NT % A_CPR == 0 && NT % B_CPR == 0, "chunk rows must tile the workgroup");
-    static_assert(BM % A_RPP == 0 && BK % B_RPP == 0, "tile chunks must divide evenly");
+    static_assert(BM % A_RPP == 0 && (BT ? BN : BK) % B_RPP == 0, "tile chunks must divide evenly");
     static_assert(WTM % 16 == 0 && WTN % 16 == 0, "wave tile must be whole 16x16 blocks");
     static_assert(2 * STAGE <= 160 * 1024, "two stages must fit in LDS");
     // LDS map: A stage 0, A stage 1, B stage 0, B stage 1
     static constexpr int a_stage(int s) { return s * A_BYTES; }
     static constexpr int b_stage(int s) { return 2 * A_BYTES + s * B_BYTES; }
-    static __device__ __forceinline__ int b_row(int r) { return r * SB + (r / RB) * 128; }
+    // LDS byte offset of staged B row r (a k row, or for BT an n row)
+    static __device__ __forceinline__ int b_row(int r) { return BT ? r * SA : r * SB + (r / RB) * 128; }
 };
 
 // MFMA operand type, LDS operand reads and the multiply for each element size.
@@ -166,12 +169,12 @@ __device__ __forceinline__ void store_one(void* C, int64_t idx, float y, int efl
     }
 }
 
-template <int ES, int OUT, int BM, int BN, int BK, int WM, int WN, int FA, int FB>
+template <int ES, int OUT, int BM, int BN, int BK, int WM, int WN, int FA, int FB, bool BT>
 __global__ __launch_bounds__(64 * WM * WN) void gemm_tile_kernel(
     const uint8_t* __restrict__ A, const uint8_t* __restrict__ B, void* __restrict__ C, int M, int N, int K,
     const float* __restrict__ sA, const float* __restrict__ sB, const float* __restrict__ sOut, int tiles_m,
     int tiles_n, int aligned, int eflags, int kchunk) {
-    using T = Tile<ES, BM, BN, BK, WM, WN>;
+    using T = Tile<ES, BM, BN, BK, WM, WN, BT>;
     __shared__ __attribute__((aligned(16))) uint8_t smem_raw[2 * T::STAGE];
     LDS_AS uint8_t* smem = (LDS_AS uint8_t*)smem_raw;
 
@@ -213,8 +216,10 @@ __global__ __launch_bounds__(64 * WM * WN) void gemm_tile_kernel(
     const int b_row_in = (ES == 2) ? (j16 >> 2) : (j16 >> 1);
     const int b_col_in = (ES == 2) ? 4 * (j16 & 3) : 8 * (j16 & 1);
     const int a_lds = (wm * T::WTM + j16) * T::SA + g * T::OPB;          // + stage + tm*16*SA + ks*KPI*ES
-    const int b_lds = T::b_row(8 * (ES == 2 ? 1 : 4) * g + b_row_in)    // + stage + b_row(ks*KPI) + tn*16*ES
-                      + (wn * T::WTN + b_col_in) * ES;
+    // BT: + stage + tn*16*SA + ks*KPI*ES, as for A
+    const int b_lds = BT ? (wn * T::WTN + j16) * T::SA + g * T::OPB
+                         : T::b_row(8 * (ES == 2 ? 1 : 4) * g + b_row_in)  // + stage + b_row(ks*KPI) + tn*16*ES
+                               + (wn * T::WTN + b_col_in) * ES;
 
     const int nk = (klen + BK - 1) / BK;
     typedef typename Operand<ES>::type Op;
@@ -224,7 +229,7 @@ __global__ __launch_bounds__(64 * WM * WN) void gemm_tile_kernel(
     // per-lane offset, so the 16 loads of a tile need no 64-bit VGPR addresses.
     // Valid while one tile row block spans less than 2^31 bytes (checked below).
     const uint8_t* a_tile = A + ((int64_t)m0 * K + kbeg) * ES;
-    const uint8_t* b_tile = B + ((int64_t)kbeg * N + n0) * ES;
+    const uint8_t* b_tile = BT ? B + ((int64_t)n0 * K + kbeg) * ES : B + ((int64_t)kbeg * N + n0) * ES;
     // Edge tiles (aligned operands) use the same unguarded loads with the
     // addresses clamped into the matrix: A rows past M re-read row M-1 and B
     // column chunks past N re-read the last chunk. Those values only reach
@@ -237,8 +242,13 @@ __global__ __launch_bounds__(64 * WM * WN) void gemm_tile_kernel(
     }
 #pragma unroll
     for (int i = 0; i < T::CB; ++i) {
-        const int c = min(n0 + b_col * T::VE, N - T::VE) - n0;
-        b_offs[i] = (uint32_t)(((b_row + i * T::B_RPP) * N + c) * ES);
+        if constexpr (BT) {
+            const int r = min(n0 + b_row + i * T::B_RPP, N - 1) - n0;
+            b_offs[i] = (uint32_t)((r * K + b_col * T::VE) * ES);
+        } else {
+            const int c = min(n0 + b_col * T::VE, N - T::VE) - n0;
+            b_offs[i] = (uint32_t)(((b_row + i * T::B_RPP) * N + c) * ES);
+        }
     }
     auto load_a = [&](int kt) __attribute__((always_inline)) {
         const uint8_t* pa = a_tile + (int64_t)kt * BK * ES;
@@ -246,7 +256,7 @@ __global__ __launch_bounds__(64 * WM * WN) void gemm_tile_kernel(
         for (int i = 0; i < T::CA; ++i) ra[i] = *reinterpret_cast<const v4u*>(pa + a_offs[i]);
     };
     auto load_b = [&](int kt) __attribute__((always_inline)) {
-        const uint8_t* pb = b_tile + (int64_t)kt * BK * N * ES;
+        const uint8_t* pb = b_tile + (BT ? (int64_t)kt * BK * ES : (int64_t)kt * BK * N * ES);
 #pragma unroll
         for (int i = 0; i < T::CB; ++i) rb[i] = *reinterpret_cast<const v4u*>(pb + b_offs[i]);
     };
@@ -283,6 +293,18 @@ __global__ __launch_bounds__(64 * WM * WN) void gemm_tile_kernel(
         }
 #pragma unroll 1
         for (int i = 0; i < T::CB; ++i) {
+            if constexpr (BT) {
+                const int gn = n0 + b_row + i * T::B_RPP;
+                const int64_t gk = (int64_t)k0 + b_col * T::VE;
+                const uint8_t* rp = B + (int64_t)gn * K * ES;
+                v4u v;
+                if (aligned && gn < N && gk + T::VE <= kend)
+                    v = *reinterpret_cast<const v4u*>(rp + gk * ES);
+                else
+                    v = load_chunk_guarded<ES>(rp, gn < N, gk, kend);
+                *(LDS_AS v4u*)(Bs + T::b_row(b_row + i * T::B_RPP) + b_col * 16) = v;
+                continue;
+            }
             const int gk = k0 + b_row + i * T::B_RPP;
             const int64_t gn = (int64_t)n0 + b_col * T::VE;
             const uint8_t* rp = B + (int64_t)gk * N * ES;
@@ -301,8 +323,12 @@ __global__ __launch_bounds__(64 * WM * WN) void gemm_tile_kernel(
 #pragma unroll
         for (int ks = 0; ks < T::KS; ++ks)
 #pragma unroll
-            for (int tn = 0; tn < T::TN; ++tn)
-                bop[ks][tn] = Operand<ES>::read_b(base + T::b_row(ks * T::KPI) + tn * 16 * ES, T::SB);
+            for (int tn = 0; tn < T::TN; ++tn) {
+                if constexpr (BT)
+                    bop[ks][tn] = Operand<ES>::read_a(base + tn * 16 * T::SA + ks * T::KPI * ES);
+                else
+                    bop[ks][tn] = Operand<ES>::read_b(base + T::b_row(ks * T::KPI) + tn * 16 * ES, T::SB);
+            }
     };
     auto mma_tile = [&](int stage, const Op (&bop)[T::KS][T::TN]) __attribute__((always_inline)) {
         const LDS_AS uint8_t* base = smem + T::a_stage(stage) + a_lds;
@@ -326,7 +352,8 @@ __global__ __launch_bounds__(64 * WM * WN) void gemm_tile_kernel(
             }
     };
 
-    const bool offsets_fit = (int64_t)BM * K * ES < (1ll << 31) && (int64_t)BK * N * ES < (1ll << 31);
+    const bool offsets_fit = (int64_t)BM * K * ES < (1ll << 31) &&
+                             (BT ? (int64_t)BN * K * ES : (int64_t)BK * N * ES) < (1ll << 31);
     if (kRegisterPipeline && interior_mn && klen % BK == 0 && nk > 0 && offsets_fit) {
         // Software pipeline, one barrier per K tile. Entering iteration kt:
         // LDS holds A(kt) in A stage kt%2 and B(kt+1) in B stage (kt+1)%2,
@@ -446,7 +473,7 @@ inline bool aligned16(const void* p) { return ((uintptr_t)p & 15u) == 0; }
 
 // Launches one configuration for operand formats FA, FB (FP8 only; FP16 uses
 // 0, 0). Defined here for every translation unit that instantiates it.
-template <int ES, int BM, int BN, int BK, int WM, int WN, int FA, int FB>
+template <int ES, int BM, int BN, int BK, int WM, int WN, int FA, int FB, bool BT = false>
 hipError_t launch_tile(const GemmArgs& a) {
     const int64_t tiles_m = (a.M + BM - 1) / BM;
     const int64_t tiles_n = (a.N + BN - 1) / BN;
@@ -458,29 +485,32 @@ hipError_t launch_tile(const GemmArgs& a) {
                        splits > 65535 || !a.ws))
         return hipErrorInvalidValue;
     const int kchunk = splits > 1 ? (int)a.k_chunk : (int)a.K;
-    const int aligned = aligned16(a.A) && aligned16(a.B) && ((a.K * ES) % 16 == 0) && ((a.N * ES) % 16 == 0);
+    if (BT != (a.b_kmajor != 0)) return hipErrorInvalidValue;
+    // Vector loads need 16-byte aligned bases and row pitches (for BT, B's
+    // rows are K long like A's, so N needs no alignment).
+    const int aligned = aligned16(a.A) && aligned16(a.B) && ((a.K * ES) % 16 == 0) && (BT || (a.N * ES) % 16 == 0);
     const uint8_t* A = reinterpret_cast<const uint8_t*>(a.A);
     const uint8_t* B = reinterpret_cast<const uint8_t*>(a.B);
     const int M = (int)a.M, N = (int)a.N, K = (int)a.K;
     const dim3 grid((unsigned)blocks, (unsigned)splits), block(64 * WM * WN);
     if (splits > 1) {   // FP32 partial sums into the workspace
-        gemm_tile_kernel<ES, OUT_F32, BM, BN, BK, WM, WN, FA, FB><<<grid, block, 0, a.stream>>>(
+        gemm_tile_kernel<ES, OUT_F32, BM, BN, BK, WM, WN, FA, FB, BT><<<grid, block, 0, a.stream>>>(
             A, B, a.ws, M, N, K, nullptr, nullptr, nullptr, (int)tiles_m, (int)tiles_n, aligned, EPI_PARTIAL, kchunk);
         return hipGetLastError();
     }
     const int eflags = (a.out_dtype == OUT_E5M2 ? EPI_E5M2 : 0) | (a.channel ? EPI_CHANNEL : 0);
     switch (a.out_dtype) {
         case OUT_F32:
-            gemm_tile_kernel<ES, OUT_F32, BM, BN, BK, WM, WN, FA, FB><<<grid, block, 0, a.stream>>>(
+            gemm_tile_kernel<ES, OUT_F32, BM, BN, BK, WM, WN, FA, FB, BT><<<grid, block, 0, a.stream>>>(
                 A, B, a.C, M, N, K, a.sA, a.sB, a.sOut, (int)tiles_m, (int)tiles_n, aligned, eflags, kchunk);
             break;
         case OUT_F16:
-            gemm_tile_kernel<ES, OUT_F16, BM, BN, BK, WM, WN, FA, FB><<<grid, block, 0, a.stream>>>(
+            gemm_tile_kernel<ES, OUT_F16, BM, BN, BK, WM, WN, FA, FB, BT><<<grid, block, 0, a.stream>>>(
                 A, B, a.C, M, N, K, a.sA, a.sB, a.sOut, (int)tiles_m, (int)tiles_n, aligned, eflags, kchunk);
             break;
         default:
             if constexpr (ES == 1) {
-                gemm_tile_kernel<ES, OUT_E4M3, BM, BN, BK, WM, WN, FA, FB><<<grid, block, 0, a.stream>>>(
+                gemm_tile_kernel<ES, OUT_E4M3, BM, BN, BK, WM, WN, FA, FB, BT><<<grid, block, 0, a.stream>>>(
                     A, B, a.C, M, N, K, a.sA, a.sB, a.sOut, (int)tiles_m, (int)tiles_n, aligned,
                     eflags, kchunk);
             } else {
@@ -492,13 +522,13 @@ hipError_t launch_tile(const GemmArgs& a) {
 
 // Operand-format dispatch for configurations compiled for every FP8 pair; the
 // pairs other than E4M3 x E4M3 are instantiated in gemm_tile_mixed.hip.
-template <int BM, int BN, int BK, int WM, int WN>
+template <int BM, int BN, int BK, int WM, int WN, bool BT = false>
 hipError_t launch_tile_fp8_any(const GemmArgs& a) {
     switch (a.fmt_a * 2 + a.fmt_b) {
-        case 0: return launch_tile<1, BM, BN, BK, WM, WN, 0, 0>(a);
-        case 1: return launch_tile<1, BM, BN, BK, WM, WN, 0, 1>(a);
-        case 2: return launch_tile<1, BM, BN, BK, WM, WN, 1, 0>(a);
-        default: return launch_tile<1, BM, BN, BK, WM, WN, 1, 1>(a);
+        case 0: return launch_tile<1, BM, BN, BK, WM, WN, 0, 0, BT>(a);
+        case 1: return launch_tile<1, BM, BN, BK, WM, WN, 0, 1, BT>(a);
+        case 2: return launch_tile<1, BM, BN, BK, WM, WN, 1, 0, BT>(a);
+        default: return launch_tile<1, BM, BN, BK, WM, WN, 1, 1, BT>(a);
     }
 }
 

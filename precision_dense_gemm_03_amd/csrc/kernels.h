@@ -28,6 +28,8 @@ struct GemmArgs {
     float* ws = nullptr;
     int splits = 1;
     int64_t k_chunk = 0;
+    // 1: B is stored K-major, as Bt[N,K] row-major (element (k, n) at n*K + k)
+    int b_kmajor = 0;
 };
 
 typedef hipError_t (*GemmLauncher)(const GemmArgs&);
@@ -41,6 +43,7 @@ struct GemmConfig {
     GemmLauncher launch;
     int fmt_mask = 0;   // FP8 operand pairs served: bit (2*fmt_a + fmt_b); 0 means E4M3 x E4M3 only
     int kgran = 0;      // split-K: K ranges are multiples of kgran; 0 = this config does not split
+    int b_kmajor = 0;   // B layout served: 0 row-major B[K,N], 1 K-major Bt[N,K]
 };
 
 constexpr int kAllFp8Pairs = 15;
@@ -55,11 +58,12 @@ inline bool serves_formats(const GemmConfig& c, int fa, int fb) {
 const GemmConfig* tile_configs(int* count);
 const GemmConfig* stream_configs(int* count);
 const GemmConfig* dma_configs(int* count);
+const GemmConfig* gemv_kmajor_configs(int* count);
 
 // Shape (and FP8 operand formats) -> configuration (host only, no HIP calls).
 // Returns NULL if none fits.
 const GemmConfig* select_config(int kind, int out_dtype, int64_t M, int64_t N, int64_t K, int fmt_a = 0,
-                                int fmt_b = 0);
+                                int fmt_b = 0, int b_kmajor = 0);
 
 // Split-K plan for the workspace entry points: the configuration, the number
 // of K ranges and their length (splits == 1: no split, the plain launch).
@@ -78,6 +82,9 @@ hipError_t launch_splitk_reduce(const GemmArgs& a);
 // power-of-two scale.
 hipError_t launch_amax(const float* x, int64_t n, float* amax, float* scale, int fmt, int pow2, hipStream_t stream);
 hipError_t launch_quantize(const float* x, int64_t n, const float* scale, uint8_t* q, int fmt, hipStream_t stream);
+// Quantize with a transposed output: q[c * rows + r] = code(x[r * cols + c] / scale).
+hipError_t launch_quantize_transposed(const float* x, int64_t rows, int64_t cols, const float* scale, uint8_t* q,
+                                      int fmt, hipStream_t stream);
 // Per-channel amax / scale / quantize over a row-major x[rows, cols]: axis 0
 // one channel per row, axis 1 one per column. For axis 1, amax doubles as the
 // running maximum while the launches run.

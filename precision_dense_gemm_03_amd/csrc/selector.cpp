@@ -41,22 +41,29 @@ namespace {
 
 constexpr int64_t kNumCUs = 256;
 constexpr int64_t kStreamMaxM = 4;
+constexpr int64_t kGemvMaxM = 8;
 constexpr int64_t kSplitMaxM = 256;
 
-const GemmConfig* find_named(const char* name, int kind, int64_t M, int fa = 0, int fb = 0) {
-    int ns = 0, nt = 0;
+// Whether c can serve the request (operand kind, FP8 formats, B layout).
+bool serves(const GemmConfig& c, int kind, int fa, int fb, int bt) {
+    return c.kind == kind && serves_formats(c, fa, fb) && c.b_kmajor == bt;
+}
+
+const GemmConfig* find_named(const char* name, int kind, int64_t M, int fa = 0, int fb = 0, int bt = 0) {
+    int ns = 0, nt = 0, nv = 0;
     const GemmConfig* st = stream_configs(&ns);
     const GemmConfig* tt = tile_configs(&nt);
+    const GemmConfig* vt = gemv_kmajor_configs(&nv);
     for (int i = 0; i < ns; ++i)
-        if (std::strcmp(st[i].name, name) == 0 && st[i].kind == kind && M <= st[i].bm &&
-            serves_formats(st[i], fa, fb))
-            return &st[i];
+        if (std::strcmp(st[i].name, name) == 0 && serves(st[i], kind, fa, fb, bt) && M <= st[i].bm) return &st[i];
+    for (int i = 0; i < nv; ++i)
+        if (std::strcmp(vt[i].name, name) == 0 && serves(vt[i], kind, fa, fb, bt) && M <= vt[i].bm) return &vt[i];
     for (int i = 0; i < nt; ++i)
-        if (std::strcmp(tt[i].name, name) == 0 && tt[i].kind == kind && serves_formats(tt[i], fa, fb)) return &tt[i];
+        if (std::strcmp(tt[i].name, name) == 0 && serves(tt[i], kind, fa, fb, bt)) return &tt[i];
     int nd = 0;
     const GemmConfig* dt = dma_configs(&nd);
     for (int i = 0; i < nd; ++i)
-        if (std::strcmp(dt[i].name, name) == 0 && dt[i].kind == kind && serves_formats(dt[i], fa, fb)) return &dt[i];
+        if (std::strcmp(dt[i].name, name) == 0 && serves(dt[i], kind, fa, fb, bt)) return &dt[i];
     return nullptr;
 }
 
@@ -69,8 +76,13 @@ const GemmConfig* find_named(const char* name, int kind, int64_t M, int fa = 0, 
 // vs 877, FP8 8192^3 481 vs 492; FP16 4096^3 144 vs 153; FP16 8192^3 1051
 // vs 1022 (register-staged vs direct-load). Smaller tiles use the
 // register-staged kernel with 4 waves.
-const GemmConfig* tile_with(int kind, int bm, int64_t tiles, int fa, int fb) {
-    if (bm == 256) {
+const GemmConfig* tile_with(int kind, int bm, int64_t tiles, int fa, int fb, int bt = 0) {
+    if (bm == 256 && bt) {
+        const GemmConfig* c =
+            find_named(kind == KIND_FP8 ? "tile_fp8_256x256x128_w2x4_bt" : "tile_f16_256x256x64_w2x4_bt", kind, 0,
+                       fa, fb, 1);
+        if (c) return c;
+    } else if (bm == 256) {
         const bool direct = kind == KIND_F16 && tiles >= 2 * kNumCUs;
         const char* want = direct ? "dma_f16_256x256x32_s4"
                                   : (kind == KIND_FP8 ? "tile_fp8_256x256x128_w2x4" : "tile_f16_256x256x64_w2x4");
@@ -80,18 +92,45 @@ const GemmConfig* tile_with(int kind, int bm, int64_t tiles, int fa, int fb) {
     int nt = 0;
     const GemmConfig* tt = tile_configs(&nt);
     for (int i = 0; i < nt; ++i)
-        if (tt[i].kind == kind && tt[i].bm == bm && serves_formats(tt[i], fa, fb)) return &tt[i];
+        if (serves(tt[i], kind, fa, fb, bt) && tt[i].bm == bm) return &tt[i];
     return nullptr;
 }
 
 }  // namespace
 
-const GemmConfig* select_config(int kind, int out_dtype, int64_t M, int64_t N, int64_t K, int fa, int fb) {
+const GemmConfig* select_config(int kind, int out_dtype, int64_t M, int64_t N, int64_t K, int fa, int fb, int bt) {
     (void)out_dtype;
     (void)K;
     if (kind == KIND_F16) fa = fb = 0;
     if (const char* env = std::getenv("LIBGEMM_CONFIG")) {
-        if (const GemmConfig* c = find_named(env, kind, M, fa, fb)) return c;
+        if (const GemmConfig* c = find_named(env, kind, M, fa, fb, bt)) return c;
+    }
+    if (bt) {
+        // K-major B: decode shapes (M <= 8) read each weight row once as a dot
+        // product (no transposition, no split of K across workgroups); the
+        // first table entry of the smallest bound >= M is taken.
+        if (M <= kGemvMaxM) {
+            int nv = 0;
+            const GemmConfig* vt = gemv_kmajor_configs(&nv);
+            const GemmConfig* best = nullptr;
+            for (int i = 0; i < nv; ++i)
+                if (serves(vt[i], kind, fa, fb, 1) && M <= vt[i].bm && (!best || vt[i].bm < best->bm)) best = &vt[i];
+            if (best) return best;
+        }
+        // Tiles as for row-major B, except that a 256x256 grid covering 3/4
+        // of the CUs already beats 128x128 tiles (E4M3 3000x4096x4096: 66.6 us
+        // on 192 tiles vs 71.4 us on 768).
+        static const int bt_sizes[] = {256, 128, 64};
+        for (int bm : bt_sizes) {
+            const int64_t tm = (M + bm - 1) / bm, tn = (N + bm - 1) / bm;
+            const double useful = (double)M * (double)N;
+            const double padded = (double)(tm * bm) * (double)(tn * bm);
+            const int64_t min_tiles = bm == 256 ? kNumCUs * 3 / 4 : kNumCUs;
+            if (tm * tn >= min_tiles && useful >= 0.75 * padded) {
+                if (const GemmConfig* c = tile_with(kind, bm, tm * tn, fa, fb, 1)) return c;
+            }
+        }
+        return tile_with(kind, 64, 0, fa, fb, 1);
     }
     if (M <= kStreamMaxM) {
         const GemmConfig* best = nullptr;
@@ -99,7 +138,7 @@ const GemmConfig* select_config(int kind, int out_dtype, int64_t M, int64_t N, i
         const GemmConfig* st = stream_configs(&ns);
         for (int i = 0; i < ns; ++i) {
             const GemmConfig& c = st[i];
-            if (c.kind == kind && M <= c.bm && serves_formats(c, fa, fb) && (!best || c.bm < best->bm)) best = &c;
+            if (serves(c, kind, fa, fb, 0) && M <= c.bm && (!best || c.bm < best->bm)) best = &c;
         }
         if (best) return best;
     }

@@ -302,3 +302,46 @@ def test_select_config_validation():
     assert L.gemm_select_config(1, 0, -1, 1, 1, buf, 8) == -2
     assert L.gemm_select_config(1, 0, 1, 1, 1, None, 8) == -1
     assert L.gemm_select_config(1, 0, 4096, 4096, 4096, buf, 8) == 0 and len(buf.value) == 7  # truncated
+
+
+def test_kmajor_entry_points_argument_validation():
+    L = g.lib()
+    s = FAKE3 + 4096
+    # gemm_f16_bt(A, Bt, C, out, M, N, K, stream)
+    assert L.gemm_f16_bt(FAKE, FAKE2, FAKE3, 2, 4, 4, 4, None) == -3
+    assert L.gemm_f16_bt(FAKE, FAKE2, FAKE3, 0, 4, -4, 4, None) == -2
+    assert L.gemm_f16_bt(FAKE, None, FAKE3, 0, 4, 4, 4, None) == -1
+    assert L.gemm_f16_bt(FAKE, FAKE2, FAKE2 + 30, 1, 4, 4, 4, None) == -8   # C overlaps Bt
+    # gemm_fp8_scaled_bt(A, Bt, sA, sB, sOut, C, out, M, N, K, stream)
+    assert L.gemm_fp8_scaled_bt(FAKE, FAKE2, s, s + 4, None, FAKE3, 2, 4, 4, 4, None) == -4
+    assert L.gemm_fp8_scaled_bt(FAKE, FAKE2, None, s, None, FAKE3, 0, 4, 4, 4, None) == -1
+    assert L.gemm_fp8_scaled_bt(FAKE, FAKE2, s, s, None, FAKE3, 9, 4, 4, 4, None) == -3
+    assert L.gemm_fp8_scaled_bt(FAKE, FAKE2, FAKE3 + 8, s, None, FAKE3, 0, 4, 4, 4, None) == -8
+    # quantize_fp8_transposed(x, rows, cols, scale, q, stream)
+    assert L.quantize_fp8_transposed(FAKE, -1, 4, FAKE2, FAKE3, None) == -2
+    assert L.quantize_fp8_transposed(FAKE, 4, 4, None, FAKE3, None) == -1
+    assert L.quantize_fp8_transposed(FAKE, 4, 4, FAKE2, FAKE + 60, None) == -8   # q overlaps x
+    assert L.quantize_fp8_transposed(None, 0, 4, None, None, None) == 0
+
+
+def test_kmajor_selector():
+    """K-major B: decode shapes (M <= 8) take the dot-product decode kernels,
+    larger M the K-major tile kernels, by the tile rules of row-major B (a
+    256x256 grid already from 3/4 of the CUs)."""
+    assert g.select_config_bt(g.KIND_F16, g.OUT_F16, 1, 12288, 4096) == "gemv_coop_f16_m1_r4_w8"
+    assert g.select_config_bt(g.KIND_F16, g.OUT_F16, 2, 12288, 4096) == "gemv_bt_f16_m4_r4_u2"
+    assert g.select_config_bt(g.KIND_F16, g.OUT_F16, 4, 12288, 4096) == "gemv_bt_f16_m4_r4_u2"
+    assert g.select_config_bt(g.KIND_F16, g.OUT_F16, 8, 12288, 4096) == "gemv_bt_f16_m8_r2_u2"
+    assert g.select_config_bt(g.KIND_F16, g.OUT_F16, 9, 12288, 4096) == "tile_f16_64x64x64_w2x2_bt"
+    assert g.select_config_bt(g.KIND_FP8, g.OUT_E4M3, 1, 4096, 4096) == "gemv_bt_fp8_m1_r4_u4"
+    assert g.select_config_bt(g.KIND_FP8, g.OUT_E4M3, 3, 4096, 4096) == "gemv_coop_fp8_m4_r4_w4"
+    assert g.select_config_bt(g.KIND_FP8, g.OUT_E4M3, 8, 4096, 4096) == "gemv_coop_fp8_m8_r2_w4"
+    assert g.select_config_bt(g.KIND_FP8, g.OUT_E4M3, 4096, 4096, 4096) == "tile_fp8_256x256x128_w2x4_bt"
+    assert g.select_config_bt(g.KIND_FP8, g.OUT_E4M3, 3000, 4096, 4096) == "tile_fp8_256x256x128_w2x4_bt"
+    assert g.select_config_bt(g.KIND_F16, g.OUT_F16, 4096, 4096, 4096) == "tile_f16_256x256x64_w2x4_bt"
+    assert g.select_config_bt(g.KIND_FP8, g.OUT_F32, 1024, 1024, 1024) == "tile_fp8_64x64x128_w2x2_bt"
+    assert g.select_config_bt(g.KIND_FP8, g.OUT_F32, 65, 4096, 4096) == "tile_fp8_64x64x128_w2x2_bt"
+    # the row-major selector never returns a K-major configuration, nor the reverse
+    assert not g.select_config(g.KIND_FP8, g.OUT_F32, 4096, 4096, 4096).endswith("_bt")
+    assert g.select_config(g.KIND_F16, g.OUT_F16, 1, 12288, 4096).startswith("stream_")
+    assert g.select_config(g.KIND_FP8, g.OUT_F32, 3000, 4096, 4096) == "tile_fp8_128x128x128_w2x2"
