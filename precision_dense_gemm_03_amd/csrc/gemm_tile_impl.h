@@ -46,6 +46,17 @@ namespace tile {
 // The fully register-pipelined loop (two B operand sets) needs more registers
 // than a 256x256 tile leaves; it stays compiled out until it fits.
 constexpr bool kRegisterPipeline = false;
+// 8-wave kernels with K-major B: read the next A operand before the current
+// row block's MFMAs (one more operand register set) and raise the wave's issue
+// priority while it issues MFMAs. Measured on one MI355X (us, K-major B):
+// E4M3 4096^3 80.2-81.5 -> 78.3, E4M3 16384x12288x4096 822-827 -> 785, FP16
+// 4096^3 158-161 -> 151; the same change slowed the row-major kernels (83 ->
+// 86, 832 -> 887), whose B operands come from transpose reads, so it is
+// applied with K-major B only.
+template <bool BT>
+constexpr bool kPrefetchA = BT;
+template <bool BT>
+constexpr bool kMfmaPrio = BT;
 
 // BT: B is stored K-major, as Bt[N,K] row-major (the layout of a linear
 // layer's weight); its tile is then staged and read exactly like A's.
@@ -332,13 +343,36 @@ __global__ __launch_bounds__(64 * WM * WN) void gemm_tile_kernel(
     };
     auto mma_tile = [&](int stage, const Op (&bop)[T::KS][T::TN]) __attribute__((always_inline)) {
         const LDS_AS uint8_t* base = smem + T::a_stage(stage) + a_lds;
+        if constexpr (kPrefetchA<BT> && T::NT > 256) {
+            // Row blocks in (ks, tm) order; the A operand of the next block is
+            // read before this block's MFMAs, so its LDS latency runs under them.
+            constexpr int NB = T::KS * T::TM;
+            auto a_addr = [&](int b) { return base + (b % T::TM) * 16 * T::SA + (b / T::TM) * T::KPI * ES; };
+            Op acur = Operand<ES>::read_a(a_addr(0));
+#pragma unroll
+            for (int b = 0; b < NB; ++b) {
+                const int ks = b / T::TM, tm = b % T::TM;
+                const Op anext = Operand<ES>::read_a(a_addr(b + 1 < NB ? b + 1 : b));
+                if constexpr (kMfmaPrio<BT>) __builtin_amdgcn_s_setprio(1);
+#pragma unroll
+                for (int tn = 0; tn < T::TN; ++tn)
+                    acc[tm][tn] = Operand<ES>::template mma<FA, FB>(acur, bop[ks][tn], acc[tm][tn]);
+                if constexpr (kMfmaPrio<BT>) __builtin_amdgcn_s_setprio(0);
+#pragma unroll
+                for (int tn = 0; tn < T::TN; ++tn) asm volatile("" : "+v"(acc[tm][tn])::"memory");
+                acur = anext;
+            }
+            return;
+        }
 #pragma unroll
         for (int ks = 0; ks < T::KS; ++ks)
 #pragma unroll
             for (int tm = 0; tm < T::TM; ++tm) {
                 const Op aop = Operand<ES>::read_a(base + tm * 16 * T::SA + ks * T::KPI * ES);
+                if constexpr (kMfmaPrio<BT> && T::NT > 256) __builtin_amdgcn_s_setprio(1);
 #pragma unroll
                 for (int tn = 0; tn < T::TN; ++tn) acc[tm][tn] = Operand<ES>::template mma<FA, FB>(aop, bop[ks][tn], acc[tm][tn]);
+                if constexpr (kMfmaPrio<BT> && T::NT > 256) __builtin_amdgcn_s_setprio(0);
                 // With two waves per SIMD the other wave hides the A read
                 // latency. Pinning this row block's products here (an empty
                 // asm that reads and rewrites its accumulators, after which no
