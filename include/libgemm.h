@@ -372,6 +372,27 @@ int quantize_fp8_transposed(const float* x, int64_t rows, int64_t cols, const fl
 int gemm_select_config_bt(int kind, int out_dtype, int64_t M, int64_t N, int64_t K,
                           char* buf, int buflen);
 
+/*
+ * gemm_fp8_splitk_bt / gemm_f16_splitk_bt — gemm_fp8_scaled_bt / gemm_f16_bt
+ * that may split K over a caller-provided workspace, exactly as
+ * gemm_fp8_splitk / gemm_f16_splitk do for row-major B (P3 §6: K split to
+ * spread one GEMM over more compute; the epilogue's scale and rounding are
+ * applied once, to the full sum). Shapes up to M = 256 may split; decode
+ * shapes (M <= 8) keep the K-major decode kernels and never split. Workspace
+ * rules, errors and the determinism of the result as gemm_fp8_splitk; the
+ * FP8 call takes E4M3 operands.
+ */
+int gemm_fp8_splitk_bt(const uint8_t* A, const uint8_t* Bt, const float* sA, const float* sB,
+                       const float* sOut, void* C, int out_dtype, int64_t M, int64_t N, int64_t K,
+                       void* workspace, int64_t workspace_bytes, hipStream_t stream);
+int gemm_f16_splitk_bt(const void* A, const void* Bt, void* C, int out_dtype,
+                       int64_t M, int64_t N, int64_t K, void* workspace, int64_t workspace_bytes,
+                       hipStream_t stream);
+
+/* gemm_splitk_plan for the two calls above (kind 0: FP16, 1: E4M3). */
+int gemm_splitk_plan_bt(int kind, int out_dtype, int64_t M, int64_t N, int64_t K,
+                        char* buf, int buflen, int* splits, int64_t* workspace_bytes);
+
 #ifdef __cplusplus
 }
 #endif

@@ -28,6 +28,9 @@ Functions keep the C names:
     gemm_fp8_scaled_bt(A, Bt, sA, sB, C, sOut=None, stream=None, out_fmt=None)
     quantize_fp8_transposed(x, scale, q=None, stream=None) -> q[cols, rows]
     select_config_bt(kind, out_dtype, M, N, K) -> str
+    gemm_fp8_splitk_bt(A, Bt, sA, sB, C, sOut=None, workspace=None, stream=None, out_fmt=None)
+    gemm_f16_splitk_bt(A, Bt, C, workspace=None, stream=None)
+    splitk_plan_bt(kind, out_dtype, M, N, K) -> (config, splits, workspace_bytes)
 The output dtype of a GEMM is taken from C: float32, float16, or 8-bit codes
 (uint8 or torch.float8_e4m3fn: E4M3; torch.float8_e5m2, or uint8 with
 out_fmt=FMT_E5M2: E5M2). FP8 operands are uint8 codes or torch float8 tensors.
@@ -120,6 +123,13 @@ def lib() -> ctypes.CDLL:
     L.quantize_fp8_transposed.argtypes = [vp, i64, i64, vp, vp, vp]
     L.gemm_select_config_bt.restype = i32
     L.gemm_select_config_bt.argtypes = [i32, i32, i64, i64, i64, ctypes.c_char_p, i32]
+    L.gemm_fp8_splitk_bt.restype = i32
+    L.gemm_fp8_splitk_bt.argtypes = [vp, vp, vp, vp, vp, vp, i32, i64, i64, i64, vp, i64, vp]
+    L.gemm_f16_splitk_bt.restype = i32
+    L.gemm_f16_splitk_bt.argtypes = [vp, vp, vp, i32, i64, i64, i64, vp, i64, vp]
+    L.gemm_splitk_plan_bt.restype = i32
+    L.gemm_splitk_plan_bt.argtypes = [i32, i32, i64, i64, i64, ctypes.c_char_p, i32, ctypes.POINTER(i32),
+                                      ctypes.POINTER(i64)]
     _lib = L
     return L
 
@@ -482,3 +492,48 @@ def select_config_bt(kind: int, out_dtype: int, M: int, N: int, K: int) -> str:
     buf = ctypes.create_string_buffer(128)
     _check(lib().gemm_select_config_bt(kind, out_dtype, M, N, K, buf, len(buf)), "gemm_select_config_bt")
     return buf.value.decode()
+
+
+def splitk_plan_bt(kind: int, out_dtype: int, M: int, N: int, K: int):
+    """splitk_plan for the K-major split-K calls."""
+    buf = ctypes.create_string_buffer(64)
+    sp = ctypes.c_int(0)
+    wb = ctypes.c_int64(0)
+    _check(lib().gemm_splitk_plan_bt(kind, out_dtype, M, N, K, buf, 64, ctypes.byref(sp), ctypes.byref(wb)),
+           "gemm_splitk_plan_bt")
+    return buf.value.decode(), sp.value, wb.value
+
+
+def _workspace_bt(kind, out, M, N, K, workspace, device):
+    if workspace is not None:
+        return workspace
+    _, _, nbytes = splitk_plan_bt(kind, out, M, N, K)
+    if nbytes == 0:
+        return None
+    return _torch().empty(nbytes, dtype=_torch().uint8, device=device)
+
+
+def gemm_fp8_splitk_bt(A, Bt, sA, sB, C, sOut=None, workspace=None, stream=None, out_fmt=None):
+    """gemm_fp8_scaled_bt that splits K over a workspace for mid-M shapes;
+    workspace=None allocates one of the planned size."""
+    A, Bt = _u8(A), _u8(Bt)
+    out = _out_dtype(C, out_fmt)
+    Cv = _u8(C) if out in (OUT_E4M3, OUT_E5M2) else C
+    M, N, K = _dims_bt(A, Bt, Cv)
+    ws, nbytes = _ws_args(_workspace_bt(KIND_FP8, out, M, N, K, workspace, C.device))
+    _check(lib().gemm_fp8_splitk_bt(_ptr(A), _ptr(Bt), _ptr(sA), _ptr(sB), _ptr(sOut), _ptr(Cv), out, M, N, K, ws,
+                                    nbytes, _stream_handle(stream)), "gemm_fp8_splitk_bt")
+    return C
+
+
+def gemm_f16_splitk_bt(A, Bt, C, workspace=None, stream=None):
+    """gemm_f16_bt that splits K over a workspace for mid-M shapes."""
+    torch = _torch()
+    if A.dtype != torch.float16 or Bt.dtype != torch.float16:
+        raise ValueError("gemm_f16_splitk_bt takes float16 operands")
+    M, N, K = _dims_bt(A, Bt, C)
+    out = _out_dtype(C)
+    ws, nbytes = _ws_args(_workspace_bt(KIND_F16, out, M, N, K, workspace, C.device))
+    _check(lib().gemm_f16_splitk_bt(_ptr(A), _ptr(Bt), _ptr(C), out, M, N, K, ws, nbytes, _stream_handle(stream)),
+           "gemm_f16_splitk_bt")
+    return C

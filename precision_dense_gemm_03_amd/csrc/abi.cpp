@@ -81,7 +81,7 @@ int run_gemm_splitk(int kind, GemmArgs a, void* ws, int64_t ws_bytes, const void
                     const int64_t* in_bytes, int n_in) {
     if (a.M == 0 || a.N == 0 || a.K == 0 || !ws) return run_gemm(kind, a);
     if (ws_bytes < 0) return GEMM_ERR_WORKSPACE;
-    const SplitPlan p = plan_splitk(kind, a.out_dtype, a.M, a.N, a.K, a.fmt_a, a.fmt_b);
+    const SplitPlan p = plan_splitk(kind, a.out_dtype, a.M, a.N, a.K, a.fmt_a, a.fmt_b, a.b_kmajor);
     if (!p.cfg) return GEMM_ERR_UNSUPPORTED;
     const int64_t need = splitk_bytes(p, a.M, a.N);
     if (need == 0) return run_gemm(kind, a);
@@ -183,8 +183,17 @@ int gemm_fp8_splitk(const uint8_t* A, int fmt_a, const uint8_t* B, int fmt_b, co
                            workspace_bytes);
 }
 
-int gemm_f16_splitk(const void* A, const void* B, void* C, int out_dtype, int64_t M, int64_t N, int64_t K,
-                    void* workspace, int64_t workspace_bytes, hipStream_t stream) {
+int gemm_fp8_splitk_bt(const uint8_t* A, const uint8_t* Bt, const float* sA, const float* sB, const float* sOut,
+                       void* C, int out_dtype, int64_t M, int64_t N, int64_t K, void* workspace,
+                       int64_t workspace_bytes, hipStream_t stream) {
+    return gemm_fp8_common(A, GEMM_FMT_E4M3, Bt, GEMM_FMT_E4M3, sA, sB, sOut, C, out_dtype, M, N, K, stream, 0,
+                           workspace, workspace_bytes, 1);
+}
+
+// gemm_f16_splitk and gemm_f16_splitk_bt.
+static int gemm_f16_splitk_common(const void* A, const void* B, void* C, int out_dtype, int64_t M, int64_t N,
+                                  int64_t K, void* workspace, int64_t workspace_bytes, hipStream_t stream,
+                                  int b_kmajor) {
     if (out_dtype != GEMM_OUT_F32 && out_dtype != GEMM_OUT_F16) return GEMM_ERR_DTYPE;
     if (!dim_ok(M) || !dim_ok(N) || !dim_ok(K)) return GEMM_ERR_DIM;
     if (M > 0 && N > 0) {
@@ -194,9 +203,20 @@ int gemm_f16_splitk(const void* A, const void* B, void* C, int out_dtype, int64_
         if (K > 0 && (overlaps(C, cbytes, A, M * K * 2) || overlaps(C, cbytes, B, K * N * 2))) return GEMM_ERR_ALIAS;
     }
     GemmArgs a{A, B, C, nullptr, nullptr, nullptr, out_dtype, M, N, K, stream};
+    a.b_kmajor = b_kmajor;
     const void* in_ptr[3] = {A, B, C};
     const int64_t in_bytes[3] = {M * K * 2, K * N * 2, M * N * out_size(out_dtype)};
     return run_gemm_splitk(KIND_F16, a, workspace, workspace_bytes, in_ptr, in_bytes, 3);
+}
+
+int gemm_f16_splitk(const void* A, const void* B, void* C, int out_dtype, int64_t M, int64_t N, int64_t K,
+                    void* workspace, int64_t workspace_bytes, hipStream_t stream) {
+    return gemm_f16_splitk_common(A, B, C, out_dtype, M, N, K, workspace, workspace_bytes, stream, 0);
+}
+
+int gemm_f16_splitk_bt(const void* A, const void* Bt, void* C, int out_dtype, int64_t M, int64_t N, int64_t K,
+                       void* workspace, int64_t workspace_bytes, hipStream_t stream) {
+    return gemm_f16_splitk_common(A, Bt, C, out_dtype, M, N, K, workspace, workspace_bytes, stream, 1);
 }
 
 // Workspace of gemm_f16_guarded: 256 bytes of scalars (amax of A and B, s,
@@ -247,15 +267,16 @@ int gemm_f16_guarded(const float* A, const float* B, void* C, int out_dtype, int
     return run_gemm(KIND_F16, a);
 }
 
-int gemm_splitk_plan(int kind, int out_dtype, int64_t M, int64_t N, int64_t K, int fmt_a, int fmt_b, char* buf,
-                     int buflen, int* splits, int64_t* workspace_bytes) {
+// gemm_splitk_plan and gemm_splitk_plan_bt.
+static int splitk_plan_common(int kind, int out_dtype, int64_t M, int64_t N, int64_t K, int fmt_a, int fmt_b,
+                              char* buf, int buflen, int* splits, int64_t* workspace_bytes, int b_kmajor) {
     if (kind != KIND_F16 && kind != KIND_FP8) return GEMM_ERR_DTYPE;
     if (out_dtype < GEMM_OUT_F32 || out_dtype > GEMM_OUT_E5M2 || (kind == KIND_F16 && fp8_out(out_dtype)))
         return GEMM_ERR_DTYPE;
     if ((fmt_a != GEMM_FMT_E4M3 && fmt_a != GEMM_FMT_E5M2) || (fmt_b != GEMM_FMT_E4M3 && fmt_b != GEMM_FMT_E5M2))
         return GEMM_ERR_DTYPE;
     if (!dim_ok(M) || !dim_ok(N) || !dim_ok(K)) return GEMM_ERR_DIM;
-    const SplitPlan p = plan_splitk(kind, out_dtype, M, N, K, fmt_a, fmt_b);
+    const SplitPlan p = plan_splitk(kind, out_dtype, M, N, K, fmt_a, fmt_b, b_kmajor);
     if (!p.cfg) return GEMM_ERR_UNSUPPORTED;
     if (buf && buflen > 0) {
         std::strncpy(buf, p.cfg->name, (size_t)buflen - 1);
@@ -264,6 +285,17 @@ int gemm_splitk_plan(int kind, int out_dtype, int64_t M, int64_t N, int64_t K, i
     if (splits) *splits = p.splits;
     if (workspace_bytes) *workspace_bytes = splitk_bytes(p, M, N);
     return GEMM_OK;
+}
+
+int gemm_splitk_plan(int kind, int out_dtype, int64_t M, int64_t N, int64_t K, int fmt_a, int fmt_b, char* buf,
+                     int buflen, int* splits, int64_t* workspace_bytes) {
+    return splitk_plan_common(kind, out_dtype, M, N, K, fmt_a, fmt_b, buf, buflen, splits, workspace_bytes, 0);
+}
+
+int gemm_splitk_plan_bt(int kind, int out_dtype, int64_t M, int64_t N, int64_t K, char* buf, int buflen, int* splits,
+                        int64_t* workspace_bytes) {
+    return splitk_plan_common(kind, out_dtype, M, N, K, GEMM_FMT_E4M3, GEMM_FMT_E4M3, buf, buflen, splits,
+                              workspace_bytes, 1);
 }
 
 int gemm_fp8_channel(const uint8_t* A, int fmt_a, const uint8_t* B, int fmt_b, const float* sA, const float* sB,

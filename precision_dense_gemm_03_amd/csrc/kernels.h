@@ -72,7 +72,8 @@ struct SplitPlan {
     int splits;
     int64_t k_chunk;
 };
-SplitPlan plan_splitk(int kind, int out_dtype, int64_t M, int64_t N, int64_t K, int fmt_a = 0, int fmt_b = 0);
+SplitPlan plan_splitk(int kind, int out_dtype, int64_t M, int64_t N, int64_t K, int fmt_a = 0, int fmt_b = 0,
+                      int b_kmajor = 0);
 
 // C = epilogue(sum over a.splits slices of a.ws), in slice order.
 hipError_t launch_splitk_reduce(const GemmArgs& a);

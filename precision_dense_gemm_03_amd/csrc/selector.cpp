@@ -154,11 +154,14 @@ const GemmConfig* select_config(int kind, int out_dtype, int64_t M, int64_t N, i
     return tile_with(kind, 64, 0, fa, fb);
 }
 
-SplitPlan plan_splitk(int kind, int out_dtype, int64_t M, int64_t N, int64_t K, int fa, int fb) {
+SplitPlan plan_splitk(int kind, int out_dtype, int64_t M, int64_t N, int64_t K, int fa, int fb, int bt) {
     if (kind == KIND_F16) fa = fb = 0;
-    SplitPlan p{select_config(kind, out_dtype, M, N, K, fa, fb), 1, K};
+    SplitPlan p{select_config(kind, out_dtype, M, N, K, fa, fb, bt), 1, K};
     const GemmConfig* c = p.cfg;
     if (!c || M <= 0 || N <= 0 || K <= 0 || M > kSplitMaxM) return p;
+    // K-major B: decode shapes keep their dot-product kernels (each weight
+    // row read once, no partial sums); larger M splits like row-major B.
+    if (bt && c->family == 3) return p;
     if (c->family == 1 && !std::getenv("LIBGEMM_CONFIG")) {
         // Decode shapes split over 64x64 MFMA tiles (two launches, measured
         // against the streaming kernels' own split: FP8 N = K = 4096 M = 1

@@ -345,3 +345,26 @@ def test_kmajor_selector():
     assert not g.select_config(g.KIND_FP8, g.OUT_F32, 4096, 4096, 4096).endswith("_bt")
     assert g.select_config(g.KIND_F16, g.OUT_F16, 1, 12288, 4096).startswith("stream_")
     assert g.select_config(g.KIND_FP8, g.OUT_F32, 3000, 4096, 4096) == "tile_fp8_128x128x128_w2x2"
+
+
+def test_kmajor_splitk_plan_and_validation():
+    """K-major split-K: decode shapes keep the decode kernels (no split), mid-M
+    shapes split like row-major B; workspace errors come before any launch."""
+    assert g.splitk_plan_bt(g.KIND_FP8, g.OUT_E4M3, 1, 4096, 4096) == ("gemv_bt_fp8_m1_r4_u4", 1, 0)
+    assert g.splitk_plan_bt(g.KIND_F16, g.OUT_F16, 4, 12288, 4096) == ("gemv_bt_f16_m4_r4_u2", 1, 0)
+    cfg, splits, nbytes = g.splitk_plan_bt(g.KIND_FP8, g.OUT_E4M3, 65, 4096, 4096)
+    assert cfg == "tile_fp8_64x64x128_w2x2_bt" and splits > 1 and nbytes == splits * 65 * 4096 * 4
+    cfg, splits, nbytes = g.splitk_plan_bt(g.KIND_F16, g.OUT_F16, 16, 12288, 4096)
+    assert cfg == "tile_f16_64x64x64_w2x2_bt" and splits > 1 and nbytes == splits * 16 * 12288 * 4
+    assert g.splitk_plan_bt(g.KIND_FP8, g.OUT_F32, 300, 4096, 4096)[1] == 1
+    L = g.lib()
+    s = 6 << 40          # scales well away from C (C here spans MB)
+    ws = 5 << 40
+    # gemm_fp8_splitk_bt(A, Bt, sA, sB, sOut, C, out, M, N, K, ws, bytes, stream)
+    assert L.gemm_fp8_splitk_bt(FAKE, FAKE2, s, s + 4, None, FAKE3, 2, 65, 4096, 4096, ws, 1 << 30, None) == -4
+    assert L.gemm_fp8_splitk_bt(FAKE, FAKE2, s, s + 4, None, FAKE3, 0, 65, 4096, 4096, ws, 16, None) == -9
+    assert L.gemm_fp8_splitk_bt(FAKE, FAKE2, s, s + 4, None, FAKE3, 0, 65, 4096, 4096, ws + 4, 1 << 30, None) == -9
+    assert L.gemm_fp8_splitk_bt(FAKE, FAKE2, s, s + 4, None, FAKE3, 0, 65, 4096, 4096, FAKE2, 1 << 30, None) == -8
+    # gemm_f16_splitk_bt(A, Bt, C, out, M, N, K, ws, bytes, stream)
+    assert L.gemm_f16_splitk_bt(FAKE, FAKE2, FAKE3, 2, 16, 12288, 4096, ws, 1 << 30, None) == -3
+    assert L.gemm_f16_splitk_bt(FAKE, FAKE2, FAKE3, 1, 16, 12288, 4096, ws, 1024, None) == -9

@@ -391,3 +391,62 @@ def test_gemv_bt_config_parity(cfg, kind, bound, monkeypatch):
                     s_out = orc.scale_from_amax(np.float32(np.max(np.abs(R * float(sa) * float(sb)))))
                     check_e4m3(run_fp8_bt(ta, tbt, scalar(sa), scalar(sb), g.OUT_E4M3, s_out), R, S, sa, sb, s_out,
                                what=f"{cfg} e4m3 {M}x{N}x{K}")
+
+
+# ------------------------------------------------------------ K-major split-K
+
+@pytest.mark.parametrize("M", [9, 63, 65, 129, 256])
+def test_fp8_splitk_bt_C4_shapes(M):
+    """Split-K over K-major B at the M-sweep shapes (N = K = 4096, E4M3 output
+    with its own scale, the sweep's outlier inputs), against the oracle; a
+    second call must give the same bits (slices are added in range order)."""
+    w = next((x for x in wl.C4 if x.M == M), None)
+    xa = wl.operand(w, 0) if w else wl.normal_with_outliers_f32((M, 4096), 900 + M)
+    xb = wl.operand(w, 1) if w else wl.normal_with_outliers_f32((4096, 4096), 901)
+    say(f"gemm_fp8_splitk_bt M={M}")
+    qa, sa, qbt, sb, oqa, osa, oqb, osb = fp8_chain_bt(xa, xb)
+    cfg, splits, nbytes = g.splitk_plan_bt(g.KIND_FP8, g.OUT_E4M3, M, 4096, 4096)
+    assert splits > 1, (cfg, splits)
+    R, S = orc.gemm(orc.FMT_E4M3, oqa, oqb)
+    s_out = orc.scale_from_amax(np.float32(np.max(np.abs(R * float(osa) * float(osb)))))
+    ws = torch.empty(nbytes, dtype=torch.uint8, device=DEV)
+    outs = []
+    for _ in range(2):
+        C = torch.empty((M, 4096), dtype=torch.uint8, device=DEV)
+        g.gemm_fp8_splitk_bt(qa, qbt, sa, sb, C, scalar(s_out), workspace=ws)
+        outs.append(host(C))
+    assert np.array_equal(outs[0], outs[1])
+    check_e4m3(outs[0], R, S, osa, osb, s_out, what=f"splitk bt M={M}")
+    C = torch.empty((M, 4096), dtype=torch.float32, device=DEV)
+    g.gemm_fp8_splitk_bt(qa, qbt, sa, sb, C, workspace=ws)
+    check_f32(host(C), R, S, osa, osb, what=f"splitk bt f32 M={M}")
+
+
+@pytest.mark.parametrize("M", [9, 16, 64, 100])
+def test_f16_splitk_bt_decode_weight(M):
+    """Split-K over the K-major FP16 weight [4096,12288] for M past the decode
+    kernels' bound, F16 and F32 outputs, against the oracle."""
+    say(f"gemm_f16_splitk_bt M={M}")
+    a16 = wl.random_normal_f32((M, 4096), 950 + M).astype(np.float16)
+    b16 = (wl.random_normal_f32((4096, 12288), 951) * np.float32(0.02)).astype(np.float16)
+    cfg, splits, nbytes = g.splitk_plan_bt(g.KIND_F16, g.OUT_F16, M, 12288, 4096)
+    assert splits > 1, (cfg, splits)
+    R, S = orc.gemm(orc.FMT_F16, a16.view(np.uint16), b16.view(np.uint16))
+    ta, tbt = dev(a16), dev(b16.T)
+    for out, dt, chk in ((g.OUT_F16, torch.float16, check_f16), (g.OUT_F32, torch.float32, check_f32)):
+        C = torch.empty((M, 12288), dtype=dt, device=DEV)
+        g.gemm_f16_splitk_bt(ta, tbt, C)
+        chk(host(C), R, S, what=f"f16 splitk bt M={M}")
+
+
+def test_splitk_bt_decode_shapes_do_not_split():
+    """M <= 8 with a workspace runs the decode kernel (the plan does not split)."""
+    say("gemm_fp8_splitk_bt M=1 with a workspace")
+    ca = wl.random_e4m3_codes((1, 4096), 5)
+    cb = wl.random_e4m3_codes((4096, 1000), 6)
+    assert g.splitk_plan_bt(g.KIND_FP8, g.OUT_F32, 1, 1000, 4096)[1] == 1
+    ws = torch.empty(1 << 20, dtype=torch.uint8, device=DEV)
+    C = torch.empty((1, 1000), dtype=torch.float32, device=DEV)
+    g.gemm_fp8_splitk_bt(dev(ca), dev(cb.T), scalar(1.0), scalar(1.0), C, workspace=ws)
+    R, S = orc.gemm(orc.FMT_E4M3, ca, cb)
+    check_f32(host(C), R, S, 1.0, 1.0, what="splitk bt decode")
