@@ -298,6 +298,38 @@ def main():
         rows["decode_m1" + sfx] = {
             "gbs": dec_bytes / ms_dec / 1e6, "pct_hbm": 100 * dec_bytes / ms_dec / 1e6 / PEAK_HBM_GBS,
             "us": ms_dec * 1e3, "cold": "B rotated over 6 copies (604 MB)", "config": seld, "b_layout": lay}
+    # The decode config's other sizes (M = 4; M = 16 through split-K) and the
+    # E4M3 M = 1 decode of the M-sweep config, all on K-major weights rotated
+    # so that the Infinity Cache cannot serve them.
+    for wx in wl.C3[1:]:
+        ax = to(wl.operand(wx, 0))
+        cx = torch.empty((wx.M, wx.N), dtype=torch.float16, device=dev)
+        plan = g.splitk_plan_bt(g.KIND_F16, g.OUT_F16, wx.M, wx.N, wx.K)
+        wsx = torch.empty(plan[2], dtype=torch.uint8, device=dev) if plan[1] > 1 else None
+
+        def dec_x(ax=ax, cx=cx, wsx=wsx):
+            g.gemm_f16_splitk_bt(ax, dbt_copies[rot[0] % len(dbt_copies)], cx, workspace=wsx)
+            rot[0] += 1
+        ms_x = time_launches(torch, dec_x, reps * 2)
+        bytes_x = 2.0 * (wx.M * wx.K + wx.K * wx.N + wx.M * wx.N)
+        rows[f"decode_m{wx.M}_bt"] = {"gbs": bytes_x / ms_x / 1e6, "pct_hbm": 100 * bytes_x / ms_x / 1e6 / PEAK_HBM_GBS,
+                                      "us": ms_x * 1e3, "config": plan[0], "splits": plan[1], "b_layout": "kmajor"}
+        del ax, cx, wsx
+    wq = wl.C4[0]
+    q_copies = [torch.empty((wq.N, wq.K), dtype=torch.uint8, device=dev) for _ in range(32)]
+    for q in q_copies:
+        q.copy_(qbt)
+    a1, c1 = qa[:1], torch.empty((1, wq.N), dtype=torch.uint8, device=dev)
+
+    def fp8_dec():
+        g.gemm_fp8_scaled_bt(a1, q_copies[rot[0] % len(q_copies)], s_a, s_b, c1, s_out)
+        rot[0] += 1
+    ms_q = time_launches(torch, fp8_dec, reps * 2)
+    bytes_q = 1.0 * (wq.K + wq.K * wq.N + wq.N)
+    rows["fp8_decode_m1_bt"] = {"gbs": bytes_q / ms_q / 1e6, "pct_hbm": 100 * bytes_q / ms_q / 1e6 / PEAK_HBM_GBS,
+                                "us": ms_q * 1e3, "config": g.select_config_bt(g.KIND_FP8, g.OUT_E4M3, 1, wq.N, wq.K),
+                                "cold": "B rotated over 32 copies (537 MB)", "b_layout": "kmajor"}
+    del q_copies
     ms_amax = time_launches(torch, lambda: g.amax_f32(xa, amax_a, s_a), reps)
     ms_quant = time_launches(torch, lambda: g.quantize_fp8(xa, s_a, qa), reps)
     ms_quant_t = time_launches(torch, lambda: g.quantize_fp8_transposed(xb, s_b, qbt), reps)

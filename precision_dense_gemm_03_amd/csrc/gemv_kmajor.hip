@@ -80,8 +80,9 @@ __global__ __launch_bounds__(NT) void gemv_kmajor_kernel(const uint8_t* __restri
                                                                int vec, int eflags) {
     constexpr int VE = 16 / ES;
     const int lane = threadIdx.x & 63;
-    const int n0 = (blockIdx.x * (NT / 64) + (threadIdx.x >> 6)) * R;
-    if (n0 >= N) return;  // the whole wave leaves together
+    const int64_t n0l = ((int64_t)blockIdx.x * (NT / 64) + (threadIdx.x >> 6)) * R;
+    if (n0l >= N) return;  // the whole wave leaves together
+    const int n0 = (int)n0l;
 
     float acc[MMAX][R];
 #pragma unroll
@@ -92,7 +93,7 @@ __global__ __launch_bounds__(NT) void gemv_kmajor_kernel(const uint8_t* __restri
     // Rows past N re-read row N-1 (valid addresses; never stored).
     const uint8_t* brow[R];
 #pragma unroll
-    for (int r = 0; r < R; ++r) brow[r] = B + (int64_t)min(n0 + r, N - 1) * K * ES;
+    for (int r = 0; r < R; ++r) brow[r] = B + min((int64_t)n0 + r, (int64_t)N - 1) * K * ES;
 
     // Whole 16-byte chunks of a row (vector path: aligned bases, K*ES % 16 == 0).
     const int64_t nchunks = vec ? K / VE : 0;
@@ -152,7 +153,7 @@ __global__ __launch_bounds__(NT) void gemv_kmajor_kernel(const uint8_t* __restri
     for (int m = 0; m < MMAX; ++m)
 #pragma unroll
         for (int r = 0; r < R; ++r) {
-            const int n = n0 + r;
+            const int64_t n = (int64_t)n0 + r;
             if (lane == m * R + r && m < M && n < N) {
                 float y = acc[m][r] * scale;
                 if (channel) y *= sA[m] * sB[n];
@@ -176,7 +177,7 @@ __global__ __launch_bounds__(64 * W) void gemv_kmajor_coop_kernel(const uint8_t*
     constexpr int VE = 16 / ES;
     __shared__ float red[W][MMAX * R];
     const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-    const int n0 = blockIdx.x * R;
+    const int n0 = (int)((int64_t)blockIdx.x * R);  // < N: the grid has ceil(N / R) blocks
 
     float acc[MMAX][R];
 #pragma unroll
@@ -185,7 +186,7 @@ __global__ __launch_bounds__(64 * W) void gemv_kmajor_coop_kernel(const uint8_t*
         for (int r = 0; r < R; ++r) acc[m][r] = 0.0f;
     const uint8_t* brow[R];
 #pragma unroll
-    for (int r = 0; r < R; ++r) brow[r] = B + (int64_t)min(n0 + r, N - 1) * K * ES;
+    for (int r = 0; r < R; ++r) brow[r] = B + min((int64_t)n0 + r, (int64_t)N - 1) * K * ES;
 
     const int64_t nchunks = vec ? K / VE : 0;
     for (int64_t c = wave * 64 + lane; c < nchunks; c += 64 * W) {
@@ -227,7 +228,8 @@ __global__ __launch_bounds__(64 * W) void gemv_kmajor_coop_kernel(const uint8_t*
     const bool channel = (eflags & EPI_CHANNEL) != 0;
     const float scale = epilogue_base(sA, sB, sOut, out_dtype == OUT_E4M3 || out_dtype == OUT_E5M2, channel);
     for (int o = threadIdx.x; o < MMAX * R; o += 64 * W) {
-        const int m = o / R, r = o % R, n = n0 + r;
+        const int m = o / R, r = o % R;
+        const int64_t n = (int64_t)n0 + r;
         float sum = red[0][o];
 #pragma unroll
         for (int w = 1; w < W; ++w) sum += red[w][o];
@@ -281,8 +283,11 @@ hipError_t launch_gemv_kmajor(const GemmArgs& a) {
 // Measured on MI355X (weights rotated over enough copies to miss the 256 MB
 // Infinity Cache; us): FP16 [M,4096] x [4096,12288]: M = 1 cooperative 4 rows
 // x 8 waves 16.1-16.5 (6.2 TB/s) vs per-wave 4 rows x 4 chunks 18.3, 3 x 4
-// 17.5, cooperative 16 waves 21.1; M = 4 per-wave 26.6 vs cooperative 31.3;
-// M = 8 per-wave 37.4 vs cooperative 56.1 and the 64x64 MFMA tile 53.4.
+// 17.5, cooperative 16 waves 21.1; M = 4 per-wave 2 rows x 4 chunks 24.7, 4 x
+// 2 26.6, 4 x 4 25.5, 8 x 2 35.6, cooperative 31.1; M = 8 per-wave 4 x 2 35.7,
+// 2 x 2 37.5, cooperative 56.1, the 64x64 MFMA tile 53.4. At M = 16 every
+// variant tried (57-87) lost to the 64x64 tile (53.4) and to split-K over it
+// (22.9), so decode kernels stop at M = 8.
 // E4M3 [M,4096] x [4096,4096]: M = 1 10.0 for every variant tried (launch and
 // latency bound at 16 MB); M = 4 cooperative 10.4 vs per-wave 14.8; M = 8
 // cooperative 14.7 vs per-wave 16.5 and the 64x64 tile 28.9.
@@ -292,8 +297,10 @@ const GemmConfig* gemv_kmajor_configs(int* count) {
     static const GemmConfig table[] = {
         {"gemv_coop_f16_m1_r4_w8", KIND_F16, 3, 1, 4, 8, launch_gemv_kmajor_coop<2, 1, 4, 8>, 0, 0, 1},
         {"gemv_bt_f16_m1_r4_u4", KIND_F16, 3, 1, 16, 4, launch_gemv_kmajor<2, 1, 4, 4>, 0, 0, 1},
+        {"gemv_bt_f16_m4_r2_u4", KIND_F16, 3, 4, 8, 4, launch_gemv_kmajor<2, 4, 2, 4>, 0, 0, 1},
         {"gemv_bt_f16_m4_r4_u2", KIND_F16, 3, 4, 16, 2, launch_gemv_kmajor<2, 4, 4, 2>, 0, 0, 1},
         {"gemv_coop_f16_m4_r2_w8", KIND_F16, 3, 4, 2, 8, launch_gemv_kmajor_coop<2, 4, 2, 8>, 0, 0, 1},
+        {"gemv_bt_f16_m8_r4_u2", KIND_F16, 3, 8, 16, 2, launch_gemv_kmajor<2, 8, 4, 2>, 0, 0, 1},
         {"gemv_bt_f16_m8_r2_u2", KIND_F16, 3, 8, 8, 2, launch_gemv_kmajor<2, 8, 2, 2>, 0, 0, 1},
         {"gemv_bt_fp8_m1_r4_u4", KIND_FP8, 3, 1, 16, 4, launch_gemv_kmajor<1, 1, 4, 4>, 0, 0, 1},
         {"gemv_coop_fp8_m1_r4_w4", KIND_FP8, 3, 1, 4, 4, launch_gemv_kmajor_coop<1, 1, 4, 4>, 0, 0, 1},

@@ -329,9 +329,9 @@ def test_kmajor_selector():
     larger M the K-major tile kernels, by the tile rules of row-major B (a
     256x256 grid already from 3/4 of the CUs)."""
     assert g.select_config_bt(g.KIND_F16, g.OUT_F16, 1, 12288, 4096) == "gemv_coop_f16_m1_r4_w8"
-    assert g.select_config_bt(g.KIND_F16, g.OUT_F16, 2, 12288, 4096) == "gemv_bt_f16_m4_r4_u2"
-    assert g.select_config_bt(g.KIND_F16, g.OUT_F16, 4, 12288, 4096) == "gemv_bt_f16_m4_r4_u2"
-    assert g.select_config_bt(g.KIND_F16, g.OUT_F16, 8, 12288, 4096) == "gemv_bt_f16_m8_r2_u2"
+    assert g.select_config_bt(g.KIND_F16, g.OUT_F16, 2, 12288, 4096) == "gemv_bt_f16_m4_r2_u4"
+    assert g.select_config_bt(g.KIND_F16, g.OUT_F16, 4, 12288, 4096) == "gemv_bt_f16_m4_r2_u4"
+    assert g.select_config_bt(g.KIND_F16, g.OUT_F16, 8, 12288, 4096) == "gemv_bt_f16_m8_r4_u2"
     assert g.select_config_bt(g.KIND_F16, g.OUT_F16, 9, 12288, 4096) == "tile_f16_64x64x64_w2x2_bt"
     assert g.select_config_bt(g.KIND_FP8, g.OUT_E4M3, 1, 4096, 4096) == "gemv_bt_fp8_m1_r4_u4"
     assert g.select_config_bt(g.KIND_FP8, g.OUT_E4M3, 3, 4096, 4096) == "gemv_coop_fp8_m4_r4_w4"
@@ -351,7 +351,7 @@ def test_kmajor_splitk_plan_and_validation():
     """K-major split-K: decode shapes keep the decode kernels (no split), mid-M
     shapes split like row-major B; workspace errors come before any launch."""
     assert g.splitk_plan_bt(g.KIND_FP8, g.OUT_E4M3, 1, 4096, 4096) == ("gemv_bt_fp8_m1_r4_u4", 1, 0)
-    assert g.splitk_plan_bt(g.KIND_F16, g.OUT_F16, 4, 12288, 4096) == ("gemv_bt_f16_m4_r4_u2", 1, 0)
+    assert g.splitk_plan_bt(g.KIND_F16, g.OUT_F16, 4, 12288, 4096) == ("gemv_bt_f16_m4_r2_u4", 1, 0)
     cfg, splits, nbytes = g.splitk_plan_bt(g.KIND_FP8, g.OUT_E4M3, 65, 4096, 4096)
     assert cfg == "tile_fp8_64x64x128_w2x2_bt" and splits > 1 and nbytes == splits * 65 * 4096 * 4
     cfg, splits, nbytes = g.splitk_plan_bt(g.KIND_F16, g.OUT_F16, 16, 12288, 4096)
