@@ -60,11 +60,11 @@ constexpr bool kMfmaPrio = BT;
 // K-major kernels keep A and B rows unpadded (128 bytes) with chunk c of row r
 // in slot c ^ ((r >> 1) & 7): the 16 lanes an LDS pass serves (16 consecutive
 // rows at one chunk for operand reads, two rows of 8 chunks for the stores)
-// then cover all 16 four-bank groups of the 64 banks. Counters on MI355X: the
-// FP16 kernel's bank-conflict cycles fall from 12.6 M to 0 per 4096^3 launch
-// (LDS-active cycles 33.6 M -> 21.0 M, run time about 1 % lower); the FP8
-// kernel, whose operand is two adjacent chunks per lane, keeps its conflict
-// rate (about 3 cycles per LDS instruction) and its run time.
+// then cover all 16 four-bank groups of the 64 banks. Counters on MI355X, per
+// 4096^3 launch: FP16 bank-conflict cycles 12.6 M -> 0 (LDS-active 33.6 M ->
+// 21.0 M, run time about 1 % lower); FP8, with each lane's operand split over
+// chunks g and g + 4 (rd below), 6.3 M -> 0 (LDS-active 16.8 M -> 10.5 M, run
+// time 1-2 % lower).
 constexpr bool kSwizzleBT = true;
 
 // BT: B is stored K-major, as Bt[N,K] row-major (the layout of a linear
@@ -353,8 +353,14 @@ __global__ __launch_bounds__(64 * WM * WN) void gemm_tile_kernel(
         if constexpr (T::SWZ) {
             const int q = off >> 4;
             if constexpr (ES == 1) {
-                const v4i lo = *(const LDS_AS v4i*)(rowp + ((q ^ rsw) << 4));
-                const v4i hi = *(const LDS_AS v4i*)(rowp + (((q + 1) ^ rsw) << 4));
+                // The 32 codes of k-group g are chunks g and g + 4 of the row
+                // (A and B alike, so the sum over k is unchanged; every aligned
+                // group of 8 k the FP8 matrix cores add together is still 8
+                // consecutive k). Two adjacent chunks per lane left about 3
+                // bank-conflict cycles per LDS read; this split leaves none.
+                const int q0 = q >> 1;
+                const v4i lo = *(const LDS_AS v4i*)(rowp + ((q0 ^ rsw) << 4));
+                const v4i hi = *(const LDS_AS v4i*)(rowp + (((q0 + 4) ^ rsw) << 4));
                 return __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
             } else {
                 return __builtin_bit_cast(v8h, *(const LDS_AS v4u*)(rowp + ((q ^ rsw) << 4)));

@@ -266,17 +266,24 @@ def test_gemm_fp8_bt_C5_sampled():
     check_f16(got, R, S, osa, osb, what=w.name)
 
 
-def test_gemm_fp8_bt_matches_row_major_tile_bitwise():
-    say("gemm_fp8_scaled_bt vs gemm_fp8_scaled, 4096^3")
-    ca = dev(wl.random_e4m3_codes((4096, 4096), 1))
-    cb = dev(wl.random_e4m3_codes((4096, 4096), 2))
-    s = scalar(0.5)
-    c1 = torch.empty(4096, 4096, device=DEV, dtype=torch.float32)
-    c2 = torch.empty_like(c1)
-    g.gemm_fp8_scaled(ca, cb, s, s, c1)
-    g.gemm_fp8_scaled_bt(ca, cb.t().contiguous(), s, s, c2)
-    torch.cuda.synchronize()
-    assert torch.equal(c1, c2)
+def test_gemm_fp8_bt_4096_against_oracle_and_deterministic():
+    """The K-major FP8 tile kernel at 4096^3 on full-range codes: sampled rows
+    within the FP32 bound plus the FP8 matrix-core allowance, and two launches
+    bit-identical. (It takes each lane's 32 codes as two 16-code pieces of the
+    row, A and B alike, so its sum order differs from the row-major kernel's.)"""
+    say("gemm_fp8_scaled_bt 4096^3 vs oracle, twice")
+    ca = wl.random_e4m3_codes((4096, 4096), 1)
+    cb = wl.random_e4m3_codes((4096, 4096), 2)
+    ta, tbt, s = dev(ca), dev(cb.T), scalar(0.5)
+    outs = []
+    for _ in range(2):
+        c = torch.empty(4096, 4096, device=DEV, dtype=torch.float32)
+        g.gemm_fp8_scaled_bt(ta, tbt, s, s, c)
+        outs.append(host(c))
+    assert np.array_equal(outs[0], outs[1])
+    rows = sample_rows(4096, 12)
+    R, S = orc.gemm(orc.FMT_E4M3, ca, cb, rows=rows)
+    check_f32(outs[0][rows], R, S, 0.5, 0.5, what="fp8 bt 4096^3", T=fp8_dot_allowance(ca, cb, rows=rows))
 
 
 # ----------------------------------------- every K-major configuration forced
