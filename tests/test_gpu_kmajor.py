@@ -463,3 +463,20 @@ def test_splitk_bt_decode_shapes_do_not_split():
     g.gemm_fp8_splitk_bt(dev(ca), dev(cb.T), scalar(1.0), scalar(1.0), C, workspace=ws)
     R, S = orc.gemm(orc.FMT_E4M3, ca, cb)
     check_f32(host(C), R, S, 1.0, 1.0, what="splitk bt decode")
+
+
+@pytest.mark.parametrize("M,N,K", [(9, 1, 100), (70, 5, 256), (130, 17, 4096), (300, 1, 512)])
+def test_tile_bt_narrow_n(M, N, K):
+    """K-major tile kernels with fewer output columns than one tile row of B:
+    every Bt row past N is clamped to row N-1 and never stored."""
+    say(f"tile bt narrow N {M}x{N}x{K}")
+    a16 = wl.random_f16((M, K), 3 * M + N)
+    b16 = wl.random_f16((K, N), 5 * N + K)
+    assert g.select_config_bt(g.KIND_F16, g.OUT_F32, M, N, K).startswith("tile_")
+    R, S = orc.gemm(orc.FMT_F16, a16.view(np.uint16), b16.view(np.uint16))
+    check_f32(run_f16_bt(a16, b16, g.OUT_F32), R, S, what=f"f16 bt {M}x{N}x{K}")
+    ca = wl.random_e4m3_codes((M, K), 7 * M + N)
+    cb = wl.random_e4m3_codes((K, N), 11 * N + K)
+    R, S = orc.gemm(orc.FMT_E4M3, ca, cb)
+    check_f32(run_fp8_bt(dev(ca), dev(cb.T), scalar(0.25), scalar(2.0), g.OUT_F32), R, S, 0.25, 2.0,
+              what=f"fp8 bt {M}x{N}x{K}", T=fp8_dot_allowance(ca, cb))
