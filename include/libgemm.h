@@ -368,6 +368,23 @@ int gemm_fp8_scaled_bt(const uint8_t* A, const uint8_t* Bt, const float* sA, con
 int quantize_fp8_transposed(const float* x, int64_t rows, int64_t cols, const float* scale,
                             uint8_t* q, hipStream_t stream);
 
+/*
+ * gemm_fp8_fmt_bt — gemm_fp8_fmt (A in FP8 format fmt_a, B in fmt_b: E4M3 or
+ * E5M2, P2 §2.1) with B given as Bt[N,K] codes, row-major. Arguments, element
+ * value, outputs and errors as gemm_fp8_fmt.
+ */
+int gemm_fp8_fmt_bt(const uint8_t* A, int fmt_a, const uint8_t* Bt, int fmt_b,
+                    const float* sA, const float* sB, const float* sOut, void* C, int out_dtype,
+                    int64_t M, int64_t N, int64_t K, hipStream_t stream);
+
+/*
+ * quantize_fp8_transposed_fmt — quantize_fp8_transposed into FP8 format fmt
+ * (E4M3 as quantize_fp8, E5M2 as quantize_fp8_fmt: saturate at +-57344, P2
+ * §4.3). Unknown fmt: GEMM_ERR_DTYPE; otherwise as quantize_fp8_transposed.
+ */
+int quantize_fp8_transposed_fmt(const float* x, int64_t rows, int64_t cols, const float* scale,
+                                uint8_t* q, int fmt, hipStream_t stream);
+
 /* gemm_select_config for gemm_f16_bt (kind 0) and gemm_fp8_scaled_bt (kind 1). */
 int gemm_select_config_bt(int kind, int out_dtype, int64_t M, int64_t N, int64_t K,
                           char* buf, int buflen);

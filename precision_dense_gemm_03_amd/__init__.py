@@ -27,6 +27,8 @@ Functions keep the C names:
     gemm_f16_bt(A, Bt, C, stream=None)
     gemm_fp8_scaled_bt(A, Bt, sA, sB, C, sOut=None, stream=None, out_fmt=None)
     quantize_fp8_transposed(x, scale, q=None, stream=None) -> q[cols, rows]
+    gemm_fp8_fmt_bt(A, fmt_a, Bt, fmt_b, sA, sB, C, sOut=None, stream=None, out_fmt=None)
+    quantize_fp8_transposed_fmt(x, scale, fmt, q=None, stream=None) -> q[cols, rows]
     select_config_bt(kind, out_dtype, M, N, K) -> str
     gemm_fp8_splitk_bt(A, Bt, sA, sB, C, sOut=None, workspace=None, stream=None, out_fmt=None)
     gemm_f16_splitk_bt(A, Bt, C, workspace=None, stream=None)
@@ -123,6 +125,10 @@ def lib() -> ctypes.CDLL:
     L.quantize_fp8_transposed.argtypes = [vp, i64, i64, vp, vp, vp]
     L.gemm_select_config_bt.restype = i32
     L.gemm_select_config_bt.argtypes = [i32, i32, i64, i64, i64, ctypes.c_char_p, i32]
+    L.gemm_fp8_fmt_bt.restype = i32
+    L.gemm_fp8_fmt_bt.argtypes = [vp, i32, vp, i32, vp, vp, vp, vp, i32, i64, i64, i64, vp]
+    L.quantize_fp8_transposed_fmt.restype = i32
+    L.quantize_fp8_transposed_fmt.argtypes = [vp, i64, i64, vp, vp, i32, vp]
     L.gemm_fp8_splitk_bt.restype = i32
     L.gemm_fp8_splitk_bt.argtypes = [vp, vp, vp, vp, vp, vp, i32, i64, i64, i64, vp, i64, vp]
     L.gemm_f16_splitk_bt.restype = i32
@@ -251,6 +257,33 @@ def gemm_fp8_scaled_bt(A, Bt, sA, sB, C, sOut=None, stream=None, out_fmt=None):
     _check(lib().gemm_fp8_scaled_bt(_ptr(A), _ptr(Bt), _ptr(sA), _ptr(sB), _ptr(sOut), _ptr(Cv), out, M, N, K,
                                     _stream_handle(stream)), "gemm_fp8_scaled_bt")
     return C
+
+
+def gemm_fp8_fmt_bt(A, fmt_a, Bt, fmt_b, sA, sB, C, sOut=None, stream=None, out_fmt=None):
+    """gemm_fp8_scaled_bt with A in FP8 format fmt_a and Bt in fmt_b (FMT_E4M3 / FMT_E5M2)."""
+    A, Bt = _u8(A), _u8(Bt)
+    out = _out_dtype(C, out_fmt)
+    Cv = _u8(C) if out in (OUT_E4M3, OUT_E5M2) else C
+    M, N, K = _dims_bt(A, Bt, Cv)
+    _check(lib().gemm_fp8_fmt_bt(_ptr(A), int(fmt_a), _ptr(Bt), int(fmt_b), _ptr(sA), _ptr(sB), _ptr(sOut), _ptr(Cv),
+                                 out, M, N, K, _stream_handle(stream)), "gemm_fp8_fmt_bt")
+    return C
+
+
+def quantize_fp8_transposed_fmt(x, scale, fmt, q=None, stream=None):
+    """quantize_fp8_transposed into FP8 format fmt (FMT_E4M3 / FMT_E5M2)."""
+    torch = _torch()
+    if x.dtype != torch.float32:
+        raise ValueError("quantize_fp8_transposed_fmt takes float32 input")
+    rows, cols = _rows_cols(x)
+    if q is None:
+        q = torch.empty((cols, rows), dtype=torch.uint8, device=x.device)
+    qv = _u8(q)
+    if qv.numel() != x.numel():
+        raise ValueError("q must have as many elements as x")
+    _check(lib().quantize_fp8_transposed_fmt(_ptr(x), rows, cols, _ptr(scale), _ptr(qv), int(fmt),
+                                             _stream_handle(stream)), "quantize_fp8_transposed_fmt")
+    return q
 
 
 def quantize_fp8_transposed(x, scale, q=None, stream=None):

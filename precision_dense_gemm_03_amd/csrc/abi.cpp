@@ -171,6 +171,11 @@ int gemm_fp8_scaled_bt(const uint8_t* A, const uint8_t* Bt, const float* sA, con
                            nullptr, 0, 1);
 }
 
+int gemm_fp8_fmt_bt(const uint8_t* A, int fmt_a, const uint8_t* Bt, int fmt_b, const float* sA, const float* sB,
+                    const float* sOut, void* C, int out_dtype, int64_t M, int64_t N, int64_t K, hipStream_t stream) {
+    return gemm_fp8_common(A, fmt_a, Bt, fmt_b, sA, sB, sOut, C, out_dtype, M, N, K, stream, 0, nullptr, 0, 1);
+}
+
 int gemm_fp8_fmt(const uint8_t* A, int fmt_a, const uint8_t* B, int fmt_b, const float* sA, const float* sB,
                  const float* sOut, void* C, int out_dtype, int64_t M, int64_t N, int64_t K, hipStream_t stream) {
     return gemm_fp8_common(A, fmt_a, B, fmt_b, sA, sB, sOut, C, out_dtype, M, N, K, stream);
@@ -347,8 +352,9 @@ int quantize_fp8_fmt(const float* x, int64_t n, const float* scale, uint8_t* q, 
     return status_of(launch_quantize(x, n, scale, q, fmt, stream));
 }
 
-int quantize_fp8_transposed(const float* x, int64_t rows, int64_t cols, const float* scale, uint8_t* q,
-                            hipStream_t stream) {
+int quantize_fp8_transposed_fmt(const float* x, int64_t rows, int64_t cols, const float* scale, uint8_t* q,
+                                int fmt, hipStream_t stream) {
+    if (fmt != GEMM_FMT_E4M3 && fmt != GEMM_FMT_E5M2) return GEMM_ERR_DTYPE;
     if (!dim_ok(rows) || !dim_ok(cols)) return GEMM_ERR_DIM;
     const int64_t n = rows * cols;
     if (n == 0) return GEMM_OK;
@@ -356,7 +362,12 @@ int quantize_fp8_transposed(const float* x, int64_t rows, int64_t cols, const fl
     if (overlaps(q, n, x, 4 * n) || overlaps(q, n, scale, 4)) return GEMM_ERR_ALIAS;
     const int st = check_device();
     if (st != GEMM_OK) return st;
-    return status_of(launch_quantize_transposed(x, rows, cols, scale, q, GEMM_FMT_E4M3, stream));
+    return status_of(launch_quantize_transposed(x, rows, cols, scale, q, fmt, stream));
+}
+
+int quantize_fp8_transposed(const float* x, int64_t rows, int64_t cols, const float* scale, uint8_t* q,
+                            hipStream_t stream) {
+    return quantize_fp8_transposed_fmt(x, rows, cols, scale, q, GEMM_FMT_E4M3, stream);
 }
 
 int quantize_fp8(const float* x, int64_t n, const float* scale, uint8_t* q, hipStream_t stream) {

@@ -6,10 +6,10 @@
 namespace libgemm {
 namespace tile {
 // The other FP8 operand pairs are compiled in gemm_tile_mixed.hip.
-#define LIBGEMM_TILE_EXTERN(BM, BN, BK, WM, WN)                                         \
-    extern template hipError_t launch_tile<1, BM, BN, BK, WM, WN, 0, 1>(const GemmArgs&); \
-    extern template hipError_t launch_tile<1, BM, BN, BK, WM, WN, 1, 0>(const GemmArgs&); \
-    extern template hipError_t launch_tile<1, BM, BN, BK, WM, WN, 1, 1>(const GemmArgs&);
+#define LIBGEMM_TILE_EXTERN(BM, BN, BK, WM, WN, BT)                                         \
+    extern template hipError_t launch_tile<1, BM, BN, BK, WM, WN, 0, 1, BT>(const GemmArgs&); \
+    extern template hipError_t launch_tile<1, BM, BN, BK, WM, WN, 1, 0, BT>(const GemmArgs&); \
+    extern template hipError_t launch_tile<1, BM, BN, BK, WM, WN, 1, 1, BT>(const GemmArgs&);
 LIBGEMM_TILE_MIXED_CONFIGS(LIBGEMM_TILE_EXTERN)
 #undef LIBGEMM_TILE_EXTERN
 }  // namespace tile
@@ -24,13 +24,13 @@ const GemmConfig* tile_configs(int* count) {
         {"tile_fp8_128x128x128_w2x2", KIND_FP8, 0, 128, 128, 128, tile::launch_tile_fp8_any<128, 128, 128, 2, 2>, kAllFp8Pairs, 128},
         {"tile_fp8_256x256x128_w2x4", KIND_FP8, 0, 256, 256, 128, tile::launch_tile_fp8_any<256, 256, 128, 2, 4>, kAllFp8Pairs, 128},
         {"tile_f16_256x256x64_w2x4", KIND_F16, 0, 256, 256, 64, tile::launch_tile<2, 256, 256, 64, 2, 4, 0, 0>, 0, 64},
-        // K-major B (Bt[N,K]): B staged and read like A; E4M3 x E4M3 and FP16.
+        // K-major B (Bt[N,K]): B staged and read like A; every FP8 operand pair, and FP16.
         {"tile_f16_64x64x64_w2x2_bt", KIND_F16, 0, 64, 64, 64, tile::launch_tile<2, 64, 64, 64, 2, 2, 0, 0, true>, 0, 64, 1},
         {"tile_f16_128x128x64_w2x2_bt", KIND_F16, 0, 128, 128, 64, tile::launch_tile<2, 128, 128, 64, 2, 2, 0, 0, true>, 0, 64, 1},
         {"tile_f16_256x256x64_w2x4_bt", KIND_F16, 0, 256, 256, 64, tile::launch_tile<2, 256, 256, 64, 2, 4, 0, 0, true>, 0, 64, 1},
-        {"tile_fp8_64x64x128_w2x2_bt", KIND_FP8, 0, 64, 64, 128, tile::launch_tile<1, 64, 64, 128, 2, 2, 0, 0, true>, 0, 128, 1},
-        {"tile_fp8_128x128x128_w2x2_bt", KIND_FP8, 0, 128, 128, 128, tile::launch_tile<1, 128, 128, 128, 2, 2, 0, 0, true>, 0, 128, 1},
-        {"tile_fp8_256x256x128_w2x4_bt", KIND_FP8, 0, 256, 256, 128, tile::launch_tile<1, 256, 256, 128, 2, 4, 0, 0, true>, 0, 128, 1},
+        {"tile_fp8_64x64x128_w2x2_bt", KIND_FP8, 0, 64, 64, 128, tile::launch_tile_fp8_any<64, 64, 128, 2, 2, true>, kAllFp8Pairs, 128, 1},
+        {"tile_fp8_128x128x128_w2x2_bt", KIND_FP8, 0, 128, 128, 128, tile::launch_tile_fp8_any<128, 128, 128, 2, 2, true>, kAllFp8Pairs, 128, 1},
+        {"tile_fp8_256x256x128_w2x4_bt", KIND_FP8, 0, 256, 256, 128, tile::launch_tile_fp8_any<256, 256, 128, 2, 4, true>, kAllFp8Pairs, 128, 1},
     };
     *count = (int)(sizeof(table) / sizeof(table[0]));
     return table;

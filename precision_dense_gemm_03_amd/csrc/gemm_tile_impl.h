@@ -607,9 +607,12 @@ hipError_t launch_tile_fp8_any(const GemmArgs& a) {
 }
 
 #define LIBGEMM_TILE_MIXED_CONFIGS(X) \
-    X(64, 64, 128, 2, 2)              \
-    X(128, 128, 128, 2, 2)            \
-    X(256, 256, 128, 2, 4)
+    X(64, 64, 128, 2, 2, false)       \
+    X(128, 128, 128, 2, 2, false)     \
+    X(256, 256, 128, 2, 4, false)     \
+    X(64, 64, 128, 2, 2, true)        \
+    X(128, 128, 128, 2, 2, true)      \
+    X(256, 256, 128, 2, 4, true)
 
 }  // namespace tile
 }  // namespace libgemm

@@ -5,10 +5,10 @@
 
 namespace libgemm {
 namespace tile {
-#define LIBGEMM_TILE_INSTANTIATE(BM, BN, BK, WM, WN)                             \
-    template hipError_t launch_tile<1, BM, BN, BK, WM, WN, 0, 1>(const GemmArgs&); \
-    template hipError_t launch_tile<1, BM, BN, BK, WM, WN, 1, 0>(const GemmArgs&); \
-    template hipError_t launch_tile<1, BM, BN, BK, WM, WN, 1, 1>(const GemmArgs&);
+#define LIBGEMM_TILE_INSTANTIATE(BM, BN, BK, WM, WN, BT)                             \
+    template hipError_t launch_tile<1, BM, BN, BK, WM, WN, 0, 1, BT>(const GemmArgs&); \
+    template hipError_t launch_tile<1, BM, BN, BK, WM, WN, 1, 0, BT>(const GemmArgs&); \
+    template hipError_t launch_tile<1, BM, BN, BK, WM, WN, 1, 1, BT>(const GemmArgs&);
 LIBGEMM_TILE_MIXED_CONFIGS(LIBGEMM_TILE_INSTANTIATE)
 #undef LIBGEMM_TILE_INSTANTIATE
 }  // namespace tile

@@ -35,8 +35,16 @@ namespace {
 
 typedef _Float16 v2h __attribute__((ext_vector_type(2)));
 
-// Sum over the 8 (FP16) or 16 (FP8) products of two 16-byte chunks, in FP32.
-template <int ES>
+// Two FP8 codes (the low or high half HI of a 32-bit word) as floats, format F.
+template <int F, bool HI>
+__device__ __forceinline__ auto fp8x2(uint32_t w) {
+    if constexpr (F == FMT_E5M2) return __builtin_amdgcn_cvt_pk_f32_bf8((int)w, HI);
+    else return __builtin_amdgcn_cvt_pk_f32_fp8((int)w, HI);
+}
+
+// Sum over the 8 (FP16) or 16 (FP8, formats FA and FB) products of two
+// 16-byte chunks, in FP32.
+template <int ES, int FA, int FB>
 __device__ __forceinline__ float chunk_dot(const v4u& a, const v4u& b) {
     const uint32_t wa[4] = {a.x, a.y, a.z, a.w};
     const uint32_t wb[4] = {b.x, b.y, b.z, b.w};
@@ -48,10 +56,10 @@ __device__ __forceinline__ float chunk_dot(const v4u& a, const v4u& b) {
     } else {
 #pragma unroll
         for (int q = 0; q < 4; ++q) {
-            const auto alo = __builtin_amdgcn_cvt_pk_f32_fp8((int)wa[q], false);
-            const auto ahi = __builtin_amdgcn_cvt_pk_f32_fp8((int)wa[q], true);
-            const auto blo = __builtin_amdgcn_cvt_pk_f32_fp8((int)wb[q], false);
-            const auto bhi = __builtin_amdgcn_cvt_pk_f32_fp8((int)wb[q], true);
+            const auto alo = fp8x2<FA, false>(wa[q]);
+            const auto ahi = fp8x2<FA, true>(wa[q]);
+            const auto blo = fp8x2<FB, false>(wb[q]);
+            const auto bhi = fp8x2<FB, true>(wb[q]);
             s = fmaf(alo[0], blo[0], s);
             s = fmaf(alo[1], blo[1], s);
             s = fmaf(ahi[0], bhi[0], s);
@@ -61,17 +69,17 @@ __device__ __forceinline__ float chunk_dot(const v4u& a, const v4u& b) {
     return s;
 }
 
-// One element (FP16 value or E4M3 code) as a float.
-template <int ES>
+// One element (FP16 value, or FP8 code of format F) as a float.
+template <int ES, int F>
 __device__ __forceinline__ float elem(const uint8_t* p, int64_t idx) {
     if constexpr (ES == 2) return (float)reinterpret_cast<const _Float16*>(p)[idx];
-    else return __builtin_amdgcn_cvt_pk_f32_fp8((int)(uint32_t)p[idx], false)[0];
+    else return fp8x2<F, false>((uint32_t)p[idx])[0];
 }
 
-// ES: element bytes (2 FP16, 1 E4M3). MMAX: largest M served. R: weight rows
+// ES: element bytes (2 FP16, 1 FP8). MMAX: largest M served. R: weight rows
 // per wave. U: 16-byte chunks of each row in flight per lane. NT: threads per
-// workgroup.
-template <int ES, int MMAX, int R, int U, int NT>
+// workgroup. FA, FB: FP8 formats of A and B (0 for FP16).
+template <int ES, int MMAX, int R, int U, int NT, int FA, int FB>
 __global__ __launch_bounds__(NT) void gemv_kmajor_kernel(const uint8_t* __restrict__ A,
                                                                const uint8_t* __restrict__ B, void* __restrict__ C,
                                                                int M, int N, int64_t K, const float* __restrict__ sA,
@@ -112,7 +120,7 @@ __global__ __launch_bounds__(NT) void gemv_kmajor_kernel(const uint8_t* __restri
                 if (m < M) {
                     const v4u av = *reinterpret_cast<const v4u*>(A + ((int64_t)m * K + (c + u * 64) * VE) * ES);
 #pragma unroll
-                    for (int r = 0; r < R; ++r) acc[m][r] += chunk_dot<ES>(av, bv[u][r]);
+                    for (int r = 0; r < R; ++r) acc[m][r] += chunk_dot<ES, FA, FB>(av, bv[u][r]);
                 }
             }
     }
@@ -123,7 +131,7 @@ __global__ __launch_bounds__(NT) void gemv_kmajor_kernel(const uint8_t* __restri
                 const v4u av = *reinterpret_cast<const v4u*>(A + ((int64_t)m * K + c * VE) * ES);
 #pragma unroll
                 for (int r = 0; r < R; ++r)
-                    acc[m][r] += chunk_dot<ES>(av, *reinterpret_cast<const v4u*>(brow[r] + c * 16));
+                    acc[m][r] += chunk_dot<ES, FA, FB>(av, *reinterpret_cast<const v4u*>(brow[r] + c * 16));
             }
         }
     }
@@ -132,9 +140,9 @@ __global__ __launch_bounds__(NT) void gemv_kmajor_kernel(const uint8_t* __restri
 #pragma unroll
         for (int m = 0; m < MMAX; ++m) {
             if (m < M) {
-                const float a = elem<ES>(A, (int64_t)m * K + k);
+                const float a = elem<ES, FA>(A, (int64_t)m * K + k);
 #pragma unroll
-                for (int r = 0; r < R; ++r) acc[m][r] = fmaf(a, elem<ES>(brow[r], k), acc[m][r]);
+                for (int r = 0; r < R; ++r) acc[m][r] = fmaf(a, elem<ES, FB>(brow[r], k), acc[m][r]);
             }
         }
     }
@@ -166,7 +174,7 @@ __global__ __launch_bounds__(NT) void gemv_kmajor_kernel(const uint8_t* __restri
 // weight rows together (wave w takes chunks w*64 + lane + i*64*W), so each
 // workgroup load instruction covers W KiB of one row; the per-wave sums meet
 // in LDS, added in wave order.
-template <int ES, int MMAX, int R, int W>
+template <int ES, int MMAX, int R, int W, int FA, int FB>
 __global__ __launch_bounds__(64 * W) void gemv_kmajor_coop_kernel(const uint8_t* __restrict__ A,
                                                                   const uint8_t* __restrict__ B,
                                                                   void* __restrict__ C, int M, int N, int64_t K,
@@ -198,7 +206,7 @@ __global__ __launch_bounds__(64 * W) void gemv_kmajor_coop_kernel(const uint8_t*
             if (m < M) {
                 const v4u av = *reinterpret_cast<const v4u*>(A + ((int64_t)m * K + c * VE) * ES);
 #pragma unroll
-                for (int r = 0; r < R; ++r) acc[m][r] += chunk_dot<ES>(av, bv[r]);
+                for (int r = 0; r < R; ++r) acc[m][r] += chunk_dot<ES, FA, FB>(av, bv[r]);
             }
         }
     }
@@ -206,9 +214,9 @@ __global__ __launch_bounds__(64 * W) void gemv_kmajor_coop_kernel(const uint8_t*
 #pragma unroll
         for (int m = 0; m < MMAX; ++m) {
             if (m < M) {
-                const float a = elem<ES>(A, (int64_t)m * K + k);
+                const float a = elem<ES, FA>(A, (int64_t)m * K + k);
 #pragma unroll
-                for (int r = 0; r < R; ++r) acc[m][r] = fmaf(a, elem<ES>(brow[r], k), acc[m][r]);
+                for (int r = 0; r < R; ++r) acc[m][r] = fmaf(a, elem<ES, FB>(brow[r], k), acc[m][r]);
             }
         }
     }
@@ -243,36 +251,57 @@ __global__ __launch_bounds__(64 * W) void gemv_kmajor_coop_kernel(const uint8_t*
 
 bool aligned16(const void* p) { return ((uintptr_t)p & 15u) == 0; }
 
-template <int ES, int MMAX, int R, int W>
+template <int ES, int MMAX, int R, int W, int FA = 0, int FB = 0>
 hipError_t launch_gemv_kmajor_coop(const GemmArgs& a) {
     if (a.M <= 0 || a.N <= 0) return hipSuccess;
     if (a.M > MMAX || !a.b_kmajor || a.splits > 1) return hipErrorInvalidValue;
-    if (ES == 1 && (a.fmt_a != FMT_E4M3 || a.fmt_b != FMT_E4M3)) return hipErrorInvalidValue;
+    if (ES == 1 && (a.fmt_a != FA || a.fmt_b != FB)) return hipErrorInvalidValue;
     const int64_t blocks = (a.N + R - 1) / R;
     if (blocks > 0x7FFFFFFF) return hipErrorInvalidValue;
     const int vec = aligned16(a.A) && aligned16(a.B) && ((a.K * ES) % 16 == 0);
     const int eflags = a.channel ? EPI_CHANNEL : 0;
-    gemv_kmajor_coop_kernel<ES, MMAX, R, W><<<(unsigned)blocks, 64 * W, 0, a.stream>>>(
+    gemv_kmajor_coop_kernel<ES, MMAX, R, W, FA, FB><<<(unsigned)blocks, 64 * W, 0, a.stream>>>(
         reinterpret_cast<const uint8_t*>(a.A), reinterpret_cast<const uint8_t*>(a.B), a.C, (int)a.M, (int)a.N, a.K,
         a.sA, a.sB, a.sOut, a.out_dtype, vec, eflags);
     return hipGetLastError();
 }
 
-template <int ES, int MMAX, int R, int U, int NT = 256>
+template <int ES, int MMAX, int R, int U, int NT = 256, int FA = 0, int FB = 0>
 hipError_t launch_gemv_kmajor(const GemmArgs& a) {
     static_assert(MMAX * R <= 64, "one lane stores each output");
     if (a.M <= 0 || a.N <= 0) return hipSuccess;
     if (a.M > MMAX || !a.b_kmajor || a.splits > 1) return hipErrorInvalidValue;
-    if (ES == 1 && (a.fmt_a != FMT_E4M3 || a.fmt_b != FMT_E4M3)) return hipErrorInvalidValue;
+    if (ES == 1 && (a.fmt_a != FA || a.fmt_b != FB)) return hipErrorInvalidValue;
     constexpr int rows_per_block = (NT / 64) * R;
     const int64_t blocks = (a.N + rows_per_block - 1) / rows_per_block;
     if (blocks > 0x7FFFFFFF) return hipErrorInvalidValue;
     const int vec = aligned16(a.A) && aligned16(a.B) && ((a.K * ES) % 16 == 0);
     const int eflags = a.channel ? EPI_CHANNEL : 0;
-    gemv_kmajor_kernel<ES, MMAX, R, U, NT><<<(unsigned)blocks, NT, 0, a.stream>>>(
+    gemv_kmajor_kernel<ES, MMAX, R, U, NT, FA, FB><<<(unsigned)blocks, NT, 0, a.stream>>>(
         reinterpret_cast<const uint8_t*>(a.A), reinterpret_cast<const uint8_t*>(a.B), a.C, (int)a.M, (int)a.N, a.K,
         a.sA, a.sB, a.sOut, a.out_dtype, vec, eflags);
     return hipGetLastError();
+}
+
+// FP8 operand-format dispatch (every pair of E4M3 / E5M2).
+template <int MMAX, int R, int U>
+hipError_t launch_gemv_kmajor_fp8(const GemmArgs& a) {
+    switch (a.fmt_a * 2 + a.fmt_b) {
+        case 0: return launch_gemv_kmajor<1, MMAX, R, U, 256, 0, 0>(a);
+        case 1: return launch_gemv_kmajor<1, MMAX, R, U, 256, 0, 1>(a);
+        case 2: return launch_gemv_kmajor<1, MMAX, R, U, 256, 1, 0>(a);
+        default: return launch_gemv_kmajor<1, MMAX, R, U, 256, 1, 1>(a);
+    }
+}
+
+template <int MMAX, int R, int W>
+hipError_t launch_gemv_kmajor_coop_fp8(const GemmArgs& a) {
+    switch (a.fmt_a * 2 + a.fmt_b) {
+        case 0: return launch_gemv_kmajor_coop<1, MMAX, R, W, 0, 0>(a);
+        case 1: return launch_gemv_kmajor_coop<1, MMAX, R, W, 0, 1>(a);
+        case 2: return launch_gemv_kmajor_coop<1, MMAX, R, W, 1, 0>(a);
+        default: return launch_gemv_kmajor_coop<1, MMAX, R, W, 1, 1>(a);
+    }
 }
 
 }  // namespace
@@ -302,12 +331,12 @@ const GemmConfig* gemv_kmajor_configs(int* count) {
         {"gemv_coop_f16_m4_r2_w8", KIND_F16, 3, 4, 2, 8, launch_gemv_kmajor_coop<2, 4, 2, 8>, 0, 0, 1},
         {"gemv_bt_f16_m8_r4_u2", KIND_F16, 3, 8, 16, 2, launch_gemv_kmajor<2, 8, 4, 2>, 0, 0, 1},
         {"gemv_bt_f16_m8_r2_u2", KIND_F16, 3, 8, 8, 2, launch_gemv_kmajor<2, 8, 2, 2>, 0, 0, 1},
-        {"gemv_bt_fp8_m1_r4_u4", KIND_FP8, 3, 1, 16, 4, launch_gemv_kmajor<1, 1, 4, 4>, 0, 0, 1},
-        {"gemv_coop_fp8_m1_r4_w4", KIND_FP8, 3, 1, 4, 4, launch_gemv_kmajor_coop<1, 1, 4, 4>, 0, 0, 1},
-        {"gemv_coop_fp8_m4_r4_w4", KIND_FP8, 3, 4, 4, 4, launch_gemv_kmajor_coop<1, 4, 4, 4>, 0, 0, 1},
-        {"gemv_bt_fp8_m4_r4_u2", KIND_FP8, 3, 4, 16, 2, launch_gemv_kmajor<1, 4, 4, 2>, 0, 0, 1},
-        {"gemv_coop_fp8_m8_r2_w4", KIND_FP8, 3, 8, 2, 4, launch_gemv_kmajor_coop<1, 8, 2, 4>, 0, 0, 1},
-        {"gemv_bt_fp8_m8_r2_u2", KIND_FP8, 3, 8, 8, 2, launch_gemv_kmajor<1, 8, 2, 2>, 0, 0, 1},
+        {"gemv_bt_fp8_m1_r4_u4", KIND_FP8, 3, 1, 16, 4, launch_gemv_kmajor_fp8<1, 4, 4>, kAllFp8Pairs, 0, 1},
+        {"gemv_coop_fp8_m1_r4_w4", KIND_FP8, 3, 1, 4, 4, launch_gemv_kmajor_coop_fp8<1, 4, 4>, kAllFp8Pairs, 0, 1},
+        {"gemv_coop_fp8_m4_r4_w4", KIND_FP8, 3, 4, 4, 4, launch_gemv_kmajor_coop_fp8<4, 4, 4>, kAllFp8Pairs, 0, 1},
+        {"gemv_bt_fp8_m4_r4_u2", KIND_FP8, 3, 4, 16, 2, launch_gemv_kmajor_fp8<4, 4, 2>, kAllFp8Pairs, 0, 1},
+        {"gemv_coop_fp8_m8_r2_w4", KIND_FP8, 3, 8, 2, 4, launch_gemv_kmajor_coop_fp8<8, 2, 4>, kAllFp8Pairs, 0, 1},
+        {"gemv_bt_fp8_m8_r2_u2", KIND_FP8, 3, 8, 8, 2, launch_gemv_kmajor_fp8<8, 2, 2>, kAllFp8Pairs, 0, 1},
     };
     *count = (int)(sizeof(table) / sizeof(table[0]));
     return table;

@@ -368,3 +368,16 @@ def test_kmajor_splitk_plan_and_validation():
     # gemm_f16_splitk_bt(A, Bt, C, out, M, N, K, ws, bytes, stream)
     assert L.gemm_f16_splitk_bt(FAKE, FAKE2, FAKE3, 2, 16, 12288, 4096, ws, 1 << 30, None) == -3
     assert L.gemm_f16_splitk_bt(FAKE, FAKE2, FAKE3, 1, 16, 12288, 4096, ws, 1024, None) == -9
+
+
+def test_kmajor_format_entry_points_validation():
+    L = g.lib()
+    s = 6 << 40
+    # gemm_fp8_fmt_bt(A, fa, Bt, fb, sA, sB, sOut, C, out, M, N, K, stream)
+    assert L.gemm_fp8_fmt_bt(FAKE, 2, FAKE2, 0, s, s + 4, None, FAKE3, 0, 4, 4, 4, None) == -3
+    assert L.gemm_fp8_fmt_bt(FAKE, 1, FAKE2, 1, s, s + 4, None, FAKE3, 3, 4, 4, 4, None) == -4
+    assert L.gemm_fp8_fmt_bt(FAKE, 1, FAKE2, 0, s, None, None, FAKE3, 0, 4, 4, 4, None) == -1
+    # quantize_fp8_transposed_fmt(x, rows, cols, scale, q, fmt, stream)
+    assert L.quantize_fp8_transposed_fmt(FAKE, 4, 4, FAKE2, FAKE3, 2, None) == -3
+    assert L.quantize_fp8_transposed_fmt(FAKE, 4, 4, FAKE2, FAKE + 8, 1, None) == -8
+    assert L.quantize_fp8_transposed_fmt(None, 0, 4, None, None, 1, None) == 0

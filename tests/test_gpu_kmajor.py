@@ -480,3 +480,79 @@ def test_tile_bt_narrow_n(M, N, K):
     R, S = orc.gemm(orc.FMT_E4M3, ca, cb)
     check_f32(run_fp8_bt(dev(ca), dev(cb.T), scalar(0.25), scalar(2.0), g.OUT_F32), R, S, 0.25, 2.0,
               what=f"fp8 bt {M}x{N}x{K}", T=fp8_dot_allowance(ca, cb))
+
+
+# ------------------------------------------------ FP8 operand formats, K-major
+
+from parity import check_fp8  # noqa: E402
+
+ORC_FMT = {g.FMT_E4M3: orc.FMT_E4M3, g.FMT_E5M2: orc.FMT_E5M2}
+PAIRS = [(g.FMT_E4M3, g.FMT_E4M3), (g.FMT_E4M3, g.FMT_E5M2), (g.FMT_E5M2, g.FMT_E4M3), (g.FMT_E5M2, g.FMT_E5M2)]
+# (config forced, M, N, K): the decode kernels (per-wave M = 1, cooperative
+# M <= 4 and M <= 8, by the selector) and each K-major tile configuration
+FMT_SHAPES = [(None, 1, 1000, 512), (None, 4, 520, 640), (None, 8, 300, 256),
+              ("tile_fp8_64x64x128_w2x2_bt", 100, 200, 256), ("tile_fp8_128x128x128_w2x2_bt", 300, 272, 384),
+              ("tile_fp8_256x256x128_w2x4_bt", 257, 512, 320)]
+
+
+def fp8_codes(fmt, shape, seed):
+    return wl.random_e5m2_codes(shape, seed) if fmt == g.FMT_E5M2 else wl.random_e4m3_codes(shape, seed)
+
+
+@pytest.mark.parametrize("fa,fb", PAIRS)
+@pytest.mark.parametrize("cfg,M,N,K", FMT_SHAPES)
+def test_gemm_fp8_fmt_bt(fa, fb, cfg, M, N, K, monkeypatch):
+    if cfg:
+        monkeypatch.setenv("LIBGEMM_CONFIG", cfg)
+    say(f"gemm_fp8_fmt_bt a={fa} b={fb} {cfg} {M}x{N}x{K}")
+    ca = fp8_codes(fa, (M, K), 13 * M + K + fa)
+    cb = fp8_codes(fb, (K, N), 17 * N + K + fb)
+    ofa, ofb = ORC_FMT[fa], ORC_FMT[fb]
+    R, S = orc.gemm(ofa, ca, cb, fmt_b=ofb)
+    T = fp8_dot_allowance(ca, cb, fmt_a=ofa, fmt_b=ofb)
+    sa, sb = np.float32(0.5), np.float32(0.25)
+    ta, tbt, tsa, tsb = dev(ca), dev(cb.T), scalar(sa), scalar(sb)
+    C = torch.empty((M, N), dtype=torch.float32, device=DEV)
+    g.gemm_fp8_fmt_bt(ta, fa, tbt, fb, tsa, tsb, C)
+    check_f32(host(C), R, S, sa, sb, what="f32", T=T)
+    V = R * float(sa) * float(sb)
+    for out_fmt in (g.FMT_E4M3, g.FMT_E5M2):
+        s_out = orc.scale(np.float32(np.max(np.abs(V))), ORC_FMT[out_fmt])
+        C = torch.empty((M, N), dtype=torch.uint8, device=DEV)
+        g.gemm_fp8_fmt_bt(ta, fa, tbt, fb, tsa, tsb, C, scalar(s_out), out_fmt=out_fmt)
+        check_fp8(host(C), R, S, sa, sb, s_out, ORC_FMT[out_fmt], what=f"fp8 out {out_fmt}", T=T)
+
+
+@pytest.mark.parametrize("rows,cols", [(1, 1), (63, 65), (129, 200), (4096, 1000)])
+def test_quantize_transposed_e5m2_bit_exact(rows, cols):
+    say(f"quantize_transposed e5m2 {rows}x{cols}")
+    x = wl.normal_with_outliers_f32((rows, cols), 77 * rows + cols) * np.float32(1000.0)
+    x[0, 0] = np.float32(-1e30)
+    for pow2 in (False, True):
+        s = orc.scale(orc.amax(x), orc.FMT_E5M2, pow2)
+        q = g.quantize_fp8_transposed_fmt(dev(x), scalar(s), g.FMT_E5M2)
+        assert np.array_equal(host(q), orc.quantize(x, s, orc.FMT_E5M2).T)
+
+
+def test_pow2_e5m2_chain_kmajor():
+    """FP32 A and B -> power-of-two E5M2 scale for A, E4M3 for B -> quantize A,
+    quantize B transposed -> mixed K-major GEMM -> F16; every step against the
+    oracle's chain."""
+    M, N, K = 300, 1024, 512
+    xa = wl.random_normal_f32((M, K), 51) * np.float32(1000.0)
+    xb = wl.random_normal_f32((K, N), 52)
+    ta, tb = dev(xa), dev(xb)
+    _, s_a = g.amax_scale_f32(ta, g.FMT_E5M2, True)
+    _, s_b = g.amax_scale_f32(tb, g.FMT_E4M3, True)
+    qa = g.quantize_fp8_fmt(ta, s_a, g.FMT_E5M2)
+    qbt = g.quantize_fp8_transposed_fmt(tb, s_b, g.FMT_E4M3)
+    osa = orc.scale(orc.amax(xa), orc.FMT_E5M2, True)
+    osb = orc.scale(orc.amax(xb), orc.FMT_E4M3, True)
+    assert host(s_a)[0] == osa and host(s_b)[0] == osb
+    cqa, cqb = orc.quantize(xa, osa, orc.FMT_E5M2), orc.quantize(xb, osb, orc.FMT_E4M3)
+    assert np.array_equal(host(qa), cqa) and np.array_equal(host(qbt), cqb.T)
+    C = torch.empty((M, N), dtype=torch.float16, device=DEV)
+    g.gemm_fp8_fmt_bt(qa, g.FMT_E5M2, qbt, g.FMT_E4M3, s_a, s_b, C)
+    R, S = orc.gemm(orc.FMT_E5M2, cqa, cqb, fmt_b=orc.FMT_E4M3)
+    T = fp8_dot_allowance(cqa, cqb, fmt_a=orc.FMT_E5M2, fmt_b=orc.FMT_E4M3)
+    check_f16(host(C), R, S, osa, osb, what="pow2 chain k-major", T=T)
