@@ -385,6 +385,19 @@ int gemm_fp8_fmt_bt(const uint8_t* A, int fmt_a, const uint8_t* Bt, int fmt_b,
 int quantize_fp8_transposed_fmt(const float* x, int64_t rows, int64_t cols, const float* scale,
                                 uint8_t* q, int fmt, hipStream_t stream);
 
+/*
+ * pack_b_kmajor — the one-time re-layout of a weight into the K-major form the
+ * _bt calls take (P1 §3.2: the weight is stored in a layout chosen for the
+ * kernel, ahead of the GEMMs that read it): Bt[n*K + k] = B[k*N + n].
+ *   B           device, row-major [K, N] elements of elem_bytes bytes (2: FP16,
+ *               1: FP8 codes); read only
+ *   K, N        sizes (either 0: no-op; each at most 2^31 - 1)
+ *   elem_bytes  1 or 2 (else GEMM_ERR_DTYPE)
+ *   Bt          device, [N, K] elements, written; must not overlap B
+ * One launch on `stream`; bytes are moved unchanged.
+ */
+int pack_b_kmajor(const void* B, int64_t K, int64_t N, int elem_bytes, void* Bt, hipStream_t stream);
+
 /* gemm_select_config for gemm_f16_bt (kind 0) and gemm_fp8_scaled_bt (kind 1). */
 int gemm_select_config_bt(int kind, int out_dtype, int64_t M, int64_t N, int64_t K,
                           char* buf, int buflen);

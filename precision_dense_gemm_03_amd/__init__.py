@@ -29,6 +29,7 @@ Functions keep the C names:
     quantize_fp8_transposed(x, scale, q=None, stream=None) -> q[cols, rows]
     gemm_fp8_fmt_bt(A, fmt_a, Bt, fmt_b, sA, sB, C, sOut=None, stream=None, out_fmt=None)
     quantize_fp8_transposed_fmt(x, scale, fmt, q=None, stream=None) -> q[cols, rows]
+    pack_b_kmajor(B, Bt=None, stream=None) -> Bt[N, K]   (FP16 or FP8 codes)
     select_config_bt(kind, out_dtype, M, N, K) -> str
     gemm_fp8_splitk_bt(A, Bt, sA, sB, C, sOut=None, workspace=None, stream=None, out_fmt=None)
     gemm_f16_splitk_bt(A, Bt, C, workspace=None, stream=None)
@@ -129,6 +130,8 @@ def lib() -> ctypes.CDLL:
     L.gemm_fp8_fmt_bt.argtypes = [vp, i32, vp, i32, vp, vp, vp, vp, i32, i64, i64, i64, vp]
     L.quantize_fp8_transposed_fmt.restype = i32
     L.quantize_fp8_transposed_fmt.argtypes = [vp, i64, i64, vp, vp, i32, vp]
+    L.pack_b_kmajor.restype = i32
+    L.pack_b_kmajor.argtypes = [vp, i64, i64, i32, vp, vp]
     L.gemm_fp8_splitk_bt.restype = i32
     L.gemm_fp8_splitk_bt.argtypes = [vp, vp, vp, vp, vp, vp, i32, i64, i64, i64, vp, i64, vp]
     L.gemm_f16_splitk_bt.restype = i32
@@ -284,6 +287,24 @@ def quantize_fp8_transposed_fmt(x, scale, fmt, q=None, stream=None):
     _check(lib().quantize_fp8_transposed_fmt(_ptr(x), rows, cols, _ptr(scale), _ptr(qv), int(fmt),
                                              _stream_handle(stream)), "quantize_fp8_transposed_fmt")
     return q
+
+
+def pack_b_kmajor(B, Bt=None, stream=None):
+    """The K-major copy Bt[N, K] of a row-major weight B[K, N] (float16, or
+    FP8 codes as uint8 / torch float8), made once on the GPU."""
+    torch = _torch()
+    if B.dim() != 2:
+        raise ValueError("pack_b_kmajor takes a 2-D B")
+    es = B.element_size()
+    if es not in (1, 2):
+        raise ValueError("pack_b_kmajor takes 1- or 2-byte elements")
+    K, N = int(B.shape[0]), int(B.shape[1])
+    if Bt is None:
+        Bt = torch.empty((N, K), dtype=B.dtype, device=B.device)
+    if tuple(Bt.shape) != (N, K) or Bt.element_size() != es:
+        raise ValueError("Bt must be [N, K] with B's element size")
+    _check(lib().pack_b_kmajor(_ptr(B), K, N, es, _ptr(Bt), _stream_handle(stream)), "pack_b_kmajor")
+    return Bt
 
 
 def quantize_fp8_transposed(x, scale, q=None, stream=None):

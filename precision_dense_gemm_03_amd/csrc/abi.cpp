@@ -370,6 +370,18 @@ int quantize_fp8_transposed(const float* x, int64_t rows, int64_t cols, const fl
     return quantize_fp8_transposed_fmt(x, rows, cols, scale, q, GEMM_FMT_E4M3, stream);
 }
 
+int pack_b_kmajor(const void* B, int64_t K, int64_t N, int elem_bytes, void* Bt, hipStream_t stream) {
+    if (elem_bytes != 1 && elem_bytes != 2) return GEMM_ERR_DTYPE;
+    if (!dim_ok(K) || !dim_ok(N)) return GEMM_ERR_DIM;
+    const int64_t bytes = K * N * elem_bytes;
+    if (bytes == 0) return GEMM_OK;
+    if (!B || !Bt) return GEMM_ERR_NULL;
+    if (overlaps(Bt, bytes, B, bytes)) return GEMM_ERR_ALIAS;
+    const int st = check_device();
+    if (st != GEMM_OK) return st;
+    return status_of(launch_transpose(B, K, N, elem_bytes, Bt, stream));
+}
+
 int quantize_fp8(const float* x, int64_t n, const float* scale, uint8_t* q, hipStream_t stream) {
     return quantize_fp8_fmt(x, n, scale, q, GEMM_FMT_E4M3, stream);
 }

@@ -188,6 +188,35 @@ __global__ __launch_bounds__(kThreads) void quantize_transposed_kernel(const flo
     }
 }
 
+// Transpose of a row-major [rows, cols] matrix of ES-byte elements (the
+// K-major packing of a weight B[K,N] into Bt[N,K]). A workgroup moves a 64 x 64
+// block through LDS: each of its 4 waves reads 16 rows of the block (lane j
+// takes column j, so a wave instruction reads one contiguous 64-element row
+// piece) and, after the barrier, writes 16 rows of the transposed block the
+// same way. The LDS row pitch of 65 elements spreads a column read over
+// distinct banks. Edge blocks are predicated.
+constexpr int kTrTile = 64;
+
+template <typename T>
+__global__ __launch_bounds__(kThreads) void transpose_kernel(const T* __restrict__ src, int64_t rows, int64_t cols,
+                                                             T* __restrict__ dst, int64_t tiles_c) {
+    __shared__ T t[kTrTile][kTrTile + 1];
+    const int64_t tile = blockIdx.x;
+    const int64_t r0 = (tile / tiles_c) * kTrTile, c0 = (tile % tiles_c) * kTrTile;
+    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+#pragma unroll 4
+    for (int i = wave; i < kTrTile; i += kThreads / 64) {
+        const int64_t r = r0 + i, c = c0 + lane;
+        if (r < rows && c < cols) t[i][lane] = src[r * cols + c];
+    }
+    __syncthreads();
+#pragma unroll 4
+    for (int i = wave; i < kTrTile; i += kThreads / 64) {
+        const int64_t orow = c0 + i, ocol = r0 + lane;  // dst[orow, ocol] = src[ocol, orow]
+        if (orow < cols && ocol < rows) dst[orow * rows + ocol] = t[lane][i];
+    }
+}
+
 __global__ __launch_bounds__(kThreads) void fill_zero_kernel(uint8_t* C, int64_t nbytes) {
     const int64_t tid = (int64_t)blockIdx.x * kThreads + threadIdx.x;
     const int64_t nthreads = (int64_t)gridDim.x * kThreads;
@@ -242,6 +271,23 @@ hipError_t launch_quantize_transposed(const float* x, int64_t rows, int64_t cols
     else
         quantize_transposed_kernel<FMT_E4M3><<<(unsigned)blocks, kThreads, 0, stream>>>(x, rows, cols, scale, q,
                                                                                          tiles_c, vec_in, vec_out);
+    return hipGetLastError();
+}
+
+hipError_t launch_transpose(const void* src, int64_t rows, int64_t cols, int elem_bytes, void* dst,
+                            hipStream_t stream) {
+    if (rows <= 0 || cols <= 0) return hipSuccess;
+    const int64_t tiles_r = (rows + kTrTile - 1) / kTrTile, tiles_c = (cols + kTrTile - 1) / kTrTile;
+    const int64_t blocks = tiles_r * tiles_c;
+    if (blocks > 0x7FFFFFFF) return hipErrorInvalidValue;
+    if (elem_bytes == 2)
+        transpose_kernel<uint16_t><<<(unsigned)blocks, kThreads, 0, stream>>>(
+            reinterpret_cast<const uint16_t*>(src), rows, cols, reinterpret_cast<uint16_t*>(dst), tiles_c);
+    else if (elem_bytes == 1)
+        transpose_kernel<uint8_t><<<(unsigned)blocks, kThreads, 0, stream>>>(
+            reinterpret_cast<const uint8_t*>(src), rows, cols, reinterpret_cast<uint8_t*>(dst), tiles_c);
+    else
+        return hipErrorInvalidValue;
     return hipGetLastError();
 }
 

@@ -98,6 +98,9 @@ hipError_t launch_quantize_channel(const float* x, int64_t rows, int64_t cols, i
 hipError_t launch_guard_scale(const float* amax_a, const float* amax_b, float* scalars, float* scale_out,
                               hipStream_t stream);
 hipError_t launch_guard_to_f16(const float* x, int64_t n, const float* scalars, _Float16* y, hipStream_t stream);
+// dst[c * rows + r] = src[r * cols + c] for 1- or 2-byte elements.
+hipError_t launch_transpose(const void* src, int64_t rows, int64_t cols, int elem_bytes, void* dst,
+                            hipStream_t stream);
 // Writes zeros to an [M,N] output of the given dtype (the K = 0 empty sum).
 hipError_t launch_fill_zero(void* C, int64_t count, int out_dtype, hipStream_t stream);
 

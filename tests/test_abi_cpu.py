@@ -381,3 +381,13 @@ def test_kmajor_format_entry_points_validation():
     assert L.quantize_fp8_transposed_fmt(FAKE, 4, 4, FAKE2, FAKE3, 2, None) == -3
     assert L.quantize_fp8_transposed_fmt(FAKE, 4, 4, FAKE2, FAKE + 8, 1, None) == -8
     assert L.quantize_fp8_transposed_fmt(None, 0, 4, None, None, 1, None) == 0
+
+
+def test_pack_b_kmajor_validation():
+    L = g.lib()
+    # pack_b_kmajor(B, K, N, elem_bytes, Bt, stream)
+    assert L.pack_b_kmajor(FAKE, 4, 4, 4, FAKE2, None) == -3
+    assert L.pack_b_kmajor(FAKE, -1, 4, 2, FAKE2, None) == -2
+    assert L.pack_b_kmajor(None, 4, 4, 2, FAKE2, None) == -1
+    assert L.pack_b_kmajor(FAKE, 4, 4, 2, FAKE + 16, None) == -8
+    assert L.pack_b_kmajor(None, 0, 4, 1, None, None) == 0

@@ -556,3 +556,30 @@ def test_pow2_e5m2_chain_kmajor():
     R, S = orc.gemm(orc.FMT_E5M2, cqa, cqb, fmt_b=orc.FMT_E4M3)
     T = fp8_dot_allowance(cqa, cqb, fmt_a=orc.FMT_E5M2, fmt_b=orc.FMT_E4M3)
     check_f16(host(C), R, S, osa, osb, what="pow2 chain k-major", T=T)
+
+
+# ------------------------------------------------------------- weight packing
+
+@pytest.mark.parametrize("K,N", [(1, 1), (1, 1000), (1000, 1), (63, 65), (64, 64), (4096, 12288), (4100, 333)])
+def test_pack_b_kmajor_exact(K, N):
+    """pack_b_kmajor moves FP16 values and FP8 codes unchanged into Bt[N, K]."""
+    say(f"pack_b_kmajor {K}x{N}")
+    b16 = wl.random_f16((K, N), K + 3 * N)
+    bt = g.pack_b_kmajor(dev(b16))
+    assert tuple(bt.shape) == (N, K)
+    assert np.array_equal(host(bt).view(np.uint16), np.ascontiguousarray(b16.T).view(np.uint16))
+    c8 = wl.random_e4m3_codes((K, N), K + 5 * N)
+    bt8 = g.pack_b_kmajor(dev(c8))
+    assert np.array_equal(host(bt8), np.ascontiguousarray(c8.T))
+
+
+def test_pack_then_decode():
+    """A row-major FP16 weight packed once, then the K-major M = 1 decode, against the oracle."""
+    w = wl.C3[0]
+    say(f"pack + decode {w.name}")
+    a16, b16 = wl.operand(w, 0), wl.operand(w, 1)
+    bt = g.pack_b_kmajor(dev(b16))
+    C = torch.empty((w.M, w.N), dtype=torch.float16, device=DEV)
+    g.gemm_f16_bt(dev(a16), bt, C)
+    R, S = orc.gemm(orc.FMT_F16, a16.view(np.uint16), b16.view(np.uint16))
+    check_f16(host(C), R, S, what=f"pack + decode {w.name}")
