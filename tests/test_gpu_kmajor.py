@@ -14,7 +14,7 @@ import torch
 import oracle as orc
 import precision_dense_gemm_03_amd as g
 import workloads as wl
-from parity import check_e4m3, check_f16, check_f32, fp8_dot_allowance
+from parity import check_e4m3, check_f16, check_f32, check_fp8, fp8_dot_allowance
 
 pytestmark = pytest.mark.gpu
 
@@ -483,8 +483,6 @@ def test_tile_bt_narrow_n(M, N, K):
 
 
 # ------------------------------------------------ FP8 operand formats, K-major
-
-from parity import check_fp8  # noqa: E402
 
 ORC_FMT = {g.FMT_E4M3: orc.FMT_E4M3, g.FMT_E5M2: orc.FMT_E5M2}
 PAIRS = [(g.FMT_E4M3, g.FMT_E4M3), (g.FMT_E4M3, g.FMT_E5M2), (g.FMT_E5M2, g.FMT_E4M3), (g.FMT_E5M2, g.FMT_E5M2)]
