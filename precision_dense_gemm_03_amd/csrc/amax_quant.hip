@@ -132,6 +132,7 @@ __global__ __launch_bounds__(kThreads) void quantize_kernel(const float* __restr
 // words land in 64 distinct banks); then each thread writes two 16-byte pieces
 // of output rows, a wave writing whole 128-byte rows.
 constexpr int kQtRows = 128, kQtCols = 64;
+static_assert(kQtRows % 64 == 0 && kQtRows <= 256, "a thread takes kQtRows / 64 row blocks");
 constexpr int kQtPitch = kQtRows + 4;
 
 template <int FMT>
@@ -147,7 +148,7 @@ __global__ __launch_bounds__(kThreads) void quantize_transposed_kernel(const flo
     const bool interior = r0 + kQtRows <= rows && c0 + kQtCols <= cols;
 
 #pragma unroll
-    for (int h = 0; h < 2; ++h) {
+    for (int h = 0; h < kQtRows / 64; ++h) {
         const int rb = tr + 16 * h;  // row block: rows 4 rb .. 4 rb + 3 of the tile
         uint32_t w[4];
 #pragma unroll
@@ -172,9 +173,10 @@ __global__ __launch_bounds__(kThreads) void quantize_transposed_kernel(const flo
     }
     __syncthreads();
 
+    constexpr int kSegs = kQtRows / 16;  // 16-code pieces per output row
 #pragma unroll
-    for (int h = 0; h < 2; ++h) {
-        const int oc = threadIdx.x / 8 + 32 * h, seg = threadIdx.x % 8;  // output row c0 + oc, codes 16 seg ..
+    for (int h = 0; h < kQtRows / 64; ++h) {
+        const int oc = threadIdx.x / kSegs + (kThreads / kSegs) * h, seg = threadIdx.x % kSegs;  // row c0 + oc
         const int64_t orow = c0 + oc, ocol = r0 + 16 * seg;
         const uint32_t* src = reinterpret_cast<const uint32_t*>(&t[oc * kQtPitch + 16 * seg]);
         if (interior && vec_out) {
