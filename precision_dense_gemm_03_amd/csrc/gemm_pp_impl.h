@@ -1,0 +1,533 @@
+// Ping-pong MFMA tile GEMM for gfx950: kernel and launcher templates, shared by
+// gemm_pp.hip (configuration table, E4M3 x E4M3 and FP16 instantiations) and
+// gemm_pp_mixed.hip (the other FP8 operand pairs).
+//
+// C[M,N] = (sA*A[M,K]) (sB*B[K,N]) with FP32 accumulation on the matrix cores
+// ("DeepGEMM实战：FP8矩阵乘法与JIT编译优化指南" §2.1: FP8 in, FP32 accumulate, scales
+// applied at write-back, §3.2; "HGEMM优化：深度学习中的矩阵乘法性能提升策略" §1.3 for
+// FP16 with an FP32 accumulator). B is row-major B[K,N] or K-major Bt[N,K].
+//
+// One workgroup computes a 256 x 256 output tile with 8 waves, two per SIMD.
+// The waves form two groups of four (one wave of each group per SIMD): group
+// G owns output rows [128 G, 128 G + 128), and wave j of a group the columns
+// [64 j, 64 j + 64), i.e. a 128 x 64 wave tile held as 4 x 2 accumulators of
+// the 32x32 MFMA (v_mfma_scale_f32_32x32x64_f8f6f4 with neutral block scales
+// for FP8, v_mfma_f32_32x32x16_f16 for FP16): 128 registers per lane.
+//
+// K advances in tiles of 64 bytes of every A row (64 FP8 or 32 FP16 values).
+// Each K tile runs as two phases per group, and the groups are offset by one
+// phase, so that on every SIMD one wave issues MFMAs while the other moves
+// data:
+//   MEM(t): read this wave's operands of tile t from LDS into registers; issue
+//           this group's share of the direct global->LDS loads of tile t+3
+//           (group 0 loads A's tile, group 1 B's); wait until this wave's loads
+//           of tile t+1 have landed and its LDS reads are done; barrier.
+//   MMA(t): the 8 (FP8) or 16 (FP16) MFMAs of tile t, at raised issue
+//           priority; barrier.
+// Group 1 enters the loop one barrier later than group 0, so the barrier that
+// ends one group's MMA phase ends the other group's MEM phase. The staging is
+// a ring of four LDS stages of 32 KiB (A 256 x 64 bytes + B 64 bytes x 256
+// n), loaded three tiles ahead (the double buffering of the FP8 guide §2.3,
+// deepened as the HGEMM article §3.2/§3.3 discusses). Every LDS stage is its
+// own LDS object, so the compiler can tell the in-flight direct loads from the
+// operand reads of other stages and inserts no waits of its own.
+//
+// LDS layouts are bank-conflict free for the 16-lane passes of 16-byte reads
+// (the DeepGEMM deep-dive §3.2 argues for a bank-aware layout; here it is an
+// XOR permutation, since a direct load fixes each lane's LDS slot):
+//   A and Bt rows (64 bytes = 4 chunks of 16): chunk c of row r lives in slot
+//   c ^ ((r >> 2) & 3), so 16 consecutive rows read at one chunk cover all 16
+//   four-bank groups;
+//   row-major B rows (256 or 512 bytes): chunk c of k-row r lives in slot
+//   c ^ swz_b(r), so the rows and chunks of one transpose-read pass land in
+//   distinct bank groups.
+// Row-major B reaches the MFMA's K-contiguous operand layout through gfx950's
+// LDS transpose reads (ds_read_b64_tr_b8 / _b16); a lane of a 16-lane group
+// receives element (lane % E) of lanes (16 / E) e + lane / E of the group.
+//
+// The MFMAs take B's operand first and A's second, so each lane's 16
+// accumulator values of a 32 x 32 block are one output row (lane % 32) and
+// four runs of four consecutive columns. The epilogue multiplies by the scale
+// product (sA*sB, or sA*sB/sOut for an FP8 output; per-channel sA[i]*sB[j]),
+// converts, and for FP8 and FP16 outputs stages the wave's 128 x 64 block in
+// LDS so that every lane stores 16-byte pieces of output rows.
+//
+// Edges (FP8 guide §3.3): rows of A (and Bt) past M (N) are loaded from the
+// last valid row and column chunks of row-major B past N from the last valid
+// chunk (valid addresses, never stored); a partial last K tile is loaded with
+// guarded vector loads and zero fill; edge tiles store element by element with
+// predicates. Operands that are not 16-byte aligned, or row blocks beyond
+// 32-bit offsets, go to the register-staged tile kernel.
+#pragma once
+
+#include <cstring>
+
+#include "device_common.h"
+#include "kernels.h"
+#include "tile_order.h"
+
+namespace libgemm {
+namespace pp {
+
+template <int ES>
+struct Pp {
+    static constexpr int BM = 256, BN = 256;
+    static constexpr int NT = 512;                  // 8 waves
+    static constexpr int S = 4;                     // LDS ring stages
+    static constexpr int ROWB = 64;                 // bytes of every A row per K tile
+    static constexpr int BK = ROWB / ES;            // k per K tile (64 FP8, 32 FP16)
+    static constexpr int VE = 16 / ES;              // elements per 16-byte chunk
+    static constexpr int STAGE_BYTES = 16384;       // A: 256 rows x 64 B; B: the same bytes
+    static constexpr int BNB = BN * ES;             // row-major B: bytes of one k-row of the tile
+    static constexpr int B_CPR = BNB / 16;          // chunks per row-major B row
+    static constexpr int B_RPB = 1024 / BNB;        // row-major B rows per 1 KiB direct load
+    static constexpr int LOADS = 4;                 // direct loads per wave per K tile (its group's 16 KiB / 4 waves)
+    static constexpr int KSUB = ES == 1 ? 1 : 2;    // MFMA k-steps per K tile (64 or 2 x 16 values)
+    static_assert(S * 2 * STAGE_BYTES <= 160 * 1024, "the LDS ring must fit in 160 KiB");
+};
+
+__device__ __forceinline__ int swz_a(int r) { return (r >> 2) & 3; }
+
+// Row-major B: k-row r's chunk c lives in slot c ^ swz_b(r). FP8 passes read 8
+// rows x 2 adjacent chunks, FP16 passes 4 rows x 4 adjacent chunks; the values
+// below differ in the bits those chunk pairs/quads do not cover.
+template <int ES>
+__device__ __forceinline__ int swz_b(int r) {
+    return ES == 1 ? ((2 * (r & 7)) | ((r >> 2) & 1)) : (2 * (r & 3) + 8 * (r & 1));
+}
+
+// s_waitcnt immediate (gfx9 encoding): at most `vm` vector-memory and `lgkm`
+// LDS operations of this wave outstanding.
+constexpr int waitcnt_imm(int vm, int lgkm) { return (vm & 0xF) | ((vm >> 4) << 14) | (7 << 4) | ((lgkm & 0xF) << 8); }
+
+template <int ES>
+struct Mfma;
+
+template <>
+struct Mfma<1> {
+    typedef v8i op;
+    // FA, FB: operand formats (0 = E4M3, 1 = E5M2) of the instruction's first
+    // and second operand.
+    template <int FA, int FB>
+    static __device__ __forceinline__ v16f mma(v8i a, v8i b, v16f c) {
+        return __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(a, b, c, FA, FB, 0, 127, 0, 127);
+    }
+};
+
+template <>
+struct Mfma<2> {
+    typedef v8h op;
+    template <int FA, int FB>
+    static __device__ __forceinline__ v16f mma(v8h a, v8h b, v16f c) {
+        return __builtin_amdgcn_mfma_f32_32x32x16_f16(a, b, c, 0, 0, 0);
+    }
+};
+
+// OUT_E4M3 stands for both FP8 outputs; EPI_E5M2 in eflags picks the format.
+template <int OUT>
+__device__ __forceinline__ void store_elem(void* C, int64_t idx, float y, int eflags) {
+    if constexpr (OUT == OUT_F32) {
+        reinterpret_cast<float*>(C)[idx] = y;
+    } else if constexpr (OUT == OUT_F16) {
+        reinterpret_cast<_Float16*>(C)[idx] = (_Float16)y;
+    } else {
+        reinterpret_cast<uint8_t*>(C)[idx] = (eflags & EPI_E5M2) ? e5m2_from_f32(y) : e4m3_from_f32(y);
+    }
+}
+
+template <int ES, int OUT, int FA, int FB, bool BT>
+__global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2, 2))) void gemm_pp_kernel(
+    const uint8_t* __restrict__ A, const uint8_t* __restrict__ B, void* __restrict__ C, int M, int N, int K,
+    const float* __restrict__ sA, const float* __restrict__ sB, const float* __restrict__ sOut, int tiles_m,
+    int tiles_n, int eflags, int vec_out) {
+    using T = Pp<ES>;
+    using Op = typename Mfma<ES>::op;
+    __shared__ __attribute__((aligned(1024))) uint8_t a0[T::STAGE_BYTES], a1[T::STAGE_BYTES], a2[T::STAGE_BYTES],
+        a3[T::STAGE_BYTES];
+    __shared__ __attribute__((aligned(1024))) uint8_t b0[T::STAGE_BYTES], b1[T::STAGE_BYTES], b2[T::STAGE_BYTES],
+        b3[T::STAGE_BYTES];
+    // Stage selection; st is a compile-time constant wherever it matters
+    // (the main loop is unrolled by the ring size).
+    auto stage_a = [&](int st) __attribute__((always_inline)) -> LDS_AS uint8_t* {
+        switch (st) {
+            case 0: return (LDS_AS uint8_t*)a0;
+            case 1: return (LDS_AS uint8_t*)a1;
+            case 2: return (LDS_AS uint8_t*)a2;
+            default: return (LDS_AS uint8_t*)a3;
+        }
+    };
+    auto stage_b = [&](int st) __attribute__((always_inline)) -> LDS_AS uint8_t* {
+        switch (st) {
+            case 0: return (LDS_AS uint8_t*)b0;
+            case 1: return (LDS_AS uint8_t*)b1;
+            case 2: return (LDS_AS uint8_t*)b2;
+            default: return (LDS_AS uint8_t*)b3;
+        }
+    };
+
+    const int tid = threadIdx.x, lane = tid & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const int G = wave >> 2, wj = wave & 3;
+    int tile_m, tile_n;
+    tile_coords(blockIdx.x, tiles_m, tiles_n, tile_m, tile_n);
+    const int m0 = tile_m * T::BM, n0 = tile_n * T::BN;
+    const int nk = (K + T::BK - 1) / T::BK;
+    const int nk_full = K / T::BK;
+
+    // ---- this lane's direct-load slots: group 0 loads A, group 1 loads B ----
+    // Load i of wave j fills 1 KiB of the group's 16 KiB: A / Bt rows
+    // 64 j + 16 i + lane / 4 (slot lane % 4), or row-major B rows
+    // B_RPB (4 j + i) + lane / B_CPR (slot lane % B_CPR).
+    const uint8_t* src = G == 0 ? A + (int64_t)m0 * K * ES
+                                : (BT ? B + (int64_t)n0 * K * ES : B + (int64_t)n0 * ES);
+    uint32_t goff[T::LOADS];
+#pragma unroll
+    for (int i = 0; i < T::LOADS; ++i) {
+        if (G == 0 || BT) {
+            const int r = 64 * wj + 16 * i + (lane >> 2);
+            const int c = (lane & 3) ^ swz_a(r);
+            const int rr = G == 0 ? min(m0 + r, M - 1) - m0 : min(n0 + r, N - 1) - n0;
+            goff[i] = (uint32_t)(rr * K * ES + c * 16);
+        } else {
+            const int r = T::B_RPB * (4 * wj + i) + lane / T::B_CPR;
+            const int c = (lane % T::B_CPR) ^ swz_b<ES>(r);
+            const int col = min(n0 + c * T::VE, N - T::VE) - n0;
+            goff[i] = (uint32_t)(r * N * ES + col * ES);
+        }
+    }
+    // Byte step of the source between K tiles.
+    const int64_t kstep = (G == 0 || BT) ? (int64_t)T::ROWB : (int64_t)T::BK * N * ES;
+
+    // Direct loads of full K tile kt into stage st.
+    auto issue_full = [&](int kt, int st) __attribute__((always_inline)) {
+        const uint8_t* p = src + (int64_t)kt * kstep;
+        if (G == 0) {
+            LDS_AS uint8_t* dst = stage_a(st) + wj * 4096;
+#pragma unroll
+            for (int i = 0; i < T::LOADS; ++i)
+                __builtin_amdgcn_global_load_lds((const void*)(p + goff[i]), (LDS_AS void*)(dst + i * 1024), 16, 0, 0);
+        } else {
+            LDS_AS uint8_t* dst = stage_b(st) + wj * 4096;
+#pragma unroll
+            for (int i = 0; i < T::LOADS; ++i)
+                __builtin_amdgcn_global_load_lds((const void*)(p + goff[i]), (LDS_AS void*)(dst + i * 1024), 16, 0, 0);
+        }
+    };
+    // The partial last K tile: the same slots, loaded with guards and zero
+    // beyond K, written with ordinary LDS stores (waiting for these loads also
+    // waits for every direct load this wave has in flight).
+    auto issue_partial = [&](int kt, int st) __attribute__((always_inline)) {
+        const uint8_t* p = src + (int64_t)kt * kstep;
+        const int k0 = kt * T::BK;
+        LDS_AS uint8_t* dst = (G == 0 ? stage_a(st) : stage_b(st)) + wj * 4096;
+#pragma unroll 1
+        for (int i = 0; i < T::LOADS; ++i) {
+            v4u v = v4u{0u, 0u, 0u, 0u};
+            if (G == 0 || BT) {
+                const int r = 64 * wj + 16 * i + (lane >> 2);
+                const int c = (lane & 3) ^ swz_a(r);
+                if (k0 + c * T::VE < K) v = *reinterpret_cast<const v4u*>(p + goff[i]);
+            } else {
+                const int r = T::B_RPB * (4 * wj + i) + lane / T::B_CPR;
+                if (k0 + r < K) v = *reinterpret_cast<const v4u*>(p + goff[i]);
+            }
+            *(LDS_AS v4u*)(dst + i * 1024 + lane * 16) = v;
+        }
+    };
+
+    // ---- operand reads ----
+    // A: rows 128 G + 32 i + lane % 32; FP8 takes chunks 2h, 2h + 1 of the row
+    // (k = 32 h .. 32 h + 31), FP16 k-step u takes chunk 2u + h (h = lane / 32).
+    // The row's swizzle is that of lane % 32 (row blocks start at multiples of 32).
+    const int lr = lane & 31, h = lane >> 5;
+    const int sw = swz_a(lr);
+    const int j16 = lane & 15, half = (lane >> 4) & 1;
+    auto rd_row = [&](const LDS_AS uint8_t* rowp, int u) __attribute__((always_inline)) -> Op {
+        if constexpr (ES == 1) {
+            const v4i lo = *(const LDS_AS v4i*)(rowp + (((2 * h) ^ sw) << 4));
+            const v4i hi = *(const LDS_AS v4i*)(rowp + (((2 * h + 1) ^ sw) << 4));
+            return __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
+        } else {
+            return __builtin_bit_cast(v8h, *(const LDS_AS v4u*)(rowp + (((2 * u + h) ^ sw) << 4)));
+        }
+    };
+    // Row-major B, block jb of this wave's columns (64 wj + 32 jb + 0..31).
+    auto rd_b_rowmajor = [&](const LDS_AS uint8_t* sb, int jb, int u) __attribute__((always_inline)) -> Op {
+        if constexpr (ES == 1) {
+            // 16-lane group (h, half): columns 64 wj + 32 jb + 16 half + 0..15;
+            // read q: lane j16 addresses k-row 32 h + 8 q + j16 / 2, bytes
+            // 8 (j16 % 2) of the column chunk; k-row % 8 = j16 / 2.
+            const int chunk = (4 * wj + 2 * jb + half) ^ swz_b<1>(j16 >> 1);
+            v2i t[4];
+#pragma unroll
+            for (int q = 0; q < 4; ++q) {
+                const int k = 32 * h + 8 * q + (j16 >> 1);
+                t[q] = __builtin_amdgcn_ds_read_tr8_b64_v2i32((LDS_AS v2i*)(sb + k * T::BNB + chunk * 16 + 8 * (j16 & 1)));
+            }
+            const v4i t01 = __builtin_shufflevector(t[0], t[1], 0, 1, 2, 3);
+            const v4i t23 = __builtin_shufflevector(t[2], t[3], 0, 1, 2, 3);
+            return __builtin_shufflevector(t01, t23, 0, 1, 2, 3, 4, 5, 6, 7);
+        } else {
+            // k-step u: lane j16 addresses k-row 16 u + 8 h + 4 q + j16 / 4,
+            // columns 64 wj + 32 jb + 16 half + 4 (j16 % 4) .. + 3; k-row % 4 = j16 / 4.
+            const int chunk = (8 * wj + 4 * jb + 2 * half + ((j16 & 3) >> 1)) ^ swz_b<2>(j16 >> 2);
+            v4s t[2];
+#pragma unroll
+            for (int q = 0; q < 2; ++q) {
+                const int k = 16 * u + 8 * h + 4 * q + (j16 >> 2);
+                t[q] = __builtin_amdgcn_ds_read_tr16_b64_v4i16((LDS_AS v4s*)(sb + k * T::BNB + chunk * 16 + 8 * (j16 & 1)));
+            }
+            return __builtin_bit_cast(v8h, __builtin_shufflevector(t[0], t[1], 0, 1, 2, 3, 4, 5, 6, 7));
+        }
+    };
+
+    v16f acc[4][2];
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+#pragma unroll
+        for (int j = 0; j < 2; ++j)
+#pragma unroll
+            for (int r = 0; r < 16; ++r) acc[i][j][r] = 0.0f;
+
+    Op opa[T::KSUB][4], opb[T::KSUB][2];
+    // One K tile: MEM(t) then MMA(t). steady: tile t+3 exists and is full
+    // (the unrolled main loop); otherwise the loads of tile t+3 are chosen at
+    // run time.
+    auto step = [&](int t, int st, bool steady) __attribute__((always_inline)) {
+        // MEM(t)
+        const LDS_AS uint8_t* sa = stage_a(st) + (128 * G + lr) * T::ROWB;
+#pragma unroll
+        for (int u = 0; u < T::KSUB; ++u)
+#pragma unroll
+            for (int i = 0; i < 4; ++i) opa[u][i] = rd_row(sa + 32 * i * T::ROWB, u);
+        if constexpr (BT) {
+            const LDS_AS uint8_t* sbt = stage_b(st) + (64 * wj + lr) * T::ROWB;
+#pragma unroll
+            for (int u = 0; u < T::KSUB; ++u)
+#pragma unroll
+                for (int j = 0; j < 2; ++j) opb[u][j] = rd_row(sbt + 32 * j * T::ROWB, u);
+        } else {
+#pragma unroll
+            for (int u = 0; u < T::KSUB; ++u)
+#pragma unroll
+                for (int j = 0; j < 2; ++j) opb[u][j] = rd_b_rowmajor(stage_b(st), j, u);
+        }
+        const int nt = t + T::S - 1, nst = (st + T::S - 1) % T::S;
+        if (steady || nt < nk_full) {
+            issue_full(nt, nst);
+            __builtin_amdgcn_s_waitcnt(waitcnt_imm(T::LOADS * (T::S - 2), 0));
+        } else {
+            if (nt < nk) issue_partial(nt, nst);
+            __builtin_amdgcn_s_waitcnt(0);
+        }
+        asm volatile("s_barrier" ::: "memory");
+        // MMA(t): operands pinned after the barrier, products before the next one
+#pragma unroll
+        for (int u = 0; u < T::KSUB; ++u) {
+#pragma unroll
+            for (int i = 0; i < 4; ++i) asm volatile("" : "+v"(opa[u][i]));
+#pragma unroll
+            for (int j = 0; j < 2; ++j) asm volatile("" : "+v"(opb[u][j]));
+        }
+        __builtin_amdgcn_s_setprio(1);
+#pragma unroll
+        for (int u = 0; u < T::KSUB; ++u)
+#pragma unroll
+            for (int i = 0; i < 4; ++i)
+#pragma unroll
+                for (int j = 0; j < 2; ++j)
+                    acc[i][j] = Mfma<ES>::template mma<FB, FA>(opb[u][j], opa[u][i], acc[i][j]);
+#pragma unroll
+        for (int i = 0; i < 4; ++i)
+#pragma unroll
+            for (int j = 0; j < 2; ++j) asm volatile("" : "+v"(acc[i][j]));
+        __builtin_amdgcn_s_setprio(0);
+        asm volatile("s_barrier" ::: "memory");
+    };
+
+    // ---- prologue: tiles 0 .. S-2, then wait for tile 0 ----
+#pragma unroll
+    for (int p = 0; p < T::S - 1; ++p) {
+        if (p < nk_full) issue_full(p, p);
+        else if (p < nk) issue_partial(p, p);
+    }
+    if (nk >= T::S - 1) __builtin_amdgcn_s_waitcnt(waitcnt_imm(T::LOADS * (T::S - 2), 15));
+    else __builtin_amdgcn_s_waitcnt(0);
+    asm volatile("s_barrier" ::: "memory");
+    if (G == 1) asm volatile("s_barrier" ::: "memory");
+
+    // Main loop, unrolled by the ring size so that every stage is a fixed LDS
+    // object; it runs while the tiles it loads (up to t + 6) are full tiles.
+    int t = 0;
+    for (; t + 2 * T::S - 1 <= nk_full; t += T::S) {
+        step(t, 0, true);
+        step(t + 1, 1, true);
+        step(t + 2, 2, true);
+        step(t + 3, 3, true);
+    }
+#pragma unroll 1
+    for (; t < nk; ++t) step(t, t % T::S, false);
+    if (G == 0) asm volatile("s_barrier" ::: "memory");
+
+    // ---- epilogue ----
+    // Block (i, j), element 4q + e: row 128 G + 32 i + lr, column
+    // 64 wj + 32 j + 8 q + 4 h + e of the tile.
+    const bool chan = (eflags & EPI_CHANNEL) != 0;
+    const float scale = epilogue_base(sA, sB, sOut, OUT == OUT_E4M3, chan);
+    const int row_t = 128 * G + lr;            // + 32 i
+    const int col_t = 64 * wj + 4 * h;         // + 32 j + 8 q
+    // Vector stores need a 16-byte aligned C with 16-byte row pitches (vec_out).
+    const bool interior = vec_out && (m0 + T::BM <= M) && (n0 + T::BN <= N);
+    if (!interior) {
+#pragma unroll
+        for (int i = 0; i < 4; ++i)
+#pragma unroll
+            for (int j = 0; j < 2; ++j)
+#pragma unroll
+                for (int r = 0; r < 16; ++r) {
+                    const int row = m0 + row_t + 32 * i, col = n0 + col_t + 32 * j + 8 * (r >> 2) + (r & 3);
+                    if (row < M && col < N) {
+                        float y = acc[i][j][r] * scale;
+                        if (chan) y *= sA[row] * sB[col];
+                        store_elem<OUT>(C, (int64_t)row * N + col, y, eflags);
+                    }
+                }
+        return;
+    }
+    // Interior tile: the scaled values of one run of four columns.
+    auto run4 = [&](int i, int j, int q) __attribute__((always_inline)) -> v4f {
+        v4f y;
+#pragma unroll
+        for (int e = 0; e < 4; ++e) y[e] = acc[i][j][4 * q + e] * scale;
+        if (chan) {
+            const float sr = sA[m0 + row_t + 32 * i];
+            const int col = n0 + col_t + 32 * j + 8 * q;
+#pragma unroll
+            for (int e = 0; e < 4; ++e) y[e] *= sr * sB[col + e];
+        }
+        return y;
+    };
+    if constexpr (OUT == OUT_F32) {
+        float* Cf = reinterpret_cast<float*>(C);
+#pragma unroll
+        for (int i = 0; i < 4; ++i)
+#pragma unroll
+            for (int j = 0; j < 2; ++j)
+#pragma unroll
+                for (int q = 0; q < 4; ++q)
+                    *reinterpret_cast<v4f*>(Cf + (int64_t)(m0 + row_t + 32 * i) * N + n0 + col_t + 32 * j + 8 * q) =
+                        run4(i, j, q);
+        return;
+    }
+    // FP8 / FP16: the wave's 128 x 64 block goes to its own LDS stage array
+    // (row pitch 64 ES bytes), then each lane stores 16-byte row pieces. Every
+    // wave has finished its last operand read (the final barrier above).
+    constexpr int RB = 64 * (OUT == OUT_F16 ? 2 : 1);  // bytes of one block row
+    LDS_AS uint8_t* ep = wave < 4 ? stage_a(wave) : stage_b(wave - 4);
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+#pragma unroll
+        for (int j = 0; j < 2; ++j)
+#pragma unroll
+            for (int q = 0; q < 4; ++q) {
+                const v4f y = run4(i, j, q);
+                const int r = 32 * i + lr, cb = (32 * j + 8 * q + 4 * h) * (RB / 64);
+                if constexpr (OUT == OUT_F16) {
+                    typedef _Float16 v4hh __attribute__((ext_vector_type(4)));
+                    const v4hh hv = {(_Float16)y[0], (_Float16)y[1], (_Float16)y[2], (_Float16)y[3]};
+                    *(LDS_AS v2i*)(ep + r * RB + cb) = __builtin_bit_cast(v2i, hv);
+                } else {
+                    const uint32_t w = (eflags & EPI_E5M2) ? e5m2_pack4(y[0], y[1], y[2], y[3])
+                                                          : e4m3_pack4(y[0], y[1], y[2], y[3]);
+                    *(LDS_AS uint32_t*)(ep + r * RB + cb) = w;
+                }
+            }
+    __builtin_amdgcn_s_waitcnt(waitcnt_imm(63, 0));
+    constexpr int LPR = RB / 16;             // lanes per block row
+    constexpr int RPI = 64 / LPR;            // block rows per store instruction
+    uint8_t* Cb = reinterpret_cast<uint8_t*>(C);
+    const int es_out = RB / 64;
+#pragma unroll
+    for (int p = 0; p < 128 / RPI; ++p) {
+        const int r = RPI * p + lane / LPR, seg = lane % LPR;
+        const v4i v = *(const LDS_AS v4i*)(ep + r * RB + 16 * seg);
+        *reinterpret_cast<v4i*>(Cb + ((int64_t)(m0 + 128 * G + r) * N + n0 + 64 * wj) * es_out + 16 * seg) = v;
+    }
+}
+
+inline bool aligned16(const void* p) { return ((uintptr_t)p & 15u) == 0; }
+
+// Whether the ping-pong kernel can take the request: 16-byte aligned operands
+// and row pitches, and 32-bit offsets within a tile's row block.
+template <int ES, bool BT>
+inline bool pp_fits(const GemmArgs& a) {
+    using T = Pp<ES>;
+    const bool aligned = aligned16(a.A) && aligned16(a.B) && (a.K * ES) % 16 == 0 && (BT || (a.N * ES) % 16 == 0);
+    const bool fits = (int64_t)T::BM * a.K * ES < (1ll << 31) &&
+                      (BT ? (int64_t)T::BN * a.K * ES : (int64_t)T::BK * a.N * ES) < (1ll << 31);
+    return aligned && fits;
+}
+
+// The register-staged 256 x 256 kernel, for requests the ping-pong kernel
+// cannot take.
+inline hipError_t fallback(int kind, const GemmArgs& a) {
+    const char* name = a.b_kmajor ? (kind == KIND_FP8 ? "tile_fp8_256x256x128_w2x4_bt" : "tile_f16_256x256x64_w2x4_bt")
+                                  : (kind == KIND_FP8 ? "tile_fp8_256x256x128_w2x4" : "tile_f16_256x256x64_w2x4");
+    int nt = 0;
+    const GemmConfig* tt = tile_configs(&nt);
+    for (int i = 0; i < nt; ++i)
+        if (std::strcmp(tt[i].name, name) == 0) return tt[i].launch(a);
+    return hipErrorInvalidValue;
+}
+
+template <int ES, int FA, int FB, bool BT>
+hipError_t launch_pp(const GemmArgs& a) {
+    using T = Pp<ES>;
+    if (a.splits > 1) return hipErrorInvalidValue;  // no split-K (kgran 0 in the table)
+    if (BT != (a.b_kmajor != 0)) return hipErrorInvalidValue;
+    const int64_t tiles_m = (a.M + T::BM - 1) / T::BM;
+    const int64_t tiles_n = (a.N + T::BN - 1) / T::BN;
+    const int64_t blocks = tiles_m * tiles_n;
+    if (blocks <= 0) return hipSuccess;
+    if (!pp_fits<ES, BT>(a) || blocks > 0x7FFFFFFF) return fallback(ES == 1 ? KIND_FP8 : KIND_F16, a);
+    const uint8_t* A = reinterpret_cast<const uint8_t*>(a.A);
+    const uint8_t* B = reinterpret_cast<const uint8_t*>(a.B);
+    const int M = (int)a.M, N = (int)a.N, K = (int)a.K;
+    const dim3 grid((unsigned)blocks), block(T::NT);
+    const int eflags = (a.out_dtype == OUT_E5M2 ? EPI_E5M2 : 0) | (a.channel ? EPI_CHANNEL : 0);
+    const int64_t out_es = a.out_dtype == OUT_F32 ? 4 : (a.out_dtype == OUT_F16 ? 2 : 1);
+    const int vec_out = aligned16(a.C) && (a.N * out_es) % 16 == 0;
+    switch (a.out_dtype) {
+        case OUT_F32:
+            gemm_pp_kernel<ES, OUT_F32, FA, FB, BT><<<grid, block, 0, a.stream>>>(
+                A, B, a.C, M, N, K, a.sA, a.sB, a.sOut, (int)tiles_m, (int)tiles_n, eflags, vec_out);
+            break;
+        case OUT_F16:
+            gemm_pp_kernel<ES, OUT_F16, FA, FB, BT><<<grid, block, 0, a.stream>>>(
+                A, B, a.C, M, N, K, a.sA, a.sB, a.sOut, (int)tiles_m, (int)tiles_n, eflags, vec_out);
+            break;
+        default:
+            if constexpr (ES == 1) {
+                gemm_pp_kernel<ES, OUT_E4M3, FA, FB, BT><<<grid, block, 0, a.stream>>>(
+                    A, B, a.C, M, N, K, a.sA, a.sB, a.sOut, (int)tiles_m, (int)tiles_n, eflags, vec_out);
+            } else {
+                return hipErrorInvalidValue;
+            }
+    }
+    return hipGetLastError();
+}
+
+// Operand-format dispatch; the pairs other than E4M3 x E4M3 are instantiated
+// in gemm_pp_mixed.hip.
+template <bool BT>
+hipError_t launch_pp_fp8_any(const GemmArgs& a) {
+    switch (a.fmt_a * 2 + a.fmt_b) {
+        case 0: return launch_pp<1, 0, 0, BT>(a);
+        case 1: return launch_pp<1, 0, 1, BT>(a);
+        case 2: return launch_pp<1, 1, 0, BT>(a);
+        default: return launch_pp<1, 1, 1, BT>(a);
+    }
+}
+
+}  // namespace pp
+}  // namespace libgemm

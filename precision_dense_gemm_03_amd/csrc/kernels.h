@@ -38,7 +38,8 @@ typedef hipError_t (*GemmLauncher)(const GemmArgs&);
 struct GemmConfig {
     const char* name;   // e.g. "tile_fp8_256x256x128_w2x2"
     int kind;           // OperandKind
-    int family;         // 0 = MFMA tile kernel, 1 = M<=16 streaming kernel, 2 = direct-load tile kernel
+    int family;         // 0 = MFMA tile kernel, 1 = M<=16 streaming kernel, 2 = direct-load tile kernel,
+                        // 3 = K-major decode kernel, 4 = ping-pong tile kernel
     int bm, bn, bk;     // tile (stream: bm = max M, bn = columns per block, bk = k-slices)
     GemmLauncher launch;
     int fmt_mask = 0;   // FP8 operand pairs served: bit (2*fmt_a + fmt_b); 0 means E4M3 x E4M3 only
@@ -59,6 +60,7 @@ const GemmConfig* tile_configs(int* count);
 const GemmConfig* stream_configs(int* count);
 const GemmConfig* dma_configs(int* count);
 const GemmConfig* gemv_kmajor_configs(int* count);
+const GemmConfig* pp_configs(int* count);
 
 // Shape (and FP8 operand formats) -> configuration (host only, no HIP calls).
 // Returns NULL if none fits.

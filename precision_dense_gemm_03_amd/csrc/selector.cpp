@@ -13,10 +13,10 @@
 //      vs 52.9 us). The M = 8 and M = 16 streaming configurations stay
 //      selectable by name.
 //   2. Otherwise the MFMA tile kernel: the largest square tile (256, 128, 64)
-//      whose grid still gives every CU a tile (>= 256 tiles) and whose padded
-//      area wastes at most 25 %; if none fills the chip, the tile with the
-//      most tiles (64). Which kernel runs a 256x256 tile is chosen in
-//      tile_with below.
+//      whose grid still gives every CU a tile (>= 256 tiles; 256x256 tiles
+//      from 192) and whose padded area wastes at most 25 %; if none fills the
+//      chip, the tile with the most tiles (64). Which kernel runs a 256x256
+//      tile is chosen in tile_with below.
 //   3. LIBGEMM_CONFIG=<config name> replaces the choice when that config can
 //      serve the request (same operand kind and FP8 operand formats; streaming
 //      configs need M <= bound).
@@ -64,30 +64,23 @@ const GemmConfig* find_named(const char* name, int kind, int64_t M, int fa = 0, 
     const GemmConfig* dt = dma_configs(&nd);
     for (int i = 0; i < nd; ++i)
         if (std::strcmp(dt[i].name, name) == 0 && serves(dt[i], kind, fa, fb, bt)) return &dt[i];
+    int np = 0;
+    const GemmConfig* pt = pp_configs(&np);
+    for (int i = 0; i < np; ++i)
+        if (std::strcmp(pt[i].name, name) == 0 && serves(pt[i], kind, fa, fb, bt)) return &pt[i];
     return nullptr;
 }
 
 // The preferred configuration of each tile size. 256x256 tiles use the
-// register-staged 8-wave kernel (two waves per SIMD overlap one another's
-// loads, prologue and epilogue), except for FP16 grids of several rounds of
-// tiles (at least 2 per CU), where the direct-load kernel (4 waves of
-// 128x128, 4-stage LDS ring) measured faster. Measured on two MI355X boxes,
-// same box per row (us): FP8 4096^3 78.4 vs 79.6, FP8 16384x12288x4096 774
-// vs 877, FP8 8192^3 481 vs 492; FP16 4096^3 144 vs 153; FP16 8192^3 1051
-// vs 1022 (register-staged vs direct-load). Smaller tiles use the
-// register-staged kernel with 4 waves.
+// ping-pong kernel (8 waves, two per SIMD taking turns at the matrix core,
+// direct loads into a 4-stage LDS ring); smaller tiles the register-staged
+// kernel with 4 waves.
 const GemmConfig* tile_with(int kind, int bm, int64_t tiles, int fa, int fb, int bt = 0) {
-    if (bm == 256 && bt) {
-        const GemmConfig* c =
-            find_named(kind == KIND_FP8 ? "tile_fp8_256x256x128_w2x4_bt" : "tile_f16_256x256x64_w2x4_bt", kind, 0,
-                       fa, fb, 1);
-        if (c) return c;
-    } else if (bm == 256) {
-        const bool direct = kind == KIND_F16 && tiles >= 2 * kNumCUs;
-        const char* want = direct ? "dma_f16_256x256x32_s4"
-                                  : (kind == KIND_FP8 ? "tile_fp8_256x256x128_w2x4" : "tile_f16_256x256x64_w2x4");
-        const GemmConfig* c = find_named(want, kind, 0, fa, fb);
-        if (c) return c;
+    (void)tiles;
+    if (bm == 256) {
+        const char* want = kind == KIND_FP8 ? (bt ? "pp_fp8_256x256x64_bt" : "pp_fp8_256x256x64")
+                                            : (bt ? "pp_f16_256x256x32_bt" : "pp_f16_256x256x32");
+        if (const GemmConfig* c = find_named(want, kind, 0, fa, fb, bt)) return c;
     }
     int nt = 0;
     const GemmConfig* tt = tile_configs(&nt);
@@ -117,9 +110,7 @@ const GemmConfig* select_config(int kind, int out_dtype, int64_t M, int64_t N, i
                 if (serves(vt[i], kind, fa, fb, 1) && M <= vt[i].bm && (!best || vt[i].bm < best->bm)) best = &vt[i];
             if (best) return best;
         }
-        // Tiles as for row-major B, except that a 256x256 grid covering 3/4
-        // of the CUs already beats 128x128 tiles (E4M3 3000x4096x4096: 66.6 us
-        // on 192 tiles vs 71.4 us on 768).
+        // Tiles as for row-major B.
         static const int bt_sizes[] = {256, 128, 64};
         for (int bm : bt_sizes) {
             const int64_t tm = (M + bm - 1) / bm, tn = (N + bm - 1) / bm;
@@ -142,12 +133,15 @@ const GemmConfig* select_config(int kind, int out_dtype, int64_t M, int64_t N, i
         }
         if (best) return best;
     }
+    // 256x256 tiles already from 3/4 of the CUs (E4M3 3000x4096x4096: 61.3 us
+    // on 192 ping-pong tiles vs 72.7 us on 768 tiles of 128x128).
     static const int sizes[] = {256, 128, 64};
     for (int bm : sizes) {
         const int64_t tm = (M + bm - 1) / bm, tn = (N + bm - 1) / bm;
         const double useful = (double)M * (double)N;
         const double padded = (double)(tm * bm) * (double)(tn * bm);
-        if (tm * tn >= kNumCUs && useful >= 0.75 * padded) {
+        const int64_t min_tiles = bm == 256 ? kNumCUs * 3 / 4 : kNumCUs;
+        if (tm * tn >= min_tiles && useful >= 0.75 * padded) {
             if (const GemmConfig* c = tile_with(kind, bm, tm * tn, fa, fb)) return c;
         }
     }

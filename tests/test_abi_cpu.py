@@ -231,7 +231,7 @@ def test_select_config_formats():
             for (M, N, K) in [(1, 4096, 4096), (4, 4096, 4096), (16, 4096, 4096), (65, 4096, 4096),
                               (3000, 4096, 4096), (4096, 4096, 4096), (16384, 12288, 4096)]:
                 name = g.select_config_fmt(g.KIND_FP8, g.OUT_E5M2, M, N, K, fa, fb)
-                assert name.startswith(("stream_fp8", "tile_fp8", "dma_fp8")), name
+                assert name.startswith(("stream_fp8", "tile_fp8", "dma_fp8", "pp_fp8")), name
     assert g.select_config_fmt(g.KIND_FP8, g.OUT_F16, 4096, 4096, 4096, 0, 0) == \
         g.select_config(g.KIND_FP8, g.OUT_F16, 4096, 4096, 4096)
 
@@ -268,15 +268,16 @@ def test_select_config_rules():
     assert sel(g.KIND_F16, g.OUT_F16, 16, 12288, 4096) == "tile_f16_64x64x64_w2x2"
     assert sel(g.KIND_F16, g.OUT_F16, 5, 12288, 4096) == "tile_f16_64x64x64_w2x2"
     assert sel(g.KIND_FP8, g.OUT_E4M3, 1, 4096, 4096).startswith("stream_fp8_m1_")
-    # 4096^2 fills the chip with 256x256 tiles (256 tiles): FP8 always runs
-    # them on the 8-wave register-staged kernel, FP16 too for one round of
-    # tiles and on the direct-load kernel for larger grids
-    assert sel(g.KIND_FP8, g.OUT_E4M3, 4096, 4096, 4096) == "tile_fp8_256x256x128_w2x4"
-    assert sel(g.KIND_F16, g.OUT_F16, 4096, 4096, 4096) == "tile_f16_256x256x64_w2x4"
-    assert sel(g.KIND_FP8, g.OUT_F16, 16384, 12288, 4096) == "tile_fp8_256x256x128_w2x4"
-    assert sel(g.KIND_F16, g.OUT_F16, 8192, 8192, 8192) == "dma_f16_256x256x32_s4"
-    # M = 3000 gives 192 tiles of 256 (not enough): one size down
-    assert sel(g.KIND_FP8, g.OUT_E4M3, 3000, 4096, 4096).startswith("tile_fp8_128x128")
+    # 4096^2 fills the chip with 256x256 tiles (256 tiles): they run on the
+    # ping-pong kernel, FP8 and FP16 alike, and so do larger grids
+    assert sel(g.KIND_FP8, g.OUT_E4M3, 4096, 4096, 4096) == "pp_fp8_256x256x64"
+    assert sel(g.KIND_F16, g.OUT_F16, 4096, 4096, 4096) == "pp_f16_256x256x32"
+    assert sel(g.KIND_FP8, g.OUT_F16, 16384, 12288, 4096) == "pp_fp8_256x256x64"
+    assert sel(g.KIND_F16, g.OUT_F16, 8192, 8192, 8192) == "pp_f16_256x256x32"
+    # M = 3000 gives 192 tiles of 256, 3/4 of the CUs: still 256x256 tiles
+    assert sel(g.KIND_FP8, g.OUT_E4M3, 3000, 4096, 4096) == "pp_fp8_256x256x64"
+    # 2048^2: 64 tiles of 256, 256 of 128
+    assert sel(g.KIND_FP8, g.OUT_E4M3, 2048, 2048, 4096).startswith("tile_fp8_128x128")
     # small problems take the smallest tile
     assert sel(g.KIND_FP8, g.OUT_F32, 1024, 1024, 1024).startswith("tile_fp8_64x64")
     assert sel(g.KIND_F16, g.OUT_F32, 256, 256, 256).startswith("tile_f16_64x64")
@@ -287,7 +288,7 @@ def test_select_config_override(monkeypatch):
     monkeypatch.setenv("LIBGEMM_CONFIG", "tile_fp8_128x128x128_w2x2")
     assert g.select_config(g.KIND_FP8, g.OUT_F32, 4096, 4096, 4096) == "tile_fp8_128x128x128_w2x2"
     # an override that cannot serve the request is ignored
-    assert g.select_config(g.KIND_F16, g.OUT_F32, 4096, 4096, 4096) == "tile_f16_256x256x64_w2x4"
+    assert g.select_config(g.KIND_F16, g.OUT_F32, 4096, 4096, 4096) == "pp_f16_256x256x32"
     monkeypatch.setenv("LIBGEMM_CONFIG", "stream_f16_m1_c64_t1024")
     assert g.select_config(g.KIND_F16, g.OUT_F16, 8, 100, 100) == "tile_f16_64x64x64_w2x2"
     monkeypatch.setenv("LIBGEMM_CONFIG", "stream_f16_m8_c64_t256")      # still selectable by name
@@ -336,15 +337,15 @@ def test_kmajor_selector():
     assert g.select_config_bt(g.KIND_FP8, g.OUT_E4M3, 1, 4096, 4096) == "gemv_bt_fp8_m1_r4_u4"
     assert g.select_config_bt(g.KIND_FP8, g.OUT_E4M3, 3, 4096, 4096) == "gemv_coop_fp8_m4_r4_w4"
     assert g.select_config_bt(g.KIND_FP8, g.OUT_E4M3, 8, 4096, 4096) == "gemv_coop_fp8_m8_r2_w4"
-    assert g.select_config_bt(g.KIND_FP8, g.OUT_E4M3, 4096, 4096, 4096) == "tile_fp8_256x256x128_w2x4_bt"
-    assert g.select_config_bt(g.KIND_FP8, g.OUT_E4M3, 3000, 4096, 4096) == "tile_fp8_256x256x128_w2x4_bt"
-    assert g.select_config_bt(g.KIND_F16, g.OUT_F16, 4096, 4096, 4096) == "tile_f16_256x256x64_w2x4_bt"
+    assert g.select_config_bt(g.KIND_FP8, g.OUT_E4M3, 4096, 4096, 4096) == "pp_fp8_256x256x64_bt"
+    assert g.select_config_bt(g.KIND_FP8, g.OUT_E4M3, 3000, 4096, 4096) == "pp_fp8_256x256x64_bt"
+    assert g.select_config_bt(g.KIND_F16, g.OUT_F16, 4096, 4096, 4096) == "pp_f16_256x256x32_bt"
     assert g.select_config_bt(g.KIND_FP8, g.OUT_F32, 1024, 1024, 1024) == "tile_fp8_64x64x128_w2x2_bt"
     assert g.select_config_bt(g.KIND_FP8, g.OUT_F32, 65, 4096, 4096) == "tile_fp8_64x64x128_w2x2_bt"
     # the row-major selector never returns a K-major configuration, nor the reverse
     assert not g.select_config(g.KIND_FP8, g.OUT_F32, 4096, 4096, 4096).endswith("_bt")
     assert g.select_config(g.KIND_F16, g.OUT_F16, 1, 12288, 4096).startswith("stream_")
-    assert g.select_config(g.KIND_FP8, g.OUT_F32, 3000, 4096, 4096) == "tile_fp8_128x128x128_w2x2"
+    assert g.select_config(g.KIND_FP8, g.OUT_F32, 3000, 4096, 4096) == "pp_fp8_256x256x64"
 
 
 def test_kmajor_splitk_plan_and_validation():

@@ -48,9 +48,9 @@ def scalar(v):
     return torch.tensor([float(np.float32(v))], dtype=torch.float32, device=DEV)
 
 
-FP8_CONFIGS = ["dma_fp8_256x256x64_s4", "dma_fp8_256x256x64_s5", "tile_fp8_256x256x128_w2x4",
+FP8_CONFIGS = ["pp_fp8_256x256x64", "dma_fp8_256x256x64_s4", "dma_fp8_256x256x64_s5", "tile_fp8_256x256x128_w2x4",
                "tile_fp8_128x128x128_w2x2", "tile_fp8_64x64x128_w2x2"]
-F16_CONFIGS = ["dma_f16_256x256x32_s4", "dma_f16_256x256x32_s5", "tile_f16_256x256x64_w2x4",
+F16_CONFIGS = ["pp_f16_256x256x32", "dma_f16_256x256x32_s4", "dma_f16_256x256x32_s5", "tile_f16_256x256x64_w2x4",
                "tile_f16_128x128x64_w2x2", "tile_f16_64x64x64_w2x2"]
 
 # (M, N, K): full tiles; M/N edges with a K tail; an odd number of K tiles;
@@ -102,11 +102,11 @@ def test_f16_config_parity(cfg, monkeypatch):
         check_f16(host(C), R, S, what=f"{cfg} f16 {M}x{N}x{K}")
 
 
-@pytest.mark.parametrize("kind", ["fp8", "f16"])
-def test_direct_load_kernel_offset_operands(kind, monkeypatch):
+@pytest.mark.parametrize("kind,cfg", [("fp8", "dma_fp8_256x256x64_s4"), ("f16", "dma_f16_256x256x32_s4"),
+                                      ("fp8", "pp_fp8_256x256x64"), ("f16", "pp_f16_256x256x32")])
+def test_direct_load_kernel_offset_operands(kind, cfg, monkeypatch):
     """Operands starting 16 bytes into an allocation (aligned) and 2 bytes in
     (unaligned: handed to the register-staged kernel) give the oracle's result."""
-    cfg = "dma_fp8_256x256x64_s4" if kind == "fp8" else "dma_f16_256x256x32_s4"
     monkeypatch.setenv("LIBGEMM_CONFIG", cfg)
     M, N, K = 270, 288, 320
     for shift in (16, 2):

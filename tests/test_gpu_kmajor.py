@@ -288,9 +288,9 @@ def test_gemm_fp8_bt_4096_against_oracle_and_deterministic():
 
 # ----------------------------------------- every K-major configuration forced
 
-FP8_BT_CONFIGS = ["dma_fp8_256x256x64_s4_bt", "tile_fp8_256x256x128_w2x4_bt", "tile_fp8_128x128x128_w2x2_bt",
+FP8_BT_CONFIGS = ["pp_fp8_256x256x64_bt", "dma_fp8_256x256x64_s4_bt", "tile_fp8_256x256x128_w2x4_bt", "tile_fp8_128x128x128_w2x2_bt",
                   "tile_fp8_64x64x128_w2x2_bt"]
-F16_BT_CONFIGS = ["dma_f16_256x256x32_s4_bt", "tile_f16_256x256x64_w2x4_bt", "tile_f16_128x128x64_w2x2_bt",
+F16_BT_CONFIGS = ["pp_f16_256x256x32_bt", "dma_f16_256x256x32_s4_bt", "tile_f16_256x256x64_w2x4_bt", "tile_f16_128x128x64_w2x2_bt",
                   "tile_f16_64x64x64_w2x2_bt"]
 # full tiles; M/N edges with a K tail; odd K tile counts; a single partial K
 # tile; K not a multiple of 16 bytes (element loads / the register-staged kernel)
@@ -331,23 +331,25 @@ def test_f16_bt_config_parity(cfg, monkeypatch):
         check_f16(run_f16_bt(a16, b16, g.OUT_F16), R, S, what=f"{cfg} f16 {M}x{N}x{K}")
 
 
-@pytest.mark.parametrize("kind", ["fp8", "f16"])
-def test_dma_bt_matches_row_major_dma_bitwise(kind, monkeypatch):
-    """The direct-load kernel with K-major B and with row-major B feed the
-    same operand values in the same k order to the same MFMAs."""
-    say(f"dma {kind} K-major vs row-major, 1024 x 768 x 512")
+@pytest.mark.parametrize("kind,family", [("fp8", "dma"), ("f16", "dma"), ("fp8", "pp"), ("f16", "pp")])
+def test_dma_bt_matches_row_major_dma_bitwise(kind, family, monkeypatch):
+    """The direct-load and ping-pong kernels with K-major B and with row-major
+    B feed the same operand values in the same k order to the same MFMAs."""
+    say(f"{family} {kind} K-major vs row-major, 1024 x 768 x 512")
     M, N, K = 1024, 768, 512
     if kind == "fp8":
         a = dev(wl.random_e4m3_codes((M, K), 5))
         b = dev(wl.random_e4m3_codes((K, N), 6))
         s = scalar(0.25)
         run = lambda bb, c, bt: (g.gemm_fp8_scaled_bt if bt else g.gemm_fp8_scaled)(a, bb, s, s, c)  # noqa: E731
-        names = ("dma_fp8_256x256x64_s4", "dma_fp8_256x256x64_s4_bt")
+        names = (("dma_fp8_256x256x64_s4", "dma_fp8_256x256x64_s4_bt") if family == "dma"
+                 else ("pp_fp8_256x256x64", "pp_fp8_256x256x64_bt"))
     else:
         a = dev(wl.random_f16((M, K), 5))
         b = dev(wl.random_f16((K, N), 6))
         run = lambda bb, c, bt: (g.gemm_f16_bt if bt else g.gemm_f16)(a, bb, c)  # noqa: E731
-        names = ("dma_f16_256x256x32_s4", "dma_f16_256x256x32_s4_bt")
+        names = (("dma_f16_256x256x32_s4", "dma_f16_256x256x32_s4_bt") if family == "dma"
+                 else ("pp_f16_256x256x32", "pp_f16_256x256x32_bt"))
     c1 = torch.empty(M, N, device=DEV, dtype=torch.float32)
     c2 = torch.empty_like(c1)
     monkeypatch.setenv("LIBGEMM_CONFIG", names[0])
@@ -490,7 +492,7 @@ PAIRS = [(g.FMT_E4M3, g.FMT_E4M3), (g.FMT_E4M3, g.FMT_E5M2), (g.FMT_E5M2, g.FMT_
 # M <= 4 and M <= 8, by the selector) and each K-major tile configuration
 FMT_SHAPES = [(None, 1, 1000, 512), (None, 4, 520, 640), (None, 8, 300, 256),
               ("tile_fp8_64x64x128_w2x2_bt", 100, 200, 256), ("tile_fp8_128x128x128_w2x2_bt", 300, 272, 384),
-              ("tile_fp8_256x256x128_w2x4_bt", 257, 512, 320)]
+              ("tile_fp8_256x256x128_w2x4_bt", 257, 512, 320), ("pp_fp8_256x256x64_bt", 300, 272, 192)]
 
 
 def fp8_codes(fmt, shape, seed):
