@@ -38,7 +38,8 @@ extern "C" {
 /* ------------------------------------------------------------ statuses */
 #define GEMM_OK 0
 #define GEMM_ERR_NULL (-1)        /* a required pointer is NULL                          */
-#define GEMM_ERR_DIM (-2)         /* a dimension is negative or above 2^31 - 1             */
+#define GEMM_ERR_DIM (-2)         /* a dimension is negative or above 2^31 - 1, or an      */
+                                  /* operand or output would span 2^62 bytes or more      */
 #define GEMM_ERR_DTYPE (-3)       /* unknown out_dtype, or one the entry point cannot write */
 #define GEMM_ERR_SCALE (-4)       /* sOut is NULL while out_dtype is an FP8 output         */
 #define GEMM_ERR_LAUNCH (-5)      /* the HIP runtime rejected a kernel launch              */

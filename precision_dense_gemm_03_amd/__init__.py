@@ -229,9 +229,15 @@ def gemm_f16(A, B, C, stream=None):
     return C
 
 
-def _u8(t):
+def _u8(t, fmt=None):
+    """The uint8 view of FP8 codes. A torch float8 tensor must be of format
+    fmt when one is given (FMT_E4M3 / FMT_E5M2): its bits are not re-encoded."""
     torch = _torch()
     if t.dtype in (torch.float8_e4m3fn, torch.float8_e5m2):
+        have = FMT_E5M2 if t.dtype == torch.float8_e5m2 else FMT_E4M3
+        if fmt is not None and int(fmt) != have:
+            want = "E5M2" if int(fmt) == FMT_E5M2 else "E4M3"
+            raise ValueError(f"a {t.dtype} tensor was passed where {want} codes are expected")
         return t.view(torch.uint8)
     if t.dtype != torch.uint8:
         raise ValueError("FP8 tensors must be uint8 codes or torch float8 tensors")
@@ -241,7 +247,7 @@ def _u8(t):
 def gemm_fp8_scaled(A, B, sA, sB, C, sOut=None, stream=None, out_fmt=None):
     """C = (sA*A) @ (sB*B) for E4M3 A[M,K], B[K,N]; sA, sB (and sOut for an
     FP8 C) are one-element float32 device tensors."""
-    A, B = _u8(A), _u8(B)
+    A, B = _u8(A, FMT_E4M3), _u8(B, FMT_E4M3)
     out = _out_dtype(C, out_fmt)
     Cv = _u8(C) if out in (OUT_E4M3, OUT_E5M2) else C
     M, N, K = _dims(A, B, Cv)
@@ -253,7 +259,7 @@ def gemm_fp8_scaled(A, B, sA, sB, C, sOut=None, stream=None, out_fmt=None):
 def gemm_fp8_scaled_bt(A, Bt, sA, sB, C, sOut=None, stream=None, out_fmt=None):
     """gemm_fp8_scaled with B given K-major: C = (sA*A) @ (sB*Bt).T for E4M3
     A[M,K] and Bt[N,K]."""
-    A, Bt = _u8(A), _u8(Bt)
+    A, Bt = _u8(A, FMT_E4M3), _u8(Bt, FMT_E4M3)
     out = _out_dtype(C, out_fmt)
     Cv = _u8(C) if out in (OUT_E4M3, OUT_E5M2) else C
     M, N, K = _dims_bt(A, Bt, Cv)
@@ -264,7 +270,7 @@ def gemm_fp8_scaled_bt(A, Bt, sA, sB, C, sOut=None, stream=None, out_fmt=None):
 
 def gemm_fp8_fmt_bt(A, fmt_a, Bt, fmt_b, sA, sB, C, sOut=None, stream=None, out_fmt=None):
     """gemm_fp8_scaled_bt with A in FP8 format fmt_a and Bt in fmt_b (FMT_E4M3 / FMT_E5M2)."""
-    A, Bt = _u8(A), _u8(Bt)
+    A, Bt = _u8(A, fmt_a), _u8(Bt, fmt_b)
     out = _out_dtype(C, out_fmt)
     Cv = _u8(C) if out in (OUT_E4M3, OUT_E5M2) else C
     M, N, K = _dims_bt(A, Bt, Cv)
@@ -281,7 +287,7 @@ def quantize_fp8_transposed_fmt(x, scale, fmt, q=None, stream=None):
     rows, cols = _rows_cols(x)
     if q is None:
         q = torch.empty((cols, rows), dtype=torch.uint8, device=x.device)
-    qv = _u8(q)
+    qv = _u8(q, fmt)
     if qv.numel() != x.numel():
         raise ValueError("q must have as many elements as x")
     _check(lib().quantize_fp8_transposed_fmt(_ptr(x), rows, cols, _ptr(scale), _ptr(qv), int(fmt),
@@ -316,7 +322,7 @@ def quantize_fp8_transposed(x, scale, q=None, stream=None):
     rows, cols = _rows_cols(x)
     if q is None:
         q = torch.empty((cols, rows), dtype=torch.uint8, device=x.device)
-    qv = _u8(q)
+    qv = _u8(q, FMT_E4M3)
     if qv.numel() != x.numel():
         raise ValueError("q must have as many elements as x")
     _check(lib().quantize_fp8_transposed(_ptr(x), rows, cols, _ptr(scale), _ptr(qv), _stream_handle(stream)),
@@ -326,7 +332,7 @@ def quantize_fp8_transposed(x, scale, q=None, stream=None):
 
 def gemm_fp8_fmt(A, fmt_a, B, fmt_b, sA, sB, C, sOut=None, stream=None, out_fmt=None):
     """gemm_fp8_scaled with A in FP8 format fmt_a and B in fmt_b (FMT_E4M3 / FMT_E5M2)."""
-    A, B = _u8(A), _u8(B)
+    A, B = _u8(A, fmt_a), _u8(B, fmt_b)
     out = _out_dtype(C, out_fmt)
     Cv = _u8(C) if out in (OUT_E4M3, OUT_E5M2) else C
     M, N, K = _dims(A, B, Cv)
@@ -338,7 +344,7 @@ def gemm_fp8_fmt(A, fmt_a, B, fmt_b, sA, sB, C, sOut=None, stream=None, out_fmt=
 def gemm_fp8_channel(A, fmt_a, B, fmt_b, sA, sB, C, sOut=None, stream=None, out_fmt=None):
     """gemm_fp8_fmt with per-channel scales: sA float32[M] (one per row of A),
     sB float32[N] (one per column of B); sOut stays one element."""
-    A, B = _u8(A), _u8(B)
+    A, B = _u8(A, fmt_a), _u8(B, fmt_b)
     out = _out_dtype(C, out_fmt)
     Cv = _u8(C) if out in (OUT_E4M3, OUT_E5M2) else C
     M, N, K = _dims(A, B, Cv)
@@ -367,7 +373,7 @@ def quantize_fp8_channel(x, scale, axis, fmt, q=None, stream=None):
         raise ValueError("one float32 scale per channel")
     if q is None:
         q = torch.empty(x.shape, dtype=torch.uint8, device=x.device)
-    qv = _u8(q)
+    qv = _u8(q, fmt)
     if qv.numel() != x.numel():
         raise ValueError("q must have as many elements as x")
     _check(lib().quantize_fp8_channel(_ptr(x), rows, cols, int(axis), _ptr(scale), _ptr(qv), int(fmt),
@@ -422,7 +428,7 @@ def _ws_args(workspace):
 def gemm_fp8_splitk(A, fmt_a, B, fmt_b, sA, sB, C, sOut=None, workspace=None, stream=None, out_fmt=None):
     """gemm_fp8_fmt that splits K over a workspace when the shape has too few
     output tiles; workspace=None allocates one of the planned size."""
-    A, B = _u8(A), _u8(B)
+    A, B = _u8(A, fmt_a), _u8(B, fmt_b)
     out = _out_dtype(C, out_fmt)
     Cv = _u8(C) if out in (OUT_E4M3, OUT_E5M2) else C
     M, N, K = _dims(A, B, Cv)
@@ -478,7 +484,7 @@ def quantize_fp8(x, scale, q=None, stream=None):
         raise ValueError("quantize_fp8 takes float32 input")
     if q is None:
         q = torch.empty(x.shape, dtype=torch.uint8, device=x.device)
-    qv = _u8(q)
+    qv = _u8(q, FMT_E4M3)
     if qv.numel() != x.numel():
         raise ValueError("q must have as many elements as x")
     _check(lib().quantize_fp8(_ptr(x), x.numel(), _ptr(scale), _ptr(qv), _stream_handle(stream)), "quantize_fp8")
@@ -492,7 +498,7 @@ def quantize_fp8_fmt(x, scale, fmt, q=None, stream=None):
         raise ValueError("quantize_fp8_fmt takes float32 input")
     if q is None:
         q = torch.empty(x.shape, dtype=torch.uint8, device=x.device)
-    qv = _u8(q)
+    qv = _u8(q, fmt)
     if qv.numel() != x.numel():
         raise ValueError("q must have as many elements as x")
     _check(lib().quantize_fp8_fmt(_ptr(x), x.numel(), _ptr(scale), _ptr(qv), int(fmt), _stream_handle(stream)),
@@ -570,7 +576,7 @@ def _workspace_bt(kind, out, M, N, K, workspace, device):
 def gemm_fp8_splitk_bt(A, Bt, sA, sB, C, sOut=None, workspace=None, stream=None, out_fmt=None):
     """gemm_fp8_scaled_bt that splits K over a workspace for mid-M shapes;
     workspace=None allocates one of the planned size."""
-    A, Bt = _u8(A), _u8(Bt)
+    A, Bt = _u8(A, FMT_E4M3), _u8(Bt, FMT_E4M3)
     out = _out_dtype(C, out_fmt)
     Cv = _u8(C) if out in (OUT_E4M3, OUT_E5M2) else C
     M, N, K = _dims_bt(A, Bt, Cv)

@@ -22,6 +22,19 @@ constexpr int kMaxDevices = 64;
 
 bool dim_ok(int64_t d) { return d >= 0 && d <= kMaxDim; }
 
+// Byte counts are formed only after this check: an operand of 2^62 bytes or
+// more is a GEMM_ERR_DIM (no device holds one), so every later product of a
+// dimension pair and an element size fits in int64.
+constexpr unsigned __int128 kMaxBytes = (unsigned __int128)1 << 62;
+bool bytes_ok(int64_t a, int64_t b, int64_t es) {
+    if (a < 0 || b < 0) return false;
+    return (unsigned __int128)a * (unsigned __int128)b * (unsigned __int128)es < kMaxBytes;
+}
+// A[M,K] with element size ea, B[K,N] with eb, C[M,N] with ec.
+bool gemm_sizes_ok(int64_t M, int64_t N, int64_t K, int64_t ea, int64_t eb, int64_t ec) {
+    return dim_ok(M) && dim_ok(N) && dim_ok(K) && bytes_ok(M, K, ea) && bytes_ok(K, N, eb) && bytes_ok(M, N, ec);
+}
+
 // Byte ranges [p, p+n) and [q, q+m) overlap (empty ranges never do).
 bool overlaps(const void* p, int64_t n, const void* q, int64_t m) {
     if (!p || !q || n <= 0 || m <= 0) return false;
@@ -106,7 +119,7 @@ extern "C" {
 static int gemm_f16_common(const void* A, const void* B, void* C, int out_dtype, int64_t M, int64_t N, int64_t K,
                            hipStream_t stream, int b_kmajor) {
     if (out_dtype != GEMM_OUT_F32 && out_dtype != GEMM_OUT_F16) return GEMM_ERR_DTYPE;
-    if (!dim_ok(M) || !dim_ok(N) || !dim_ok(K)) return GEMM_ERR_DIM;
+    if (!gemm_sizes_ok(M, N, K, 2, 2, out_size(out_dtype))) return GEMM_ERR_DIM;
     if (M > 0 && N > 0) {
         if (!C) return GEMM_ERR_NULL;
         if (K > 0 && (!A || !B)) return GEMM_ERR_NULL;
@@ -138,7 +151,7 @@ static int gemm_fp8_common(const uint8_t* A, int fmt_a, const uint8_t* B, int fm
     if (out_dtype < GEMM_OUT_F32 || out_dtype > GEMM_OUT_E5M2) return GEMM_ERR_DTYPE;
     if ((fmt_a != GEMM_FMT_E4M3 && fmt_a != GEMM_FMT_E5M2) || (fmt_b != GEMM_FMT_E4M3 && fmt_b != GEMM_FMT_E5M2))
         return GEMM_ERR_DTYPE;
-    if (!dim_ok(M) || !dim_ok(N) || !dim_ok(K)) return GEMM_ERR_DIM;
+    if (!gemm_sizes_ok(M, N, K, 1, 1, out_size(out_dtype))) return GEMM_ERR_DIM;
     if (M > 0 && N > 0) {
         if (!C || !sA || !sB) return GEMM_ERR_NULL;
         if (fp8_out(out_dtype) && !sOut) return GEMM_ERR_SCALE;
@@ -200,7 +213,7 @@ static int gemm_f16_splitk_common(const void* A, const void* B, void* C, int out
                                   int64_t K, void* workspace, int64_t workspace_bytes, hipStream_t stream,
                                   int b_kmajor) {
     if (out_dtype != GEMM_OUT_F32 && out_dtype != GEMM_OUT_F16) return GEMM_ERR_DTYPE;
-    if (!dim_ok(M) || !dim_ok(N) || !dim_ok(K)) return GEMM_ERR_DIM;
+    if (!gemm_sizes_ok(M, N, K, 2, 2, out_size(out_dtype))) return GEMM_ERR_DIM;
     if (M > 0 && N > 0) {
         if (!C) return GEMM_ERR_NULL;
         if (K > 0 && (!A || !B)) return GEMM_ERR_NULL;
@@ -232,14 +245,14 @@ static int64_t guard_ws_a16(int64_t, int64_t, int64_t) { return 256; }
 static int64_t guard_ws_b16(int64_t M, int64_t, int64_t K) { return 256 + round256(M * K * 2); }
 
 int64_t gemm_f16_guarded_workspace_size(int64_t M, int64_t N, int64_t K) {
-    if (!dim_ok(M) || !dim_ok(N) || !dim_ok(K)) return GEMM_ERR_DIM;
+    if (!gemm_sizes_ok(M, N, K, 4, 4, 4)) return GEMM_ERR_DIM;
     return guard_ws_b16(M, N, K) + round256(K * N * 2);
 }
 
 int gemm_f16_guarded(const float* A, const float* B, void* C, int out_dtype, int64_t M, int64_t N, int64_t K,
                      float* scale, void* workspace, int64_t workspace_bytes, hipStream_t stream) {
     if (out_dtype != GEMM_OUT_F32 && out_dtype != GEMM_OUT_F16) return GEMM_ERR_DTYPE;
-    if (!dim_ok(M) || !dim_ok(N) || !dim_ok(K)) return GEMM_ERR_DIM;
+    if (!gemm_sizes_ok(M, N, K, 4, 4, 4)) return GEMM_ERR_DIM;
     if (M == 0 || N == 0) return GEMM_OK;
     if (!C || !workspace) return GEMM_ERR_NULL;
     if (K > 0 && (!A || !B)) return GEMM_ERR_NULL;
@@ -280,7 +293,7 @@ static int splitk_plan_common(int kind, int out_dtype, int64_t M, int64_t N, int
         return GEMM_ERR_DTYPE;
     if ((fmt_a != GEMM_FMT_E4M3 && fmt_a != GEMM_FMT_E5M2) || (fmt_b != GEMM_FMT_E4M3 && fmt_b != GEMM_FMT_E5M2))
         return GEMM_ERR_DTYPE;
-    if (!dim_ok(M) || !dim_ok(N) || !dim_ok(K)) return GEMM_ERR_DIM;
+    if (!gemm_sizes_ok(M, N, K, 2, 2, 4)) return GEMM_ERR_DIM;
     const SplitPlan p = plan_splitk(kind, out_dtype, M, N, K, fmt_a, fmt_b, b_kmajor);
     if (!p.cfg) return GEMM_ERR_UNSUPPORTED;
     if (buf && buflen > 0) {
@@ -312,7 +325,7 @@ int amax_scale_channel_f32(const float* x, int64_t rows, int64_t cols, int axis,
                            int pow2, hipStream_t stream) {
     if (fmt != GEMM_FMT_E4M3 && fmt != GEMM_FMT_E5M2) return GEMM_ERR_DTYPE;
     if (axis != GEMM_AXIS_ROW && axis != GEMM_AXIS_COL) return GEMM_ERR_DIM;
-    if (!dim_ok(rows) || !dim_ok(cols)) return GEMM_ERR_DIM;
+    if (!dim_ok(rows) || !dim_ok(cols) || !bytes_ok(rows, cols, 4)) return GEMM_ERR_DIM;
     const int64_t nch = axis == GEMM_AXIS_ROW ? rows : cols;
     if (nch == 0) return GEMM_OK;
     if (!amax) return GEMM_ERR_NULL;
@@ -330,7 +343,7 @@ int quantize_fp8_channel(const float* x, int64_t rows, int64_t cols, int axis, c
                          int fmt, hipStream_t stream) {
     if (fmt != GEMM_FMT_E4M3 && fmt != GEMM_FMT_E5M2) return GEMM_ERR_DTYPE;
     if (axis != GEMM_AXIS_ROW && axis != GEMM_AXIS_COL) return GEMM_ERR_DIM;
-    if (!dim_ok(rows) || !dim_ok(cols)) return GEMM_ERR_DIM;
+    if (!dim_ok(rows) || !dim_ok(cols) || !bytes_ok(rows, cols, 4)) return GEMM_ERR_DIM;
     const int64_t n = rows * cols;
     if (n == 0) return GEMM_OK;
     if (!x || !scale || !q) return GEMM_ERR_NULL;
@@ -343,7 +356,7 @@ int quantize_fp8_channel(const float* x, int64_t rows, int64_t cols, int axis, c
 
 int quantize_fp8_fmt(const float* x, int64_t n, const float* scale, uint8_t* q, int fmt, hipStream_t stream) {
     if (fmt != GEMM_FMT_E4M3 && fmt != GEMM_FMT_E5M2) return GEMM_ERR_DTYPE;
-    if (n < 0) return GEMM_ERR_DIM;
+    if (!bytes_ok(n, 1, 4)) return GEMM_ERR_DIM;
     if (n == 0) return GEMM_OK;
     if (!x || !scale || !q) return GEMM_ERR_NULL;
     if (overlaps(q, n, x, 4 * n) || overlaps(q, n, scale, 4)) return GEMM_ERR_ALIAS;
@@ -355,7 +368,7 @@ int quantize_fp8_fmt(const float* x, int64_t n, const float* scale, uint8_t* q, 
 int quantize_fp8_transposed_fmt(const float* x, int64_t rows, int64_t cols, const float* scale, uint8_t* q,
                                 int fmt, hipStream_t stream) {
     if (fmt != GEMM_FMT_E4M3 && fmt != GEMM_FMT_E5M2) return GEMM_ERR_DTYPE;
-    if (!dim_ok(rows) || !dim_ok(cols)) return GEMM_ERR_DIM;
+    if (!dim_ok(rows) || !dim_ok(cols) || !bytes_ok(rows, cols, 4)) return GEMM_ERR_DIM;
     const int64_t n = rows * cols;
     if (n == 0) return GEMM_OK;
     if (!x || !scale || !q) return GEMM_ERR_NULL;
@@ -372,7 +385,7 @@ int quantize_fp8_transposed(const float* x, int64_t rows, int64_t cols, const fl
 
 int pack_b_kmajor(const void* B, int64_t K, int64_t N, int elem_bytes, void* Bt, hipStream_t stream) {
     if (elem_bytes != 1 && elem_bytes != 2) return GEMM_ERR_DTYPE;
-    if (!dim_ok(K) || !dim_ok(N)) return GEMM_ERR_DIM;
+    if (!dim_ok(K) || !dim_ok(N) || !bytes_ok(K, N, elem_bytes)) return GEMM_ERR_DIM;
     const int64_t bytes = K * N * elem_bytes;
     if (bytes == 0) return GEMM_OK;
     if (!B || !Bt) return GEMM_ERR_NULL;
@@ -388,7 +401,7 @@ int quantize_fp8(const float* x, int64_t n, const float* scale, uint8_t* q, hipS
 
 int amax_scale_f32(const float* x, int64_t n, float* amax, float* scale, int fmt, int pow2, hipStream_t stream) {
     if (fmt != GEMM_FMT_E4M3 && fmt != GEMM_FMT_E5M2) return GEMM_ERR_DTYPE;
-    if (n < 0) return GEMM_ERR_DIM;
+    if (!bytes_ok(n, 1, 4)) return GEMM_ERR_DIM;
     if (!amax) return GEMM_ERR_NULL;
     if (n > 0 && !x) return GEMM_ERR_NULL;
     if (overlaps(amax, 4, x, 4 * n) || overlaps(scale, 4, x, 4 * n) || overlaps(amax, 4, scale, 4))
@@ -406,7 +419,7 @@ const char* gemm_status_str(int status) {
     switch (status) {
         case GEMM_OK: return "ok";
         case GEMM_ERR_NULL: return "a required pointer is NULL";
-        case GEMM_ERR_DIM: return "a dimension is negative or above 2^31-1";
+        case GEMM_ERR_DIM: return "a dimension is negative or above 2^31-1, or an operand spans 2^62 bytes or more";
         case GEMM_ERR_DTYPE: return "unsupported output dtype";
         case GEMM_ERR_SCALE: return "sOut is required for FP8 output";
         case GEMM_ERR_LAUNCH: return "kernel launch failed";
@@ -425,7 +438,7 @@ int gemm_select_config_fmt(int kind, int out_dtype, int64_t M, int64_t N, int64_
         return GEMM_ERR_DTYPE;
     if ((fmt_a != GEMM_FMT_E4M3 && fmt_a != GEMM_FMT_E5M2) || (fmt_b != GEMM_FMT_E4M3 && fmt_b != GEMM_FMT_E5M2))
         return GEMM_ERR_DTYPE;
-    if (!dim_ok(M) || !dim_ok(N) || !dim_ok(K)) return GEMM_ERR_DIM;
+    if (!gemm_sizes_ok(M, N, K, 2, 2, 4)) return GEMM_ERR_DIM;
     if (!buf || buflen <= 0) return GEMM_ERR_NULL;
     const GemmConfig* cfg = select_config(kind, out_dtype, M, N, K, fmt_a, fmt_b);
     if (!cfg) return GEMM_ERR_UNSUPPORTED;
@@ -437,7 +450,7 @@ int gemm_select_config_bt(int kind, int out_dtype, int64_t M, int64_t N, int64_t
     if (kind != KIND_F16 && kind != KIND_FP8) return GEMM_ERR_DTYPE;
     if (out_dtype < GEMM_OUT_F32 || out_dtype > GEMM_OUT_E5M2 || (kind == KIND_F16 && fp8_out(out_dtype)))
         return GEMM_ERR_DTYPE;
-    if (!dim_ok(M) || !dim_ok(N) || !dim_ok(K)) return GEMM_ERR_DIM;
+    if (!gemm_sizes_ok(M, N, K, 2, 2, 4)) return GEMM_ERR_DIM;
     if (!buf || buflen <= 0) return GEMM_ERR_NULL;
     const GemmConfig* cfg = select_config(kind, out_dtype, M, N, K, GEMM_FMT_E4M3, GEMM_FMT_E4M3, 1);
     if (!cfg) return GEMM_ERR_UNSUPPORTED;

@@ -132,7 +132,10 @@ __global__ __launch_bounds__(kThreads) void quantize_kernel(const float* __restr
 // words land in 64 distinct banks); then each thread writes two 16-byte pieces
 // of output rows, a wave writing whole 128-byte rows.
 constexpr int kQtRows = 128, kQtCols = 64;
-static_assert(kQtRows % 64 == 0 && kQtRows <= 256, "a thread takes kQtRows / 64 row blocks");
+// The write-out loop covers all kQtCols x (kQtRows / 16) pieces only when the
+// pieces per output row divide the thread count (kQtRows 64, 128 or 256).
+static_assert(kQtRows % 64 == 0 && kQtRows <= 256 && kThreads % (kQtRows / 16) == 0,
+              "a thread takes kQtRows / 64 row blocks and the write-out covers every piece");
 constexpr int kQtPitch = kQtRows + 4;
 
 template <int FMT>

@@ -43,9 +43,6 @@
 namespace libgemm {
 namespace tile {
 
-// The fully register-pipelined loop (two B operand sets) needs more registers
-// than a 256x256 tile leaves; it stays compiled out until it fits.
-constexpr bool kRegisterPipeline = false;
 // 8-wave kernels with K-major B: read the next A operand before the current
 // row block's MFMAs (one more operand register set) and raise the wave's issue
 // priority while it issues MFMAs. Measured on one MI355X (us, K-major B):
@@ -428,45 +425,7 @@ __global__ __launch_bounds__(64 * WM * WN) void gemm_tile_kernel(
 
     const bool offsets_fit = (int64_t)BM * K * ES < (1ll << 31) &&
                              (BT ? (int64_t)BN * K * ES : (int64_t)BK * N * ES) < (1ll << 31);
-    if (kRegisterPipeline && interior_mn && klen % BK == 0 && nk > 0 && offsets_fit) {
-        // Software pipeline, one barrier per K tile. Entering iteration kt:
-        // LDS holds A(kt) in A stage kt%2 and B(kt+1) in B stage (kt+1)%2,
-        // registers hold the B operands of tile kt (bcur) and the global data
-        // of A(kt+1) and B(kt+2). The iteration stores that data to the stages
-        // iteration kt-1 finished reading, issues the loads of A(kt+2) and
-        // B(kt+3), multiplies tile kt and reads the B operands of tile kt+1
-        // into the other register set, so LDS traffic runs under the MFMAs.
-        // Tiles past the end are clamped to the last one (loaded, never used).
-        Op b0[T::KS][T::TN], b1[T::KS][T::TN];
-        const int last = nk - 1;
-        load_a(0);
-        load_b(0);
-        store_a(0);
-        store_b(0);
-        load_b(min(1, last));
-        store_b(1);
-        load_a(min(1, last));
-        load_b(min(2, last));
-        __syncthreads();
-        read_b(0, b0);
-        __syncthreads();
-        auto iteration = [&](int kt, Op (&bcur)[T::KS][T::TN], Op (&bnext)[T::KS][T::TN])
-                             __attribute__((always_inline)) {
-            store_a((kt + 1) & 1);
-            store_b(kt & 1);
-            load_a(min(kt + 2, last));
-            load_b(min(kt + 3, last));
-            mma_tile(kt & 1, bcur);
-            read_b((kt + 1) & 1, bnext);
-            __syncthreads();
-        };
-        int kt = 0;
-        for (; kt + 1 < nk; kt += 2) {
-            iteration(kt, b0, b1);
-            iteration(kt + 1, b1, b0);
-        }
-        if (kt < nk) iteration(kt, b0, b1);
-    } else if (nk > 0) {
+    if (nk > 0) {
         Op bop[T::KS][T::TN];
         // Tile kt+1 is fetched into registers while tile kt is multiplied;
         // the K tail and unaligned operands load each chunk with element

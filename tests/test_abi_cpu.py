@@ -392,3 +392,37 @@ def test_pack_b_kmajor_validation():
     assert L.pack_b_kmajor(None, 4, 4, 2, FAKE2, None) == -1
     assert L.pack_b_kmajor(FAKE, 4, 4, 2, FAKE + 16, None) == -8
     assert L.pack_b_kmajor(None, 0, 4, 1, None, None) == 0
+
+
+def test_byte_counts_that_would_overflow_are_dim_errors():
+    """Operands of 2^62 bytes or more are rejected before any byte count is
+    formed (M * N * 4 for M = N = 2^31 - 1 would not fit in int64)."""
+    L = g.lib()
+    big = 2 ** 31 - 1
+    s = FAKE3 + 4096
+    assert L.gemm_fp8_scaled(FAKE, FAKE2, s, s + 4, None, FAKE3, 0, big, big, 1, None) == -2
+    assert L.gemm_f16(FAKE, FAKE2, FAKE3, 0, big, big, 1, None) == -2
+    assert L.gemm_f16_guarded_workspace_size(big, 4, big) == -2
+    assert L.quantize_fp8(FAKE, 2 ** 60, FAKE2, FAKE3, None) == -2
+    assert L.amax_f32(FAKE, 2 ** 61, FAKE2, None, None) == -2
+    assert L.quantize_fp8_transposed(FAKE, big, big, FAKE2, FAKE3, None) == -2
+    # just below the limit the checks move on (here: the NULL scale)
+    assert L.quantize_fp8(FAKE, 2 ** 60 - 1, None, FAKE3, None) == -1
+
+
+def test_float8_dtype_must_match_the_entry_points_format():
+    """A torch float8 tensor is passed by its bits: the binding refuses one of
+    the other FP8 format instead of decoding E5M2 bits as E4M3 (host check,
+    before any device pointer is taken)."""
+    torch = pytest.importorskip("torch")
+    e5 = torch.zeros((4, 4), dtype=torch.float8_e5m2)
+    e4 = torch.zeros((4, 4), dtype=torch.float8_e4m3fn)
+    with pytest.raises(ValueError, match="E4M3"):
+        g._u8(e5, g.FMT_E4M3)
+    with pytest.raises(ValueError, match="E5M2"):
+        g._u8(e4, g.FMT_E5M2)
+    assert g._u8(e4, g.FMT_E4M3).dtype == torch.uint8
+    assert g._u8(e5, g.FMT_E5M2).dtype == torch.uint8
+    assert g._u8(torch.zeros(3, dtype=torch.uint8), g.FMT_E5M2).dtype == torch.uint8
+    with pytest.raises(ValueError, match="E4M3"):
+        g.gemm_fp8_scaled(e5, e4, None, None, torch.zeros((4, 4)))
