@@ -34,6 +34,10 @@ Functions keep the C names:
     gemm_fp8_splitk_bt(A, Bt, sA, sB, C, sOut=None, workspace=None, stream=None, out_fmt=None)
     gemm_f16_splitk_bt(A, Bt, C, workspace=None, stream=None)
     splitk_plan_bt(kind, out_dtype, M, N, K) -> (config, splits, workspace_bytes)
+  Exact-accumulation FP8 (FP8 codes widened to FP16, FP16 matrix cores):
+    gemm_fp8_exact(A, fmt_a, B, fmt_b, sA, sB, C, sOut=None, stream=None, out_fmt=None)
+    gemm_fp8_exact_bt(A, fmt_a, Bt, fmt_b, sA, sB, C, sOut=None, stream=None, out_fmt=None)
+    select_config_exact(out_dtype, M, N, K, fmt_a=0, fmt_b=0, b_kmajor=0) -> str
 The output dtype of a GEMM is taken from C: float32, float16, or 8-bit codes
 (uint8 or torch.float8_e4m3fn: E4M3; torch.float8_e5m2, or uint8 with
 out_fmt=FMT_E5M2: E5M2). FP8 operands are uint8 codes or torch float8 tensors.
@@ -139,6 +143,12 @@ def lib() -> ctypes.CDLL:
     L.gemm_splitk_plan_bt.restype = i32
     L.gemm_splitk_plan_bt.argtypes = [i32, i32, i64, i64, i64, ctypes.c_char_p, i32, ctypes.POINTER(i32),
                                       ctypes.POINTER(i64)]
+    L.gemm_fp8_exact.restype = i32
+    L.gemm_fp8_exact.argtypes = [vp, i32, vp, i32, vp, vp, vp, vp, i32, i64, i64, i64, vp]
+    L.gemm_fp8_exact_bt.restype = i32
+    L.gemm_fp8_exact_bt.argtypes = [vp, i32, vp, i32, vp, vp, vp, vp, i32, i64, i64, i64, vp]
+    L.gemm_select_config_exact.restype = i32
+    L.gemm_select_config_exact.argtypes = [i32, i64, i64, i64, i32, i32, i32, ctypes.c_char_p, i32]
     _lib = L
     return L
 
@@ -597,3 +607,36 @@ def gemm_f16_splitk_bt(A, Bt, C, workspace=None, stream=None):
     _check(lib().gemm_f16_splitk_bt(_ptr(A), _ptr(Bt), _ptr(C), out, M, N, K, ws, nbytes, _stream_handle(stream)),
            "gemm_f16_splitk_bt")
     return C
+
+
+def gemm_fp8_exact(A, fmt_a, B, fmt_b, sA, sB, C, sOut=None, stream=None, out_fmt=None):
+    """gemm_fp8_fmt with exact products and FP32 additions throughout (the
+    codes widened to FP16 on the FP16 matrix cores, or the FP32-FMA decode
+    kernels)."""
+    A, B = _u8(A, fmt_a), _u8(B, fmt_b)
+    out = _out_dtype(C, out_fmt)
+    Cv = _u8(C) if out in (OUT_E4M3, OUT_E5M2) else C
+    M, N, K = _dims(A, B, Cv)
+    _check(lib().gemm_fp8_exact(_ptr(A), int(fmt_a), _ptr(B), int(fmt_b), _ptr(sA), _ptr(sB), _ptr(sOut), _ptr(Cv),
+                                out, M, N, K, _stream_handle(stream)), "gemm_fp8_exact")
+    return C
+
+
+def gemm_fp8_exact_bt(A, fmt_a, Bt, fmt_b, sA, sB, C, sOut=None, stream=None, out_fmt=None):
+    """gemm_fp8_exact with B given K-major as Bt[N,K]."""
+    A, Bt = _u8(A, fmt_a), _u8(Bt, fmt_b)
+    out = _out_dtype(C, out_fmt)
+    Cv = _u8(C) if out in (OUT_E4M3, OUT_E5M2) else C
+    M, N, K = _dims_bt(A, Bt, Cv)
+    _check(lib().gemm_fp8_exact_bt(_ptr(A), int(fmt_a), _ptr(Bt), int(fmt_b), _ptr(sA), _ptr(sB), _ptr(sOut),
+                                   _ptr(Cv), out, M, N, K, _stream_handle(stream)), "gemm_fp8_exact_bt")
+    return C
+
+
+def select_config_exact(out_dtype: int, M: int, N: int, K: int, fmt_a: int = 0, fmt_b: int = 0,
+                        b_kmajor: int = 0) -> str:
+    """The configuration gemm_fp8_exact (or, with b_kmajor, gemm_fp8_exact_bt) would launch."""
+    buf = ctypes.create_string_buffer(128)
+    _check(lib().gemm_select_config_exact(out_dtype, M, N, K, int(fmt_a), int(fmt_b), int(b_kmajor), buf, len(buf)),
+           "gemm_select_config_exact")
+    return buf.value.decode()

@@ -84,6 +84,17 @@ int run_gemm(int kind, const GemmArgs& a) {
     return status_of(cfg->launch(a));
 }
 
+// The exact-accumulation FP8 mode: validated arguments, the exact selector.
+int run_gemm_exact(const GemmArgs& a) {
+    int st = check_device();
+    if (st != GEMM_OK) return st;
+    if (a.M == 0 || a.N == 0) return GEMM_OK;
+    if (a.K == 0) return status_of(launch_fill_zero(a.C, a.M * a.N, a.out_dtype, a.stream));
+    const GemmConfig* cfg = select_config_exact(a.out_dtype, a.M, a.N, a.K, a.fmt_a, a.fmt_b, a.b_kmajor);
+    if (!cfg) return GEMM_ERR_UNSUPPORTED;
+    return status_of(cfg->launch(a));
+}
+
 int64_t splitk_bytes(const SplitPlan& p, int64_t M, int64_t N) { return p.splits > 1 ? p.splits * M * N * 4 : 0; }
 
 // Workspace entry points: after the caller's arguments were validated, the
@@ -147,7 +158,7 @@ int gemm_f16_bt(const void* A, const void* Bt, void* C, int out_dtype, int64_t M
 static int gemm_fp8_common(const uint8_t* A, int fmt_a, const uint8_t* B, int fmt_b, const float* sA,
                            const float* sB, const float* sOut, void* C, int out_dtype, int64_t M, int64_t N,
                            int64_t K, hipStream_t stream, int channel = 0, void* ws = nullptr,
-                           int64_t ws_bytes = 0, int b_kmajor = 0) {
+                           int64_t ws_bytes = 0, int b_kmajor = 0, int exact = 0) {
     if (out_dtype < GEMM_OUT_F32 || out_dtype > GEMM_OUT_E5M2) return GEMM_ERR_DTYPE;
     if ((fmt_a != GEMM_FMT_E4M3 && fmt_a != GEMM_FMT_E5M2) || (fmt_b != GEMM_FMT_E4M3 && fmt_b != GEMM_FMT_E5M2))
         return GEMM_ERR_DTYPE;
@@ -166,6 +177,7 @@ static int gemm_fp8_common(const uint8_t* A, int fmt_a, const uint8_t* B, int fm
     GemmArgs a{A, B, C, sA, sB, fp8_out(out_dtype) ? sOut : nullptr, out_dtype, M, N, K, stream, fmt_a, fmt_b,
                channel};
     a.b_kmajor = b_kmajor;
+    if (exact) return run_gemm_exact(a);
     if (!ws) return run_gemm(KIND_FP8, a);
     const void* in_ptr[6] = {A, B, C, sA, sB, fp8_out(out_dtype) ? sOut : nullptr};
     const int64_t in_bytes[6] = {M * K, K * N, M * N * out_size(out_dtype), channel ? 4 * M : 4, channel ? 4 * N : 4,
@@ -192,6 +204,29 @@ int gemm_fp8_fmt_bt(const uint8_t* A, int fmt_a, const uint8_t* Bt, int fmt_b, c
 int gemm_fp8_fmt(const uint8_t* A, int fmt_a, const uint8_t* B, int fmt_b, const float* sA, const float* sB,
                  const float* sOut, void* C, int out_dtype, int64_t M, int64_t N, int64_t K, hipStream_t stream) {
     return gemm_fp8_common(A, fmt_a, B, fmt_b, sA, sB, sOut, C, out_dtype, M, N, K, stream);
+}
+
+int gemm_fp8_exact(const uint8_t* A, int fmt_a, const uint8_t* B, int fmt_b, const float* sA, const float* sB,
+                   const float* sOut, void* C, int out_dtype, int64_t M, int64_t N, int64_t K, hipStream_t stream) {
+    return gemm_fp8_common(A, fmt_a, B, fmt_b, sA, sB, sOut, C, out_dtype, M, N, K, stream, 0, nullptr, 0, 0, 1);
+}
+
+int gemm_fp8_exact_bt(const uint8_t* A, int fmt_a, const uint8_t* Bt, int fmt_b, const float* sA, const float* sB,
+                      const float* sOut, void* C, int out_dtype, int64_t M, int64_t N, int64_t K, hipStream_t stream) {
+    return gemm_fp8_common(A, fmt_a, Bt, fmt_b, sA, sB, sOut, C, out_dtype, M, N, K, stream, 0, nullptr, 0, 1, 1);
+}
+
+int gemm_select_config_exact(int out_dtype, int64_t M, int64_t N, int64_t K, int fmt_a, int fmt_b, int b_kmajor,
+                             char* buf, int buflen) {
+    if (out_dtype < GEMM_OUT_F32 || out_dtype > GEMM_OUT_E5M2) return GEMM_ERR_DTYPE;
+    if ((fmt_a != GEMM_FMT_E4M3 && fmt_a != GEMM_FMT_E5M2) || (fmt_b != GEMM_FMT_E4M3 && fmt_b != GEMM_FMT_E5M2))
+        return GEMM_ERR_DTYPE;
+    if (!gemm_sizes_ok(M, N, K, 1, 1, 4)) return GEMM_ERR_DIM;
+    if (!buf || buflen <= 0) return GEMM_ERR_NULL;
+    const GemmConfig* cfg = select_config_exact(out_dtype, M, N, K, fmt_a, fmt_b, b_kmajor ? 1 : 0);
+    if (!cfg) return GEMM_ERR_UNSUPPORTED;
+    std::snprintf(buf, (size_t)buflen, "%s", cfg->name);
+    return GEMM_OK;
 }
 
 int gemm_fp8_splitk(const uint8_t* A, int fmt_a, const uint8_t* B, int fmt_b, const float* sA, const float* sB,

@@ -122,7 +122,9 @@ __device__ __forceinline__ float epilogue_multiplier(const float* sA, const floa
 // the workgroup stores the raw FP32 sum over its K range (no scale, no
 // conversion) into its split's [M, N] slice of the workspace; a reduce kernel
 // then applies the epilogue to the sum of the slices.
-enum EpilogueFlags { EPI_E5M2 = 1, EPI_CHANNEL = 2, EPI_PARTIAL = 4 };
+// EPI_A_E5M2 / EPI_B_E5M2: operand formats of the exact-accumulation FP8
+// mode, whose kernels widen the codes to FP16 as they stage them.
+enum EpilogueFlags { EPI_E5M2 = 1, EPI_CHANNEL = 2, EPI_PARTIAL = 4, EPI_A_E5M2 = 8, EPI_B_E5M2 = 16 };
 
 // Per-tensor multiplier, or with per-channel scales (sA[M], sB[N]) the part
 // common to every element: 1 / sOut for an FP8 output, else 1; the element

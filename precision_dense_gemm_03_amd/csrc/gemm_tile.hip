@@ -36,4 +36,20 @@ const GemmConfig* tile_configs(int* count) {
     return table;
 }
 
+// The exact-accumulation FP8 mode (family 5): FP8 codes widened to FP16 as
+// they are staged, FP16 matrix cores, every FP8 operand pair (formats read at
+// run time). Never chosen by the plain selector; select_config_exact does.
+const GemmConfig* exact_configs(int* count) {
+    static const GemmConfig table[] = {
+        {"exact_fp8_64x64x64_w2x2", KIND_FP8, 5, 64, 64, 64, tile::launch_tile_fp8_exact<64, 64, 64, 2, 2>, kAllFp8Pairs},
+        {"exact_fp8_128x128x64_w2x2", KIND_FP8, 5, 128, 128, 64, tile::launch_tile_fp8_exact<128, 128, 64, 2, 2>, kAllFp8Pairs},
+        {"exact_fp8_256x256x64_w2x4", KIND_FP8, 5, 256, 256, 64, tile::launch_tile_fp8_exact<256, 256, 64, 2, 4>, kAllFp8Pairs},
+        {"exact_fp8_64x64x64_w2x2_bt", KIND_FP8, 5, 64, 64, 64, tile::launch_tile_fp8_exact<64, 64, 64, 2, 2, true>, kAllFp8Pairs, 0, 1},
+        {"exact_fp8_128x128x64_w2x2_bt", KIND_FP8, 5, 128, 128, 64, tile::launch_tile_fp8_exact<128, 128, 64, 2, 2, true>, kAllFp8Pairs, 0, 1},
+        {"exact_fp8_256x256x64_w2x4_bt", KIND_FP8, 5, 256, 256, 64, tile::launch_tile_fp8_exact<256, 256, 64, 2, 4, true>, kAllFp8Pairs, 0, 1},
+    };
+    *count = (int)(sizeof(table) / sizeof(table[0]));
+    return table;
+}
+
 }  // namespace libgemm

@@ -178,6 +178,41 @@ __device__ __forceinline__ v4u load_chunk_guarded(const uint8_t* row_ptr, bool r
     return v4u{w[0], w[1], w[2], w[3]};
 }
 
+// Exact widening of 8 FP8 codes (two words, code e in byte e % 4 of word e / 4)
+// to 8 FP16 values for the exact-accumulation mode. Every E4M3 and E5M2 value
+// is an FP16 value: E5M2 codes are the upper byte of the FP16 encoding (inf and
+// NaN included), E4M3 codes go through gfx950's FP8 -> FP16 conversion with a
+// unit scale (the E4M3 range, 2^-9 .. 448, lies inside FP16's normal range;
+// 0x7F / 0xFF stay NaN).
+__device__ __forceinline__ v4u widen8_fp8(uint32_t w0, uint32_t w1, bool e5m2) {
+    if (e5m2) {
+        auto two = [](uint32_t w, int hi) -> uint32_t {
+            const uint32_t b = hi ? (w >> 16) : w;
+            return ((b & 0xFFu) << 8) | ((b & 0xFF00u) << 16);
+        };
+        return v4u{two(w0, 0), two(w0, 1), two(w1, 0), two(w1, 1)};
+    }
+    typedef _Float16 v2hh __attribute__((ext_vector_type(2)));
+    const v2hh a = __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(w0, 1.0f, false);
+    const v2hh b = __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(w0, 1.0f, true);
+    const v2hh c = __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(w1, 1.0f, false);
+    const v2hh d = __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(w1, 1.0f, true);
+    return v4u{__builtin_bit_cast(uint32_t, a), __builtin_bit_cast(uint32_t, b), __builtin_bit_cast(uint32_t, c),
+               __builtin_bit_cast(uint32_t, d)};
+}
+
+// Eight FP8 codes starting at element col of a row, zero beyond limit and for
+// rows out of range.
+__device__ __forceinline__ v2i load_codes8_guarded(const uint8_t* row_ptr, bool row_ok, int64_t col, int64_t limit) {
+    uint32_t w[2] = {0u, 0u};
+    if (row_ok) {
+#pragma unroll
+        for (int e = 0; e < 8; ++e)
+            if (col + e < limit) w[e >> 2] |= (uint32_t)row_ptr[col + e] << (8 * (e & 3));
+    }
+    return v2i{(int)w[0], (int)w[1]};
+}
+
 // OUT_E4M3 stands for both FP8 outputs; EPI_E5M2 in eflags (uniform) picks the
 // format.
 template <int OUT>
@@ -191,7 +226,11 @@ __device__ __forceinline__ void store_one(void* C, int64_t idx, float y, int efl
     }
 }
 
-template <int ES, int OUT, int BM, int BN, int BK, int WM, int WN, int FA, int FB, bool BT>
+// GES: bytes per element of A and B in global memory. GES == ES except for
+// the exact FP8 mode (ES = 2, GES = 1): FP8 codes are widened to FP16 as they
+// are staged (eflags EPI_A_E5M2 / EPI_B_E5M2 give the operand formats) and
+// summed on the FP16 matrix cores.
+template <int ES, int OUT, int BM, int BN, int BK, int WM, int WN, int FA, int FB, bool BT, int GES = ES>
 __global__ __launch_bounds__(64 * WM * WN) void gemm_tile_kernel(
     const uint8_t* __restrict__ A, const uint8_t* __restrict__ B, void* __restrict__ C, int M, int N, int K,
     const float* __restrict__ sA, const float* __restrict__ sB, const float* __restrict__ sOut, int tiles_m,
@@ -253,8 +292,28 @@ __global__ __launch_bounds__(64 * WM * WN) void gemm_tile_kernel(
     // Fast-path loads: a wave-uniform base (kept in SGPRs) plus a 32-bit
     // per-lane offset, so the 16 loads of a tile need no 64-bit VGPR addresses.
     // Valid while one tile row block spans less than 2^31 bytes (checked below).
-    const uint8_t* a_tile = A + ((int64_t)m0 * K + kbeg) * ES;
-    const uint8_t* b_tile = BT ? B + ((int64_t)n0 * K + kbeg) * ES : B + ((int64_t)kbeg * N + n0) * ES;
+    const uint8_t* a_tile = A + ((int64_t)m0 * K + kbeg) * GES;
+    const uint8_t* b_tile = BT ? B + ((int64_t)n0 * K + kbeg) * GES : B + ((int64_t)kbeg * N + n0) * GES;
+    constexpr bool kWiden = GES != ES;
+    const bool a_e5m2 = (eflags & EPI_A_E5M2) != 0, b_e5m2 = (eflags & EPI_B_E5M2) != 0;
+    // One staged 16-byte chunk from global memory at p (VE elements).
+    auto gload = [&](const uint8_t* p, bool e5m2) __attribute__((always_inline)) -> v4u {
+        if constexpr (kWiden) {
+            const v2i w = *reinterpret_cast<const v2i*>(p);
+            return widen8_fp8((uint32_t)w.x, (uint32_t)w.y, e5m2);
+        } else {
+            return *reinterpret_cast<const v4u*>(p);
+        }
+    };
+    auto gload_guarded = [&](const uint8_t* row_ptr, bool row_ok, int64_t col, int64_t limit, bool e5m2)
+        __attribute__((always_inline)) -> v4u {
+        if constexpr (kWiden) {
+            const v2i w = load_codes8_guarded(row_ptr, row_ok, col, limit);
+            return widen8_fp8((uint32_t)w.x, (uint32_t)w.y, e5m2);
+        } else {
+            return load_chunk_guarded<ES>(row_ptr, row_ok, col, limit);
+        }
+    };
     // Edge tiles (aligned operands) use the same unguarded loads with the
     // addresses clamped into the matrix: A rows past M re-read row M-1 and B
     // column chunks past N re-read the last chunk. Those values only reach
@@ -263,27 +322,27 @@ __global__ __launch_bounds__(64 * WM * WN) void gemm_tile_kernel(
 #pragma unroll
     for (int i = 0; i < T::CA; ++i) {
         const int r = min(m0 + a_row + i * T::A_RPP, M - 1) - m0;
-        a_offs[i] = (uint32_t)((r * K + a_col * T::VE) * ES);
+        a_offs[i] = (uint32_t)((r * K + a_col * T::VE) * GES);
     }
 #pragma unroll
     for (int i = 0; i < T::CB; ++i) {
         if constexpr (BT) {
             const int r = min(n0 + b_row + i * T::B_RPP, N - 1) - n0;
-            b_offs[i] = (uint32_t)((r * K + b_col * T::VE) * ES);
+            b_offs[i] = (uint32_t)((r * K + b_col * T::VE) * GES);
         } else {
             const int c = min(n0 + b_col * T::VE, N - T::VE) - n0;
-            b_offs[i] = (uint32_t)(((b_row + i * T::B_RPP) * N + c) * ES);
+            b_offs[i] = (uint32_t)(((b_row + i * T::B_RPP) * N + c) * GES);
         }
     }
     auto load_a = [&](int kt) __attribute__((always_inline)) {
-        const uint8_t* pa = a_tile + (int64_t)kt * BK * ES;
+        const uint8_t* pa = a_tile + (int64_t)kt * BK * GES;
 #pragma unroll
-        for (int i = 0; i < T::CA; ++i) ra[i] = *reinterpret_cast<const v4u*>(pa + a_offs[i]);
+        for (int i = 0; i < T::CA; ++i) ra[i] = gload(pa + a_offs[i], a_e5m2);
     };
     auto load_b = [&](int kt) __attribute__((always_inline)) {
-        const uint8_t* pb = b_tile + (BT ? (int64_t)kt * BK * ES : (int64_t)kt * BK * N * ES);
+        const uint8_t* pb = b_tile + (BT ? (int64_t)kt * BK * GES : (int64_t)kt * BK * N * GES);
 #pragma unroll
-        for (int i = 0; i < T::CB; ++i) rb[i] = *reinterpret_cast<const v4u*>(pb + b_offs[i]);
+        for (int i = 0; i < T::CB; ++i) rb[i] = gload(pb + b_offs[i], b_e5m2);
     };
     auto store_a = [&](int stage) __attribute__((always_inline)) {
         LDS_AS uint8_t* As = smem + T::a_stage(stage);
@@ -308,12 +367,12 @@ __global__ __launch_bounds__(64 * WM * WN) void gemm_tile_kernel(
         for (int i = 0; i < T::CA; ++i) {
             const int gm = m0 + a_row + i * T::A_RPP;
             const int64_t gk = (int64_t)k0 + a_col * T::VE;
-            const uint8_t* rp = A + (int64_t)gm * K * ES;
+            const uint8_t* rp = A + (int64_t)gm * K * GES;
             v4u v;
             if (aligned && gm < M && gk + T::VE <= kend)
-                v = *reinterpret_cast<const v4u*>(rp + gk * ES);
+                v = gload(rp + gk * GES, a_e5m2);
             else
-                v = load_chunk_guarded<ES>(rp, gm < M, gk, kend);
+                v = gload_guarded(rp, gm < M, gk, kend, a_e5m2);
             *(LDS_AS v4u*)(As + (a_row + i * T::A_RPP) * T::SA + T::chunk(a_row, a_col)) = v;
         }
 #pragma unroll 1
@@ -321,23 +380,23 @@ __global__ __launch_bounds__(64 * WM * WN) void gemm_tile_kernel(
             if constexpr (BT) {
                 const int gn = n0 + b_row + i * T::B_RPP;
                 const int64_t gk = (int64_t)k0 + b_col * T::VE;
-                const uint8_t* rp = B + (int64_t)gn * K * ES;
+                const uint8_t* rp = B + (int64_t)gn * K * GES;
                 v4u v;
                 if (aligned && gn < N && gk + T::VE <= kend)
-                    v = *reinterpret_cast<const v4u*>(rp + gk * ES);
+                    v = gload(rp + gk * GES, b_e5m2);
                 else
-                    v = load_chunk_guarded<ES>(rp, gn < N, gk, kend);
+                    v = gload_guarded(rp, gn < N, gk, kend, b_e5m2);
                 *(LDS_AS v4u*)(Bs + T::b_row(b_row + i * T::B_RPP) + T::chunk(b_row, b_col)) = v;
                 continue;
             }
             const int gk = k0 + b_row + i * T::B_RPP;
             const int64_t gn = (int64_t)n0 + b_col * T::VE;
-            const uint8_t* rp = B + (int64_t)gk * N * ES;
+            const uint8_t* rp = B + (int64_t)gk * N * GES;
             v4u v;
             if (aligned && gk < kend && gn + T::VE <= N)
-                v = *reinterpret_cast<const v4u*>(rp + gn * ES);
+                v = gload(rp + gn * GES, b_e5m2);
             else
-                v = load_chunk_guarded<ES>(rp, gk < kend, gn, N);
+                v = gload_guarded(rp, gk < kend, gn, N, b_e5m2);
             *(LDS_AS v4u*)(Bs + T::b_row(b_row + i * T::B_RPP) + T::chunk(b_row, b_col)) = v;
         }
     };
@@ -423,8 +482,8 @@ __global__ __launch_bounds__(64 * WM * WN) void gemm_tile_kernel(
             }
     };
 
-    const bool offsets_fit = (int64_t)BM * K * ES < (1ll << 31) &&
-                             (BT ? (int64_t)BN * K * ES : (int64_t)BK * N * ES) < (1ll << 31);
+    const bool offsets_fit = (int64_t)BM * K * GES < (1ll << 31) &&
+                             (BT ? (int64_t)BN * K * GES : (int64_t)BK * N * GES) < (1ll << 31);
     if (nk > 0) {
         Op bop[T::KS][T::TN];
         // Tile kt+1 is fetched into registers while tile kt is multiplied;
@@ -506,7 +565,7 @@ inline bool aligned16(const void* p) { return ((uintptr_t)p & 15u) == 0; }
 
 // Launches one configuration for operand formats FA, FB (FP8 only; FP16 uses
 // 0, 0). Defined here for every translation unit that instantiates it.
-template <int ES, int BM, int BN, int BK, int WM, int WN, int FA, int FB, bool BT = false>
+template <int ES, int BM, int BN, int BK, int WM, int WN, int FA, int FB, bool BT = false, int GES = ES>
 hipError_t launch_tile(const GemmArgs& a) {
     const int64_t tiles_m = (a.M + BM - 1) / BM;
     const int64_t tiles_n = (a.N + BN - 1) / BN;
@@ -521,29 +580,37 @@ hipError_t launch_tile(const GemmArgs& a) {
     if (BT != (a.b_kmajor != 0)) return hipErrorInvalidValue;
     // Vector loads need 16-byte aligned bases and row pitches (for BT, B's
     // rows are K long like A's, so N needs no alignment).
-    const int aligned = aligned16(a.A) && aligned16(a.B) && ((a.K * ES) % 16 == 0) && (BT || (a.N * ES) % 16 == 0);
+    // Vector loads read 16 / ES elements: 16 bytes, or 8 bytes of codes when
+    // widening.
+    const int64_t lb = 16 / ES * GES;
+    const bool al = ((uintptr_t)a.A % lb) == 0 && ((uintptr_t)a.B % lb) == 0;
+    const int aligned = al && ((a.K * GES) % lb == 0) && (BT || (a.N * GES) % lb == 0);
     const uint8_t* A = reinterpret_cast<const uint8_t*>(a.A);
     const uint8_t* B = reinterpret_cast<const uint8_t*>(a.B);
     const int M = (int)a.M, N = (int)a.N, K = (int)a.K;
     const dim3 grid((unsigned)blocks, (unsigned)splits), block(64 * WM * WN);
     if (splits > 1) {   // FP32 partial sums into the workspace
-        gemm_tile_kernel<ES, OUT_F32, BM, BN, BK, WM, WN, FA, FB, BT><<<grid, block, 0, a.stream>>>(
-            A, B, a.ws, M, N, K, nullptr, nullptr, nullptr, (int)tiles_m, (int)tiles_n, aligned, EPI_PARTIAL, kchunk);
+        const int pflags = EPI_PARTIAL | (GES != ES && a.fmt_a == FMT_E5M2 ? EPI_A_E5M2 : 0) |
+                           (GES != ES && a.fmt_b == FMT_E5M2 ? EPI_B_E5M2 : 0);
+        gemm_tile_kernel<ES, OUT_F32, BM, BN, BK, WM, WN, FA, FB, BT, GES><<<grid, block, 0, a.stream>>>(
+            A, B, a.ws, M, N, K, nullptr, nullptr, nullptr, (int)tiles_m, (int)tiles_n, aligned, pflags, kchunk);
         return hipGetLastError();
     }
-    const int eflags = (a.out_dtype == OUT_E5M2 ? EPI_E5M2 : 0) | (a.channel ? EPI_CHANNEL : 0);
+    const int eflags = (a.out_dtype == OUT_E5M2 ? EPI_E5M2 : 0) | (a.channel ? EPI_CHANNEL : 0) |
+                       (GES != ES && a.fmt_a == FMT_E5M2 ? EPI_A_E5M2 : 0) |
+                       (GES != ES && a.fmt_b == FMT_E5M2 ? EPI_B_E5M2 : 0);
     switch (a.out_dtype) {
         case OUT_F32:
-            gemm_tile_kernel<ES, OUT_F32, BM, BN, BK, WM, WN, FA, FB, BT><<<grid, block, 0, a.stream>>>(
+            gemm_tile_kernel<ES, OUT_F32, BM, BN, BK, WM, WN, FA, FB, BT, GES><<<grid, block, 0, a.stream>>>(
                 A, B, a.C, M, N, K, a.sA, a.sB, a.sOut, (int)tiles_m, (int)tiles_n, aligned, eflags, kchunk);
             break;
         case OUT_F16:
-            gemm_tile_kernel<ES, OUT_F16, BM, BN, BK, WM, WN, FA, FB, BT><<<grid, block, 0, a.stream>>>(
+            gemm_tile_kernel<ES, OUT_F16, BM, BN, BK, WM, WN, FA, FB, BT, GES><<<grid, block, 0, a.stream>>>(
                 A, B, a.C, M, N, K, a.sA, a.sB, a.sOut, (int)tiles_m, (int)tiles_n, aligned, eflags, kchunk);
             break;
         default:
-            if constexpr (ES == 1) {
-                gemm_tile_kernel<ES, OUT_E4M3, BM, BN, BK, WM, WN, FA, FB, BT><<<grid, block, 0, a.stream>>>(
+            if constexpr (GES == 1) {
+                gemm_tile_kernel<ES, OUT_E4M3, BM, BN, BK, WM, WN, FA, FB, BT, GES><<<grid, block, 0, a.stream>>>(
                     A, B, a.C, M, N, K, a.sA, a.sB, a.sOut, (int)tiles_m, (int)tiles_n, aligned,
                     eflags, kchunk);
             } else {
@@ -563,6 +630,13 @@ hipError_t launch_tile_fp8_any(const GemmArgs& a) {
         case 2: return launch_tile<1, BM, BN, BK, WM, WN, 1, 0, BT>(a);
         default: return launch_tile<1, BM, BN, BK, WM, WN, 1, 1, BT>(a);
     }
+}
+
+// The exact-accumulation FP8 mode: FP8 codes in global memory, FP16 in LDS and
+// on the matrix cores (formats from the arguments at run time).
+template <int BM, int BN, int BK, int WM, int WN, bool BT = false>
+hipError_t launch_tile_fp8_exact(const GemmArgs& a) {
+    return launch_tile<2, BM, BN, BK, WM, WN, 0, 0, BT, 1>(a);
 }
 
 #define LIBGEMM_TILE_MIXED_CONFIGS(X) \

@@ -39,7 +39,8 @@ struct GemmConfig {
     const char* name;   // e.g. "tile_fp8_256x256x128_w2x2"
     int kind;           // OperandKind
     int family;         // 0 = MFMA tile kernel, 1 = M<=16 streaming kernel, 2 = direct-load tile kernel,
-                        // 3 = K-major decode kernel, 4 = ping-pong tile kernel
+                        // 3 = K-major decode kernel, 4 = ping-pong tile kernel,
+                        // 5 = exact-accumulation FP8 tile kernel
     int bm, bn, bk;     // tile (stream: bm = max M, bn = columns per block, bk = k-slices)
     GemmLauncher launch;
     int fmt_mask = 0;   // FP8 operand pairs served: bit (2*fmt_a + fmt_b); 0 means E4M3 x E4M3 only
@@ -61,6 +62,7 @@ const GemmConfig* stream_configs(int* count);
 const GemmConfig* dma_configs(int* count);
 const GemmConfig* gemv_kmajor_configs(int* count);
 const GemmConfig* pp_configs(int* count);
+const GemmConfig* exact_configs(int* count);
 
 // Shape (and FP8 operand formats) -> configuration (host only, no HIP calls).
 // Returns NULL if none fits.
@@ -74,6 +76,13 @@ struct SplitPlan {
     int splits;
     int64_t k_chunk;
 };
+// The exact-accumulation FP8 mode: the FP32-FMA streaming (row-major B,
+// M <= 4) and decode (K-major B, M <= 8) kernels, whose products are exact and
+// whose sums are FP32 additions, else the widening tile kernels by the tile
+// rules. NULL if none fits.
+const GemmConfig* select_config_exact(int out_dtype, int64_t M, int64_t N, int64_t K, int fmt_a, int fmt_b,
+                                      int b_kmajor);
+
 SplitPlan plan_splitk(int kind, int out_dtype, int64_t M, int64_t N, int64_t K, int fmt_a = 0, int fmt_b = 0,
                       int b_kmajor = 0);
 

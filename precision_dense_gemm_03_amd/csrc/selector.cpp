@@ -148,6 +148,43 @@ const GemmConfig* select_config(int kind, int out_dtype, int64_t M, int64_t N, i
     return tile_with(kind, 64, 0, fa, fb);
 }
 
+const GemmConfig* select_config_exact(int out_dtype, int64_t M, int64_t N, int64_t K, int fa, int fb, int bt) {
+    (void)out_dtype;
+    (void)K;
+    int ne = 0;
+    const GemmConfig* et = exact_configs(&ne);
+    if (const char* env = std::getenv("LIBGEMM_CONFIG")) {
+        for (int i = 0; i < ne; ++i)
+            if (std::strcmp(et[i].name, env) == 0 && serves(et[i], KIND_FP8, fa, fb, bt)) return &et[i];
+        // the FP32-FMA decode kernels are exact too
+        if (const GemmConfig* c = find_named(env, KIND_FP8, M, fa, fb, bt))
+            if (c->family == 1 || c->family == 3) return c;
+    }
+    if (M <= (bt ? kGemvMaxM : kStreamMaxM)) {
+        const GemmConfig* best = nullptr;
+        int n = 0;
+        const GemmConfig* t = bt ? gemv_kmajor_configs(&n) : stream_configs(&n);
+        for (int i = 0; i < n; ++i)
+            if (serves(t[i], KIND_FP8, fa, fb, bt) && M <= t[i].bm && (!best || t[i].bm < best->bm)) best = &t[i];
+        if (best) return best;
+    }
+    auto exact_tile = [&](int bm) -> const GemmConfig* {
+        for (int i = 0; i < ne; ++i)
+            if (serves(et[i], KIND_FP8, fa, fb, bt) && et[i].bm == bm) return &et[i];
+        return nullptr;
+    };
+    static const int sizes[] = {256, 128, 64};
+    for (int bm : sizes) {
+        const int64_t tm = (M + bm - 1) / bm, tn = (N + bm - 1) / bm;
+        const double useful = (double)M * (double)N;
+        const double padded = (double)(tm * bm) * (double)(tn * bm);
+        const int64_t min_tiles = bm == 256 ? kNumCUs * 3 / 4 : kNumCUs;
+        if (tm * tn >= min_tiles && useful >= 0.75 * padded)
+            if (const GemmConfig* c = exact_tile(bm)) return c;
+    }
+    return exact_tile(64);
+}
+
 SplitPlan plan_splitk(int kind, int out_dtype, int64_t M, int64_t N, int64_t K, int fa, int fb, int bt) {
     if (kind == KIND_F16) fa = fb = 0;
     SplitPlan p{select_config(kind, out_dtype, M, N, K, fa, fb, bt), 1, K};

@@ -114,6 +114,22 @@ def fp8_dot_allowance(codes_a, codes_b, rows=None, group=8, fmt_a=orc.FMT_E4M3, 
     return T
 
 
+def fp8_mfma_config(name):
+    """Whether configuration `name` sums FP8 products on the FP8 matrix cores
+    (the register-staged, direct-load and ping-pong tile kernels), the only
+    place the allowance T applies. The streaming and decode kernels (FP32 FMA
+    of exact products) and the exact mode (FP16 matrix cores) take the plain
+    bound."""
+    return name.startswith(("tile_fp8", "dma_fp8", "pp_fp8"))
+
+
+def allowance_for(name, codes_a, codes_b, rows=None, fmt_a=orc.FMT_E4M3, fmt_b=orc.FMT_E4M3):
+    """fp8_dot_allowance when configuration `name` runs the FP8 matrix cores, else None."""
+    if not fp8_mfma_config(name):
+        return None
+    return fp8_dot_allowance(codes_a, codes_b, rows=rows, fmt_a=fmt_a, fmt_b=fmt_b)
+
+
 def check_f32(C, R, S, sA=1.0, sB=1.0, what="F32 output", T=None):
     C = np.asarray(C, np.float64)
     sc = scale_grid(sA, sB)

@@ -10,7 +10,7 @@ import torch
 import oracle as orc
 import precision_dense_gemm_03_amd as g
 import workloads as wl
-from parity import REL, check_f16, check_f32, check_fp8, fp8_dot_allowance, scale_grid, ulp16
+from parity import REL, allowance_for, check_f16, check_f32, check_fp8, fp8_dot_allowance, scale_grid, ulp16
 
 pytestmark = pytest.mark.gpu
 
@@ -149,7 +149,10 @@ def test_gemm_per_channel_scales(fa, fb, cfg, M, N, K, monkeypatch):
     sB = (np.exp2(rng.uniform(-6, 6, N)) * 0.11).astype(np.float32)
     ofa, ofb = ORC_FMT[fa], ORC_FMT[fb]
     R, S = orc.gemm(ofa, ca, cb, fmt_b=ofb)
-    T = fp8_dot_allowance(ca, cb, fmt_a=ofa, fmt_b=ofb)
+    T = allowance_for(cfg or g.select_config_fmt(g.KIND_FP8, g.OUT_F32, M, N, K, fa, fb), ca, cb, fmt_a=ofa,
+                      fmt_b=ofb)
+    if T is None:
+        T = np.zeros_like(S)
     ta, tb, tsa, tsb = dev(ca), dev(cb), dev(sA), dev(sB)
     C = torch.empty((M, N), dtype=torch.float32, device=DEV)
     g.gemm_fp8_channel(ta, fa, tb, fb, tsa, tsb, C)
@@ -231,9 +234,9 @@ def test_per_channel_chain_full_size(M):
     assert np.array_equal(host(qa), cqa) and np.array_equal(host(qb), cqb)
     rows = sorted(set([0, M - 1] + list(range(0, M, max(1, M // 24)))))
     R, S = orc.gemm(orc.FMT_E4M3, cqa, cqb, rows=rows)
-    # outliers put products far apart within one 8-wide k group: the matrix
-    # cores' alignment allowance applies
-    T = fp8_dot_allowance(cqa, cqb, rows=rows)
+    # outliers put products far apart within one 8-wide k group: the FP8
+    # matrix cores' alignment allowance applies where they run (not M = 1)
+    T = allowance_for(g.select_config(g.KIND_FP8, g.OUT_F32, M, N, K), cqa, cqb, rows=rows)
     for dt in (torch.float32, torch.float16):
         C = torch.empty((M, N), dtype=dt, device=DEV)
         g.gemm_fp8_channel(qa, g.FMT_E4M3, qb, g.FMT_E4M3, s_a, s_b, C)

@@ -12,7 +12,7 @@ import torch
 import oracle as orc
 import precision_dense_gemm_03_amd as g
 import workloads as wl
-from parity import check_f16, check_f32, check_fp8, fp8_dot_allowance
+from parity import allowance_for, check_f16, check_f32, check_fp8, fp8_dot_allowance
 
 pytestmark = pytest.mark.gpu
 
@@ -127,26 +127,33 @@ def test_gemm_operand_formats(fa, fb, cfg, M, N, K, monkeypatch):
     cb = codes(fb, (K, N), 11 * N + K + fb)
     ofa, ofb = ORC_FMT[fa], ORC_FMT[fb]
     R, S = orc.gemm(ofa, ca, cb, fmt_b=ofb)
-    T = fp8_dot_allowance(ca, cb, fmt_a=ofa, fmt_b=ofb)
     sa, sb = np.float32(0.5), np.float32(0.25)      # powers of two: no extra rounding in sA*sB
     ta, tb, tsa, tsb = dev(ca), dev(cb), scalar(sa), scalar(sb)
-    C = torch.empty((M, N), dtype=torch.float32, device=DEV)
-    g.gemm_fp8_fmt(ta, fa, tb, fb, tsa, tsb, C)
-    check_f32(host(C), R, S, sa, sb, what="f32", T=T)
-    C = torch.empty((M, N), dtype=torch.float16, device=DEV)
-    g.gemm_fp8_fmt(ta, fa, tb, fb, tsa, tsb, C)
     V = R * float(sa) * float(sb)
-    # E5M2 products can overflow FP16: compare the elements whose whole
-    # tolerance interval stays below 65520 (where RNE to FP16 turns into inf)
-    slack = (1e-5 * S + T) * float(sa) * float(sb)
-    fin = np.abs(V) + slack < 65520.0
-    got16 = host(C).astype(np.float64)
-    check_f16(got16[fin], R[fin], S[fin], sa, sb, what="f16", T=T[fin])
-    for out_fmt in (g.FMT_E4M3, g.FMT_E5M2):
-        s_out = orc.scale(np.float32(np.max(np.abs(V))), ORC_FMT[out_fmt])
-        C = torch.empty((M, N), dtype=torch.uint8, device=DEV)
-        g.gemm_fp8_fmt(ta, fa, tb, fb, tsa, tsb, C, scalar(s_out), out_fmt=out_fmt)
-        check_fp8(host(C), R, S, sa, sb, s_out, ORC_FMT[out_fmt], what=f"fp8 out {out_fmt}", T=T)
+    # gemm_fp8_fmt (the allowance only where an FP8 MFMA kernel runs), then
+    # gemm_fp8_exact on the same operands (the plain bound)
+    T_fast = allowance_for(cfg or g.select_config_fmt(g.KIND_FP8, g.OUT_F32, M, N, K, fa, fb), ca, cb,
+                           fmt_a=ofa, fmt_b=ofb)
+    for exact in (False, True):
+        T = None if exact else T_fast
+        tag = "exact " if exact else ""
+        run = g.gemm_fp8_exact if exact else g.gemm_fp8_fmt
+        C = torch.empty((M, N), dtype=torch.float32, device=DEV)
+        run(ta, fa, tb, fb, tsa, tsb, C)
+        check_f32(host(C), R, S, sa, sb, what=tag + "f32", T=T)
+        C = torch.empty((M, N), dtype=torch.float16, device=DEV)
+        run(ta, fa, tb, fb, tsa, tsb, C)
+        # E5M2 products can overflow FP16: compare the elements whose whole
+        # tolerance interval stays below 65520 (where RNE to FP16 turns into inf)
+        slack = (1e-5 * S + (0.0 if T is None else T)) * float(sa) * float(sb)
+        fin = np.abs(V) + slack < 65520.0
+        got16 = host(C).astype(np.float64)
+        check_f16(got16[fin], R[fin], S[fin], sa, sb, what=tag + "f16", T=None if T is None else T[fin])
+        for out_fmt in (g.FMT_E4M3, g.FMT_E5M2):
+            s_out = orc.scale(np.float32(np.max(np.abs(V))), ORC_FMT[out_fmt])
+            C = torch.empty((M, N), dtype=torch.uint8, device=DEV)
+            run(ta, fa, tb, fb, tsa, tsb, C, scalar(s_out), out_fmt=out_fmt)
+            check_fp8(host(C), R, S, sa, sb, s_out, ORC_FMT[out_fmt], what=f"{tag}fp8 out {out_fmt}", T=T)
 
 
 def test_gemm_fp8_scaled_e5m2_output():
@@ -182,6 +189,7 @@ def test_pow2_e5m2_chain_against_oracle(M):
     g.gemm_fp8_fmt(qa, g.FMT_E5M2, qb, g.FMT_E4M3, s_a, s_b, C)
     rows = None if M <= 64 else list(range(0, M, 97)) + [M - 1]
     R, S = orc.gemm(orc.FMT_E5M2, cqa, cqb, rows=rows, fmt_b=orc.FMT_E4M3)
-    T = fp8_dot_allowance(cqa, cqb, rows=rows, fmt_a=orc.FMT_E5M2, fmt_b=orc.FMT_E4M3)
+    T = allowance_for(g.select_config_fmt(g.KIND_FP8, g.OUT_F16, M, N, K, g.FMT_E5M2, g.FMT_E4M3), cqa, cqb,
+                      rows=rows, fmt_a=orc.FMT_E5M2, fmt_b=orc.FMT_E4M3)
     got = host(C)
     check_f16(got if rows is None else got[rows], R, S, osa, osb, what="pow2 chain", T=T)

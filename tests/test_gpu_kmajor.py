@@ -14,7 +14,7 @@ import torch
 import oracle as orc
 import precision_dense_gemm_03_amd as g
 import workloads as wl
-from parity import check_e4m3, check_f16, check_f32, check_fp8, fp8_dot_allowance
+from parity import allowance_for, check_e4m3, check_f16, check_f32, check_fp8, fp8_dot_allowance
 
 pytestmark = pytest.mark.gpu
 
@@ -215,7 +215,8 @@ def test_gemm_fp8_bt_small_sizes():
                 ca = wl.random_e4m3_codes((M, K), 300 + seed)
                 cb = wl.random_e4m3_codes((K, N), 8000 + seed)
                 R, S = orc.gemm(orc.FMT_E4M3, ca, cb)
-                T = fp8_dot_allowance(ca, cb)
+                # M <= 8 runs the FP32-FMA decode kernels: the plain bound
+                T = allowance_for(g.select_config_bt(g.KIND_FP8, g.OUT_F32, M, N, K), ca, cb)
                 check_f32(run_fp8_bt(dev(ca), dev(cb.T), sa, sb, g.OUT_F32), R, S, 0.75, 1.5,
                           what=f"fp8 bt {M}x{N}x{K}", T=T)
 
@@ -227,7 +228,7 @@ def test_gemm_fp8_bt_edges(M, N, K):
     cb = wl.random_e4m3_codes((K, N), N * 17 + K)
     sa, sb = np.float32(0.02), np.float32(0.003)
     R, S = orc.gemm(orc.FMT_E4M3, ca, cb)
-    T = fp8_dot_allowance(ca, cb)
+    T = allowance_for(g.select_config_bt(g.KIND_FP8, g.OUT_F32, M, N, K), ca, cb)
     ta, tbt, tsa, tsb = dev(ca), dev(cb.T), scalar(sa), scalar(sb)
     check_f32(run_fp8_bt(ta, tbt, tsa, tsb, g.OUT_F32), R, S, sa, sb, what="f32", T=T)
     check_f16(run_fp8_bt(ta, tbt, tsa, tsb, g.OUT_F16), R, S, sa, sb, what="f16", T=T)
@@ -509,7 +510,7 @@ def test_gemm_fp8_fmt_bt(fa, fb, cfg, M, N, K, monkeypatch):
     cb = fp8_codes(fb, (K, N), 17 * N + K + fb)
     ofa, ofb = ORC_FMT[fa], ORC_FMT[fb]
     R, S = orc.gemm(ofa, ca, cb, fmt_b=ofb)
-    T = fp8_dot_allowance(ca, cb, fmt_a=ofa, fmt_b=ofb)
+    T = allowance_for(cfg or g.select_config_bt(g.KIND_FP8, g.OUT_F32, M, N, K), ca, cb, fmt_a=ofa, fmt_b=ofb)
     sa, sb = np.float32(0.5), np.float32(0.25)
     ta, tbt, tsa, tsb = dev(ca), dev(cb.T), scalar(sa), scalar(sb)
     C = torch.empty((M, N), dtype=torch.float32, device=DEV)

@@ -12,7 +12,7 @@ import torch
 import oracle as orc
 import precision_dense_gemm_03_amd as g
 import workloads as wl
-from parity import check_e4m3, check_f16, check_f32, fp8_dot_allowance
+from parity import allowance_for, check_e4m3, check_f16, check_f32
 
 pytestmark = pytest.mark.gpu
 
@@ -161,13 +161,25 @@ def run_f16(a16, b16, out):
     return host(C)
 
 
-def run_fp8(qa, qb, sa, sb, out, s_out=None):
+def run_fp8(qa, qb, sa, sb, out, s_out=None, exact=False):
+    """The E4M3 GEMM through gemm_fp8_scaled, or with exact=True through the
+    exact-accumulation call gemm_fp8_exact."""
     M, K = qa.shape
     N = qb.shape[1]
     dt = {g.OUT_F32: torch.float32, g.OUT_F16: torch.float16, g.OUT_E4M3: torch.uint8}[out]
     C = torch.empty((M, N), dtype=dt, device=DEV)
-    g.gemm_fp8_scaled(qa, qb, sa, sb, C, None if s_out is None else scalar(s_out))
+    so = None if s_out is None else scalar(s_out)
+    if exact:
+        g.gemm_fp8_exact(qa, g.FMT_E4M3, qb, g.FMT_E4M3, sa, sb, C, so)
+    else:
+        g.gemm_fp8_scaled(qa, qb, sa, sb, C, so)
     return host(C)
+
+
+def fp8_allowance(M, N, K, out, ca, cb, rows=None):
+    """The FP8 matrix-core allowance for the configuration gemm_fp8_scaled
+    runs on this shape (None when it is not an FP8 MFMA kernel)."""
+    return allowance_for(g.select_config(g.KIND_FP8, out, M, N, K), ca, cb, rows=rows)
 
 
 def check_f16_gemm(a16, b16, out, rows=None, what=""):
@@ -209,12 +221,19 @@ def test_gemm_all_sizes_1_to_8():
                 ca = wl.random_e4m3_codes((M, K), seed)
                 cb = wl.random_e4m3_codes((K, N), 5000 + seed)
                 R, S = orc.gemm(orc.FMT_E4M3, ca, cb)
-                T = fp8_dot_allowance(ca, cb)
-                check_f32(run_fp8(dev(ca), dev(cb), sa, sb, g.OUT_F32), R, S, 0.75, 1.5, what=f"fp8 {M}x{N}x{K}", T=T)
                 V = R * 0.75 * 1.5
                 s_out = orc.scale_from_amax(np.float32(np.max(np.abs(V))))
-                check_e4m3(run_fp8(dev(ca), dev(cb), sa, sb, g.OUT_E4M3, s_out), R, S, 0.75, 1.5, s_out,
+                ta, tb = dev(ca), dev(cb)
+                # gemm_fp8_scaled: the allowance only where an FP8 MFMA kernel runs
+                T = fp8_allowance(M, N, K, g.OUT_F32, ca, cb)
+                check_f32(run_fp8(ta, tb, sa, sb, g.OUT_F32), R, S, 0.75, 1.5, what=f"fp8 {M}x{N}x{K}", T=T)
+                check_e4m3(run_fp8(ta, tb, sa, sb, g.OUT_E4M3, s_out), R, S, 0.75, 1.5, s_out,
                            what=f"fp8->e4m3 {M}x{N}x{K}", T=T)
+                # gemm_fp8_exact: the plain bound
+                check_f32(run_fp8(ta, tb, sa, sb, g.OUT_F32, exact=True), R, S, 0.75, 1.5,
+                          what=f"exact fp8 {M}x{N}x{K}")
+                check_e4m3(run_fp8(ta, tb, sa, sb, g.OUT_E4M3, s_out, exact=True), R, S, 0.75, 1.5, s_out,
+                           what=f"exact fp8->e4m3 {M}x{N}x{K}")
 
 
 EDGE = [(m, n, k) for m in (1, 63, 65, 127, 129) for (n, k) in ((1000, 1000), (520, 999), (4096, 4096))]
@@ -235,16 +254,21 @@ def test_gemm_fp8_edges(M, N, K):
     ca = wl.random_e4m3_codes((M, K), M * 11 + K)
     cb = wl.random_e4m3_codes((K, N), N * 13 + K)
     sa, sb = np.float32(0.02), np.float32(0.003)
-    # full-range codes: the rows checked carry the FP8 matrix-core allowance
+    # full-range codes: gemm_fp8_scaled's FP8 MFMA kernels carry the matrix-core
+    # allowance (the streaming kernel at M = 1 does not); gemm_fp8_exact meets
+    # the plain bound
     rows = None if N * K <= 1 << 20 else sample_rows(M, 6)
     R, S = orc.gemm(orc.FMT_E4M3, ca, cb, rows=rows)
-    T = fp8_dot_allowance(ca, cb, rows=rows)
     sel = slice(None) if rows is None else rows
     ta, tb, tsa, tsb = dev(ca), dev(cb), scalar(sa), scalar(sb)
-    check_f32(run_fp8(ta, tb, tsa, tsb, g.OUT_F32)[sel], R, S, sa, sb, what="f32", T=T)
-    check_f16(run_fp8(ta, tb, tsa, tsb, g.OUT_F16)[sel], R, S, sa, sb, what="f16", T=T)
     s_out = orc.scale_from_amax(np.float32(np.max(np.abs(R * float(sa) * float(sb)))))
-    check_e4m3(run_fp8(ta, tb, tsa, tsb, g.OUT_E4M3, s_out)[sel], R, S, sa, sb, s_out, what="e4m3", T=T)
+    for exact in (False, True):
+        T = None if exact else fp8_allowance(M, N, K, g.OUT_F32, ca, cb, rows=rows)
+        tag = "exact " if exact else ""
+        check_f32(run_fp8(ta, tb, tsa, tsb, g.OUT_F32, exact=exact)[sel], R, S, sa, sb, what=tag + "f32", T=T)
+        check_f16(run_fp8(ta, tb, tsa, tsb, g.OUT_F16, exact=exact)[sel], R, S, sa, sb, what=tag + "f16", T=T)
+        check_e4m3(run_fp8(ta, tb, tsa, tsb, g.OUT_E4M3, s_out, exact=exact)[sel], R, S, sa, sb, s_out,
+                   what=tag + "e4m3", T=T)
 
 
 @pytest.mark.parametrize("w", wl.C3, ids=lambda w: w.name)
@@ -369,7 +393,7 @@ def test_guard_bands_and_poison(kind, M, N, K):
         sc = 0.125
     b = host(buf)
     assert np.all(np.isnan(b[:G])) and np.all(np.isnan(b[G + M * N:])), "guard band written"
-    T = fp8_dot_allowance(ca, cb) if kind == "fp8" and M > 16 else None
+    T = allowance_for(g.select_config(g.KIND_FP8, g.OUT_F32, M, N, K), ca, cb) if kind == "fp8" else None
     check_f32(b[G:G + M * N].reshape(M, N), R, S, sc, 1.0, T=T)
 
 

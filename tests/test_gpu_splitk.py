@@ -10,7 +10,7 @@ import torch
 import oracle as orc
 import precision_dense_gemm_03_amd as g
 import workloads as wl
-from parity import check_f16, check_f32, check_fp8, fp8_dot_allowance
+from parity import allowance_for, check_f16, check_f32, check_fp8, fp8_dot_allowance
 
 pytestmark = pytest.mark.gpu
 
@@ -72,7 +72,7 @@ def test_fp8_splitk_forced(cfg, splits, M, N, K, fa, fb, monkeypatch):
     ca, cb = enc[fa]((M, K), 3 * M + K), enc[fb]((K, N), 7 * N + K)
     ofa, ofb = ORC_FMT[fa], ORC_FMT[fb]
     R, S = orc.gemm(ofa, ca, cb, fmt_b=ofb)
-    T = fp8_dot_allowance(ca, cb, fmt_a=ofa, fmt_b=ofb) if M > 16 or name.startswith("tile") else None
+    T = allowance_for(name, ca, cb, fmt_a=ofa, fmt_b=ofb)
     sa, sb = np.float32(0.125), np.float32(0.5)
     ta, tb, tsa, tsb = dev(ca), dev(cb), scalar(sa), scalar(sb)
     C = torch.empty((M, N), dtype=torch.float32, device=DEV)
@@ -107,7 +107,7 @@ def test_fp8_splitk_m_sweep_full_size(M):
     sb = orc.scale_from_amax(orc.amax(xb))
     ca, cb = orc.quantize(xa, sa), orc.quantize(xb, sb)
     R, S = orc.gemm(orc.FMT_E4M3, ca, cb)
-    T = fp8_dot_allowance(ca, cb)
+    T = allowance_for(name, ca, cb)
     V = R * float(sa) * float(sb)
     s_out = orc.scale_from_amax(np.float32(np.max(np.abs(V))))
     ta, tb = dev(ca), dev(cb)
