@@ -1,20 +1,28 @@
 """Benchmark of the FP8/FP16 GEMM hot path on one MI355X.
 
-One step = one pass over every step of the path on seeded synthetic inputs
-already resident in HBM:
-  FP8 4096^3 job:  amax(A), amax(B) (with scales), quantize(A), quantize(B),
-                   E4M3 GEMM with FP8 output and its own output scale
+One step = one pass over every step of the path, on seeded synthetic inputs
+already resident in HBM (the metric's configuration: GEMMs at 4096^3 and the
+M = 1 decode):
+  FP8 4096^3 job:  amax, scale and E4M3 quantize of A and B (two launches),
+                   then the E4M3 GEMM with an E4M3 output and its own output
+                   scale (sOut = amax(C) / 448, computed once beforehand)
   FP16 4096^3:     FP16 GEMM, FP16 output
   FP16 decode:     [1,4096] x [4096,12288], FP16 output (HBM-bound kernel)
-With --b-layout kmajor (the default) B is held K-major, as Bt[N,K] (the layout
-a linear layer keeps its weight in): the FP8 job quantizes B straight into that
-layout and the GEMMs take it; with rowmajor every B is B[K,N]. The results are
-the same either way.
-value = all GEMM flops of a step / step time (TFLOPS). The same run also times
-each row on its own, for both layouts (TFLOPS and % of MFMA peak for the two
-4096^3 GEMMs; HBM GB/s at M = 1 with the weights rotated over 6 copies, 604 MB,
-so the 256 MB Infinity Cache cannot serve them), the dominant kernel's
-roofline figure, and the oracle on a bounded sample of the same step on the
+B is row-major B[K,N] (the calls' contract layout) unless --b-layout kmajor.
+
+value = 2*4096^3 / (the FP8 job's time inside the timed steps), in TFLOPS:
+the throughput of the whole FP8 job, quantization included. HIP events on the
+launch stream split every timed step into its parts; `roofline` is the FP8
+GEMM kernel's part against the FP8 dense peak, `roofline_f16` the FP16 GEMM's
+against the FP16 peak, `roofline_decode` the decode's against HBM.
+
+The same run times every configuration of the workload list on its own
+(`rows`): for each, R back-to-back calls each bracketed by HIP events on the
+launch stream, reported as median / p10 / p90 / mean, for row-major B and for
+K-major B (Bt[N,K]). HBM-bound rows rotate B over enough copies (>= 512 MB)
+that the 256 MB Infinity Cache cannot serve it. `clock` samples the GPU's
+engine clock (amd-smi) while the FP8 GEMM runs back to back for about a
+second. `cpu_baseline` is the oracle on a bounded sample of the step on the
 host cores.
 
 Prints ONE JSON line. Usage: python bench.py [--gpus 1] [--steps K] [--warmup W]
@@ -22,6 +30,7 @@ Prints ONE JSON line. Usage: python bench.py [--gpus 1] [--steps K] [--warmup W]
 import argparse
 import json
 import os
+import subprocess
 import sys
 import time
 
@@ -32,6 +41,7 @@ METRIC = "TFLOPS + % MFMA peak (FP8/FP16 GEMM 4096³); HBM GB/s at M=1 decode"
 PEAK_FP8_TFLOPS = 5033.2     # MI355X dense MFMA, FP8
 PEAK_F16_TFLOPS = 2516.6     # MI355X dense MFMA, FP16
 PEAK_HBM_GBS = 8000.0        # MI355X HBM3E
+COLD_BYTES = 512 << 20       # rotated operand footprint for HBM-bound rows (2x the Infinity Cache)
 
 
 def log(*a):
@@ -45,10 +55,11 @@ def parse():
     p.add_argument("--warmup", type=int, default=5)
     p.add_argument("--no-cpu-baseline", action="store_true")
     p.add_argument("--cpu-seconds", type=float, default=15.0, help="target oracle sample time")
-    p.add_argument("--rows-reps", type=int, default=200, help="launches per single-row timing")
-    p.add_argument("--b-layout", choices=("kmajor", "rowmajor"), default="kmajor",
-                   help="layout of B in the timed step: kmajor (Bt[N,K], a linear layer's weight layout; the FP8 "
-                        "job quantizes B straight into it) or rowmajor (B[K,N])")
+    p.add_argument("--rows-reps", type=int, default=100, help="timed calls per row")
+    p.add_argument("--no-rows", action="store_true", help="time the step only")
+    p.add_argument("--b-layout", choices=("rowmajor", "kmajor"), default="rowmajor",
+                   help="layout of B in the timed step: rowmajor (B[K,N], the contract layout) or kmajor "
+                        "(Bt[N,K], a linear layer's weight layout)")
     p.add_argument("--calib-copy", action="store_true",
                    help="run one 256 MiB device-to-device copy first (a known-size kernel that calibrates "
                         "HBM byte counters in a profiler run)")
@@ -57,7 +68,7 @@ def parse():
 
 def traffic_record(config):
     """HBM bytes per launch of `config` from the committed counter summary, or
-    None when the kernel source has changed since the counters were taken."""
+    None when the kernel sources have changed since the counters were taken."""
     import hashlib
     path = os.path.join(ROOT, "profiles", "hbm_traffic.json")
     if not os.path.exists(path):
@@ -67,25 +78,71 @@ def traffic_record(config):
         return None
     h = hashlib.sha256()
     for f in rec["sources"]:
-        h.update(open(os.path.join(ROOT, f), "rb").read())
+        fp = os.path.join(ROOT, f)
+        if not os.path.exists(fp):
+            return None
+        h.update(open(fp, "rb").read())
     if h.hexdigest() != rec["source_sha256"]:
         return None
     return rec
 
 
-def time_launches(torch, fn, reps, warm=10):
-    """Average ms per call of fn() over reps back-to-back calls, HIP events on
-    the current stream (the stream libgemm launches on)."""
+def stats_us(torch, fn, reps, warm=10):
+    """Times (us) of reps calls on the current stream (the stream libgemm
+    launches on): median / p10 / p90 / mean of calls each bracketed by HIP
+    events, and batch_mean, the mean of reps calls launched back to back
+    between two events (no event between calls)."""
     for _ in range(warm):
         fn()
-    s, e = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    ev = [torch.cuda.Event(enable_timing=True) for _ in range(reps + 1)]
     torch.cuda.synchronize()
-    s.record()
+    ev[0].record()
+    for i in range(reps):
+        fn()
+        ev[i + 1].record()
+    ev[-1].synchronize()
+    d = sorted(ev[i].elapsed_time(ev[i + 1]) * 1e3 for i in range(reps))
+    b0, b1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    b0.record()
     for _ in range(reps):
         fn()
-    e.record()
-    e.synchronize()
-    return s.elapsed_time(e) / reps
+    b1.record()
+    b1.synchronize()
+    pick = lambda q: d[min(reps - 1, int(q * (reps - 1) + 0.5))]  # noqa: E731
+    return {"median": pick(0.5), "p10": pick(0.1), "p90": pick(0.9), "mean": sum(d) / reps,
+            "batch_mean": b0.elapsed_time(b1) * 1e3 / reps, "calls": reps}
+
+
+def host_info():
+    model = ""
+    try:
+        for line in open("/proc/cpuinfo"):
+            if line.startswith("model name"):
+                model = line.split(":", 1)[1].strip()
+                break
+    except OSError:
+        pass
+    try:
+        nproc = int(subprocess.run(["nproc"], capture_output=True, text=True, timeout=10).stdout.strip())
+    except Exception:  # noqa: BLE001
+        nproc = os.cpu_count()
+    return nproc, model
+
+
+def sample_clock():
+    """Engine clock (MHz, mean over the XCDs) and socket power from one amd-smi call."""
+    try:
+        r = subprocess.run(["amd-smi", "metric", "-c", "-p", "--json"], capture_output=True, text=True, timeout=20)
+        d = json.loads(r.stdout)
+        g0 = d["gpu_data"][0] if isinstance(d, dict) else d[0]
+        clk = [v["clk"]["value"] for k, v in g0.get("clock", {}).items()
+               if k.startswith("gfx") and isinstance(v.get("clk", {}).get("value"), (int, float))]
+        pw = g0.get("power", {}).get("socket_power", {})
+        return {"gfx_mhz": sum(clk) / len(clk) if clk else None,
+                "power_w": pw.get("value") if isinstance(pw, dict) else None}
+    except Exception as e:  # noqa: BLE001
+        return {"error": str(e)[:160]}
 
 
 def cpu_baseline(target_s):
@@ -101,17 +158,14 @@ def cpu_baseline(target_s):
     xa, xb = wl.operand(w8, 0), wl.operand(w8, 1)
     ha, hb = wl.operand(w16, 0).view(np.uint16), wl.operand(w16, 1).view(np.uint16)
     da, db = wl.operand(wd, 0).view(np.uint16), wl.operand(wd, 1).view(np.uint16)
-    flops = 0.0
     t0 = time.perf_counter()
     sa = orc.scale_from_amax(orc.amax(xa))
     sb = orc.scale_from_amax(orc.amax(xb))
     qa, qb = orc.quantize(xa, sa), orc.quantize(xb, sb)
     t_quant = time.perf_counter() - t0
-    # probe the GEMM rate on 32 rows, then size the sample
     t1 = time.perf_counter()
     orc.gemm(orc.FMT_E4M3, qa, qb, rows=list(range(32)))
-    t_probe = time.perf_counter() - t1
-    per_row = t_probe / 32
+    per_row = (time.perf_counter() - t1) / 32
     rows = int(max(32, min(w8.M, (target_s / 2) / max(per_row, 1e-9))))
     t2 = time.perf_counter()
     R, _ = orc.gemm(orc.FMT_E4M3, qa, qb, rows=list(range(rows)))
@@ -127,8 +181,10 @@ def cpu_baseline(target_s):
     t_dec = time.perf_counter() - t4
     flops = 2.0 * rows * w8.N * w8.K + 2.0 * rows * w16.N * w16.K + 2.0 * wd.M * wd.N * wd.K
     total = t_quant + t_g8 + t_g16 + t_dec
+    nproc, model = host_info()
     return {
         "value": flops / total / 1e12, "unit": "TFLOPS", "cores": orc.num_threads(), "kind": "oracle",
+        "host_nproc": nproc, "host_cpu": model,
         "sample": (f"amax+quantize of the FP8 operands A,B [4096,4096] (full, {t_quant:.2f} s); FP8 and FP16 "
                    f"4096^3 GEMMs over the first {rows} rows of A ({t_g8:.2f} s, {t_g16:.2f} s); full M=1 decode "
                    f"1x4096x12288 ({t_dec:.2f} s); double-precision triple loop, OpenMP over rows"),
@@ -139,7 +195,7 @@ def cpu_baseline(target_s):
 def main():
     args = parse()
     if args.gpus != 1:
-        print(f"bench.py measures one GPU only (this build has no multi-GPU path); got --gpus {args.gpus}",
+        print(f"bench.py measures one GPU (every figure here is a single-GPU figure); got --gpus {args.gpus}",
               file=sys.stderr)
         sys.exit(2)
 
@@ -163,205 +219,293 @@ def main():
         torch.cuda.synchronize()
         del src, dst
 
+    kmajor = args.b_layout == "kmajor"
     w8, w16, wd = wl.C4[-1], wl.M0, wl.C3[0]
-    log(f"inputs: {w8.name}, {w16.name}, {wd.name}")
+    log(f"step inputs: {w8.name}, {w16.name}, {wd.name}; B {args.b_layout}")
     xa, xb = to(wl.operand(w8, 0)), to(wl.operand(w8, 1))
+    if kmajor:
+        xb = xb.t().contiguous()  # quantized per tensor, so Bt's codes are B's codes transposed
+    amax8, scale8 = torch.empty(2, device=dev), torch.empty(2, device=dev)
     qa = torch.empty(xa.shape, dtype=torch.uint8, device=dev)
     qb = torch.empty(xb.shape, dtype=torch.uint8, device=dev)
-    amax_a, s_a = torch.empty(1, device=dev), torch.empty(1, device=dev)
-    amax_b, s_b = torch.empty(1, device=dev), torch.empty(1, device=dev)
+    ws_pair = torch.empty(g.lib().amax_quantize_fp8_pair_workspace_size(), dtype=torch.uint8, device=dev)
     c8 = torch.empty((w8.M, w8.N), dtype=torch.uint8, device=dev)
     ha, hb = to(wl.operand(w16, 0)), to(wl.operand(w16, 1))
+    if kmajor:
+        hb = hb.t().contiguous()
     c16 = torch.empty((w16.M, w16.N), dtype=torch.float16, device=dev)
     da = to(wl.operand(wd, 0))
-    db_copies = [to(wl.operand(wd, 1))]
-    for _ in range(5):
-        db_copies.append(db_copies[0].clone())
+    db0 = to(wl.operand(wd, 1))
+    if kmajor:
+        db0 = db0.t().contiguous()
+    db_copies = [db0] + [db0.clone() for _ in range(max(0, COLD_BYTES // (db0.numel() * 2)))]
     cd = torch.empty((wd.M, wd.N), dtype=torch.float16, device=dev)
-    # K-major copies of the B operands (Bt[N,K]); the FP8 job writes its own
-    # K-major codes with the transposed quantize
-    qbt = torch.empty((w8.N, w8.K), dtype=torch.uint8, device=dev)
-    hbt = hb.t().contiguous()
-    dbt_copies = [b.t().contiguous() for b in db_copies]
 
-    # output scale of the FP8 job: amax of the FP32-output product / 448 (computed once, on the GPU)
-    g.amax_f32(xa, amax_a, s_a)
-    g.amax_f32(xb, amax_b, s_b)
-    g.quantize_fp8(xa, s_a, qa)
-    g.quantize_fp8(xb, s_b, qb)
+    gemm8 = g.gemm_fp8_scaled_bt if kmajor else g.gemm_fp8_scaled
+    gemm16 = g.gemm_f16_bt if kmajor else g.gemm_f16
+    sel = g.select_config_bt if kmajor else g.select_config
+
+    # output scale of the FP8 job: amax of the FP32-output product / 448, once
+    g.amax_quantize_fp8_pair(xa, xb, amax=amax8, scale=scale8, qa=qa, qb=qb, workspace=ws_pair)
     c32 = torch.empty((w8.M, w8.N), dtype=torch.float32, device=dev)
-    g.gemm_fp8_scaled(qa, qb, s_a, s_b, c32)
+    gemm8(qa, qb, scale8[0:1], scale8[1:2], c32)
     _, s_out = g.amax_f32(c32)
     del c32
     torch.cuda.synchronize()
-
     rot = [0]
-    kmajor = args.b_layout == "kmajor"
 
-    def fp8_job_rm(ev=None):
-        g.amax_f32(xa, amax_a, s_a)
-        g.amax_f32(xb, amax_b, s_b)
-        g.quantize_fp8(xa, s_a, qa)
-        g.quantize_fp8(xb, s_b, qb)
-        if ev is not None:
-            ev[0].record()
-        g.gemm_fp8_scaled(qa, qb, s_a, s_b, c8, s_out)
+    def fp8_job(ev=None):
+        g.amax_quantize_fp8_pair(xa, xb, amax=amax8, scale=scale8, qa=qa, qb=qb, workspace=ws_pair)
         if ev is not None:
             ev[1].record()
-
-    def fp8_job_km(ev=None):
-        g.amax_f32(xa, amax_a, s_a)
-        g.amax_f32(xb, amax_b, s_b)
-        g.quantize_fp8(xa, s_a, qa)
-        g.quantize_fp8_transposed(xb, s_b, qbt)
-        if ev is not None:
-            ev[0].record()
-        g.gemm_fp8_scaled_bt(qa, qbt, s_a, s_b, c8, s_out)
-        if ev is not None:
-            ev[1].record()
-
-    def f16_gemm_rm():
-        g.gemm_f16(ha, hb, c16)
-
-    def f16_gemm_km():
-        g.gemm_f16_bt(ha, hbt, c16)
-
-    def decode_rm():
-        g.gemm_f16(da, db_copies[rot[0] % len(db_copies)], cd)
-        rot[0] += 1
-
-    def decode_km():
-        g.gemm_f16_bt(da, dbt_copies[rot[0] % len(dbt_copies)], cd)
-        rot[0] += 1
-
-    fp8_job, f16_gemm, decode = (fp8_job_km, f16_gemm_km, decode_km) if kmajor else (fp8_job_rm, f16_gemm_rm,
-                                                                                     decode_rm)
+        gemm8(qa, qb, scale8[0:1], scale8[1:2], c8, s_out)
 
     def step(ev=None):
+        if ev is not None:
+            ev[0].record()
         fp8_job(ev)
-        f16_gemm()
-        decode()
+        if ev is not None:
+            ev[2].record()
+        gemm16(ha, hb, c16)
+        if ev is not None:
+            ev[3].record()
+        gemm16(da, db_copies[rot[0] % len(db_copies)], cd)
+        rot[0] += 1
+        if ev is not None:
+            ev[4].record()
 
     flops8 = 2.0 * w8.M * w8.N * w8.K
     flops16 = 2.0 * w16.M * w16.N * w16.K
-    flopsd = 2.0 * wd.M * wd.N * wd.K
-    flops_step = flops8 + flops16 + flopsd
+    dec_bytes = 2.0 * (wd.M * wd.K + wd.K * wd.N + wd.M * wd.N)
 
     log(f"warmup {args.warmup} steps")
     for _ in range(args.warmup):
         step()
     torch.cuda.synchronize()
     log(f"timing {args.steps} steps")
-    # HIP events around the FP8 GEMM launch of every timed step, recorded on
-    # the current stream (the one libgemm launches on): the roofline's kernel
-    # time is that launch's average inside the timed region.
-    evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(args.steps)]
+    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(5)] for _ in range(args.steps)]
+    torch.cuda.synchronize()
     t0 = time.perf_counter()
     for i in range(args.steps):
         step(evs[i])
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
     ms_step = wall * 1e3 / args.steps
-    ms_gemm8_step = sum(a.elapsed_time(b) for a, b in evs) / len(evs)
+    part = lambda a, b: sum(e[a].elapsed_time(e[b]) for e in evs) / len(evs)  # noqa: E731
+    ms_job8, ms_quant, ms_gemm8 = part(0, 2), part(0, 1), part(1, 2)
+    ms_gemm16, ms_dec = part(2, 3), part(3, 4)
+    cfg8 = sel(g.KIND_FP8, g.OUT_E4M3, w8.M, w8.N, w8.K)
+    cfg16 = sel(g.KIND_F16, g.OUT_F16, w16.M, w16.N, w16.K)
+    cfgd = sel(g.KIND_F16, g.OUT_F16, wd.M, wd.N, wd.K)
+    in_step = {
+        "fp8_job_us": ms_job8 * 1e3, "fp8_quantize_pair_us": ms_quant * 1e3, "fp8_gemm_us": ms_gemm8 * 1e3,
+        "f16_gemm_us": ms_gemm16 * 1e3, "decode_us": ms_dec * 1e3,
+        "fp8_gemm_tflops": flops8 / ms_gemm8 / 1e9, "f16_gemm_tflops": flops16 / ms_gemm16 / 1e9,
+        "decode_gbs": dec_bytes / ms_dec / 1e6,
+        "what": "HIP events on the launch stream around each part of every timed step (mean over the steps)"}
 
-    # Each row on its own (HIP events on the launch stream).
-    log("timing rows")
-    reps = args.rows_reps
-    dec_bytes = 2.0 * (wd.M * wd.K + wd.K * wd.N + wd.M * wd.N)
-    n_x = xa.numel()
     rows = {}
-    for lay, sfx in (("kmajor", "_bt"), ("rowmajor", "")):
-        km = lay == "kmajor"
-        if km:
-            gemm8 = lambda: g.gemm_fp8_scaled_bt(qa, qbt, s_a, s_b, c8, s_out)  # noqa: E731
-            sel8 = g.select_config_bt(g.KIND_FP8, g.OUT_E4M3, w8.M, w8.N, w8.K)
-            sel16 = g.select_config_bt(g.KIND_F16, g.OUT_F16, w16.M, w16.N, w16.K)
-            seld = g.select_config_bt(g.KIND_F16, g.OUT_F16, wd.M, wd.N, wd.K)
-        else:
-            gemm8 = lambda: g.gemm_fp8_scaled(qa, qb, s_a, s_b, c8, s_out)  # noqa: E731
-            sel8 = g.select_config(g.KIND_FP8, g.OUT_E4M3, w8.M, w8.N, w8.K)
-            sel16 = g.select_config(g.KIND_F16, g.OUT_F16, w16.M, w16.N, w16.K)
-            seld = g.select_config(g.KIND_F16, g.OUT_F16, wd.M, wd.N, wd.K)
-        ms_gemm8 = time_launches(torch, gemm8, reps)
-        ms_job8 = time_launches(torch, fp8_job_km if km else fp8_job_rm, max(20, reps // 4))
-        ms_gemm16 = time_launches(torch, f16_gemm_km if km else f16_gemm_rm, reps)
-        ms_dec = time_launches(torch, decode_km if km else decode_rm, reps * 2)
-        rows["fp8_gemm_4096" + sfx] = {
-            "tflops": flops8 / ms_gemm8 / 1e9, "pct_peak": 100 * flops8 / ms_gemm8 / 1e9 / PEAK_FP8_TFLOPS,
-            "us": ms_gemm8 * 1e3, "config": sel8, "b_layout": lay}
-        rows["fp8_job_4096" + sfx] = {
-            "tflops": flops8 / ms_job8 / 1e9, "us": ms_job8 * 1e3,
-            "what": "amax x2 + quantize x2 " + ("(B transposed into Bt[N,K]) " if km else "") + "+ FP8 GEMM (E4M3 out)"}
-        rows["f16_gemm_4096" + sfx] = {
-            "tflops": flops16 / ms_gemm16 / 1e9, "pct_peak": 100 * flops16 / ms_gemm16 / 1e9 / PEAK_F16_TFLOPS,
-            "us": ms_gemm16 * 1e3, "config": sel16, "b_layout": lay}
-        rows["decode_m1" + sfx] = {
-            "gbs": dec_bytes / ms_dec / 1e6, "pct_hbm": 100 * dec_bytes / ms_dec / 1e6 / PEAK_HBM_GBS,
-            "us": ms_dec * 1e3, "cold": "B rotated over 6 copies (604 MB)", "config": seld, "b_layout": lay}
-    # The decode config's other sizes (M = 4; M = 16 through split-K) and the
-    # E4M3 M = 1 decode of the M-sweep config, all on K-major weights rotated
-    # so that the Infinity Cache cannot serve them.
-    for wx in wl.C3[1:]:
-        ax = to(wl.operand(wx, 0))
-        cx = torch.empty((wx.M, wx.N), dtype=torch.float16, device=dev)
-        plan = g.splitk_plan_bt(g.KIND_F16, g.OUT_F16, wx.M, wx.N, wx.K)
-        wsx = torch.empty(plan[2], dtype=torch.uint8, device=dev) if plan[1] > 1 else None
+    if not args.no_rows:
+        log("timing rows")
+        rows = time_rows(torch, np, g, wl, to, args.rows_reps)
 
-        def dec_x(ax=ax, cx=cx, wsx=wsx):
-            g.gemm_f16_splitk_bt(ax, dbt_copies[rot[0] % len(dbt_copies)], cx, workspace=wsx)
-            rot[0] += 1
-        ms_x = time_launches(torch, dec_x, reps * 2)
-        bytes_x = 2.0 * (wx.M * wx.K + wx.K * wx.N + wx.M * wx.N)
-        rows[f"decode_m{wx.M}_bt"] = {"gbs": bytes_x / ms_x / 1e6, "pct_hbm": 100 * bytes_x / ms_x / 1e6 / PEAK_HBM_GBS,
-                                      "us": ms_x * 1e3, "config": plan[0], "splits": plan[1], "b_layout": "kmajor"}
-        del ax, cx, wsx
-    wq = wl.C4[0]
-    q_copies = [torch.empty((wq.N, wq.K), dtype=torch.uint8, device=dev) for _ in range(32)]
-    for q in q_copies:
-        q.copy_(qbt)
-    a1, c1 = qa[:1], torch.empty((1, wq.N), dtype=torch.uint8, device=dev)
+    # engine clock and power while the FP8 GEMM runs back to back (~2 s queued)
+    log("clock under load")
+    n_launch = int(2.0e6 / max(ms_gemm8 * 1e3, 1.0))
+    sa8, sb8 = scale8[0:1], scale8[1:2]
+    torch.cuda.synchronize()
+    for _ in range(n_launch):
+        gemm8(qa, qb, sa8, sb8, c8, s_out)
+    time.sleep(0.2)
+    clock = [sample_clock(), sample_clock()]
+    torch.cuda.synchronize()
 
-    def fp8_dec():
-        g.gemm_fp8_scaled_bt(a1, q_copies[rot[0] % len(q_copies)], s_a, s_b, c1, s_out)
-        rot[0] += 1
-    ms_q = time_launches(torch, fp8_dec, reps * 2)
-    bytes_q = 1.0 * (wq.K + wq.K * wq.N + wq.N)
-    rows["fp8_decode_m1_bt"] = {"gbs": bytes_q / ms_q / 1e6, "pct_hbm": 100 * bytes_q / ms_q / 1e6 / PEAK_HBM_GBS,
-                                "us": ms_q * 1e3, "config": g.select_config_bt(g.KIND_FP8, g.OUT_E4M3, 1, wq.N, wq.K),
-                                "cold": "B rotated over 32 copies (537 MB)", "b_layout": "kmajor"}
-    del q_copies
-    ms_amax = time_launches(torch, lambda: g.amax_f32(xa, amax_a, s_a), reps)
-    ms_quant = time_launches(torch, lambda: g.quantize_fp8(xa, s_a, qa), reps)
-    ms_quant_t = time_launches(torch, lambda: g.quantize_fp8_transposed(xb, s_b, qbt), reps)
-    rows["amax_64MiB"] = {"gbs": 4.0 * n_x / ms_amax / 1e6, "us": ms_amax * 1e3}
-    rows["quantize_64MiB"] = {"gbs": 5.0 * n_x / ms_quant / 1e6, "us": ms_quant * 1e3}
-    rows["quantize_transposed_64MiB"] = {"gbs": 5.0 * n_x / ms_quant_t / 1e6, "us": ms_quant_t * 1e3}
-    key8 = "fp8_gemm_4096" + ("_bt" if kmajor else "")
-    rows[key8]["us_in_step"] = ms_gemm8_step * 1e3
-    achieved = flops8 / ms_gemm8_step / 1e9
-    rec = traffic_record(rows[key8]["config"])
-    roofline = {"bound": "mfma", "kernel": "FP8 GEMM 4096^3 (" + rows[key8]["config"] + ")",
-                "kernel_us": ms_gemm8_step * 1e3,
-                "achieved": achieved, "peak": PEAK_FP8_TFLOPS, "unit": "TFLOP/s", "frac": achieved / PEAK_FP8_TFLOPS,
-                "traffic": None if rec is None else rec["hbm_bytes"],
-                "traffic_unit": "bytes per launch (FETCH_SIZE x2.0 + WRITE_SIZE x1.0, calibrated on a copy kernel)",
-                "algorithmic_bytes": float(w8.M * w8.K + w8.K * w8.N + w8.M * w8.N)}
+    def roof(bound, kernel, us, work, peak, unit, traffic=None, algo=None):
+        achieved = work / us / 1e6 if unit == "TFLOP/s" else work / us / 1e3
+        r = {"bound": bound, "kernel": kernel, "kernel_us": us, "achieved": achieved, "peak": peak, "unit": unit,
+             "frac": achieved / peak, "traffic": traffic}
+        if algo is not None:
+            r["algorithmic_bytes"] = algo
+        return r
+
+    rec8 = traffic_record(cfg8)
+    roofline = roof("mfma", f"FP8 GEMM 4096^3 E4M3 out ({cfg8})", ms_gemm8 * 1e3, flops8, PEAK_FP8_TFLOPS, "TFLOP/s",
+                    None if rec8 is None else rec8["hbm_bytes"], float(w8.M * w8.K + w8.K * w8.N + w8.M * w8.N))
+    roofline["traffic_unit"] = "HBM bytes per launch (FETCH_SIZE + WRITE_SIZE, scaled by a copy kernel's counters)"
+    rec16 = traffic_record(cfg16)
+    roofline_f16 = roof("mfma", f"FP16 GEMM 4096^3 ({cfg16})", ms_gemm16 * 1e3, flops16, PEAK_F16_TFLOPS, "TFLOP/s",
+                        None if rec16 is None else rec16["hbm_bytes"], float(2 * (3 * 4096 * 4096)))
+    recd = traffic_record(cfgd)
+    roofline_dec = roof("hbm", f"FP16 decode 1x4096x12288 ({cfgd}), B rotated over {len(db_copies)} copies",
+                        ms_dec * 1e3, dec_bytes, PEAK_HBM_GBS, "GB/s",
+                        None if recd is None else recd["hbm_bytes"], dec_bytes)
 
     cpu = None
     if not args.no_cpu_baseline:
         log("cpu baseline (oracle)")
         cpu = cpu_baseline(args.cpu_seconds)
 
+    ok_clk = [c for c in clock if c.get("gfx_mhz")]
     out = {
-        "metric": METRIC, "value": flops_step / (ms_step * 1e-3) / 1e12, "unit": "TFLOPS", "n_gpus": 1,
+        "metric": METRIC, "value": flops8 / ms_job8 / 1e9, "unit": "TFLOPS", "n_gpus": 1,
         "steps": args.steps, "warmup": args.warmup, "ms_per_step": ms_step, "higher_is_better": True,
-        "scaling": "weak", "vs_baseline": None, "dtype": "fp8_e4m3+f16 (f32 accumulate)", "data": "synthetic",
-        "config": {"workload": "fp8 e4m3 job 4096^3 (amax, quantize, GEMM, fp8 out) + fp16 GEMM 4096^3 + "
-                               "fp16 decode 1x4096x12288", "M": 4096, "N": 4096, "K": 4096,
-                   "decode": [1, 4096, 12288], "b_layout": args.b_layout},
-        "rows": rows, "roofline": roofline, "cpu_baseline": cpu,
+        "scaling": "weak", "vs_baseline": None, "dtype": "fp8_e4m3 and fp16 operands, f32 accumulate",
+        "data": "synthetic (seeded; the workload list's shapes and distributions)",
+        "config": {"workload": "fp8 e4m3 4096^3 job (amax, scale, quantize of A and B; GEMM, e4m3 out) + fp16 "
+                               "GEMM 4096^3 + fp16 decode 1x4096x12288", "M": 4096, "N": 4096, "K": 4096,
+                   "decode": [1, 4096, 12288], "b_layout": args.b_layout,
+                   "value": "FP8 job TFLOPS: 2*4096^3 / in-step time of amax+scale+quantize of A and B plus the "
+                            "GEMM (E4M3 out)"},
+        "in_step": in_step, "roofline": roofline, "roofline_f16": roofline_f16, "roofline_decode": roofline_dec,
+        "clock": {"samples": ok_clk or clock, "what": "amd-smi engine clock (mean over XCDs) and socket power, "
+                  "sampled twice while the FP8 4096^3 GEMM runs back to back", "peak_mhz": 2400},
+        "rows": rows, "cpu_baseline": cpu,
     }
     print(json.dumps(out), flush=True)
+
+
+def time_rows(torch, np, g, wl, to, reps):
+    """Every configuration of the workload list, row-major and K-major B."""
+    rows = {}
+
+    def add(name, st, flops=None, nbytes=None, cfg=None, peak=None, extra=None):
+        r = {"us": st, "config": cfg}
+        us = st["median"]
+        if flops:
+            r["tflops_median"] = flops / us / 1e6
+            if peak:
+                r["pct_peak_median"] = 100 * flops / us / 1e6 / peak
+        if nbytes:
+            r["gbs_median"] = nbytes / us / 1e3
+            r["pct_hbm_median"] = 100 * nbytes / us / 1e3 / PEAK_HBM_GBS
+        if extra:
+            r.update(extra)
+        rows[name] = r
+        log(f"  {name}: {us:.2f} us ({cfg})")
+
+    def fp8_inputs(w):
+        xa, xb = to(wl.operand(w, 0)), to(wl.operand(w, 1))
+        _, scale, qa, qb = g.amax_quantize_fp8_pair(xa, xb)
+        del xa, xb
+        return qa, qb, scale
+
+    one = torch.ones(1, device="cuda")
+    # ---- FP16 GEMMs: C1 (F32 out), M0 and C5 (F16 out)
+    for w in (wl.C1, wl.M0, wl.C5_F16):
+        a, b = to(wl.operand(w, 0)), to(wl.operand(w, 1))
+        bt = b.t().contiguous()
+        c = torch.empty((w.M, w.N), dtype=torch.float32 if w.out == 0 else torch.float16, device="cuda")
+        out = g.OUT_F32 if w.out == 0 else g.OUT_F16
+        f = 2.0 * w.M * w.N * w.K
+        n_rep = reps if w.M * w.N * w.K <= 4096 ** 3 else max(20, reps // 4)
+        add(w.name, stats_us(torch, lambda: g.gemm_f16(a, b, c), n_rep), f, cfg=g.select_config(g.KIND_F16, out, w.M, w.N, w.K),
+            peak=PEAK_F16_TFLOPS, extra={"b_layout": "rowmajor"})
+        add(w.name + "_bt", stats_us(torch, lambda: g.gemm_f16_bt(a, bt, c), n_rep), f,
+            cfg=g.select_config_bt(g.KIND_F16, out, w.M, w.N, w.K), peak=PEAK_F16_TFLOPS, extra={"b_layout": "kmajor"})
+        del a, b, bt, c
+    # ---- FP8 GEMMs: C2 (F32 out), C5 FP8 (F16 out)
+    for w in (wl.C2, wl.C5_FP8):
+        qa, qb, scale = fp8_inputs(w)
+        qbt = qb.t().contiguous()
+        c = torch.empty((w.M, w.N), dtype=torch.float32 if w.out == 0 else torch.float16, device="cuda")
+        out = g.OUT_F32 if w.out == 0 else g.OUT_F16
+        f = 2.0 * w.M * w.N * w.K
+        n_rep = reps if w.M * w.N * w.K <= 4096 ** 3 else max(20, reps // 4)
+        add(w.name, stats_us(torch, lambda: g.gemm_fp8_scaled(qa, qb, scale[0:1], scale[1:2], c), n_rep), f,
+            cfg=g.select_config(g.KIND_FP8, out, w.M, w.N, w.K), peak=PEAK_FP8_TFLOPS, extra={"b_layout": "rowmajor"})
+        add(w.name + "_bt", stats_us(torch, lambda: g.gemm_fp8_scaled_bt(qa, qbt, scale[0:1], scale[1:2], c), n_rep), f,
+            cfg=g.select_config_bt(g.KIND_FP8, out, w.M, w.N, w.K), peak=PEAK_FP8_TFLOPS, extra={"b_layout": "kmajor"})
+        del qa, qb, qbt, c
+    # ---- C4: FP8 N = K = 4096, M swept, E4M3 output; B rotated for M <= 129
+    wbig = wl.C4[-1]
+    xb = to(wl.operand(wbig, 1))
+    _, sb = g.amax_f32(xb)
+    qb = g.quantize_fp8(xb, sb)
+    del xb
+    qbt = qb.t().contiguous()
+    n_copies = COLD_BYTES // qb.numel()
+    cold_b = [qb] + [qb.clone() for _ in range(n_copies - 1)]
+    cold_bt = [qbt] + [qbt.clone() for _ in range(n_copies - 1)]
+    rot = [0]
+    for w in wl.C4:
+        xa = to(wl.operand(w, 0))
+        _, sa = g.amax_f32(xa)
+        qa = g.quantize_fp8(xa, sa)
+        del xa
+        c32 = torch.empty((w.M, w.N), dtype=torch.float32, device="cuda")
+        g.gemm_fp8_scaled(qa, qb, sa, sb, c32)
+        _, s_out = g.amax_f32(c32)
+        del c32
+        c = torch.empty((w.M, w.N), dtype=torch.uint8, device="cuda")
+        cold = w.M <= 129
+        f = 2.0 * w.M * w.N * w.K
+        nb = float(w.M * w.K + w.K * w.N + w.M * w.N)
+
+        def run_rm(qa=qa, sa=sa, c=c, s_out=s_out, cold=cold):
+            b = cold_b[rot[0] % len(cold_b)] if cold else qb
+            rot[0] += 1
+            g.gemm_fp8_scaled(qa, b, sa, sb, c, s_out)
+
+        def run_km(qa=qa, sa=sa, c=c, s_out=s_out, cold=cold):
+            b = cold_bt[rot[0] % len(cold_bt)] if cold else qbt
+            rot[0] += 1
+            g.gemm_fp8_scaled_bt(qa, b, sa, sb, c, s_out)
+
+        ex = {"cold": f"B rotated over {n_copies} copies" if cold else "warm"}
+        add(w.name, stats_us(torch, run_rm, reps), f, nb, g.select_config(g.KIND_FP8, g.OUT_E4M3, w.M, w.N, w.K),
+            PEAK_FP8_TFLOPS, dict(ex, b_layout="rowmajor"))
+        add(w.name + "_bt", stats_us(torch, run_km, reps), f, nb,
+            g.select_config_bt(g.KIND_FP8, g.OUT_E4M3, w.M, w.N, w.K), PEAK_FP8_TFLOPS, dict(ex, b_layout="kmajor"))
+        if w.M == 4096:
+            # the exact-accumulation call on the same operands (context: FP16 matrix cores)
+            add(w.name + "_exact", stats_us(torch, lambda: g.gemm_fp8_exact(qa, g.FMT_E4M3, qb, g.FMT_E4M3, sa, sb, c,
+                                                                            s_out), reps), f, nb,
+                g.select_config_exact(g.OUT_E4M3, w.M, w.N, w.K), PEAK_F16_TFLOPS, {"b_layout": "rowmajor"})
+        del qa, c
+    del cold_b, cold_bt, qb, qbt
+    # ---- C3: FP16 decode M in {1, 4, 16}, B rotated
+    b0 = to(wl.operand(wl.C3[0], 1))
+    n_copies = max(2, COLD_BYTES // (b0.numel() * 2))
+    cold_b = [b0] + [b0.clone() for _ in range(n_copies - 1)]
+    cold_bt = [x.t().contiguous() for x in cold_b]
+    for w in wl.C3:
+        a = to(wl.operand(w, 0))
+        c = torch.empty((w.M, w.N), dtype=torch.float16, device="cuda")
+        nb = 2.0 * (w.M * w.K + w.K * w.N + w.M * w.N)
+        f = 2.0 * w.M * w.N * w.K
+
+        def run_rm(a=a, c=c):
+            g.gemm_f16(a, cold_b[rot[0] % len(cold_b)], c)
+            rot[0] += 1
+
+        def run_km(a=a, c=c):
+            g.gemm_f16_bt(a, cold_bt[rot[0] % len(cold_bt)], c)
+            rot[0] += 1
+
+        ex = {"cold": f"B rotated over {n_copies} copies"}
+        add(w.name, stats_us(torch, run_rm, 2 * reps), f, nb, g.select_config(g.KIND_F16, g.OUT_F16, w.M, w.N, w.K),
+            extra=dict(ex, b_layout="rowmajor"))
+        add(w.name + "_bt", stats_us(torch, run_km, 2 * reps), f, nb,
+            g.select_config_bt(g.KIND_F16, g.OUT_F16, w.M, w.N, w.K), extra=dict(ex, b_layout="kmajor"))
+        del a, c
+    del cold_b, cold_bt, b0
+    # ---- amax / quantize of the FP8 4096^3 operands (128 MiB of FP32)
+    xa, xb = to(wl.operand(wbig, 0)), to(wl.operand(wbig, 1))
+    n2 = xa.numel() + xb.numel()
+    ws = torch.empty(g.lib().amax_quantize_fp8_pair_workspace_size(), dtype=torch.uint8, device="cuda")
+    am, sc = torch.empty(2, device="cuda"), torch.empty(2, device="cuda")
+    q1, q2 = torch.empty_like(xa, dtype=torch.uint8), torch.empty_like(xb, dtype=torch.uint8)
+    add("amax_quantize_pair_2x64MiB",
+        stats_us(torch, lambda: g.amax_quantize_fp8_pair(xa, xb, amax=am, scale=sc, qa=q1, qb=q2, workspace=ws), reps),
+        nbytes=9.0 * n2, cfg="pair_reduce + pair_quantize",
+        extra={"what": "amax, scale and E4M3 codes of A and B (4 B read twice + 1 B written per element)"})
+    a1, s1 = torch.empty(1, device="cuda"), torch.empty(1, device="cuda")
+    add("amax_64MiB", stats_us(torch, lambda: g.amax_f32(xa, a1, s1), reps), nbytes=4.0 * xa.numel(),
+        cfg="amax_init + amax_reduce + amax_finalize")
+    add("quantize_64MiB", stats_us(torch, lambda: g.quantize_fp8(xa, s1, q1), reps), nbytes=5.0 * xa.numel(),
+        cfg="quantize")
+    del one
+    return rows
 
 
 if __name__ == "__main__":

@@ -425,6 +425,34 @@ int gemm_splitk_plan_bt(int kind, int out_dtype, int64_t M, int64_t N, int64_t K
                         char* buf, int buflen, int* splits, int64_t* workspace_bytes);
 
 /*
+ * amax_quantize_fp8_pair — both operands of an FP8 GEMM in two launches:
+ * amax[0] = max|A|, scale[0] = the scale of amax[0] for format fmt (pow2 = 0:
+ * fl32(amax / fmax) with 0 -> 1, as amax_f32 / amax_scale_f32; pow2 != 0: the
+ * power of two of amax_scale_f32), qa = FP8(fl32(A / scale[0])) as
+ * quantize_fp8_fmt; the same for B into amax[1], scale[1], qb. Every value is
+ * bit-identical to the separate calls. P2 §3.2 (per-tensor scale max/448 for
+ * each operand), §4.3 (the quantize formula), §4.4 (launch overhead dominates
+ * small work: batch it); P1 §3.3 (maxima on the GPU, on a stream).
+ *   A, na      device, float[na]; na = 0 gives amax 0, scale 1, no codes
+ *   B, nb      device, float[nb]; nb = 0: only A is processed, amax[1] and
+ *              scale[1] are not written
+ *   fmt, pow2  GEMM_FMT_E4M3 or GEMM_FMT_E5M2; scale rule as amax_scale_f32
+ *   amax, scale  device, float[2] (float[1] when nb = 0), written
+ *   qa, qb     device, uint8[na] and uint8[nb], written
+ *   workspace  device scratch of at least
+ *              amax_quantize_fp8_pair_workspace_size() bytes, 16-byte
+ *              aligned, owned by the caller; its contents are overwritten
+ * Errors: GEMM_ERR_DTYPE (fmt), GEMM_ERR_DIM (a count negative or of 2^62
+ * bytes or more), GEMM_ERR_NULL, GEMM_ERR_WORKSPACE, GEMM_ERR_ALIAS (any two
+ * written ranges, or a written range and an input, overlap). No allocation.
+ */
+int amax_quantize_fp8_pair(const float* A, int64_t na, const float* B, int64_t nb, int fmt, int pow2,
+                           float* amax, float* scale, uint8_t* qa, uint8_t* qb, void* workspace,
+                           int64_t workspace_bytes, hipStream_t stream);
+/* Bytes of scratch amax_quantize_fp8_pair needs (a constant, 4096). */
+int64_t amax_quantize_fp8_pair_workspace_size(void);
+
+/*
  * gemm_fp8_exact / gemm_fp8_exact_bt — gemm_fp8_fmt / gemm_fp8_fmt_bt with
  * every product exact and every addition an FP32 addition (P2 §2.1: FP8
  * inputs with FP32 accumulation; §4.3: results are checked against an FP32

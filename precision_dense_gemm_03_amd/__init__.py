@@ -34,6 +34,9 @@ Functions keep the C names:
     gemm_fp8_splitk_bt(A, Bt, sA, sB, C, sOut=None, workspace=None, stream=None, out_fmt=None)
     gemm_f16_splitk_bt(A, Bt, C, workspace=None, stream=None)
     splitk_plan_bt(kind, out_dtype, M, N, K) -> (config, splits, workspace_bytes)
+  Both FP8 operands in two launches (amax, scale and quantize of A and B):
+    amax_quantize_fp8_pair(xa, xb, fmt=FMT_E4M3, pow2=False, amax=None, scale=None, qa=None, qb=None,
+                           workspace=None, stream=None) -> (amax[2], scale[2], qa, qb)
   Exact-accumulation FP8 (FP8 codes widened to FP16, FP16 matrix cores):
     gemm_fp8_exact(A, fmt_a, B, fmt_b, sA, sB, C, sOut=None, stream=None, out_fmt=None)
     gemm_fp8_exact_bt(A, fmt_a, Bt, fmt_b, sA, sB, C, sOut=None, stream=None, out_fmt=None)
@@ -143,6 +146,10 @@ def lib() -> ctypes.CDLL:
     L.gemm_splitk_plan_bt.restype = i32
     L.gemm_splitk_plan_bt.argtypes = [i32, i32, i64, i64, i64, ctypes.c_char_p, i32, ctypes.POINTER(i32),
                                       ctypes.POINTER(i64)]
+    L.amax_quantize_fp8_pair.restype = i32
+    L.amax_quantize_fp8_pair.argtypes = [vp, i64, vp, i64, i32, i32, vp, vp, vp, vp, vp, i64, vp]
+    L.amax_quantize_fp8_pair_workspace_size.restype = i64
+    L.amax_quantize_fp8_pair_workspace_size.argtypes = []
     L.gemm_fp8_exact.restype = i32
     L.gemm_fp8_exact.argtypes = [vp, i32, vp, i32, vp, vp, vp, vp, i32, i64, i64, i64, vp]
     L.gemm_fp8_exact_bt.restype = i32
@@ -640,3 +647,39 @@ def select_config_exact(out_dtype: int, M: int, N: int, K: int, fmt_a: int = 0, 
     _check(lib().gemm_select_config_exact(out_dtype, M, N, K, int(fmt_a), int(fmt_b), int(b_kmajor), buf, len(buf)),
            "gemm_select_config_exact")
     return buf.value.decode()
+
+
+def amax_quantize_fp8_pair(xa, xb, fmt=FMT_E4M3, pow2=False, amax=None, scale=None, qa=None, qb=None,
+                           workspace=None, stream=None):
+    """amax, scale and FP8 codes of two float32 tensors in two launches:
+    returns (amax[2], scale[2], qa, qb), bit-identical to amax_scale_f32 and
+    quantize_fp8_fmt on each. xb may be None (then amax and scale have one
+    element and qb is None)."""
+    torch = _torch()
+    for name, x in (("xa", xa), ("xb", xb)):
+        if x is not None and x.dtype != torch.float32:
+            raise ValueError(f"{name} must be float32")
+    dev = xa.device
+    two = xb is not None
+    if amax is None:
+        amax = torch.empty(2 if two else 1, dtype=torch.float32, device=dev)
+    if scale is None:
+        scale = torch.empty(2 if two else 1, dtype=torch.float32, device=dev)
+    if qa is None:
+        qa = torch.empty(xa.shape, dtype=torch.uint8, device=dev)
+    if two and qb is None:
+        qb = torch.empty(xb.shape, dtype=torch.uint8, device=dev)
+    qav = _u8(qa, fmt)
+    qbv = _u8(qb, fmt) if two else None
+    if qav.numel() != xa.numel() or (two and qbv.numel() != xb.numel()):
+        raise ValueError("q must have as many elements as its x")
+    if amax.numel() < (2 if two else 1) or scale.numel() < (2 if two else 1):
+        raise ValueError("amax and scale need one element per tensor")
+    if workspace is None:
+        workspace = torch.empty(int(lib().amax_quantize_fp8_pair_workspace_size()), dtype=torch.uint8, device=dev)
+    _check(lib().amax_quantize_fp8_pair(_ptr(xa), xa.numel(), _ptr(xb) if two else None, xb.numel() if two else 0,
+                                        int(fmt), 1 if pow2 else 0, _ptr(amax), _ptr(scale), _ptr(qav),
+                                        _ptr(qbv) if two else None, _ptr(workspace),
+                                        workspace.numel() * workspace.element_size(), _stream_handle(stream)),
+           "amax_quantize_fp8_pair")
+    return amax, scale, qa, qb

@@ -94,6 +94,13 @@ hipError_t launch_splitk_reduce(const GemmArgs& a);
 // power-of-two scale.
 hipError_t launch_amax(const float* x, int64_t n, float* amax, float* scale, int fmt, int pow2, hipStream_t stream);
 hipError_t launch_quantize(const float* x, int64_t n, const float* scale, uint8_t* q, int fmt, hipStream_t stream);
+// amax, scale and quantize of two tensors in two launches (A, and B when
+// nb > 0): amax[0..1], scale[0..1], qa, qb. slots: kPairSlots words of device
+// scratch for the per-block maxima.
+constexpr int kPairSlots = 1024;
+hipError_t launch_amax_quantize_pair(const float* xa, int64_t na, const float* xb, int64_t nb, int fmt, int pow2,
+                                     float* amax, float* scale, uint8_t* qa, uint8_t* qb, uint32_t* slots,
+                                     hipStream_t stream);
 // Quantize with a transposed output: q[c * rows + r] = code(x[r * cols + c] / scale).
 hipError_t launch_quantize_transposed(const float* x, int64_t rows, int64_t cols, const float* scale, uint8_t* q,
                                       int fmt, hipStream_t stream);

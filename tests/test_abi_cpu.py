@@ -426,3 +426,24 @@ def test_float8_dtype_must_match_the_entry_points_format():
     assert g._u8(torch.zeros(3, dtype=torch.uint8), g.FMT_E5M2).dtype == torch.uint8
     with pytest.raises(ValueError, match="E4M3"):
         g.gemm_fp8_scaled(e5, e4, None, None, torch.zeros((4, 4)))
+
+
+def test_pair_quantize_argument_validation():
+    L = g.lib()
+    ws = L.amax_quantize_fp8_pair_workspace_size()
+    assert ws == 4096
+    A, B = FAKE, FAKE2
+    am, sc, qa, qb, w = FAKE3, FAKE3 + 64, FAKE3 + 4096, FAKE3 + 8192, FAKE3 + 65536
+    # (A, na, B, nb, fmt, pow2, amax, scale, qa, qb, ws, ws_bytes, stream)
+    assert L.amax_quantize_fp8_pair(A, 10, B, 10, 7, 0, am, sc, qa, qb, w, ws, None) == -3     # format
+    assert L.amax_quantize_fp8_pair(A, -1, B, 10, 0, 0, am, sc, qa, qb, w, ws, None) == -2    # count
+    assert L.amax_quantize_fp8_pair(A, 2 ** 61, B, 10, 0, 0, am, sc, qa, qb, w, ws, None) == -2
+    assert L.amax_quantize_fp8_pair(A, 10, B, 10, 0, 0, None, sc, qa, qb, w, ws, None) == -1
+    assert L.amax_quantize_fp8_pair(A, 10, B, 10, 0, 0, am, sc, qa, None, w, ws, None) == -1
+    assert L.amax_quantize_fp8_pair(A, 10, B, 10, 0, 0, am, sc, qa, qb, None, ws, None) == -1
+    assert L.amax_quantize_fp8_pair(A, 10, B, 10, 0, 0, am, sc, qa, qb, w, ws - 1, None) == -9
+    assert L.amax_quantize_fp8_pair(A, 10, B, 10, 0, 0, am, sc, qa, qb, w + 4, ws, None) == -9  # misaligned
+    assert L.amax_quantize_fp8_pair(A, 10, B, 10, 0, 0, am, sc, A + 8, qb, w, ws, None) == -8   # qa over A
+    assert L.amax_quantize_fp8_pair(A, 10, B, 10, 0, 0, am, sc, qa, qa + 5, w, ws, None) == -8  # qa, qb overlap
+    assert L.amax_quantize_fp8_pair(A, 10, B, 10, 0, 0, am, am + 4, qa, qb, w, ws, None) == -8  # amax[1] is scale
+    assert L.amax_quantize_fp8_pair(A, 10, B, 10, 0, 0, am, sc, qa, qb, qb, ws, None) == -8     # ws over qb
