@@ -149,4 +149,64 @@ __device__ __forceinline__ void store_out(void* C, int64_t idx, float y, int out
     }
 }
 
+// LDS reads issued as a group and waited for inside the same asm block, so
+// the results are complete when the block ends. Written in asm for kernels
+// that fill LDS with direct global->LDS loads and wait for them explicitly:
+// where the compiler cannot tell which LDS object a read touches (always for
+// the transpose-read builtins, and at some loop heads for plain loads) it
+// waits for every outstanding global->LDS load before the read, which drains
+// the prefetch ring. The outputs are early-
+// clobber (a result must not land in a register that a later address of the
+// group still needs). Arguments are LDS byte addresses.
+__device__ __forceinline__ void lds_tr8_x4(v2i (&t)[4], uint32_t a0, uint32_t a1, uint32_t a2, uint32_t a3) {
+    asm volatile(
+        "ds_read_b64_tr_b8 %0, %4\n\t"
+        "ds_read_b64_tr_b8 %1, %5\n\t"
+        "ds_read_b64_tr_b8 %2, %6\n\t"
+        "ds_read_b64_tr_b8 %3, %7\n\t"
+        "s_waitcnt lgkmcnt(0)"
+        : "=&v"(t[0]), "=&v"(t[1]), "=&v"(t[2]), "=&v"(t[3])
+        : "v"(a0), "v"(a1), "v"(a2), "v"(a3)
+        : "memory");
+}
+
+__device__ __forceinline__ void lds_tr16_x2(v4s (&t)[2], uint32_t a0, uint32_t a1) {
+    asm volatile(
+        "ds_read_b64_tr_b16 %0, %2\n\t"
+        "ds_read_b64_tr_b16 %1, %3\n\t"
+        "s_waitcnt lgkmcnt(0)"
+        : "=&v"(t[0]), "=&v"(t[1])
+        : "v"(a0), "v"(a1)
+        : "memory");
+}
+
+// 16-byte LDS reads in one asm block with their wait, for the same reason.
+__device__ __forceinline__ void lds_b128_x1(v4i& t, uint32_t a0) {
+    asm volatile("ds_read_b128 %0, %1\n\ts_waitcnt lgkmcnt(0)" : "=&v"(t) : "v"(a0) : "memory");
+}
+
+__device__ __forceinline__ void lds_b128_x2(v4i (&t)[2], uint32_t a0, uint32_t a1) {
+    asm volatile(
+        "ds_read_b128 %0, %2\n\t"
+        "ds_read_b128 %1, %3\n\t"
+        "s_waitcnt lgkmcnt(0)"
+        : "=&v"(t[0]), "=&v"(t[1])
+        : "v"(a0), "v"(a1)
+        : "memory");
+}
+
+__device__ __forceinline__ void lds_b128_x4(v4i (&t)[4], uint32_t a0, uint32_t a1, uint32_t a2, uint32_t a3) {
+    asm volatile(
+        "ds_read_b128 %0, %4\n\t"
+        "ds_read_b128 %1, %5\n\t"
+        "ds_read_b128 %2, %6\n\t"
+        "ds_read_b128 %3, %7\n\t"
+        "s_waitcnt lgkmcnt(0)"
+        : "=&v"(t[0]), "=&v"(t[1]), "=&v"(t[2]), "=&v"(t[3])
+        : "v"(a0), "v"(a1), "v"(a2), "v"(a3)
+        : "memory");
+}
+
+__device__ __forceinline__ uint32_t lds_addr(const LDS_AS void* p) { return (uint32_t)(uintptr_t)p; }
+
 }  // namespace libgemm

@@ -258,12 +258,14 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
             // read q: lane j16 addresses k-row 32 h + 8 q + j16 / 2, bytes
             // 8 (j16 % 2) of the column chunk; k-row % 8 = j16 / 2.
             const int chunk = (4 * wj + 2 * jb + half) ^ swz_b<1>(j16 >> 1);
-            v2i t[4];
+            uint32_t ad[4];
 #pragma unroll
             for (int q = 0; q < 4; ++q) {
                 const int k = 32 * h + 8 * q + (j16 >> 1);
-                t[q] = __builtin_amdgcn_ds_read_tr8_b64_v2i32((LDS_AS v2i*)(sb + k * T::BNB + chunk * 16 + 8 * (j16 & 1)));
+                ad[q] = lds_addr(sb + k * T::BNB + chunk * 16 + 8 * (j16 & 1));
             }
+            v2i t[4];
+            lds_tr8_x4(t, ad[0], ad[1], ad[2], ad[3]);
             const v4i t01 = __builtin_shufflevector(t[0], t[1], 0, 1, 2, 3);
             const v4i t23 = __builtin_shufflevector(t[2], t[3], 0, 1, 2, 3);
             return __builtin_shufflevector(t01, t23, 0, 1, 2, 3, 4, 5, 6, 7);
@@ -271,12 +273,14 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
             // k-step u: lane j16 addresses k-row 16 u + 8 h + 4 q + j16 / 4,
             // columns 64 wj + 32 jb + 16 half + 4 (j16 % 4) .. + 3; k-row % 4 = j16 / 4.
             const int chunk = (8 * wj + 4 * jb + 2 * half + ((j16 & 3) >> 1)) ^ swz_b<2>(j16 >> 2);
-            v4s t[2];
+            uint32_t ad[2];
 #pragma unroll
             for (int q = 0; q < 2; ++q) {
                 const int k = 16 * u + 8 * h + 4 * q + (j16 >> 2);
-                t[q] = __builtin_amdgcn_ds_read_tr16_b64_v4i16((LDS_AS v4s*)(sb + k * T::BNB + chunk * 16 + 8 * (j16 & 1)));
+                ad[q] = lds_addr(sb + k * T::BNB + chunk * 16 + 8 * (j16 & 1));
             }
+            v4s t[2];
+            lds_tr16_x2(t, ad[0], ad[1]);
             return __builtin_bit_cast(v8h, __builtin_shufflevector(t[0], t[1], 0, 1, 2, 3, 4, 5, 6, 7));
         }
     };

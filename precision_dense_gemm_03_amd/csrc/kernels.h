@@ -40,7 +40,7 @@ struct GemmConfig {
     int kind;           // OperandKind
     int family;         // 0 = MFMA tile kernel, 1 = M<=16 streaming kernel, 2 = direct-load tile kernel,
                         // 3 = K-major decode kernel, 4 = ping-pong tile kernel,
-                        // 5 = exact-accumulation FP8 tile kernel
+                        // 5 = exact-accumulation FP8 tile kernel, 6 = deep-ring skinny kernel
     int bm, bn, bk;     // tile (stream: bm = max M, bn = columns per block, bk = k-slices)
     GemmLauncher launch;
     int fmt_mask = 0;   // FP8 operand pairs served: bit (2*fmt_a + fmt_b); 0 means E4M3 x E4M3 only
@@ -63,6 +63,7 @@ const GemmConfig* dma_configs(int* count);
 const GemmConfig* gemv_kmajor_configs(int* count);
 const GemmConfig* pp_configs(int* count);
 const GemmConfig* exact_configs(int* count);
+const GemmConfig* ring_configs(int* count);
 
 // Shape (and FP8 operand formats) -> configuration (host only, no HIP calls).
 // Returns NULL if none fits.

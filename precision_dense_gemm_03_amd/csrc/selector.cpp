@@ -43,6 +43,7 @@ constexpr int64_t kNumCUs = 256;
 constexpr int64_t kStreamMaxM = 4;
 constexpr int64_t kGemvMaxM = 8;
 constexpr int64_t kSplitMaxM = 256;
+constexpr int64_t kRingMaxM = 256;
 
 // Whether c can serve the request (operand kind, FP8 formats, B layout).
 bool serves(const GemmConfig& c, int kind, int fa, int fb, int bt) {
@@ -68,7 +69,34 @@ const GemmConfig* find_named(const char* name, int kind, int64_t M, int fa = 0, 
     const GemmConfig* pt = pp_configs(&np);
     for (int i = 0; i < np; ++i)
         if (std::strcmp(pt[i].name, name) == 0 && serves(pt[i], kind, fa, fb, bt)) return &pt[i];
+    int nr = 0;
+    const GemmConfig* rt = ring_configs(&nr);
+    for (int i = 0; i < nr; ++i)
+        if (std::strcmp(rt[i].name, name) == 0 && serves(rt[i], kind, fa, fb, bt)) return &rt[i];
     return nullptr;
+}
+
+// Skinny shapes (M <= 256 beyond the decode kernels): the deep-ring kernel
+// whose tile minimises the bytes one compute unit must stream. A workgroup
+// reads (bm + bn) K elements; a grid of more than one workgroup per compute
+// unit repeats that per round. Ties go to the larger tile (fewer workgroups
+// re-reading A and B).
+const GemmConfig* ring_for(int kind, int64_t M, int64_t N, int fa, int fb, int bt) {
+    int nr = 0;
+    const GemmConfig* rt = ring_configs(&nr);
+    const GemmConfig* pick = nullptr;
+    int64_t best = 0;
+    for (int i = 0; i < nr; ++i) {
+        const GemmConfig& c = rt[i];
+        if (!serves(c, kind, fa, fb, bt)) continue;
+        const int64_t tiles = ((M + c.bm - 1) / c.bm) * ((N + c.bn - 1) / c.bn);
+        const int64_t cost = ((tiles + kNumCUs - 1) / kNumCUs) * (c.bm + c.bn);
+        if (!pick || cost < best || (cost == best && c.bm * c.bn > pick->bm * pick->bn)) {
+            pick = &c;
+            best = cost;
+        }
+    }
+    return pick;
 }
 
 // The preferred configuration of each tile size. 256x256 tiles use the
@@ -110,6 +138,9 @@ const GemmConfig* select_config(int kind, int out_dtype, int64_t M, int64_t N, i
                 if (serves(vt[i], kind, fa, fb, 1) && M <= vt[i].bm && (!best || vt[i].bm < best->bm)) best = &vt[i];
             if (best) return best;
         }
+        if (M <= kRingMaxM) {
+            if (const GemmConfig* c = ring_for(kind, M, N, fa, fb, 1)) return c;
+        }
         // Tiles as for row-major B.
         static const int bt_sizes[] = {256, 128, 64};
         for (int bm : bt_sizes) {
@@ -132,6 +163,9 @@ const GemmConfig* select_config(int kind, int out_dtype, int64_t M, int64_t N, i
             if (serves(c, kind, fa, fb, 0) && M <= c.bm && (!best || c.bm < best->bm)) best = &c;
         }
         if (best) return best;
+    }
+    if (M <= kRingMaxM) {
+        if (const GemmConfig* c = ring_for(kind, M, N, fa, fb, 0)) return c;
     }
     // 256x256 tiles already from 3/4 of the CUs (E4M3 3000x4096x4096: 61.3 us
     // on 192 ping-pong tiles vs 72.7 us on 768 tiles of 128x128).

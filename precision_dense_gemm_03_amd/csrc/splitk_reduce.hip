@@ -79,7 +79,15 @@ __global__ __launch_bounds__(kThreads) void splitk_reduce_kernel(const float* __
 #pragma unroll
                 for (int j = 0; j < kUnroll; ++j) s += t[j];
             }
-            for (; sp < splits; ++sp) s += __builtin_nontemporal_load(&w4[(int64_t)sp * nq + q]);
+            if (sp < splits) {  // the last < kUnroll slices, loaded together, added in order
+                v4f t[kUnroll - 1];
+#pragma unroll
+                for (int j = 0; j < kUnroll - 1; ++j)
+                    if (sp + j < splits) t[j] = __builtin_nontemporal_load(&w4[(int64_t)(sp + j) * nq + q]);
+#pragma unroll
+                for (int j = 0; j < kUnroll - 1; ++j)
+                    if (sp + j < splits) s += t[j];
+            }
             v4f y = s * scale;
             const int64_t idx = 4 * q;
             if (chan) {
@@ -103,7 +111,15 @@ __global__ __launch_bounds__(kThreads) void splitk_reduce_kernel(const float* __
 #pragma unroll
                 for (int j = 0; j < kUnroll; ++j) s += t[j];
             }
-            for (; sp < splits; ++sp) s += ws[(int64_t)sp * mn + i];
+            if (sp < splits) {
+                float t[kUnroll - 1];
+#pragma unroll
+                for (int j = 0; j < kUnroll - 1; ++j)
+                    if (sp + j < splits) t[j] = ws[(int64_t)(sp + j) * mn + i];
+#pragma unroll
+                for (int j = 0; j < kUnroll - 1; ++j)
+                    if (sp + j < splits) s += t[j];
+            }
             float y = s * scale;
             if (chan) {
                 const int64_t row = i / N;

@@ -116,11 +116,11 @@ def fp8_dot_allowance(codes_a, codes_b, rows=None, group=8, fmt_a=orc.FMT_E4M3, 
 
 def fp8_mfma_config(name):
     """Whether configuration `name` sums FP8 products on the FP8 matrix cores
-    (the register-staged, direct-load and ping-pong tile kernels), the only
+    (the register-staged, direct-load, ping-pong and deep-ring tile kernels), the only
     place the allowance T applies. The streaming and decode kernels (FP32 FMA
     of exact products) and the exact mode (FP16 matrix cores) take the plain
     bound."""
-    return name.startswith(("tile_fp8", "dma_fp8", "pp_fp8"))
+    return name.startswith(("tile_fp8", "dma_fp8", "pp_fp8", "ring_fp8"))
 
 
 def allowance_for(name, codes_a, codes_b, rows=None, fmt_a=orc.FMT_E4M3, fmt_b=orc.FMT_E4M3):

@@ -146,7 +146,7 @@ def test_channel_entry_points_argument_validation():
     assert L.quantize_fp8_channel(None, 0, 8, 0, None, None, 0, None) == 0
 
 
-def test_splitk_plan_rules():
+def test_splitk_plan_rules(monkeypatch):
     plan = g.splitk_plan
     # decode shapes split over 64x64 tiles, K cut until >= 512 workgroups;
     # the FP16 M = 1 decode keeps its plain streaming kernel
@@ -154,26 +154,36 @@ def test_splitk_plan_rules():
     assert plan(g.KIND_FP8, g.OUT_E4M3, 4, 4096, 4096) == ("tile_fp8_64x64x128_w2x2", 8, 8 * 4 * 4096 * 4)
     assert plan(g.KIND_F16, g.OUT_F16, 1, 12288, 4096) == ("stream_f16_m1_c64_t512", 1, 0)
     assert plan(g.KIND_F16, g.OUT_F16, 4, 12288, 4096) == ("tile_f16_64x64x64_w2x2", 4, 4 * 4 * 12288 * 4)
-    # mid-M: 64x64 tiles, 2 x 64 tiles -> 4 ranges of 1024
+    # 4 < M <= 256: the deep-ring kernel over all of K, no workspace; its tile
+    # minimises (bm + bn) times the rounds of workgroups per compute unit
+    assert plan(g.KIND_FP8, g.OUT_E4M3, 16, 4096, 4096) == ("ring_fp8_16x16x128", 1, 0)
+    assert plan(g.KIND_FP8, g.OUT_E4M3, 65, 4096, 4096) == ("ring_fp8_32x64x128", 1, 0)
+    assert plan(g.KIND_FP8, g.OUT_F32, 129, 4096, 4096) == ("ring_fp8_64x64x128", 1, 0)
+    assert plan(g.KIND_F16, g.OUT_F16, 16, 12288, 4096) == ("ring_f16_16x64x64", 1, 0)
+    assert plan(g.KIND_F16, g.OUT_F16, 63, 12288, 4096) == ("ring_f16_64x64x64", 1, 0)
+    # a forced 64x64 tile at mid-M: 2 x 64 tiles -> 4 ranges of 1024
+    monkeypatch.setenv("LIBGEMM_CONFIG", "tile_fp8_64x64x128_w2x2")
     assert plan(g.KIND_FP8, g.OUT_E4M3, 65, 4096, 4096) == ("tile_fp8_64x64x128_w2x2", 4, 4 * 65 * 4096 * 4)
-    assert plan(g.KIND_FP8, g.OUT_F32, 16, 4096, 4096)[1] == 8
+    monkeypatch.delenv("LIBGEMM_CONFIG")
     # enough tiles, or large M: no split, no workspace
     assert plan(g.KIND_FP8, g.OUT_E4M3, 512, 4096, 4096)[1:] == (1, 0)
     assert plan(g.KIND_FP8, g.OUT_E4M3, 4096, 4096, 4096)[1:] == (1, 0)
     # K shorter than two granules: no split
-    assert plan(g.KIND_FP8, g.OUT_F32, 65, 4096, 200)[1:] == (1, 0)
+    assert plan(g.KIND_FP8, g.OUT_F32, 4, 4096, 200)[1:] == (1, 0)
     # ragged K: ranges are granule multiples and none is empty
-    name, splits, nbytes = plan(g.KIND_FP8, g.OUT_F32, 65, 4096, 300)
-    assert (name, splits, nbytes) == ("tile_fp8_64x64x128_w2x2", 2, 2 * 65 * 4096 * 4)
+    name, splits, nbytes = plan(g.KIND_FP8, g.OUT_F32, 4, 4096, 300)
+    assert (name, splits, nbytes) == ("tile_fp8_64x64x128_w2x2", 2, 2 * 4 * 4096 * 4)
 
 
 def test_splitk_plan_overrides(monkeypatch):
     monkeypatch.setenv("LIBGEMM_SPLITS", "3")
-    assert g.splitk_plan(g.KIND_FP8, g.OUT_F32, 65, 4096, 4096)[1] == 3
+    assert g.splitk_plan(g.KIND_FP8, g.OUT_F32, 4, 4096, 4096)[1] == 3
+    # the deep-ring kernel takes no split
+    assert g.splitk_plan(g.KIND_FP8, g.OUT_F32, 65, 4096, 4096) == ("ring_fp8_32x64x128", 1, 0)
     monkeypatch.setenv("LIBGEMM_SPLITS", "1000")        # clamped to K / granule
-    assert g.splitk_plan(g.KIND_FP8, g.OUT_F32, 65, 4096, 4096)[1] == 4096 // 128
+    assert g.splitk_plan(g.KIND_FP8, g.OUT_F32, 4, 4096, 4096)[1] == 4096 // 128
     monkeypatch.setenv("LIBGEMM_SPLITS", "1")
-    assert g.splitk_plan(g.KIND_FP8, g.OUT_F32, 65, 4096, 4096)[1:] == (1, 0)
+    assert g.splitk_plan(g.KIND_FP8, g.OUT_F32, 4, 4096, 4096)[1:] == (1, 0)
     monkeypatch.delenv("LIBGEMM_SPLITS")
     monkeypatch.setenv("LIBGEMM_CONFIG", "tile_fp8_128x128x128_w2x2")
     name, splits, _ = g.splitk_plan(g.KIND_FP8, g.OUT_F32, 65, 4096, 4096)
@@ -186,15 +196,15 @@ def test_splitk_argument_validation():
     L = g.lib()
     s = FAKE3 + (1 << 24)
     W = 5 << 40
-    need = 4 * 65 * 4096 * 4
-    args = (FAKE, 0, FAKE2, 0, s, s + 4, None, FAKE3, 0, 65, 4096, 4096)
+    need = 8 * 4 * 4096 * 4                 # M = 4: eight ranges of 512
+    args = (FAKE, 0, FAKE2, 0, s, s + 4, None, FAKE3, 0, 4, 4096, 4096)
     assert L.gemm_fp8_splitk(*args, W, need - 1, None) == -9          # too small
     assert L.gemm_fp8_splitk(*args, W + 4, need, None) == -9          # not 16-byte aligned
     assert L.gemm_fp8_splitk(*args, W, -1, None) == -9
     assert L.gemm_fp8_splitk(*args, FAKE3 - 16, need, None) == -8     # covers C
-    assert L.gemm_fp8_splitk(*args, FAKE + 65 * 4096 - 16, need, None) == -8   # covers the end of A
-    assert L.gemm_fp8_splitk(FAKE, 0, FAKE2, 0, s, s + 4, None, FAKE3, 2, 65, 4096, 4096, W, need, None) == -4
-    assert L.gemm_fp8_splitk(FAKE, 0, FAKE2, 7, s, s + 4, None, FAKE3, 0, 65, 4096, 4096, W, need, None) == -3
+    assert L.gemm_fp8_splitk(*args, FAKE + 4 * 4096 - 16, need, None) == -8   # covers the end of A
+    assert L.gemm_fp8_splitk(FAKE, 0, FAKE2, 0, s, s + 4, None, FAKE3, 2, 4, 4096, 4096, W, need, None) == -4
+    assert L.gemm_fp8_splitk(FAKE, 0, FAKE2, 7, s, s + 4, None, FAKE3, 0, 4, 4096, 4096, W, need, None) == -3
     assert L.gemm_f16_splitk(FAKE, FAKE2, FAKE3, 1, 4, 12288, 4096, W, 4 * 4 * 12288 * 4 - 4, None) == -9
     assert L.gemm_f16_splitk(FAKE, FAKE2, FAKE3, 2, 1, 12288, 4096, W, 1 << 30, None) == -3
     assert L.gemm_f16_splitk(FAKE, FAKE2, FAKE3, 1, 4, 12288, 4096, FAKE2 + 64, 1 << 30, None) == -8   # inside B
@@ -231,7 +241,7 @@ def test_select_config_formats():
             for (M, N, K) in [(1, 4096, 4096), (4, 4096, 4096), (16, 4096, 4096), (65, 4096, 4096),
                               (3000, 4096, 4096), (4096, 4096, 4096), (16384, 12288, 4096)]:
                 name = g.select_config_fmt(g.KIND_FP8, g.OUT_E5M2, M, N, K, fa, fb)
-                assert name.startswith(("stream_fp8", "tile_fp8", "dma_fp8", "pp_fp8")), name
+                assert name.startswith(("stream_fp8", "tile_fp8", "dma_fp8", "pp_fp8", "ring_fp8")), name
     assert g.select_config_fmt(g.KIND_FP8, g.OUT_F16, 4096, 4096, 4096, 0, 0) == \
         g.select_config(g.KIND_FP8, g.OUT_F16, 4096, 4096, 4096)
 
@@ -264,9 +274,9 @@ def test_select_config_rules():
     # decode shapes go to the streaming kernel sized for M
     assert sel(g.KIND_F16, g.OUT_F16, 1, 12288, 4096).startswith("stream_f16_m1_")
     assert sel(g.KIND_F16, g.OUT_F16, 4, 12288, 4096).startswith("stream_f16_m4_")
-    # from M = 5 the 64x64 MFMA tile reads the weight faster than streaming
-    assert sel(g.KIND_F16, g.OUT_F16, 16, 12288, 4096) == "tile_f16_64x64x64_w2x2"
-    assert sel(g.KIND_F16, g.OUT_F16, 5, 12288, 4096) == "tile_f16_64x64x64_w2x2"
+    # from M = 5 the deep-ring MFMA kernel reads the weight faster than streaming
+    assert sel(g.KIND_F16, g.OUT_F16, 16, 12288, 4096) == "ring_f16_16x64x64"
+    assert sel(g.KIND_F16, g.OUT_F16, 5, 12288, 4096) == "ring_f16_16x64x64"
     assert sel(g.KIND_FP8, g.OUT_E4M3, 1, 4096, 4096).startswith("stream_fp8_m1_")
     # 4096^2 fills the chip with 256x256 tiles (256 tiles): they run on the
     # ping-pong kernel, FP8 and FP16 alike, and so do larger grids
@@ -280,8 +290,13 @@ def test_select_config_rules():
     assert sel(g.KIND_FP8, g.OUT_E4M3, 2048, 2048, 4096).startswith("tile_fp8_128x128")
     # small problems take the smallest tile
     assert sel(g.KIND_FP8, g.OUT_F32, 1024, 1024, 1024).startswith("tile_fp8_64x64")
-    assert sel(g.KIND_F16, g.OUT_F32, 256, 256, 256).startswith("tile_f16_64x64")
-    assert sel(g.KIND_FP8, g.OUT_E4M3, 65, 4096, 4096).startswith("tile_fp8_64x64")
+    assert sel(g.KIND_F16, g.OUT_F32, 300, 256, 256).startswith("tile_f16_64x64")
+    # M <= 256: the deep-ring kernel, tile by the bytes per compute unit
+    assert sel(g.KIND_F16, g.OUT_F32, 256, 256, 256) == "ring_f16_16x16x64"
+    assert sel(g.KIND_FP8, g.OUT_E4M3, 65, 4096, 4096) == "ring_fp8_32x64x128"
+    assert sel(g.KIND_FP8, g.OUT_E4M3, 256, 4096, 4096) == "ring_fp8_64x64x128"
+    assert g.select_config_bt(g.KIND_FP8, g.OUT_E4M3, 9, 4096, 4096) == "ring_fp8_16x16x128_bt"
+    assert sel(g.KIND_FP8, g.OUT_E4M3, 16, 4096, 4096) == "ring_fp8_16x16x128"
 
 
 def test_select_config_override(monkeypatch):
@@ -290,7 +305,7 @@ def test_select_config_override(monkeypatch):
     # an override that cannot serve the request is ignored
     assert g.select_config(g.KIND_F16, g.OUT_F32, 4096, 4096, 4096) == "pp_f16_256x256x32"
     monkeypatch.setenv("LIBGEMM_CONFIG", "stream_f16_m1_c64_t1024")
-    assert g.select_config(g.KIND_F16, g.OUT_F16, 8, 100, 100) == "tile_f16_64x64x64_w2x2"
+    assert g.select_config(g.KIND_F16, g.OUT_F16, 8, 100, 100) == "ring_f16_16x16x64"
     monkeypatch.setenv("LIBGEMM_CONFIG", "stream_f16_m8_c64_t256")      # still selectable by name
     assert g.select_config(g.KIND_F16, g.OUT_F16, 8, 100, 100) == "stream_f16_m8_c64_t256"
 
@@ -327,13 +342,13 @@ def test_kmajor_entry_points_argument_validation():
 
 def test_kmajor_selector():
     """K-major B: decode shapes (M <= 8) take the dot-product decode kernels,
-    larger M the K-major tile kernels, by the tile rules of row-major B (a
-    256x256 grid already from 3/4 of the CUs)."""
+    M <= 256 the deep-ring kernel, larger M the K-major tile kernels, by the
+    tile rules of row-major B (a 256x256 grid already from 3/4 of the CUs)."""
     assert g.select_config_bt(g.KIND_F16, g.OUT_F16, 1, 12288, 4096) == "gemv_coop_f16_m1_r4_w8"
     assert g.select_config_bt(g.KIND_F16, g.OUT_F16, 2, 12288, 4096) == "gemv_bt_f16_m4_r2_u4"
     assert g.select_config_bt(g.KIND_F16, g.OUT_F16, 4, 12288, 4096) == "gemv_bt_f16_m4_r2_u4"
     assert g.select_config_bt(g.KIND_F16, g.OUT_F16, 8, 12288, 4096) == "gemv_bt_f16_m8_r4_u2"
-    assert g.select_config_bt(g.KIND_F16, g.OUT_F16, 9, 12288, 4096) == "tile_f16_64x64x64_w2x2_bt"
+    assert g.select_config_bt(g.KIND_F16, g.OUT_F16, 9, 12288, 4096) == "ring_f16_16x64x64_bt"
     assert g.select_config_bt(g.KIND_FP8, g.OUT_E4M3, 1, 4096, 4096) == "gemv_bt_fp8_m1_r4_u4"
     assert g.select_config_bt(g.KIND_FP8, g.OUT_E4M3, 3, 4096, 4096) == "gemv_coop_fp8_m4_r4_w4"
     assert g.select_config_bt(g.KIND_FP8, g.OUT_E4M3, 8, 4096, 4096) == "gemv_coop_fp8_m8_r2_w4"
@@ -341,23 +356,26 @@ def test_kmajor_selector():
     assert g.select_config_bt(g.KIND_FP8, g.OUT_E4M3, 3000, 4096, 4096) == "pp_fp8_256x256x64_bt"
     assert g.select_config_bt(g.KIND_F16, g.OUT_F16, 4096, 4096, 4096) == "pp_f16_256x256x32_bt"
     assert g.select_config_bt(g.KIND_FP8, g.OUT_F32, 1024, 1024, 1024) == "tile_fp8_64x64x128_w2x2_bt"
-    assert g.select_config_bt(g.KIND_FP8, g.OUT_F32, 65, 4096, 4096) == "tile_fp8_64x64x128_w2x2_bt"
+    assert g.select_config_bt(g.KIND_FP8, g.OUT_F32, 65, 4096, 4096) == "ring_fp8_32x64x128_bt"
+    assert g.select_config_bt(g.KIND_FP8, g.OUT_F32, 257, 4096, 4096) == "tile_fp8_64x64x128_w2x2_bt"
     # the row-major selector never returns a K-major configuration, nor the reverse
     assert not g.select_config(g.KIND_FP8, g.OUT_F32, 4096, 4096, 4096).endswith("_bt")
     assert g.select_config(g.KIND_F16, g.OUT_F16, 1, 12288, 4096).startswith("stream_")
     assert g.select_config(g.KIND_FP8, g.OUT_F32, 3000, 4096, 4096) == "pp_fp8_256x256x64"
 
 
-def test_kmajor_splitk_plan_and_validation():
-    """K-major split-K: decode shapes keep the decode kernels (no split), mid-M
-    shapes split like row-major B; workspace errors come before any launch."""
+def test_kmajor_splitk_plan_and_validation(monkeypatch):
+    """K-major split-K: decode shapes keep the decode kernels and mid-M shapes
+    the deep-ring kernel (no split); a forced 64x64 tile splits like row-major
+    B; workspace errors come before any launch."""
     assert g.splitk_plan_bt(g.KIND_FP8, g.OUT_E4M3, 1, 4096, 4096) == ("gemv_bt_fp8_m1_r4_u4", 1, 0)
     assert g.splitk_plan_bt(g.KIND_F16, g.OUT_F16, 4, 12288, 4096) == ("gemv_bt_f16_m4_r2_u4", 1, 0)
+    assert g.splitk_plan_bt(g.KIND_FP8, g.OUT_E4M3, 65, 4096, 4096) == ("ring_fp8_32x64x128_bt", 1, 0)
+    assert g.splitk_plan_bt(g.KIND_F16, g.OUT_F16, 16, 12288, 4096) == ("ring_f16_16x64x64_bt", 1, 0)
+    assert g.splitk_plan_bt(g.KIND_FP8, g.OUT_F32, 300, 4096, 4096)[1] == 1
+    monkeypatch.setenv("LIBGEMM_CONFIG", "tile_fp8_64x64x128_w2x2_bt")
     cfg, splits, nbytes = g.splitk_plan_bt(g.KIND_FP8, g.OUT_E4M3, 65, 4096, 4096)
     assert cfg == "tile_fp8_64x64x128_w2x2_bt" and splits > 1 and nbytes == splits * 65 * 4096 * 4
-    cfg, splits, nbytes = g.splitk_plan_bt(g.KIND_F16, g.OUT_F16, 16, 12288, 4096)
-    assert cfg == "tile_f16_64x64x64_w2x2_bt" and splits > 1 and nbytes == splits * 16 * 12288 * 4
-    assert g.splitk_plan_bt(g.KIND_FP8, g.OUT_F32, 300, 4096, 4096)[1] == 1
     L = g.lib()
     s = 6 << 40          # scales well away from C (C here spans MB)
     ws = 5 << 40
@@ -367,6 +385,7 @@ def test_kmajor_splitk_plan_and_validation():
     assert L.gemm_fp8_splitk_bt(FAKE, FAKE2, s, s + 4, None, FAKE3, 0, 65, 4096, 4096, ws + 4, 1 << 30, None) == -9
     assert L.gemm_fp8_splitk_bt(FAKE, FAKE2, s, s + 4, None, FAKE3, 0, 65, 4096, 4096, FAKE2, 1 << 30, None) == -8
     # gemm_f16_splitk_bt(A, Bt, C, out, M, N, K, ws, bytes, stream)
+    monkeypatch.setenv("LIBGEMM_CONFIG", "tile_f16_64x64x64_w2x2_bt")
     assert L.gemm_f16_splitk_bt(FAKE, FAKE2, FAKE3, 2, 16, 12288, 4096, ws, 1 << 30, None) == -3
     assert L.gemm_f16_splitk_bt(FAKE, FAKE2, FAKE3, 1, 16, 12288, 4096, ws, 1024, None) == -9
 

@@ -49,9 +49,11 @@ def scalar(v):
 
 
 FP8_CONFIGS = ["pp_fp8_256x256x64", "dma_fp8_256x256x64_s4", "dma_fp8_256x256x64_s5", "tile_fp8_256x256x128_w2x4",
-               "tile_fp8_128x128x128_w2x2", "tile_fp8_64x64x128_w2x2"]
+               "tile_fp8_128x128x128_w2x2", "tile_fp8_64x64x128_w2x2", "ring_fp8_16x16x128", "ring_fp8_32x32x128",
+               "ring_fp8_64x64x128"]
 F16_CONFIGS = ["pp_f16_256x256x32", "dma_f16_256x256x32_s4", "dma_f16_256x256x32_s5", "tile_f16_256x256x64_w2x4",
-               "tile_f16_128x128x64_w2x2", "tile_f16_64x64x64_w2x2"]
+               "tile_f16_128x128x64_w2x2", "tile_f16_64x64x64_w2x2", "ring_f16_16x16x64", "ring_f16_32x32x64",
+               "ring_f16_64x64x64"]
 
 # (M, N, K): full tiles; M/N edges with a K tail; an odd number of K tiles;
 # a single partial K tile; K and N not multiples of 16 bytes (unaligned rows).
@@ -102,8 +104,57 @@ def test_f16_config_parity(cfg, monkeypatch):
         check_f16(host(C), R, S, what=f"{cfg} f16 {M}x{N}x{K}")
 
 
+RING_CONFIGS = [f"ring_{k}_{bm}x{bn}x{bk}{bt}" for (k, bk) in (("fp8", 128), ("f16", 64))
+                for (bm, bn) in ((16, 16), (16, 32), (16, 64), (32, 32), (32, 64), (64, 64)) for bt in ("", "_bt")]
+# long K: the unrolled steady loop (at least 15 K tiles), then the tail with a
+# partial last tile; M and N edges; a C4 decode-like row block
+RING_SHAPES = [(70, 200, 4160), (16, 4096, 4096), (129, 320, 2000), (5, 136, 1936)]
+
+
+@pytest.mark.parametrize("cfg", RING_CONFIGS)
+def test_ring_config_long_k(cfg, monkeypatch):
+    """The deep-ring kernel over K long enough to run its unrolled main loop,
+    row-major and K-major B, FP8 (F32 and E4M3 outputs) and FP16 operands."""
+    monkeypatch.setenv("LIBGEMM_CONFIG", cfg)
+    bt = cfg.endswith("_bt")
+    for (M, N, K) in RING_SHAPES:
+        say(f"{cfg} {M}x{N}x{K}")
+        if cfg.startswith("ring_fp8"):
+            sel = g.select_config_bt if bt else g.select_config
+            assert sel(g.KIND_FP8, g.OUT_F32, M, N, K) == cfg
+            ca = wl.random_e4m3_codes((M, K), 61 * M + K)
+            cb = wl.random_e4m3_codes((K, N), 67 * N + K)
+            R, S = orc.gemm(orc.FMT_E4M3, ca, cb)
+            T = fp8_dot_allowance(ca, cb)
+            sa, sb = np.float32(0.125), np.float32(0.0625)
+            ta, tb = dev(ca), dev(np.ascontiguousarray(cb.T) if bt else cb)
+            run = g.gemm_fp8_scaled_bt if bt else g.gemm_fp8_scaled
+            C = torch.empty((M, N), dtype=torch.float32, device=DEV)
+            run(ta, tb, scalar(sa), scalar(sb), C)
+            check_f32(host(C), R, S, sa, sb, what=f"{cfg} f32 {M}x{N}x{K}", T=T)
+            s_out = orc.scale_from_amax(np.float32(np.max(np.abs(R * float(sa) * float(sb)))))
+            C = torch.empty((M, N), dtype=torch.uint8, device=DEV)
+            run(ta, tb, scalar(sa), scalar(sb), C, scalar(s_out))
+            check_e4m3(host(C), R, S, sa, sb, s_out, what=f"{cfg} e4m3 {M}x{N}x{K}", T=T)
+        else:
+            sel = g.select_config_bt if bt else g.select_config
+            assert sel(g.KIND_F16, g.OUT_F32, M, N, K) == cfg
+            a16 = wl.random_f16((M, K), 71 * M + K)
+            b16 = wl.random_f16((K, N), 73 * N + K)
+            R, S = orc.gemm(orc.FMT_F16, a16.view(np.uint16), b16.view(np.uint16))
+            ta, tb = dev(a16), dev(np.ascontiguousarray(b16.T) if bt else b16)
+            run = g.gemm_f16_bt if bt else g.gemm_f16
+            C = torch.empty((M, N), dtype=torch.float32, device=DEV)
+            run(ta, tb, C)
+            check_f32(host(C), R, S, what=f"{cfg} f32 {M}x{N}x{K}")
+            C = torch.empty((M, N), dtype=torch.float16, device=DEV)
+            run(ta, tb, C)
+            check_f16(host(C), R, S, what=f"{cfg} f16 {M}x{N}x{K}")
+
+
 @pytest.mark.parametrize("kind,cfg", [("fp8", "dma_fp8_256x256x64_s4"), ("f16", "dma_f16_256x256x32_s4"),
-                                      ("fp8", "pp_fp8_256x256x64"), ("f16", "pp_f16_256x256x32")])
+                                      ("fp8", "pp_fp8_256x256x64"), ("f16", "pp_f16_256x256x32"),
+                                      ("fp8", "ring_fp8_32x64x128"), ("f16", "ring_f16_32x64x64")])
 def test_direct_load_kernel_offset_operands(kind, cfg, monkeypatch):
     """Operands starting 16 bytes into an allocation (aligned) and 2 bytes in
     (unaligned: handed to the register-staged kernel) give the oracle's result."""

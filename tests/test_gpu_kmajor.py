@@ -290,9 +290,9 @@ def test_gemm_fp8_bt_4096_against_oracle_and_deterministic():
 # ----------------------------------------- every K-major configuration forced
 
 FP8_BT_CONFIGS = ["pp_fp8_256x256x64_bt", "dma_fp8_256x256x64_s4_bt", "tile_fp8_256x256x128_w2x4_bt", "tile_fp8_128x128x128_w2x2_bt",
-                  "tile_fp8_64x64x128_w2x2_bt"]
+                  "tile_fp8_64x64x128_w2x2_bt", "ring_fp8_16x16x128_bt", "ring_fp8_32x32x128_bt", "ring_fp8_64x64x128_bt"]
 F16_BT_CONFIGS = ["pp_f16_256x256x32_bt", "dma_f16_256x256x32_s4_bt", "tile_f16_256x256x64_w2x4_bt", "tile_f16_128x128x64_w2x2_bt",
-                  "tile_f16_64x64x64_w2x2_bt"]
+                  "tile_f16_64x64x64_w2x2_bt", "ring_f16_16x16x64_bt", "ring_f16_32x32x64_bt", "ring_f16_64x64x64_bt"]
 # full tiles; M/N edges with a K tail; odd K tile counts; a single partial K
 # tile; K not a multiple of 16 bytes (element loads / the register-staged kernel)
 FP8_BT_SHAPES = [(256, 256, 256), (300, 272, 80), (513, 784, 192), (100, 32, 48), (257, 520, 1088), (130, 200, 100)]
@@ -332,25 +332,29 @@ def test_f16_bt_config_parity(cfg, monkeypatch):
         check_f16(run_f16_bt(a16, b16, g.OUT_F16), R, S, what=f"{cfg} f16 {M}x{N}x{K}")
 
 
-@pytest.mark.parametrize("kind,family", [("fp8", "dma"), ("f16", "dma"), ("fp8", "pp"), ("f16", "pp")])
+@pytest.mark.parametrize("kind,family", [("fp8", "dma"), ("f16", "dma"), ("fp8", "pp"), ("f16", "pp"), ("fp8", "ring"),
+                                         ("f16", "ring")])
 def test_dma_bt_matches_row_major_dma_bitwise(kind, family, monkeypatch):
-    """The direct-load and ping-pong kernels with K-major B and with row-major
-    B feed the same operand values in the same k order to the same MFMAs."""
-    say(f"{family} {kind} K-major vs row-major, 1024 x 768 x 512")
-    M, N, K = 1024, 768, 512
+    """The direct-load, ping-pong and deep-ring kernels with K-major B and with
+    row-major B feed the same operand values in the same k order to the same
+    MFMAs."""
+    M, N, K = (1024, 768, 512) if family != "ring" else (200, 768, 2560)
+    say(f"{family} {kind} K-major vs row-major, {M} x {N} x {K}")
     if kind == "fp8":
         a = dev(wl.random_e4m3_codes((M, K), 5))
         b = dev(wl.random_e4m3_codes((K, N), 6))
         s = scalar(0.25)
         run = lambda bb, c, bt: (g.gemm_fp8_scaled_bt if bt else g.gemm_fp8_scaled)(a, bb, s, s, c)  # noqa: E731
-        names = (("dma_fp8_256x256x64_s4", "dma_fp8_256x256x64_s4_bt") if family == "dma"
-                 else ("pp_fp8_256x256x64", "pp_fp8_256x256x64_bt"))
+        names = {"dma": ("dma_fp8_256x256x64_s4", "dma_fp8_256x256x64_s4_bt"),
+                 "pp": ("pp_fp8_256x256x64", "pp_fp8_256x256x64_bt"),
+                 "ring": ("ring_fp8_64x64x128", "ring_fp8_64x64x128_bt")}[family]
     else:
         a = dev(wl.random_f16((M, K), 5))
         b = dev(wl.random_f16((K, N), 6))
         run = lambda bb, c, bt: (g.gemm_f16_bt if bt else g.gemm_f16)(a, bb, c)  # noqa: E731
-        names = (("dma_f16_256x256x32_s4", "dma_f16_256x256x32_s4_bt") if family == "dma"
-                 else ("pp_f16_256x256x32", "pp_f16_256x256x32_bt"))
+        names = {"dma": ("dma_f16_256x256x32_s4", "dma_f16_256x256x32_s4_bt"),
+                 "pp": ("pp_f16_256x256x32", "pp_f16_256x256x32_bt"),
+                 "ring": ("ring_f16_64x64x64", "ring_f16_64x64x64_bt")}[family]
     c1 = torch.empty(M, N, device=DEV, dtype=torch.float32)
     c2 = torch.empty_like(c1)
     monkeypatch.setenv("LIBGEMM_CONFIG", names[0])
@@ -417,7 +421,8 @@ def test_fp8_splitk_bt_C4_shapes(M):
     say(f"gemm_fp8_splitk_bt M={M}")
     qa, sa, qbt, sb, oqa, osa, oqb, osb = fp8_chain_bt(xa, xb)
     cfg, splits, nbytes = g.splitk_plan_bt(g.KIND_FP8, g.OUT_E4M3, M, 4096, 4096)
-    assert splits > 1, (cfg, splits)
+    assert cfg.startswith("ring_fp8") and splits == 1, (cfg, splits)   # M <= 256: the deep-ring kernel
+    nbytes = max(nbytes, 16)
     R, S = orc.gemm(orc.FMT_E4M3, oqa, oqb)
     s_out = orc.scale_from_amax(np.float32(np.max(np.abs(R * float(osa) * float(osb)))))
     ws = torch.empty(nbytes, dtype=torch.uint8, device=DEV)
@@ -446,7 +451,7 @@ def test_f16_splitk_bt_decode_weight(M):
     a16 = wl.random_normal_f32((M, 4096), 950 + M).astype(np.float16)
     b16 = (wl.random_normal_f32((4096, 12288), 951) * np.float32(0.02)).astype(np.float16)
     cfg, splits, nbytes = g.splitk_plan_bt(g.KIND_F16, g.OUT_F16, M, 12288, 4096)
-    assert splits > 1, (cfg, splits)
+    assert cfg.startswith("ring_f16") and splits == 1, (cfg, splits)   # M <= 256: the deep-ring kernel
     R, S = orc.gemm(orc.FMT_F16, a16.view(np.uint16), b16.view(np.uint16))
     ta, tbt = dev(a16), dev(b16.T)
     for out, dt, chk in ((g.OUT_F16, torch.float16, check_f16), (g.OUT_F32, torch.float32, check_f32)):
@@ -475,7 +480,7 @@ def test_tile_bt_narrow_n(M, N, K):
     say(f"tile bt narrow N {M}x{N}x{K}")
     a16 = wl.random_f16((M, K), 3 * M + N)
     b16 = wl.random_f16((K, N), 5 * N + K)
-    assert g.select_config_bt(g.KIND_F16, g.OUT_F32, M, N, K).startswith("tile_")
+    assert g.select_config_bt(g.KIND_F16, g.OUT_F32, M, N, K).startswith(("tile_", "ring_"))
     R, S = orc.gemm(orc.FMT_F16, a16.view(np.uint16), b16.view(np.uint16))
     check_f32(run_f16_bt(a16, b16, g.OUT_F32), R, S, what=f"f16 bt {M}x{N}x{K}")
     ca = wl.random_e4m3_codes((M, K), 7 * M + N)
@@ -493,7 +498,8 @@ PAIRS = [(g.FMT_E4M3, g.FMT_E4M3), (g.FMT_E4M3, g.FMT_E5M2), (g.FMT_E5M2, g.FMT_
 # M <= 4 and M <= 8, by the selector) and each K-major tile configuration
 FMT_SHAPES = [(None, 1, 1000, 512), (None, 4, 520, 640), (None, 8, 300, 256),
               ("tile_fp8_64x64x128_w2x2_bt", 100, 200, 256), ("tile_fp8_128x128x128_w2x2_bt", 300, 272, 384),
-              ("tile_fp8_256x256x128_w2x4_bt", 257, 512, 320), ("pp_fp8_256x256x64_bt", 300, 272, 192)]
+              ("tile_fp8_256x256x128_w2x4_bt", 257, 512, 320), ("pp_fp8_256x256x64_bt", 300, 272, 192),
+              ("ring_fp8_32x64x128_bt", 70, 200, 2048)]
 
 
 def fp8_codes(fmt, shape, seed):

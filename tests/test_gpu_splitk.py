@@ -54,9 +54,10 @@ def workspace_for(kind, out, M, N, K, fa=0, fb=0):
 # 64 and 128 tiles; K not a multiple of the range length; N not a multiple
 # of 4 (scalar reduce); K shorter than the ranges need (fewer ranges).
 FP8_CASES = [(None, 16, 1, 4096, 4096), ("stream_fp8_m4_c128_t256", 5, 3, 1000, 1500),
-             ("stream_fp8_m1_c64_t1024", 2, 1, 777, 4100), (None, 4, 65, 1000, 4096),
+             ("stream_fp8_m1_c64_t1024", 2, 1, 777, 4100), ("tile_fp8_64x64x128_w2x2", 4, 65, 1000, 4096),
              ("tile_fp8_64x64x128_w2x2", 3, 100, 203, 1000), ("tile_fp8_128x128x128_w2x2", 7, 129, 384, 2000),
-             ("tile_fp8_256x256x128_w2x4", 2, 200, 300, 700), (None, 8, 16, 520, 640)]
+             ("tile_fp8_256x256x128_w2x4", 2, 200, 300, 700), ("tile_fp8_64x64x128_w2x2", 8, 16, 520, 640),
+             (None, 8, 4, 520, 640)]
 
 
 @pytest.mark.parametrize("cfg,splits,M,N,K", FP8_CASES)
@@ -100,7 +101,8 @@ def test_fp8_splitk_m_sweep_full_size(M):
     N = K = 4096
     name, splits, ws = workspace_for(g.KIND_FP8, g.OUT_E4M3, M, N, K)
     say(f"fp8 split-K sweep M={M}: {name} splits={splits}")
-    assert splits > 1
+    # M <= 4: split 64x64 tiles; 4 < M <= 256: the deep-ring kernel over all of K
+    assert (splits > 1) if M <= 4 else (splits == 1 and name.startswith("ring_fp8")), (name, splits)
     xa = wl.normal_with_outliers_f32((M, K), 2000 + M)
     xb = wl.normal_with_outliers_f32((K, N), 2001)
     sa = orc.scale_from_amax(orc.amax(xa))
@@ -125,7 +127,8 @@ def test_f16_splitk_decode(M):
     N, K = 12288, 4096
     name, splits, ws = workspace_for(g.KIND_F16, g.OUT_F16, M, N, K)
     say(f"f16 split-K decode M={M}: {name} splits={splits}")
-    assert (splits == 1) if M == 1 else (splits > 1)   # M = 1 keeps the plain streaming kernel
+    # M = 1 keeps the plain streaming kernel, M = 16 runs the deep-ring kernel
+    assert (splits == 1) if M in (1, 16) else (splits > 1)
     a16 = wl.random_normal_f32((M, K), 31).astype(np.float16)
     b16 = (wl.random_normal_f32((K, N), 32) * np.float32(0.02)).astype(np.float16)
     R, S = orc.gemm(orc.FMT_F16, a16.view(np.uint16), b16.view(np.uint16))
@@ -156,7 +159,8 @@ def test_f16_splitk_forced(cfg, splits, M, N, K, monkeypatch):
     check_f16(host(C16), R, S, what=f"{cfg} f16")
 
 
-def test_splitk_workspace_rules():
+def test_splitk_workspace_rules(monkeypatch):
+    monkeypatch.setenv("LIBGEMM_CONFIG", "tile_fp8_64x64x128_w2x2")   # a configuration that splits K
     M, N, K = 65, 4096, 4096
     ca, cb = wl.random_e4m3_codes((M, K), 5), wl.random_e4m3_codes((K, N), 6)
     R, S = orc.gemm(orc.FMT_E4M3, ca, cb)
