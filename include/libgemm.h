@@ -261,6 +261,26 @@ int gemm_fp8_splitk(const uint8_t* A, int fmt_a, const uint8_t* B, int fmt_b,
                     int64_t M, int64_t N, int64_t K, void* workspace, int64_t workspace_bytes,
                     hipStream_t stream);
 
+/*
+ * gemm_fp8_splitk_noalloc — gemm_fp8_splitk for callers that cannot allocate
+ * device memory (code under HIP graph capture, serving loops, harnesses that
+ * forbid hipMalloc): the FP32 partial sums go to a 16 MiB array that the
+ * library holds on every GPU it runs on (the first call on a device looks up
+ * that device's copy), so no workspace argument. A plan that needs more than
+ * gemm_fp8_splitk_noalloc_max_bytes() bytes (splits * M * N * 4) returns
+ * GEMM_ERR_WORKSPACE before any launch; a plan that does not split is the
+ * plain call. The call allocates nothing. All calls on one GPU share the
+ * array: calls that overlap in time on one GPU (other streams, other host
+ * threads) race and must be serialised by the caller. Results, other errors
+ * and determinism as gemm_fp8_splitk.
+ */
+int gemm_fp8_splitk_noalloc(const uint8_t* A, int fmt_a, const uint8_t* B, int fmt_b,
+                            const float* sA, const float* sB, const float* sOut, void* C,
+                            int out_dtype, int64_t M, int64_t N, int64_t K, hipStream_t stream);
+
+/* gemm_fp8_splitk_noalloc_max_bytes — the size of that array in bytes. */
+int64_t gemm_fp8_splitk_noalloc_max_bytes(void);
+
 /* gemm_f16_splitk — gemm_f16 that may split K, with the workspace rules of
  * gemm_fp8_splitk (the M = 1 decode of P1 §4.1 is such a shape). */
 int gemm_f16_splitk(const void* A, const void* B, void* C, int out_dtype,

@@ -17,6 +17,7 @@ Functions keep the C names:
     quantize_fp8_channel(x, scale, axis, fmt, q=None, stream=None) -> q
     amax_scale_channel_f32(x, axis, fmt, pow2, amax=None, scale=None, stream=None) -> (amax, scale)
     gemm_fp8_splitk(A, fmt_a, B, fmt_b, sA, sB, C, sOut=None, workspace=None, stream=None, out_fmt=None)
+    gemm_fp8_splitk_noalloc(A, fmt_a, B, fmt_b, sA, sB, C, sOut=None, stream=None, out_fmt=None)
     gemm_f16_splitk(A, B, C, workspace=None, stream=None)
     splitk_plan(kind, out_dtype, M, N, K, fmt_a=0, fmt_b=0) -> (config, splits, workspace_bytes)
     gemm_f16_guarded(A, B, C, scale=None, workspace=None, stream=None) -> (C, scale)
@@ -114,6 +115,10 @@ def lib() -> ctypes.CDLL:
     L.quantize_fp8_channel.argtypes = [vp, i64, i64, i32, vp, vp, i32, vp]
     L.gemm_fp8_splitk.restype = i32
     L.gemm_fp8_splitk.argtypes = [vp, i32, vp, i32, vp, vp, vp, vp, i32, i64, i64, i64, vp, i64, vp]
+    L.gemm_fp8_splitk_noalloc.restype = i32
+    L.gemm_fp8_splitk_noalloc.argtypes = [vp, i32, vp, i32, vp, vp, vp, vp, i32, i64, i64, i64, vp]
+    L.gemm_fp8_splitk_noalloc_max_bytes.restype = i64
+    L.gemm_fp8_splitk_noalloc_max_bytes.argtypes = []
     L.gemm_f16_splitk.restype = i32
     L.gemm_f16_splitk.argtypes = [vp, vp, vp, i32, i64, i64, i64, vp, i64, vp]
     L.gemm_splitk_plan.restype = i32
@@ -453,6 +458,23 @@ def gemm_fp8_splitk(A, fmt_a, B, fmt_b, sA, sB, C, sOut=None, workspace=None, st
     _check(lib().gemm_fp8_splitk(_ptr(A), int(fmt_a), _ptr(B), int(fmt_b), _ptr(sA), _ptr(sB), _ptr(sOut), _ptr(Cv),
                                  out, M, N, K, ws, nbytes, _stream_handle(stream)), "gemm_fp8_splitk")
     return C
+
+
+def gemm_fp8_splitk_noalloc(A, fmt_a, B, fmt_b, sA, sB, C, sOut=None, stream=None, out_fmt=None):
+    """gemm_fp8_splitk with the partial sums in the library's own per-GPU
+    array (no workspace, nothing allocated); calls that overlap on one GPU
+    race."""
+    A, B = _u8(A, fmt_a), _u8(B, fmt_b)
+    out = _out_dtype(C, out_fmt)
+    Cv = _u8(C) if out in (OUT_E4M3, OUT_E5M2) else C
+    M, N, K = _dims(A, B, Cv)
+    _check(lib().gemm_fp8_splitk_noalloc(_ptr(A), int(fmt_a), _ptr(B), int(fmt_b), _ptr(sA), _ptr(sB), _ptr(sOut),
+                                         _ptr(Cv), out, M, N, K, _stream_handle(stream)), "gemm_fp8_splitk_noalloc")
+    return C
+
+
+def gemm_fp8_splitk_noalloc_max_bytes() -> int:
+    return int(lib().gemm_fp8_splitk_noalloc_max_bytes())
 
 
 def gemm_f16_splitk(A, B, C, workspace=None, stream=None):
