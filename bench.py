@@ -12,9 +12,12 @@ B is row-major B[K,N] (the calls' contract layout) unless --b-layout kmajor.
 
 value = 2*4096^3 / (the FP8 job's time inside the timed steps), in TFLOPS:
 the throughput of the whole FP8 job, quantization included. HIP events on the
-launch stream split every timed step into its parts; `roofline` is the FP8
-GEMM kernel's part against the FP8 dense peak, `roofline_f16` the FP16 GEMM's
-against the FP16 peak, `roofline_decode` the decode's against HBM.
+launch stream split every timed step into its parts (`in_step`). `roofline`
+is the FP8 GEMM kernel against the FP8 dense peak, `roofline_f16` the FP16
+GEMM against the FP16 peak, `roofline_decode` the decode against HBM, each
+timed as the mean per launch of back-to-back launches between two HIP events
+on the launch stream (the figure a kernel-trace profile of the same command
+reports as that kernel's average duration).
 
 The same run times every configuration of the workload list on its own
 (`rows`): for each, R back-to-back calls each bracketed by HIP events on the
@@ -57,6 +60,9 @@ def parse():
     p.add_argument("--cpu-seconds", type=float, default=15.0, help="target oracle sample time")
     p.add_argument("--rows-reps", type=int, default=100, help="timed calls per row")
     p.add_argument("--no-rows", action="store_true", help="time the step only")
+    p.add_argument("--no-clock", action="store_true", help="skip the engine-clock sample under load (amd-smi)")
+    p.add_argument("--kernel-reps", type=int, default=30,
+                   help="back-to-back launches timed per roofline kernel")
     p.add_argument("--b-layout", choices=("rowmajor", "kmajor"), default="rowmajor",
                    help="layout of B in the timed step: rowmajor (B[K,N], the contract layout) or kmajor "
                         "(Bt[N,K], a linear layer's weight layout)")
@@ -304,40 +310,69 @@ def main():
         "decode_gbs": dec_bytes / ms_dec / 1e6,
         "what": "HIP events on the launch stream around each part of every timed step (mean over the steps)"}
 
+    # each roofline kernel on its own: R back-to-back launches on the launch
+    # stream between two HIP events (per-launch duration, launch gaps
+    # included; the step's own events also hold the dependency on the
+    # previous part)
+    def per_launch_us(fn, reps):
+        for _ in range(3):
+            fn()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        torch.cuda.synchronize()
+        e0.record()
+        for _ in range(reps):
+            fn()
+        e1.record()
+        e1.synchronize()
+        return e0.elapsed_time(e1) * 1e3 / reps
+
+    log("timing roofline kernels back to back")
+    us_gemm8 = per_launch_us(lambda: gemm8(qa, qb, scale8[0:1], scale8[1:2], c8, s_out), args.kernel_reps)
+    us_gemm16 = per_launch_us(lambda: gemm16(ha, hb, c16), args.kernel_reps)
+
+    def dec_call():
+        gemm16(da, db_copies[rot[0] % len(db_copies)], cd)
+        rot[0] += 1
+    us_dec = per_launch_us(dec_call, args.kernel_reps)
+
     rows = {}
     if not args.no_rows:
         log("timing rows")
         rows = time_rows(torch, np, g, wl, to, args.rows_reps)
 
     # engine clock and power while the FP8 GEMM runs back to back (~2 s queued)
-    log("clock under load")
-    n_launch = int(2.0e6 / max(ms_gemm8 * 1e3, 1.0))
-    sa8, sb8 = scale8[0:1], scale8[1:2]
-    torch.cuda.synchronize()
-    for _ in range(n_launch):
-        gemm8(qa, qb, sa8, sb8, c8, s_out)
-    time.sleep(0.2)
-    clock = [sample_clock(), sample_clock()]
-    torch.cuda.synchronize()
+    clock = []
+    if not args.no_clock:
+        log("clock under load")
+        n_launch = int(2.0e6 / max(ms_gemm8 * 1e3, 1.0))
+        sa8, sb8 = scale8[0:1], scale8[1:2]
+        torch.cuda.synchronize()
+        for _ in range(n_launch):
+            gemm8(qa, qb, sa8, sb8, c8, s_out)
+        time.sleep(0.2)
+        clock = [sample_clock(), sample_clock()]
+        torch.cuda.synchronize()
 
     def roof(bound, kernel, us, work, peak, unit, traffic=None, algo=None):
         achieved = work / us / 1e6 if unit == "TFLOP/s" else work / us / 1e3
         r = {"bound": bound, "kernel": kernel, "kernel_us": us, "achieved": achieved, "peak": peak, "unit": unit,
-             "frac": achieved / peak, "traffic": traffic}
+             "frac": achieved / peak, "traffic": traffic,
+             "timing": f"mean per launch over {args.kernel_reps} back-to-back launches between two HIP events "
+                       "on the launch stream, after the timed steps"}
         if algo is not None:
             r["algorithmic_bytes"] = algo
         return r
 
     rec8 = traffic_record(cfg8)
-    roofline = roof("mfma", f"FP8 GEMM 4096^3 E4M3 out ({cfg8})", ms_gemm8 * 1e3, flops8, PEAK_FP8_TFLOPS, "TFLOP/s",
+    roofline = roof("mfma", f"FP8 GEMM 4096^3 E4M3 out ({cfg8})", us_gemm8, flops8, PEAK_FP8_TFLOPS, "TFLOP/s",
                     None if rec8 is None else rec8["hbm_bytes"], float(w8.M * w8.K + w8.K * w8.N + w8.M * w8.N))
     roofline["traffic_unit"] = "HBM bytes per launch (FETCH_SIZE + WRITE_SIZE, scaled by a copy kernel's counters)"
     rec16 = traffic_record(cfg16)
-    roofline_f16 = roof("mfma", f"FP16 GEMM 4096^3 ({cfg16})", ms_gemm16 * 1e3, flops16, PEAK_F16_TFLOPS, "TFLOP/s",
+    roofline_f16 = roof("mfma", f"FP16 GEMM 4096^3 ({cfg16})", us_gemm16, flops16, PEAK_F16_TFLOPS, "TFLOP/s",
                         None if rec16 is None else rec16["hbm_bytes"], float(2 * (3 * 4096 * 4096)))
     recd = traffic_record(cfgd)
     roofline_dec = roof("hbm", f"FP16 decode 1x4096x12288 ({cfgd}), B rotated over {len(db_copies)} copies",
-                        ms_dec * 1e3, dec_bytes, PEAK_HBM_GBS, "GB/s",
+                        us_dec, dec_bytes, PEAK_HBM_GBS, "GB/s",
                         None if recd is None else recd["hbm_bytes"], dec_bytes)
 
     cpu = None

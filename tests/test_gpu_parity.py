@@ -284,11 +284,26 @@ def test_fp8_C4_fp8_output(w):
     rows = None if w.M <= 129 else sample_rows(w.M)
     R, S = orc.gemm(orc.FMT_E4M3, oqa, oqb, rows=rows)
     V = R * float(osa) * float(osb)
-    s_out = orc.scale_from_amax(np.float32(np.max(np.abs(V))))  # over the oracle-computed rows
-    got = run_fp8(qa, qb, sa, sb, g.OUT_E4M3, s_out)
-    if rows is not None:
-        got = got[rows]
+    if rows is None:
+        s_out = orc.scale_from_amax(np.float32(np.max(np.abs(V))))  # amax(C_ref) / 448
+    else:
+        # the oracle covers sampled rows only: sOut from the amax of the whole
+        # FP32-output product (within the F32 bound of amax(C_ref))
+        c32 = run_fp8(qa, qb, sa, sb, g.OUT_F32)
+        s_out = orc.scale_from_amax(np.float32(np.max(np.abs(c32))))
+    full = run_fp8(qa, qb, sa, sb, g.OUT_E4M3, s_out)
+    got = full if rows is None else full[rows]
     check_e4m3(got, R, S, osa, osb, s_out, what=w.name)
+    if rows is not None:
+        # every element: a finite code (no 0x7F / 0xFF), saturated to +-448
+        # only where |C_f32| / sOut rounds to 448 or above, and saturated
+        # wherever it is beyond 448
+        mag = full & 0x7F
+        assert not np.any(mag == 0x7F), f"{w.name}: NaN codes"
+        ratio = np.abs(c32.astype(np.float64)) / float(s_out)
+        sat = mag == 0x7E
+        assert np.all(ratio[sat] >= 432.0 * (1 - 1e-3)), f"{w.name}: saturated below 432"
+        assert np.all(sat[ratio > 448.0 * (1 + 1e-3)]), f"{w.name}: not saturated above 448"
 
 
 def test_fp8_C5_large_f16out_sampled():
