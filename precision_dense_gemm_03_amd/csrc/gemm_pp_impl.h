@@ -30,7 +30,9 @@
 // n), loaded three tiles ahead (the double buffering of the FP8 guide §2.3,
 // deepened as the HGEMM article §3.2/§3.3 discusses). Every LDS stage is its
 // own LDS object, so the compiler can tell the in-flight direct loads from the
-// operand reads of other stages and inserts no waits of its own.
+// 16-byte operand reads of other stages and inserts no waits of its own for
+// them; the transpose reads of row-major B are asm groups (device_common.h),
+// since before a transpose-read builtin it would wait for every load in flight.
 //
 // LDS layouts are bank-conflict free for the 16-lane passes of 16-byte reads
 // (the DeepGEMM deep-dive §3.2 argues for a bank-aware layout; here it is an
