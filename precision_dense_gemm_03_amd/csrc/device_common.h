@@ -207,6 +207,34 @@ __device__ __forceinline__ void lds_b128_x4(v4i (&t)[4], uint32_t a0, uint32_t a
         : "memory");
 }
 
+// Mixed groups: two 16-byte reads and four 8-bit transpose reads, or one
+// 16-byte read and two 16-bit transpose reads, with one wait.
+__device__ __forceinline__ void lds_b128x2_tr8x4(v4i (&a)[2], v2i (&t)[4], uint32_t a0, uint32_t a1, uint32_t t0,
+                                                 uint32_t t1, uint32_t t2, uint32_t t3) {
+    asm volatile(
+        "ds_read_b128 %0, %6\n\t"
+        "ds_read_b128 %1, %7\n\t"
+        "ds_read_b64_tr_b8 %2, %8\n\t"
+        "ds_read_b64_tr_b8 %3, %9\n\t"
+        "ds_read_b64_tr_b8 %4, %10\n\t"
+        "ds_read_b64_tr_b8 %5, %11\n\t"
+        "s_waitcnt lgkmcnt(0)"
+        : "=&v"(a[0]), "=&v"(a[1]), "=&v"(t[0]), "=&v"(t[1]), "=&v"(t[2]), "=&v"(t[3])
+        : "v"(a0), "v"(a1), "v"(t0), "v"(t1), "v"(t2), "v"(t3)
+        : "memory");
+}
+
+__device__ __forceinline__ void lds_b128x1_tr16x2(v4i& a, v4s (&t)[2], uint32_t a0, uint32_t t0, uint32_t t1) {
+    asm volatile(
+        "ds_read_b128 %0, %3\n\t"
+        "ds_read_b64_tr_b16 %1, %4\n\t"
+        "ds_read_b64_tr_b16 %2, %5\n\t"
+        "s_waitcnt lgkmcnt(0)"
+        : "=&v"(a), "=&v"(t[0]), "=&v"(t[1])
+        : "v"(a0), "v"(t0), "v"(t1)
+        : "memory");
+}
+
 __device__ __forceinline__ uint32_t lds_addr(const LDS_AS void* p) { return (uint32_t)(uintptr_t)p; }
 
 }  // namespace libgemm

@@ -258,26 +258,21 @@ __global__ __launch_bounds__(256) void gemm_ring_kernel(const uint8_t* __restric
         if constexpr (ES == 1) return __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
         else return __builtin_bit_cast(v8h, lo);
     };
-    // Row-major B, column block tn of this wave (16 columns), k-step u.
-    auto rd_b_rm = [&](const LDS_AS uint8_t* sb, int tn, int u) __attribute__((always_inline)) -> Op {
+    // Row-major B, column block tn of this wave (16 columns), k-step u: the
+    // LDS addresses of its transpose reads (4 FP8, 2 FP16) and the operand
+    // they form.
+    auto b_rm_addrs = [&](const LDS_AS uint8_t* sb, int tn, int u, uint32_t (&ad)[4]) __attribute__((always_inline)) {
         const int nb = 16 * (T::TN * wc + tn);           // first column of the block (within the tile)
         if constexpr (ES == 1) {
             // read q: lane j16 addresses k-row 32 g + 8 q + j16 / 2, bytes 8 (j16 % 2) of column chunk nb / 16
-            uint32_t ad[4];
 #pragma unroll
             for (int q = 0; q < 4; ++q) {
                 const int k = 32 * g + 8 * q + (j16 >> 1);
                 const int slot = (nb >> 4) ^ swz_b<1, T::CPR>(k);
                 ad[q] = lds_addr(sb + k * T::BNB + slot * 16 + 8 * (j16 & 1));
             }
-            v2i t[4];
-            lds_tr8_x4(t, ad[0], ad[1], ad[2], ad[3]);
-            const v4i t01 = __builtin_shufflevector(t[0], t[1], 0, 1, 2, 3);
-            const v4i t23 = __builtin_shufflevector(t[2], t[3], 0, 1, 2, 3);
-            return __builtin_shufflevector(t01, t23, 0, 1, 2, 3, 4, 5, 6, 7);
         } else {
             // read q: lane j16 addresses k-row 32 u + 8 g + 4 q + j16 / 4, columns nb + 4 (j16 % 4) .. + 3
-            uint32_t ad[2];
 #pragma unroll
             for (int q = 0; q < 2; ++q) {
                 const int k = 32 * u + 8 * g + 4 * q + (j16 >> 2);
@@ -285,10 +280,16 @@ __global__ __launch_bounds__(256) void gemm_ring_kernel(const uint8_t* __restric
                 const int slot = (cb >> 4) ^ swz_b<2, T::CPR>(k);
                 ad[q] = lds_addr(sb + k * T::BNB + slot * 16 + (cb & 15));
             }
-            v4s t[2];
-            lds_tr16_x2(t, ad[0], ad[1]);
-            return __builtin_bit_cast(v8h, __builtin_shufflevector(t[0], t[1], 0, 1, 2, 3, 4, 5, 6, 7));
+            ad[2] = ad[3] = 0u;
         }
+    };
+    auto op_tr8 = [](const v2i (&t)[4]) __attribute__((always_inline)) -> v8i {
+        const v4i t01 = __builtin_shufflevector(t[0], t[1], 0, 1, 2, 3);
+        const v4i t23 = __builtin_shufflevector(t[2], t[3], 0, 1, 2, 3);
+        return __builtin_shufflevector(t01, t23, 0, 1, 2, 3, 4, 5, 6, 7);
+    };
+    auto op_tr16 = [](const v4s (&t)[2]) __attribute__((always_inline)) -> v8h {
+        return __builtin_bit_cast(v8h, __builtin_shufflevector(t[0], t[1], 0, 1, 2, 3, 4, 5, 6, 7));
     };
 
     v4f acc[T::TN];
@@ -338,18 +339,36 @@ __global__ __launch_bounds__(256) void gemm_ring_kernel(const uint8_t* __restric
                     acc[tn] = Op16<ES>::template mma<FB, FA>(b, a, acc[tn]);
                 }
             } else {
-                if constexpr (ES == 1) {
-                    v4i r[2];
-                    lds_b128_x2(r, row_lo(arow, asw, u), row_hi(arow, asw));
-                    a = as_op2(r[0], r[1]);
-                } else {
-                    v4i r;
-                    lds_b128_x1(r, row_lo(arow, asw, u));
-                    a = as_op2(r, r);
-                }
+                // A's operand and the first column block's transpose reads in
+                // one group, then one group per further column block
 #pragma unroll
-                for (int tn = 0; tn < T::TN; ++tn)
-                    acc[tn] = Op16<ES>::template mma<FB, FA>(rd_b_rm(base + T::A_BYTES, tn, u), a, acc[tn]);
+                for (int tn = 0; tn < T::TN; ++tn) {
+                    uint32_t ad[4];
+                    b_rm_addrs(base + T::A_BYTES, tn, u, ad);
+                    Op b;
+                    if constexpr (ES == 1) {
+                        v2i t[4];
+                        if (tn == 0) {
+                            v4i r[2];
+                            lds_b128x2_tr8x4(r, t, row_lo(arow, asw, u), row_hi(arow, asw), ad[0], ad[1], ad[2], ad[3]);
+                            a = as_op2(r[0], r[1]);
+                        } else {
+                            lds_tr8_x4(t, ad[0], ad[1], ad[2], ad[3]);
+                        }
+                        b = op_tr8(t);
+                    } else {
+                        v4s t[2];
+                        if (tn == 0) {
+                            v4i r;
+                            lds_b128x1_tr16x2(r, t, row_lo(arow, asw, u), ad[0], ad[1]);
+                            a = as_op2(r, r);
+                        } else {
+                            lds_tr16_x2(t, ad[0], ad[1]);
+                        }
+                        b = op_tr16(t);
+                    }
+                    acc[tn] = Op16<ES>::template mma<FB, FA>(b, a, acc[tn]);
+                }
             }
         }
     };
