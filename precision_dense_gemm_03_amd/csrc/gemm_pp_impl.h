@@ -322,6 +322,13 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
         if (steady || nt < nk_full) {
             issue_full(nt, nst);
             __builtin_amdgcn_s_waitcnt(waitcnt_imm(T::LOADS * (T::S - 2), 0));
+        } else if (nk == nk_full && t + 1 < nk) {
+            // the last tiles, all full: wait for tile t+1 only; min(S-2,
+            // nk-2-t) newer tiles may still be in flight
+            static_assert(T::S == 4, "the tail waits below are written for a 4-stage ring");
+            if (nk - 2 - t >= 2) __builtin_amdgcn_s_waitcnt(waitcnt_imm(2 * T::LOADS, 0));
+            else if (nk - 2 - t == 1) __builtin_amdgcn_s_waitcnt(waitcnt_imm(T::LOADS, 0));
+            else __builtin_amdgcn_s_waitcnt(waitcnt_imm(0, 0));
         } else {
             if (nt < nk) issue_partial(nt, nst);
             __builtin_amdgcn_s_waitcnt(0);
