@@ -331,6 +331,10 @@ const GemmConfig* gemv_kmajor_configs(int* count) {
         {"gemv_coop_f16_m4_r2_w8", KIND_F16, 3, 4, 2, 8, launch_gemv_kmajor_coop<2, 4, 2, 8>, 0, 0, 1},
         {"gemv_bt_f16_m8_r4_u2", KIND_F16, 3, 8, 16, 2, launch_gemv_kmajor<2, 8, 4, 2>, 0, 0, 1},
         {"gemv_bt_f16_m8_r2_u2", KIND_F16, 3, 8, 8, 2, launch_gemv_kmajor<2, 8, 2, 2>, 0, 0, 1},
+        // E4M3 M = 1, N = K = 4096, rotated cold weights: one row per wave
+        // (1024 workgroups) 11.05 us, two 11.15, four 12.12
+        {"gemv_bt_fp8_m1_r1_u4", KIND_FP8, 3, 1, 4, 4, launch_gemv_kmajor_fp8<1, 1, 4>, kAllFp8Pairs, 0, 1},
+        {"gemv_bt_fp8_m1_r2_u4", KIND_FP8, 3, 1, 8, 4, launch_gemv_kmajor_fp8<1, 2, 4>, kAllFp8Pairs, 0, 1},
         {"gemv_bt_fp8_m1_r4_u4", KIND_FP8, 3, 1, 16, 4, launch_gemv_kmajor_fp8<1, 4, 4>, kAllFp8Pairs, 0, 1},
         {"gemv_coop_fp8_m1_r4_w4", KIND_FP8, 3, 1, 4, 4, launch_gemv_kmajor_coop_fp8<1, 4, 4>, kAllFp8Pairs, 0, 1},
         {"gemv_coop_fp8_m4_r4_w4", KIND_FP8, 3, 4, 4, 4, launch_gemv_kmajor_coop_fp8<4, 4, 4>, kAllFp8Pairs, 0, 1},

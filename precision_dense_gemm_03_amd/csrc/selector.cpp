@@ -154,7 +154,10 @@ const GemmConfig* select_config(int kind, int out_dtype, int64_t M, int64_t N, i
         }
         return tile_with(kind, 64, 0, fa, fb, 1);
     }
-    if (M <= kStreamMaxM) {
+    // FP16 decode shapes stream B once through FMA sums; FP8 ones take the
+    // deep-ring kernel below (E4M3 [1,4096]x[4096,4096], cold weight: 17.2 us
+    // against 19.3 us streaming).
+    if (M <= kStreamMaxM && kind == KIND_F16) {
         const GemmConfig* best = nullptr;
         int ns = 0;
         const GemmConfig* st = stream_configs(&ns);
@@ -227,7 +230,13 @@ SplitPlan plan_splitk(int kind, int out_dtype, int64_t M, int64_t N, int64_t K, 
     // K-major B: decode shapes keep their dot-product kernels (each weight
     // row read once, no partial sums); larger M splits like row-major B.
     if (bt && c->family == 3) return p;
-    if (c->family == 1 && !std::getenv("LIBGEMM_CONFIG")) {
+    // FP8 with row-major B up to M = 64: the deep-ring kernel's plain call is
+    // replaced by split 64x64 tiles when a workspace is given (cold weight,
+    // N = K = 4096, E4M3: M = 16 14.2 vs 18.0 us, M = 63 15.2 vs 18.4 us; from
+    // M = 65 the two are even and the ring kernel needs no workspace; FP16
+    // keeps the ring kernel: [16,4096]x[4096,12288] 25.0 vs 43.1 us).
+    const bool ring_small = c->family == 6 && kind == KIND_FP8 && !bt && M <= 64;
+    if ((c->family == 1 || ring_small) && !std::getenv("LIBGEMM_CONFIG")) {
         // Decode shapes split over 64x64 MFMA tiles (two launches, measured
         // against the streaming kernels' own split: FP8 N = K = 4096 M = 1
         // 13.3 vs 13.7 us, M = 4 12.9 vs 16.9 us; FP16 [M,4096]x[4096,12288]

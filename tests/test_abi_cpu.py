@@ -154,9 +154,11 @@ def test_splitk_plan_rules(monkeypatch):
     assert plan(g.KIND_FP8, g.OUT_E4M3, 4, 4096, 4096) == ("tile_fp8_64x64x128_w2x2", 8, 8 * 4 * 4096 * 4)
     assert plan(g.KIND_F16, g.OUT_F16, 1, 12288, 4096) == ("stream_f16_m1_c64_t512", 1, 0)
     assert plan(g.KIND_F16, g.OUT_F16, 4, 12288, 4096) == ("tile_f16_64x64x64_w2x2", 4, 4 * 4 * 12288 * 4)
-    # 4 < M <= 256: the deep-ring kernel over all of K, no workspace; its tile
-    # minimises (bm + bn) times the rounds of workgroups per compute unit
-    assert plan(g.KIND_FP8, g.OUT_E4M3, 16, 4096, 4096) == ("ring_fp8_16x16x128", 1, 0)
+    # FP8, row-major B, M <= 64: split 64x64 tiles; above (and FP16) the
+    # deep-ring kernel over all of K, no workspace; its tile minimises
+    # (bm + bn) times the rounds of workgroups per compute unit
+    assert plan(g.KIND_FP8, g.OUT_E4M3, 16, 4096, 4096) == ("tile_fp8_64x64x128_w2x2", 8, 8 * 16 * 4096 * 4)
+    assert plan(g.KIND_FP8, g.OUT_E4M3, 64, 4096, 4096)[0] == "tile_fp8_64x64x128_w2x2"
     assert plan(g.KIND_FP8, g.OUT_E4M3, 65, 4096, 4096) == ("ring_fp8_32x64x128", 1, 0)
     assert plan(g.KIND_FP8, g.OUT_F32, 129, 4096, 4096) == ("ring_fp8_64x64x128", 1, 0)
     assert plan(g.KIND_F16, g.OUT_F16, 16, 12288, 4096) == ("ring_f16_16x64x64", 1, 0)
@@ -277,7 +279,9 @@ def test_select_config_rules():
     # from M = 5 the deep-ring MFMA kernel reads the weight faster than streaming
     assert sel(g.KIND_F16, g.OUT_F16, 16, 12288, 4096) == "ring_f16_16x64x64"
     assert sel(g.KIND_F16, g.OUT_F16, 5, 12288, 4096) == "ring_f16_16x64x64"
-    assert sel(g.KIND_FP8, g.OUT_E4M3, 1, 4096, 4096).startswith("stream_fp8_m1_")
+    # FP8 decode shapes on row-major B take the deep-ring kernel
+    assert sel(g.KIND_FP8, g.OUT_E4M3, 1, 4096, 4096) == "ring_fp8_16x16x128"
+    assert sel(g.KIND_FP8, g.OUT_E4M3, 4, 4096, 4096) == "ring_fp8_16x16x128"
     # 4096^2 fills the chip with 256x256 tiles (256 tiles): they run on the
     # ping-pong kernel, FP8 and FP16 alike, and so do larger grids
     assert sel(g.KIND_FP8, g.OUT_E4M3, 4096, 4096, 4096) == "pp_fp8_256x256x64"
@@ -349,7 +353,7 @@ def test_kmajor_selector():
     assert g.select_config_bt(g.KIND_F16, g.OUT_F16, 4, 12288, 4096) == "gemv_bt_f16_m4_r2_u4"
     assert g.select_config_bt(g.KIND_F16, g.OUT_F16, 8, 12288, 4096) == "gemv_bt_f16_m8_r4_u2"
     assert g.select_config_bt(g.KIND_F16, g.OUT_F16, 9, 12288, 4096) == "ring_f16_16x64x64_bt"
-    assert g.select_config_bt(g.KIND_FP8, g.OUT_E4M3, 1, 4096, 4096) == "gemv_bt_fp8_m1_r4_u4"
+    assert g.select_config_bt(g.KIND_FP8, g.OUT_E4M3, 1, 4096, 4096) == "gemv_bt_fp8_m1_r1_u4"
     assert g.select_config_bt(g.KIND_FP8, g.OUT_E4M3, 3, 4096, 4096) == "gemv_coop_fp8_m4_r4_w4"
     assert g.select_config_bt(g.KIND_FP8, g.OUT_E4M3, 8, 4096, 4096) == "gemv_coop_fp8_m8_r2_w4"
     assert g.select_config_bt(g.KIND_FP8, g.OUT_E4M3, 4096, 4096, 4096) == "pp_fp8_256x256x64_bt"
@@ -368,7 +372,7 @@ def test_kmajor_splitk_plan_and_validation(monkeypatch):
     """K-major split-K: decode shapes keep the decode kernels and mid-M shapes
     the deep-ring kernel (no split); a forced 64x64 tile splits like row-major
     B; workspace errors come before any launch."""
-    assert g.splitk_plan_bt(g.KIND_FP8, g.OUT_E4M3, 1, 4096, 4096) == ("gemv_bt_fp8_m1_r4_u4", 1, 0)
+    assert g.splitk_plan_bt(g.KIND_FP8, g.OUT_E4M3, 1, 4096, 4096) == ("gemv_bt_fp8_m1_r1_u4", 1, 0)
     assert g.splitk_plan_bt(g.KIND_F16, g.OUT_F16, 4, 12288, 4096) == ("gemv_bt_f16_m4_r2_u4", 1, 0)
     assert g.splitk_plan_bt(g.KIND_FP8, g.OUT_E4M3, 65, 4096, 4096) == ("ring_fp8_32x64x128_bt", 1, 0)
     assert g.splitk_plan_bt(g.KIND_F16, g.OUT_F16, 16, 12288, 4096) == ("ring_f16_16x64x64_bt", 1, 0)

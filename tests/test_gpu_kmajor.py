@@ -369,7 +369,7 @@ def test_dma_bt_matches_row_major_dma_bitwise(kind, family, monkeypatch):
 
 GEMV_CONFIGS = [("gemv_coop_f16_m1_r4_w8", 0, 1), ("gemv_bt_f16_m1_r4_u4", 0, 1), ("gemv_bt_f16_m4_r2_u4", 0, 4),
                 ("gemv_bt_f16_m4_r4_u2", 0, 4), ("gemv_coop_f16_m4_r2_w8", 0, 4), ("gemv_bt_f16_m8_r4_u2", 0, 8),
-                ("gemv_bt_f16_m8_r2_u2", 0, 8), ("gemv_bt_fp8_m1_r4_u4", 1, 1),
+                ("gemv_bt_f16_m8_r2_u2", 0, 8), ("gemv_bt_fp8_m1_r4_u4", 1, 1), ("gemv_bt_fp8_m1_r2_u4", 1, 1), ("gemv_bt_fp8_m1_r1_u4", 1, 1),
                 ("gemv_coop_fp8_m1_r4_w4", 1, 1), ("gemv_coop_fp8_m4_r4_w4", 1, 4), ("gemv_bt_fp8_m4_r4_u2", 1, 4),
                 ("gemv_coop_fp8_m8_r2_w4", 1, 8), ("gemv_bt_fp8_m8_r2_u2", 1, 8)]
 

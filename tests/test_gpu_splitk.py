@@ -101,8 +101,8 @@ def test_fp8_splitk_m_sweep_full_size(M):
     N = K = 4096
     name, splits, ws = workspace_for(g.KIND_FP8, g.OUT_E4M3, M, N, K)
     say(f"fp8 split-K sweep M={M}: {name} splits={splits}")
-    # M <= 4: split 64x64 tiles; 4 < M <= 256: the deep-ring kernel over all of K
-    assert (splits > 1) if M <= 4 else (splits == 1 and name.startswith("ring_fp8")), (name, splits)
+    # M <= 64: split 64x64 tiles; 64 < M <= 256: the deep-ring kernel over all of K
+    assert (splits > 1) if M <= 64 else (splits == 1 and name.startswith("ring_fp8")), (name, splits)
     xa = wl.normal_with_outliers_f32((M, K), 2000 + M)
     xb = wl.normal_with_outliers_f32((K, N), 2001)
     sa = orc.scale_from_amax(orc.amax(xa))
