@@ -19,7 +19,7 @@ LIB = os.path.join(PKG, "libgemm.so")
 SOURCES = ["abi.cpp", "selector.cpp", "amax_quant.hip", "amax_quant_channel.hip", "splitk_reduce.hip",
            "guard_f16.hip", "gemm_tile.hip", "gemm_tile_mixed.hip", "gemm_dma.hip", "gemm_dma_mixed.hip",
            "gemm_stream.hip", "gemv_kmajor.hip", "gemm_pp.hip", "gemm_pp_mixed.hip",
-           "amax_quant_pair.hip", "gemm_ring.hip", "gemm_ring_mixed.hip", "noalloc.hip"]
+           "amax_quant_pair.hip", "gemm_ring.hip", "gemm_ring_mixed.hip", "noalloc.hip", "gemm_pp_exact.hip"]
 
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 

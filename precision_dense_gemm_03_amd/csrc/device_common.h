@@ -149,6 +149,29 @@ __device__ __forceinline__ void store_out(void* C, int64_t idx, float y, int out
     }
 }
 
+// Exact widening of 8 FP8 codes (two words, code e in byte e % 4 of word e / 4)
+// to 8 FP16 values for the exact-accumulation mode. Every E4M3 and E5M2 value
+// is an FP16 value: E5M2 codes are the upper byte of the FP16 encoding (inf and
+// NaN included), E4M3 codes go through gfx950's FP8 -> FP16 conversion with a
+// unit scale (the E4M3 range, 2^-9 .. 448, lies inside FP16's normal range;
+// 0x7F / 0xFF stay NaN).
+__device__ __forceinline__ v4u widen8_fp8(uint32_t w0, uint32_t w1, bool e5m2) {
+    if (e5m2) {
+        auto two = [](uint32_t w, int hi) -> uint32_t {
+            const uint32_t b = hi ? (w >> 16) : w;
+            return ((b & 0xFFu) << 8) | ((b & 0xFF00u) << 16);
+        };
+        return v4u{two(w0, 0), two(w0, 1), two(w1, 0), two(w1, 1)};
+    }
+    typedef _Float16 v2hh __attribute__((ext_vector_type(2)));
+    const v2hh a = __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(w0, 1.0f, false);
+    const v2hh b = __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(w0, 1.0f, true);
+    const v2hh c = __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(w1, 1.0f, false);
+    const v2hh d = __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(w1, 1.0f, true);
+    return v4u{__builtin_bit_cast(uint32_t, a), __builtin_bit_cast(uint32_t, b), __builtin_bit_cast(uint32_t, c),
+               __builtin_bit_cast(uint32_t, d)};
+}
+
 // LDS reads issued as a group and waited for inside the same asm block, so
 // the results are complete when the block ends. Written in asm for kernels
 // that fill LDS with direct global->LDS loads and wait for them explicitly:

@@ -137,7 +137,13 @@ __device__ __forceinline__ void store_elem(void* C, int64_t idx, float y, int ef
     }
 }
 
-template <int ES, int OUT, int FA, int FB, bool BT>
+// EX (FP8 only): exact accumulation. The FP8 codes are staged and read as in
+// the FP8 kernel, then each 64-k operand is widened in registers to FP16 (every
+// E4M3 and E5M2 value is an FP16 value) and multiplied as four k-steps of the
+// FP16 MFMA (v_mfma_f32_32x32x16_f16), whose products and sums are exact in
+// FP32. A lane's 32 codes cover k = 32 h .. 32 h + 31; k-step s takes codes
+// 8 s .. 8 s + 7 of both operands, so every product pairs the same k.
+template <int ES, int OUT, int FA, int FB, bool BT, bool EX = false>
 __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2, 2))) void gemm_pp_kernel(
     const uint8_t* __restrict__ A, const uint8_t* __restrict__ B, void* __restrict__ C, int M, int N, int K,
     const float* __restrict__ sA, const float* __restrict__ sB, const float* __restrict__ sOut, int tiles_m,
@@ -343,13 +349,35 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
             for (int j = 0; j < 2; ++j) asm volatile("" : "+v"(opb[u][j]));
         }
         __builtin_amdgcn_s_setprio(1);
+        if constexpr (EX) {
+            static_assert(ES == 1, "exact accumulation widens FP8 codes");
 #pragma unroll
-        for (int u = 0; u < T::KSUB; ++u)
-#pragma unroll
-            for (int i = 0; i < 4; ++i)
+            for (int ks = 0; ks < 4; ++ks) {
+                // B's two operands widened once per k-step, A's one at a time
+                // (fewer live registers)
+                v8h wb[2];
 #pragma unroll
                 for (int j = 0; j < 2; ++j)
-                    acc[i][j] = Mfma<ES>::template mma<FB, FA>(opb[u][j], opa[u][i], acc[i][j]);
+                    wb[j] = __builtin_bit_cast(
+                        v8h, widen8_fp8((uint32_t)opb[0][j][2 * ks], (uint32_t)opb[0][j][2 * ks + 1], FB == 1));
+#pragma unroll
+                for (int i = 0; i < 4; ++i) {
+                    const v8h wa = __builtin_bit_cast(
+                        v8h, widen8_fp8((uint32_t)opa[0][i][2 * ks], (uint32_t)opa[0][i][2 * ks + 1], FA == 1));
+#pragma unroll
+                    for (int j = 0; j < 2; ++j)
+                        acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_f16(wb[j], wa, acc[i][j], 0, 0, 0);
+                }
+            }
+        } else {
+#pragma unroll
+            for (int u = 0; u < T::KSUB; ++u)
+#pragma unroll
+                for (int i = 0; i < 4; ++i)
+#pragma unroll
+                    for (int j = 0; j < 2; ++j)
+                        acc[i][j] = Mfma<ES>::template mma<FB, FA>(opb[u][j], opa[u][i], acc[i][j]);
+        }
 #pragma unroll
         for (int i = 0; i < 4; ++i)
 #pragma unroll
@@ -491,17 +519,18 @@ inline bool pp_fits(const GemmArgs& a) {
 
 // The register-staged 256 x 256 kernel, for requests the ping-pong kernel
 // cannot take.
-inline hipError_t fallback(int kind, const GemmArgs& a) {
-    const char* name = a.b_kmajor ? (kind == KIND_FP8 ? "tile_fp8_256x256x128_w2x4_bt" : "tile_f16_256x256x64_w2x4_bt")
+inline hipError_t fallback(int kind, const GemmArgs& a, bool exact = false) {
+    const char* name = exact ? (a.b_kmajor ? "exact_fp8_256x256x64_w2x4_bt" : "exact_fp8_256x256x64_w2x4")
+                     : a.b_kmajor ? (kind == KIND_FP8 ? "tile_fp8_256x256x128_w2x4_bt" : "tile_f16_256x256x64_w2x4_bt")
                                   : (kind == KIND_FP8 ? "tile_fp8_256x256x128_w2x4" : "tile_f16_256x256x64_w2x4");
     int nt = 0;
-    const GemmConfig* tt = tile_configs(&nt);
+    const GemmConfig* tt = exact ? exact_configs(&nt) : tile_configs(&nt);
     for (int i = 0; i < nt; ++i)
         if (std::strcmp(tt[i].name, name) == 0) return tt[i].launch(a);
     return hipErrorInvalidValue;
 }
 
-template <int ES, int FA, int FB, bool BT>
+template <int ES, int FA, int FB, bool BT, bool EX = false>
 hipError_t launch_pp(const GemmArgs& a) {
     using T = Pp<ES>;
     if (a.splits > 1) return hipErrorInvalidValue;  // no split-K (kgran 0 in the table)
@@ -510,7 +539,7 @@ hipError_t launch_pp(const GemmArgs& a) {
     const int64_t tiles_n = (a.N + T::BN - 1) / T::BN;
     const int64_t blocks = tiles_m * tiles_n;
     if (blocks <= 0) return hipSuccess;
-    if (!pp_fits<ES, BT>(a) || blocks > 0x7FFFFFFF) return fallback(ES == 1 ? KIND_FP8 : KIND_F16, a);
+    if (!pp_fits<ES, BT>(a) || blocks > 0x7FFFFFFF) return fallback(ES == 1 ? KIND_FP8 : KIND_F16, a, EX);
     const uint8_t* A = reinterpret_cast<const uint8_t*>(a.A);
     const uint8_t* B = reinterpret_cast<const uint8_t*>(a.B);
     const int M = (int)a.M, N = (int)a.N, K = (int)a.K;
@@ -520,16 +549,16 @@ hipError_t launch_pp(const GemmArgs& a) {
     const int vec_out = aligned16(a.C) && (a.N * out_es) % 16 == 0;
     switch (a.out_dtype) {
         case OUT_F32:
-            gemm_pp_kernel<ES, OUT_F32, FA, FB, BT><<<grid, block, 0, a.stream>>>(
+            gemm_pp_kernel<ES, OUT_F32, FA, FB, BT, EX><<<grid, block, 0, a.stream>>>(
                 A, B, a.C, M, N, K, a.sA, a.sB, a.sOut, (int)tiles_m, (int)tiles_n, eflags, vec_out);
             break;
         case OUT_F16:
-            gemm_pp_kernel<ES, OUT_F16, FA, FB, BT><<<grid, block, 0, a.stream>>>(
+            gemm_pp_kernel<ES, OUT_F16, FA, FB, BT, EX><<<grid, block, 0, a.stream>>>(
                 A, B, a.C, M, N, K, a.sA, a.sB, a.sOut, (int)tiles_m, (int)tiles_n, eflags, vec_out);
             break;
         default:
             if constexpr (ES == 1) {
-                gemm_pp_kernel<ES, OUT_E4M3, FA, FB, BT><<<grid, block, 0, a.stream>>>(
+                gemm_pp_kernel<ES, OUT_E4M3, FA, FB, BT, EX><<<grid, block, 0, a.stream>>>(
                     A, B, a.C, M, N, K, a.sA, a.sB, a.sOut, (int)tiles_m, (int)tiles_n, eflags, vec_out);
             } else {
                 return hipErrorInvalidValue;
@@ -547,6 +576,17 @@ hipError_t launch_pp_fp8_any(const GemmArgs& a) {
         case 1: return launch_pp<1, 0, 1, BT>(a);
         case 2: return launch_pp<1, 1, 0, BT>(a);
         default: return launch_pp<1, 1, 1, BT>(a);
+    }
+}
+
+// Exact accumulation (gemm_pp_exact.hip instantiates it).
+template <bool BT>
+hipError_t launch_pp_fp8_exact(const GemmArgs& a) {
+    switch (a.fmt_a * 2 + a.fmt_b) {
+        case 0: return launch_pp<1, 0, 0, BT, true>(a);
+        case 1: return launch_pp<1, 0, 1, BT, true>(a);
+        case 2: return launch_pp<1, 1, 0, BT, true>(a);
+        default: return launch_pp<1, 1, 1, BT, true>(a);
     }
 }
 

@@ -41,6 +41,10 @@ const GemmConfig* tile_configs(int* count) {
 // run time). Never chosen by the plain selector; select_config_exact does.
 const GemmConfig* exact_configs(int* count) {
     static const GemmConfig table[] = {
+        // 256x256: the ping-pong kernel with FP16 matrix cores (listed first,
+        // so the selector's 256 rule takes it), then the register-staged kernels
+        {"exact_pp_fp8_256x256x64", KIND_FP8, 5, 256, 256, 64, launch_pp_exact_rm, kAllFp8Pairs},
+        {"exact_pp_fp8_256x256x64_bt", KIND_FP8, 5, 256, 256, 64, launch_pp_exact_bt, kAllFp8Pairs, 0, 1},
         {"exact_fp8_64x64x64_w2x2", KIND_FP8, 5, 64, 64, 64, tile::launch_tile_fp8_exact<64, 64, 64, 2, 2>, kAllFp8Pairs},
         {"exact_fp8_128x128x64_w2x2", KIND_FP8, 5, 128, 128, 64, tile::launch_tile_fp8_exact<128, 128, 64, 2, 2>, kAllFp8Pairs},
         {"exact_fp8_256x256x64_w2x4", KIND_FP8, 5, 256, 256, 64, tile::launch_tile_fp8_exact<256, 256, 64, 2, 4>, kAllFp8Pairs},

@@ -63,6 +63,9 @@ const GemmConfig* dma_configs(int* count);
 const GemmConfig* gemv_kmajor_configs(int* count);
 const GemmConfig* pp_configs(int* count);
 const GemmConfig* exact_configs(int* count);
+// exact-accumulation ping-pong launchers (gemm_pp_exact.hip), row-major / K-major B
+hipError_t launch_pp_exact_rm(const GemmArgs& a);
+hipError_t launch_pp_exact_bt(const GemmArgs& a);
 const GemmConfig* ring_configs(int* count);
 
 // Shape (and FP8 operand formats) -> configuration (host only, no HIP calls).

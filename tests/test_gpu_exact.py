@@ -65,7 +65,8 @@ def run_exact(ca, fa, cb, fb, sa, sb, out_dtype, s_out=None, bt=False, out_fmt=N
     return host(C)
 
 
-EXACT_CONFIGS = ["exact_fp8_64x64x64_w2x2", "exact_fp8_128x128x64_w2x2", "exact_fp8_256x256x64_w2x4"]
+EXACT_CONFIGS = ["exact_fp8_64x64x64_w2x2", "exact_fp8_128x128x64_w2x2", "exact_fp8_256x256x64_w2x4",
+                 "exact_pp_fp8_256x256x64"]
 
 
 @pytest.mark.parametrize("cfg", EXACT_CONFIGS + [None])
@@ -166,6 +167,28 @@ def test_mixed_formats_plain_bound(fa, fb, M, N, K):
             s_out = orc.scale(np.float32(np.max(np.abs(V))), ORC_FMT[out_fmt])
             got = run_exact(ca, fa, cb, fb, sa, sb, torch.uint8, s_out, bt=bt, out_fmt=out_fmt)
             check_fp8(got, R, S, sa, sb, s_out, ORC_FMT[out_fmt], what=f"fp8 out {out_fmt} bt={bt}")
+
+
+@pytest.mark.parametrize("fa,fb", [(g.FMT_E4M3, g.FMT_E4M3), (g.FMT_E4M3, g.FMT_E5M2), (g.FMT_E5M2, g.FMT_E4M3),
+                                   (g.FMT_E5M2, g.FMT_E5M2)])
+@pytest.mark.parametrize("bt", [False, True])
+def test_pingpong_exact_ragged(fa, fb, bt, monkeypatch):
+    """The ping-pong kernel in exact mode forced on a ragged grid (M and N
+    not multiples of 256, a partial last K tile, several ring turns), every
+    operand pair, F32 / F16 / FP8 outputs, plain bound."""
+    cfg = "exact_pp_fp8_256x256x64" + ("_bt" if bt else "")
+    monkeypatch.setenv("LIBGEMM_CONFIG", cfg)
+    M, N, K = 600, 528, 720
+    assert g.select_config_exact(g.OUT_F32, M, N, K, fa, fb, int(bt)) == cfg
+    enc = {g.FMT_E4M3: wl.random_e4m3_codes, g.FMT_E5M2: wl.random_e5m2_codes}
+    ca, cb = enc[fa]((M, K), 7 * M + fa), enc[fb]((K, N), 5 * N + fb)
+    say(f"exact ping-pong a={fa} b={fb} bt={bt} {M}x{N}x{K}")
+    R, S = orc.gemm(ORC_FMT[fa], ca, cb, fmt_b=ORC_FMT[fb])
+    sa, sb = np.float32(2.0 ** -9), np.float32(2.0 ** -11)
+    check_f32(run_exact(ca, fa, cb, fb, sa, sb, torch.float32, bt=bt), R, S, sa, sb, what="f32")
+    check_f16(run_exact(ca, fa, cb, fb, sa, sb, torch.float16, bt=bt), R, S, sa, sb, what="f16")
+    s_out = orc.scale_from_amax(np.float32(np.max(np.abs(R * float(sa) * float(sb)))))
+    check_e4m3(run_exact(ca, fa, cb, fb, sa, sb, torch.uint8, s_out, bt=bt), R, S, sa, sb, s_out, what="e4m3")
 
 
 def test_unaligned_operands_and_k_tail():
