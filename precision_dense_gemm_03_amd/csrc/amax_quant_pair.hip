@@ -19,8 +19,12 @@
 // is deterministic and bit-identical to the separate calls.
 //
 // HBM traffic: 4 B per element read by launch 1, 4 B read and 1 B written by
-// launch 2. The reduce uses ordinary (cached) loads so that launch 2 can find
-// the operands in the memory-side cache.
+// launch 2. All of it is non-temporal. A second pass finds nothing useful in
+// the caches at these sizes. Cached loads that must first evict dirty lines
+// (left by whatever ran before, e.g. a GEMM's output) measured twice as slow
+// (reduce of 2 x 64 MiB after a 512 MiB write: 51.8 us cached, 24.0 us
+// non-temporal; back to back both about 19.5 us). Non-temporal code stores
+// took the quantize of 2 x 64 MiB from 35.6 to 28.2 us back to back.
 #include <algorithm>
 
 #include "device_common.h"
@@ -31,7 +35,8 @@ namespace libgemm {
 namespace {
 
 constexpr int kThreads = 256;
-constexpr int kUnroll = 4;
+constexpr int kUnroll = 4;       // 16-byte loads in flight per thread, reduce
+constexpr int kQuantUnroll = 2;  // the same, quantize (measured: 28.2 us for 2 x 64 MiB against 29.8 with 4)
 
 __device__ __forceinline__ uint32_t wave_max_u32(uint32_t v) {
 #pragma unroll
@@ -71,11 +76,11 @@ __device__ __forceinline__ uint32_t range_max(const float* __restrict__ x, int64
         for (; i + (kUnroll - 1) * kThreads < v1; i += kUnroll * kThreads) {
             v4u v[kUnroll];
 #pragma unroll
-            for (int j = 0; j < kUnroll; ++j) v[j] = x4[i + j * kThreads];
+            for (int j = 0; j < kUnroll; ++j) v[j] = __builtin_nontemporal_load(&x4[i + j * kThreads]);
 #pragma unroll
             for (int j = 0; j < kUnroll; ++j) m = max(m, max_abs_bits4(v[j]));
         }
-        for (; i < v1; i += kThreads) m = max(m, max_abs_bits4(x4[i]));
+        for (; i < v1; i += kThreads) m = max(m, max_abs_bits4(__builtin_nontemporal_load(&x4[i])));
         done = v1 * 4;
     }
     for (int64_t i = done + threadIdx.x; i < hi; i += kThreads) m = max(m, f32_bits(x[i]) & 0x7FFFFFFFu);
@@ -106,15 +111,16 @@ __device__ __forceinline__ void quantize_range(const float* __restrict__ x, int6
         const v4f* x4 = reinterpret_cast<const v4f*>(x);
         uint32_t* q4 = reinterpret_cast<uint32_t*>(q);
         const int64_t n4 = n / 4;
-        for (int64_t i = tid; i < n4; i += kUnroll * nthreads) {
-            v4f v[kUnroll];
+        for (int64_t i = tid; i < n4; i += kQuantUnroll * nthreads) {
+            v4f v[kQuantUnroll];
 #pragma unroll
-            for (int j = 0; j < kUnroll; ++j)
+            for (int j = 0; j < kQuantUnroll; ++j)
                 if (i + j * nthreads < n4) v[j] = __builtin_nontemporal_load(&x4[i + j * nthreads]);
 #pragma unroll
-            for (int j = 0; j < kUnroll; ++j)
+            for (int j = 0; j < kQuantUnroll; ++j)
                 if (i + j * nthreads < n4)
-                    q4[i + j * nthreads] = fp8_pack4<FMT>(v[j].x / s, v[j].y / s, v[j].z / s, v[j].w / s);
+                    __builtin_nontemporal_store(fp8_pack4<FMT>(v[j].x / s, v[j].y / s, v[j].z / s, v[j].w / s),
+                                                &q4[i + j * nthreads]);
         }
         done = n4 * 4;
     }
@@ -176,7 +182,7 @@ hipError_t launch_amax_quantize_pair(const float* xa, int64_t na, const float* x
     pair_reduce_kernel<<<pa + pb, kThreads, 0, stream>>>(xa, na, xb, nb, pa, pb, ca, cb, vec_a, vec_b, slots);
     const int qvec_a = vec_a && ((uintptr_t)qa & 3u) == 0;
     const int qvec_b = vec_b && ((uintptr_t)qb & 3u) == 0;
-    const int64_t work = (na + nb) / 4 / kUnroll;
+    const int64_t work = (na + nb) / 4 / kQuantUnroll;
     const int grid = (int)std::min<int64_t>(4096, std::max<int64_t>(1, (work + kThreads - 1) / kThreads));
     if (fmt == FMT_E5M2)
         pair_quantize_kernel<FMT_E5M2><<<grid, kThreads, 0, stream>>>(xa, na, xb, nb, pa, pb, slots, pow2, amax, scale,
