@@ -149,6 +149,10 @@ __device__ __forceinline__ void store_out(void* C, int64_t idx, float y, int out
     }
 }
 
+// s_waitcnt immediate (gfx9 encoding): at most `vm` vector-memory and `lgkm`
+// LDS operations of this wave outstanding.
+constexpr int waitcnt_imm(int vm, int lgkm) { return (vm & 0xF) | ((vm >> 4) << 14) | (7 << 4) | ((lgkm & 0xF) << 8); }
+
 // Exact widening of 8 FP8 codes (two words, code e in byte e % 4 of word e / 4)
 // to 8 FP16 values for the exact-accumulation mode. Every E4M3 and E5M2 value
 // is an FP16 value: E5M2 codes are the upper byte of the FP16 encoding (inf and

@@ -98,10 +98,6 @@ __device__ __forceinline__ int swz_b(int r) {
     return ES == 1 ? ((2 * (r & 7)) | ((r >> 2) & 1)) : (2 * (r & 3) + 8 * (r & 1));
 }
 
-// s_waitcnt immediate (gfx9 encoding): at most `vm` vector-memory and `lgkm`
-// LDS operations of this wave outstanding.
-constexpr int waitcnt_imm(int vm, int lgkm) { return (vm & 0xF) | ((vm >> 4) << 14) | (7 << 4) | ((lgkm & 0xF) << 8); }
-
 template <int ES>
 struct Mfma;
 

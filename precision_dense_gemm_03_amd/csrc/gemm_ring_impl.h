@@ -102,7 +102,6 @@ __device__ __forceinline__ int swz_b(int r) {
     return (ES == 1 ? (((r >> 2) & 1) | ((r >> 4) & 2)) : (2 * ((r >> 1) & 1) + 4 * ((r >> 3) & 1))) & (CPR - 1);
 }
 
-constexpr int waitcnt_imm(int vm, int lgkm) { return (vm & 0xF) | ((vm >> 4) << 14) | (7 << 4) | ((lgkm & 0xF) << 8); }
 
 // Wait until at most L * n of this wave's loads are outstanding (0 <= n <= N)
 // and its LDS operations have completed (the count is an immediate, so one
