@@ -15,9 +15,10 @@ the throughput of the whole FP8 job, quantization included. HIP events on the
 launch stream split every timed step into its parts (`in_step`). `roofline`
 is the FP8 GEMM kernel against the FP8 dense peak, `roofline_f16` the FP16
 GEMM against the FP16 peak, `roofline_decode` the decode against HBM, each
-timed as the mean per launch of back-to-back launches between two HIP events
-on the launch stream (the figure a kernel-trace profile of the same command
-reports as that kernel's average duration).
+timed as the median over five batches of the mean per launch of back-to-back
+launches between two HIP events on the launch stream (the figure a
+kernel-trace profile of the same command reports as that kernel's average
+duration).
 
 The same run times every configuration of the workload list on its own
 (`rows`): for each, R back-to-back calls each bracketed by HIP events on the
@@ -62,7 +63,7 @@ def parse():
     p.add_argument("--no-rows", action="store_true", help="time the step only")
     p.add_argument("--no-clock", action="store_true", help="skip the engine-clock sample under load (amd-smi)")
     p.add_argument("--kernel-reps", type=int, default=30,
-                   help="back-to-back launches timed per roofline kernel")
+                   help="back-to-back launches per batch timed per roofline kernel (median of 5 batches)")
     p.add_argument("--b-layout", choices=("rowmajor", "kmajor"), default="rowmajor",
                    help="layout of B in the timed step: rowmajor (B[K,N], the contract layout) or kmajor "
                         "(Bt[N,K], a linear layer's weight layout)")
@@ -310,21 +311,26 @@ def main():
         "decode_gbs": dec_bytes / ms_dec / 1e6,
         "what": "HIP events on the launch stream around each part of every timed step (mean over the steps)"}
 
-    # each roofline kernel on its own: R back-to-back launches on the launch
-    # stream between two HIP events (per-launch duration, launch gaps
-    # included; the step's own events also hold the dependency on the
+    # each roofline kernel on its own: batches of R back-to-back launches on
+    # the launch stream between two HIP events (per-launch duration, launch
+    # gaps included; the step's own events also hold the dependency on the
     # previous part)
-    def per_launch_us(fn, reps):
+    def per_launch_us(fn, reps, batches=5):
+        """Median over `batches` batches of the mean per launch of `reps`
+        back-to-back launches between two HIP events."""
         for _ in range(3):
             fn()
-        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-        torch.cuda.synchronize()
-        e0.record()
-        for _ in range(reps):
-            fn()
-        e1.record()
-        e1.synchronize()
-        return e0.elapsed_time(e1) * 1e3 / reps
+        means = []
+        for _ in range(batches):
+            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            torch.cuda.synchronize()
+            e0.record()
+            for _ in range(reps):
+                fn()
+            e1.record()
+            e1.synchronize()
+            means.append(e0.elapsed_time(e1) * 1e3 / reps)
+        return sorted(means)[len(means) // 2]
 
     log("timing roofline kernels back to back")
     us_gemm8 = per_launch_us(lambda: gemm8(qa, qb, scale8[0:1], scale8[1:2], c8, s_out), args.kernel_reps)
@@ -357,8 +363,8 @@ def main():
         achieved = work / us / 1e6 if unit == "TFLOP/s" else work / us / 1e3
         r = {"bound": bound, "kernel": kernel, "kernel_us": us, "achieved": achieved, "peak": peak, "unit": unit,
              "frac": achieved / peak, "traffic": traffic,
-             "timing": f"mean per launch over {args.kernel_reps} back-to-back launches between two HIP events "
-                       "on the launch stream, after the timed steps"}
+             "timing": f"median over 5 batches of the mean per launch of {args.kernel_reps} back-to-back "
+                       "launches between two HIP events on the launch stream, after the timed steps"}
         if algo is not None:
             r["algorithmic_bytes"] = algo
         return r
