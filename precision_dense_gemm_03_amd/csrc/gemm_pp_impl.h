@@ -7,12 +7,13 @@
 // applied at write-back, §3.2; "HGEMM优化：深度学习中的矩阵乘法性能提升策略" §1.3 for
 // FP16 with an FP32 accumulator). B is row-major B[K,N] or K-major Bt[N,K].
 //
-// One workgroup computes a 256 x 256 output tile with 8 waves, two per SIMD.
-// The waves form two groups of four (one wave of each group per SIMD): group
-// G owns output rows [128 G, 128 G + 128), and wave j of a group the columns
-// [64 j, 64 j + 64), i.e. a 128 x 64 wave tile held as 4 x 2 accumulators of
-// the 32x32 MFMA (v_mfma_scale_f32_32x32x64_f8f6f4 with neutral block scales
-// for FP8, v_mfma_f32_32x32x16_f16 for FP16): 128 registers per lane.
+// One workgroup computes a 256 x 256 output tile (or 192 x 256, see Pp) with 8
+// waves, two per SIMD. The waves form two groups of four (one wave of each
+// group per SIMD): group G owns output rows [128 G, 128 G + 128), and wave j
+// of a group the columns [64 j, 64 j + 64), i.e. a 128 x 64 wave tile held as
+// 4 x 2 accumulators of the 32x32 MFMA (v_mfma_scale_f32_32x32x64_f8f6f4 with
+// neutral block scales for FP8, v_mfma_f32_32x32x16_f16 for FP16): 128
+// registers per lane. With 192-row tiles a group owns 96 rows, 3 x 2 blocks.
 //
 // K advances in tiles of 64 bytes of every A row (64 FP8 or 32 FP16 values).
 // Each K tile runs as two phases per group, and the groups are offset by one
@@ -71,22 +72,39 @@
 namespace libgemm {
 namespace pp {
 
-template <int ES>
+// BM_: tile rows, 256 or 192 (three 32-row blocks per wave instead of four:
+// 3000 x 4096 is 16 x 16 tiles of 192 x 256 on 256 CUs, against 12 x 16 tiles
+// of 256 x 256 that leave a quarter of them idle).
+template <int ES, int BM_ = 256>
 struct Pp {
-    static constexpr int BM = 256, BN = 256;
+    static constexpr int BM = BM_, BN = 256;
+    static_assert(BM == 256 || BM == 192, "tile rows: 256 or 192");
     static constexpr int NT = 512;                  // 8 waves
     static constexpr int S = 4;                     // LDS ring stages
     static constexpr int ROWB = 64;                 // bytes of every A row per K tile
     static constexpr int BK = ROWB / ES;            // k per K tile (64 FP8, 32 FP16)
     static constexpr int VE = 16 / ES;              // elements per 16-byte chunk
-    static constexpr int STAGE_BYTES = 16384;       // A: 256 rows x 64 B; B: the same bytes
+    static constexpr int MR = BM / 2;               // A rows of one group
+    static constexpr int MI = BM / 64;              // 32-row blocks per wave
+    static constexpr int A_STAGE = BM * ROWB;       // A: BM rows x 64 B
+    static constexpr int B_STAGE = 16384;           // B: 64 B of k x 256 n
+    static constexpr int A_RPW = BM / 4;            // A rows one wave of group 0 loads
     static constexpr int BNB = BN * ES;             // row-major B: bytes of one k-row of the tile
     static constexpr int B_CPR = BNB / 16;          // chunks per row-major B row
     static constexpr int B_RPB = 1024 / BNB;        // row-major B rows per 1 KiB direct load
-    static constexpr int LOADS = 4;                 // direct loads per wave per K tile (its group's 16 KiB / 4 waves)
+    static constexpr int LA = A_STAGE / 4096;       // direct loads per wave per K tile, group 0 (A)
+    static constexpr int LB = B_STAGE / 4096;       // the same, group 1 (B)
     static constexpr int KSUB = ES == 1 ? 1 : 2;    // MFMA k-steps per K tile (64 or 2 x 16 values)
-    static_assert(S * 2 * STAGE_BYTES <= 160 * 1024, "the LDS ring must fit in 160 KiB");
+    static_assert(S * (A_STAGE + B_STAGE) <= 160 * 1024, "the LDS ring must fit in 160 KiB");
 };
+
+// s_waitcnt vmcnt(NA) for a wave of group 0, vmcnt(NB) for group 1 (their
+// direct loads per K tile differ when BM < 256); LDS count LGKM.
+template <int NA, int NB, int LGKM = 0>
+__device__ __forceinline__ void wait_vm(bool group0) {
+    if (NA == NB || !group0) __builtin_amdgcn_s_waitcnt(waitcnt_imm(NB, LGKM));
+    else __builtin_amdgcn_s_waitcnt(waitcnt_imm(NA, LGKM));
+}
 
 __device__ __forceinline__ int swz_a(int r) { return (r >> 2) & 3; }
 
@@ -139,17 +157,15 @@ __device__ __forceinline__ void store_elem(void* C, int64_t idx, float y, int ef
 // FP16 MFMA (v_mfma_f32_32x32x16_f16), whose products and sums are exact in
 // FP32. A lane's 32 codes cover k = 32 h .. 32 h + 31; k-step s takes codes
 // 8 s .. 8 s + 7 of both operands, so every product pairs the same k.
-template <int ES, int OUT, int FA, int FB, bool BT, bool EX = false>
+template <int ES, int OUT, int FA, int FB, bool BT, bool EX = false, int BM = 256>
 __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2, 2))) void gemm_pp_kernel(
     const uint8_t* __restrict__ A, const uint8_t* __restrict__ B, void* __restrict__ C, int M, int N, int K,
     const float* __restrict__ sA, const float* __restrict__ sB, const float* __restrict__ sOut, int tiles_m,
     int tiles_n, int eflags, int vec_out) {
-    using T = Pp<ES>;
+    using T = Pp<ES, BM>;
     using Op = typename Mfma<ES>::op;
-    __shared__ __attribute__((aligned(1024))) uint8_t a0[T::STAGE_BYTES], a1[T::STAGE_BYTES], a2[T::STAGE_BYTES],
-        a3[T::STAGE_BYTES];
-    __shared__ __attribute__((aligned(1024))) uint8_t b0[T::STAGE_BYTES], b1[T::STAGE_BYTES], b2[T::STAGE_BYTES],
-        b3[T::STAGE_BYTES];
+    __shared__ __attribute__((aligned(1024))) uint8_t a0[T::A_STAGE], a1[T::A_STAGE], a2[T::A_STAGE], a3[T::A_STAGE];
+    __shared__ __attribute__((aligned(1024))) uint8_t b0[T::B_STAGE], b1[T::B_STAGE], b2[T::B_STAGE], b3[T::B_STAGE];
     // Stage selection; st is a compile-time constant wherever it matters
     // (the main loop is unrolled by the ring size).
     auto stage_a = [&](int st) __attribute__((always_inline)) -> LDS_AS uint8_t* {
@@ -179,19 +195,21 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
     const int nk_full = K / T::BK;
 
     // ---- this lane's direct-load slots: group 0 loads A, group 1 loads B ----
-    // Load i of wave j fills 1 KiB of the group's 16 KiB: A / Bt rows
-    // 64 j + 16 i + lane / 4 (slot lane % 4), or row-major B rows
-    // B_RPB (4 j + i) + lane / B_CPR (slot lane % B_CPR).
+    // Load i of wave j fills 1 KiB of its group's stage: A rows
+    // A_RPW j + 16 i + lane / 4 (i < LA) or Bt rows 64 j + 16 i + lane / 4
+    // (slot lane % 4), or row-major B rows B_RPB (4 j + i) + lane / B_CPR
+    // (slot lane % B_CPR).
     const uint8_t* src = G == 0 ? A + (int64_t)m0 * K * ES
                                 : (BT ? B + (int64_t)n0 * K * ES : B + (int64_t)n0 * ES);
-    uint32_t goff[T::LOADS];
+    const int rpw = G == 0 ? T::A_RPW : 64;  // rows of A or Bt one wave loads
+    uint32_t goff[T::LB];
 #pragma unroll
-    for (int i = 0; i < T::LOADS; ++i) {
+    for (int i = 0; i < T::LB; ++i) {
         if (G == 0 || BT) {
-            const int r = 64 * wj + 16 * i + (lane >> 2);
+            const int r = rpw * wj + 16 * i + (lane >> 2);
             const int c = (lane & 3) ^ swz_a(r);
             const int rr = G == 0 ? min(m0 + r, M - 1) - m0 : min(n0 + r, N - 1) - n0;
-            goff[i] = (uint32_t)(rr * K * ES + c * 16);
+            goff[i] = (uint32_t)(rr * K * ES + c * 16);  // i >= LA of group 0: never used
         } else {
             const int r = T::B_RPB * (4 * wj + i) + lane / T::B_CPR;
             const int c = (lane % T::B_CPR) ^ swz_b<ES>(r);
@@ -206,14 +224,14 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
     auto issue_full = [&](int kt, int st) __attribute__((always_inline)) {
         const uint8_t* p = src + (int64_t)kt * kstep;
         if (G == 0) {
-            LDS_AS uint8_t* dst = stage_a(st) + wj * 4096;
+            LDS_AS uint8_t* dst = stage_a(st) + wj * (T::A_RPW * T::ROWB);
 #pragma unroll
-            for (int i = 0; i < T::LOADS; ++i)
+            for (int i = 0; i < T::LA; ++i)
                 __builtin_amdgcn_global_load_lds((const void*)(p + goff[i]), (LDS_AS void*)(dst + i * 1024), 16, 0, 0);
         } else {
             LDS_AS uint8_t* dst = stage_b(st) + wj * 4096;
 #pragma unroll
-            for (int i = 0; i < T::LOADS; ++i)
+            for (int i = 0; i < T::LB; ++i)
                 __builtin_amdgcn_global_load_lds((const void*)(p + goff[i]), (LDS_AS void*)(dst + i * 1024), 16, 0, 0);
         }
     };
@@ -223,12 +241,13 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
     auto issue_partial = [&](int kt, int st) __attribute__((always_inline)) {
         const uint8_t* p = src + (int64_t)kt * kstep;
         const int k0 = kt * T::BK;
-        LDS_AS uint8_t* dst = (G == 0 ? stage_a(st) : stage_b(st)) + wj * 4096;
+        LDS_AS uint8_t* dst = G == 0 ? stage_a(st) + wj * (T::A_RPW * T::ROWB) : stage_b(st) + wj * 4096;
+        const int nl = G == 0 ? T::LA : T::LB;
 #pragma unroll 1
-        for (int i = 0; i < T::LOADS; ++i) {
+        for (int i = 0; i < nl; ++i) {
             v4u v = v4u{0u, 0u, 0u, 0u};
             if (G == 0 || BT) {
-                const int r = 64 * wj + 16 * i + (lane >> 2);
+                const int r = rpw * wj + 16 * i + (lane >> 2);
                 const int c = (lane & 3) ^ swz_a(r);
                 if (k0 + c * T::VE < K) v = *reinterpret_cast<const v4u*>(p + goff[i]);
             } else {
@@ -240,7 +259,7 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
     };
 
     // ---- operand reads ----
-    // A: rows 128 G + 32 i + lane % 32; FP8 takes chunks 2h, 2h + 1 of the row
+    // A: rows MR G + 32 i + lane % 32; FP8 takes chunks 2h, 2h + 1 of the row
     // (k = 32 h .. 32 h + 31), FP16 k-step u takes chunk 2u + h (h = lane / 32).
     // The row's swizzle is that of lane % 32 (row blocks start at multiples of 32).
     const int lr = lane & 31, h = lane >> 5;
@@ -289,25 +308,25 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
         }
     };
 
-    v16f acc[4][2];
+    v16f acc[T::MI][2];
 #pragma unroll
-    for (int i = 0; i < 4; ++i)
+    for (int i = 0; i < T::MI; ++i)
 #pragma unroll
         for (int j = 0; j < 2; ++j)
 #pragma unroll
             for (int r = 0; r < 16; ++r) acc[i][j][r] = 0.0f;
 
-    Op opa[T::KSUB][4], opb[T::KSUB][2];
+    Op opa[T::KSUB][T::MI], opb[T::KSUB][2];
     // One K tile: MEM(t) then MMA(t). steady: tile t+3 exists and is full
     // (the unrolled main loop); otherwise the loads of tile t+3 are chosen at
     // run time.
     auto step = [&](int t, int st, bool steady) __attribute__((always_inline)) {
         // MEM(t)
-        const LDS_AS uint8_t* sa = stage_a(st) + (128 * G + lr) * T::ROWB;
+        const LDS_AS uint8_t* sa = stage_a(st) + (T::MR * G + lr) * T::ROWB;
 #pragma unroll
         for (int u = 0; u < T::KSUB; ++u)
 #pragma unroll
-            for (int i = 0; i < 4; ++i) opa[u][i] = rd_row(sa + 32 * i * T::ROWB, u);
+            for (int i = 0; i < T::MI; ++i) opa[u][i] = rd_row(sa + 32 * i * T::ROWB, u);
         if constexpr (BT) {
             const LDS_AS uint8_t* sbt = stage_b(st) + (64 * wj + lr) * T::ROWB;
 #pragma unroll
@@ -323,13 +342,13 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
         const int nt = t + T::S - 1, nst = (st + T::S - 1) % T::S;
         if (steady || nt < nk_full) {
             issue_full(nt, nst);
-            __builtin_amdgcn_s_waitcnt(waitcnt_imm(T::LOADS * (T::S - 2), 0));
+            wait_vm<T::LA * (T::S - 2), T::LB * (T::S - 2)>(G == 0);
         } else if (nk == nk_full && t + 1 < nk) {
             // the last tiles, all full: wait for tile t+1 only; min(S-2,
             // nk-2-t) newer tiles may still be in flight
             static_assert(T::S == 4, "the tail waits below are written for a 4-stage ring");
-            if (nk - 2 - t >= 2) __builtin_amdgcn_s_waitcnt(waitcnt_imm(2 * T::LOADS, 0));
-            else if (nk - 2 - t == 1) __builtin_amdgcn_s_waitcnt(waitcnt_imm(T::LOADS, 0));
+            if (nk - 2 - t >= 2) wait_vm<2 * T::LA, 2 * T::LB>(G == 0);
+            else if (nk - 2 - t == 1) wait_vm<T::LA, T::LB>(G == 0);
             else __builtin_amdgcn_s_waitcnt(waitcnt_imm(0, 0));
         } else {
             if (nt < nk) issue_partial(nt, nst);
@@ -340,7 +359,7 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
 #pragma unroll
         for (int u = 0; u < T::KSUB; ++u) {
 #pragma unroll
-            for (int i = 0; i < 4; ++i) asm volatile("" : "+v"(opa[u][i]));
+            for (int i = 0; i < T::MI; ++i) asm volatile("" : "+v"(opa[u][i]));
 #pragma unroll
             for (int j = 0; j < 2; ++j) asm volatile("" : "+v"(opb[u][j]));
         }
@@ -357,7 +376,7 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
                     wb[j] = __builtin_bit_cast(
                         v8h, widen8_fp8((uint32_t)opb[0][j][2 * ks], (uint32_t)opb[0][j][2 * ks + 1], FB == 1));
 #pragma unroll
-                for (int i = 0; i < 4; ++i) {
+                for (int i = 0; i < T::MI; ++i) {
                     const v8h wa = __builtin_bit_cast(
                         v8h, widen8_fp8((uint32_t)opa[0][i][2 * ks], (uint32_t)opa[0][i][2 * ks + 1], FA == 1));
 #pragma unroll
@@ -369,13 +388,13 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
 #pragma unroll
             for (int u = 0; u < T::KSUB; ++u)
 #pragma unroll
-                for (int i = 0; i < 4; ++i)
+                for (int i = 0; i < T::MI; ++i)
 #pragma unroll
                     for (int j = 0; j < 2; ++j)
                         acc[i][j] = Mfma<ES>::template mma<FB, FA>(opb[u][j], opa[u][i], acc[i][j]);
         }
 #pragma unroll
-        for (int i = 0; i < 4; ++i)
+        for (int i = 0; i < T::MI; ++i)
 #pragma unroll
             for (int j = 0; j < 2; ++j) asm volatile("" : "+v"(acc[i][j]));
         __builtin_amdgcn_s_setprio(0);
@@ -388,7 +407,7 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
         if (p < nk_full) issue_full(p, p);
         else if (p < nk) issue_partial(p, p);
     }
-    if (nk >= T::S - 1) __builtin_amdgcn_s_waitcnt(waitcnt_imm(T::LOADS * (T::S - 2), 15));
+    if (nk >= T::S - 1) wait_vm<T::LA * (T::S - 2), T::LB * (T::S - 2), 15>(G == 0);
     else __builtin_amdgcn_s_waitcnt(0);
     asm volatile("s_barrier" ::: "memory");
     if (G == 1) asm volatile("s_barrier" ::: "memory");
@@ -407,17 +426,17 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
     if (G == 0) asm volatile("s_barrier" ::: "memory");
 
     // ---- epilogue ----
-    // Block (i, j), element 4q + e: row 128 G + 32 i + lr, column
+    // Block (i, j), element 4q + e: row MR G + 32 i + lr, column
     // 64 wj + 32 j + 8 q + 4 h + e of the tile.
     const bool chan = (eflags & EPI_CHANNEL) != 0;
     const float scale = epilogue_base(sA, sB, sOut, OUT == OUT_E4M3, chan);
-    const int row_t = 128 * G + lr;            // + 32 i
+    const int row_t = T::MR * G + lr;          // + 32 i
     const int col_t = 64 * wj + 4 * h;         // + 32 j + 8 q
     // Vector stores need a 16-byte aligned C with 16-byte row pitches (vec_out).
     const bool interior = vec_out && (m0 + T::BM <= M) && (n0 + T::BN <= N);
     if (!interior) {
 #pragma unroll
-        for (int i = 0; i < 4; ++i)
+        for (int i = 0; i < T::MI; ++i)
 #pragma unroll
             for (int j = 0; j < 2; ++j)
 #pragma unroll
@@ -447,7 +466,7 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
     if constexpr (OUT == OUT_F32) {
         float* Cf = reinterpret_cast<float*>(C);
 #pragma unroll
-        for (int i = 0; i < 4; ++i)
+        for (int i = 0; i < T::MI; ++i)
 #pragma unroll
             for (int j = 0; j < 2; ++j)
 #pragma unroll
@@ -456,7 +475,7 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
                         run4(i, j, q);
         return;
     }
-    // FP8 / FP16: the wave's 128 x 64 block goes to its own LDS stage array
+    // FP8 / FP16: the wave's 32 MI x 64 block goes to its own LDS stage array
     // (row pitch 64 ES bytes), then each lane stores 16-byte row pieces. Every
     // wave has finished its last operand read (the final barrier above).
     // The 16-byte chunk c of block row r sits at slot c ^ esw(r): a write
@@ -467,9 +486,10 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
     auto esw = [](int r) __attribute__((always_inline)) -> int {
         return OUT == OUT_F16 ? ((r >> 1) & 7) : ((r >> 2) & 3);
     };
+    static_assert(32 * T::MI * RB <= T::A_STAGE, "a wave's staged block fits in one LDS stage");
     LDS_AS uint8_t* ep = wave < 4 ? stage_a(wave) : stage_b(wave - 4);
 #pragma unroll
-    for (int i = 0; i < 4; ++i)
+    for (int i = 0; i < T::MI; ++i)
 #pragma unroll
         for (int j = 0; j < 2; ++j)
 #pragma unroll
@@ -493,10 +513,10 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
     uint8_t* Cb = reinterpret_cast<uint8_t*>(C);
     const int es_out = RB / 64;
 #pragma unroll
-    for (int p = 0; p < 128 / RPI; ++p) {
+    for (int p = 0; p < 32 * T::MI / RPI; ++p) {
         const int r = RPI * p + lane / LPR, seg = lane % LPR;
         const v4i v = *(const LDS_AS v4i*)(ep + r * RB + 16 * (seg ^ esw(r)));
-        *reinterpret_cast<v4i*>(Cb + ((int64_t)(m0 + 128 * G + r) * N + n0 + 64 * wj) * es_out + 16 * seg) = v;
+        *reinterpret_cast<v4i*>(Cb + ((int64_t)(m0 + T::MR * G + r) * N + n0 + 64 * wj) * es_out + 16 * seg) = v;
     }
 }
 
@@ -504,9 +524,9 @@ inline bool aligned16(const void* p) { return ((uintptr_t)p & 15u) == 0; }
 
 // Whether the ping-pong kernel can take the request: 16-byte aligned operands
 // and row pitches, and 32-bit offsets within a tile's row block.
-template <int ES, bool BT>
+template <int ES, bool BT, int BM = 256>
 inline bool pp_fits(const GemmArgs& a) {
-    using T = Pp<ES>;
+    using T = Pp<ES, BM>;
     const bool aligned = aligned16(a.A) && aligned16(a.B) && (a.K * ES) % 16 == 0 && (BT || (a.N * ES) % 16 == 0);
     const bool fits = (int64_t)T::BM * a.K * ES < (1ll << 31) &&
                       (BT ? (int64_t)T::BN * a.K * ES : (int64_t)T::BK * a.N * ES) < (1ll << 31);
@@ -526,16 +546,16 @@ inline hipError_t fallback(int kind, const GemmArgs& a, bool exact = false) {
     return hipErrorInvalidValue;
 }
 
-template <int ES, int FA, int FB, bool BT, bool EX = false>
+template <int ES, int FA, int FB, bool BT, bool EX = false, int BM = 256>
 hipError_t launch_pp(const GemmArgs& a) {
-    using T = Pp<ES>;
+    using T = Pp<ES, BM>;
     if (a.splits > 1) return hipErrorInvalidValue;  // no split-K (kgran 0 in the table)
     if (BT != (a.b_kmajor != 0)) return hipErrorInvalidValue;
     const int64_t tiles_m = (a.M + T::BM - 1) / T::BM;
     const int64_t tiles_n = (a.N + T::BN - 1) / T::BN;
     const int64_t blocks = tiles_m * tiles_n;
     if (blocks <= 0) return hipSuccess;
-    if (!pp_fits<ES, BT>(a) || blocks > 0x7FFFFFFF) return fallback(ES == 1 ? KIND_FP8 : KIND_F16, a, EX);
+    if (!pp_fits<ES, BT, BM>(a) || blocks > 0x7FFFFFFF) return fallback(ES == 1 ? KIND_FP8 : KIND_F16, a, EX);
     const uint8_t* A = reinterpret_cast<const uint8_t*>(a.A);
     const uint8_t* B = reinterpret_cast<const uint8_t*>(a.B);
     const int M = (int)a.M, N = (int)a.N, K = (int)a.K;
@@ -545,16 +565,16 @@ hipError_t launch_pp(const GemmArgs& a) {
     const int vec_out = aligned16(a.C) && (a.N * out_es) % 16 == 0;
     switch (a.out_dtype) {
         case OUT_F32:
-            gemm_pp_kernel<ES, OUT_F32, FA, FB, BT, EX><<<grid, block, 0, a.stream>>>(
+            gemm_pp_kernel<ES, OUT_F32, FA, FB, BT, EX, BM><<<grid, block, 0, a.stream>>>(
                 A, B, a.C, M, N, K, a.sA, a.sB, a.sOut, (int)tiles_m, (int)tiles_n, eflags, vec_out);
             break;
         case OUT_F16:
-            gemm_pp_kernel<ES, OUT_F16, FA, FB, BT, EX><<<grid, block, 0, a.stream>>>(
+            gemm_pp_kernel<ES, OUT_F16, FA, FB, BT, EX, BM><<<grid, block, 0, a.stream>>>(
                 A, B, a.C, M, N, K, a.sA, a.sB, a.sOut, (int)tiles_m, (int)tiles_n, eflags, vec_out);
             break;
         default:
             if constexpr (ES == 1) {
-                gemm_pp_kernel<ES, OUT_E4M3, FA, FB, BT, EX><<<grid, block, 0, a.stream>>>(
+                gemm_pp_kernel<ES, OUT_E4M3, FA, FB, BT, EX, BM><<<grid, block, 0, a.stream>>>(
                     A, B, a.C, M, N, K, a.sA, a.sB, a.sOut, (int)tiles_m, (int)tiles_n, eflags, vec_out);
             } else {
                 return hipErrorInvalidValue;
@@ -565,13 +585,13 @@ hipError_t launch_pp(const GemmArgs& a) {
 
 // Operand-format dispatch; the pairs other than E4M3 x E4M3 are instantiated
 // in gemm_pp_mixed.hip.
-template <bool BT>
+template <bool BT, int BM = 256>
 hipError_t launch_pp_fp8_any(const GemmArgs& a) {
     switch (a.fmt_a * 2 + a.fmt_b) {
-        case 0: return launch_pp<1, 0, 0, BT>(a);
-        case 1: return launch_pp<1, 0, 1, BT>(a);
-        case 2: return launch_pp<1, 1, 0, BT>(a);
-        default: return launch_pp<1, 1, 1, BT>(a);
+        case 0: return launch_pp<1, 0, 0, BT, false, BM>(a);
+        case 1: return launch_pp<1, 0, 1, BT, false, BM>(a);
+        case 2: return launch_pp<1, 1, 0, BT, false, BM>(a);
+        default: return launch_pp<1, 1, 1, BT, false, BM>(a);
     }
 }
 

@@ -10,5 +10,11 @@ template hipError_t launch_pp<1, 1, 1, false>(const GemmArgs&);
 template hipError_t launch_pp<1, 0, 1, true>(const GemmArgs&);
 template hipError_t launch_pp<1, 1, 0, true>(const GemmArgs&);
 template hipError_t launch_pp<1, 1, 1, true>(const GemmArgs&);
+template hipError_t launch_pp<1, 0, 1, false, false, 192>(const GemmArgs&);
+template hipError_t launch_pp<1, 1, 0, false, false, 192>(const GemmArgs&);
+template hipError_t launch_pp<1, 1, 1, false, false, 192>(const GemmArgs&);
+template hipError_t launch_pp<1, 0, 1, true, false, 192>(const GemmArgs&);
+template hipError_t launch_pp<1, 1, 0, true, false, 192>(const GemmArgs&);
+template hipError_t launch_pp<1, 1, 1, true, false, 192>(const GemmArgs&);
 }  // namespace pp
 }  // namespace libgemm

@@ -101,13 +101,22 @@ const GemmConfig* ring_for(int kind, int64_t M, int64_t N, int fa, int fb, int b
 
 // The preferred configuration of each tile size. 256x256 tiles use the
 // ping-pong kernel (8 waves, two per SIMD taking turns at the matrix core,
-// direct loads into a 4-stage LDS ring); smaller tiles the register-staged
-// kernel with 4 waves.
-const GemmConfig* tile_with(int kind, int bm, int64_t tiles, int fa, int fb, int bt = 0) {
-    (void)tiles;
+// direct loads into a 4-stage LDS ring), in its 192-row form when that leaves
+// each CU fewer rows to compute: ceil(tiles / CUs) rounds of BM rows (E4M3
+// 3000x4096x4096: 12 x 16 = 192 tiles of 256 rows, one round of 256, against
+// 16 x 16 = 256 tiles of 192 rows, one round of 192). Smaller tiles use the
+// register-staged kernel with 4 waves.
+const GemmConfig* tile_with(int kind, int bm, int64_t M, int64_t N, int fa, int fb, int bt = 0) {
     if (bm == 256) {
-        const char* want = kind == KIND_FP8 ? (bt ? "pp_fp8_256x256x64_bt" : "pp_fp8_256x256x64")
-                                            : (bt ? "pp_f16_256x256x32_bt" : "pp_f16_256x256x32");
+        const int64_t tn = (N + 255) / 256;
+        const int64_t rows256 = (((M + 255) / 256) * tn + kNumCUs - 1) / kNumCUs * 256;
+        const int64_t rows192 = (((M + 191) / 192) * tn + kNumCUs - 1) / kNumCUs * 192;
+        const bool r192 = rows192 < rows256;
+        const char* want = kind == KIND_FP8
+                               ? (bt ? (r192 ? "pp_fp8_192x256x64_bt" : "pp_fp8_256x256x64_bt")
+                                     : (r192 ? "pp_fp8_192x256x64" : "pp_fp8_256x256x64"))
+                               : (bt ? (r192 ? "pp_f16_192x256x32_bt" : "pp_f16_256x256x32_bt")
+                                     : (r192 ? "pp_f16_192x256x32" : "pp_f16_256x256x32"));
         if (const GemmConfig* c = find_named(want, kind, 0, fa, fb, bt)) return c;
     }
     int nt = 0;
@@ -149,10 +158,10 @@ const GemmConfig* select_config(int kind, int out_dtype, int64_t M, int64_t N, i
             const double padded = (double)(tm * bm) * (double)(tn * bm);
             const int64_t min_tiles = bm == 256 ? kNumCUs * 3 / 4 : kNumCUs;
             if (tm * tn >= min_tiles && useful >= 0.75 * padded) {
-                if (const GemmConfig* c = tile_with(kind, bm, tm * tn, fa, fb, 1)) return c;
+                if (const GemmConfig* c = tile_with(kind, bm, M, N, fa, fb, 1)) return c;
             }
         }
-        return tile_with(kind, 64, 0, fa, fb, 1);
+        return tile_with(kind, 64, M, N, fa, fb, 1);
     }
     // FP16 decode shapes stream B once through FMA sums; FP8 ones take the
     // deep-ring kernel below (E4M3 [1,4096]x[4096,4096], cold weight: 17.2 us
@@ -179,10 +188,10 @@ const GemmConfig* select_config(int kind, int out_dtype, int64_t M, int64_t N, i
         const double padded = (double)(tm * bm) * (double)(tn * bm);
         const int64_t min_tiles = bm == 256 ? kNumCUs * 3 / 4 : kNumCUs;
         if (tm * tn >= min_tiles && useful >= 0.75 * padded) {
-            if (const GemmConfig* c = tile_with(kind, bm, tm * tn, fa, fb)) return c;
+            if (const GemmConfig* c = tile_with(kind, bm, M, N, fa, fb)) return c;
         }
     }
-    return tile_with(kind, 64, 0, fa, fb);
+    return tile_with(kind, 64, M, N, fa, fb);
 }
 
 const GemmConfig* select_config_exact(int out_dtype, int64_t M, int64_t N, int64_t K, int fa, int fb, int bt) {
@@ -243,7 +252,7 @@ SplitPlan plan_splitk(int kind, int out_dtype, int64_t M, int64_t N, int64_t K, 
         // M = 8 23.3 us vs 53.3 us plain), except the FP16 M = 1 decode,
         // whose plain streaming kernel (21.5 us) beats every split tried.
         if (kind == KIND_F16 && M == 1) return p;
-        if (const GemmConfig* t = tile_with(kind, 64, 0, fa, fb)) c = t;
+        if (const GemmConfig* t = tile_with(kind, 64, M, N, fa, fb)) c = t;
     }
     if (c->kgran <= 0) return p;
     const int64_t base = c->family == 1 ? (N + c->bn - 1) / c->bn : ((M + c->bm - 1) / c->bm) * ((N + c->bn - 1) / c->bn);

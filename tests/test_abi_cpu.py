@@ -288,8 +288,15 @@ def test_select_config_rules():
     assert sel(g.KIND_F16, g.OUT_F16, 4096, 4096, 4096) == "pp_f16_256x256x32"
     assert sel(g.KIND_FP8, g.OUT_F16, 16384, 12288, 4096) == "pp_fp8_256x256x64"
     assert sel(g.KIND_F16, g.OUT_F16, 8192, 8192, 8192) == "pp_f16_256x256x32"
-    # M = 3000 gives 192 tiles of 256, 3/4 of the CUs: still 256x256 tiles
-    assert sel(g.KIND_FP8, g.OUT_E4M3, 3000, 4096, 4096) == "pp_fp8_256x256x64"
+    # M = 3000 gives 192 tiles of 256 rows (a quarter of the CUs idle) but
+    # 16 x 16 = 256 tiles of 192 rows: the 192-row ping-pong tiles, for both
+    # layouts and FP16 too; 6000 likewise (two rounds of 192 rows, not of 256)
+    assert sel(g.KIND_FP8, g.OUT_E4M3, 3000, 4096, 4096) == "pp_fp8_192x256x64"
+    assert g.select_config_bt(g.KIND_FP8, g.OUT_E4M3, 3000, 4096, 4096) == "pp_fp8_192x256x64_bt"
+    assert sel(g.KIND_F16, g.OUT_F16, 3000, 4096, 4096) == "pp_f16_192x256x32"
+    assert sel(g.KIND_FP8, g.OUT_E4M3, 6000, 4096, 4096) == "pp_fp8_192x256x64"
+    # where 192-row tiles need as many rounds of more tiles, 256 rows stay
+    assert sel(g.KIND_FP8, g.OUT_E4M3, 4000, 4096, 4096) == "pp_fp8_256x256x64"
     # 2048^2: 64 tiles of 256, 256 of 128
     assert sel(g.KIND_FP8, g.OUT_E4M3, 2048, 2048, 4096).startswith("tile_fp8_128x128")
     # small problems take the smallest tile
@@ -357,7 +364,7 @@ def test_kmajor_selector():
     assert g.select_config_bt(g.KIND_FP8, g.OUT_E4M3, 3, 4096, 4096) == "gemv_coop_fp8_m4_r4_w4"
     assert g.select_config_bt(g.KIND_FP8, g.OUT_E4M3, 8, 4096, 4096) == "gemv_coop_fp8_m8_r2_w4"
     assert g.select_config_bt(g.KIND_FP8, g.OUT_E4M3, 4096, 4096, 4096) == "pp_fp8_256x256x64_bt"
-    assert g.select_config_bt(g.KIND_FP8, g.OUT_E4M3, 3000, 4096, 4096) == "pp_fp8_256x256x64_bt"
+    assert g.select_config_bt(g.KIND_FP8, g.OUT_E4M3, 3000, 4096, 4096) == "pp_fp8_192x256x64_bt"
     assert g.select_config_bt(g.KIND_F16, g.OUT_F16, 4096, 4096, 4096) == "pp_f16_256x256x32_bt"
     assert g.select_config_bt(g.KIND_FP8, g.OUT_F32, 1024, 1024, 1024) == "tile_fp8_64x64x128_w2x2_bt"
     assert g.select_config_bt(g.KIND_FP8, g.OUT_F32, 65, 4096, 4096) == "ring_fp8_32x64x128_bt"
@@ -365,7 +372,7 @@ def test_kmajor_selector():
     # the row-major selector never returns a K-major configuration, nor the reverse
     assert not g.select_config(g.KIND_FP8, g.OUT_F32, 4096, 4096, 4096).endswith("_bt")
     assert g.select_config(g.KIND_F16, g.OUT_F16, 1, 12288, 4096).startswith("stream_")
-    assert g.select_config(g.KIND_FP8, g.OUT_F32, 3000, 4096, 4096) == "pp_fp8_256x256x64"
+    assert g.select_config(g.KIND_FP8, g.OUT_F32, 3000, 4096, 4096) == "pp_fp8_192x256x64"
 
 
 def test_kmajor_splitk_plan_and_validation(monkeypatch):

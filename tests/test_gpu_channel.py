@@ -126,6 +126,7 @@ SHAPES_GEMM = [(None, 1, 1000, 512), (None, 4, 520, 640), ("tile_fp8_64x64x128_w
                ("tile_fp8_128x128x128_w2x2", 300, 272, 384), ("tile_fp8_256x256x128_w2x4", 257, 512, 320),
                ("dma_fp8_256x256x64_s4", 300, 272, 192), ("dma_fp8_256x256x64_s5", 513, 784, 192),
                ("pp_fp8_256x256x64", 300, 272, 192), ("pp_fp8_256x256x64", 512, 768, 320),
+               ("pp_fp8_192x256x64", 400, 520, 320),
                ("ring_fp8_32x64x128", 70, 200, 2048), ("ring_fp8_64x64x128", 129, 264, 640)]
 
 

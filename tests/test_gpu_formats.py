@@ -114,6 +114,7 @@ PAIRS = [(g.FMT_E4M3, g.FMT_E4M3), (g.FMT_E4M3, g.FMT_E5M2), (g.FMT_E5M2, g.FMT_
 SHAPES = [(None, 1, 1000, 512), (None, 4, 520, 640), ("tile_fp8_64x64x128_w2x2", 100, 200, 256),
           ("tile_fp8_128x128x128_w2x2", 300, 272, 384), ("tile_fp8_256x256x128_w2x4", 257, 512, 320),
           ("dma_fp8_256x256x64_s4", 300, 272, 192), ("pp_fp8_256x256x64", 300, 272, 192),
+          ("pp_fp8_192x256x64", 400, 272, 192),
           ("ring_fp8_32x64x128", 70, 200, 2048), ("ring_fp8_16x64x128", 9, 136, 384)]
 
 

@@ -48,10 +48,10 @@ def scalar(v):
     return torch.tensor([float(np.float32(v))], dtype=torch.float32, device=DEV)
 
 
-FP8_CONFIGS = ["pp_fp8_256x256x64", "dma_fp8_256x256x64_s4", "dma_fp8_256x256x64_s5", "tile_fp8_256x256x128_w2x4",
+FP8_CONFIGS = ["pp_fp8_256x256x64", "pp_fp8_192x256x64", "dma_fp8_256x256x64_s4", "dma_fp8_256x256x64_s5", "tile_fp8_256x256x128_w2x4",
                "tile_fp8_128x128x128_w2x2", "tile_fp8_64x64x128_w2x2", "ring_fp8_16x16x128", "ring_fp8_32x32x128",
                "ring_fp8_64x64x128"]
-F16_CONFIGS = ["pp_f16_256x256x32", "dma_f16_256x256x32_s4", "dma_f16_256x256x32_s5", "tile_f16_256x256x64_w2x4",
+F16_CONFIGS = ["pp_f16_256x256x32", "pp_f16_192x256x32", "dma_f16_256x256x32_s4", "dma_f16_256x256x32_s5", "tile_f16_256x256x64_w2x4",
                "tile_f16_128x128x64_w2x2", "tile_f16_64x64x64_w2x2", "ring_f16_16x16x64", "ring_f16_32x32x64",
                "ring_f16_64x64x64"]
 
@@ -154,6 +154,7 @@ def test_ring_config_long_k(cfg, monkeypatch):
 
 @pytest.mark.parametrize("kind,cfg", [("fp8", "dma_fp8_256x256x64_s4"), ("f16", "dma_f16_256x256x32_s4"),
                                       ("fp8", "pp_fp8_256x256x64"), ("f16", "pp_f16_256x256x32"),
+                                      ("fp8", "pp_fp8_192x256x64"), ("f16", "pp_f16_192x256x32"),
                                       ("fp8", "ring_fp8_32x64x128"), ("f16", "ring_f16_32x64x64")])
 def test_direct_load_kernel_offset_operands(kind, cfg, monkeypatch):
     """Operands starting 16 bytes into an allocation (aligned) and 2 bytes in

@@ -289,9 +289,9 @@ def test_gemm_fp8_bt_4096_against_oracle_and_deterministic():
 
 # ----------------------------------------- every K-major configuration forced
 
-FP8_BT_CONFIGS = ["pp_fp8_256x256x64_bt", "dma_fp8_256x256x64_s4_bt", "tile_fp8_256x256x128_w2x4_bt", "tile_fp8_128x128x128_w2x2_bt",
+FP8_BT_CONFIGS = ["pp_fp8_256x256x64_bt", "pp_fp8_192x256x64_bt", "dma_fp8_256x256x64_s4_bt", "tile_fp8_256x256x128_w2x4_bt", "tile_fp8_128x128x128_w2x2_bt",
                   "tile_fp8_64x64x128_w2x2_bt", "ring_fp8_16x16x128_bt", "ring_fp8_32x32x128_bt", "ring_fp8_64x64x128_bt"]
-F16_BT_CONFIGS = ["pp_f16_256x256x32_bt", "dma_f16_256x256x32_s4_bt", "tile_f16_256x256x64_w2x4_bt", "tile_f16_128x128x64_w2x2_bt",
+F16_BT_CONFIGS = ["pp_f16_256x256x32_bt", "pp_f16_192x256x32_bt", "dma_f16_256x256x32_s4_bt", "tile_f16_256x256x64_w2x4_bt", "tile_f16_128x128x64_w2x2_bt",
                   "tile_f16_64x64x64_w2x2_bt", "ring_f16_16x16x64_bt", "ring_f16_32x32x64_bt", "ring_f16_64x64x64_bt"]
 # full tiles; M/N edges with a K tail; odd K tile counts; a single partial K
 # tile; K not a multiple of 16 bytes (element loads / the register-staged kernel)
@@ -332,7 +332,7 @@ def test_f16_bt_config_parity(cfg, monkeypatch):
         check_f16(run_f16_bt(a16, b16, g.OUT_F16), R, S, what=f"{cfg} f16 {M}x{N}x{K}")
 
 
-@pytest.mark.parametrize("kind,family", [("fp8", "dma"), ("f16", "dma"), ("fp8", "pp"), ("f16", "pp"), ("fp8", "ring"),
+@pytest.mark.parametrize("kind,family", [("fp8", "dma"), ("f16", "dma"), ("fp8", "pp"), ("f16", "pp"), ("fp8", "pp192"), ("f16", "pp192"), ("fp8", "ring"),
                                          ("f16", "ring")])
 def test_dma_bt_matches_row_major_dma_bitwise(kind, family, monkeypatch):
     """The direct-load, ping-pong and deep-ring kernels with K-major B and with
@@ -347,6 +347,7 @@ def test_dma_bt_matches_row_major_dma_bitwise(kind, family, monkeypatch):
         run = lambda bb, c, bt: (g.gemm_fp8_scaled_bt if bt else g.gemm_fp8_scaled)(a, bb, s, s, c)  # noqa: E731
         names = {"dma": ("dma_fp8_256x256x64_s4", "dma_fp8_256x256x64_s4_bt"),
                  "pp": ("pp_fp8_256x256x64", "pp_fp8_256x256x64_bt"),
+                 "pp192": ("pp_fp8_192x256x64", "pp_fp8_192x256x64_bt"),
                  "ring": ("ring_fp8_64x64x128", "ring_fp8_64x64x128_bt")}[family]
     else:
         a = dev(wl.random_f16((M, K), 5))
@@ -354,6 +355,7 @@ def test_dma_bt_matches_row_major_dma_bitwise(kind, family, monkeypatch):
         run = lambda bb, c, bt: (g.gemm_f16_bt if bt else g.gemm_f16)(a, bb, c)  # noqa: E731
         names = {"dma": ("dma_f16_256x256x32_s4", "dma_f16_256x256x32_s4_bt"),
                  "pp": ("pp_f16_256x256x32", "pp_f16_256x256x32_bt"),
+                 "pp192": ("pp_f16_192x256x32", "pp_f16_192x256x32_bt"),
                  "ring": ("ring_f16_64x64x64", "ring_f16_64x64x64_bt")}[family]
     c1 = torch.empty(M, N, device=DEV, dtype=torch.float32)
     c2 = torch.empty_like(c1)
