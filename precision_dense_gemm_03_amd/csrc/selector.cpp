@@ -40,7 +40,11 @@ namespace libgemm {
 namespace {
 
 constexpr int64_t kNumCUs = 256;
-constexpr int64_t kStreamMaxM = 4;
+constexpr int64_t kStreamMaxM = 4;      // the exact mode's FP32-FMA decode kernels
+// FP16 on row-major B streams only at M = 1: [M,4096]x[4096,12288] with a cold
+// weight, M = 1: 21.5 us streaming against 23.1 us on the deep-ring kernel;
+// M = 2 / 4: 29.8 / 31.8 us streaming against 23.3 us.
+constexpr int64_t kStreamF16MaxM = 1;
 constexpr int64_t kGemvMaxM = 8;
 constexpr int64_t kSplitMaxM = 256;
 constexpr int64_t kRingMaxM = 256;
@@ -163,10 +167,10 @@ const GemmConfig* select_config(int kind, int out_dtype, int64_t M, int64_t N, i
         }
         return tile_with(kind, 64, M, N, fa, fb, 1);
     }
-    // FP16 decode shapes stream B once through FMA sums; FP8 ones take the
-    // deep-ring kernel below (E4M3 [1,4096]x[4096,4096], cold weight: 17.2 us
-    // against 19.3 us streaming).
-    if (M <= kStreamMaxM && kind == KIND_F16) {
+    // The FP16 M = 1 decode streams B once through FMA sums; larger M and FP8
+    // take the deep-ring kernel below (E4M3 [1,4096]x[4096,4096], cold weight:
+    // 17.2 us against 19.3 us streaming).
+    if (M <= kStreamF16MaxM && kind == KIND_F16) {
         const GemmConfig* best = nullptr;
         int ns = 0;
         const GemmConfig* st = stream_configs(&ns);

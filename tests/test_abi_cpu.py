@@ -148,12 +148,14 @@ def test_channel_entry_points_argument_validation():
 
 def test_splitk_plan_rules(monkeypatch):
     plan = g.splitk_plan
-    # decode shapes split over 64x64 tiles, K cut until >= 512 workgroups;
-    # the FP16 M = 1 decode keeps its plain streaming kernel
+    # FP8 decode shapes split over 64x64 tiles, K cut until >= 512
+    # workgroups; the FP16 M = 1 decode keeps its plain streaming kernel and
+    # FP16 from M = 2 the deep-ring kernel (23.3 us at M = 4, level with the
+    # split, in one launch)
     assert plan(g.KIND_FP8, g.OUT_E4M3, 1, 4096, 4096) == ("tile_fp8_64x64x128_w2x2", 8, 8 * 4096 * 4)
     assert plan(g.KIND_FP8, g.OUT_E4M3, 4, 4096, 4096) == ("tile_fp8_64x64x128_w2x2", 8, 8 * 4 * 4096 * 4)
     assert plan(g.KIND_F16, g.OUT_F16, 1, 12288, 4096) == ("stream_f16_m1_c64_t512", 1, 0)
-    assert plan(g.KIND_F16, g.OUT_F16, 4, 12288, 4096) == ("tile_f16_64x64x64_w2x2", 4, 4 * 4 * 12288 * 4)
+    assert plan(g.KIND_F16, g.OUT_F16, 4, 12288, 4096) == ("ring_f16_16x64x64", 1, 0)
     # FP8, row-major B, M <= 64: split 64x64 tiles; above (and FP16) the
     # deep-ring kernel over all of K, no workspace; its tile minimises
     # (bm + bn) times the rounds of workgroups per compute unit
@@ -194,7 +196,7 @@ def test_splitk_plan_overrides(monkeypatch):
     assert g.splitk_plan(g.KIND_FP8, g.OUT_F32, 65, 4096, 4096)[1:] == (1, 0)
 
 
-def test_splitk_argument_validation():
+def test_splitk_argument_validation(monkeypatch):
     L = g.lib()
     s = FAKE3 + (1 << 24)
     W = 5 << 40
@@ -207,9 +209,13 @@ def test_splitk_argument_validation():
     assert L.gemm_fp8_splitk(*args, FAKE + 4 * 4096 - 16, need, None) == -8   # covers the end of A
     assert L.gemm_fp8_splitk(FAKE, 0, FAKE2, 0, s, s + 4, None, FAKE3, 2, 4, 4096, 4096, W, need, None) == -4
     assert L.gemm_fp8_splitk(FAKE, 0, FAKE2, 7, s, s + 4, None, FAKE3, 0, 4, 4096, 4096, W, need, None) == -3
+    # the FP16 M = 4 decode does not split by itself (deep-ring kernel); forced
+    # onto 64x64 tiles it takes 4 ranges
+    monkeypatch.setenv("LIBGEMM_CONFIG", "tile_f16_64x64x64_w2x2")
     assert L.gemm_f16_splitk(FAKE, FAKE2, FAKE3, 1, 4, 12288, 4096, W, 4 * 4 * 12288 * 4 - 4, None) == -9
-    assert L.gemm_f16_splitk(FAKE, FAKE2, FAKE3, 2, 1, 12288, 4096, W, 1 << 30, None) == -3
     assert L.gemm_f16_splitk(FAKE, FAKE2, FAKE3, 1, 4, 12288, 4096, FAKE2 + 64, 1 << 30, None) == -8   # inside B
+    monkeypatch.delenv("LIBGEMM_CONFIG")
+    assert L.gemm_f16_splitk(FAKE, FAKE2, FAKE3, 2, 1, 12288, 4096, W, 1 << 30, None) == -3
     assert L.gemm_splitk_plan(5, 0, 1, 1, 1, 0, 0, None, 0, None, None) == -3
     assert L.gemm_splitk_plan(1, 0, 1, -1, 1, 0, 0, None, 0, None, None) == -2
     assert L.gemm_splitk_plan(1, 0, 1, 1, 1, 0, 0, None, 0, None, None) == 0   # every output may be NULL
@@ -275,8 +281,9 @@ def test_select_config_rules():
     sel = g.select_config
     # decode shapes go to the streaming kernel sized for M
     assert sel(g.KIND_F16, g.OUT_F16, 1, 12288, 4096).startswith("stream_f16_m1_")
-    assert sel(g.KIND_F16, g.OUT_F16, 4, 12288, 4096).startswith("stream_f16_m4_")
-    # from M = 5 the deep-ring MFMA kernel reads the weight faster than streaming
+    # from M = 2 the deep-ring MFMA kernel reads the weight faster than streaming
+    assert sel(g.KIND_F16, g.OUT_F16, 2, 12288, 4096) == "ring_f16_16x64x64"
+    assert sel(g.KIND_F16, g.OUT_F16, 4, 12288, 4096) == "ring_f16_16x64x64"
     assert sel(g.KIND_F16, g.OUT_F16, 16, 12288, 4096) == "ring_f16_16x64x64"
     assert sel(g.KIND_F16, g.OUT_F16, 5, 12288, 4096) == "ring_f16_16x64x64"
     # FP8 decode shapes on row-major B take the deep-ring kernel
