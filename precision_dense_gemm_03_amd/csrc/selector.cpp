@@ -45,7 +45,12 @@ constexpr int64_t kStreamMaxM = 4;      // the exact mode's FP32-FMA decode kern
 // weight, M = 1: 21.5 us streaming against 23.1 us on the deep-ring kernel;
 // M = 2 / 4: 29.8 / 31.8 us streaming against 23.3 us.
 constexpr int64_t kStreamF16MaxM = 1;
-constexpr int64_t kGemvMaxM = 8;
+constexpr int64_t kGemvMaxM = 8;        // the exact mode's FP32-FMA K-major decode kernels
+// K-major B, plain calls: the dot-product decode kernels up to M = 1 (FP16) or
+// M = 4 (FP8), the deep-ring kernel beyond. Cold weight, us: FP16
+// [M,4096]x[4096,12288] M = 1 16.3 vs 20.7, M = 2 / 4 / 8 21.5 / 24.8 / 36.7
+// vs 20.3-20.4; FP8 [M,4096]x[4096,4096] M = 4 10.7 vs 11.1, M = 8 15.6 vs 10.5.
+constexpr int64_t kGemvF16MaxM = 1, kGemvFp8MaxM = 4;
 constexpr int64_t kSplitMaxM = 256;
 constexpr int64_t kRingMaxM = 256;
 
@@ -140,10 +145,10 @@ const GemmConfig* select_config(int kind, int out_dtype, int64_t M, int64_t N, i
         if (const GemmConfig* c = find_named(env, kind, M, fa, fb, bt)) return c;
     }
     if (bt) {
-        // K-major B: decode shapes (M <= 8) read each weight row once as a dot
-        // product (no transposition, no split of K across workgroups); the
-        // first table entry of the smallest bound >= M is taken.
-        if (M <= kGemvMaxM) {
+        // K-major B: decode shapes read each weight row once as a dot product
+        // (no transposition, no split of K across workgroups); the first table
+        // entry of the smallest bound >= M is taken.
+        if (M <= (kind == KIND_F16 ? kGemvF16MaxM : kGemvFp8MaxM)) {
             int nv = 0;
             const GemmConfig* vt = gemv_kmajor_configs(&nv);
             const GemmConfig* best = nullptr;

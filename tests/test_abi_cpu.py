@@ -359,17 +359,19 @@ def test_kmajor_entry_points_argument_validation():
 
 
 def test_kmajor_selector():
-    """K-major B: decode shapes (M <= 8) take the dot-product decode kernels,
-    M <= 256 the deep-ring kernel, larger M the K-major tile kernels, by the
-    tile rules of row-major B (a 256x256 grid already from 3/4 of the CUs)."""
+    """K-major B: decode shapes take the dot-product decode kernels (FP16 at
+    M = 1, FP8 up to M = 4), the rest up to M = 256 the deep-ring kernel,
+    larger M the K-major tile kernels, by the tile rules of row-major B (a
+    256x256 grid already from 3/4 of the CUs)."""
     assert g.select_config_bt(g.KIND_F16, g.OUT_F16, 1, 12288, 4096) == "gemv_coop_f16_m1_r4_w8"
-    assert g.select_config_bt(g.KIND_F16, g.OUT_F16, 2, 12288, 4096) == "gemv_bt_f16_m4_r2_u4"
-    assert g.select_config_bt(g.KIND_F16, g.OUT_F16, 4, 12288, 4096) == "gemv_bt_f16_m4_r2_u4"
-    assert g.select_config_bt(g.KIND_F16, g.OUT_F16, 8, 12288, 4096) == "gemv_bt_f16_m8_r4_u2"
+    assert g.select_config_bt(g.KIND_F16, g.OUT_F16, 2, 12288, 4096) == "ring_f16_16x64x64_bt"
+    assert g.select_config_bt(g.KIND_F16, g.OUT_F16, 4, 12288, 4096) == "ring_f16_16x64x64_bt"
+    assert g.select_config_bt(g.KIND_F16, g.OUT_F16, 8, 12288, 4096) == "ring_f16_16x64x64_bt"
     assert g.select_config_bt(g.KIND_F16, g.OUT_F16, 9, 12288, 4096) == "ring_f16_16x64x64_bt"
     assert g.select_config_bt(g.KIND_FP8, g.OUT_E4M3, 1, 4096, 4096) == "gemv_bt_fp8_m1_r1_u4"
     assert g.select_config_bt(g.KIND_FP8, g.OUT_E4M3, 3, 4096, 4096) == "gemv_coop_fp8_m4_r4_w4"
-    assert g.select_config_bt(g.KIND_FP8, g.OUT_E4M3, 8, 4096, 4096) == "gemv_coop_fp8_m8_r2_w4"
+    assert g.select_config_bt(g.KIND_FP8, g.OUT_E4M3, 4, 4096, 4096) == "gemv_coop_fp8_m4_r4_w4"
+    assert g.select_config_bt(g.KIND_FP8, g.OUT_E4M3, 8, 4096, 4096) == "ring_fp8_16x16x128_bt"
     assert g.select_config_bt(g.KIND_FP8, g.OUT_E4M3, 4096, 4096, 4096) == "pp_fp8_256x256x64_bt"
     assert g.select_config_bt(g.KIND_FP8, g.OUT_E4M3, 3000, 4096, 4096) == "pp_fp8_192x256x64_bt"
     assert g.select_config_bt(g.KIND_F16, g.OUT_F16, 4096, 4096, 4096) == "pp_f16_256x256x32_bt"
@@ -387,7 +389,8 @@ def test_kmajor_splitk_plan_and_validation(monkeypatch):
     the deep-ring kernel (no split); a forced 64x64 tile splits like row-major
     B; workspace errors come before any launch."""
     assert g.splitk_plan_bt(g.KIND_FP8, g.OUT_E4M3, 1, 4096, 4096) == ("gemv_bt_fp8_m1_r1_u4", 1, 0)
-    assert g.splitk_plan_bt(g.KIND_F16, g.OUT_F16, 4, 12288, 4096) == ("gemv_bt_f16_m4_r2_u4", 1, 0)
+    assert g.splitk_plan_bt(g.KIND_FP8, g.OUT_E4M3, 4, 4096, 4096) == ("gemv_coop_fp8_m4_r4_w4", 1, 0)
+    assert g.splitk_plan_bt(g.KIND_F16, g.OUT_F16, 4, 12288, 4096) == ("ring_f16_16x64x64_bt", 1, 0)
     assert g.splitk_plan_bt(g.KIND_FP8, g.OUT_E4M3, 65, 4096, 4096) == ("ring_fp8_32x64x128_bt", 1, 0)
     assert g.splitk_plan_bt(g.KIND_F16, g.OUT_F16, 16, 12288, 4096) == ("ring_f16_16x64x64_bt", 1, 0)
     assert g.splitk_plan_bt(g.KIND_FP8, g.OUT_F32, 300, 4096, 4096)[1] == 1
