@@ -23,6 +23,12 @@ typedef float v16f __attribute__((ext_vector_type(16)));
 
 enum OutDtype { OUT_F32 = 0, OUT_F16 = 1, OUT_E4M3 = 2, OUT_E5M2 = 3 };
 
+// A compile-time flag passed as a value (for generic lambdas).
+template <bool B>
+struct BoolC {
+    static constexpr bool value = B;
+};
+
 // FP8 element formats (operands and quantize): OCP E4M3 ("FN") and OCP E5M2.
 enum Fp8Format { FMT_E4M3 = 0, FMT_E5M2 = 1 };
 

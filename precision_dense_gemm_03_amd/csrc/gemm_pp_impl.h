@@ -463,16 +463,28 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
         }
         return y;
     };
+    // The same without per-channel factors (the per-tensor case, decided once
+    // for the whole block rather than per run).
+    auto plain4 = [&](int i, int j, int q) __attribute__((always_inline)) -> v4f {
+        v4f y;
+#pragma unroll
+        for (int e = 0; e < 4; ++e) y[e] = acc[i][j][4 * q + e] * scale;
+        return y;
+    };
     if constexpr (OUT == OUT_F32) {
         float* Cf = reinterpret_cast<float*>(C);
+        auto store_all = [&](auto val4) __attribute__((always_inline)) {
 #pragma unroll
-        for (int i = 0; i < T::MI; ++i)
+            for (int i = 0; i < T::MI; ++i)
 #pragma unroll
-            for (int j = 0; j < 2; ++j)
+                for (int j = 0; j < 2; ++j)
 #pragma unroll
-                for (int q = 0; q < 4; ++q)
-                    *reinterpret_cast<v4f*>(Cf + (int64_t)(m0 + row_t + 32 * i) * N + n0 + col_t + 32 * j + 8 * q) =
-                        run4(i, j, q);
+                    for (int q = 0; q < 4; ++q)
+                        *reinterpret_cast<v4f*>(Cf + (int64_t)(m0 + row_t + 32 * i) * N + n0 + col_t + 32 * j +
+                                                8 * q) = val4(i, j, q);
+        };
+        if (chan) store_all(run4);
+        else store_all(plain4);
         return;
     }
     // FP8 / FP16: the wave's 32 MI x 64 block goes to its own LDS stage array
@@ -488,25 +500,81 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
     };
     static_assert(32 * T::MI * RB <= T::A_STAGE, "a wave's staged block fits in one LDS stage");
     LDS_AS uint8_t* ep = wave < 4 ? stage_a(wave) : stage_b(wave - 4);
+    auto slot = [&](int i, int j, int q) __attribute__((always_inline)) -> int {
+        const int r = 32 * i + lr, cb = (32 * j + 8 * q + 4 * h) * (RB / 64);
+        return r * RB + ((((cb >> 4) ^ esw(r)) << 4) | (cb & 15));
+    };
+    if constexpr (OUT == OUT_F16) {
+        auto stage_all = [&](auto val4) __attribute__((always_inline)) {
 #pragma unroll
-    for (int i = 0; i < T::MI; ++i)
+            for (int i = 0; i < T::MI; ++i)
 #pragma unroll
-        for (int j = 0; j < 2; ++j)
+                for (int j = 0; j < 2; ++j)
 #pragma unroll
-            for (int q = 0; q < 4; ++q) {
-                const v4f y = run4(i, j, q);
-                const int r = 32 * i + lr, cb = (32 * j + 8 * q + 4 * h) * (RB / 64);
-                const int off = r * RB + ((((cb >> 4) ^ esw(r)) << 4) | (cb & 15));
-                if constexpr (OUT == OUT_F16) {
-                    typedef _Float16 v4hh __attribute__((ext_vector_type(4)));
-                    const v4hh hv = {(_Float16)y[0], (_Float16)y[1], (_Float16)y[2], (_Float16)y[3]};
-                    *(LDS_AS v2i*)(ep + off) = __builtin_bit_cast(v2i, hv);
-                } else {
-                    const uint32_t w = (eflags & EPI_E5M2) ? e5m2_pack4(y[0], y[1], y[2], y[3])
-                                                          : e4m3_pack4(y[0], y[1], y[2], y[3]);
-                    *(LDS_AS uint32_t*)(ep + off) = w;
-                }
-            }
+                    for (int q = 0; q < 4; ++q) {
+                        const v4f y = val4(i, j, q);
+                        typedef _Float16 v4hh __attribute__((ext_vector_type(4)));
+                        const v4hh hv = {(_Float16)y[0], (_Float16)y[1], (_Float16)y[2], (_Float16)y[3]};
+                        *(LDS_AS v2i*)(ep + slot(i, j, q)) = __builtin_bit_cast(v2i, hv);
+                    }
+        };
+        if (chan) stage_all(run4);
+        else stage_all(plain4);
+    } else {
+        // FP8 codes. Per-tensor blocks take a short path: the clamp to the
+        // format's largest finite value is one median-of-three (as the
+        // fmin/fmax pair of the code functions, for every value but NaN), and
+        // NaN is only detected, one unordered compare per pair; a wave that
+        // met one writes its block again with the code functions, which map
+        // NaN to 0x7F. Per-channel blocks take the code functions directly.
+        bool exact = chan;
+        if (!chan) {
+            bool nan = false;
+            auto stage_fast = [&](auto fmt) __attribute__((always_inline)) {
+                constexpr bool E5 = decltype(fmt)::value;
+                constexpr float hi = E5 ? 57344.0f : 448.0f;
+#pragma unroll
+                for (int i = 0; i < T::MI; ++i)
+#pragma unroll
+                    for (int j = 0; j < 2; ++j)
+#pragma unroll
+                        for (int q = 0; q < 4; ++q) {
+                            const v4f y = plain4(i, j, q);
+                            nan |= __builtin_isunordered(y[0], y[1]) | __builtin_isunordered(y[2], y[3]);
+                            float c[4];
+#pragma unroll
+                            for (int e = 0; e < 4; ++e) c[e] = __builtin_amdgcn_fmed3f(y[e], -hi, hi);
+                            // the first conversion's upper half is overwritten by
+                            // the second, so any register serves as its old value
+                            uint32_t w = __builtin_bit_cast(uint32_t, c[3]);
+                            if constexpr (E5) {
+                                w = (uint32_t)__builtin_amdgcn_cvt_pk_bf8_f32(c[0], c[1], (int)w, false);
+                                w = (uint32_t)__builtin_amdgcn_cvt_pk_bf8_f32(c[2], c[3], (int)w, true);
+                            } else {
+                                w = (uint32_t)__builtin_amdgcn_cvt_pk_fp8_f32(c[0], c[1], (int)w, false);
+                                w = (uint32_t)__builtin_amdgcn_cvt_pk_fp8_f32(c[2], c[3], (int)w, true);
+                            }
+                            *(LDS_AS uint32_t*)(ep + slot(i, j, q)) = w;
+                        }
+            };
+            if (eflags & EPI_E5M2) stage_fast(BoolC<true>{});
+            else stage_fast(BoolC<false>{});
+            exact = __builtin_amdgcn_ballot_w64(nan) != 0;
+        }
+        if (exact) {
+#pragma unroll
+            for (int i = 0; i < T::MI; ++i)
+#pragma unroll
+                for (int j = 0; j < 2; ++j)
+#pragma unroll
+                    for (int q = 0; q < 4; ++q) {
+                        const v4f y = run4(i, j, q);
+                        const uint32_t w = (eflags & EPI_E5M2) ? e5m2_pack4(y[0], y[1], y[2], y[3])
+                                                              : e4m3_pack4(y[0], y[1], y[2], y[3]);
+                        *(LDS_AS uint32_t*)(ep + slot(i, j, q)) = w;
+                    }
+        }
+    }
     __builtin_amdgcn_s_waitcnt(waitcnt_imm(63, 0));
     constexpr int LPR = RB / 16;             // lanes per block row
     constexpr int RPI = 64 / LPR;            // block rows per store instruction

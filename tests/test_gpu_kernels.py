@@ -19,6 +19,7 @@ from parity import check_e4m3, check_f16, check_f32, fp8_dot_allowance
 pytestmark = pytest.mark.gpu
 
 DEV = torch.device("cuda:0")
+ORC_FMT_OF = {g.FMT_E4M3: orc.FMT_E4M3, g.FMT_E5M2: orc.FMT_E5M2}
 
 
 def say(*a):
@@ -231,3 +232,38 @@ def test_stream_config_parity(cfg, bm, monkeypatch):
             C16 = torch.empty((M, N), dtype=torch.float16, device=DEV)
             g.gemm_f16(ta, tb, C16)
             check_f16(host(C16), R, S, what=f"{cfg} f16 M={M}")
+
+
+@pytest.mark.parametrize("cfg", ["pp_fp8_256x256x64", "pp_fp8_192x256x64"])
+@pytest.mark.parametrize("bt", [False, True])
+def test_pingpong_fp8_out_codes(cfg, bt, monkeypatch):
+    """FP8 outputs of the ping-pong kernel on interior tiles, code for code
+    against the oracle. The operands are small integers (every product and sum
+    is exact in FP32 and on the FP8 matrix cores), so the only rounding is the
+    output conversion: ties to even, saturation at the format's largest finite
+    value, zeros, and NaN from rows of A that hold the NaN code. Only the waves
+    whose rows hold NaN meet one, so both the per-tensor short path and the
+    exact code functions it falls back to are exercised in one launch."""
+    cfg_bt = cfg + ("_bt" if bt else "")
+    monkeypatch.setenv("LIBGEMM_CONFIG", cfg_bt)
+    M, N, K = 768, 512, 192       # whole tiles of 256 and of 192 rows; three K tiles
+    rng = np.random.default_rng(11)
+    ca = orc.e4m3_encode(rng.integers(-12, 13, (M, K)).astype(np.float64))
+    cb = orc.e4m3_encode(rng.integers(-12, 13, (K, N)).astype(np.float64))
+    for r, k in ((5, 17), (300, 0), (700, 191)):
+        ca[r, k] = 0x7F
+    R, _ = orc.gemm(orc.FMT_E4M3, ca, cb)
+    assert np.isnan(R[[5, 300, 700]]).all() and np.isfinite(np.delete(R, [5, 300, 700], axis=0)).all()
+    ta, tb = dev(ca), dev(np.ascontiguousarray(cb.T) if bt else cb)
+    one = scalar(1.0)
+    for fmt, s_out in ((g.FMT_E4M3, 4.0), (g.FMT_E5M2, 1.0 / 32)):
+        ref = orc.out_fp8(R, s_out, ORC_FMT_OF[fmt])
+        assert np.any(ref == (0x7E if fmt == g.FMT_E4M3 else 0x7B)), "saturation is covered"
+        C = torch.empty((M, N), dtype=torch.uint8, device=DEV)
+        say(f"{cfg_bt} fp8 out fmt {fmt} {M}x{N}x{K}")
+        call = g.gemm_fp8_scaled_bt if bt else g.gemm_fp8_scaled
+        call(ta, tb, one, one, C, scalar(s_out), out_fmt=fmt)
+        got = host(C)
+        bad = np.argwhere(got != ref)
+        assert bad.size == 0, f"{cfg_bt} fmt {fmt}: {len(bad)} codes differ, first at {bad[0]}: " \
+                              f"{got[tuple(bad[0])]:#x} vs {ref[tuple(bad[0])]:#x}"
