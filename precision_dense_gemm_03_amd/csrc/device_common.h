@@ -270,4 +270,19 @@ __device__ __forceinline__ void lds_b128x1_tr16x2(v4i& a, v4s (&t)[2], uint32_t 
 
 __device__ __forceinline__ uint32_t lds_addr(const LDS_AS void* p) { return (uint32_t)(uintptr_t)p; }
 
+// Raw buffer resource over `bytes` bytes from p (clamped to 2^31 - 1): 32-bit
+// per-lane and uniform offsets, and loads at or past the end read zero.
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t buffer_rsrc(const void* p, int64_t bytes) {
+    const int n = (int)(bytes < 0 ? 0 : (bytes > 0x7FFFFFFF ? 0x7FFFFFFF : bytes));
+    return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(p), (short)0, n, 0x00020000);
+}
+
+// 16-byte buffer load of each lane straight into LDS (lane i's bytes land at
+// dst + 16 i); voff per lane, soff uniform. (A plain function, so that kernel
+// templates never name the builtin with dependent arguments.)
+__device__ __forceinline__ void buffer_load_lds16(__amdgpu_buffer_rsrc_t rs, LDS_AS void* dst, uint32_t voff,
+                                                  uint32_t soff) {
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, dst, 16, voff, soff, 0, 0);
+}
+
 }  // namespace libgemm

@@ -20,25 +20,36 @@
 // phase, so that on every SIMD one wave issues MFMAs while the other moves
 // data:
 //   MEM(t): read this wave's operands of tile t from LDS into registers; issue
-//           this group's share of the direct global->LDS loads of tile t+3
-//           (group 0 loads A's tile, group 1 B's); wait until this wave's loads
-//           of tile t+1 have landed and its LDS reads are done; barrier.
+//           this group's share of the direct loads (group 0: at odd t, A's
+//           tiles t+3 and t+4; group 1: B's tile t+3); wait until this wave's
+//           loads of tile t+1 have landed and its LDS reads are done; barrier.
 //   MMA(t): the 8 (FP8) or 16 (FP16) MFMAs of tile t, at raised issue
 //           priority; barrier.
 // Group 1 enters the loop one barrier later than group 0, so the barrier that
-// ends one group's MMA phase ends the other group's MEM phase. The staging is
-// a ring of four LDS stages of 32 KiB (A 256 x 64 bytes + B 64 bytes x 256
-// n), loaded three tiles ahead (the double buffering of the FP8 guide §2.3,
-// deepened as the HGEMM article §3.2/§3.3 discusses). Every LDS stage is its
-// own LDS object, so the compiler can tell the in-flight direct loads from the
-// 16-byte operand reads of other stages and inserts no waits of its own for
-// them; the transpose reads of row-major B are asm groups (device_common.h),
-// since before a transpose-read builtin it would wait for every load in flight.
+// ends one group's MMA phase ends the other group's MEM phase. The staging
+// (the double buffering of the FP8 guide §2.3, deepened as the HGEMM article
+// §3.2/§3.3 discusses) is two rings filled by direct buffer->LDS loads:
+//   A: three regions of BM rows x 128 bytes, each holding two K tiles, so that
+//      every load reads whole 128-byte pieces of A's rows (a 64-byte piece
+//      costs the L1 a whole line as well); pairs are loaded two or three
+//      tiles before their first tile is read;
+//   B: four stages of one K tile (64 k-rows x 256 n, or 256 Bt rows x 64
+//      bytes), loaded three tiles ahead.
+// 160 KiB of LDS in all (136 KiB with 192-row tiles). Every region and stage
+// is its own LDS object, so the compiler can tell the in-flight direct loads
+// from the 16-byte operand reads of the others and inserts no waits of its
+// own for them; the transpose reads of row-major B are asm groups
+// (device_common.h), since before a transpose-read builtin it would wait for
+// every load in flight. The loads take 32-bit per-lane offsets and uniform
+// ones through buffer resources, which keeps the address registers few.
 //
 // LDS layouts are bank-conflict free for the 16-lane passes of 16-byte reads
 // (the DeepGEMM deep-dive §3.2 argues for a bank-aware layout; here it is an
 // XOR permutation, since a direct load fixes each lane's LDS slot):
-//   A and Bt rows (64 bytes = 4 chunks of 16): chunk c of row r lives in slot
+//   A region rows (128 bytes = 8 chunks of 16): chunk c of row r lives in
+//   slot c ^ swz8(r), so 16 consecutive rows read at one chunk cover all 16
+//   four-bank groups of two rows' 256 bytes;
+//   Bt rows (64 bytes = 4 chunks of 16): chunk c of row r lives in slot
 //   c ^ ((r >> 2) & 3), so 16 consecutive rows read at one chunk cover all 16
 //   four-bank groups;
 //   row-major B rows (256 or 512 bytes): chunk c of k-row r lives in slot
@@ -80,22 +91,24 @@ struct Pp {
     static constexpr int BM = BM_, BN = 256;
     static_assert(BM == 256 || BM == 192, "tile rows: 256 or 192");
     static constexpr int NT = 512;                  // 8 waves
-    static constexpr int S = 4;                     // LDS ring stages
+    static constexpr int S = 4;                     // B: LDS ring stages, one K tile each
+    static constexpr int AP = 3;                    // A: LDS regions, two K tiles each
     static constexpr int ROWB = 64;                 // bytes of every A row per K tile
     static constexpr int BK = ROWB / ES;            // k per K tile (64 FP8, 32 FP16)
     static constexpr int VE = 16 / ES;              // elements per 16-byte chunk
     static constexpr int MR = BM / 2;               // A rows of one group
     static constexpr int MI = BM / 64;              // 32-row blocks per wave
-    static constexpr int A_STAGE = BM * ROWB;       // A: BM rows x 64 B
+    static constexpr int A_STAGE = BM * ROWB;       // A of one K tile: BM rows x 64 B
+    static constexpr int A_PAIR = 2 * A_STAGE;      // A region: BM rows x 128 B (two K tiles)
     static constexpr int B_STAGE = 16384;           // B: 64 B of k x 256 n
     static constexpr int A_RPW = BM / 4;            // A rows one wave of group 0 loads
     static constexpr int BNB = BN * ES;             // row-major B: bytes of one k-row of the tile
     static constexpr int B_CPR = BNB / 16;          // chunks per row-major B row
     static constexpr int B_RPB = 1024 / BNB;        // row-major B rows per 1 KiB direct load
-    static constexpr int LA = A_STAGE / 4096;       // direct loads per wave per K tile, group 0 (A)
-    static constexpr int LB = B_STAGE / 4096;       // the same, group 1 (B)
+    static constexpr int LAP = A_RPW / 8;           // direct loads per wave per A region, group 0
+    static constexpr int LB = B_STAGE / 4096;       // direct loads per wave per B stage, group 1
     static constexpr int KSUB = ES == 1 ? 1 : 2;    // MFMA k-steps per K tile (64 or 2 x 16 values)
-    static_assert(S * (A_STAGE + B_STAGE) <= 160 * 1024, "the LDS ring must fit in 160 KiB");
+    static_assert(AP * A_PAIR + S * B_STAGE <= 160 * 1024, "the LDS rings must fit in 160 KiB");
 };
 
 // s_waitcnt vmcnt(NA) for a wave of group 0, vmcnt(NB) for group 1 (their
@@ -107,6 +120,11 @@ __device__ __forceinline__ void wait_vm(bool group0) {
 }
 
 __device__ __forceinline__ int swz_a(int r) { return (r >> 2) & 3; }
+
+// A region rows (128 bytes, 8 chunks): chunk c of row r lives in slot
+// c ^ swz8(r). Any 8 consecutive rows from a multiple of 8, and the even and
+// the odd rows of 16 from a multiple of 16, take 8 distinct values.
+__device__ __forceinline__ int swz8(int r) { return (r & 7) ^ ((r >> 3) & 1); }
 
 // Row-major B: k-row r's chunk c lives in slot c ^ swz_b(r). FP8 passes read 8
 // rows x 2 adjacent chunks, FP16 passes 4 rows x 4 adjacent chunks; the values
@@ -164,16 +182,15 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
     int tiles_n, int eflags, int vec_out) {
     using T = Pp<ES, BM>;
     using Op = typename Mfma<ES>::op;
-    __shared__ __attribute__((aligned(1024))) uint8_t a0[T::A_STAGE], a1[T::A_STAGE], a2[T::A_STAGE], a3[T::A_STAGE];
+    __shared__ __attribute__((aligned(1024))) uint8_t a0[T::A_PAIR], a1[T::A_PAIR], a2[T::A_PAIR];
     __shared__ __attribute__((aligned(1024))) uint8_t b0[T::B_STAGE], b1[T::B_STAGE], b2[T::B_STAGE], b3[T::B_STAGE];
-    // Stage selection; st is a compile-time constant wherever it matters
-    // (the main loop is unrolled by the ring size).
-    auto stage_a = [&](int st) __attribute__((always_inline)) -> LDS_AS uint8_t* {
-        switch (st) {
+    // Region and stage selection; the index is a compile-time constant wherever
+    // it matters (the main loop is unrolled by the ring periods).
+    auto region_a = [&](int r) __attribute__((always_inline)) -> LDS_AS uint8_t* {
+        switch (r) {
             case 0: return (LDS_AS uint8_t*)a0;
             case 1: return (LDS_AS uint8_t*)a1;
-            case 2: return (LDS_AS uint8_t*)a2;
-            default: return (LDS_AS uint8_t*)a3;
+            default: return (LDS_AS uint8_t*)a2;
         }
     };
     auto stage_b = [&](int st) __attribute__((always_inline)) -> LDS_AS uint8_t* {
@@ -193,61 +210,118 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
     const int m0 = tile_m * T::BM, n0 = tile_n * T::BN;
     const int nk = (K + T::BK - 1) / T::BK;
     const int nk_full = K / T::BK;
+    const int npf = nk_full / 2;            // K tile pairs whose two tiles are full
+    const int KE = K * ES;                  // bytes of one A (or Bt) row
 
-    // ---- this lane's direct-load slots: group 0 loads A, group 1 loads B ----
-    // Load i of wave j fills 1 KiB of its group's stage: A rows
-    // A_RPW j + 16 i + lane / 4 (i < LA) or Bt rows 64 j + 16 i + lane / 4
-    // (slot lane % 4), or row-major B rows B_RPB (4 j + i) + lane / B_CPR
-    // (slot lane % B_CPR).
-    const uint8_t* src = G == 0 ? A + (int64_t)m0 * K * ES
-                                : (BT ? B + (int64_t)n0 * K * ES : B + (int64_t)n0 * ES);
-    const int rpw = G == 0 ? T::A_RPW : 64;  // rows of A or Bt one wave loads
-    uint32_t goff[T::LB];
+    // ---- group 0: A in pairs of K tiles, as whole 128-byte row pieces ----
+    // Load i (< LAP) of wave j fills 1 KiB of a pair region: rows
+    // A_RPW j + 8 i + lane / 8, slot lane % 8, which holds chunk slot ^ swz8(row)
+    // of the row's 128 bytes (rows past M read the last row). The loads are
+    // buffer loads: a 32-bit per-lane offset (two values, for even and odd i,
+    // in interior tiles) and a uniform one.
+    const uint8_t* srcA = A + (int64_t)m0 * KE;
+    const int64_t a_end = (int64_t)M * KE, b_end = (int64_t)K * N * ES;
+    const int arow = T::A_RPW * wj + (lane >> 3);
+    const int cb_even = 16 * ((lane & 7) ^ (lane >> 3));   // chunk bytes where (row >> 3) is even
+    const int par0 = (T::A_RPW * wj / 8) & 1;             // parity of the wave's first 8-row block
+    const int mlast = M - 1 - m0;
+    const bool a_inner = m0 + T::BM <= M;
+    auto a_cb = [&](int i) __attribute__((always_inline)) -> int {
+        return ((i + par0) & 1) ? (cb_even ^ 16) : cb_even;
+    };
+    auto a_off = [&](int i) __attribute__((always_inline)) -> uint32_t {
+        return __umul24((uint32_t)min(arow + 8 * i, mlast), (uint32_t)KE) + (uint32_t)a_cb(i);
+    };
+    const uint32_t va[2] = {a_off(0), a_off(1)};          // interior tiles: rows arow, arow + 8
+    // One resource for the tile's rows of A; the pair's K offset is uniform.
+    const auto rsA = buffer_rsrc(srcA, a_end - (int64_t)m0 * KE);
+    auto issue_a_pair = [&](int p, int reg) __attribute__((always_inline)) {
+        const uint32_t kofs = (uint32_t)p * (2 * T::ROWB);
+        LDS_AS uint8_t* dst = region_a(reg) + T::A_RPW * wj * (2 * T::ROWB);
+        if (a_inner) {
 #pragma unroll
-    for (int i = 0; i < T::LB; ++i) {
-        if (G == 0 || BT) {
-            const int r = rpw * wj + 16 * i + (lane >> 2);
+            for (int i = 0; i < T::LAP; ++i)
+                buffer_load_lds16(rsA, (LDS_AS void*)(dst + i * 1024), va[i & 1],
+                                  kofs + (uint32_t)(16 * (i >> 1)) * (uint32_t)KE);
+        } else {
+#pragma unroll
+            for (int i = 0; i < T::LAP; ++i) buffer_load_lds16(rsA, (LDS_AS void*)(dst + i * 1024), a_off(i), kofs);
+        }
+    };
+    // A pair with a partial or missing tile: guarded vector loads, zero beyond
+    // K, ordinary LDS stores (waiting for them also waits for every direct load
+    // this wave has in flight).
+    auto issue_a_pair_guarded = [&](int p, int reg) __attribute__((always_inline)) {
+        const uint8_t* base = srcA + (int64_t)p * (2 * T::ROWB);
+        LDS_AS uint8_t* dst = region_a(reg) + T::A_RPW * wj * (2 * T::ROWB);
+#pragma unroll 1
+        for (int i = 0; i < T::LAP; ++i) {
+            const int k8 = (((i + par0) & 1) ? (cb_even ^ 16) : cb_even) >> 4;
+            v4u v = v4u{0u, 0u, 0u, 0u};
+            if ((p * 2 * T::ROWB + 16 * k8) / ES < K) v = *reinterpret_cast<const v4u*>(base + a_off(i));
+            *(LDS_AS v4u*)(dst + i * 1024 + lane * 16) = v;
+        }
+    };
+
+    // ---- group 1: B, one K tile per stage ----
+    // Load i of wave j fills 1 KiB of a B stage: Bt rows 64 j + 16 i + lane / 4
+    // (slot lane % 4), or row-major B rows B_RPB (4 j + i) + lane / B_CPR (slot
+    // lane % B_CPR). goff: the byte offset of load i within the K tile.
+    const uint8_t* srcB = BT ? B + (int64_t)n0 * KE : B + (int64_t)n0 * ES;
+    auto b_off = [&](int i) __attribute__((always_inline)) -> uint32_t {
+        if (BT) {
+            const int r = 64 * wj + 16 * i + (lane >> 2);
             const int c = (lane & 3) ^ swz_a(r);
-            const int rr = G == 0 ? min(m0 + r, M - 1) - m0 : min(n0 + r, N - 1) - n0;
-            goff[i] = (uint32_t)(rr * K * ES + c * 16);  // i >= LA of group 0: never used
+            const int rr = min(n0 + r, N - 1) - n0;
+            return (uint32_t)(rr * KE + c * 16);
         } else {
             const int r = T::B_RPB * (4 * wj + i) + lane / T::B_CPR;
             const int c = (lane % T::B_CPR) ^ swz_b<ES>(r);
             const int col = min(n0 + c * T::VE, N - T::VE) - n0;
-            goff[i] = (uint32_t)(r * N * ES + col * ES);
-        }
-    }
-    // Byte step of the source between K tiles.
-    const int64_t kstep = (G == 0 || BT) ? (int64_t)T::ROWB : (int64_t)T::BK * N * ES;
-
-    // Direct loads of full K tile kt into stage st.
-    auto issue_full = [&](int kt, int st) __attribute__((always_inline)) {
-        const uint8_t* p = src + (int64_t)kt * kstep;
-        if (G == 0) {
-            LDS_AS uint8_t* dst = stage_a(st) + wj * (T::A_RPW * T::ROWB);
-#pragma unroll
-            for (int i = 0; i < T::LA; ++i)
-                __builtin_amdgcn_global_load_lds((const void*)(p + goff[i]), (LDS_AS void*)(dst + i * 1024), 16, 0, 0);
-        } else {
-            LDS_AS uint8_t* dst = stage_b(st) + wj * 4096;
-#pragma unroll
-            for (int i = 0; i < T::LB; ++i)
-                __builtin_amdgcn_global_load_lds((const void*)(p + goff[i]), (LDS_AS void*)(dst + i * 1024), 16, 0, 0);
+            return (uint32_t)(r * N * ES + col * ES);
         }
     };
-    // The partial last K tile: the same slots, loaded with guards and zero
-    // beyond K, written with ordinary LDS stores (waiting for these loads also
-    // waits for every direct load this wave has in flight).
-    auto issue_partial = [&](int kt, int st) __attribute__((always_inline)) {
-        const uint8_t* p = src + (int64_t)kt * kstep;
+    uint32_t goff[T::LB];
+#pragma unroll
+    for (int i = 0; i < T::LB; ++i) goff[i] = b_off(i);
+    // The same as a per-lane part (even or odd i) and a uniform one, where
+    // that holds: row-major B always, Bt in interior tiles.
+    const bool b_split = !BT || n0 + T::BN <= N;
+    const uint32_t vb[2] = {goff[0], goff[1]};
+    auto b_uni = [&](int i) __attribute__((always_inline)) -> uint32_t {
+        return BT ? (uint32_t)(16 * (i & ~1)) * (uint32_t)KE : (uint32_t)(T::B_RPB * (i & ~1)) * (uint32_t)(N * ES);
+    };
+    const int64_t kstep_b = BT ? (int64_t)T::ROWB : (int64_t)T::BK * N * ES;
+    // Loads of B tile kt into stage st through resource rs, whose base is
+    // kb K tiles before tile kt (kb <= 15; the offsets stay below 2^31, see
+    // pp_fits).
+    auto issue_b_via = [&](__amdgpu_buffer_rsrc_t rs, int kb, int st) __attribute__((always_inline)) {
+        const uint32_t kofs = (uint32_t)kb * (uint32_t)kstep_b;
+        LDS_AS uint8_t* dst = stage_b(st) + wj * 4096;
+        if (b_split) {
+#pragma unroll
+            for (int i = 0; i < T::LB; ++i)
+                buffer_load_lds16(rs, (LDS_AS void*)(dst + i * 1024), vb[i & 1], kofs + b_uni(i));
+        } else {
+#pragma unroll
+            for (int i = 0; i < T::LB; ++i) buffer_load_lds16(rs, (LDS_AS void*)(dst + i * 1024), goff[i], kofs);
+        }
+    };
+    // B from K tile kt on (a resource per block of the main loop, or per tile).
+    auto rsrc_b = [&](int kt) __attribute__((always_inline)) {
+        const uint8_t* p = srcB + (int64_t)kt * kstep_b;
+        return buffer_rsrc(p, b_end - (p - B));
+    };
+    auto issue_b = [&](int kt, int st) __attribute__((always_inline)) { issue_b_via(rsrc_b(kt), 0, st); };
+    auto issue_b_partial = [&](int kt, int st) __attribute__((always_inline)) {
+        const uint8_t* p = srcB + (int64_t)kt * kstep_b;
         const int k0 = kt * T::BK;
-        LDS_AS uint8_t* dst = G == 0 ? stage_a(st) + wj * (T::A_RPW * T::ROWB) : stage_b(st) + wj * 4096;
-        const int nl = G == 0 ? T::LA : T::LB;
+        LDS_AS uint8_t* dst = stage_b(st) + wj * 4096;
 #pragma unroll 1
-        for (int i = 0; i < nl; ++i) {
+        for (int i = 0; i < T::LB; ++i) {
             v4u v = v4u{0u, 0u, 0u, 0u};
-            if (G == 0 || BT) {
-                const int r = rpw * wj + 16 * i + (lane >> 2);
+            if (BT) {
+                const int r = 64 * wj + 16 * i + (lane >> 2);
                 const int c = (lane & 3) ^ swz_a(r);
                 if (k0 + c * T::VE < K) v = *reinterpret_cast<const v4u*>(p + goff[i]);
             } else {
@@ -259,13 +333,25 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
     };
 
     // ---- operand reads ----
-    // A: rows MR G + 32 i + lane % 32; FP8 takes chunks 2h, 2h + 1 of the row
+    // A: rows MR G + 32 i + lane % 32 of the pair region; tile t is chunks
+    // 4 (t % 2) .. + 3 of the row; FP8 takes chunks 2h, 2h + 1 of the tile
     // (k = 32 h .. 32 h + 31), FP16 k-step u takes chunk 2u + h (h = lane / 32).
-    // The row's swizzle is that of lane % 32 (row blocks start at multiples of 32).
+    // The row's swizzle is that of lane % 32 (row blocks start at multiples of 16).
     const int lr = lane & 31, h = lane >> 5;
+    const int sw8 = swz8(lr);
     const int sw = swz_a(lr);
     const int j16 = lane & 15, half = (lane >> 4) & 1;
-    auto rd_row = [&](const LDS_AS uint8_t* rowp, int u) __attribute__((always_inline)) -> Op {
+    auto rd_a = [&](const LDS_AS uint8_t* rowp, int u, int par) __attribute__((always_inline)) -> Op {
+        if constexpr (ES == 1) {
+            const v4i lo = *(const LDS_AS v4i*)(rowp + (((4 * par + 2 * h) ^ sw8) << 4));
+            const v4i hi = *(const LDS_AS v4i*)(rowp + (((4 * par + 2 * h + 1) ^ sw8) << 4));
+            return __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
+        } else {
+            return __builtin_bit_cast(v8h, *(const LDS_AS v4u*)(rowp + (((4 * par + 2 * u + h) ^ sw8) << 4)));
+        }
+    };
+    // Bt rows of a B stage (64 bytes, 4 chunks, swizzle swz_a).
+    auto rd_bt = [&](const LDS_AS uint8_t* rowp, int u) __attribute__((always_inline)) -> Op {
         if constexpr (ES == 1) {
             const v4i lo = *(const LDS_AS v4i*)(rowp + (((2 * h) ^ sw) << 4));
             const v4i hi = *(const LDS_AS v4i*)(rowp + (((2 * h + 1) ^ sw) << 4));
@@ -316,43 +402,82 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
 #pragma unroll
             for (int r = 0; r < 16; ++r) acc[i][j][r] = 0.0f;
 
+
     Op opa[T::KSUB][T::MI], opb[T::KSUB][2];
-    // One K tile: MEM(t) then MMA(t). steady: tile t+3 exists and is full
-    // (the unrolled main loop); otherwise the loads of tile t+3 are chosen at
-    // run time.
-    auto step = [&](int t, int st, bool steady) __attribute__((always_inline)) {
+    // vmcnt immediate for at most n of this wave's loads in flight, n known at
+    // run time: the largest count used here that is not above n (waiting for
+    // fewer is always safe).
+    auto wait_rt = [&](int n) __attribute__((always_inline)) {
+        if (n >= 8) __builtin_amdgcn_s_waitcnt(waitcnt_imm(8, 0));
+        else if (n >= 6) __builtin_amdgcn_s_waitcnt(waitcnt_imm(6, 0));
+        else if (n >= 4) __builtin_amdgcn_s_waitcnt(waitcnt_imm(4, 0));
+        else __builtin_amdgcn_s_waitcnt(0);
+    };
+    // This wave's loads that may stay in flight once K tile t+1 has landed,
+    // after the loads of step t were issued (t = -1: the prologue).
+    // Group 0: pairs issued after the pair of tile t+1 (at most one), unless
+    // a guarded pair load has drained them. Group 1: B tiles issued after t+1
+    // (at most two), likewise.
+    auto younger = [&](int t) __attribute__((always_inline)) -> int {
+        if (G == 0) {
+            const int sched = (t & 1) ? (t + 3) / 2 : (t + 2) / 2;  // last pair issued by now
+            if (2 * npf < nk && sched >= npf) return 0;
+            return max(0, min(sched, npf - 1) - (t + 1) / 2) * T::LAP;
+        }
+        if (nk > nk_full && t + 3 >= nk_full) return 0;
+        return max(0, min(t + 3, nk_full - 1) - (t + 1)) * T::LB;
+    };
+    // Loads of step t (odd t: group 0 the A pair (t+3)/2; every t: group 1
+    // B tile t+3), choosing full, guarded or none at run time.
+    auto issue_rt = [&](int t) __attribute__((always_inline)) {
+        if (G == 0) {
+            if (t & 1) {
+                const int p = (t + 3) / 2;
+                if (p < npf) issue_a_pair(p, p % T::AP);
+                else if (2 * p < nk) issue_a_pair_guarded(p, p % T::AP);
+            }
+        } else {
+            const int nt = t + 3;
+            if (nt < nk_full) issue_b(nt, nt % T::S);
+            else if (nt < nk) issue_b_partial(nt, nt % T::S);
+        }
+    };
+    // One K tile: MEM(t) then MMA(t). steady: every tile step t loads exists
+    // and is full, and the LDS indices are compile-time constants (t is
+    // congruent to tm modulo 12); otherwise everything is chosen at run time.
+    __amdgpu_buffer_rsrc_t rs_blk;  // B from the first K tile of the main-loop block
+    auto step = [&](int t, int tm, bool steady) __attribute__((always_inline)) {
+        const int ar = steady ? (tm / 2) % T::AP : (t / 2) % T::AP;
+        const int par = steady ? (tm & 1) : (t & 1);
+        const int bs = steady ? tm % T::S : t % T::S;
         // MEM(t)
-        const LDS_AS uint8_t* sa = stage_a(st) + (T::MR * G + lr) * T::ROWB;
+        const LDS_AS uint8_t* sa = region_a(ar) + (T::MR * G + lr) * (2 * T::ROWB);
 #pragma unroll
         for (int u = 0; u < T::KSUB; ++u)
 #pragma unroll
-            for (int i = 0; i < T::MI; ++i) opa[u][i] = rd_row(sa + 32 * i * T::ROWB, u);
+            for (int i = 0; i < T::MI; ++i) opa[u][i] = rd_a(sa + 32 * i * (2 * T::ROWB), u, par);
         if constexpr (BT) {
-            const LDS_AS uint8_t* sbt = stage_b(st) + (64 * wj + lr) * T::ROWB;
+            const LDS_AS uint8_t* sbt = stage_b(bs) + (64 * wj + lr) * T::ROWB;
 #pragma unroll
             for (int u = 0; u < T::KSUB; ++u)
 #pragma unroll
-                for (int j = 0; j < 2; ++j) opb[u][j] = rd_row(sbt + 32 * j * T::ROWB, u);
+                for (int j = 0; j < 2; ++j) opb[u][j] = rd_bt(sbt + 32 * j * T::ROWB, u);
         } else {
 #pragma unroll
             for (int u = 0; u < T::KSUB; ++u)
 #pragma unroll
-                for (int j = 0; j < 2; ++j) opb[u][j] = rd_b_rowmajor(stage_b(st), j, u);
+                for (int j = 0; j < 2; ++j) opb[u][j] = rd_b_rowmajor(stage_b(bs), j, u);
         }
-        const int nt = t + T::S - 1, nst = (st + T::S - 1) % T::S;
-        if (steady || nt < nk_full) {
-            issue_full(nt, nst);
-            wait_vm<T::LA * (T::S - 2), T::LB * (T::S - 2)>(G == 0);
-        } else if (nk == nk_full && t + 1 < nk) {
-            // the last tiles, all full: wait for tile t+1 only; min(S-2,
-            // nk-2-t) newer tiles may still be in flight
-            static_assert(T::S == 4, "the tail waits below are written for a 4-stage ring");
-            if (nk - 2 - t >= 2) wait_vm<2 * T::LA, 2 * T::LB>(G == 0);
-            else if (nk - 2 - t == 1) wait_vm<T::LA, T::LB>(G == 0);
-            else __builtin_amdgcn_s_waitcnt(waitcnt_imm(0, 0));
+        if (steady) {
+            if (G == 0) {
+                if (tm & 1) issue_a_pair((t + 3) / 2, ((tm + 3) / 2) % T::AP);
+            } else {
+                issue_b_via(rs_blk, tm + 3, (tm + 3) % T::S);
+            }
+            wait_vm<T::LAP, 2 * T::LB>(G == 0);
         } else {
-            if (nt < nk) issue_partial(nt, nst);
-            __builtin_amdgcn_s_waitcnt(0);
+            issue_rt(t);
+            wait_rt(t + 1 < nk ? younger(t) : 0);
         }
         asm volatile("s_barrier" ::: "memory");
         // MMA(t): operands pinned after the barrier, products before the next one
@@ -401,28 +526,45 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
         asm volatile("s_barrier" ::: "memory");
     };
 
-    // ---- prologue: tiles 0 .. S-2, then wait for tile 0 ----
+    // ---- prologue: A pairs 0 and 1 (tiles 0-3), B tiles 0-2; wait for tile 0 ----
+    if (G == 0) {
 #pragma unroll
-    for (int p = 0; p < T::S - 1; ++p) {
-        if (p < nk_full) issue_full(p, p);
-        else if (p < nk) issue_partial(p, p);
+        for (int p = 0; p < 2; ++p) {
+            if (p < npf) issue_a_pair(p, p);
+            else if (2 * p < nk) issue_a_pair_guarded(p, p);
+        }
+    } else {
+#pragma unroll
+        for (int kt = 0; kt < 3; ++kt) {
+            if (kt < nk_full) issue_b(kt, kt);
+            else if (kt < nk) issue_b_partial(kt, kt);
+        }
     }
-    if (nk >= T::S - 1) wait_vm<T::LA * (T::S - 2), T::LB * (T::S - 2), 15>(G == 0);
-    else __builtin_amdgcn_s_waitcnt(0);
+    wait_rt(younger(-1));
     asm volatile("s_barrier" ::: "memory");
     if (G == 1) asm volatile("s_barrier" ::: "memory");
 
-    // Main loop, unrolled by the ring size so that every stage is a fixed LDS
-    // object; it runs while the tiles it loads (up to t + 6) are full tiles.
+    // Main loop, unrolled by 12 (the A regions repeat every 6 tiles, the B
+    // stages every 4) so that every region and stage is a fixed LDS object; it
+    // runs while the tiles it loads (up to t + 15) are full tiles.
     int t = 0;
-    for (; t + 2 * T::S - 1 <= nk_full; t += T::S) {
+    for (; t + 16 <= nk_full; t += 12) {
+        rs_blk = rsrc_b(t);
         step(t, 0, true);
         step(t + 1, 1, true);
         step(t + 2, 2, true);
         step(t + 3, 3, true);
+        step(t + 4, 4, true);
+        step(t + 5, 5, true);
+        step(t + 6, 6, true);
+        step(t + 7, 7, true);
+        step(t + 8, 8, true);
+        step(t + 9, 9, true);
+        step(t + 10, 10, true);
+        step(t + 11, 11, true);
     }
 #pragma unroll 1
-    for (; t < nk; ++t) step(t, t % T::S, false);
+    for (; t < nk; ++t) step(t, 0, false);
     if (G == 0) asm volatile("s_barrier" ::: "memory");
 
     // ---- epilogue ----
@@ -499,7 +641,7 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
         return OUT == OUT_F16 ? ((r >> 1) & 7) : ((r >> 2) & 3);
     };
     static_assert(32 * T::MI * RB <= T::A_STAGE, "a wave's staged block fits in one LDS stage");
-    LDS_AS uint8_t* ep = wave < 4 ? stage_a(wave) : stage_b(wave - 4);
+    LDS_AS uint8_t* ep = wave < 4 ? stage_b(wave) : region_a((wave - 4) >> 1) + ((wave - 4) & 1) * T::A_STAGE;
     auto slot = [&](int i, int j, int q) __attribute__((always_inline)) -> int {
         const int r = 32 * i + lr, cb = (32 * j + 8 * q + 4 * h) * (RB / 64);
         return r * RB + ((((cb >> 4) ^ esw(r)) << 4) | (cb & 15));
@@ -597,7 +739,7 @@ inline bool pp_fits(const GemmArgs& a) {
     using T = Pp<ES, BM>;
     const bool aligned = aligned16(a.A) && aligned16(a.B) && (a.K * ES) % 16 == 0 && (BT || (a.N * ES) % 16 == 0);
     const bool fits = (int64_t)T::BM * a.K * ES < (1ll << 31) &&
-                      (BT ? (int64_t)T::BN * a.K * ES : (int64_t)T::BK * a.N * ES) < (1ll << 31);
+                      (BT ? (int64_t)T::BN * a.K * ES : (int64_t)16 * T::BK * a.N * ES) < (1ll << 31);
     return aligned && fits;
 }
 
