@@ -473,6 +473,26 @@ int amax_quantize_fp8_pair(const float* A, int64_t na, const float* B, int64_t n
 int64_t amax_quantize_fp8_pair_workspace_size(void);
 
 /*
+ * amax_quantize_fp8_pair_bt — amax_quantize_fp8_pair for a GEMM whose B is
+ * given row-major, with B's codes written K-major for the _bt GEMM calls:
+ * qbt[n * K + k] = FP8(fl32(B[k * N + n] / scale[1])). amax, scale and qa are
+ * those of amax_quantize_fp8_pair on (A, na, B, K * N), and qbt is its qb
+ * transposed, bit for bit. P1 §3.2 (the weight held in the layout the kernel
+ * reads), with P2 §3.2 / §4.3 / §4.4 and P1 §3.3 as for the call above.
+ *   A, na      device, float[na]
+ *   B, K, N    device, float[K * N], row-major [K, N]; K * N = 0: only A is
+ *              processed, amax[1] and scale[1] are not written
+ *   fmt, pow2, amax, scale, qa, workspace  as amax_quantize_fp8_pair
+ *   qbt        device, uint8[N * K], row-major [N, K], written
+ * Errors: as amax_quantize_fp8_pair (GEMM_ERR_DIM also for K or N negative or
+ * above 2^31 - 1).
+ * No allocation.
+ */
+int amax_quantize_fp8_pair_bt(const float* A, int64_t na, const float* B, int64_t K, int64_t N, int fmt,
+                              int pow2, float* amax, float* scale, uint8_t* qa, uint8_t* qbt, void* workspace,
+                              int64_t workspace_bytes, hipStream_t stream);
+
+/*
  * gemm_fp8_exact / gemm_fp8_exact_bt — gemm_fp8_fmt / gemm_fp8_fmt_bt with
  * every product exact and every addition an FP32 addition (P2 §2.1: FP8
  * inputs with FP32 accumulation; §4.3: results are checked against an FP32

@@ -38,6 +38,8 @@ Functions keep the C names:
   Both FP8 operands in two launches (amax, scale and quantize of A and B):
     amax_quantize_fp8_pair(xa, xb, fmt=FMT_E4M3, pow2=False, amax=None, scale=None, qa=None, qb=None,
                            workspace=None, stream=None) -> (amax[2], scale[2], qa, qb)
+    amax_quantize_fp8_pair_bt(xa, xb, fmt=FMT_E4M3, pow2=False, amax=None, scale=None, qa=None, qbt=None,
+                              workspace=None, stream=None) -> (amax[2], scale[2], qa, qbt[N, K])
   Exact-accumulation FP8 (FP8 codes widened to FP16, FP16 matrix cores):
     gemm_fp8_exact(A, fmt_a, B, fmt_b, sA, sB, C, sOut=None, stream=None, out_fmt=None)
     gemm_fp8_exact_bt(A, fmt_a, Bt, fmt_b, sA, sB, C, sOut=None, stream=None, out_fmt=None)
@@ -153,6 +155,8 @@ def lib() -> ctypes.CDLL:
                                       ctypes.POINTER(i64)]
     L.amax_quantize_fp8_pair.restype = i32
     L.amax_quantize_fp8_pair.argtypes = [vp, i64, vp, i64, i32, i32, vp, vp, vp, vp, vp, i64, vp]
+    L.amax_quantize_fp8_pair_bt.restype = i32
+    L.amax_quantize_fp8_pair_bt.argtypes = [vp, i64, vp, i64, i64, i32, i32, vp, vp, vp, vp, vp, i64, vp]
     L.amax_quantize_fp8_pair_workspace_size.restype = i64
     L.amax_quantize_fp8_pair_workspace_size.argtypes = []
     L.gemm_fp8_exact.restype = i32
@@ -705,3 +709,38 @@ def amax_quantize_fp8_pair(xa, xb, fmt=FMT_E4M3, pow2=False, amax=None, scale=No
                                         workspace.numel() * workspace.element_size(), _stream_handle(stream)),
            "amax_quantize_fp8_pair")
     return amax, scale, qa, qb
+
+
+def amax_quantize_fp8_pair_bt(xa, xb, fmt=FMT_E4M3, pow2=False, amax=None, scale=None, qa=None, qbt=None,
+                              workspace=None, stream=None):
+    """amax_quantize_fp8_pair for a row-major float32 xb[K, N] whose codes are
+    written K-major: returns (amax[2], scale[2], qa, qbt) with qbt[N, K] the
+    transpose of amax_quantize_fp8_pair's qb, for the gemm_*_bt calls."""
+    torch = _torch()
+    for name, x in (("xa", xa), ("xb", xb)):
+        if x.dtype != torch.float32:
+            raise ValueError(f"{name} must be float32")
+    if xb.dim() != 2 or not xb.is_contiguous():
+        raise ValueError("xb must be a contiguous [K, N] matrix")
+    K, N = xb.shape
+    dev = xa.device
+    if amax is None:
+        amax = torch.empty(2, dtype=torch.float32, device=dev)
+    if scale is None:
+        scale = torch.empty(2, dtype=torch.float32, device=dev)
+    if qa is None:
+        qa = torch.empty(xa.shape, dtype=torch.uint8, device=dev)
+    if qbt is None:
+        qbt = torch.empty((N, K), dtype=torch.uint8, device=dev)
+    qav, qbv = _u8(qa, fmt), _u8(qbt, fmt)
+    if qav.numel() != xa.numel() or qbv.numel() != xb.numel():
+        raise ValueError("q must have as many elements as its x")
+    if amax.numel() < 2 or scale.numel() < 2:
+        raise ValueError("amax and scale need one element per tensor")
+    if workspace is None:
+        workspace = torch.empty(int(lib().amax_quantize_fp8_pair_workspace_size()), dtype=torch.uint8, device=dev)
+    _check(lib().amax_quantize_fp8_pair_bt(_ptr(xa), xa.numel(), _ptr(xb), K, N, int(fmt), 1 if pow2 else 0,
+                                           _ptr(amax), _ptr(scale), _ptr(qav), _ptr(qbv), _ptr(workspace),
+                                           workspace.numel() * workspace.element_size(), _stream_handle(stream)),
+           "amax_quantize_fp8_pair_bt")
+    return amax, scale, qa, qbt

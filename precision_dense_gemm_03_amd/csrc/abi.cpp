@@ -475,6 +475,33 @@ int amax_quantize_fp8_pair(const float* A, int64_t na, const float* B, int64_t n
                                                reinterpret_cast<uint32_t*>(workspace), stream));
 }
 
+int amax_quantize_fp8_pair_bt(const float* A, int64_t na, const float* B, int64_t K, int64_t N, int fmt, int pow2,
+                              float* amax, float* scale, uint8_t* qa, uint8_t* qbt, void* workspace,
+                              int64_t workspace_bytes, hipStream_t stream) {
+    if (fmt != GEMM_FMT_E4M3 && fmt != GEMM_FMT_E5M2) return GEMM_ERR_DTYPE;
+    if (!dim_ok(K) || !dim_ok(N) || !bytes_ok(na, 1, 4) || !bytes_ok(K, N, 4)) return GEMM_ERR_DIM;
+    const int64_t nb = K * N;
+    if (!amax || !scale || !workspace) return GEMM_ERR_NULL;
+    if ((na > 0 && (!A || !qa)) || (nb > 0 && (!B || !qbt))) return GEMM_ERR_NULL;
+    const int64_t ws_need = amax_quantize_fp8_pair_workspace_size();
+    if (workspace_bytes < ws_need || ((uintptr_t)workspace & 15u) != 0) return GEMM_ERR_WORKSPACE;
+    const int64_t sb = nb > 0 ? 8 : 4;  // bytes of amax and of scale
+    const void* w_ptr[5] = {amax, scale, workspace, qa, qbt};
+    const int64_t w_bytes[5] = {sb, sb, ws_need, na, nb};
+    const void* r_ptr[2] = {A, B};
+    const int64_t r_bytes[2] = {4 * na, 4 * nb};
+    for (int i = 0; i < 5; ++i) {
+        for (int j = 0; j < 2; ++j)
+            if (overlaps(w_ptr[i], w_bytes[i], r_ptr[j], r_bytes[j])) return GEMM_ERR_ALIAS;
+        for (int j = i + 1; j < 5; ++j)
+            if (overlaps(w_ptr[i], w_bytes[i], w_ptr[j], w_bytes[j])) return GEMM_ERR_ALIAS;
+    }
+    const int st = check_device();
+    if (st != GEMM_OK) return st;
+    return status_of(launch_amax_quantize_pair_bt(A, na, B, K, N, fmt, pow2 ? 1 : 0, amax, scale, qa, qbt,
+                                                  reinterpret_cast<uint32_t*>(workspace), stream));
+}
+
 int amax_f32(const float* x, int64_t n, float* amax, float* scale, hipStream_t stream) {
     return amax_scale_f32(x, n, amax, scale, GEMM_FMT_E4M3, 0, stream);
 }

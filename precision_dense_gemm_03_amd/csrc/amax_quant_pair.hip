@@ -29,6 +29,7 @@
 
 #include "device_common.h"
 #include "kernels.h"
+#include "quantize_tile.h"
 
 namespace libgemm {
 
@@ -101,11 +102,12 @@ __global__ __launch_bounds__(kThreads) void pair_reduce_kernel(const float* __re
     if (threadIdx.x == 0) slots[b] = m;
 }
 
+// Quantize x[0, n) into q by blocks [0, nblk) of the grid (this is block bid).
 template <int FMT>
 __device__ __forceinline__ void quantize_range(const float* __restrict__ x, int64_t n, float s,
-                                               uint8_t* __restrict__ q, bool vec) {
-    const int64_t tid = (int64_t)blockIdx.x * kThreads + threadIdx.x;
-    const int64_t nthreads = (int64_t)gridDim.x * kThreads;
+                                               uint8_t* __restrict__ q, bool vec, int bid, int nblk) {
+    const int64_t tid = (int64_t)bid * kThreads + threadIdx.x;
+    const int64_t nthreads = (int64_t)nblk * kThreads;
     int64_t done = 0;
     if (vec) {
         const v4f* x4 = reinterpret_cast<const v4f*>(x);
@@ -151,8 +153,48 @@ __global__ __launch_bounds__(kThreads) void pair_quantize_kernel(const float* __
             scale[1] = sb;
         }
     }
-    quantize_range<FMT>(xa, na, sa, qa, vec_a);
-    if (pb > 0) quantize_range<FMT>(xb, nb, sb, qb, vec_b);
+    quantize_range<FMT>(xa, na, sa, qa, vec_a, blockIdx.x, gridDim.x);
+    if (pb > 0) quantize_range<FMT>(xb, nb, sb, qb, vec_b, blockIdx.x, gridDim.x);
+}
+
+// The maxima of the slots, both scales, and (block 0) amax[0..1], scale[0..1].
+template <int FMT>
+__device__ __forceinline__ void pair_scales(int pa, int pb, const uint32_t* __restrict__ slots, int pow2,
+                                            float* __restrict__ amax, float* __restrict__ scale, uint32_t* red,
+                                            float& sa, float& sb) {
+    uint32_t ma = 0u, mb = 0u;
+    for (int i = threadIdx.x; i < pa; i += kThreads) ma = max(ma, slots[i]);
+    for (int i = threadIdx.x; i < pb; i += kThreads) mb = max(mb, slots[pa + i]);
+    ma = block_max(ma, red);
+    mb = block_max(mb, red);
+    const float amax_a = bits_f32(ma), amax_b = bits_f32(mb);
+    sa = scale_for_format(amax_a, FMT, pow2);
+    sb = scale_for_format(amax_b, FMT, pow2);
+    if (blockIdx.x == 0 && threadIdx.x == 0) {
+        amax[0] = amax_a;
+        scale[0] = sa;
+        amax[1] = amax_b;
+        scale[1] = sb;
+    }
+}
+
+// Launch 2 with B's codes written K-major: blocks [0, ga) quantize A as
+// pair_quantize_kernel does, blocks [ga, ga + tiles) one 128 x 64 block of
+// B[K, N] each into Bt[N, K] (quantize_tile.h), with the same arithmetic.
+template <int FMT>
+__global__ __launch_bounds__(kThreads) void pair_quantize_bt_kernel(
+    const float* __restrict__ xa, int64_t na, const float* __restrict__ xb, int64_t K, int64_t N, int pa, int pb,
+    const uint32_t* __restrict__ slots, int pow2, float* __restrict__ amax, float* __restrict__ scale,
+    uint8_t* __restrict__ qa, uint8_t* __restrict__ qbt, int vec_a, int ga, int64_t tiles_c, int vec_in_b,
+    int vec_out_b) {
+    static_assert(kThreads == kQtThreads, "one thread count");
+    __shared__ uint32_t red[kThreads / 64];
+    __shared__ __attribute__((aligned(16))) uint8_t t[kQtCols * kQtPitch];
+    float sa, sb;
+    pair_scales<FMT>(pa, pb, slots, pow2, amax, scale, red, sa, sb);
+    if ((int)blockIdx.x < ga) quantize_range<FMT>(xa, na, sa, qa, vec_a, blockIdx.x, ga);
+    else quantize_transposed_tile<FMT>(xb, K, N, sb, qbt, blockIdx.x - ga, tiles_c, vec_in_b, vec_out_b,
+                                       (LDS_AS uint8_t*)t);
 }
 
 bool aligned16(const void* p) { return ((uintptr_t)p & 15u) == 0; }
@@ -190,6 +232,47 @@ hipError_t launch_amax_quantize_pair(const float* xa, int64_t na, const float* x
     else
         pair_quantize_kernel<FMT_E4M3><<<grid, kThreads, 0, stream>>>(xa, na, xb, nb, pa, pb, slots, pow2, amax, scale,
                                                                       qa, qb, qvec_a, qvec_b);
+    return hipGetLastError();
+}
+
+// As launch_amax_quantize_pair with B = xb[K, N] row-major and its codes
+// written K-major into qbt[N, K]. Launch 1 is the same reduce; in launch 2
+// A's blocks take 8192 elements each (the size of one B block), at most 4096.
+hipError_t launch_amax_quantize_pair_bt(const float* xa, int64_t na, const float* xb, int64_t K, int64_t N, int fmt,
+                                        int pow2, float* amax, float* scale, uint8_t* qa, uint8_t* qbt,
+                                        uint32_t* slots, hipStream_t stream) {
+    const int64_t nb = K * N;
+    if (nb == 0) return launch_amax_quantize_pair(xa, na, xb, 0, fmt, pow2, amax, scale, qa, qbt, slots, stream);
+    const int64_t total = na + nb;
+    const int64_t want = std::min<int64_t>(kPairSlots, (total + 16383) / 16384);
+    int pa = (int)std::max<int64_t>(1, want * na / total);
+    int pb = (int)std::max<int64_t>(1, want - pa);
+    if (pa + pb > kPairSlots) pa = kPairSlots - pb;
+    auto chunk_of = [](int64_t n, int p) -> int64_t {
+        const int64_t c = (n + p - 1) / p;
+        return (c + 1023) / 1024 * 1024;
+    };
+    const int64_t ca = chunk_of(na, pa), cb = chunk_of(nb, pb);
+    const int vec_a = aligned16(xa), vec_b = aligned16(xb);
+    pair_reduce_kernel<<<pa + pb, kThreads, 0, stream>>>(xa, na, xb, nb, pa, pb, ca, cb, vec_a, vec_b, slots);
+    const int qvec_a = vec_a && ((uintptr_t)qa & 3u) == 0;
+    const int64_t tiles_r = (K + kQtRows - 1) / kQtRows, tiles_c = (N + kQtCols - 1) / kQtCols;
+    const int64_t tiles = tiles_r * tiles_c;
+    const int ga = (int)std::min<int64_t>(4096, std::max<int64_t>(1, (na + 8191) / 8192));
+    if (tiles + ga > 0x7FFFFFFF) return hipErrorInvalidValue;
+    // 16-byte input rows: an aligned base and N % 4 == 0; 16-byte output
+    // pieces: an aligned base and K % 16 == 0.
+    const int vec_in = vec_b && N % 4 == 0;
+    const int vec_out = aligned16(qbt) && K % 16 == 0;
+    const unsigned grid = (unsigned)(ga + tiles);
+    if (fmt == FMT_E5M2)
+        pair_quantize_bt_kernel<FMT_E5M2><<<grid, kThreads, 0, stream>>>(xa, na, xb, K, N, pa, pb, slots, pow2, amax,
+                                                                         scale, qa, qbt, qvec_a, ga, tiles_c, vec_in,
+                                                                         vec_out);
+    else
+        pair_quantize_bt_kernel<FMT_E4M3><<<grid, kThreads, 0, stream>>>(xa, na, xb, K, N, pa, pb, slots, pow2, amax,
+                                                                         scale, qa, qbt, qvec_a, ga, tiles_c, vec_in,
+                                                                         vec_out);
     return hipGetLastError();
 }
 

@@ -105,6 +105,10 @@ constexpr int kPairSlots = 1024;
 hipError_t launch_amax_quantize_pair(const float* xa, int64_t na, const float* xb, int64_t nb, int fmt, int pow2,
                                      float* amax, float* scale, uint8_t* qa, uint8_t* qb, uint32_t* slots,
                                      hipStream_t stream);
+// The same with B = xb[K, N] row-major and its codes written K-major, qbt[N, K].
+hipError_t launch_amax_quantize_pair_bt(const float* xa, int64_t na, const float* xb, int64_t K, int64_t N, int fmt,
+                                        int pow2, float* amax, float* scale, uint8_t* qa, uint8_t* qbt,
+                                        uint32_t* slots, hipStream_t stream);
 // Quantize with a transposed output: q[c * rows + r] = code(x[r * cols + c] / scale).
 hipError_t launch_quantize_transposed(const float* x, int64_t rows, int64_t cols, const float* scale, uint8_t* q,
                                       int fmt, hipStream_t stream);

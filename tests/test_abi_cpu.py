@@ -487,3 +487,21 @@ def test_pair_quantize_argument_validation():
     assert L.amax_quantize_fp8_pair(A, 10, B, 10, 0, 0, am, sc, qa, qa + 5, w, ws, None) == -8  # qa, qb overlap
     assert L.amax_quantize_fp8_pair(A, 10, B, 10, 0, 0, am, am + 4, qa, qb, w, ws, None) == -8  # amax[1] is scale
     assert L.amax_quantize_fp8_pair(A, 10, B, 10, 0, 0, am, sc, qa, qb, qb, ws, None) == -8     # ws over qb
+
+
+def test_pair_bt_argument_validation():
+    """amax_quantize_fp8_pair_bt rejects what amax_quantize_fp8_pair rejects,
+    and K or N out of range, before any device work."""
+    L = g.lib()
+    ws = L.amax_quantize_fp8_pair_workspace_size()
+    A, B = FAKE, FAKE2
+    am, sc, qa, qb, w = FAKE3, FAKE3 + 64, FAKE3 + 4096, FAKE3 + 8192, FAKE3 + 65536
+    # (A, na, B, K, N, fmt, pow2, amax, scale, qa, qbt, ws, ws_bytes, stream)
+    assert L.amax_quantize_fp8_pair_bt(A, 10, B, 2, 5, 7, 0, am, sc, qa, qb, w, ws, None) == -3      # format
+    assert L.amax_quantize_fp8_pair_bt(A, 10, B, -1, 5, 0, 0, am, sc, qa, qb, w, ws, None) == -2     # K
+    assert L.amax_quantize_fp8_pair_bt(A, 10, B, 2, 2 ** 31, 0, 0, am, sc, qa, qb, w, ws, None) == -2  # N
+    assert L.amax_quantize_fp8_pair_bt(A, -1, B, 2, 5, 0, 0, am, sc, qa, qb, w, ws, None) == -2     # na
+    assert L.amax_quantize_fp8_pair_bt(A, 10, B, 2, 5, 0, 0, am, sc, qa, None, w, ws, None) == -1   # qbt
+    assert L.amax_quantize_fp8_pair_bt(A, 10, B, 2, 5, 0, 0, am, sc, qa, qb, w, ws - 1, None) == -9
+    assert L.amax_quantize_fp8_pair_bt(A, 10, B, 2, 5, 0, 0, am, sc, qa, qa + 5, w, ws, None) == -8  # qa, qbt overlap
+    assert L.amax_quantize_fp8_pair_bt(A, 10, B, 2, 5, 0, 0, am, sc, qa, B + 4, w, ws, None) == -8   # qbt over B
