@@ -213,6 +213,40 @@ __device__ __forceinline__ void lds_tr16_x2(v4s (&t)[2], uint32_t a0, uint32_t a
         : "memory");
 }
 
+// Eight transpose reads with one wait: every operand read of a MEM phase
+// waits for the LDS once, not once per group of four.
+__device__ __forceinline__ void lds_tr8_x8(v2i (&t)[8], const uint32_t (&a)[8]) {
+    asm volatile(
+        "ds_read_b64_tr_b8 %0, %8\n\t"
+        "ds_read_b64_tr_b8 %1, %9\n\t"
+        "ds_read_b64_tr_b8 %2, %10\n\t"
+        "ds_read_b64_tr_b8 %3, %11\n\t"
+        "ds_read_b64_tr_b8 %4, %12\n\t"
+        "ds_read_b64_tr_b8 %5, %13\n\t"
+        "ds_read_b64_tr_b8 %6, %14\n\t"
+        "ds_read_b64_tr_b8 %7, %15\n\t"
+        "s_waitcnt lgkmcnt(0)"
+        : "=&v"(t[0]), "=&v"(t[1]), "=&v"(t[2]), "=&v"(t[3]), "=&v"(t[4]), "=&v"(t[5]), "=&v"(t[6]), "=&v"(t[7])
+        : "v"(a[0]), "v"(a[1]), "v"(a[2]), "v"(a[3]), "v"(a[4]), "v"(a[5]), "v"(a[6]), "v"(a[7])
+        : "memory");
+}
+
+__device__ __forceinline__ void lds_tr16_x8(v4s (&t)[8], const uint32_t (&a)[8]) {
+    asm volatile(
+        "ds_read_b64_tr_b16 %0, %8\n\t"
+        "ds_read_b64_tr_b16 %1, %9\n\t"
+        "ds_read_b64_tr_b16 %2, %10\n\t"
+        "ds_read_b64_tr_b16 %3, %11\n\t"
+        "ds_read_b64_tr_b16 %4, %12\n\t"
+        "ds_read_b64_tr_b16 %5, %13\n\t"
+        "ds_read_b64_tr_b16 %6, %14\n\t"
+        "ds_read_b64_tr_b16 %7, %15\n\t"
+        "s_waitcnt lgkmcnt(0)"
+        : "=&v"(t[0]), "=&v"(t[1]), "=&v"(t[2]), "=&v"(t[3]), "=&v"(t[4]), "=&v"(t[5]), "=&v"(t[6]), "=&v"(t[7])
+        : "v"(a[0]), "v"(a[1]), "v"(a[2]), "v"(a[3]), "v"(a[4]), "v"(a[5]), "v"(a[6]), "v"(a[7])
+        : "memory");
+}
+
 // 16-byte LDS reads in one asm block with their wait, for the same reason.
 __device__ __forceinline__ void lds_b128_x1(v4i& t, uint32_t a0) {
     asm volatile("ds_read_b128 %0, %1\n\ts_waitcnt lgkmcnt(0)" : "=&v"(t) : "v"(a0) : "memory");

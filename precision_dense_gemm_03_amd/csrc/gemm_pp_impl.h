@@ -360,37 +360,55 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
             return __builtin_bit_cast(v8h, *(const LDS_AS v4u*)(rowp + (((2 * u + h) ^ sw) << 4)));
         }
     };
-    // Row-major B, block jb of this wave's columns (64 wj + 32 jb + 0..31).
-    auto rd_b_rowmajor = [&](const LDS_AS uint8_t* sb, int jb, int u) __attribute__((always_inline)) -> Op {
+    // Row-major B: all of this wave's operands of one K tile, ob[u][jb] for
+    // column block jb (64 wj + 32 jb + 0..31), as eight transpose reads with
+    // one wait.
+    // FP8: 16-lane group (h, half) reads columns 64 wj + 32 jb + 16 half +
+    // 0..15; read q: lane j16 addresses k-row 32 h + 8 q + j16 / 2, bytes
+    // 8 (j16 % 2) of the column chunk; k-row % 8 = j16 / 2.
+    // FP16, k-step u: lane j16 addresses k-row 16 u + 8 h + 4 q + j16 / 4,
+    // columns 64 wj + 32 jb + 16 half + 4 (j16 % 4) .. + 3; k-row % 4 = j16 / 4.
+    auto rd_b_rowmajor_all = [&](const LDS_AS uint8_t* sb, typename Mfma<ES>::op (&ob)[T::KSUB][2])
+        __attribute__((always_inline)) {
+        uint32_t ad[8];
         if constexpr (ES == 1) {
-            // 16-lane group (h, half): columns 64 wj + 32 jb + 16 half + 0..15;
-            // read q: lane j16 addresses k-row 32 h + 8 q + j16 / 2, bytes
-            // 8 (j16 % 2) of the column chunk; k-row % 8 = j16 / 2.
-            const int chunk = (4 * wj + 2 * jb + half) ^ swz_b<1>(j16 >> 1);
-            uint32_t ad[4];
 #pragma unroll
-            for (int q = 0; q < 4; ++q) {
-                const int k = 32 * h + 8 * q + (j16 >> 1);
-                ad[q] = lds_addr(sb + k * T::BNB + chunk * 16 + 8 * (j16 & 1));
+            for (int jb = 0; jb < 2; ++jb) {
+                const int chunk = (4 * wj + 2 * jb + half) ^ swz_b<1>(j16 >> 1);
+#pragma unroll
+                for (int q = 0; q < 4; ++q) {
+                    const int k = 32 * h + 8 * q + (j16 >> 1);
+                    ad[4 * jb + q] = lds_addr(sb + k * T::BNB + chunk * 16 + 8 * (j16 & 1));
+                }
             }
-            v2i t[4];
-            lds_tr8_x4(t, ad[0], ad[1], ad[2], ad[3]);
-            const v4i t01 = __builtin_shufflevector(t[0], t[1], 0, 1, 2, 3);
-            const v4i t23 = __builtin_shufflevector(t[2], t[3], 0, 1, 2, 3);
-            return __builtin_shufflevector(t01, t23, 0, 1, 2, 3, 4, 5, 6, 7);
+            v2i t[8];
+            lds_tr8_x8(t, ad);
+#pragma unroll
+            for (int jb = 0; jb < 2; ++jb) {
+                const v4i t01 = __builtin_shufflevector(t[4 * jb], t[4 * jb + 1], 0, 1, 2, 3);
+                const v4i t23 = __builtin_shufflevector(t[4 * jb + 2], t[4 * jb + 3], 0, 1, 2, 3);
+                ob[0][jb] = __builtin_shufflevector(t01, t23, 0, 1, 2, 3, 4, 5, 6, 7);
+            }
         } else {
-            // k-step u: lane j16 addresses k-row 16 u + 8 h + 4 q + j16 / 4,
-            // columns 64 wj + 32 jb + 16 half + 4 (j16 % 4) .. + 3; k-row % 4 = j16 / 4.
-            const int chunk = (8 * wj + 4 * jb + 2 * half + ((j16 & 3) >> 1)) ^ swz_b<2>(j16 >> 2);
-            uint32_t ad[2];
 #pragma unroll
-            for (int q = 0; q < 2; ++q) {
-                const int k = 16 * u + 8 * h + 4 * q + (j16 >> 2);
-                ad[q] = lds_addr(sb + k * T::BNB + chunk * 16 + 8 * (j16 & 1));
-            }
-            v4s t[2];
-            lds_tr16_x2(t, ad[0], ad[1]);
-            return __builtin_bit_cast(v8h, __builtin_shufflevector(t[0], t[1], 0, 1, 2, 3, 4, 5, 6, 7));
+            for (int u = 0; u < 2; ++u)
+#pragma unroll
+                for (int jb = 0; jb < 2; ++jb) {
+                    const int chunk = (8 * wj + 4 * jb + 2 * half + ((j16 & 3) >> 1)) ^ swz_b<2>(j16 >> 2);
+#pragma unroll
+                    for (int q = 0; q < 2; ++q) {
+                        const int k = 16 * u + 8 * h + 4 * q + (j16 >> 2);
+                        ad[4 * u + 2 * jb + q] = lds_addr(sb + k * T::BNB + chunk * 16 + 8 * (j16 & 1));
+                    }
+                }
+            v4s t[8];
+            lds_tr16_x8(t, ad);
+#pragma unroll
+            for (int u = 0; u < 2; ++u)
+#pragma unroll
+                for (int jb = 0; jb < 2; ++jb)
+                    ob[u][jb] = __builtin_bit_cast(
+                        v8h, __builtin_shufflevector(t[4 * u + 2 * jb], t[4 * u + 2 * jb + 1], 0, 1, 2, 3, 4, 5, 6, 7));
         }
     };
 
@@ -463,10 +481,7 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
 #pragma unroll
                 for (int j = 0; j < 2; ++j) opb[u][j] = rd_bt(sbt + 32 * j * T::ROWB, u);
         } else {
-#pragma unroll
-            for (int u = 0; u < T::KSUB; ++u)
-#pragma unroll
-                for (int j = 0; j < 2; ++j) opb[u][j] = rd_b_rowmajor(stage_b(bs), j, u);
+            rd_b_rowmajor_all(stage_b(bs), opb);
         }
         if (steady) {
             if (G == 0) {
