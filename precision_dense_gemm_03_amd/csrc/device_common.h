@@ -141,6 +141,16 @@ __device__ __forceinline__ float epilogue_base(const float* sA, const float* sB,
     return epilogue_multiplier(sA, sB, sOut, fp8_out);
 }
 
+// The same, taken at a kernel's start and held in a scalar register: its
+// loads then wait under the prologue instead of after the main loop, where
+// their two round trips to memory stood between the last MFMA and the
+// stores.
+__device__ __forceinline__ float epilogue_base_early(const float* sA, const float* sB, const float* sOut,
+                                                     bool fp8_out, bool channel) {
+    return __builtin_bit_cast(
+        float, __builtin_amdgcn_readfirstlane(__builtin_bit_cast(int, epilogue_base(sA, sB, sOut, fp8_out, channel))));
+}
+
 // Stores one output element of the final value y (already multiplied by the
 // epilogue multiplier).
 __device__ __forceinline__ void store_out(void* C, int64_t idx, float y, int out_dtype) {

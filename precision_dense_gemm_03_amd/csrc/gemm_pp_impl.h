@@ -210,6 +210,9 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
     const int m0 = tile_m * T::BM, n0 = tile_n * T::BN;
     const int nk = (K + T::BK - 1) / T::BK;
     const int nk_full = K / T::BK;
+    // the epilogue's multiplier, loaded now (see epilogue_base_early)
+    const bool chan = (eflags & EPI_CHANNEL) != 0;
+    const float scale = epilogue_base_early(sA, sB, sOut, OUT == OUT_E4M3, chan);
     const int npf = nk_full / 2;            // K tile pairs whose two tiles are full
     const int KE = K * ES;                  // bytes of one A (or Bt) row
 
@@ -585,8 +588,6 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
     // ---- epilogue ----
     // Block (i, j), element 4q + e: row MR G + 32 i + lr, column
     // 64 wj + 32 j + 8 q + 4 h + e of the tile.
-    const bool chan = (eflags & EPI_CHANNEL) != 0;
-    const float scale = epilogue_base(sA, sB, sOut, OUT == OUT_E4M3, chan);
     const int row_t = T::MR * G + lr;          // + 32 i
     const int col_t = 64 * wj + 4 * h;         // + 32 j + 8 q
     // Vector stores need a 16-byte aligned C with 16-byte row pitches (vec_out).

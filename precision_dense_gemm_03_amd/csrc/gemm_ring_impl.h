@@ -172,6 +172,9 @@ __global__ __launch_bounds__(256) void gemm_ring_kernel(const uint8_t* __restric
     tile_coords(blockIdx.x, tiles_m, tiles_n, tile_m, tile_n);
     const int m0 = tile_m * BM, n0 = tile_n * BN;
     const int nk = (K + T::BK - 1) / T::BK, nk_full = K / T::BK;
+    // the epilogue's multiplier, loaded now (see epilogue_base_early)
+    const bool chan = (eflags & EPI_CHANNEL) != 0;
+    const float scale = epilogue_base_early(sA, sB, sOut, OUT == OUT_E4M3, chan);
     const int k0p = nk_full * T::BK;                 // first k of the partial tile (when nk > nk_full)
 
     // ---- this wave's direct loads: 1 KiB load j = wave + 4 i of every stage ----
@@ -418,8 +421,6 @@ __global__ __launch_bounds__(256) void gemm_ring_kernel(const uint8_t* __restric
     }
 
     // ---- epilogue: lane holds row 16 wr + j16 and columns 16 (TN wc + tn) + 4 g + 0..3 ----
-    const bool chan = (eflags & EPI_CHANNEL) != 0;
-    const float scale = epilogue_base(sA, sB, sOut, OUT == OUT_E4M3, chan);
     const int row = m0 + 16 * wr + j16;
     const bool interior = vec_out && (m0 + BM <= M) && (n0 + BN <= N);
 #pragma unroll
