@@ -267,3 +267,42 @@ def test_pingpong_fp8_out_codes(cfg, bt, monkeypatch):
         bad = np.argwhere(got != ref)
         assert bad.size == 0, f"{cfg_bt} fmt {fmt}: {len(bad)} codes differ, first at {bad[0]}: " \
                               f"{got[tuple(bad[0])]:#x} vs {ref[tuple(bad[0])]:#x}"
+
+
+# Long K on the ping-pong kernel: several unrolled 12-step blocks of the main
+# loop, then the run-time tail: a partial last K tile, an odd number of full
+# tiles (the last A pair holds one tile, loaded with guards), or both; M and N
+# edges (clamped rows of A and Bt, clamped columns of row-major B).
+# Every shape keeps 16-byte rows (K * e and N * e multiples of 16), so the
+# kernel takes it rather than handing it to the register-staged kernel.
+PP_LONG = [("pp_fp8_256x256x64", "fp8", (300, 272, 4128)), ("pp_fp8_256x256x64", "fp8", (260, 528, 4160)),
+           ("pp_fp8_192x256x64", "fp8", (200, 304, 4208)), ("pp_f16_256x256x32", "f16", (300, 272, 2064)),
+           ("pp_f16_192x256x32", "f16", (200, 264, 2080))]
+
+
+@pytest.mark.parametrize("cfg,kind,shape", PP_LONG)
+@pytest.mark.parametrize("bt", [False, True])
+def test_pingpong_long_k_tails(cfg, kind, shape, bt, monkeypatch):
+    M, N, K = shape
+    e = 1 if kind == "fp8" else 2
+    assert (K * e) % 16 == 0 and (N * e) % 16 == 0
+    name = cfg + ("_bt" if bt else "")
+    monkeypatch.setenv("LIBGEMM_CONFIG", name)
+    say(f"{name} {M}x{N}x{K}")
+    if kind == "fp8":
+        ca = wl.random_e4m3_codes((M, K), 3 * M + K)
+        cb = wl.random_e4m3_codes((K, N), 5 * N + K)
+        R, S = orc.gemm(orc.FMT_E4M3, ca, cb)
+        ta, tb = dev(ca), dev(np.ascontiguousarray(cb.T) if bt else cb)
+        s1 = scalar(1.0)
+        C = torch.empty((M, N), dtype=torch.float32, device=DEV)
+        (g.gemm_fp8_scaled_bt if bt else g.gemm_fp8_scaled)(ta, tb, s1, s1, C)
+        check_f32(host(C), R, S, what=name, T=fp8_dot_allowance(ca, cb))
+    else:
+        a16 = wl.random_f16((M, K), 7 * M + K)
+        b16 = wl.random_f16((K, N), 11 * N + K)
+        R, S = orc.gemm(orc.FMT_F16, a16.view(np.uint16), b16.view(np.uint16))
+        ta, tb = dev(a16), dev(np.ascontiguousarray(b16.T) if bt else b16)
+        C = torch.empty((M, N), dtype=torch.float32, device=DEV)
+        (g.gemm_f16_bt if bt else g.gemm_f16)(ta, tb, C)
+        check_f32(host(C), R, S, what=name)
