@@ -101,9 +101,99 @@ __device__ __forceinline__ int swz_row(int r) { return (r >> 1) & 7; }
 // One K-step's operand reads of every column block in one asm group with one
 // LDS wait (A's operand first, then the column blocks' reads in order): the
 // wave pays one LDS round trip per k-step instead of one per column block
-// (row-major B, and FP16 K-major B).
+// (row-major FP8 B; FP16 takes both of its k-steps in one group).
 // The outputs are early-clobber and the wait is inside the block, for the
 // reasons given with the groups in device_common.h.
+__device__ __forceinline__ void ring_b128x2_tr16x4(v4i (&r)[2], v4s (&t)[4], const uint32_t (&a)[6]) {
+    asm volatile(
+        "ds_read_b128 %0, %6\n\t"
+        "ds_read_b128 %1, %7\n\t"
+        "ds_read_b64_tr_b16 %2, %8\n\t"
+        "ds_read_b64_tr_b16 %3, %9\n\t"
+        "ds_read_b64_tr_b16 %4, %10\n\t"
+        "ds_read_b64_tr_b16 %5, %11\n\t"
+        "s_waitcnt lgkmcnt(0)"
+        : "=&v"(r[0]), "=&v"(r[1]), "=&v"(t[0]), "=&v"(t[1]), "=&v"(t[2]), "=&v"(t[3])
+        : "v"(a[0]), "v"(a[1]), "v"(a[2]), "v"(a[3]), "v"(a[4]), "v"(a[5])
+        : "memory");
+}
+
+__device__ __forceinline__ void ring_b128x2_tr16x8(v4i (&r)[2], v4s (&t)[8], const uint32_t (&a)[10]) {
+    asm volatile(
+        "ds_read_b128 %0, %10\n\t"
+        "ds_read_b128 %1, %11\n\t"
+        "ds_read_b64_tr_b16 %2, %12\n\t"
+        "ds_read_b64_tr_b16 %3, %13\n\t"
+        "ds_read_b64_tr_b16 %4, %14\n\t"
+        "ds_read_b64_tr_b16 %5, %15\n\t"
+        "ds_read_b64_tr_b16 %6, %16\n\t"
+        "ds_read_b64_tr_b16 %7, %17\n\t"
+        "ds_read_b64_tr_b16 %8, %18\n\t"
+        "ds_read_b64_tr_b16 %9, %19\n\t"
+        "s_waitcnt lgkmcnt(0)"
+        : "=&v"(r[0]), "=&v"(r[1]), "=&v"(t[0]), "=&v"(t[1]), "=&v"(t[2]), "=&v"(t[3]), "=&v"(t[4]), "=&v"(t[5]), "=&v"(t[6]), "=&v"(t[7])
+        : "v"(a[0]), "v"(a[1]), "v"(a[2]), "v"(a[3]), "v"(a[4]), "v"(a[5]), "v"(a[6]), "v"(a[7]), "v"(a[8]), "v"(a[9])
+        : "memory");
+}
+
+__device__ __forceinline__ void ring_b128x2_tr16x16(v4i (&r)[2], v4s (&t)[16], const uint32_t (&a)[18]) {
+    asm volatile(
+        "ds_read_b128 %0, %18\n\t"
+        "ds_read_b128 %1, %19\n\t"
+        "ds_read_b64_tr_b16 %2, %20\n\t"
+        "ds_read_b64_tr_b16 %3, %21\n\t"
+        "ds_read_b64_tr_b16 %4, %22\n\t"
+        "ds_read_b64_tr_b16 %5, %23\n\t"
+        "ds_read_b64_tr_b16 %6, %24\n\t"
+        "ds_read_b64_tr_b16 %7, %25\n\t"
+        "ds_read_b64_tr_b16 %8, %26\n\t"
+        "ds_read_b64_tr_b16 %9, %27\n\t"
+        "ds_read_b64_tr_b16 %10, %28\n\t"
+        "ds_read_b64_tr_b16 %11, %29\n\t"
+        "ds_read_b64_tr_b16 %12, %30\n\t"
+        "ds_read_b64_tr_b16 %13, %31\n\t"
+        "ds_read_b64_tr_b16 %14, %32\n\t"
+        "ds_read_b64_tr_b16 %15, %33\n\t"
+        "ds_read_b64_tr_b16 %16, %34\n\t"
+        "ds_read_b64_tr_b16 %17, %35\n\t"
+        "s_waitcnt lgkmcnt(0)"
+        : "=&v"(r[0]), "=&v"(r[1]), "=&v"(t[0]), "=&v"(t[1]), "=&v"(t[2]), "=&v"(t[3]), "=&v"(t[4]), "=&v"(t[5]), "=&v"(t[6]), "=&v"(t[7]), "=&v"(t[8]), "=&v"(t[9]), "=&v"(t[10]), "=&v"(t[11]), "=&v"(t[12]), "=&v"(t[13]), "=&v"(t[14]), "=&v"(t[15])
+        : "v"(a[0]), "v"(a[1]), "v"(a[2]), "v"(a[3]), "v"(a[4]), "v"(a[5]), "v"(a[6]), "v"(a[7]), "v"(a[8]), "v"(a[9]), "v"(a[10]), "v"(a[11]), "v"(a[12]), "v"(a[13]), "v"(a[14]), "v"(a[15]), "v"(a[16]), "v"(a[17])
+        : "memory");
+}
+
+__device__ __forceinline__ void ring_b128x6(v4i (&r)[6], const uint32_t (&a)[6]) {
+    asm volatile(
+        "ds_read_b128 %0, %6\n\t"
+        "ds_read_b128 %1, %7\n\t"
+        "ds_read_b128 %2, %8\n\t"
+        "ds_read_b128 %3, %9\n\t"
+        "ds_read_b128 %4, %10\n\t"
+        "ds_read_b128 %5, %11\n\t"
+        "s_waitcnt lgkmcnt(0)"
+        : "=&v"(r[0]), "=&v"(r[1]), "=&v"(r[2]), "=&v"(r[3]), "=&v"(r[4]), "=&v"(r[5])
+        : "v"(a[0]), "v"(a[1]), "v"(a[2]), "v"(a[3]), "v"(a[4]), "v"(a[5])
+        : "memory");
+}
+
+__device__ __forceinline__ void ring_b128x10(v4i (&r)[10], const uint32_t (&a)[10]) {
+    asm volatile(
+        "ds_read_b128 %0, %10\n\t"
+        "ds_read_b128 %1, %11\n\t"
+        "ds_read_b128 %2, %12\n\t"
+        "ds_read_b128 %3, %13\n\t"
+        "ds_read_b128 %4, %14\n\t"
+        "ds_read_b128 %5, %15\n\t"
+        "ds_read_b128 %6, %16\n\t"
+        "ds_read_b128 %7, %17\n\t"
+        "ds_read_b128 %8, %18\n\t"
+        "ds_read_b128 %9, %19\n\t"
+        "s_waitcnt lgkmcnt(0)"
+        : "=&v"(r[0]), "=&v"(r[1]), "=&v"(r[2]), "=&v"(r[3]), "=&v"(r[4]), "=&v"(r[5]), "=&v"(r[6]), "=&v"(r[7]), "=&v"(r[8]), "=&v"(r[9])
+        : "v"(a[0]), "v"(a[1]), "v"(a[2]), "v"(a[3]), "v"(a[4]), "v"(a[5]), "v"(a[6]), "v"(a[7]), "v"(a[8]), "v"(a[9])
+        : "memory");
+}
+
 __device__ __forceinline__ void ring_b128x2_tr8x8(v4i (&r)[2], v2i (&t)[8], const uint32_t (&a)[10]) {
     asm volatile(
         "ds_read_b128 %0, %10\n\t"
@@ -145,60 +235,6 @@ __device__ __forceinline__ void ring_b128x2_tr8x16(v4i (&r)[2], v2i (&t)[16], co
         "s_waitcnt lgkmcnt(0)"
         : "=&v"(r[0]), "=&v"(r[1]), "=&v"(t[0]), "=&v"(t[1]), "=&v"(t[2]), "=&v"(t[3]), "=&v"(t[4]), "=&v"(t[5]), "=&v"(t[6]), "=&v"(t[7]), "=&v"(t[8]), "=&v"(t[9]), "=&v"(t[10]), "=&v"(t[11]), "=&v"(t[12]), "=&v"(t[13]), "=&v"(t[14]), "=&v"(t[15])
         : "v"(a[0]), "v"(a[1]), "v"(a[2]), "v"(a[3]), "v"(a[4]), "v"(a[5]), "v"(a[6]), "v"(a[7]), "v"(a[8]), "v"(a[9]), "v"(a[10]), "v"(a[11]), "v"(a[12]), "v"(a[13]), "v"(a[14]), "v"(a[15]), "v"(a[16]), "v"(a[17])
-        : "memory");
-}
-
-__device__ __forceinline__ void ring_b128x1_tr16x4(v4i (&r)[1], v4s (&t)[4], const uint32_t (&a)[5]) {
-    asm volatile(
-        "ds_read_b128 %0, %5\n\t"
-        "ds_read_b64_tr_b16 %1, %6\n\t"
-        "ds_read_b64_tr_b16 %2, %7\n\t"
-        "ds_read_b64_tr_b16 %3, %8\n\t"
-        "ds_read_b64_tr_b16 %4, %9\n\t"
-        "s_waitcnt lgkmcnt(0)"
-        : "=&v"(r[0]), "=&v"(t[0]), "=&v"(t[1]), "=&v"(t[2]), "=&v"(t[3])
-        : "v"(a[0]), "v"(a[1]), "v"(a[2]), "v"(a[3]), "v"(a[4])
-        : "memory");
-}
-
-__device__ __forceinline__ void ring_b128x1_tr16x8(v4i (&r)[1], v4s (&t)[8], const uint32_t (&a)[9]) {
-    asm volatile(
-        "ds_read_b128 %0, %9\n\t"
-        "ds_read_b64_tr_b16 %1, %10\n\t"
-        "ds_read_b64_tr_b16 %2, %11\n\t"
-        "ds_read_b64_tr_b16 %3, %12\n\t"
-        "ds_read_b64_tr_b16 %4, %13\n\t"
-        "ds_read_b64_tr_b16 %5, %14\n\t"
-        "ds_read_b64_tr_b16 %6, %15\n\t"
-        "ds_read_b64_tr_b16 %7, %16\n\t"
-        "ds_read_b64_tr_b16 %8, %17\n\t"
-        "s_waitcnt lgkmcnt(0)"
-        : "=&v"(r[0]), "=&v"(t[0]), "=&v"(t[1]), "=&v"(t[2]), "=&v"(t[3]), "=&v"(t[4]), "=&v"(t[5]), "=&v"(t[6]), "=&v"(t[7])
-        : "v"(a[0]), "v"(a[1]), "v"(a[2]), "v"(a[3]), "v"(a[4]), "v"(a[5]), "v"(a[6]), "v"(a[7]), "v"(a[8])
-        : "memory");
-}
-
-__device__ __forceinline__ void ring_b128x3(v4i (&r)[3], const uint32_t (&a)[3]) {
-    asm volatile(
-        "ds_read_b128 %0, %3\n\t"
-        "ds_read_b128 %1, %4\n\t"
-        "ds_read_b128 %2, %5\n\t"
-        "s_waitcnt lgkmcnt(0)"
-        : "=&v"(r[0]), "=&v"(r[1]), "=&v"(r[2])
-        : "v"(a[0]), "v"(a[1]), "v"(a[2])
-        : "memory");
-}
-
-__device__ __forceinline__ void ring_b128x5(v4i (&r)[5], const uint32_t (&a)[5]) {
-    asm volatile(
-        "ds_read_b128 %0, %5\n\t"
-        "ds_read_b128 %1, %6\n\t"
-        "ds_read_b128 %2, %7\n\t"
-        "ds_read_b128 %3, %8\n\t"
-        "ds_read_b128 %4, %9\n\t"
-        "s_waitcnt lgkmcnt(0)"
-        : "=&v"(r[0]), "=&v"(r[1]), "=&v"(r[2]), "=&v"(r[3]), "=&v"(r[4])
-        : "v"(a[0]), "v"(a[1]), "v"(a[2]), "v"(a[3]), "v"(a[4])
         : "memory");
 }
 
@@ -438,23 +474,33 @@ __global__ __launch_bounds__(256) void gemm_ring_kernel(const uint8_t* __restric
                 }
                 continue;
             } else if constexpr (BT) {
-                constexpr int PA = 1;  // one 16-byte read per FP16 operand
-                uint32_t ad[PA * (1 + T::TN)];
-                ad[0] = row_lo(arow, asw, u);
+                // FP16: both k-steps' reads (A's operand, then the column
+                // blocks', per k-step) in one group, then both k-steps' MFMAs
+                if (u > 0) break;
+                uint32_t ad[2 * (1 + T::TN)];
 #pragma unroll
-                for (int tn = 0; tn < T::TN; ++tn) {
-                    const int br = 16 * (T::TN * wc + tn) + j16;
-                    const LDS_AS uint8_t* brow = base + T::A_BYTES + br * T::ROWB;
-                    const int bsw = swz_row(br);
-                    ad[PA * (1 + tn)] = row_lo(brow, bsw, u);
+                for (int uu = 0; uu < 2; ++uu) {
+                    ad[uu * (1 + T::TN)] = row_lo(arow, asw, uu);
+#pragma unroll
+                    for (int tn = 0; tn < T::TN; ++tn) {
+                        const int br = 16 * (T::TN * wc + tn) + j16;
+                        ad[uu * (1 + T::TN) + 1 + tn] = row_lo(base + T::A_BYTES + br * T::ROWB, swz_row(br), uu);
+                    }
                 }
-                v4i r[PA * (1 + T::TN)];
-                if constexpr (PA * (1 + T::TN) == 2) lds_b128_x2(r, ad[0], ad[1]);
-                else if constexpr (PA * (1 + T::TN) == 3) ring_b128x3(r, ad);
-                else ring_b128x5(r, ad);
-                a = as_op2(r[0], r[PA - 1]);
+                v4i r[2 * (1 + T::TN)];
+                if constexpr (T::TN == 1) lds_b128_x4(r, ad[0], ad[1], ad[2], ad[3]);
+                else if constexpr (T::TN == 2) ring_b128x6(r, ad);
+                else ring_b128x10(r, ad);
 #pragma unroll
-                for (int tn = 0; tn < T::TN; ++tn) b[tn] = as_op2(r[PA * (1 + tn)], r[PA * (1 + tn) + PA - 1]);
+                for (int uu = 0; uu < 2; ++uu) {
+                    const Op au = as_op2(r[uu * (1 + T::TN)], r[uu * (1 + T::TN)]);
+#pragma unroll
+                    for (int tn = 0; tn < T::TN; ++tn) {
+                        const v4i rb = r[uu * (1 + T::TN) + 1 + tn];
+                        acc[tn] = Op16<ES>::template mma<FB, FA>(as_op2(rb, rb), au, acc[tn]);
+                    }
+                }
+                break;
             } else if constexpr (ES == 1) {
                 uint32_t ad[2 + 4 * T::TN];
                 ad[0] = row_lo(arow, asw, u);
@@ -485,33 +531,35 @@ __global__ __launch_bounds__(256) void gemm_ring_kernel(const uint8_t* __restric
                     b[tn] = op_tr8(tt);
                 }
             } else {
-                uint32_t ad[1 + 2 * T::TN];
-                ad[0] = row_lo(arow, asw, u);
+                // FP16, row-major B: both k-steps in one group, as above
+                if (u > 0) break;
+                uint32_t ad[2 + 4 * T::TN];
+                ad[0] = row_lo(arow, asw, 0);
+                ad[1] = row_lo(arow, asw, 1);
 #pragma unroll
-                for (int tn = 0; tn < T::TN; ++tn) {
-                    uint32_t q4[4];
-                    b_rm_addrs(base + T::A_BYTES, tn, u, q4);
-                    ad[1 + 2 * tn] = q4[0];
-                    ad[2 + 2 * tn] = q4[1];
-                }
-                v4i r[1];
-                v4s t[2 * T::TN];
-                if constexpr (T::TN == 1) {
-                    v4s t2[2];
-                    lds_b128x1_tr16x2(r[0], t2, ad[0], ad[1], ad[2]);
-                    t[0] = t2[0];
-                    t[1] = t2[1];
-                } else if constexpr (T::TN == 2) {
-                    ring_b128x1_tr16x4(r, t, ad);
-                } else {
-                    ring_b128x1_tr16x8(r, t, ad);
-                }
-                a = as_op2(r[0], r[0]);
+                for (int uu = 0; uu < 2; ++uu)
 #pragma unroll
-                for (int tn = 0; tn < T::TN; ++tn) {
-                    const v4s tt[2] = {t[2 * tn], t[2 * tn + 1]};
-                    b[tn] = op_tr16(tt);
+                    for (int tn = 0; tn < T::TN; ++tn) {
+                        uint32_t q4[4];
+                        b_rm_addrs(base + T::A_BYTES, tn, uu, q4);
+                        ad[2 + 2 * (uu * T::TN + tn)] = q4[0];
+                        ad[3 + 2 * (uu * T::TN + tn)] = q4[1];
+                    }
+                v4i r[2];
+                v4s t[4 * T::TN];
+                if constexpr (T::TN == 1) ring_b128x2_tr16x4(r, t, ad);
+                else if constexpr (T::TN == 2) ring_b128x2_tr16x8(r, t, ad);
+                else ring_b128x2_tr16x16(r, t, ad);
+#pragma unroll
+                for (int uu = 0; uu < 2; ++uu) {
+                    const Op au = as_op2(r[uu], r[uu]);
+#pragma unroll
+                    for (int tn = 0; tn < T::TN; ++tn) {
+                        const v4s tt[2] = {t[2 * (uu * T::TN + tn)], t[2 * (uu * T::TN + tn) + 1]};
+                        acc[tn] = Op16<ES>::template mma<FB, FA>(op_tr16(tt), au, acc[tn]);
+                    }
                 }
+                break;
             }
 #pragma unroll
             for (int tn = 0; tn < T::TN; ++tn) acc[tn] = Op16<ES>::template mma<FB, FA>(b[tn], a, acc[tn]);
